@@ -1,0 +1,17 @@
+"""CPU oracle for the FP8 flash-attention forward.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+CPU-baseline leg of ``bench.py`` may import, call or execute anything in this
+package.  The HIP library never links it and the Python binding never imports
+it; the two share no code.  The oracle is plain and slow on purpose:
+
+* ``oracle.attention`` - float64 softmax(Q K^T * scale) V per segment and head.
+* ``oracle.quantize``  - per-head E4M3 quantization of Q/K/V (K centred by its
+  segment's per-channel mean).
+* ``oracle.e4m3``      - bit-level OCP E4M3 encoder/decoder.
+* ``oracle.compare``   - relative-RMS and max-abs comparators.
+
+Every function is pinned by ``-m "not gpu"`` tests in ``tests/test_oracle_*.py``
+against closed forms, brute force, a library routine or invariants.
+"""
+from . import attention, compare, e4m3, quantize  # noqa: F401

@@ -1,0 +1,120 @@
+"""CPU reference for the per-head E4M3 quantization of Q, K and V.
+
+TEST INFRASTRUCTURE ONLY: imported by ``tests/``, ``__graft_entry__.smoke()``
+and the CPU-baseline leg of ``bench.py``; never by the product path.
+
+What it follows
+---------------
+* Two passes per tensor, a per-head amax and then the pack into E4M3 codes
+  (sglang PR "[diffusion] attention: add fp8_fa_sm120 FP8 backend for SM120
+  GPUs", "Modifications", the fused_prep item).
+* Scale ``s_h = fl32(amax_h / 448)`` per (tensor, head) over every token of the
+  call, and ``1.0`` for an all-zero head (reading of "per-head scale =
+  amax/448"; E4M3 max is 448).
+* K is centred by its segment's per-channel mean before quantization.  The
+  FlashInfer "minimax_h3_sm120_varlen_attention_nvfp4" page does this for its
+  block-scaled operands and notes that the softmax is unchanged by it: a
+  per-segment constant added to every key only adds a per-query constant to
+  every score of that segment.  Q is not centred.
+* Codes: ``e4m3(fl32(y / s_h))`` with IEEE float32 division, where ``y = x``
+  for Q and V and ``y = fl32(x - mu)`` for K.
+
+Fixed-order mean (a reading; the pages fix no summation order): for segment
+``[a, b)``, channel ``(h, d)``:
+
+    sum64 = 0.0;  for each 256-token chunk [c, min(c+256, b)), c = a, a+256, ...
+        chunk = 0.0;  for t in chunk, ascending:  chunk = chunk + x[t]   (float64)
+        sum64 = sum64 + chunk                                             (float64)
+    mu = fl32(fl64(sum64 / L))
+
+Empty segments have no mean; their ``mu`` rows are 0.
+Parity pins live in ``tests/test_oracle_quantize.py``.
+"""
+from __future__ import annotations
+
+from typing import Dict, List
+
+import numpy as np
+
+from . import e4m3
+
+CHUNK = 256
+
+
+def _as_f32(x) -> np.ndarray:
+    """BF16 tensor (torch) or array -> float32 numpy array (exact widening)."""
+    try:
+        import torch
+        if isinstance(x, torch.Tensor):
+            return x.detach().to("cpu").float().numpy()
+    except ImportError:  # pragma: no cover
+        pass
+    return np.asarray(x, dtype=np.float32)
+
+
+def head_scale(amax: np.ndarray) -> np.ndarray:
+    """fl32(amax / 448) per head, 1.0 where amax == 0."""
+    amax = np.asarray(amax, dtype=np.float32)
+    s = amax / np.float32(448.0)
+    return np.where(amax == 0, np.float32(1.0), s).astype(np.float32)
+
+
+def segment_mean(x: np.ndarray, a: int, b: int) -> np.ndarray:
+    """Fixed-order float64 mean of rows [a, b) of x [T, H, D], rounded to float32."""
+    H, D = x.shape[1], x.shape[2]
+    if b <= a:
+        return np.zeros((H, D), np.float32)
+    total = np.zeros((H, D), np.float64)
+    for c in range(a, b, CHUNK):
+        chunk = np.zeros((H, D), np.float64)
+        for t in range(c, min(c + CHUNK, b)):
+            chunk = chunk + x[t].astype(np.float64)
+        total = total + chunk
+    return (total / float(b - a)).astype(np.float32)
+
+
+def quantize_plain(x) -> Dict[str, np.ndarray]:
+    """Per-head quantization of Q or V: codes [T, H, D] uint8, scale [H] float32."""
+    xf = _as_f32(x)
+    amax = np.abs(xf).max(axis=(0, 2)) if xf.shape[0] > 0 else np.zeros(xf.shape[1], np.float32)
+    s = head_scale(amax)
+    y = xf / s[None, :, None]                     # float32 / float32: IEEE division
+    return {"codes": e4m3.encode(y), "scale": s}
+
+
+def quantize_k(x, cu_seqlens: List[int]) -> Dict[str, np.ndarray]:
+    """Per-head quantization of K after per-(segment, head, channel) centring.
+
+    Returns codes [T, H, D] uint8, scale [H] float32, mu [nseg, H, D] float32.
+    """
+    xf = _as_f32(x)
+    T, H, D = xf.shape
+    nseg = len(cu_seqlens) - 1
+    mu = np.zeros((nseg, H, D), np.float32)
+    y = np.zeros_like(xf)
+    for s in range(nseg):
+        a, b = cu_seqlens[s], cu_seqlens[s + 1]
+        mu[s] = segment_mean(xf, a, b)
+        y[a:b] = xf[a:b] - mu[s][None]            # float32 subtraction, correctly rounded
+    amax = np.abs(y).max(axis=(0, 2)) if T > 0 else np.zeros(H, np.float32)
+    sc = head_scale(amax)
+    codes = e4m3.encode(y / sc[None, :, None])
+    return {"codes": codes, "scale": sc, "mu": mu}
+
+
+def quantize(q, k, v, cu_seqlens: List[int]) -> Dict[str, np.ndarray]:
+    """All three tensors.  Keys: q_codes, k_codes, v_codes ([T, H, D] uint8),
+    scales ([3, H] float32, rows Q, K, V) and mu ([nseg, H, D] float32)."""
+    rq = quantize_plain(q)
+    rk = quantize_k(k, cu_seqlens)
+    rv = quantize_plain(v)
+    return {
+        "q_codes": rq["codes"], "k_codes": rk["codes"], "v_codes": rv["codes"],
+        "scales": np.stack([rq["scale"], rk["scale"], rv["scale"]]).astype(np.float32),
+        "mu": rk["mu"],
+    }
+
+
+def dequantize(codes: np.ndarray, scale: np.ndarray) -> np.ndarray:
+    """float64 values e4m3_value(code) * s_h (the operands the attention consumes)."""
+    return e4m3.decode(codes) * np.asarray(scale, np.float64)[None, :, None]

@@ -1,0 +1,119 @@
+"""Pins for the CPU quantizer (oracle/quantize.py).
+
+* scale: closed form fl32(amax/448) with amax taken by torch, and the all-zero head;
+* fixed-order K mean: equals the exactly rounded mean (fractions) where the
+  float64 sums are exact, and a hand-worked case where the summation order
+  decides the result;
+* K amax: the brute-force max |fl32(x - mu)| equals the min/max route
+  max(fl32(max - mu), fl32(mu - min)) (rounding is monotone);
+* centring: shifting K by a per-channel constant leaves K codes unchanged when
+  the mean is exact, and dequantized centred keys give the same attention as
+  the raw keys up to quantization error;
+* codes of Q and V: one element at a time against the e4m3 brute force in
+  tests/test_oracle_e4m3.py is indirect, so here a few elements are checked
+  against torch's float8_e4m3fn cast of the same fl32(x/s).
+"""
+from fractions import Fraction
+
+import numpy as np
+import torch
+
+from oracle import quantize as Qz
+from oracle import e4m3
+
+
+def _bf16(shape, seed, scale=1.0, offset=0.0):
+    g = torch.Generator().manual_seed(seed)
+    return (torch.randn(shape, generator=g) * scale + offset).to(torch.bfloat16)
+
+
+def test_plain_scale_closed_form_and_codes():
+    x = _bf16((300, 3, 128), 1, 2.0)
+    x[:, 2] = 0                                     # an all-zero head
+    r = Qz.quantize_plain(x)
+    amax = x.float().abs().amax(dim=(0, 2)).numpy()
+    assert r["scale"][0] == np.float32(amax[0]) / np.float32(448)
+    assert r["scale"][1] == np.float32(amax[1]) / np.float32(448)
+    assert r["scale"][2] == np.float32(1.0)
+    assert np.all(r["codes"][:, 2] == 0)
+    # the max element of each head lands exactly on +-448
+    for h in range(2):
+        flat = x[:, h].float().abs().flatten()
+        i = int(flat.argmax())
+        assert e4m3.decode(r["codes"][:, h].reshape(-1)[i:i + 1])[0] in (448.0, -448.0)
+    ref = (torch.from_numpy(x.float().numpy() / r["scale"][None, :, None])
+           .to(torch.float8_e4m3fn).view(torch.uint8).numpy())
+    assert np.array_equal(r["codes"], ref)
+
+
+def test_mean_equals_exact_rational_mean():
+    T, H, D = 700, 2, 16
+    x = _bf16((T, H, D), 2).float().numpy()
+    for a, b in [(0, 700), (0, 256), (13, 600), (699, 700)]:
+        mu = Qz.segment_mean(x, a, b)
+        for h in range(H):
+            for d in range(D):
+                exact = sum(Fraction(float(v)) for v in x[a:b, h, d]) / (b - a)
+                # bf16 data: float64 partial sums are exact here, so the only
+                # roundings are the division and the final float32 cast
+                assert mu[h, d] == np.float32(float(exact))
+
+
+def test_mean_fixed_chunk_order():
+    # 257 tokens: chunk 0 = [2^60, 1, 1, ..., 1] (255 ones), chunk 1 = [-2^60].
+    # In chunk 0 each +1 is below half an ulp of 2^60 and is lost: chunk sum 2^60.
+    # Total = 2^60 + (-2^60) = 0, so mu = 0 (the exact mean would be 255/257).
+    x = np.ones((257, 1, 1), np.float32)
+    x[0] = 2.0 ** 60
+    x[256] = -(2.0 ** 60)
+    assert Qz.segment_mean(x, 0, 257)[0, 0] == 0.0
+    # with the large values in the same chunk and the ones after, the ones survive
+    y = np.ones((257, 1, 1), np.float32)
+    y[0] = 2.0 ** 60
+    y[1] = -(2.0 ** 60)
+    assert Qz.segment_mean(y, 0, 257)[0, 0] == np.float32(255.0 / 257.0)
+
+
+def test_k_amax_min_max_route_and_mu_layout():
+    T, H, D = 600, 2, 128
+    cu = [0, 100, 100, 599, 600]
+    x = _bf16((T, H, D), 3, 1.0, 0.5)
+    r = Qz.quantize_k(x, cu)
+    xf = x.float().numpy()
+    amax = np.zeros(H, np.float32)
+    for s in range(len(cu) - 1):
+        a, b = cu[s], cu[s + 1]
+        if b <= a:
+            assert np.all(r["mu"][s] == 0)
+            continue
+        mx = xf[a:b].max(axis=0)
+        mn = xf[a:b].min(axis=0)
+        mu = r["mu"][s]
+        amax = np.maximum(amax, np.maximum((mx - mu), (mu - mn)).max(axis=1))
+    assert np.array_equal(r["scale"], np.float32(amax) / np.float32(448))
+
+
+def test_k_shift_leaves_codes_unchanged_when_mean_is_exact():
+    # K on a 1/16 grid in [-2, 2]; +8 stays exactly representable in bf16 and the
+    # segment lengths are powers of two, so mu shifts by exactly 8 and y is unchanged
+    g = torch.Generator().manual_seed(4)
+    T, H, D = 512, 2, 128
+    cu = [0, 256, 512]
+    k = (torch.randint(-32, 33, (T, H, D), generator=g).float() / 16).to(torch.bfloat16)
+    k8 = (k.float() + 8.0).to(torch.bfloat16)
+    assert torch.equal(k8.float() - 8.0, k.float())
+    r0, r1 = Qz.quantize_k(k, cu), Qz.quantize_k(k8, cu)
+    assert np.array_equal(r0["codes"], r1["codes"])
+    assert np.array_equal(r0["scale"], r1["scale"])
+    assert np.array_equal(r1["mu"], r0["mu"] + np.float32(8.0))
+
+
+def test_quantize_bundle_shapes():
+    T, H = 130, 2
+    q, k, v = _bf16((T, H, 128), 5), _bf16((T, H, 128), 6), _bf16((T, H, 128), 7)
+    r = Qz.quantize(q, k, v, [0, 65, 130])
+    assert r["q_codes"].shape == (T, H, 128) and r["q_codes"].dtype == np.uint8
+    assert r["scales"].shape == (3, H) and r["scales"].dtype == np.float32
+    assert r["mu"].shape == (2, H, 128)
+    deq = Qz.dequantize(r["v_codes"], r["scales"][2])
+    assert np.abs(deq - v.float().numpy()).max() <= float(r["scales"][2].max()) * 16.0

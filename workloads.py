@@ -1,0 +1,135 @@
+"""Seeded synthetic inputs shared by the tests, the bench and the smoke check.
+
+This module draws random BF16 Q/K/V tensors and segment tables and nothing
+else: it holds none of the attention or quantization arithmetic, so both the
+CPU oracle and the HIP path can take their inputs from it without sharing any
+of the method.
+
+The workloads follow the pages' own measurement setup: normally distributed
+synthetic Q/K/V at 56 heads and head_dim 128 (sglang PR "[diffusion] attention:
+add fp8_fa_sm120 FP8 backend for SM120 GPUs", sections "Accuracy Tests" and
+"Speed Tests and Profiling"), the diffusion-transformer denoise-step length
+S=30272 (same page, "Motivation"), and the packed-varlen segment tables of the
+FlashInfer "minimax_h3_sm120_varlen_attention_nvfp4" page (parameter
+"cu_seqlens": 0 first, non-decreasing, token count last; empty segments and
+segments shorter than one tile allowed).
+
+Recipe (also stated in the design notes): a CPU ``torch.Generator`` seeded with
+``seed`` draws Q, then K, then V as float32 N(0, 1) of shape [T, H, 128] and
+rounds each to bfloat16 (round-to-nearest-even).  When ``k_offset_var`` is set,
+one more draw gives a per-(head, channel) offset ``sqrt(k_offset_var) *
+N(0, 1)`` of shape [H, 128] that is added to K in float32 before the bfloat16
+rounding.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+from typing import List, Optional
+
+import torch
+
+HEAD_DIM = 128
+
+
+@dataclass
+class Workload:
+    name: str
+    tokens: int
+    heads: int
+    cu_seqlens: List[int]
+    seed: int
+    k_offset_var: Optional[float] = None
+    # "thd": three separate contiguous [T, H, 128] tensors.
+    # "fused": views q/k/v = buf[:, 0/1/2] of one [T, 3, H, 128] buffer
+    #          (token stride 3*H*128 elements, head stride 128).
+    layout: str = "thd"
+    note: str = ""
+    softmax_scale: float = field(default=1.0 / math.sqrt(HEAD_DIM))
+
+    @property
+    def segments(self) -> List[int]:
+        c = self.cu_seqlens
+        return [c[i + 1] - c[i] for i in range(len(c) - 1)]
+
+    @property
+    def flops(self) -> float:
+        """4 * sum(L^2) * H * D: two L x L x D contractions of 2 flops per term."""
+        return 4.0 * sum(L * L for L in self.segments) * self.heads * HEAD_DIM
+
+
+def _single(T: int) -> List[int]:
+    return [0, T]
+
+
+# The five workloads, smallest first.  Seeds are 1000 + index.
+WORKLOADS = {
+    "s256_h2": Workload("s256_h2", 256, 2, _single(256), 1001,
+                        note="single segment, S=256, H=2"),
+    "s4096_h56": Workload("s4096_h56", 4096, 56, _single(4096), 1002,
+                          note="single segment, packed THD [T, 56, 128]"),
+    "s20440_h56_strided": Workload(
+        "s20440_h56_strided", 20440, 56, _single(20440), 1003,
+        note="single segment; views passed with explicit strides "
+             "{token: 56*128, head: 128}"),
+    "s30272_h56_koffset": Workload(
+        "s30272_h56_koffset", 30272, 56, _single(30272), 1004, k_offset_var=2.0,
+        note="single segment, denoise-step length; K gets a per-(head, channel) "
+             "offset drawn from N(0, 2) (variance 2)"),
+    "varlen_30272_h56": Workload(
+        "varlen_30272_h56", 30272, 56, [0, 15104, 30208, 30208, 30271, 30272], 1005,
+        note="packed varlen, segments 15104, 15104, 0, 63, 1"),
+}
+
+
+def make_workload(name: str, tokens: int, heads: int, cu_seqlens: List[int], seed: int,
+                  k_offset_var: Optional[float] = None, layout: str = "thd") -> Workload:
+    return Workload(name, tokens, heads, list(cu_seqlens), seed, k_offset_var, layout)
+
+
+def generate(w: Workload, device: str = "cpu"):
+    """Return (q, k, v) bfloat16 tensors of shape [T, H, 128] for workload ``w``.
+
+    For ``layout == "fused"`` the three tensors are non-contiguous views into
+    one [T, 3, H, 128] buffer.  The random draws are the same for both layouts.
+    """
+    g = torch.Generator(device="cpu")
+    g.manual_seed(w.seed)
+    shape = (w.tokens, w.heads, HEAD_DIM)
+    q = torch.randn(shape, generator=g, dtype=torch.float32)
+    k = torch.randn(shape, generator=g, dtype=torch.float32)
+    v = torch.randn(shape, generator=g, dtype=torch.float32)
+    if w.k_offset_var is not None:
+        off = math.sqrt(w.k_offset_var) * torch.randn((w.heads, HEAD_DIM), generator=g,
+                                                      dtype=torch.float32)
+        k = k + off.unsqueeze(0)
+    q, k, v = (t.to(torch.bfloat16) for t in (q, k, v))
+    if w.layout == "fused":
+        buf = torch.stack([q, k, v], dim=1)  # [T, 3, H, 128]
+        buf = buf.to(device)
+        return buf[:, 0], buf[:, 1], buf[:, 2]
+    return q.to(device), k.to(device), v.to(device)
+
+
+def sample_rows(tokens: int, count: int, seed: int, cu_seqlens: Optional[List[int]] = None):
+    """A sorted, seeded sample of query rows.
+
+    The last row of every non-empty segment is always included so that the
+    ragged tail of each segment is checked; the rest are drawn uniformly.
+    """
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed)
+    rows = set()
+    if cu_seqlens is not None:
+        for a, b in zip(cu_seqlens[:-1], cu_seqlens[1:]):
+            if b > a:
+                rows.add(a)
+                rows.add(b - 1)
+    count = min(count, tokens)
+    if count > len(rows):
+        perm = torch.randperm(tokens, generator=g)[: count].tolist()
+        for r in perm:
+            if len(rows) >= count:
+                break
+            rows.add(r)
+    return sorted(rows)
