@@ -6,9 +6,16 @@ TEST INFRASTRUCTURE ONLY (see the package docstring).
   The pages quote a "relative RMS" for E4M3 Q/K/V against a BF16 reference
   without defining it (sglang PR "[diffusion] attention: add fp8_fa_sm120
   FP8 backend for SM120 GPUs", "Accuracy Tests"); this is the plain reading.
-* max absolute error, compared with the FP8 operator tolerance 0.1 named on
-  the FlashInfer "minimax_h3_sm120_varlen_attention_nvfp4" page (read as an
-  element-wise absolute bound, rtol 0).
+* an element-wise bound |o - r| <= ATOL + RTOL * |r| with ATOL = 0.1 and
+  RTOL = 0.1.  The FlashInfer "minimax_h3_sm120_varlen_attention_nvfp4" page
+  (paragraph on the FP4 error) validates its FP4 route with atol = 1.0,
+  rtol = 0.1 "not the FP8 operator's 0.1"; the reading taken here is that the
+  FP8 operator uses the same pair with the absolute part 0.1.  A pure absolute
+  bound (rtol 0) cannot hold for any E4M3 path: where a row's softmax falls on
+  a single key (a length-1 segment, a one-hot row) the exact output is that V
+  row, and E4M3 rounds |v| with a relative error up to 2^-4, i.e. more than
+  0.1 once |v| > 1.6.  ``max_abs`` is still reported, and the tests also hold
+  it to 0.1 on the single-segment N(0, 1) workloads where it does apply.
 """
 from __future__ import annotations
 
@@ -17,6 +24,7 @@ import torch
 
 REL_RMS_BAR = 0.06
 ATOL_BAR = 0.1
+RTOL_BAR = 0.1
 
 
 def _f64(x) -> np.ndarray:
@@ -37,5 +45,13 @@ def max_abs(o, r) -> float:
     return float(np.max(np.abs(o - r))) if o.size else 0.0
 
 
+def allclose_excess(o, r) -> float:
+    """max over elements of |o - r| - (ATOL + RTOL |r|); <= 0 means every element is inside."""
+    o, r = _f64(o), _f64(r)
+    if not o.size:
+        return -ATOL_BAR
+    return float(np.max(np.abs(o - r) - (ATOL_BAR + RTOL_BAR * np.abs(r))))
+
+
 def within_bar(o, r) -> bool:
-    return rel_rms(o, r) <= REL_RMS_BAR and max_abs(o, r) <= ATOL_BAR
+    return rel_rms(o, r) <= REL_RMS_BAR and allclose_excess(o, r) <= 0.0
