@@ -1,0 +1,213 @@
+"""FP8 (E4M3) flash-attention forward for AMD MI355X (gfx950).
+
+Thin Python binding over the C ABI of ``libfp8attn.so`` (include/fp8attn.h):
+argument marshalling only, every step of the computation runs in the HIP
+kernels.  PyTorch provides device memory and streams.
+
+    import fp8_flash_attention_amd as fa
+    out = fa.attention(q, k, v, cu_seqlens=[0, 15104, 30208, 30208, 30271, 30272])
+
+or, with an explicit plan and workspace (no allocation per call):
+
+    plan = fa.Plan(tokens, heads, cu_seqlens, device=0)
+    ws = plan.new_workspace()
+    fa.quantize(plan, q, k, v, ws)
+    fa.forward(plan, ws, out)
+
+The computation, for every segment [a, b) of cu_seqlens and every head h, is
+``out[a:b, h] = softmax(q[a:b, h] @ k[a:b, h]^T * softmax_scale) @ v[a:b, h]``
+(FlashInfer "minimax_h3_sm120_varlen_attention_nvfp4" page), with Q/K/V
+quantized per head to E4M3 and both products on FP8 MFMA.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+from typing import Dict, Optional, Sequence, Tuple
+
+import torch
+
+from . import _lib
+from ._lib import Fp8AttnError  # noqa: F401
+
+HEAD_DIM = 128
+DEFAULT_SCALE = 1.0 / math.sqrt(HEAD_DIM)
+
+__all__ = ["Plan", "quantize", "forward", "attention", "Fp8AttnError", "HEAD_DIM", "DEFAULT_SCALE"]
+
+
+def _stream_handle(device: torch.device, stream=None) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+class Plan:
+    """A validated segment table and work schedule (``fp8attn_plan``).
+
+    ``device=None`` uses the current CUDA/HIP device; ``device=-1`` builds a
+    host-only plan that can be inspected but not run.
+    """
+
+    def __init__(self, tokens: int, heads: int, cu_seqlens: Optional[Sequence[int]] = None,
+                 softmax_scale: Optional[float] = None, device=None):
+        L = _lib.lib()
+        if cu_seqlens is None:
+            cu_seqlens = [0, tokens]
+        cu = [int(x) for x in cu_seqlens]
+        if len(cu) < 2:
+            raise ValueError("cu_seqlens needs at least two entries")
+        if device is None:
+            device = torch.cuda.current_device()
+        if isinstance(device, torch.device):
+            device = device.index if device.index is not None else torch.cuda.current_device()
+        self.device_index = int(device)
+        self.tokens = int(tokens)
+        self.heads = int(heads)
+        self.cu_seqlens = tuple(cu)
+        self.softmax_scale = float(DEFAULT_SCALE if softmax_scale is None else softmax_scale)
+        arr = (ctypes.c_int32 * len(cu))(*cu)
+        h = ctypes.c_void_p()
+        self._h = None
+        _lib.check(L.fp8attn_plan(ctypes.byref(h), self.tokens, self.heads, arr, len(cu) - 1,
+                                  ctypes.c_float(self.softmax_scale), self.device_index), "fp8attn_plan")
+        self._h = h
+        self.workspace_bytes = int(L.fp8attn_workspace_bytes(h))
+
+    @property
+    def handle(self) -> ctypes.c_void_p:
+        return self._h
+
+    @property
+    def device(self) -> torch.device:
+        return torch.device("cuda", self.device_index)
+
+    def info(self) -> Dict[str, int]:
+        buf = (ctypes.c_int64 * 8)()
+        _lib.check(_lib.lib().fp8attn_plan_info(self._h, buf), "fp8attn_plan_info")
+        keys = ["tokens", "heads", "num_segments", "workspace_rows", "work_items", "stat_chunks",
+                "query_tile", "key_tile"]
+        return dict(zip(keys, list(buf)))
+
+    def work_items(self):
+        n = ctypes.c_int64()
+        _lib.check(_lib.lib().fp8attn_plan_work_items(self._h, None, 0, ctypes.byref(n)), "work_items")
+        buf = (ctypes.c_int32 * (4 * max(1, n.value)))()
+        _lib.check(_lib.lib().fp8attn_plan_work_items(self._h, buf, n.value, ctypes.byref(n)), "work_items")
+        flat = list(buf)[: 4 * n.value]
+        return [tuple(flat[4 * i: 4 * i + 4]) for i in range(n.value)]
+
+    def new_workspace(self) -> torch.Tensor:
+        return torch.empty(self.workspace_bytes, dtype=torch.uint8, device=self.device)
+
+    def region(self, workspace: torch.Tensor, which: int) -> torch.Tensor:
+        """A typed view of one workspace region (codes, scales or K means)."""
+        ptr = ctypes.c_void_p()
+        dims = (ctypes.c_int64 * 3)()
+        _lib.check(_lib.lib().fp8attn_workspace_region(self._h, ctypes.c_void_p(workspace.data_ptr()), which,
+                                                       ctypes.byref(ptr), dims), "fp8attn_workspace_region")
+        off = ptr.value - workspace.data_ptr()
+        shape = tuple(dims)
+        if which in (_lib.REGION_Q, _lib.REGION_K, _lib.REGION_V):
+            n = shape[0] * shape[1] * shape[2]
+            return workspace[off: off + n].view(shape)
+        n = shape[0] * shape[1] * shape[2]
+        if which == _lib.REGION_SCALES:
+            shape = shape[:2]
+        return workspace[off: off + 4 * n].view(torch.float32).view(shape)
+
+    def close(self):
+        if self._h is not None:
+            _lib.lib().fp8attn_plan_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def _strides(x: torch.Tensor, name: str):
+    if x.dtype != torch.bfloat16:
+        raise TypeError(f"{name} must be bfloat16 (got {x.dtype})")
+    if x.dim() != 3 or x.shape[2] != HEAD_DIM:
+        raise ValueError(f"{name} must have shape [tokens, heads, {HEAD_DIM}] (got {tuple(x.shape)})")
+    if x.stride(2) != 1:
+        raise ValueError(f"{name} must have unit stride in the head dimension")
+    return _lib.i64_array([x.stride(0), x.stride(1)])
+
+
+def quantize(plan: Plan, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, workspace: torch.Tensor,
+             stream=None) -> None:
+    """``fp8attn_quantize``: E4M3 codes and per-head scales of q, k, v into ``workspace``."""
+    for name, x in (("q", q), ("k", k), ("v", v)):
+        if tuple(x.shape[:2]) != (plan.tokens, plan.heads):
+            raise ValueError(f"{name} shape {tuple(x.shape)} does not match the plan")
+    qs, ks, vs = _strides(q, "q"), _strides(k, "k"), _strides(v, "v")
+    st = _stream_handle(plan.device, stream)
+    _lib.check(_lib.lib().fp8attn_quantize(plan.handle, ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k.data_ptr()),
+                                           ctypes.c_void_p(v.data_ptr()), qs, ks, vs,
+                                           ctypes.c_void_p(workspace.data_ptr()), workspace.numel(), st),
+               "fp8attn_quantize")
+
+
+def forward(plan: Plan, workspace: torch.Tensor, out: Optional[torch.Tensor] = None,
+            lse: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """``fp8attn_forward``: BF16 output from the codes in ``workspace``."""
+    if out is None:
+        out = torch.empty((plan.tokens, plan.heads, HEAD_DIM), dtype=torch.bfloat16, device=plan.device)
+    if tuple(out.shape) != (plan.tokens, plan.heads, HEAD_DIM):
+        raise ValueError("out shape does not match the plan")
+    os_ = _strides(out, "out")
+    lse_ptr = None
+    if lse is not None:
+        if lse.dtype != torch.float32 or tuple(lse.shape) != (plan.heads, plan.tokens) or not lse.is_contiguous():
+            raise ValueError("lse must be a contiguous float32 [heads, tokens] tensor")
+        lse_ptr = ctypes.c_void_p(lse.data_ptr())
+    st = _stream_handle(plan.device, stream)
+    _lib.check(_lib.lib().fp8attn_forward(plan.handle, ctypes.c_void_p(workspace.data_ptr()), workspace.numel(),
+                                          ctypes.c_void_p(out.data_ptr()), os_, lse_ptr, st), "fp8attn_forward")
+    return out
+
+
+_PLANS: Dict[Tuple, Plan] = {}
+
+
+def get_plan(tokens: int, heads: int, cu_seqlens: Sequence[int], softmax_scale: float, device: int) -> Plan:
+    """Plans are cached per (cu_seqlens, heads, scale, device), as the FlashInfer page caches its
+    segment plan per (cu_seqlens, heads, device).  A plan holds only small tables."""
+    key = (tuple(int(x) for x in cu_seqlens), int(heads), float(softmax_scale), int(device))
+    p = _PLANS.get(key)
+    if p is None:
+        p = Plan(tokens, heads, cu_seqlens, softmax_scale, device)
+        _PLANS[key] = p
+    return p
+
+
+def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: Optional[Sequence[int]] = None,
+              softmax_scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+              return_lse: bool = False, causal: bool = False, workspace: Optional[torch.Tensor] = None):
+    """Dense non-causal FP8 attention over packed [tokens, heads, 128] BF16 q/k/v.
+
+    ``cu_seqlens`` is a host sequence of segment boundaries (None = one segment).
+    Causal attention is not supported and raises (there is no fallback path).
+    """
+    if causal:
+        raise Fp8AttnError(_lib.EUNSUPPORTED, "attention", "causal attention is not supported")
+    if q.dim() == 4:
+        raise Fp8AttnError(_lib.EUNSUPPORTED, "attention", "batched [B, T, H, D] input is not supported; pack "
+                           "the batch along tokens and pass cu_seqlens")
+    T, H = q.shape[0], q.shape[1]
+    if cu_seqlens is None:
+        cu_seqlens = [0, T]
+    elif isinstance(cu_seqlens, torch.Tensor):
+        cu_seqlens = cu_seqlens.tolist()
+    scale = DEFAULT_SCALE if softmax_scale is None else float(softmax_scale)
+    dev = q.device.index if q.device.index is not None else torch.cuda.current_device()
+    plan = get_plan(T, H, cu_seqlens, scale, dev)
+    ws = workspace if workspace is not None else plan.new_workspace()
+    quantize(plan, q, k, v, ws)
+    lse = torch.empty((H, T), dtype=torch.float32, device=q.device) if return_lse else None
+    out = forward(plan, ws, out, lse)
+    return (out, lse) if return_lse else out

@@ -1,0 +1,372 @@
+// C ABI of libfp8attn.so (declared in include/fp8attn.h): argument validation,
+// the segment planner / scheduler, workspace layout and launches.
+//
+// The planner follows the varlen contract of the FlashInfer
+// "minimax_h3_sm120_varlen_attention_nvfp4" page: any token count and any
+// segment lengths, including empty segments and segments shorter than one
+// tile, from a host copy of cu_seqlens (parameters "cu_seqlens" and
+// "cu_seqlens_host"; the plan is built once per segment table and head count).
+// As in the plan rework of sglang PR "[diffusion] attention: add fp8_fa_sm120
+// FP8 backend for SM120 GPUs" (review thread), a plan holds only small host
+// and device tables and never retains input or output buffers.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "../../include/fp8attn.h"
+#include "internal.h"
+
+using namespace fp8attn;
+
+struct fp8attn_plan_s {
+  int64_t tokens = 0;
+  int32_t heads = 0;
+  int32_t nseg = 0;
+  float scale = 0.f;
+  int device = -1;
+  std::vector<int32_t> cu;
+  std::vector<SegInfo> segs;
+  std::vector<Chunk> chunks;
+  std::vector<int32_t> group_seg;
+  std::vector<int4> items;        // in launch order (XCD-remapped)
+  int64_t real_items = 0;
+  WorkspaceLayout ws{};
+  // device copies, one allocation
+  void* dev = nullptr;
+  SegInfo* d_segs = nullptr;
+  Chunk* d_chunks = nullptr;
+  int32_t* d_group_seg = nullptr;
+  int4* d_items = nullptr;
+  int32_t* d_rowmap = nullptr;
+};
+
+namespace {
+
+thread_local std::string g_last_error;
+
+fp8attn_status fail(fp8attn_status s, const std::string& msg) {
+  g_last_error = msg;
+  return s;
+}
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+WorkspaceLayout make_layout(int64_t rows, int heads, int nseg, int nchunks) {
+  WorkspaceLayout w{};
+  w.rows = rows;
+  const size_t codes = (size_t)heads * rows * kHeadDim;
+  size_t off = 0;
+  w.q_off = off; off = align_up(off + codes, 256);
+  w.k_off = off; off = align_up(off + codes, 256);
+  w.v_off = off; off = align_up(off + codes, 256);
+  w.scale_off = off; off = align_up(off + sizeof(float) * 3 * heads, 256);
+  w.mu_off = off; off = align_up(off + sizeof(float) * (size_t)nseg * heads * kHeadDim, 256);
+  w.kstat_off = off; off = align_up(off + sizeof(KStat) * (size_t)nchunks * heads * kHeadDim, 256);
+  w.amax_off = off; off = align_up(off + sizeof(float) * 2 * (size_t)nchunks * heads, 256);
+  w.total = off;
+  return w;
+}
+
+// Work list: head-major; inside a head, longer segments first, then query
+// tiles in order.  The list is split into kNumXcd contiguous parts of equal
+// count (padded with empty items) and interleaved so that workgroup w, which
+// the hardware sends to XCD w % 8, takes item (w % 8) * per + w / 8: each XCD
+// walks its own contiguous run, so the concurrent workgroups of an XCD mostly
+// read the same head's K/V through that XCD's L2.
+void build_items(fp8attn_plan_s* p) {
+  std::vector<int> order(p->nseg);
+  for (int s = 0; s < p->nseg; s++) order[s] = s;
+  std::stable_sort(order.begin(), order.end(),
+                   [&](int x, int y) { return p->segs[x].len > p->segs[y].len; });
+  std::vector<int4> list;
+  for (int h = 0; h < p->heads; h++)
+    for (int s : order) {
+      const int L = p->segs[s].len;
+      for (int q0 = 0; q0 < L; q0 += kBM) list.push_back(int4{s, q0, h, 0});
+    }
+  p->real_items = (int64_t)list.size();
+  const size_t per = (list.size() + kNumXcd - 1) / kNumXcd;
+  const size_t n = per * kNumXcd;
+  p->items.assign(n, int4{-1, 0, 0, 0});
+  for (size_t w = 0; w < n; w++) {
+    const size_t src = (w % kNumXcd) * per + w / kNumXcd;
+    if (src < list.size()) p->items[w] = list[src];
+  }
+}
+
+bool strides_ok(const int64_t s[2]) {
+  return s != nullptr && s[0] > 0 && s[1] > 0 && s[0] % 8 == 0 && s[1] % 8 == 0;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
+struct DeviceGuard {
+  int prev = -1;
+  bool ok = true;
+  explicit DeviceGuard(int dev) {
+    if (hipGetDevice(&prev) != hipSuccess) { ok = false; return; }
+    if (prev != dev && hipSetDevice(dev) != hipSuccess) ok = false;
+  }
+  ~DeviceGuard() {
+    int cur = -1;
+    if (prev >= 0 && hipGetDevice(&cur) == hipSuccess && cur != prev) (void)hipSetDevice(prev);
+  }
+};
+
+}  // namespace
+
+extern "C" {
+
+fp8attn_status fp8attn_plan(fp8attn_plan_t* plan_out, int64_t tokens, int32_t heads,
+                            const int32_t* cu, int32_t num_segments, float softmax_scale,
+                            int32_t device) {
+  if (plan_out == nullptr) return fail(FP8ATTN_EINVAL, "plan_out is NULL");
+  *plan_out = nullptr;
+  if (cu == nullptr) return fail(FP8ATTN_EINVAL, "cu_seqlens_host is NULL");
+  if (num_segments < 1) return fail(FP8ATTN_EINVAL, "num_segments must be >= 1");
+  if (heads < 1) return fail(FP8ATTN_EINVAL, "heads must be >= 1");
+  if (tokens < 0) return fail(FP8ATTN_EINVAL, "tokens must be >= 0");
+  if (tokens > (int64_t)INT32_MAX / 2) return fail(FP8ATTN_EUNSUPPORTED, "tokens too large (int32 indexing)");
+  if (!std::isfinite(softmax_scale) || !(softmax_scale > 0.f))
+    return fail(FP8ATTN_EINVAL, "softmax_scale must be finite and > 0");
+  if (cu[0] != 0) return fail(FP8ATTN_EINVAL, "cu_seqlens[0] must be 0");
+  for (int s = 0; s < num_segments; s++)
+    if (cu[s + 1] < cu[s]) return fail(FP8ATTN_EINVAL, "cu_seqlens must be non-decreasing");
+  if ((int64_t)cu[num_segments] != tokens)
+    return fail(FP8ATTN_EINVAL, "cu_seqlens[num_segments] must equal tokens");
+
+  fp8attn_plan_s* p = new (std::nothrow) fp8attn_plan_s();
+  if (p == nullptr) return fail(FP8ATTN_ENOMEM, "host allocation failed");
+  p->tokens = tokens;
+  p->heads = heads;
+  p->nseg = num_segments;
+  p->scale = softmax_scale;
+  p->device = device;
+  p->cu.assign(cu, cu + num_segments + 1);
+  int64_t row = 0;
+  int32_t chunk = 0;
+  for (int s = 0; s < num_segments; s++) {
+    const int32_t L = cu[s + 1] - cu[s];
+    p->segs.push_back(SegInfo{cu[s], L, (int32_t)row, chunk});
+    for (int32_t t = 0; t < L; t += kStatChunk)
+      p->chunks.push_back(Chunk{s, cu[s] + t, std::min(kStatChunk, L - t), 0});
+    chunk += (L + kStatChunk - 1) / kStatChunk;
+    const int64_t padded = (int64_t)(L + kRowPad - 1) / kRowPad * kRowPad;
+    for (int64_t g = 0; g < padded / kPackRows; g++) p->group_seg.push_back(s);
+    row += padded;
+  }
+  for (int g = 0; g < kGuardRows / kPackRows; g++) p->group_seg.push_back(-1);
+  row += kGuardRows;
+  if (row > (int64_t)INT32_MAX / 2) {
+    delete p;
+    return fail(FP8ATTN_EUNSUPPORTED, "too many padded rows");
+  }
+  p->ws = make_layout(row, heads, num_segments, (int)p->chunks.size());
+  build_items(p);
+
+  if (device >= 0) {
+    DeviceGuard g(device);
+    if (!g.ok) {
+      delete p;
+      return fail(FP8ATTN_EHIP, "cannot select device");
+    }
+    const size_t b_segs = align_up(sizeof(SegInfo) * p->segs.size(), 256);
+    const size_t b_chunks = align_up(sizeof(Chunk) * std::max<size_t>(1, p->chunks.size()), 256);
+    const size_t b_groups = align_up(sizeof(int32_t) * p->group_seg.size(), 256);
+    const size_t b_items = align_up(sizeof(int4) * std::max<size_t>(1, p->items.size()), 256);
+    const size_t b_rowmap = align_up(sizeof(int32_t) * p->segs.size(), 256);
+    const size_t total = b_segs + b_chunks + b_groups + b_items + b_rowmap;
+    std::vector<uint8_t> host(total, 0);
+    size_t off = 0;
+    std::memcpy(host.data() + off, p->segs.data(), sizeof(SegInfo) * p->segs.size());
+    off += b_segs;
+    if (!p->chunks.empty()) std::memcpy(host.data() + off, p->chunks.data(), sizeof(Chunk) * p->chunks.size());
+    off += b_chunks;
+    std::memcpy(host.data() + off, p->group_seg.data(), sizeof(int32_t) * p->group_seg.size());
+    off += b_groups;
+    if (!p->items.empty()) std::memcpy(host.data() + off, p->items.data(), sizeof(int4) * p->items.size());
+    off += b_items;
+    for (size_t s = 0; s < p->segs.size(); s++) {
+      const int32_t r = p->segs[s].row0;
+      std::memcpy(host.data() + off + 4 * s, &r, 4);
+    }
+    hipError_t e = hipMalloc(&p->dev, total);
+    if (e != hipSuccess) {
+      delete p;
+      return fail(FP8ATTN_ENOMEM, std::string("hipMalloc of plan tables failed: ") + hipGetErrorString(e));
+    }
+    e = hipMemcpy(p->dev, host.data(), total, hipMemcpyHostToDevice);
+    if (e != hipSuccess) {
+      (void)hipFree(p->dev);
+      delete p;
+      return fail(FP8ATTN_EHIP, std::string("upload of plan tables failed: ") + hipGetErrorString(e));
+    }
+    uint8_t* d = static_cast<uint8_t*>(p->dev);
+    p->d_segs = reinterpret_cast<SegInfo*>(d);
+    p->d_chunks = reinterpret_cast<Chunk*>(d + b_segs);
+    p->d_group_seg = reinterpret_cast<int32_t*>(d + b_segs + b_chunks);
+    p->d_items = reinterpret_cast<int4*>(d + b_segs + b_chunks + b_groups);
+    p->d_rowmap = reinterpret_cast<int32_t*>(d + b_segs + b_chunks + b_groups + b_items);
+  }
+  *plan_out = p;
+  return FP8ATTN_OK;
+}
+
+size_t fp8attn_workspace_bytes(fp8attn_plan_t p) { return p == nullptr ? 0 : p->ws.total; }
+
+fp8attn_status fp8attn_quantize(fp8attn_plan_t p, const void* q, const void* k, const void* v,
+                                const int64_t q_strides[2], const int64_t k_strides[2],
+                                const int64_t v_strides[2], void* workspace, size_t workspace_bytes,
+                                void* stream) {
+  if (p == nullptr) return fail(FP8ATTN_EINVAL, "plan is NULL");
+  if (p->device < 0) return fail(FP8ATTN_EINVAL, "host-only plan cannot run");
+  if (workspace == nullptr || ((uintptr_t)workspace & 255) != 0)
+    return fail(FP8ATTN_EWORKSPACE, "workspace must be non-NULL and 256-byte aligned");
+  if (workspace_bytes < p->ws.total) return fail(FP8ATTN_EWORKSPACE, "workspace too small");
+  if (p->tokens > 0) {
+    if (q == nullptr || k == nullptr || v == nullptr) return fail(FP8ATTN_EINVAL, "q, k, v must be non-NULL");
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v))
+      return fail(FP8ATTN_EINVAL, "q, k, v must be 16-byte aligned");
+    if (!strides_ok(q_strides) || !strides_ok(k_strides) || !strides_ok(v_strides))
+      return fail(FP8ATTN_EINVAL, "strides must be positive multiples of 8 elements");
+  }
+  DeviceGuard g(p->device);
+  if (!g.ok) return fail(FP8ATTN_EHIP, "cannot select device");
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  QuantizeArgs a{};
+  a.x[0] = static_cast<const uint16_t*>(q);
+  a.x[1] = static_cast<const uint16_t*>(k);
+  a.x[2] = static_cast<const uint16_t*>(v);
+  for (int i = 0; i < 3; i++) {
+    const int64_t* st = i == 0 ? q_strides : (i == 1 ? k_strides : v_strides);
+    a.ts[i] = p->tokens > 0 ? st[0] : 0;
+    a.hs[i] = p->tokens > 0 ? st[1] : 0;
+  }
+  a.codes[0] = ws + p->ws.q_off;
+  a.codes[1] = ws + p->ws.k_off;
+  a.codes[2] = ws + p->ws.v_off;
+  a.scales = reinterpret_cast<float*>(ws + p->ws.scale_off);
+  a.mu = reinterpret_cast<float*>(ws + p->ws.mu_off);
+  a.kstat = reinterpret_cast<KStat*>(ws + p->ws.kstat_off);
+  a.amax = reinterpret_cast<float*>(ws + p->ws.amax_off);
+  a.segs = p->d_segs;
+  a.chunks = p->d_chunks;
+  a.group_seg = p->d_group_seg;
+  a.heads = p->heads;
+  a.nseg = p->nseg;
+  a.nchunks = (int32_t)p->chunks.size();
+  a.ngroups = (int32_t)p->group_seg.size();
+  a.rows = p->ws.rows;
+  hipError_t e = launch_quantize(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(FP8ATTN_EHIP, std::string("quantize launch failed: ") + hipGetErrorString(e));
+  return FP8ATTN_OK;
+}
+
+fp8attn_status fp8attn_forward(fp8attn_plan_t p, const void* workspace, size_t workspace_bytes,
+                               void* out, const int64_t out_strides[2], float* lse, void* stream) {
+  if (p == nullptr) return fail(FP8ATTN_EINVAL, "plan is NULL");
+  if (p->device < 0) return fail(FP8ATTN_EINVAL, "host-only plan cannot run");
+  if (workspace == nullptr || ((uintptr_t)workspace & 255) != 0)
+    return fail(FP8ATTN_EWORKSPACE, "workspace must be non-NULL and 256-byte aligned");
+  if (workspace_bytes < p->ws.total) return fail(FP8ATTN_EWORKSPACE, "workspace too small");
+  if (p->tokens > 0) {
+    if (out == nullptr) return fail(FP8ATTN_EINVAL, "out must be non-NULL");
+    if (!aligned16(out)) return fail(FP8ATTN_EINVAL, "out must be 16-byte aligned");
+    if (!strides_ok(out_strides)) return fail(FP8ATTN_EINVAL, "out strides must be positive multiples of 8");
+    if (lse != nullptr && ((uintptr_t)lse & 3) != 0) return fail(FP8ATTN_EINVAL, "lse must be 4-byte aligned");
+  }
+  DeviceGuard g(p->device);
+  if (!g.ok) return fail(FP8ATTN_EHIP, "cannot select device");
+  const uint8_t* ws = static_cast<const uint8_t*>(workspace);
+  AttentionArgs a{};
+  a.q_codes = ws + p->ws.q_off;
+  a.k_codes = ws + p->ws.k_off;
+  a.v_codes = ws + p->ws.v_off;
+  a.scales = reinterpret_cast<const float*>(ws + p->ws.scale_off);
+  a.mu = reinterpret_cast<const float*>(ws + p->ws.mu_off);
+  a.segs = p->d_segs;
+  a.items = p->d_items;
+  a.out = static_cast<uint16_t*>(out);
+  a.os0 = p->tokens > 0 ? out_strides[0] : 0;
+  a.os1 = p->tokens > 0 ? out_strides[1] : 0;
+  a.lse = lse;
+  a.tokens = p->tokens;
+  a.rows = p->ws.rows;
+  a.heads = p->heads;
+  a.nitems = p->real_items > 0 ? (int32_t)p->items.size() : 0;
+  a.softmax_scale = p->scale;
+  hipError_t e = launch_attention(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(FP8ATTN_EHIP, std::string("attention launch failed: ") + hipGetErrorString(e));
+  return FP8ATTN_OK;
+}
+
+fp8attn_status fp8attn_workspace_region(fp8attn_plan_t p, const void* workspace, int which,
+                                        const void** ptr_out, int64_t dims_out[3]) {
+  if (p == nullptr || ptr_out == nullptr || dims_out == nullptr) return fail(FP8ATTN_EINVAL, "NULL argument");
+  const uint8_t* ws = static_cast<const uint8_t*>(workspace);
+  const int64_t H = p->heads, R = p->ws.rows, D = kHeadDim;
+  if (which == FP8ATTN_REGION_ROWMAP) {
+    if (p->device < 0) return fail(FP8ATTN_EINVAL, "host-only plan has no device tables");
+    *ptr_out = p->d_rowmap;
+    dims_out[0] = p->nseg; dims_out[1] = 1; dims_out[2] = 1;
+    return FP8ATTN_OK;
+  }
+  if (ws == nullptr) return fail(FP8ATTN_EWORKSPACE, "workspace is NULL");
+  switch (which) {
+    case FP8ATTN_REGION_Q_CODES: *ptr_out = ws + p->ws.q_off; dims_out[0] = H; dims_out[1] = R; dims_out[2] = D; break;
+    case FP8ATTN_REGION_K_CODES: *ptr_out = ws + p->ws.k_off; dims_out[0] = H; dims_out[1] = R; dims_out[2] = D; break;
+    case FP8ATTN_REGION_V_CODES: *ptr_out = ws + p->ws.v_off; dims_out[0] = H; dims_out[1] = D; dims_out[2] = R; break;
+    case FP8ATTN_REGION_SCALES: *ptr_out = ws + p->ws.scale_off; dims_out[0] = 3; dims_out[1] = H; dims_out[2] = 1; break;
+    case FP8ATTN_REGION_MU: *ptr_out = ws + p->ws.mu_off; dims_out[0] = p->nseg; dims_out[1] = H; dims_out[2] = D; break;
+    default: return fail(FP8ATTN_EINVAL, "unknown region");
+  }
+  return FP8ATTN_OK;
+}
+
+fp8attn_status fp8attn_plan_info(fp8attn_plan_t p, int64_t info[8]) {
+  if (p == nullptr || info == nullptr) return fail(FP8ATTN_EINVAL, "NULL argument");
+  info[0] = p->tokens;
+  info[1] = p->heads;
+  info[2] = p->nseg;
+  info[3] = p->ws.rows;
+  info[4] = p->real_items;
+  info[5] = (int64_t)p->chunks.size();
+  info[6] = kBM;
+  info[7] = kBN;
+  return FP8ATTN_OK;
+}
+
+fp8attn_status fp8attn_plan_work_items(fp8attn_plan_t p, int32_t* items_out, int64_t capacity,
+                                       int64_t* count_out) {
+  if (p == nullptr || count_out == nullptr) return fail(FP8ATTN_EINVAL, "NULL argument");
+  if (capacity < 0 || (capacity > 0 && items_out == nullptr)) return fail(FP8ATTN_EINVAL, "bad capacity");
+  const int64_t n = (int64_t)p->items.size();
+  *count_out = n;
+  const int64_t m = std::min(n, capacity);
+  for (int64_t i = 0; i < m; i++) {
+    items_out[4 * i + 0] = p->items[i].x;
+    items_out[4 * i + 1] = p->items[i].y;
+    items_out[4 * i + 2] = p->items[i].z;
+    items_out[4 * i + 3] = p->items[i].w;
+  }
+  return FP8ATTN_OK;
+}
+
+fp8attn_status fp8attn_plan_destroy(fp8attn_plan_t p) {
+  if (p == nullptr) return FP8ATTN_OK;
+  if (p->dev != nullptr) {
+    DeviceGuard g(p->device);
+    (void)hipFree(p->dev);
+  }
+  delete p;
+  return FP8ATTN_OK;
+}
+
+const char* fp8attn_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

@@ -1,0 +1,251 @@
+// Per-head E4M3 quantization of BF16 Q/K/V views into the attention workspace.
+//
+// Two passes over the inputs, as in the fused_prep item of sglang PR
+// "[diffusion] attention: add fp8_fa_sm120 FP8 backend for SM120 GPUs"
+// ("Modifications"): a statistics pass (amax of Q and V; float64 sum, min and
+// max of K per channel) and a pack pass that writes the codes.  A tiny
+// finalize launch in between turns the statistics into per-head scales and
+// per-(segment, head, channel) K means.  K is centred by its segment's
+// per-channel mean (FlashInfer "minimax_h3_sm120_varlen_attention_nvfp4" page,
+// description of the K operand: the mean leaves the softmax unchanged).
+//
+// All three kernels are bound by HBM bandwidth: the stats pass reads 2 B per
+// element, the pack pass reads 2 B and writes 1 B per element.
+#include "internal.h"
+
+namespace fp8attn {
+namespace {
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
+
+// Unpack 8 bf16 values held in a 16-byte vector.
+__device__ __forceinline__ void unpack8(const uint4 v, float f[8]) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    f[2 * i] = __uint_as_float(w[i] << 16);
+    f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+}
+
+// E4M3 codes of 4 floats packed little-endian into one dword.  v_cvt_pk_fp8_f32
+// on gfx950 converts to OCP E4M3 with round-to-nearest-even and keeps
+// subnormals; the quantizer's inputs satisfy |y| <= 448 * (1 + 2^-23), inside
+// the range where it rounds (inputs of 464 and above would become NaN).
+__device__ __forceinline__ uint32_t cvt4(float a, float b, float c, float d) {
+  int r = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  r = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, r, true);
+  return (uint32_t)r;
+}
+
+// ---------------------------------------------------------------------------
+// Pass 1: statistics.  grid = (nchunks, ceil(H/16), 3), block = 256.
+// Thread t handles head 16*blockIdx.y + t/16 and channels 8*(t%16) .. +8 over
+// the chunk's tokens in ascending order.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_stats(QuantizeArgs a) {
+  const int c = blockIdx.x;
+  const int tensor = blockIdx.z;
+  const int t = threadIdx.x;
+  const int h = blockIdx.y * 16 + t / 16;
+  const int c0 = (t % 16) * 8;
+  const bool active = h < a.heads;
+  const Chunk ch = a.chunks[c];
+  const uint16_t* base = a.x[tensor] + (int64_t)h * a.hs[tensor] + c0;
+  const int64_t ts = a.ts[tensor];
+
+  if (tensor == 1) {
+    if (!active) return;
+    double sum[8];
+    float mn[8], mx[8];
+#pragma unroll
+    for (int i = 0; i < 8; i++) { sum[i] = 0.0; mn[i] = __builtin_inff(); mx[i] = -__builtin_inff(); }
+    for (int j = 0; j < ch.ntok; j++) {
+      const uint4 v = *reinterpret_cast<const uint4*>(base + (int64_t)(ch.tok0 + j) * ts);
+      float f[8];
+      unpack8(v, f);
+#pragma unroll
+      for (int i = 0; i < 8; i++) {
+        sum[i] = sum[i] + (double)f[i];
+        mn[i] = fminf(mn[i], f[i]);
+        mx[i] = fmaxf(mx[i], f[i]);
+      }
+    }
+    KStat* out = a.kstat + ((int64_t)c * a.heads + h) * kHeadDim + c0;
+#pragma unroll
+    for (int i = 0; i < 8; i++) out[i] = KStat{sum[i], mn[i], mx[i]};
+    return;
+  }
+
+  float m = 0.f;
+  if (active) {
+    for (int j = 0; j < ch.ntok; j++) {
+      const uint4 v = *reinterpret_cast<const uint4*>(base + (int64_t)(ch.tok0 + j) * ts);
+      float f[8];
+      unpack8(v, f);
+#pragma unroll
+      for (int i = 0; i < 8; i++) m = fmaxf(m, fabsf(f[i]));
+    }
+  }
+  // reduce over the 16 lanes that share a head (they are consecutive lanes of one wave)
+#pragma unroll
+  for (int off = 8; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 16));
+  if (active && (t % 16) == 0) {
+    const int slot = tensor == 0 ? 0 : 1;
+    a.amax[((int64_t)slot * a.nchunks + c) * a.heads + h] = m;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Pass 1b: finalize.  grid = H, block = 128 (thread = channel d).
+// mu[s][h][d] = fl32(sum64 / L) with chunk sums added in ascending order from
+// +0.0; K amax = max over segments and channels of |fl32(max - mu)| and
+// |fl32(min - mu)|, which equals max |fl32(x - mu)| over the tokens because
+// rounding is monotone; s = fl32(amax / 448), or 1 for amax == 0.
+// ---------------------------------------------------------------------------
+__device__ float block_max128(float v, float* red) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
+  const int w = threadIdx.x / 64;
+  __syncthreads();
+  if ((threadIdx.x % 64) == 0) red[w] = v;
+  __syncthreads();
+  return fmaxf(red[0], red[1]);
+}
+
+__device__ __forceinline__ float scale_of(float amax) { return amax > 0.f ? amax / 448.0f : 1.0f; }
+
+__global__ __launch_bounds__(128) void k_finalize(QuantizeArgs a) {
+  __shared__ float red[2];
+  const int h = blockIdx.x;
+  const int d = threadIdx.x;
+  float qa = 0.f, va = 0.f;
+  for (int c = d; c < a.nchunks; c += 128) {
+    qa = fmaxf(qa, a.amax[(int64_t)c * a.heads + h]);
+    va = fmaxf(va, a.amax[((int64_t)a.nchunks + c) * a.heads + h]);
+  }
+  float ka = 0.f;
+  for (int s = 0; s < a.nseg; s++) {
+    const SegInfo si = a.segs[s];
+    float mu = 0.f;
+    if (si.len > 0) {
+      double sum = 0.0;
+      float mn = __builtin_inff(), mx = -__builtin_inff();
+      const int nch = (si.len + kStatChunk - 1) / kStatChunk;
+      for (int c = si.chunk0; c < si.chunk0 + nch; c++) {
+        const KStat st = a.kstat[((int64_t)c * a.heads + h) * kHeadDim + d];
+        sum = sum + st.sum;
+        mn = fminf(mn, st.mn);
+        mx = fmaxf(mx, st.mx);
+      }
+      mu = (float)(sum / (double)si.len);
+      ka = fmaxf(ka, fmaxf(fabsf(mx - mu), fabsf(mn - mu)));
+    }
+    a.mu[((int64_t)s * a.heads + h) * kHeadDim + d] = mu;
+  }
+  qa = block_max128(qa, red);
+  va = block_max128(va, red);
+  ka = block_max128(ka, red);
+  if (d == 0) {
+    a.scales[h] = scale_of(qa);
+    a.scales[a.heads + h] = scale_of(ka);
+    a.scales[2 * a.heads + h] = scale_of(va);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Pass 2: pack.  grid = (ngroups, H, 3), block = 256.  One block writes one
+// 64-row group of one head of one tensor; rows past the segment's end (and the
+// guard rows) are written as zero codes, so every workspace byte the attention
+// kernel can read is defined and finite.
+//
+// Q, K codes: row-major [H][rows][128].  V codes: transposed [H][128][rows]
+// with the keys of each 64-row group permuted so that the attention kernel's
+// probability registers line up with the V operand: byte p = 32j + 16b + 4r + i
+// of a group holds key 32b + 8r + 4j + i.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_pack(QuantizeArgs a) {
+  __shared__ uint8_t tile[kPackRows][kHeadDim + 16];
+  const int g = blockIdx.x;
+  const int h = blockIdx.y;
+  const int tensor = blockIdx.z;
+  const int t = threadIdx.x;
+  const int seg = a.group_seg[g];
+  const int64_t R = (int64_t)g * kPackRows;  // first workspace row of the group
+  SegInfo si{0, 0, 0, 0};
+  if (seg >= 0) si = a.segs[seg];
+  const float s = a.scales[tensor * a.heads + h];
+  const int c0 = (t % 16) * 8;
+  const uint16_t* base = a.x[tensor] + (int64_t)h * a.hs[tensor] + c0;
+  const int64_t ts = a.ts[tensor];
+  float mu[8];
+  if (tensor == 1 && seg >= 0) {
+    const float* m = a.mu + ((int64_t)seg * a.heads + h) * kHeadDim + c0;
+#pragma unroll
+    for (int i = 0; i < 8; i++) mu[i] = m[i];
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; i++) mu[i] = 0.f;
+  }
+
+#pragma unroll
+  for (int pass = 0; pass < kPackRows / 16; pass++) {
+    const int i = pass * 16 + t / 16;                // row within the group
+    const int rel = (int)(R - (seg >= 0 ? si.row0 : 0)) + i;  // segment-relative row
+    uint2 code = make_uint2(0u, 0u);
+    if (seg >= 0 && rel < si.len) {
+      const uint4 v = *reinterpret_cast<const uint4*>(base + (int64_t)(si.start + rel) * ts);
+      float f[8];
+      unpack8(v, f);
+      float y[8];
+#pragma unroll
+      for (int j = 0; j < 8; j++) y[j] = (f[j] - mu[j]) / s;   // K: fl32(x - mu); Q, V: mu = 0
+      code.x = cvt4(y[0], y[1], y[2], y[3]);
+      code.y = cvt4(y[4], y[5], y[6], y[7]);
+    }
+    if (tensor < 2) {
+      uint8_t* dst = a.codes[tensor] + ((int64_t)h * a.rows + R + i) * kHeadDim + c0;
+      *reinterpret_cast<uint2*>(dst) = code;
+    } else {
+      *reinterpret_cast<uint2*>(&tile[i][c0]) = code;
+    }
+  }
+  if (tensor < 2) return;
+  __syncthreads();
+  // transposed, permuted write: thread t -> channel d = t/2, bytes p in [32*(t%2), +32)
+  const int d = t / 2;
+  const int j = t % 2;
+  uint32_t w[8];
+#pragma unroll
+  for (int q = 0; q < 8; q++) {
+    uint32_t acc = 0;
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      const int pp = 4 * q + i;               // byte within this lane's 32: 16b + 4r + i
+      const int b = pp / 16, r = (pp % 16) / 4;
+      const int key = 32 * b + 8 * r + 4 * j + i;
+      acc |= (uint32_t)tile[key][d] << (8 * i);
+    }
+    w[q] = acc;
+  }
+  uint8_t* dst = a.codes[2] + ((int64_t)h * kHeadDim + d) * a.rows + R + 32 * j;
+  *reinterpret_cast<uint4*>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
+  *reinterpret_cast<uint4*>(dst + 16) = make_uint4(w[4], w[5], w[6], w[7]);
+}
+
+}  // namespace
+
+hipError_t launch_quantize(const QuantizeArgs& a, hipStream_t stream) {
+  if (a.nchunks > 0) {
+    hipLaunchKernelGGL(k_stats, dim3(a.nchunks, (a.heads + 15) / 16, 3), dim3(256), 0, stream, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(k_finalize, dim3(a.heads), dim3(128), 0, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_pack, dim3(a.ngroups, a.heads, 3), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace fp8attn

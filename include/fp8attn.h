@@ -1,0 +1,186 @@
+/*
+ * fp8attn.h - C ABI of libfp8attn.so, an FP8 (E4M3) flash-attention forward
+ * for AMD Instinct MI355X (gfx950, CDNA4).
+ *
+ * What is computed (FlashInfer "minimax_h3_sm120_varlen_attention_nvfp4" page,
+ * the formula for out[a:b, h] and the cu_seqlens / softmax_scale parameters):
+ * for every segment [a, b) of cu_seqlens and every head h,
+ *
+ *     out[a:b, h] = softmax(q[a:b, h] @ k[a:b, h]^T * softmax_scale) @ v[a:b, h]
+ *
+ * dense and non-causal, head_dim 128, BF16 in and BF16 out.  The method is the
+ * one of sglang PR "[diffusion] attention: add fp8_fa_sm120 FP8 backend for
+ * SM120 GPUs" ("Modifications"): quantize Q/K/V per head to E4M3 in two passes
+ * (amax, then pack), then one flash-attention forward with E4M3 operands for
+ * both products, FP32 accumulation, an FP32 online softmax and the
+ * probabilities packed to E4M3 in registers; the output is rounded to BF16 once.
+ *
+ * Three calls make one attention:
+ *     fp8attn_plan      (host, once per cu_seqlens/heads; synchronous)
+ *     fp8attn_quantize  (stream-ordered, no host sync)
+ *     fp8attn_forward   (stream-ordered, no host sync)
+ *
+ * Ownership: the caller owns every large device buffer (q, k, v, out, lse and
+ * the workspace).  The library keeps no pointer to any of them after a call
+ * returns.  A plan owns only its host tables and a small device copy of them
+ * (tens to hundreds of KB), freed by fp8attn_plan_destroy.  A plan may be used
+ * from several threads and streams at once provided each concurrent use has
+ * its own workspace.
+ *
+ * Errors: every call returns a status.  Arguments are validated before
+ * anything is enqueued, so a non-OK status means no work was launched.
+ * fp8attn_last_error() returns a text for the last non-OK status of the
+ * calling thread.  A GPU fault inside an enqueued kernel surfaces at the
+ * caller's next synchronization, as for any HIP work.
+ */
+#ifndef FP8ATTN_H
+#define FP8ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FP8ATTN_HEAD_DIM 128
+
+typedef struct fp8attn_plan_s* fp8attn_plan_t;
+
+typedef enum {
+  FP8ATTN_OK = 0,
+  FP8ATTN_EINVAL = 1,        /* bad argument (NULL, size, stride, alignment, cu_seqlens) */
+  FP8ATTN_EUNSUPPORTED = 2,  /* a request outside dense non-causal D=128 BF16 */
+  FP8ATTN_ENOMEM = 3,        /* host or device allocation of plan tables failed */
+  FP8ATTN_EWORKSPACE = 4,    /* workspace pointer NULL/misaligned or smaller than needed */
+  FP8ATTN_EHIP = 5           /* a HIP runtime call or kernel launch failed */
+} fp8attn_status;
+
+/* Workspace regions, for fp8attn_workspace_region(). */
+typedef enum {
+  FP8ATTN_REGION_Q_CODES = 0, /* uint8 [H][rows][128]                                  */
+  FP8ATTN_REGION_K_CODES = 1, /* uint8 [H][rows][128] (centred K)                       */
+  FP8ATTN_REGION_V_CODES = 2, /* uint8 [H][128][rows], keys permuted in 64-key groups  */
+  FP8ATTN_REGION_SCALES = 3,  /* float [3][H]: rows Q, K, V                             */
+  FP8ATTN_REGION_MU = 4,      /* float [num_segments][H][128]: per-channel K means     */
+  FP8ATTN_REGION_ROWMAP = 5   /* plan-owned device int32 [num_segments]: first workspace
+                                 row of each segment (rows are padded per segment)    */
+} fp8attn_region;
+
+/*
+ * fp8attn_plan - validate a segment table and build the work schedule.
+ *
+ *   plan_out         receives the new plan (set to NULL on error).
+ *   tokens           T >= 0, total tokens of the packed batch.
+ *   heads            H >= 1.
+ *   cu_seqlens_host  host int32 array of num_segments + 1 entries: cu[0] == 0,
+ *                    non-decreasing, cu[num_segments] == tokens (FlashInfer page,
+ *                    parameter "cu_seqlens").  Copied; the caller keeps ownership.
+ *                    Empty segments are allowed and produce no work.
+ *   num_segments     >= 1.
+ *   softmax_scale    finite and > 0 (1/sqrt(128) is the usual value).
+ *   device           HIP device ordinal on which the plan will run; the plan's
+ *                    device tables are uploaded there (one synchronous copy).
+ *                    A negative value makes a host-only plan: tables are built
+ *                    and can be inspected, but quantize/forward reject it.
+ *
+ * Workspace rows: each segment occupies round_up(L, 128) rows of the code
+ * regions, segments in order, followed by 128 guard rows; every row past a
+ * segment's end is written as zero codes by fp8attn_quantize.
+ */
+fp8attn_status fp8attn_plan(fp8attn_plan_t* plan_out, int64_t tokens, int32_t heads,
+                            const int32_t* cu_seqlens_host, int32_t num_segments,
+                            float softmax_scale, int32_t device);
+
+/* Bytes of workspace fp8attn_quantize/fp8attn_forward need for this plan (0 on NULL). */
+size_t fp8attn_workspace_bytes(fp8attn_plan_t plan);
+
+/*
+ * fp8attn_quantize - BF16 Q/K/V views -> E4M3 codes + per-head scales in the workspace.
+ *
+ * q, k, v       device pointers to bfloat16 data viewed as [tokens][heads][128]:
+ *               element (t, h, d) is at base[t * strides[0] + h * strides[1] + d]
+ *               (strides in elements, dim stride 1).  Strides must be positive
+ *               multiples of 8 and bases 16-byte aligned.  Views of one fused
+ *               [T][3][H][128] buffer are fine.  Read-only.
+ * workspace     device buffer of at least fp8attn_workspace_bytes(plan) bytes,
+ *               256-byte aligned.  Its prior contents do not matter.
+ * stream        hipStream_t to enqueue on (NULL = default stream).
+ *
+ * Per head h and tensor X in {Q, K, V}: s_X[h] = fl32(amax / 448), or 1.0 when
+ * amax == 0; codes = E4M3(fl32(y / s_X[h])) with round-to-nearest-even,
+ * subnormals kept and the sign copied; y = x for Q and V; for K, y =
+ * fl32(x - mu[seg][h][d]) with mu the segment's per-channel mean, summed in
+ * float64 in 256-token chunks from the segment start (ascending inside a chunk,
+ * then chunk sums ascending) and rounded to float32.  Centring K leaves the
+ * softmax unchanged (FlashInfer page, description of the K mean).
+ * The pass is two-phase (sglang PR, "Modifications", fused_prep: amax, then
+ * pack): three launches (stats, finalize, pack) on `stream`.
+ */
+fp8attn_status fp8attn_quantize(fp8attn_plan_t plan, const void* q, const void* k,
+                                const void* v, const int64_t q_strides[2],
+                                const int64_t k_strides[2], const int64_t v_strides[2],
+                                void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * fp8attn_forward - attention over the codes that the last fp8attn_quantize
+ * into `workspace` wrote (stream order).
+ *
+ * out           device bfloat16 [tokens][heads][128] with element (t, h, d) at
+ *               out[t * out_strides[0] + h * out_strides[1] + d]; strides positive
+ *               multiples of 8, base 16-byte aligned.  Every row of every
+ *               non-empty segment is written.
+ * lse           NULL, or device float [heads][tokens]: natural-log
+ *               log-sum-exp of softmax_scale * q.k over the row's segment
+ *               (uncentred keys).
+ * stream        hipStream_t (NULL = default stream).
+ *
+ * One kernel launch.  Output rows are written exactly once; repeated calls on
+ * the same workspace give bit-identical results.
+ */
+fp8attn_status fp8attn_forward(fp8attn_plan_t plan, const void* workspace, size_t workspace_bytes,
+                               void* out, const int64_t out_strides[2], float* lse, void* stream);
+
+/*
+ * fp8attn_workspace_region - where a region lives (for tests and tools).
+ *
+ * ptr_out    receives a device pointer into `workspace` (or, for
+ *            FP8ATTN_REGION_ROWMAP, into the plan's own device table).
+ * dims_out   int64[3] receives the region's logical dimensions as listed in
+ *            fp8attn_region (unused trailing entries set to 1).
+ *
+ * V code layout: for head h, channel d, 64-key group g of workspace rows
+ * [64g, 64g + 64), byte p = 32*j + 16*b + 4*r + i (j, b in {0,1}; r, i in
+ * 0..3) of the group holds key row 64g + 32*b + 8*r + 4*j + i.
+ */
+fp8attn_status fp8attn_workspace_region(fp8attn_plan_t plan, const void* workspace, int which,
+                                        const void** ptr_out, int64_t dims_out[3]);
+
+/*
+ * fp8attn_plan_info - schedule facts (for tests and tools).
+ *   info_out int64[8]: {tokens, heads, num_segments, workspace_rows,
+ *                       work_items, stat_chunks, query_tile, key_tile}
+ */
+fp8attn_status fp8attn_plan_info(fp8attn_plan_t plan, int64_t info_out[8]);
+
+/*
+ * fp8attn_plan_work_items - copy the ordered work list to host memory.
+ *   items_out int32[4 * capacity]: per item {segment, first query of the tile
+ *   (segment-relative), head, 0}; padding items have segment == -1.
+ *   count_out receives the number of items (which may exceed capacity; only
+ *   min(count, capacity) are copied).
+ */
+fp8attn_status fp8attn_plan_work_items(fp8attn_plan_t plan, int32_t* items_out, int64_t capacity,
+                                       int64_t* count_out);
+
+/* Free a plan (NULL is a no-op).  Work already enqueued with it must be complete. */
+fp8attn_status fp8attn_plan_destroy(fp8attn_plan_t plan);
+
+/* Text of the calling thread's last non-OK status ("" if none).  Valid until the next call. */
+const char* fp8attn_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP8ATTN_H */

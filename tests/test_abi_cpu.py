@@ -1,0 +1,156 @@
+"""CPU checks of the C-ABI library: it loads, exports every declared symbol,
+validates arguments, and builds the documented schedule.  No GPU compute.
+
+Host-only plans (device = -1) exercise the planner without a device.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from fp8_flash_attention_amd import _lib
+import fp8_flash_attention_amd as fa
+from workloads import WORKLOADS
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "fp8attn.h")
+
+
+def _declared():
+    txt = open(HEADER).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(fp8attn_[a-z_]+)\s*\(", txt)))
+
+
+def test_exports_every_declared_symbol():
+    names = _declared()
+    assert len(names) >= 9
+    L = _lib.lib()
+    for n in names:
+        assert hasattr(L, n), n
+        assert n in _lib.SIGNATURES, f"{n} has no ctypes signature"
+
+
+def _plan(tokens, heads, cu, scale=0.088, device=-1):
+    L = _lib.lib()
+    h = ctypes.c_void_p()
+    arr = (ctypes.c_int32 * len(cu))(*cu)
+    st = L.fp8attn_plan(ctypes.byref(h), tokens, heads, arr, len(cu) - 1, ctypes.c_float(scale), device)
+    return st, h
+
+
+@pytest.mark.parametrize("tokens,heads,cu,scale,msg", [
+    (10, 2, [1, 10], 0.1, "cu_seqlens[0]"),
+    (10, 2, [0, 6, 5, 10], 0.1, "non-decreasing"),
+    (10, 2, [0, 9], 0.1, "equal tokens"),
+    (10, 0, [0, 10], 0.1, "heads"),
+    (-1, 2, [0, -1], 0.1, "tokens"),
+    (10, 2, [0, 10], 0.0, "softmax_scale"),
+    (10, 2, [0, 10], float("nan"), "softmax_scale"),
+    (10, 2, [0, 10], float("inf"), "softmax_scale"),
+    (10, 2, [0, 10], -1.0, "softmax_scale"),
+])
+def test_plan_rejects_bad_arguments(tokens, heads, cu, scale, msg):
+    st, h = _plan(tokens, heads, cu, scale)
+    assert st == _lib.EINVAL
+    assert h.value is None
+    assert msg in _lib.lib().fp8attn_last_error().decode()
+
+
+def test_plan_null_arguments():
+    L = _lib.lib()
+    h = ctypes.c_void_p()
+    assert L.fp8attn_plan(None, 1, 1, (ctypes.c_int32 * 2)(0, 1), 1, ctypes.c_float(1.0), -1) == _lib.EINVAL
+    assert L.fp8attn_plan(ctypes.byref(h), 1, 1, None, 1, ctypes.c_float(1.0), -1) == _lib.EINVAL
+    assert L.fp8attn_plan(ctypes.byref(h), 1, 1, (ctypes.c_int32 * 2)(0, 1), 0, ctypes.c_float(1.0), -1) == _lib.EINVAL
+    assert L.fp8attn_workspace_bytes(None) == 0
+    assert L.fp8attn_plan_destroy(None) == _lib.OK
+
+
+def test_host_only_plan_cannot_run():
+    p = fa.Plan(256, 2, [0, 256], device=-1)
+    L = _lib.lib()
+    s = _lib.i64_array([256, 128])
+    st = L.fp8attn_quantize(p.handle, ctypes.c_void_p(16), ctypes.c_void_p(16), ctypes.c_void_p(16), s, s, s,
+                            ctypes.c_void_p(256), p.workspace_bytes, None)
+    assert st == _lib.EINVAL and "host-only" in L.fp8attn_last_error().decode()
+    st = L.fp8attn_forward(p.handle, ctypes.c_void_p(256), p.workspace_bytes, ctypes.c_void_p(16), s, None, None)
+    assert st == _lib.EINVAL
+
+
+def _expected_items(cu, heads, bm=128):
+    segs = [cu[i + 1] - cu[i] for i in range(len(cu) - 1)]
+    return heads * sum((L + bm - 1) // bm for L in segs)
+
+
+@pytest.mark.parametrize("name", list(WORKLOADS))
+def test_schedule_for_each_workload(name):
+    w = WORKLOADS[name]
+    p = fa.Plan(w.tokens, w.heads, w.cu_seqlens, device=-1)
+    info = p.info()
+    assert info["tokens"] == w.tokens and info["heads"] == w.heads
+    assert info["num_segments"] == len(w.cu_seqlens) - 1
+    assert info["query_tile"] == 128
+    segs = w.segments
+    assert info["workspace_rows"] == sum((L + 127) // 128 * 128 for L in segs) + 128
+    assert info["stat_chunks"] == sum((L + 255) // 256 for L in segs)
+    assert info["work_items"] == _expected_items(w.cu_seqlens, w.heads)
+    items = p.work_items()
+    assert len(items) % 8 == 0
+    real = [it for it in items if it[0] >= 0]
+    assert len(real) == info["work_items"]
+    # every (segment, query tile, head) appears exactly once; empty segments never appear
+    want = {(s, q0, h) for h in range(w.heads) for s, L in enumerate(segs) for q0 in range(0, L, 128)}
+    got = [(s, q0, h) for s, q0, h, _ in real]
+    assert len(set(got)) == len(got) and set(got) == want
+    # XCD interleave: workgroup i belongs to XCD i % 8, and each XCD walks a contiguous
+    # run of the head-major list
+    per = len(items) // 8
+    for x in range(8):
+        run = [items[x + 8 * j] for j in range(per)]
+        heads_seen = [it[2] for it in run if it[0] >= 0]
+        assert heads_seen == sorted(heads_seen)
+
+
+def test_varlen_schedule_longest_segment_first():
+    w = WORKLOADS["varlen_30272_h56"]
+    p = fa.Plan(w.tokens, w.heads, w.cu_seqlens, device=-1)
+    items = p.work_items()
+    per = len(items) // 8
+    lin = [items[(j % per) * 8 + j // per] for j in range(len(items))]
+    head0 = [it for it in lin if it[0] >= 0 and it[2] == 0]
+    segs = [it[0] for it in head0]
+    # segment lengths 15104, 15104, 0, 63, 1: the two long ones first, then 63, then 1
+    assert segs[:118] == [0] * 118 and segs[118:236] == [1] * 118 and segs[236:] == [3, 4]
+
+
+def test_empty_input_plan():
+    p = fa.Plan(0, 3, [0, 0], device=-1)
+    info = p.info()
+    assert info["work_items"] == 0 and info["stat_chunks"] == 0
+    assert p.workspace_bytes > 0
+
+
+def test_workspace_region_host_plan():
+    p = fa.Plan(300, 2, [0, 100, 300], device=-1)
+    L = _lib.lib()
+    ptr = ctypes.c_void_p()
+    dims = (ctypes.c_int64 * 3)()
+    base = 1 << 20
+    assert L.fp8attn_workspace_region(p.handle, ctypes.c_void_p(base), _lib.REGION_V, ctypes.byref(ptr), dims) == 0
+    rows = 128 + 256 + 128
+    assert tuple(dims) == (2, 128, rows)
+    assert L.fp8attn_workspace_region(p.handle, ctypes.c_void_p(base), _lib.REGION_MU, ctypes.byref(ptr), dims) == 0
+    assert tuple(dims) == (2, 2, 128)
+    assert L.fp8attn_workspace_region(p.handle, ctypes.c_void_p(base), 99, ctypes.byref(ptr), dims) == _lib.EINVAL
+    assert L.fp8attn_workspace_region(p.handle, ctypes.c_void_p(base), _lib.REGION_ROWMAP,
+                                      ctypes.byref(ptr), dims) == _lib.EINVAL
+
+
+def test_python_wrapper_rejects_unsupported():
+    import torch
+    q = torch.zeros((4, 2, 128), dtype=torch.bfloat16)
+    with pytest.raises(fa.Fp8AttnError):
+        fa.attention(q, q, q, causal=True)
+    with pytest.raises(fa.Fp8AttnError):
+        fa.attention(q.unsqueeze(0), q.unsqueeze(0), q.unsqueeze(0))
