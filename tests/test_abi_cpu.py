@@ -78,7 +78,7 @@ def test_host_only_plan_cannot_run():
     assert st == _lib.EINVAL
 
 
-def _expected_items(cu, heads, bm=128):
+def _expected_items(cu, heads, bm):
     segs = [cu[i + 1] - cu[i] for i in range(len(cu) - 1)]
     return heads * sum((L + bm - 1) // bm for L in segs)
 
@@ -90,17 +90,18 @@ def test_schedule_for_each_workload(name):
     info = p.info()
     assert info["tokens"] == w.tokens and info["heads"] == w.heads
     assert info["num_segments"] == len(w.cu_seqlens) - 1
-    assert info["query_tile"] == 128
+    bm = info["query_tile"]
+    assert bm in (128, 256) and info["key_tile"] == 64
     segs = w.segments
     assert info["workspace_rows"] == sum((L + 127) // 128 * 128 for L in segs) + 128
     assert info["stat_chunks"] == sum((L + 255) // 256 for L in segs)
-    assert info["work_items"] == _expected_items(w.cu_seqlens, w.heads)
+    assert info["work_items"] == _expected_items(w.cu_seqlens, w.heads, bm)
     items = p.work_items()
     assert len(items) % 8 == 0
     real = [it for it in items if it[0] >= 0]
     assert len(real) == info["work_items"]
     # every (segment, query tile, head) appears exactly once; empty segments never appear
-    want = {(s, q0, h) for h in range(w.heads) for s, L in enumerate(segs) for q0 in range(0, L, 128)}
+    want = {(s, q0, h) for h in range(w.heads) for s, L in enumerate(segs) for q0 in range(0, L, bm)}
     got = [(s, q0, h) for s, q0, h, _ in real]
     assert len(set(got)) == len(got) and set(got) == want
     # XCD interleave: workgroup i belongs to XCD i % 8, and each XCD walks a contiguous
@@ -121,7 +122,8 @@ def test_varlen_schedule_longest_segment_first():
     head0 = [it for it in lin if it[0] >= 0 and it[2] == 0]
     segs = [it[0] for it in head0]
     # segment lengths 15104, 15104, 0, 63, 1: the two long ones first, then 63, then 1
-    assert segs[:118] == [0] * 118 and segs[118:236] == [1] * 118 and segs[236:] == [3, 4]
+    n = (15104 + p.info()["query_tile"] - 1) // p.info()["query_tile"]
+    assert segs[:n] == [0] * n and segs[n:2 * n] == [1] * n and segs[2 * n:] == [3, 4]
 
 
 def test_empty_input_plan():
