@@ -20,6 +20,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -34,10 +35,15 @@ COUNTERS_FILE = os.path.join(ROOT, "profiles", "attention_counters.json")
 
 
 def kernel_source_hash() -> str:
+    """sha256 (16 hex) of the attention kernel's code with comments and blank lines
+    removed, so that counters stay attached to the code they were taken on."""
     h = hashlib.sha256()
     for f in ("attention.hip", "internal.h"):
-        with open(os.path.join(ROOT, "fp8_flash_attention_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "fp8_flash_attention_amd", "csrc", f)) as fh:
+            t = fh.read()
+        t = re.sub(r"/\*.*?\*/", "", t, flags=re.S)
+        t = re.sub(r"//[^\n]*", "", t)
+        h.update("\n".join(l.rstrip() for l in t.splitlines() if l.strip()).encode())
     return h.hexdigest()[:16]
 
 
@@ -91,6 +97,9 @@ def main() -> int:
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="after timing, run one plain device copy of BYTES bytes (a known-size "
+                         "reference dispatch for scaling HBM traffic counters)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -144,6 +153,13 @@ def main() -> int:
     value = flops / (ms_step * 1e-3) / 1e12
     fwd_tflops = flops / (ms_fwd * 1e-3) / 1e12
 
+    # MFMA-only skeleton: measured matrix-core ceiling and shader clock
+    from fp8_flash_attention_amd import _lib
+    import ctypes
+    sk_tf, sk_mhz = ctypes.c_double(), ctypes.c_double()
+    sk_rc = _lib.lib().fp8attn_mfma_peak(0, 2000, ctypes.byref(sk_tf), ctypes.byref(sk_mhz))
+    skeleton = {"tflops": round(sk_tf.value, 1), "sclk_mhz": round(sk_mhz.value, 0)} if sk_rc == 0 else None
+
     traffic = measured_traffic(w.name)
     res = {
         "metric": METRIC,
@@ -165,6 +181,8 @@ def main() -> int:
         "forward_tflops": round(fwd_tflops, 2),
         "forward_pct_fp8_peak": round(100.0 * fwd_tflops / FP8_PEAK_TFLOPS, 2),
         "quantize_ms": round(ms_quant, 4),
+        "mfma_skeleton": skeleton,
+        "forward_frac_of_skeleton": round(fwd_tflops / skeleton["tflops"], 4) if skeleton else None,
         "roofline": {
             "kernel": "k_attn (fp8attn_forward)",
             "bound": "mfma",
@@ -173,8 +191,17 @@ def main() -> int:
             "unit": "TFLOP/s",
             "frac": round(fwd_tflops / FP8_PEAK_TFLOPS, 4),
             "traffic": traffic,
+            "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
+            "algorithmic_bytes": 5 * w.tokens * w.heads * 128,
         },
     }
+    if args.copy_calibration > 0:
+        src = torch.ones(args.copy_calibration, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        res["copy_calibration_bytes"] = args.copy_calibration
+        del src, dst
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_budget)
     print(json.dumps(res), flush=True)

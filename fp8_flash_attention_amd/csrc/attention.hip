@@ -8,16 +8,17 @@
 // (FlashInfer "minimax_h3_sm120_varlen_attention_nvfp4" page).
 //
 // gfx950 mapping
-//   * One workgroup = 4 waves = 256 queries of one (segment, head); each wave
-//     owns 64 queries as two blocks of 32.  Two workgroups share a CU, so
-//     every SIMD runs two waves and interleaves one wave's softmax (VALU)
-//     with the other's matrix products (MFMA).  Keys are walked in tiles of 64.
+//   * One workgroup = 4 waves = kBM queries of one (segment, head); each wave
+//     owns kBM/4 queries as kQB blocks of 32 (kBM = 128: one block per wave).
+//     Three workgroups share a CU, so every SIMD runs three waves and
+//     interleaves one wave's softmax (VALU) with another's matrix products
+//     (MFMA).  Keys are walked in tiles of kBN = 64.
 //   * Scores are computed transposed, S^T = K Q^T, with
 //     v_mfma_f32_32x32x64_f8f6f4 (A = 32 keys x 64 channels read from LDS,
 //     B = 32 queries x 64 channels held in registers for the whole loop).
-//     Each A fragment read from LDS feeds the MFMAs of both query blocks,
-//     which halves the LDS read traffic per MFMA (LDS bandwidth, ~160 B/clk
-//     per CU, would otherwise bound the loop).
+//     With kQB = 2 each A fragment read from LDS would feed the MFMAs of both
+//     query blocks; at kQB = 1 the LDS reads (~160 B/clk per CU) still stay
+//     below the MFMA time and the smaller register file buys the third wave.
 //   * In the 32x32 accumulator layout lane l holds query l%32 and 16 keys of
 //     a 32-key block, so the row max and row sum are in-lane plus one
 //     exchange between lanes l and l^32 (v_permlane32_swap).
@@ -55,7 +56,7 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLog2Ref = 6.807354922057604f;   // log2(112): reference maximum maps to 448 / 4
-constexpr float kSlack = 2.0f;                   // log2 headroom between 112 and 448
+constexpr float kLog2Max = 8.807354922057604f;   // log2(448), the largest E4M3 value
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kQB = kBM / (4 * 32);              // 32-query blocks per wave
 constexpr int kQW = 32 * kQB;                    // queries per wave
@@ -63,6 +64,7 @@ static_assert(kQB == 1 || kQB == 2, "4 waves x 32 or 64 queries");
 constexpr int kKTile = kBN * kHeadDim;           // bytes of one K (or V) tile
 constexpr int kStage = 2 * kKTile;               // K tile + V tile
 constexpr int kStages = 3;
+constexpr int kBufferFlags = 0x00020000;         // raw buffer descriptor word 3 (gfx9 family)
 
 __device__ __forceinline__ v16f mfma_fp8(const v8i& a, const v8i& b, const v16f& c) {
   // cbsz = blgp = 0 selects E4M3 for both operands; zero scales select the
@@ -70,11 +72,26 @@ __device__ __forceinline__ v16f mfma_fp8(const v8i& a, const v8i& b, const v16f&
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
 
-// Value from lane l^32 of x.
-__device__ __forceinline__ float swap32(float x) {
+// max / sum of x over lanes l and l^32.  v_permlane32_swap on (x, x) leaves
+// {x[l], x[l^32]} in its two results (in an order that depends on the lane
+// half), so combining both results needs no lane select.
+__device__ __forceinline__ float max_pair32(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  const int lane = threadIdx.x & 63;
-  return __uint_as_float(lane < 32 ? r[1] : r[0]);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_pair32(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// max of the 16 values of one accumulator block as a v_max3 tree
+__device__ __forceinline__ float max16(const v16f& s) {
+  const float a = fmaxf(fmaxf(s[0], s[1]), s[2]);
+  const float b = fmaxf(fmaxf(s[3], s[4]), s[5]);
+  const float c = fmaxf(fmaxf(s[6], s[7]), s[8]);
+  const float d = fmaxf(fmaxf(s[9], s[10]), s[11]);
+  const float e = fmaxf(fmaxf(s[12], s[13]), s[14]);
+  return fmaxf(fmaxf(fmaxf(a, b), c), fmaxf(fmaxf(d, e), s[15]));
 }
 
 __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
@@ -82,8 +99,10 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
   return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
 }
 
+// E4M3 codes of four floats in one dword.  Both halves are written, so the
+// first conversion's merge operand is left undefined (no register to clear).
 __device__ __forceinline__ int cvt4(float a, float b, float c, float d) {
-  int r = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  int r = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, __builtin_nondeterministic_value(0), false);
   return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, r, true);
 }
 
@@ -124,7 +143,6 @@ __global__ __launch_bounds__(256, kQB == 1 ? 3 : 2) void k_attn(AttentionArgs a)
   const float s_k = a.scales[a.heads + h];
   const float s_v = a.scales[2 * a.heads + h];
   const float c = a.softmax_scale * s_q * s_k * kLog2e;
-  const float thr = kSlack / c;   // raw-score headroom before p could pass 448
 
   // Q as B operands: block qb holds queries q0 + 64*wave + 32*qb + (lane%32),
   // channels 64*half + 32*(lane/32) .. +32.  Rows past the segment end read
@@ -148,39 +166,45 @@ __global__ __launch_bounds__(256, kQB == 1 ? 3 : 2) void k_attn(AttentionArgs a)
   for (int sub = 0; sub < 2; sub++) voff[sub] = v_lds_off(lq, 2 * lg + sub);
 
   // Copy geometry: thread t moves 16-byte chunks t and t+256 of the K tile
-  // (64 rows x 8 chunks) and of the V^T tile (128 rows x 4 chunks).
-  uint32_t ksrc[2], vsrc[2];   // per-lane byte offsets from the tile base
-  int kdst[2], vdst[2];        // per-lane LDS offsets inside a stage
+  // (64 rows x 8 chunks) and of the V^T tile (128 rows x 4 chunks).  Loads go
+  // through buffer descriptors of this head's K and V^T regions: the lane
+  // offset is a 32-bit register, the tile offset a scalar, so no vector
+  // address arithmetic runs per tile.
+  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)Kh, (short)0, (int)((a.rows - si.row0) * kHeadDim), kBufferFlags);
+  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)Vh, (short)0, (int)(a.rows * kHeadDim - si.row0), kBufferFlags);
+  int ksrc[2], vsrc[2];   // per-lane byte offsets inside a tile
+  int kdst[2], vdst[2];   // per-lane LDS offsets inside a stage
 #pragma unroll
   for (int u = 0; u < 2; u++) {
     const int ci = tid + 256 * u;
-    ksrc[u] = (uint32_t)((ci >> 3) * kHeadDim + (ci & 7) * 16);
+    ksrc[u] = (ci >> 3) * kHeadDim + (ci & 7) * 16;
     kdst[u] = k_lds_off(ci >> 3, ci & 7);
-    vsrc[u] = (uint32_t)((ci >> 2) * a.rows + (ci & 3) * 16);
+    vsrc[u] = (ci >> 2) * (int)a.rows + (ci & 3) * 16;
     vdst[u] = v_lds_off(ci >> 2, ci & 3);
   }
   const int nkt = (L + kBN - 1) / kBN;
-  uint4 stg0, stg1;   // two staged 16-byte chunks (separate variables keep them in registers)
+  u32x4 stg0, stg1;   // two staged 16-byte chunks (separate variables keep them in registers)
   // clamped tile index: always a valid tile of this segment
   auto fetch_k = [&](int kt) __attribute__((always_inline)) {
     kt = kt < nkt ? kt : nkt - 1;
-    const uint8_t* base = Kh + (size_t)kt * kBN * kHeadDim;
-    stg0 = *reinterpret_cast<const uint4*>(base + ksrc[0]);
-    stg1 = *reinterpret_cast<const uint4*>(base + ksrc[1]);
+    stg0 = __builtin_amdgcn_raw_buffer_load_b128(krs, ksrc[0], kt * kBN * kHeadDim, 0);
+    stg1 = __builtin_amdgcn_raw_buffer_load_b128(krs, ksrc[1], kt * kBN * kHeadDim, 0);
   };
   auto fetch_v = [&](int kt) __attribute__((always_inline)) {
     kt = kt < nkt ? kt : nkt - 1;
-    const uint8_t* base = Vh + (size_t)kt * kBN;
-    stg0 = *reinterpret_cast<const uint4*>(base + vsrc[0]);
-    stg1 = *reinterpret_cast<const uint4*>(base + vsrc[1]);
+    stg0 = __builtin_amdgcn_raw_buffer_load_b128(vrs, vsrc[0], kt * kBN, 0);
+    stg1 = __builtin_amdgcn_raw_buffer_load_b128(vrs, vsrc[1], kt * kBN, 0);
   };
   auto put_k = [&](uint8_t* stage) __attribute__((always_inline)) {
-    *reinterpret_cast<uint4*>(stage + kdst[0]) = stg0;
-    *reinterpret_cast<uint4*>(stage + kdst[1]) = stg1;
+    *reinterpret_cast<u32x4*>(stage + kdst[0]) = stg0;
+    *reinterpret_cast<u32x4*>(stage + kdst[1]) = stg1;
   };
   auto put_v = [&](uint8_t* stage) __attribute__((always_inline)) {
-    *reinterpret_cast<uint4*>(stage + vdst[0]) = stg0;
-    *reinterpret_cast<uint4*>(stage + vdst[1]) = stg1;
+    *reinterpret_cast<u32x4*>(stage + vdst[0]) = stg0;
+    *reinterpret_cast<u32x4*>(stage + vdst[1]) = stg1;
   };
 
   // q_hat . mu per query, for the natural-log LSE of the uncentred scores:
@@ -204,32 +228,52 @@ __global__ __launch_bounds__(256, kQB == 1 ? 3 : 2) void k_attn(AttentionArgs a)
           dot += __builtin_amdgcn_cvt_f32_fp8(qf[qb][half][w], 2) * md[2];
           dot += __builtin_amdgcn_cvt_f32_fp8(qf[qb][half][w], 3) * md[3];
         }
-      qmu[qb] = dot + swap32(dot);
+      qmu[qb] = sum_pair32(dot);
     }
   }
 
   v16f O[kQB][4];
-  float m[kQB], l[kQB];   // reference max (raw score units); partial row sums (this lane's keys)
+  float nb[kQB];   // exp2 argument offset: x = c*s + nb, i.e. nb = log2(112) - c*m
+  float l[kQB];    // partial row sums (this lane's keys)
+  v8i P[kQB];      // packed probabilities; kept across tiles so packing needs no cleared register
 #pragma unroll
   for (int qb = 0; qb < kQB; qb++) {
 #pragma unroll
     for (int db = 0; db < 4; db++) O[qb][db] = v16f{};
-    m[qb] = -__builtin_inff();
     l[qb] = 0.f;
+    P[qb] = v8i{};
   }
+
+  // 32x32 score block S^T = K Q^T for key block kb of the tile in `sb`.
+  auto scores = [&](const uint8_t* sb, int kb, int qb) __attribute__((always_inline)) {
+    const v8i k0 = lds_read32(sb + kb * 32 * 128, koff[0][0], koff[0][1]);
+    const v8i k1 = lds_read32(sb + kb * 32 * 128, koff[1][0], koff[1][1]);
+    return mfma_fp8(k1, qf[qb][1], mfma_fp8(k0, qf[qb][0], v16f{}));
+  };
+  // keys at or past the segment end -> -inf.  Register r of lane l holds key
+  // kbase + 32*kb + 8*(r/4) + 4*(l/32) + r%4.
+  auto mask = [&](v16f& S, int kbase, int kb) __attribute__((always_inline)) {
+    const int lim = L - kbase - 32 * kb - 4 * lg;
+#pragma unroll
+    for (int r = 0; r < 16; r++)
+      if (8 * (r >> 2) + (r & 3) >= lim) S[r] = -__builtin_inff();
+  };
 
   // One 64-key tile from LDS stage `sb`.  Main-loop tiles (MASKED false)
   // fetch tile kt+2 into stage `nxt` along the way; the last tile (MASKED
-  // true) fetches nothing and sets keys at or past the segment end to -inf.
+  // true) fetches nothing and masks keys at or past the segment end.
+  //
+  // Per 32x32 block: x = c*s + nb are the exp2 arguments; p = 2^x <= 448 as
+  // long as max x <= log2(448).  Otherwise (rare) the reference moves so that
+  // the block maximum maps to 112: x, nb shift by log2(112) - max x, and O, l
+  // (and the tile's already packed first block) scale by 2^shift.  The max is
+  // taken over x, FMA results, which need no NaN canonicalization.
   auto tile = [&](const uint8_t* sb, int kt, uint8_t* nxt, auto masked_c) __attribute__((always_inline)) {
     constexpr bool MASKED = decltype(masked_c)::value;
     constexpr bool PREFETCH = !MASKED;
     const int kbase = kt * kBN;
-    v8i P[kQB];
 #pragma unroll
     for (int kb = 0; kb < 2; kb++) {
-      const v8i k0 = lds_read32(sb + kb * 32 * 128, koff[0][0], koff[0][1]);
-      const v8i k1 = lds_read32(sb + kb * 32 * 128, koff[1][0], koff[1][1]);
       if (PREFETCH) {
         if (kb == 0) fetch_k(kt + 2);
         else {
@@ -239,45 +283,47 @@ __global__ __launch_bounds__(256, kQB == 1 ? 3 : 2) void k_attn(AttentionArgs a)
       }
 #pragma unroll
       for (int qb = 0; qb < kQB; qb++) {
-        v16f S = mfma_fp8(k0, qf[qb][0], v16f{});
-        S = mfma_fp8(k1, qf[qb][1], S);
-        if (MASKED) {
-          // key of register r: kbase + 32*kb + 8*(r/4) + 4*(lane/32) + r%4
-          const int lim = L - kbase - 32 * kb - 4 * lg;
+        v16f S = scores(sb, kb, qb);
+        if (MASKED) mask(S, kbase, kb);
+        float x[16];
 #pragma unroll
-          for (int r = 0; r < 16; r++)
-            if (8 * (r >> 2) + (r & 3) >= lim) S[r] = -__builtin_inff();
-        }
-        float t = fmaxf(S[0], S[1]);
-#pragma unroll
-        for (int r = 2; r < 16; r++) t = fmaxf(t, S[r]);
-        t = fmaxf(t, swap32(t));
-        if (__ballot(t > m[qb] + thr)) {
-          const float mn = fmaxf(m[qb], t);
-          const float alpha = __builtin_amdgcn_exp2f(c * (m[qb] - mn));
+        for (int r = 0; r < 16; r++) x[r] = __builtin_fmaf(S[r], c, nb[qb]);
+        // v_max3 tree: 5 + 2 + 1 instructions
+        const float m0 = fmaxf(fmaxf(x[0], x[1]), x[2]), m1 = fmaxf(fmaxf(x[3], x[4]), x[5]);
+        const float m2 = fmaxf(fmaxf(x[6], x[7]), x[8]), m3 = fmaxf(fmaxf(x[9], x[10]), x[11]);
+        const float m4 = fmaxf(fmaxf(x[12], x[13]), x[14]);
+        const float tb = fmaxf(fmaxf(fmaxf(m0, m1), m2), fmaxf(fmaxf(m3, m4), x[15]));
+        auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(tb), __float_as_uint(tb), false, false);
+        const float t0 = __uint_as_float(pr[0]), t1 = __uint_as_float(pr[1]);
+        if (__ballot(t0 > kLog2Max || t1 > kLog2Max)) {
+          const float tm = fmaxf(t0, t1);
+          const float shift = tm > kLog2Max ? kLog2Ref - tm : 0.f;
+          const float alpha = __builtin_amdgcn_exp2f(shift);
           if (kb == 1) {
             // the first key block's probabilities were packed against the old
             // reference: re-encode them scaled by alpha
 #pragma unroll
             for (int w = 0; w < 4; w++) {
-              const int x = P[qb][w];
-              P[qb][w] = cvt4(__builtin_amdgcn_cvt_f32_fp8(x, 0) * alpha, __builtin_amdgcn_cvt_f32_fp8(x, 1) * alpha,
-                              __builtin_amdgcn_cvt_f32_fp8(x, 2) * alpha, __builtin_amdgcn_cvt_f32_fp8(x, 3) * alpha);
+              const int v = P[qb][w];
+              P[qb][w] = cvt4(__builtin_amdgcn_cvt_f32_fp8(v, 0) * alpha, __builtin_amdgcn_cvt_f32_fp8(v, 1) * alpha,
+                              __builtin_amdgcn_cvt_f32_fp8(v, 2) * alpha, __builtin_amdgcn_cvt_f32_fp8(v, 3) * alpha);
             }
           }
           l[qb] *= alpha;
 #pragma unroll
           for (int db = 0; db < 4; db++) O[qb][db] *= alpha;
-          m[qb] = mn;
+          nb[qb] += shift;
+#pragma unroll
+          for (int r = 0; r < 16; r++) x[r] += shift;
         }
-        const float nb = kLog2Ref - c * m[qb];
 #pragma unroll
         for (int q4 = 0; q4 < 4; q4++) {
           float p[4];
 #pragma unroll
-          for (int i = 0; i < 4; i++) p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[4 * q4 + i], c, nb));
+          for (int i = 0; i < 4; i++) p[i] = __builtin_amdgcn_exp2f(x[4 * q4 + i]);
           l[qb] += (p[0] + p[1]) + (p[2] + p[3]);
-          P[qb][4 * kb + q4] = cvt4(p[0], p[1], p[2], p[3]);
+          int w = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], P[qb][4 * kb + q4], false);
+          P[qb][4 * kb + q4] = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], w, true);
         }
       }
     }
@@ -303,6 +349,20 @@ __global__ __launch_bounds__(256, kQB == 1 ? 3 : 2) void k_attn(AttentionArgs a)
   put_k(stage0 + kStage);
   fetch_v(1);
   put_v(stage0 + kStage);
+  // Initial reference: the maximum score of the first key block of tile 0
+  // (masked when the segment is shorter than the block), mapped to 112.
+  __syncthreads();
+#pragma unroll
+  for (int qb = 0; qb < kQB; qb++) {
+    v16f S = scores(stage0, 0, qb);
+    if (L < 32) mask(S, 0, 0);
+    float t = S[0];
+#pragma unroll
+    for (int r = 1; r < 16; r++) t = fmaxf(t, S[r]);
+    auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(t), __float_as_uint(t), false, false);
+    t = fmaxf(__uint_as_float(pr[0]), __uint_as_float(pr[1]));
+    nb[qb] = kLog2Ref - c * t;
+  }
   auto step = [&](auto stage_c, int kt) __attribute__((always_inline)) {
     constexpr int ST = decltype(stage_c)::value;
     __syncthreads();              // tile kt is in stage ST; stage (ST+2)%3 is free
@@ -330,7 +390,7 @@ __global__ __launch_bounds__(256, kQB == 1 ? 3 : 2) void k_attn(AttentionArgs a)
 #pragma unroll
   for (int qb = 0; qb < kQB; qb++) {
     const int qrow = q0 + kQW * wave + 32 * qb + lq;
-    const float lt = l[qb] + swap32(l[qb]);
+    const float lt = sum_pair32(l[qb]);
     if (qrow < L) {
       const float inv = s_v / lt;
       uint16_t* orow = a.out + (int64_t)(si.start + qrow) * a.os0 + (int64_t)h * a.os1;
@@ -347,7 +407,7 @@ __global__ __launch_bounds__(256, kQB == 1 ? 3 : 2) void k_attn(AttentionArgs a)
         }
     }
     if (a.lse != nullptr && lg == 0 && qrow < L) {
-      const float lse2 = c * m[qb] + __log2f(lt) - kLog2Ref;
+      const float lse2 = __log2f(lt) - nb[qb];
       a.lse[(int64_t)h * a.tokens + si.start + qrow] = lse2 * kLn2 + a.softmax_scale * s_q * qmu[qb];
     }
   }

@@ -13,13 +13,16 @@ from fp8_flash_attention_amd import _lib
 import fp8_flash_attention_amd as fa
 from workloads import WORKLOADS
 
-HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "fp8attn.h")
+INCLUDE = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include")
 
 
 def _declared():
-    txt = open(HEADER).read()
-    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
-    return sorted(set(re.findall(r"\b(fp8attn_[a-z_]+)\s*\(", txt)))
+    names = set()
+    for h in sorted(os.listdir(INCLUDE)):
+        if h.endswith(".h"):
+            txt = re.sub(r"/\*.*?\*/", "", open(os.path.join(INCLUDE, h)).read(), flags=re.S)
+            names |= set(re.findall(r"\b(fp8attn_[a-z_]+)\s*\(", txt))
+    return sorted(names)
 
 
 def test_exports_every_declared_symbol():

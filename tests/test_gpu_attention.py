@@ -202,7 +202,8 @@ def test_lse_matches_oracle():
     plan, ws, out, lse = _gpu_attention(w, q.cuda(), k.cuda(), v.cuda(), lse=True)
     got = lse.cpu().double().numpy()
     # against the LSE of the dequantized operands (centred keys plus their segment mean):
-    # only accumulation order and the FP32 softmax remain
+    # the kernel sums the FP32 probabilities, so only accumulation order and the FP32
+    # exponentials remain
     r = Qz.quantize(q, k, v, cu)
     dq = Qz.dequantize(r["q_codes"], r["scales"][0])
     dk = Qz.dequantize(r["k_codes"], r["scales"][1])
