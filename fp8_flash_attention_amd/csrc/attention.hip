@@ -20,13 +20,20 @@
 //     query blocks; at kQB = 1 the LDS reads (~160 B/clk per CU) still stay
 //     below the MFMA time and the smaller register file buys the third wave.
 //   * In the 32x32 accumulator layout lane l holds query l%32 and 16 keys of
-//     a 32-key block, so the row max and row sum are in-lane plus one
-//     exchange between lanes l and l^32 (v_permlane32_swap).
+//     a 32-key block, so the row max is in-lane plus one exchange between
+//     lanes l and l^32 (v_permlane32_swap).
 //   * The accumulators of two 32-key blocks, converted to E4M3 with
 //     v_cvt_pk_fp8_f32, are exactly the B operand (64 keys x 32 queries) of
 //     O^T += V^T P^T.  The key order this implies inside a 64-key group is
 //     baked into the workspace V layout by the pack pass, so the P registers
 //     never leave the lane.
+//   * Row sums l come from the matrix core too: one
+//     v_mfma_f32_16x16x128_f8f6f4 per tile multiplies the packed P^T by a
+//     constant 0/1 selector, which adds the 64 key bytes of query j (lanes j
+//     and j+32) into row 0 and those of query 16+j (lanes j+16 and j+48) into
+//     row 1.  l is the sum of the E4M3 probabilities that actually weight V,
+//     and no vector adds are spent on it.  When the caller asks for the LSE,
+//     an FP32 sum of the unrounded probabilities is kept as well.
 //   * Probabilities: p = exp2(c*s - (c*m - log2 112)) with
 //     c = softmax_scale * s_q * s_k * log2(e) and m a per-query reference
 //     maximum.  m is only moved (and O, l rescaled) when a 32-key block holds
@@ -35,8 +42,7 @@
 //     the rescale runs only on the rare blocks where a maximum grows by more
 //     than a factor 4.  If that happens in the second key block of a tile,
 //     the first block's probabilities (already packed against the old m) are
-//     first added into O with an MFMA whose other half of P is zero.  The row
-//     sum l accumulates the FP32 p; the final O = acc * s_v / l.
+//     re-encoded scaled by the same factor.  The final O = acc * s_v / l.
 //   * K/V tiles go through three LDS stages: while tile j is consumed, tile
 //     j+2 is fetched into registers in two halves (its K part during the first
 //     key block, its V part during the second) and written to its stage after
@@ -53,6 +59,7 @@ namespace {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
+typedef float v4f __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLog2Ref = 6.807354922057604f;   // log2(112): reference maximum maps to 448 / 4
@@ -119,6 +126,11 @@ __device__ __forceinline__ v8i lds_read32(const uint8_t* base, int off_lo, int o
 __device__ __forceinline__ int k_lds_off(int row, int chunk) { return row * 128 + ((chunk ^ ((row >> 1) & 7)) << 4); }
 __device__ __forceinline__ int v_lds_off(int d, int chunk) { return kKTile + d * 64 + ((chunk ^ ((d >> 2) & 3)) << 4); }
 
+__device__ __forceinline__ v4f mfma16_fp8(const v8i& a, const v8i& b, const v4f& c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+template <bool EXACT_SUM>
 __global__ __launch_bounds__(256, kQB == 1 ? 3 : 2) void k_attn(AttentionArgs a) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kStages * kStage];
 
@@ -213,7 +225,7 @@ __global__ __launch_bounds__(256, kQB == 1 ? 3 : 2) void k_attn(AttentionArgs a)
   float qmu[kQB];
 #pragma unroll
   for (int qb = 0; qb < kQB; qb++) qmu[qb] = 0.f;
-  if (a.lse != nullptr) {
+  if (EXACT_SUM) {
     const float* mu = a.mu + ((size_t)it.x * a.heads + h) * kHeadDim;
 #pragma unroll
     for (int qb = 0; qb < kQB; qb++) {
@@ -232,6 +244,13 @@ __global__ __launch_bounds__(256, kQB == 1 ? 3 : 2) void k_attn(AttentionArgs a)
     }
   }
 
+  // Row-sum selector for the 16x16x128 product: E4M3 1.0 in every byte of
+  // lanes 0 and 32 (row 0: lanes j and j+32 of P, query j) and lanes 17 and
+  // 49 (row 1: lanes 16+j and 48+j, query 16+j), zero elsewhere.
+  const int one = (lane == 0 || lane == 32 || lane == 17 || lane == 49) ? 0x38383838 : 0;
+  const v8i sel = v8i{one, one, one, one, one, one, one, one};
+  v4f lacc[kQB];   // row sums of the packed P: lane j < 16 holds query j (row 0) and 16+j (row 1)
+
   v16f O[kQB][4];
   float nb[kQB];   // exp2 argument offset: x = c*s + nb, i.e. nb = log2(112) - c*m
   float l[kQB];    // partial row sums (this lane's keys)
@@ -241,6 +260,7 @@ __global__ __launch_bounds__(256, kQB == 1 ? 3 : 2) void k_attn(AttentionArgs a)
 #pragma unroll
     for (int db = 0; db < 4; db++) O[qb][db] = v16f{};
     l[qb] = 0.f;
+    lacc[qb] = v4f{};
     P[qb] = v8i{};
   }
 
@@ -309,7 +329,12 @@ __global__ __launch_bounds__(256, kQB == 1 ? 3 : 2) void k_attn(AttentionArgs a)
                               __builtin_amdgcn_cvt_f32_fp8(v, 2) * alpha, __builtin_amdgcn_cvt_f32_fp8(v, 3) * alpha);
             }
           }
-          l[qb] *= alpha;
+          if (EXACT_SUM) l[qb] *= alpha;
+          {
+            auto pa = __builtin_amdgcn_permlane16_swap(__float_as_uint(alpha), __float_as_uint(alpha), false, false);
+            lacc[qb][0] *= alpha;
+            lacc[qb][1] *= __uint_as_float(pa[1]);   // lane j < 16: alpha of query 16+j
+          }
 #pragma unroll
           for (int db = 0; db < 4; db++) O[qb][db] *= alpha;
           nb[qb] += shift;
@@ -321,7 +346,7 @@ __global__ __launch_bounds__(256, kQB == 1 ? 3 : 2) void k_attn(AttentionArgs a)
           float p[4];
 #pragma unroll
           for (int i = 0; i < 4; i++) p[i] = __builtin_amdgcn_exp2f(x[4 * q4 + i]);
-          l[qb] += (p[0] + p[1]) + (p[2] + p[3]);
+          if (EXACT_SUM) l[qb] += (p[0] + p[1]) + (p[2] + p[3]);
           int w = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], P[qb][4 * kb + q4], false);
           P[qb][4 * kb + q4] = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], w, true);
         }
@@ -334,6 +359,8 @@ __global__ __launch_bounds__(256, kQB == 1 ? 3 : 2) void k_attn(AttentionArgs a)
 #pragma unroll
       for (int qb = 0; qb < kQB; qb++) O[qb][db] = mfma_fp8(vf, P[qb], O[qb][db]);
     }
+#pragma unroll
+    for (int qb = 0; qb < kQB; qb++) lacc[qb] = mfma16_fp8(sel, P[qb], lacc[qb]);
     if (PREFETCH) put_v(nxt);
   };
 
@@ -390,7 +417,10 @@ __global__ __launch_bounds__(256, kQB == 1 ? 3 : 2) void k_attn(AttentionArgs a)
 #pragma unroll
   for (int qb = 0; qb < kQB; qb++) {
     const int qrow = q0 + kQW * wave + 32 * qb + lq;
-    const float lt = sum_pair32(l[qb]);
+    // row sum of the E4M3 probabilities (the weights actually applied to V)
+    const float l0 = __shfl(lacc[qb][0], lq & 15);
+    const float l1 = __shfl(lacc[qb][1], lq & 15);
+    const float lt = lq < 16 ? l0 : l1;
     if (qrow < L) {
       const float inv = s_v / lt;
       uint16_t* orow = a.out + (int64_t)(si.start + qrow) * a.os0 + (int64_t)h * a.os1;
@@ -406,9 +436,12 @@ __global__ __launch_bounds__(256, kQB == 1 ? 3 : 2) void k_attn(AttentionArgs a)
           *reinterpret_cast<uint2*>(orow + d) = make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
         }
     }
-    if (a.lse != nullptr && lg == 0 && qrow < L) {
-      const float lse2 = __log2f(lt) - nb[qb];
+    if (EXACT_SUM) {
+      const float le = sum_pair32(l[qb]);
+      if (lg == 0 && qrow < L) {
+      const float lse2 = __log2f(le) - nb[qb];
       a.lse[(int64_t)h * a.tokens + si.start + qrow] = lse2 * kLn2 + a.softmax_scale * s_q * qmu[qb];
+      }
     }
   }
 }
@@ -417,7 +450,10 @@ __global__ __launch_bounds__(256, kQB == 1 ? 3 : 2) void k_attn(AttentionArgs a)
 
 hipError_t launch_attention(const AttentionArgs& a, hipStream_t stream) {
   if (a.nitems == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_attn, dim3(a.nitems), dim3(256), 0, stream, a);
+  if (a.lse != nullptr)
+    hipLaunchKernelGGL(k_attn<true>, dim3(a.nitems), dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL(k_attn<false>, dim3(a.nitems), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
