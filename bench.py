@@ -153,12 +153,19 @@ def main() -> int:
     value = flops / (ms_step * 1e-3) / 1e12
     fwd_tflops = flops / (ms_fwd * 1e-3) / 1e12
 
-    # MFMA-only skeleton: measured matrix-core ceiling and shader clock
+    # MFMA-only skeletons: measured matrix-core ceilings and shader clocks, with a
+    # fixed operand pattern (short run) and with rotating random E4M3 operands long
+    # enough (~30 ms) for the clock to settle where random data holds it
     from fp8_flash_attention_amd import _lib
     import ctypes
-    sk_tf, sk_mhz = ctypes.c_double(), ctypes.c_double()
-    sk_rc = _lib.lib().fp8attn_mfma_peak(0, 2000, ctypes.byref(sk_tf), ctypes.byref(sk_mhz))
-    skeleton = {"tflops": round(sk_tf.value, 1), "sclk_mhz": round(sk_mhz.value, 0)} if sk_rc == 0 else None
+
+    def skeleton_run(iters, random_operands):
+        tf, mhz = ctypes.c_double(), ctypes.c_double()
+        rc = _lib.lib().fp8attn_mfma_peak(0, iters, random_operands, ctypes.byref(tf), ctypes.byref(mhz))
+        return {"tflops": round(tf.value, 1), "sclk_mhz": round(mhz.value, 0)} if rc == 0 else None
+
+    skeleton = skeleton_run(2000, 0)
+    skeleton_random = skeleton_run(100000, 1)
 
     traffic = measured_traffic(w.name)
     res = {
@@ -182,7 +189,10 @@ def main() -> int:
         "forward_pct_fp8_peak": round(100.0 * fwd_tflops / FP8_PEAK_TFLOPS, 2),
         "quantize_ms": round(ms_quant, 4),
         "mfma_skeleton": skeleton,
+        "mfma_skeleton_random_operands": skeleton_random,
         "forward_frac_of_skeleton": round(fwd_tflops / skeleton["tflops"], 4) if skeleton else None,
+        "forward_frac_of_random_skeleton": (round(fwd_tflops / skeleton_random["tflops"], 4)
+                                            if skeleton_random else None),
         "roofline": {
             "kernel": "k_attn (fp8attn_forward)",
             "bound": "mfma",

@@ -35,7 +35,7 @@ SIGNATURES = {
     "fp8attn_plan_destroy": (ctypes.c_int, [ctypes.c_void_p]),
     "fp8attn_last_error": (ctypes.c_char_p, []),
     # include/fp8attn_bench.h
-    "fp8attn_mfma_peak": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_double),
+    "fp8attn_mfma_peak": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_double),
                                          ctypes.POINTER(ctypes.c_double)]),
 }
 

@@ -8,9 +8,10 @@
 // (FlashInfer "minimax_h3_sm120_varlen_attention_nvfp4" page).
 //
 // gfx950 mapping
-//   * One workgroup = 4 waves = kBM = 128 queries of one (segment, head); each
-//     wave owns 32 queries.  Two workgroups share a CU, so every SIMD runs two
-//     waves (up to 256 registers each).  Keys are walked in tiles of kBN = 64.
+//   * One workgroup = kBM/32 waves (4 for kBM = 128) of 32 queries each, all
+//     on one (segment, head); two 4-wave workgroups share a CU, so every SIMD
+//     runs two waves (up to 256 registers each).  Keys are walked in tiles of
+//     kBN = 64.
 //   * A single wave issues one vector instruction every ~5 clocks, two waves
 //     together one every ~2.7, and the exp2 and the E4M3 conversion take ~8.5
 //     clocks each; per score the vector work is about as long as the matrix
@@ -47,9 +48,9 @@
 //     2^shift runs at the top of the next iteration, after the P V product of
 //     the older tiles and before that of the tile that moved m.
 //   * K and V^T tiles reach LDS by direct buffer loads (no register staging):
-//     a K ring and a V ring of three 8 KB slots each.  Iteration t loads K of
-//     tile t+3 and V of tile t+1; it reads K of tile t+1 and V of tile t-1.
-//     One barrier per iteration, after waiting for the loads issued two
+//     a K ring and a V ring of four 8 KB slots each.  Iteration t loads K of
+//     tile t+4 and V of tile t+2; it reads K of tile t+1 and V of tile t-1.
+//     One barrier per iteration, after waiting for the loads issued three
 //     iterations earlier, keeps every slot's writes and reads apart.  16-byte
 //     chunks are XOR-swizzled against bank conflicts of the operand reads; the
 //     swizzle is applied to the source addresses of the lane-linear loads.
@@ -69,10 +70,12 @@ constexpr float kLog2Max = 8.807354922057604f;   // log2(448), the largest E4M3 
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kTile = kBN * kHeadDim;            // bytes of one K (or V^T) tile
 constexpr int kSlots = 4;                        // ring slots per operand
-constexpr int kLoadsPerIter = 4;                 // direct loads per wave per iteration (2 K + 2 V)
+constexpr int kWavesWG = kBM / 32;               // waves per workgroup, 32 queries each
+constexpr int kLoadsPerTile = kTile / 1024 / kWavesWG;   // direct 1 KB loads per wave per K (or V) tile
+constexpr int kLoadsPerIter = 2 * kLoadsPerTile; // direct loads per wave per iteration
 constexpr int kVRing = kSlots * kTile;           // V ring follows the K ring in LDS
 constexpr int kBufferFlags = 0x00020000;         // raw buffer descriptor word 3 (gfx9 family)
-static_assert(kBM == 128 && kBN == 64, "4 waves x 32 queries, 64-key tiles");
+static_assert((kBM == 128 || kBM == 256) && kBN == 64, "4 or 8 waves x 32 queries, 64-key tiles");
 
 __device__ __forceinline__ v16f mfma_fp8(const v8i& a, const v8i& b, const v16f& c) {
   // cbsz = blgp = 0 selects E4M3 for both operands; zero scales select the
@@ -145,7 +148,7 @@ __device__ __forceinline__ void fence() { __builtin_amdgcn_sched_barrier(0); }
 __device__ __forceinline__ void keep(const v8i& v) { asm volatile("" ::"v"(v)); }
 
 template <bool LSE>
-__global__ __launch_bounds__(256, 2) void k_attn(AttentionArgs a) {
+__global__ __launch_bounds__(64 * kWavesWG, 8 / kWavesWG) void k_attn(AttentionArgs a) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * kVRing];
 
   const int4 it = a.items[blockIdx.x];
@@ -196,27 +199,27 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttentionArgs a) {
       (void*)Kh, (short)0, (int)((a.rows - si.row0) * kHeadDim), kBufferFlags);
   const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
       (void*)Vh, (short)0, (int)(a.rows * kHeadDim - si.row0), kBufferFlags);
-  int ksrc[2], vsrc[2];
+  int ksrc[kLoadsPerTile], vsrc[kLoadsPerTile];
 #pragma unroll
-  for (int u = 0; u < 2; u++) {
-    const int p = 64 * (2 * wave + u) + lane;
+  for (int u = 0; u < kLoadsPerTile; u++) {
+    const int p = 64 * (kLoadsPerTile * wave + u) + lane;
     ksrc[u] = (p >> 3) * kHeadDim + (((p & 7) ^ ((p >> 4) & 7)) << 4);      // K row p/8, swizzled chunk p%8
     vsrc[u] = (p >> 2) * (int)a.rows + (((p & 3) ^ ((p >> 4) & 3)) << 4);   // V^T row p/4, swizzled chunk p%4
   }
   const int nkt = (L + kBN - 1) / kBN;
-  const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_ptr_t)smem + 2048 * wave;   // LDS byte address of this wave's loads
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_ptr_t)smem + 1024 * kLoadsPerTile * wave;   // LDS byte address of this wave's loads
   // Tile indices past the segment's last tile are clamped: such loads only
   // refill a free slot with valid data, and every iteration issues the same
   // number of loads, which the vmcnt waits rely on.
   auto load_k = [&](int kt, int slot) __attribute__((always_inline)) {
     kt = kt < nkt ? kt : nkt - 1;
 #pragma unroll
-    for (int u = 0; u < 2; u++) lds_dma(krs, lds0 + slot * kTile + u * 1024, ksrc[u], kt * kTile);
+    for (int u = 0; u < kLoadsPerTile; u++) lds_dma(krs, lds0 + slot * kTile + u * 1024, ksrc[u], kt * kTile);
   };
   auto load_v = [&](int kt, int slot) __attribute__((always_inline)) {
     kt = kt < nkt ? kt : nkt - 1;
 #pragma unroll
-    for (int u = 0; u < 2; u++) lds_dma(vrs, lds0 + kVRing + slot * kTile + u * 1024, vsrc[u], kt * kBN);
+    for (int u = 0; u < kLoadsPerTile; u++) lds_dma(vrs, lds0 + kVRing + slot * kTile + u * 1024, vsrc[u], kt * kBN);
   };
 
   // q_hat . mu per query, for the natural-log LSE of the uncentred scores:
@@ -507,9 +510,9 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttentionArgs a) {
 hipError_t launch_attention(const AttentionArgs& a, hipStream_t stream) {
   if (a.nitems == 0) return hipSuccess;
   if (a.lse != nullptr)
-    hipLaunchKernelGGL(k_attn<true>, dim3(a.nitems), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(k_attn<true>, dim3(a.nitems), dim3(64 * kWavesWG), 0, stream, a);
   else
-    hipLaunchKernelGGL(k_attn<false>, dim3(a.nitems), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(k_attn<false>, dim3(a.nitems), dim3(64 * kWavesWG), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -13,7 +13,10 @@ constexpr int kRowPad = 128;     // workspace rows of a segment are padded to th
 constexpr int kGuardRows = 128;  // zero rows after the last segment
 constexpr int kStatChunk = 256;  // tokens per stats chunk; fixes the K-mean summation order
 constexpr int kPackRows = 64;    // workspace rows per pack block (one V key group)
-constexpr int kBM = 128;         // queries per attention work item (4 waves x 32)
+#ifndef FP8ATTN_BM
+#define FP8ATTN_BM 128
+#endif
+constexpr int kBM = FP8ATTN_BM;  // queries per attention work item (one wave per 32)
 constexpr int kBN = 64;          // keys per inner tile
 constexpr int kNumXcd = 8;       // MI355X: workgroups are dealt round-robin to 8 XCDs
 

@@ -4,6 +4,11 @@
 // the measured denominator that sits beside the published peak, as the
 // FlashInfer "minimax_h3_sm120_varlen_attention_nvfp4" page sets its launch
 // against an "MMA-only skeleton" (performance-ceiling paragraph).
+//
+// The operands are either one fixed pattern or four sets of pseudo-random
+// finite E4M3 codes rotated every product.  The two differ: the matrix core's
+// power draw depends on how its operand bits toggle, and with random codes
+// (like the attention kernel's) the device lowers its shader clock.
 #include <hip/hip_runtime.h>
 
 #include "../../include/fp8attn_bench.h"
@@ -15,14 +20,27 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 
 constexpr int kChains = 4;
 
+__device__ __forceinline__ unsigned mix32(unsigned x) {
+  x ^= x >> 16;
+  x *= 0x7feb352du;
+  x ^= x >> 15;
+  x *= 0x846ca68bu;
+  x ^= x >> 16;
+  return x;
+}
+
 // Every wave runs `iters` rounds of kChains independent MFMAs.
-__global__ __launch_bounds__(256) void k_mfma_skeleton(float* sink, int iters, long long* clocks) {
-  v8i a, b;
+__global__ __launch_bounds__(256) void k_mfma_skeleton(float* sink, int iters, int random_operands, long long* clocks) {
+  v8i a[4], b[4];
 #pragma unroll
-  for (int i = 0; i < 8; i++) {
-    a[i] = (int)((threadIdx.x * 7u + i) & 0x3b3b3b3bu);
-    b[i] = (int)((threadIdx.x * 3u + i) & 0x3b3b3b3bu);
-  }
+  for (int s = 0; s < 4; s++)
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+      // fixed: one pattern; random: codes with |code| < 0x78, all finite
+      const unsigned r = mix32(threadIdx.x * 131u + blockIdx.x * 7919u + s * 17u + i * 1031u) & 0x77777777u;
+      a[s][i] = (int)(random_operands ? r : ((threadIdx.x * 7u + i) & 0x3b3b3b3bu));
+      b[s][i] = (int)(random_operands ? (mix32(r) & 0x77777777u) : ((threadIdx.x * 3u + i) & 0x3b3b3b3bu));
+    }
   v16f c[kChains];
 #pragma unroll
   for (int j = 0; j < kChains; j++) c[j] = v16f{};
@@ -30,7 +48,8 @@ __global__ __launch_bounds__(256) void k_mfma_skeleton(float* sink, int iters, l
   const long long r0 = __builtin_amdgcn_s_memrealtime();
   for (int it = 0; it < iters; it++) {
 #pragma unroll
-    for (int j = 0; j < kChains; j++) c[j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c[j], 0, 0, 0, 0, 0, 0);
+    for (int j = 0; j < kChains; j++)
+      c[j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[(it + j) & 3], b[(it + 2 * j) & 3], c[j], 0, 0, 0, 0, 0, 0);
   }
   const long long t1 = __builtin_readcyclecounter();
   const long long r1 = __builtin_amdgcn_s_memrealtime();
@@ -48,7 +67,8 @@ __global__ __launch_bounds__(256) void k_mfma_skeleton(float* sink, int iters, l
 
 }  // namespace
 
-extern "C" int fp8attn_mfma_peak(int device, int iters, double* tflops_out, double* sclk_mhz_out) {
+extern "C" int fp8attn_mfma_peak(int device, int iters, int random_operands, double* tflops_out,
+                                 double* sclk_mhz_out) {
   if (tflops_out == nullptr || sclk_mhz_out == nullptr || iters < 1) return 1;
   int prev = -1;
   if (hipGetDevice(&prev) != hipSuccess || hipSetDevice(device) != hipSuccess) return 5;
@@ -63,9 +83,9 @@ extern "C" int fp8attn_mfma_peak(int device, int iters, double* tflops_out, doub
     if (hipMalloc(&sink, sizeof(float) * grid * 256) != hipSuccess) { status = 3; break; }
     if (hipMalloc(&clocks, 2 * sizeof(long long)) != hipSuccess) { status = 3; break; }
     if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess) { status = 5; break; }
-    hipLaunchKernelGGL(k_mfma_skeleton, dim3(grid), dim3(256), 0, 0, sink, iters, clocks);   // warmup
+    hipLaunchKernelGGL(k_mfma_skeleton, dim3(grid), dim3(256), 0, 0, sink, iters, random_operands, clocks);   // warmup
     if (hipEventRecord(e0, 0) != hipSuccess) { status = 5; break; }
-    hipLaunchKernelGGL(k_mfma_skeleton, dim3(grid), dim3(256), 0, 0, sink, iters, clocks);
+    hipLaunchKernelGGL(k_mfma_skeleton, dim3(grid), dim3(256), 0, 0, sink, iters, random_operands, clocks);
     if (hipEventRecord(e1, 0) != hipSuccess || hipEventSynchronize(e1) != hipSuccess) { status = 5; break; }
     float ms = 0.f;
     long long clk[2] = {0, 0};

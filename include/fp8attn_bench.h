@@ -12,8 +12,15 @@
  * way the FlashInfer "minimax_h3_sm120_varlen_attention_nvfp4" page compares
  * its launch with an MMA-only skeleton.
  *
- * device  HIP device ordinal (the calling thread's current device is restored).
- * iters   rounds of four independent MFMAs per wave (>= 1; 2000 takes ~0.3 ms).
+ * device           HIP device ordinal (the calling thread's current device is
+ *                  restored).
+ * iters            rounds of four independent MFMAs per wave (>= 1; 2000 takes
+ *                  ~0.3 ms, 100000 ~30 ms).
+ * random_operands  0: one fixed operand pattern; 1: four sets of pseudo-random
+ *                  finite E4M3 codes rotated every product.  Random operands
+ *                  draw more power and the device lowers its clock under a long
+ *                  run, so the random, long measurement is the ceiling for
+ *                  kernels that multiply random data.
  * Returns 0 on success, 1 for a bad argument, 3 if a small device allocation
  * failed, 5 for a HIP error.  Synchronous.
  */
@@ -24,7 +31,7 @@
 extern "C" {
 #endif
 
-int fp8attn_mfma_peak(int device, int iters, double* tflops_out, double* sclk_mhz_out);
+int fp8attn_mfma_peak(int device, int iters, int random_operands, double* tflops_out, double* sclk_mhz_out);
 
 #ifdef __cplusplus
 }
