@@ -262,6 +262,7 @@ fp8attn_status fp8attn_quantize(fp8attn_plan_t p, const void* q, const void* k, 
   a.nchunks = (int32_t)p->chunks.size();
   a.ngroups = (int32_t)p->group_seg.size();
   a.rows = p->ws.rows;
+  a.softmax_scale = p->scale;
   hipError_t e = launch_quantize(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(FP8ATTN_EHIP, std::string("quantize launch failed: ") + hipGetErrorString(e));
   return FP8ATTN_OK;

@@ -39,14 +39,18 @@
 //     row 1.  l is the sum of the E4M3 probabilities that actually weight V.
 //     When the caller asks for the LSE, an FP32 sum of the unrounded
 //     probabilities is kept as well.
-//   * Probabilities: p = exp2(c*s + nb) with c = softmax_scale * s_q * s_k *
-//     log2(e) and nb = log2(112) - c*m for a per-query reference maximum m.
-//     The first tile sets m to its row maximum (mapped to 112 = 448/4).  Later
-//     tiles move m only when their maximum would give a p above 448, the
-//     largest E4M3 value, so most tiles need no rescale.  The test is
-//     branch-free (it only updates nb); the rare rescale of O and l by
-//     2^shift runs at the top of the next iteration, after the P V product of
-//     the older tiles and before that of the tile that moved m.
+//   * Probabilities: p = exp2(x), x = c*s + nb with c = softmax_scale * s_q *
+//     s_k * log2(e) and nb = log2(112) - c*m for a per-query reference maximum
+//     m.  The quantizer makes c a power of two, so the score products run on
+//     the scaled MFMA (E8M0 factor c) with nb as the initial accumulator and
+//     deliver x itself: the vector work per score is one exp2 and half a
+//     conversion.  The first tile sets m to its row maximum (mapped to 112 =
+//     448/4).  Later tiles move m only when their maximum would give a p above
+//     448, the largest E4M3 value, so most tiles need no rescale: the common
+//     path is a max tree and one wave-wide vote; the rare path shifts x, nb and
+//     the accumulator offset, and the rescale of O and l by 2^shift runs at
+//     the top of the next iteration, after the P V product of the older tiles
+//     and before that of the tile that moved m.
 //   * K and V^T tiles reach LDS by direct buffer loads (no register staging):
 //     a K ring and a V ring of four 8 KB slots each.  Iteration t loads K of
 //     tile t+4 and V of tile t+2; it reads K of tile t+1 and V of tile t-1.
@@ -81,6 +85,10 @@ __device__ __forceinline__ v16f mfma_fp8(const v8i& a, const v8i& b, const v16f&
   // cbsz = blgp = 0 selects E4M3 for both operands; zero scales select the
   // unscaled instruction.
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+// a*b scaled by 2^(ea - 127) (ea an E8M0 code, the same in every lane), plus c.
+__device__ __forceinline__ v16f mfma_fp8_scaled(const v8i& a, const v8i& b, const v16f& c, int ea) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, ea, 0, 127);
 }
 __device__ __forceinline__ v4f mfma16_fp8(const v8i& a, const v8i& b, const v4f& c) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
@@ -146,6 +154,7 @@ __device__ __forceinline__ void fence() { __builtin_amdgcn_sched_barrier(0); }
 // Pins the computation of v before this point (an empty instruction that
 // reads it), so the softmax of a tile is not moved into the next iteration.
 __device__ __forceinline__ void keep(const v8i& v) { asm volatile("" ::"v"(v)); }
+__device__ __forceinline__ void keep(const v16f& v) { asm volatile("" ::"v"(v)); }
 
 template <bool LSE>
 __global__ __launch_bounds__(64 * kWavesWG, 8 / kWavesWG) void k_attn(AttentionArgs a) {
@@ -171,7 +180,13 @@ __global__ __launch_bounds__(64 * kWavesWG, 8 / kWavesWG) void k_attn(AttentionA
   const float s_q = a.scales[h];
   const float s_k = a.scales[a.heads + h];
   const float s_v = a.scales[2 * a.heads + h];
+  // Score factor c = softmax_scale * s_q * s_k * log2(e).  The quantizer picks
+  // s_q so that c is a power of two up to the rounding of this product, so its
+  // E8M0 code (the biased exponent rounded to nearest) scales the score
+  // products exactly: x = c * (q . k) + nb comes out of the matrix core with the
+  // per-query exp2 offset nb as the accumulator's initial value.
   const float c = a.softmax_scale * s_q * s_k * kLog2e;
+  const int c_e8m0 = min((int)((__float_as_uint(c) + 0x400000u) >> 23), 254);
 
   // Q as B operands: queries q0 + 32*wave + (lane%32), channels
   // 64*half + 32*(lane/32) .. +32.  Rows past the segment end read zero codes,
@@ -257,7 +272,8 @@ __global__ __launch_bounds__(64 * kWavesWG, 8 / kWavesWG) void k_attn(AttentionA
   bool pending = false; // wave-uniform: some lane has a pshift
 #pragma unroll
   for (int db = 0; db < 4; db++) O[db] = v16f{};
-  v16f S[2];       // scores of the current tile [32-key block], refilled with the next tile's
+  v16f NB = {};    // nb in every register: the initial accumulator of the score products
+  v16f S[2];       // exp2 arguments x of the current tile [32-key block], refilled with the next tile's
   v8i P;           // packed probabilities of the previous tile, then of the current one
 
   // Scores of the tile whose K is in slot ks into S.
@@ -267,7 +283,7 @@ __global__ __launch_bounds__(64 * kWavesWG, 8 / kWavesWG) void k_attn(AttentionA
     for (int kb = 0; kb < 2; kb++) {
       const v8i k0 = lds_read32(kb_base + kb * 32 * 128, koff[0][0], koff[0][1]);
       const v8i k1 = lds_read32(kb_base + kb * 32 * 128, koff[1][0], koff[1][1]);
-      S[kb] = mfma_fp8(k1, qf[1], mfma_fp8(k0, qf[0], v16f{}));
+      S[kb] = mfma_fp8_scaled(k1, qf[1], mfma_fp8_scaled(k0, qf[0], NB, c_e8m0), c_e8m0);
     }
   };
   // O^T += V^T P^T for the tile whose V^T is in slot vs, and its row sums
@@ -295,11 +311,10 @@ __global__ __launch_bounds__(64 * kWavesWG, 8 / kWavesWG) void k_attn(AttentionA
       pending = false;
     }
   };
-  // Softmax of the tile whose scores are in S (kbase = its first key) into P,
-  // and the scores of the next tile (K in slot ks_next) into S, block by block
-  // as soon as the old block's scores are consumed.  FIRST sets the reference
-  // from the tile maximum.  Keys past the segment end are not masked: their K
-  // rows are zero codes, so their scores are exactly 0, which does not exceed
+  // Reference update for the tile whose exp2 arguments are in S.  FIRST sets
+  // the reference from the tile maximum.  Keys past the segment end are not
+  // masked: their K rows are zero codes, so their scores are exactly 0 (x =
+  // nb), which does not exceed
   // the row maximum (the centred keys of a segment average to zero, so the
   // largest score is >= 0 up to rounding); their V rows are zero too, and the
   // row sum of the last tile uses a selector without them.  Only the FP32 sum
@@ -307,7 +322,8 @@ __global__ __launch_bounds__(64 * kWavesWG, 8 / kWavesWG) void k_attn(AttentionA
   // kbase + 32*kb + 8*(r/4) + 4*(l/32) + r%4.
   auto rowmax_update = [&](auto first_c) __attribute__((always_inline)) {
     constexpr bool FIRST = decltype(first_c)::value;
-    // row maximum of the raw scores: 15 v_max3 + 1 v_max in-lane, then the pair lane
+    // this lane's maximum of x: 15 v_max3 + 1 v_max (the pair lane holds the
+    // other half of the row)
     float m8[8];
 #pragma unroll
     for (int i = 0; i < 5; i++) m8[i] = __builtin_fmaxf(__builtin_fmaxf(S[0][3 * i], S[0][3 * i + 1]), S[0][3 * i + 2]);
@@ -322,26 +338,35 @@ __global__ __launch_bounds__(64 * kWavesWG, 8 / kWavesWG) void k_attn(AttentionA
     const float n4 = __builtin_fmaxf(__builtin_fmaxf(m8[4], m8[5]), m8[6]);
     const float n5 = __builtin_fmaxf(__builtin_fmaxf(m8[7], n0), n1);
     const float tl = __builtin_fmaxf(__builtin_fmaxf(__builtin_fmaxf(n2, n3), n4), n5);
-    auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(tl), __float_as_uint(tl), false, false);
-    const float tm = __builtin_fmaxf(__uint_as_float(pr[0]), __uint_as_float(pr[1]));
     if (FIRST) {
-      nb = kLog2Ref - c * tm;
+      auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(tl), __float_as_uint(tl), false, false);
+      const float tm = __builtin_fmaxf(__uint_as_float(pr[0]), __uint_as_float(pr[1]));
+      const float shift = kLog2Ref - tm;
+      nb = shift;
+#pragma unroll
+      for (int i = 0; i < 16; i++) { S[0][i] += shift; S[1][i] += shift; NB[i] = shift; }
     } else {
-      // move the reference only if the tile's largest p would exceed 448
-      const float xm = __builtin_fmaf(tm, c, nb);
-      const bool over = xm > kLog2Max;
-      const float shift = over ? kLog2Ref - xm : 0.f;
-      nb += shift;
-      pshift = shift;
-      if (LSE) lex *= __builtin_amdgcn_exp2f(shift);   // lex takes this tile's p in the new frame
-      pending = __builtin_amdgcn_ballot_w64(over) != 0;
+      // move the reference only if the tile's largest p would exceed 448: one
+      // vote over the wave; the row maxima and shifts only on the rare path
+      pending = __builtin_amdgcn_ballot_w64(tl > kLog2Max) != 0;
+      if (pending) {
+        auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(tl), __float_as_uint(tl), false, false);
+        const float xm = __builtin_fmaxf(__uint_as_float(pr[0]), __uint_as_float(pr[1]));
+        const bool over = xm > kLog2Max;
+        const float shift = over ? kLog2Ref - xm : 0.f;
+        nb += shift;
+        pshift = shift;
+        if (LSE) lex *= __builtin_amdgcn_exp2f(shift);   // lex takes this tile's p in the new frame
+#pragma unroll
+        for (int i = 0; i < 16; i++) { S[0][i] += shift; S[1][i] += shift; NB[i] += shift; }
+      }
     }
   };
   // E4M3 probabilities of keys 8*q4 + 4*(lane/32) + 0..3 of block kb (one P dword).
   auto probs4 = [&](int kb, int q4, int kbase) __attribute__((always_inline)) {
     float p[4];
 #pragma unroll
-    for (int i = 0; i < 4; i++) p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kb][4 * q4 + i], c, nb));
+    for (int i = 0; i < 4; i++) p[i] = __builtin_amdgcn_exp2f(S[kb][4 * q4 + i]);
     if (LSE) {
       const int key0 = kbase + 32 * kb + 8 * q4 + 4 * lg;
 #pragma unroll
@@ -425,19 +450,21 @@ __global__ __launch_bounds__(64 * kWavesWG, 8 / kWavesWG) void k_attn(AttentionA
     Pn[2] = probs4(0, 2, kbase);
     fence();
     Pn[3] = probs4(0, 3, kbase);
-    const v16f s0 = mfma_fp8(kf[0][0], qf[0], v16f{});
+    const v16f s0 = mfma_fp8_scaled(kf[0][0], qf[0], NB, c_e8m0);
     fence();
-    S[0] = mfma_fp8(kf[0][1], qf[1], s0);
+    S[0] = mfma_fp8_scaled(kf[0][1], qf[1], s0, c_e8m0);
     Pn[4] = probs4(1, 0, kbase);
     fence();
     Pn[5] = probs4(1, 1, kbase);
-    const v16f s1 = mfma_fp8(kf[1][0], qf[0], v16f{});
+    const v16f s1 = mfma_fp8_scaled(kf[1][0], qf[0], NB, c_e8m0);
     fence();
     Pn[6] = probs4(1, 2, kbase);
     Pn[7] = probs4(1, 3, kbase);
-    S[1] = mfma_fp8(kf[1][1], qf[1], s1);
+    S[1] = mfma_fp8_scaled(kf[1][1], qf[1], s1, c_e8m0);
     P = Pn;
     keep(P);
+    keep(S[0]);   // the next tile's score products stay in this iteration
+    keep(S[1]);
   };
   // Unrolled by the ring depth so that every slot address is static.
   static_assert(kSlots == 4, "unrolled for four slots");

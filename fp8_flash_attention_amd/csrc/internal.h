@@ -59,6 +59,7 @@ struct QuantizeArgs {
   const int32_t* group_seg;  // [ngroups]: segment of each 64-row pack group, -1 = guard
   int32_t heads, nseg, nchunks, ngroups;
   int64_t rows;
+  float softmax_scale;       // fixes Q's scale (see k_finalize)
 };
 
 struct AttentionArgs {

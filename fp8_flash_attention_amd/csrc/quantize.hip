@@ -30,8 +30,8 @@ __device__ __forceinline__ void unpack8(const uint4 v, float f[8]) {
 
 // E4M3 codes of 4 floats packed little-endian into one dword.  v_cvt_pk_fp8_f32
 // on gfx950 converts to OCP E4M3 with round-to-nearest-even and keeps
-// subnormals; the quantizer's inputs satisfy |y| <= 448 * (1 + 2^-23), inside
-// the range where it rounds (inputs of 464 and above would become NaN).
+// subnormals; the quantizer's inputs lie within a few ulps of +-448 at most,
+// inside the range where it rounds (inputs of 464 and above would become NaN).
 __device__ __forceinline__ uint32_t cvt4(float a, float b, float c, float d) {
   int r = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
   r = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, r, true);
@@ -101,7 +101,8 @@ __global__ __launch_bounds__(256) void k_stats(QuantizeArgs a) {
 // mu[s][h][d] = fl32(sum64 / L) with chunk sums added in ascending order from
 // +0.0; K amax = max over segments and channels of |fl32(max - mu)| and
 // |fl32(min - mu)|, which equals max |fl32(x - mu)| over the tokens because
-// rounding is monotone; s = fl32(amax / 448), or 1 for amax == 0.
+// rounding is monotone; s = fl32(amax / 448), or 1 for amax == 0, for K and
+// V; Q's scale is rounded up from that (q_scale_of).
 // ---------------------------------------------------------------------------
 __device__ float block_max128(float v, float* red) {
 #pragma unroll
@@ -114,6 +115,24 @@ __device__ float block_max128(float v, float* red) {
 }
 
 __device__ __forceinline__ float scale_of(float amax) { return amax > 0.f ? amax / 448.0f : 1.0f; }
+
+// Q's scale: amax/448 rounded up to the nearest value that makes the score
+// factor c = softmax_scale * s_q * s_k * log2(e) a power of two, so that the
+// attention kernel applies c exactly as an E8M0 factor of its score products.
+// The largest Q code stays in (224, 448] (E4M3 keeps its relative precision
+// over that range).  fl32(2^m / f) can fall an ulp below amax/448; the
+// largest code then rounds to 448 all the same.  If f * amax/448 is not a
+// normal float the plain amax/448 scale is kept.
+__device__ __forceinline__ float q_scale_of(float qa, float s_k, float softmax_scale) {
+  const float base = scale_of(qa);
+  const float f = softmax_scale * s_k * 1.4426950408889634f;   // c / s_q
+  const float t = f * base;
+  if (!(t >= 0x1p-126f && t < 0x1p126f)) return base;
+  int e;
+  const float fr = frexpf(t, &e);            // t = fr * 2^e, fr in [0.5, 1)
+  const int m = fr == 0.5f ? e - 1 : e;      // smallest 2^m >= t
+  return ldexpf(1.0f, m) / f;
+}
 
 __global__ __launch_bounds__(128) void k_finalize(QuantizeArgs a) {
   __shared__ float red[2];
@@ -147,7 +166,7 @@ __global__ __launch_bounds__(128) void k_finalize(QuantizeArgs a) {
   va = block_max128(va, red);
   ka = block_max128(ka, red);
   if (d == 0) {
-    a.scales[h] = scale_of(qa);
+    a.scales[h] = q_scale_of(qa, scale_of(ka), a.softmax_scale);
     a.scales[a.heads + h] = scale_of(ka);
     a.scales[2 * a.heads + h] = scale_of(va);
   }

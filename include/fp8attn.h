@@ -107,8 +107,13 @@ size_t fp8attn_workspace_bytes(fp8attn_plan_t plan);
  *               256-byte aligned.  Its prior contents do not matter.
  * stream        hipStream_t to enqueue on (NULL = default stream).
  *
- * Per head h and tensor X in {Q, K, V}: s_X[h] = fl32(amax / 448), or 1.0 when
- * amax == 0; codes = E4M3(fl32(y / s_X[h])) with round-to-nearest-even,
+ * Per head h and tensor X in {K, V}: s_X[h] = fl32(amax / 448), or 1.0 when
+ * amax == 0.  Q's scale is that value rounded up to make the score factor
+ * softmax_scale * s_Q * s_K * log2(e) a power of two: with b = the amax/448
+ * scale of Q and f = fl32(fl32(softmax_scale * s_K[h]) * log2(e)),
+ * s_Q[h] = fl32(2^m / f) for the smallest m with 2^m >= fl32(f * b) (b itself
+ * if fl32(f * b) is not a normal float), so Q's largest code lies in
+ * (224, 448].  Codes = E4M3(fl32(y / s_X[h])) with round-to-nearest-even,
  * subnormals kept and the sign copied; y = x for Q and V; for K, y =
  * fl32(x - mu[seg][h][d]) with mu the segment's per-channel mean, summed in
  * float64 in 256-token chunks from the segment start (ascending inside a chunk,

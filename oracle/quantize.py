@@ -28,7 +28,17 @@ Fixed-order mean (a reading; the pages fix no summation order): for segment
     mu = fl32(fl64(sum64 / L))
 
 Empty segments have no mean; their ``mu`` rows are 0.
-Parity pins live in ``tests/test_oracle_quantize.py``.
+
+Q's scale in the product (``q_scale_pow2``): the pages ask for per-head amax
+scaling and fix no exact formula; the product rounds Q's amax/448 scale up so
+that the score factor ``softmax_scale * s_q * s_k * log2(e)`` is a power of two
+(the attention kernel then applies it exactly on the matrix core).  This is the
+product's choice, not a reading of the pages; it is mirrored here so that tests
+derive the expected Q codes from the inputs alone.  ``quantize`` uses it when a
+``softmax_scale`` is given and the plain amax/448 scale otherwise.
+Parity pins live in ``tests/test_oracle_quantize.py`` (for ``q_scale_pow2``:
+the scale is at least amax/448 and below twice it, and the score factor is a
+power of two up to float32 rounding).
 """
 from __future__ import annotations
 
@@ -59,6 +69,29 @@ def head_scale(amax: np.ndarray) -> np.ndarray:
     return np.where(amax == 0, np.float32(1.0), s).astype(np.float32)
 
 
+LOG2E_F32 = np.float32(1.4426950408889634)
+
+
+def q_scale_pow2(base: np.ndarray, s_k: np.ndarray, softmax_scale: float) -> np.ndarray:
+    """Q's per-head scale: ``base`` (amax/448) rounded up to the smallest
+    fl32(2^m / f), f = fl32(fl32(softmax_scale * s_k) * log2(e)), with
+    2^m >= fl32(f * base); ``base`` itself where fl32(f * base) is not a normal
+    float.  All arithmetic in float32, in the order written."""
+    base = np.asarray(base, np.float32)
+    s_k = np.asarray(s_k, np.float32)
+    f = (np.float32(softmax_scale) * s_k) * LOG2E_F32
+    t = (f * base).astype(np.float32)
+    out = base.copy()
+    for i in np.ndindex(t.shape):
+        ti = np.float32(t[i])
+        if not (np.float32(2.0 ** -126) <= ti < np.float32(2.0 ** 126)):
+            continue
+        fr, e = np.frexp(ti)                    # ti = fr * 2^e, fr in [0.5, 1)
+        m = int(e) - 1 if fr == 0.5 else int(e)
+        out[i] = np.float32(2.0 ** m) / np.float32(f[i])
+    return out.astype(np.float32)
+
+
 def segment_mean(x: np.ndarray, a: int, b: int) -> np.ndarray:
     """Fixed-order float64 mean of rows [a, b) of x [T, H, D], rounded to float32."""
     H, D = x.shape[1], x.shape[2]
@@ -73,13 +106,21 @@ def segment_mean(x: np.ndarray, a: int, b: int) -> np.ndarray:
     return (total / float(b - a)).astype(np.float32)
 
 
-def quantize_plain(x) -> Dict[str, np.ndarray]:
-    """Per-head quantization of Q or V: codes [T, H, D] uint8, scale [H] float32."""
+def encode_at_scale(x, s: np.ndarray) -> np.ndarray:
+    """E4M3 codes of fl32(x / s_h): codes [T, H, D] uint8 for per-head scales s [H]."""
+    y = _as_f32(x) / np.asarray(s, np.float32)[None, :, None]   # float32 / float32: IEEE division
+    return e4m3.encode(y)
+
+
+def quantize_plain(x, scale: np.ndarray = None) -> Dict[str, np.ndarray]:
+    """Per-head quantization of Q or V: codes [T, H, D] uint8, scale [H] float32
+    (amax/448 unless ``scale`` is given)."""
     xf = _as_f32(x)
-    amax = np.abs(xf).max(axis=(0, 2)) if xf.shape[0] > 0 else np.zeros(xf.shape[1], np.float32)
-    s = head_scale(amax)
-    y = xf / s[None, :, None]                     # float32 / float32: IEEE division
-    return {"codes": e4m3.encode(y), "scale": s}
+    if scale is None:
+        amax = np.abs(xf).max(axis=(0, 2)) if xf.shape[0] > 0 else np.zeros(xf.shape[1], np.float32)
+        scale = head_scale(amax)
+    s = np.asarray(scale, np.float32)
+    return {"codes": encode_at_scale(xf, s), "scale": s}
 
 
 def quantize_k(x, cu_seqlens: List[int]) -> Dict[str, np.ndarray]:
@@ -102,11 +143,15 @@ def quantize_k(x, cu_seqlens: List[int]) -> Dict[str, np.ndarray]:
     return {"codes": codes, "scale": sc, "mu": mu}
 
 
-def quantize(q, k, v, cu_seqlens: List[int]) -> Dict[str, np.ndarray]:
+def quantize(q, k, v, cu_seqlens: List[int], softmax_scale: float = None) -> Dict[str, np.ndarray]:
     """All three tensors.  Keys: q_codes, k_codes, v_codes ([T, H, D] uint8),
-    scales ([3, H] float32, rows Q, K, V) and mu ([nseg, H, D] float32)."""
-    rq = quantize_plain(q)
+    scales ([3, H] float32, rows Q, K, V) and mu ([nseg, H, D] float32).  With
+    ``softmax_scale`` given, Q's scale is ``q_scale_pow2`` of its amax/448 scale
+    (the product's rule)."""
     rk = quantize_k(k, cu_seqlens)
+    rq = quantize_plain(q)
+    if softmax_scale is not None:
+        rq = quantize_plain(q, q_scale_pow2(rq["scale"], rk["scale"], softmax_scale))
     rv = quantize_plain(v)
     return {
         "q_codes": rq["codes"], "k_codes": rk["codes"], "v_codes": rv["codes"],

@@ -42,8 +42,8 @@ def _gpu_attention(w, q, k, v, lse=False):
     return plan, ws, out, l
 
 
-def _dequantized(q, k, v, cu):
-    r = Qz.quantize(q, k, v, cu)
+def _dequantized(q, k, v, cu, softmax_scale):
+    r = Qz.quantize(q, k, v, cu, softmax_scale)
     sc = r["scales"]
     return (Qz.dequantize(r["q_codes"], sc[0]), Qz.dequantize(r["k_codes"], sc[1]),
             Qz.dequantize(r["v_codes"], sc[2]))
@@ -72,7 +72,7 @@ def _check_rows(w, rows, heads=None, pure_atol=False):
 def test_s256_h2_every_element():
     w = WORKLOADS["s256_h2"]
     got, (q, k, v) = _check_rows(w, list(range(w.tokens)), pure_atol=True)
-    dq, dk, dv = _dequantized(q, k, v, w.cu_seqlens)
+    dq, dk, dv = _dequantized(q, k, v, w.cu_seqlens, w.softmax_scale)
     diag = A.attention(dq, dk, dv, w.cu_seqlens, w.softmax_scale).numpy()
     assert compare.rel_rms(got, diag) <= DIAG_BAR
 
@@ -89,7 +89,7 @@ def test_full_size_sampled_rows(name, nrows):
     got, (q, k, v) = _check_rows(w, rows, pure_atol=len(w.segments) == 1)
     # kernel-only error on three heads against the dequantized-operand oracle
     hs = [0, 31, 55]
-    dq, dk, dv = _dequantized(q[:, hs], k[:, hs], v[:, hs], w.cu_seqlens)
+    dq, dk, dv = _dequantized(q[:, hs], k[:, hs], v[:, hs], w.cu_seqlens, w.softmax_scale)
     diag = A.attention_rows(dq, dk, dv, w.cu_seqlens, w.softmax_scale, rows).numpy()
     rr = compare.rel_rms(got[:, hs], diag)
     log(f"  diagnostic rel_rms={rr:.5f}")
@@ -204,7 +204,7 @@ def test_lse_matches_oracle():
     # against the LSE of the dequantized operands (centred keys plus their segment mean):
     # the kernel sums the FP32 probabilities, so only accumulation order and the FP32
     # exponentials remain
-    r = Qz.quantize(q, k, v, cu)
+    r = Qz.quantize(q, k, v, cu, w.softmax_scale)
     dq = Qz.dequantize(r["q_codes"], r["scales"][0])
     dk = Qz.dequantize(r["k_codes"], r["scales"][1])
     for s, (a, b) in enumerate(zip(cu[:-1], cu[1:])):

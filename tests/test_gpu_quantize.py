@@ -1,6 +1,9 @@
 """GPU parity of fp8attn_quantize against the CPU quantizer: E4M3 codes, per-head
 scales and per-(segment, head, channel) K means must match bit for bit.
 
+Q's scale follows the product's rule (amax/448 rounded up to a power-of-two
+score factor, ``oracle.quantize.q_scale_pow2``); K and V use amax/448.
+
 Quantization is independent across heads (every scale and mean is per head), so
 at the full workload sizes the oracle is run on a seeded sample of heads over
 all tokens; the small cases compare every head.
@@ -33,7 +36,7 @@ def _check(w, heads, poison=False):
     plan, ws, (q, k, v) = _run_quantize(w, poison)
     got = read_codes(plan, ws, heads)
     hs = list(heads) if heads is not None else list(range(w.heads))
-    exp = Qz.quantize(q[:, hs], k[:, hs], v[:, hs], w.cu_seqlens)
+    exp = Qz.quantize(q[:, hs], k[:, hs], v[:, hs], w.cu_seqlens, w.softmax_scale)
     for name in ("q_codes", "k_codes", "v_codes"):
         a, b = got[name], exp[name]
         bad = np.argwhere(a != b)
@@ -84,7 +87,9 @@ def test_poisoned_workspace_leaves_no_nan_byte():
     _check(w, None, poison=True)
 
 
-def test_zero_head_scale_is_one():
+def test_zero_head_scale():
+    # all-zero K and V heads get scale 1; an all-zero Q head gets 1 rounded up
+    # to a power-of-two score factor; every code of such a head is zero
     w = make_workload("zeros", 300, 2, [0, 300], seed=80)
     q, k, v = generate(w, device="cuda")
     q[:, 1] = 0
@@ -96,9 +101,11 @@ def test_zero_head_scale_is_one():
     fa.quantize(plan, q, k, v, ws)
     torch.cuda.synchronize()
     sc = plan.region(ws, 3).cpu().numpy()
-    assert sc[0, 1] == 1.0 and sc[1, 1] == 1.0 and sc[2, 0] == 1.0
-    exp = Qz.quantize(q.cpu(), k.cpu(), v.cpu(), w.cu_seqlens)
+    assert sc[1, 1] == 1.0 and sc[2, 0] == 1.0 and 1.0 <= sc[0, 1] < 2.0
+    exp = Qz.quantize(q.cpu(), k.cpu(), v.cpu(), w.cu_seqlens, w.softmax_scale)
+    assert np.array_equal(sc.view(np.uint32), exp["scales"].view(np.uint32))
     got = read_codes(plan, ws)
+    assert not got["q_codes"][:, 1].any() and not got["v_codes"][:, 0].any()
     for name in ("q_codes", "k_codes", "v_codes"):
         assert np.array_equal(got[name], exp[name])
 

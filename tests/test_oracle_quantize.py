@@ -117,3 +117,53 @@ def test_quantize_bundle_shapes():
     assert r["mu"].shape == (2, H, 128)
     deq = Qz.dequantize(r["v_codes"], r["scales"][2])
     assert np.abs(deq - v.float().numpy()).max() <= float(r["scales"][2].max()) * 16.0
+
+
+def test_q_scale_pow2_properties():
+    # the product's Q scale: at least amax/448, below twice it, and the score
+    # factor softmax_scale * s_q * s_k * log2(e) a power of two up to rounding
+    rng = np.random.default_rng(11)
+    base = np.float32(10.0) ** rng.uniform(-6, 3, 400).astype(np.float32)
+    s_k = np.float32(10.0) ** rng.uniform(-6, 3, 400).astype(np.float32)
+    for sigma in (1 / np.sqrt(128), 0.05, 1.0, 3.7):
+        s = Qz.q_scale_pow2(base, s_k, sigma)
+        assert s.dtype == np.float32
+        b64, s64 = base.astype(np.float64), s.astype(np.float64)
+        assert np.all(s64 >= b64 * (1 - 2.0 ** -22)) and np.all(s64 < 2 * b64)
+        c = float(np.float32(sigma)) * s64 * s_k.astype(np.float64) * np.log2(np.e)
+        m = np.round(np.log2(c))
+        assert np.all(np.abs(c / 2.0 ** m - 1) < 2.0 ** -21)
+        # the largest |q| quantizes to a code of magnitude in (224, 448]
+        y = (base * np.float32(448)) / s
+        assert np.all(y > 224) and np.all(y <= 448 * (1 + 2.0 ** -20))
+
+
+def test_q_scale_pow2_worked_cases():
+    # a factor that is already a power of two keeps the amax/448 scale exactly:
+    # softmax_scale * s_k * log2(e) = 2^-3 with s_k = 2^-3 / fl32(sigma * log2e)
+    sigma = 1.0 / np.log2(np.e)                 # fl32(sigma) * fl32(log2 e) rounds to 1
+    f = np.float32(np.float32(sigma) * np.float32(1.0)) * Qz.LOG2E_F32
+    assert f == np.float32(1.0)
+    s = Qz.q_scale_pow2(np.float32([0.25, 0.3, 0.5 + 2.0 ** -24]), np.float32([1.0] * 3), sigma)
+    assert s[0] == np.float32(0.25)             # t = 2^-2 exactly: m = -2
+    assert s[1] == np.float32(0.5)              # t = 0.3: next power of two
+    assert s[2] == np.float32(1.0)              # just above 2^-1: m = 0
+    # outside the normal float range the plain scale is kept
+    tiny = Qz.q_scale_pow2(np.float32([1e-30]), np.float32([1e-20]), 0.1)
+    assert tiny[0] == np.float32(1e-30)
+
+
+def test_quantize_with_softmax_scale_changes_only_q():
+    T, H = 200, 2
+    q, k, v = _bf16((T, H, 128), 21), _bf16((T, H, 128), 22, 1.5), _bf16((T, H, 128), 23)
+    cu = [0, 77, 200]
+    r0 = Qz.quantize(q, k, v, cu)
+    r1 = Qz.quantize(q, k, v, cu, 1 / np.sqrt(128))
+    for key in ("k_codes", "v_codes", "mu"):
+        assert np.array_equal(r0[key], r1[key])
+    assert np.array_equal(r0["scales"][1:], r1["scales"][1:])
+    assert np.array_equal(r1["scales"][0], Qz.q_scale_pow2(r0["scales"][0], r0["scales"][1], 1 / np.sqrt(128)))
+    # Q codes against torch's E4M3 cast of fl32(q / s) at the new scale
+    ref = (torch.from_numpy(q.float().numpy() / r1["scales"][0][None, :, None])
+           .to(torch.float8_e4m3fn).view(torch.uint8).numpy())
+    assert np.array_equal(r1["q_codes"], ref)
