@@ -97,6 +97,7 @@ def main() -> int:
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-skeleton", action="store_true", help="skip the MFMA-only skeleton runs (profiling)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="after timing, run one plain device copy of BYTES bytes (a known-size "
                          "reference dispatch for scaling HBM traffic counters)")
@@ -164,8 +165,8 @@ def main() -> int:
         rc = _lib.lib().fp8attn_mfma_peak(0, iters, random_operands, ctypes.byref(tf), ctypes.byref(mhz))
         return {"tflops": round(tf.value, 1), "sclk_mhz": round(mhz.value, 0)} if rc == 0 else None
 
-    skeleton = skeleton_run(2000, 0)
-    skeleton_random = skeleton_run(100000, 1)
+    skeleton = None if args.no_skeleton else skeleton_run(2000, 0)
+    skeleton_random = None if args.no_skeleton else skeleton_run(100000, 1)
 
     traffic = measured_traffic(w.name)
     res = {

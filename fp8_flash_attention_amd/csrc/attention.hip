@@ -53,11 +53,14 @@
 //     and before that of the tile that moved m.
 //   * K and V^T tiles reach LDS by direct buffer loads (no register staging):
 //     a K ring and a V ring of four 8 KB slots each.  Iteration t loads K of
-//     tile t+4 and V of tile t+2; it reads K of tile t+1 and V of tile t-1.
-//     One barrier per iteration, after waiting for the loads issued three
-//     iterations earlier, keeps every slot's writes and reads apart.  16-byte
-//     chunks are XOR-swizzled against bank conflicts of the operand reads; the
-//     swizzle is applied to the source addresses of the lane-linear loads.
+//     tile t+4 and V of tile t+2; it reads K of tile t+1 for its score
+//     products, and V of tile t for the P V product of the next iteration, so
+//     that product starts right after the barrier with its operands already
+//     in registers.  One barrier per iteration, after waiting for the loads
+//     issued two iterations earlier, keeps every slot's writes and reads
+//     apart.  16-byte chunks are XOR-swizzled against bank conflicts of the
+//     operand reads; the swizzle is applied to the source addresses of the
+//     lane-linear loads.
 #include "internal.h"
 
 namespace fp8attn {
@@ -286,17 +289,6 @@ __global__ __launch_bounds__(64 * kWavesWG, 8 / kWavesWG) void k_attn(AttentionA
       S[kb] = mfma_fp8_scaled(k1, qf[1], mfma_fp8_scaled(k0, qf[0], NB, c_e8m0), c_e8m0);
     }
   };
-  // O^T += V^T P^T for the tile whose V^T is in slot vs, and its row sums
-  // through selector sl.
-  auto pv = [&](int vs, const v8i& sl) __attribute__((always_inline)) {
-    const uint8_t* vb_base = smem + kVRing + vs * kTile;
-#pragma unroll
-    for (int db = 0; db < 4; db++) {
-      const v8i vf = lds_read32(vb_base + db * 32 * 64, voff[0], voff[1]);
-      O[db] = mfma_fp8(vf, P, O[db]);
-    }
-    lacc = mfma16_fp8(sl, P, lacc);
-  };
   // Apply a pending reference shift to O and l (rare; wave-uniform branch):
   // they hold the products of tiles up to t-1, computed in the old frame.
   auto rescale = [&]() __attribute__((always_inline)) {
@@ -368,9 +360,9 @@ __global__ __launch_bounds__(64 * kWavesWG, 8 / kWavesWG) void k_attn(AttentionA
 #pragma unroll
     for (int i = 0; i < 4; i++) p[i] = __builtin_amdgcn_exp2f(S[kb][4 * q4 + i]);
     if (LSE) {
-      const int key0 = kbase + 32 * kb + 8 * q4 + 4 * lg;
+      // every key of the tile, padded ones included (removed after the loop)
 #pragma unroll
-      for (int i = 0; i < 4; i++) lex += key0 + i < L ? p[i] : 0.f;
+      for (int i = 0; i < 4; i++) lex += p[i];
     }
     return cvt4(p[0], p[1], p[2], p[3]);
   };
@@ -386,7 +378,9 @@ __global__ __launch_bounds__(64 * kWavesWG, 8 / kWavesWG) void k_attn(AttentionA
   // Prologue: K(0), K(1); then K(i), V(i-2) for i = 2 .. kSlots-1, which are
   // the loads iterations 2-kSlots .. -1 would issue.  Iteration t issues
   // K(t+kSlots) and V(t+kSlots-2); at its top it waits for the loads of
-  // iteration t+1-kSlots, which hold the K(t+1) and V(t-1) it reads.
+  // iteration t-2, which hold the K(t+2) and V(t) it may read after the
+  // barrier (K(t+1) has been readable since the previous barrier).  A slot is
+  // refilled only after the barrier that follows its last read.
   load_k(0, 0);
   load_k(1, 1);
 #pragma unroll
@@ -398,73 +392,90 @@ __global__ __launch_bounds__(64 * kWavesWG, 8 / kWavesWG) void k_attn(AttentionA
   barrier();
   qk(0);
   // Iteration 0: reference from tile 0; nothing to add to O yet.
-  wait_vmcnt<kLoadsPerIter * (kSlots - 2)>();
+  wait_vmcnt<kLoadsPerIter>();
   barrier();
   load_k(kSlots, 0);
   load_v(kSlots - 2, kSlots - 2);
   first_tile();
   keep(P);
-  // Iteration t (S holds tile t's scores, P tile t-1's probabilities): wait
-  // for the loads of iteration t+1-kSlots, barrier, apply a pending rescale,
-  // load K(t+kSlots) and V(t+kSlots-2), O += P(t-1) V(t-1), softmax of tile t
-  // with the scores of tile t+1 computed into S as its blocks free up.  The
-  // scores computed by the last iteration (of a clamped copy of the last
-  // tile) are not used.
+  // V operands of the next product, read ahead of its barrier (all four; two
+  // when the LSE sum needs the registers, the other two after the barrier).
+  constexpr int kPre = LSE ? 2 : 4;
+  v8i vf[4];
+#pragma unroll
+  for (int db = 0; db < kPre; db++) vf[db] = lds_read32(smem + kVRing + db * 2048, voff[0], voff[1]);
+  // Iteration t (S holds tile t's scores, P tile t-1's probabilities, vf the
+  // V(t-1) operands): wait for the loads of iteration t-2, barrier, apply a
+  // pending rescale, load K(t+kSlots) and V(t+kSlots-2), O += P(t-1) V(t-1),
+  // softmax of tile t with the scores of tile t+1 computed into S as its
+  // blocks free up, and V(t) read into vf.  The scores computed by the last
+  // iteration (of a clamped copy of the last tile) are not used.
   //
   // The body is laid out as nine slots, each one matrix product plus about a
   // ninth of the vector work, with the LDS reads of later products' operands
-  // issued one or two slots ahead; scheduling fences keep the compiler from
-  // merging the slots.
+  // issued one or more slots ahead; scheduling fences keep the compiler from
+  // merging the slots.  The two score chains are interleaved (first halves of
+  // both 32-key blocks, then the second halves) so neither waits on the
+  // other's accumulator.
   auto iter = [&](int t, auto ph_c) __attribute__((always_inline)) {
     constexpr int PH = decltype(ph_c)::value;   // t % kSlots
-    wait_vmcnt<kLoadsPerIter * (kSlots - 2)>();
+    wait_vmcnt<kLoadsPerIter>();
     barrier();
     rescale();
     load_k(t + kSlots, PH);
     load_v(t + kSlots - 2, (PH + kSlots - 2) % kSlots);
-    const uint8_t* vb = smem + kVRing + ((PH + kSlots - 1) % kSlots) * kTile;   // V(t-1)
-    const uint8_t* kb = smem + ((PH + 1) % kSlots) * kTile;                     // K(t+1)
+    const uint8_t* vn = smem + kVRing + PH * kTile;                  // V(t), read for the next iteration
+    const uint8_t* kb = smem + ((PH + 1) % kSlots) * kTile;          // K(t+1)
     const int kbase = t * kBN;
-    v8i vf[4], kf[2][2], Pn;
-    vf[0] = lds_read32(vb + 0 * 2048, voff[0], voff[1]);
-    vf[1] = lds_read32(vb + 1 * 2048, voff[0], voff[1]);
-    vf[2] = lds_read32(vb + 2 * 2048, voff[0], voff[1]);
+    v8i kf[2][2], Pn;
+    if (LSE) {
+      const uint8_t* vp = smem + kVRing + ((PH + kSlots - 1) % kSlots) * kTile;   // V(t-1)
+      vf[2] = lds_read32(vp + 2 * 2048, voff[0], voff[1]);
+      vf[3] = lds_read32(vp + 3 * 2048, voff[0], voff[1]);
+    }
+    kf[0][0] = lds_read32(kb, koff[0][0], koff[0][1]);
+    kf[1][0] = lds_read32(kb + 4096, koff[0][0], koff[0][1]);
     fence();
     O[0] = mfma_fp8(vf[0], P, O[0]);
-    vf[3] = lds_read32(vb + 3 * 2048, voff[0], voff[1]);
-    fence();
-    O[1] = mfma_fp8(vf[1], P, O[1]);
-    kf[0][0] = lds_read32(kb, koff[0][0], koff[0][1]);
+    kf[0][1] = lds_read32(kb, koff[1][0], koff[1][1]);
     rowmax_update(std::false_type{});
     fence();
-    O[2] = mfma_fp8(vf[2], P, O[2]);
-    kf[0][1] = lds_read32(kb, koff[1][0], koff[1][1]);
+    O[1] = mfma_fp8(vf[1], P, O[1]);
+    kf[1][1] = lds_read32(kb + 4096, koff[1][0], koff[1][1]);
     Pn[0] = probs4(0, 0, kbase);
     fence();
-    O[3] = mfma_fp8(vf[3], P, O[3]);
-    kf[1][0] = lds_read32(kb + 4096, koff[0][0], koff[0][1]);
+    O[2] = mfma_fp8(vf[2], P, O[2]);
     Pn[1] = probs4(0, 1, kbase);
     fence();
-    lacc = mfma16_fp8(sel, P, lacc);
-    kf[1][1] = lds_read32(kb + 4096, koff[1][0], koff[1][1]);
+    O[3] = mfma_fp8(vf[3], P, O[3]);
     Pn[2] = probs4(0, 2, kbase);
     fence();
+    lacc = mfma16_fp8(sel, P, lacc);
+    vf[0] = lds_read32(vn + 0 * 2048, voff[0], voff[1]);
+    vf[1] = lds_read32(vn + 1 * 2048, voff[0], voff[1]);
     Pn[3] = probs4(0, 3, kbase);
-    const v16f s0 = mfma_fp8_scaled(kf[0][0], qf[0], NB, c_e8m0);
     fence();
-    S[0] = mfma_fp8_scaled(kf[0][1], qf[1], s0, c_e8m0);
+    const v16f s0 = mfma_fp8_scaled(kf[0][0], qf[0], NB, c_e8m0);
     Pn[4] = probs4(1, 0, kbase);
     fence();
-    Pn[5] = probs4(1, 1, kbase);
     const v16f s1 = mfma_fp8_scaled(kf[1][0], qf[0], NB, c_e8m0);
+    if (!LSE) {
+      vf[2] = lds_read32(vn + 2 * 2048, voff[0], voff[1]);
+      vf[3] = lds_read32(vn + 3 * 2048, voff[0], voff[1]);
+    }
+    Pn[5] = probs4(1, 1, kbase);
     fence();
+    S[0] = mfma_fp8_scaled(kf[0][1], qf[1], s0, c_e8m0);
     Pn[6] = probs4(1, 2, kbase);
+    fence();
     Pn[7] = probs4(1, 3, kbase);
     S[1] = mfma_fp8_scaled(kf[1][1], qf[1], s1, c_e8m0);
     P = Pn;
     keep(P);
     keep(S[0]);   // the next tile's score products stay in this iteration
     keep(S[1]);
+#pragma unroll
+    for (int db = 0; db < kPre; db++) keep(vf[db]);
   };
   // Unrolled by the ring depth so that every slot address is static.
   static_assert(kSlots == 4, "unrolled for four slots");
@@ -498,7 +509,14 @@ __global__ __launch_bounds__(64 * kWavesWG, 8 / kWavesWG) void k_attn(AttentionA
       }
       msel[w] = sel_lane ? word : 0;
     }
-    pv((nkt - 1) % kSlots, msel);
+    if (LSE) {
+      const uint8_t* vp = smem + kVRing + ((nkt - 1) % kSlots) * kTile;
+      vf[2] = lds_read32(vp + 2 * 2048, voff[0], voff[1]);
+      vf[3] = lds_read32(vp + 3 * 2048, voff[0], voff[1]);
+    }
+#pragma unroll
+    for (int db = 0; db < 4; db++) O[db] = mfma_fp8(vf[db], P, O[db]);
+    lacc = mfma16_fp8(msel, P, lacc);
   }
 
   // epilogue: lane l holds O^T for query l%32, channels
@@ -524,6 +542,15 @@ __global__ __launch_bounds__(64 * kWavesWG, 8 / kWavesWG) void k_attn(AttentionA
       }
   }
   if (LSE) {
+    // The padded keys of the last tile have zero codes, so their scores are
+    // exactly 0 and each added exp2(nb) in the final frame: remove them.
+    int npad = 0;
+#pragma unroll
+    for (int kb = 0; kb < 2; kb++)
+#pragma unroll
+      for (int r = 0; r < 16; r++)
+        npad += (nkt - 1) * kBN + 32 * kb + 8 * (r >> 2) + 4 * lg + (r & 3) >= L;
+    lex -= (float)npad * __builtin_amdgcn_exp2f(nb);
     const float le = sum_pair32(lex);
     if (lg == 0 && qrow < L) {
       const float lse2 = __log2f(le) - nb;
