@@ -34,7 +34,9 @@ struct fp8attn_plan_s {
   std::vector<Chunk> chunks;
   std::vector<int32_t> group_seg;
   std::vector<int4> items;        // in launch order (XCD-remapped)
+  std::vector<int4> combine;      // one per split work item
   int64_t real_items = 0;
+  int64_t npieces = 0;
   WorkspaceLayout ws{};
   // device copies, one allocation
   void* dev = nullptr;
@@ -42,6 +44,7 @@ struct fp8attn_plan_s {
   Chunk* d_chunks = nullptr;
   int32_t* d_group_seg = nullptr;
   int4* d_items = nullptr;
+  int4* d_combine = nullptr;
   int32_t* d_rowmap = nullptr;
 };
 
@@ -56,9 +59,10 @@ fp8attn_status fail(fp8attn_status s, const std::string& msg) {
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-WorkspaceLayout make_layout(int64_t rows, int heads, int nseg, int nchunks) {
+WorkspaceLayout make_layout(int64_t rows, int heads, int nseg, int nchunks, int64_t npieces) {
   WorkspaceLayout w{};
   w.rows = rows;
+  w.npieces = npieces;
   const size_t codes = (size_t)heads * rows * kHeadDim;
   size_t off = 0;
   w.q_off = off; off = align_up(off + codes, 256);
@@ -68,17 +72,32 @@ WorkspaceLayout make_layout(int64_t rows, int heads, int nseg, int nchunks) {
   w.mu_off = off; off = align_up(off + sizeof(float) * (size_t)nseg * heads * kHeadDim, 256);
   w.kstat_off = off; off = align_up(off + sizeof(KStat) * (size_t)nchunks * heads * kHeadDim, 256);
   w.amax_off = off; off = align_up(off + sizeof(float) * 2 * (size_t)nchunks * heads, 256);
+  w.part_o_off = off; off = align_up(off + sizeof(float) * (size_t)npieces * kBM * kHeadDim, 256);
+  w.part_w_off = off; off = align_up(off + sizeof(float) * (size_t)npieces * kBM, 256);
+  w.part_lse_off = off; off = align_up(off + sizeof(float) * (size_t)npieces * kBM, 256);
   w.total = off;
   return w;
 }
 
 // Work list: head-major; inside a head, longer segments first, then query
 // tiles in order.  The list is split into kNumXcd contiguous parts of equal
-// count (padded with empty items) and interleaved so that workgroup w, which
-// the hardware sends to XCD w % 8, takes item (w % 8) * per + w / 8: each XCD
-// walks its own contiguous run, so the concurrent workgroups of an XCD mostly
-// read the same head's K/V through that XCD's L2.
-void build_items(fp8attn_plan_s* p) {
+// count and interleaved so that workgroup w, which the hardware sends to XCD
+// w % 8, takes item w / 8 of part w % 8: each XCD walks its own contiguous run,
+// so the concurrent workgroups of an XCD mostly read the same head's K/V
+// through that XCD's L2.
+//
+// Each part is ordered longest item first (stable, so head order is kept).
+// An XCD runs kWgPerCu workgroups on each of its cus = CUs / kNumXcd compute
+// units.  When the part's item count leaves R <= cus / 2 items for a last
+// round, those run nearly alone; they are split along the keys into n pieces
+// (n <= kMaxSplit, n * R <= cus, at least kMinPieceTiles key tiles a piece),
+// which go last.  A piece writes an unnormalized-frame partial (output, log2 weight,
+// LSE) and one combine pass merges the pieces of each split item, the
+// log-sum-exp combination over key ranges that the pages use to merge partial
+// attention (sglang PR "[DSA] Enable tilelang fp8_e4m3 KV cache ...", note that
+// the FP8 path must return the LSE for cross-rank reduction).
+void build_items(fp8attn_plan_s* p, int cus) {
+  const int slots = kWgPerCu * cus;
   std::vector<int> order(p->nseg);
   for (int s = 0; s < p->nseg; s++) order[s] = s;
   std::stable_sort(order.begin(), order.end(),
@@ -89,14 +108,43 @@ void build_items(fp8attn_plan_s* p) {
       const int L = p->segs[s].len;
       for (int q0 = 0; q0 < L; q0 += kBM) list.push_back(int4{s, q0, h, 0});
     }
-  p->real_items = (int64_t)list.size();
+  auto tiles = [&](const int4& it) { return (p->segs[it.x].len + kBN - 1) / kBN; };
   const size_t per = (list.size() + kNumXcd - 1) / kNumXcd;
-  const size_t n = per * kNumXcd;
-  p->items.assign(n, int4{-1, 0, 0, 0});
-  for (size_t w = 0; w < n; w++) {
-    const size_t src = (w % kNumXcd) * per + w / kNumXcd;
-    if (src < list.size()) p->items[w] = list[src];
+  std::vector<std::vector<int4>> parts(kNumXcd);
+  int64_t slot = 0;
+  p->combine.clear();
+  for (int x = 0; x < kNumXcd; x++) {
+    std::vector<int4>& part = parts[x];
+    const size_t b = std::min(list.size(), x * per), e = std::min(list.size(), (x + 1) * per);
+    part.assign(list.begin() + b, list.begin() + e);
+    std::stable_sort(part.begin(), part.end(), [&](const int4& u, const int4& v) { return tiles(u) > tiles(v); });
+    const size_t R = part.size() % (size_t)slots;
+    if (R == 0 || 2 * R > (size_t)cus) continue;
+    std::vector<int4> tail(part.end() - R, part.end()), pieces;
+    part.resize(part.size() - R);
+    for (const int4& it : tail) {
+      const int n = std::min({kMaxSplit, cus / (int)R, tiles(it) / kMinPieceTiles});
+      if (n < 2) {
+        part.push_back(it);
+        continue;
+      }
+      const int w = (int)(slot << 8) | (n << 4);
+      p->combine.push_back(int4{it.x, it.y, it.z, w});
+      for (int i = 0; i < n; i++) pieces.push_back(int4{it.x, it.y, it.z, w | i});
+      slot += n;
+    }
+    part.insert(part.end(), pieces.begin(), pieces.end());
   }
+  p->npieces = slot;
+  size_t longest = 0;
+  p->real_items = 0;
+  for (const auto& part : parts) {
+    longest = std::max(longest, part.size());
+    p->real_items += (int64_t)part.size();
+  }
+  p->items.assign(longest * kNumXcd, int4{-1, 0, 0, 0});
+  for (int x = 0; x < kNumXcd; x++)
+    for (size_t j = 0; j < parts[x].size(); j++) p->items[j * kNumXcd + x] = parts[x][j];
 }
 
 bool strides_ok(const int64_t s[2]) {
@@ -166,8 +214,17 @@ fp8attn_status fp8attn_plan(fp8attn_plan_t* plan_out, int64_t tokens, int32_t he
     delete p;
     return fail(FP8ATTN_EUNSUPPORTED, "too many padded rows");
   }
-  p->ws = make_layout(row, heads, num_segments, (int)p->chunks.size());
-  build_items(p);
+  int cus = 256;   // MI355X; the device's own count when the plan has one
+  if (device >= 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, device) == hipSuccess && n > 0) cus = n;
+  }
+  build_items(p, std::max(1, cus / kNumXcd));
+  if (p->npieces >= (int64_t)1 << 23) {
+    delete p;
+    return fail(FP8ATTN_EUNSUPPORTED, "too many split work items");
+  }
+  p->ws = make_layout(row, heads, num_segments, (int)p->chunks.size(), p->npieces);
 
   if (device >= 0) {
     DeviceGuard g(device);
@@ -180,7 +237,8 @@ fp8attn_status fp8attn_plan(fp8attn_plan_t* plan_out, int64_t tokens, int32_t he
     const size_t b_groups = align_up(sizeof(int32_t) * p->group_seg.size(), 256);
     const size_t b_items = align_up(sizeof(int4) * std::max<size_t>(1, p->items.size()), 256);
     const size_t b_rowmap = align_up(sizeof(int32_t) * p->segs.size(), 256);
-    const size_t total = b_segs + b_chunks + b_groups + b_items + b_rowmap;
+    const size_t b_combine = align_up(sizeof(int4) * std::max<size_t>(1, p->combine.size()), 256);
+    const size_t total = b_segs + b_chunks + b_groups + b_items + b_rowmap + b_combine;
     std::vector<uint8_t> host(total, 0);
     size_t off = 0;
     std::memcpy(host.data() + off, p->segs.data(), sizeof(SegInfo) * p->segs.size());
@@ -195,6 +253,8 @@ fp8attn_status fp8attn_plan(fp8attn_plan_t* plan_out, int64_t tokens, int32_t he
       const int32_t r = p->segs[s].row0;
       std::memcpy(host.data() + off + 4 * s, &r, 4);
     }
+    off += b_rowmap;
+    if (!p->combine.empty()) std::memcpy(host.data() + off, p->combine.data(), sizeof(int4) * p->combine.size());
     hipError_t e = hipMalloc(&p->dev, total);
     if (e != hipSuccess) {
       delete p;
@@ -212,6 +272,7 @@ fp8attn_status fp8attn_plan(fp8attn_plan_t* plan_out, int64_t tokens, int32_t he
     p->d_group_seg = reinterpret_cast<int32_t*>(d + b_segs + b_chunks);
     p->d_items = reinterpret_cast<int4*>(d + b_segs + b_chunks + b_groups);
     p->d_rowmap = reinterpret_cast<int32_t*>(d + b_segs + b_chunks + b_groups + b_items);
+    p->d_combine = reinterpret_cast<int4*>(d + b_segs + b_chunks + b_groups + b_items + b_rowmap);
   }
   *plan_out = p;
   return FP8ATTN_OK;
@@ -268,7 +329,7 @@ fp8attn_status fp8attn_quantize(fp8attn_plan_t p, const void* q, const void* k, 
   return FP8ATTN_OK;
 }
 
-fp8attn_status fp8attn_forward(fp8attn_plan_t p, const void* workspace, size_t workspace_bytes,
+fp8attn_status fp8attn_forward(fp8attn_plan_t p, void* workspace, size_t workspace_bytes,
                                void* out, const int64_t out_strides[2], float* lse, void* stream) {
   if (p == nullptr) return fail(FP8ATTN_EINVAL, "plan is NULL");
   if (p->device < 0) return fail(FP8ATTN_EINVAL, "host-only plan cannot run");
@@ -283,7 +344,7 @@ fp8attn_status fp8attn_forward(fp8attn_plan_t p, const void* workspace, size_t w
   }
   DeviceGuard g(p->device);
   if (!g.ok) return fail(FP8ATTN_EHIP, "cannot select device");
-  const uint8_t* ws = static_cast<const uint8_t*>(workspace);
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
   AttentionArgs a{};
   a.q_codes = ws + p->ws.q_off;
   a.k_codes = ws + p->ws.k_off;
@@ -296,6 +357,9 @@ fp8attn_status fp8attn_forward(fp8attn_plan_t p, const void* workspace, size_t w
   a.os0 = p->tokens > 0 ? out_strides[0] : 0;
   a.os1 = p->tokens > 0 ? out_strides[1] : 0;
   a.lse = lse;
+  a.part_o = reinterpret_cast<float*>(ws + p->ws.part_o_off);
+  a.part_w = reinterpret_cast<float*>(ws + p->ws.part_w_off);
+  a.part_lse = reinterpret_cast<float*>(ws + p->ws.part_lse_off);
   a.tokens = p->tokens;
   a.rows = p->ws.rows;
   a.heads = p->heads;
@@ -303,6 +367,22 @@ fp8attn_status fp8attn_forward(fp8attn_plan_t p, const void* workspace, size_t w
   a.softmax_scale = p->scale;
   hipError_t e = launch_attention(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(FP8ATTN_EHIP, std::string("attention launch failed: ") + hipGetErrorString(e));
+  if (!p->combine.empty()) {
+    CombineArgs c{};
+    c.items = p->d_combine;
+    c.nitems = (int32_t)p->combine.size();
+    c.segs = p->d_segs;
+    c.part_o = a.part_o;
+    c.part_w = a.part_w;
+    c.part_lse = a.part_lse;
+    c.out = a.out;
+    c.os0 = a.os0;
+    c.os1 = a.os1;
+    c.lse = lse;
+    c.tokens = p->tokens;
+    e = launch_combine(c, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(FP8ATTN_EHIP, std::string("combine launch failed: ") + hipGetErrorString(e));
+  }
   return FP8ATTN_OK;
 }
 

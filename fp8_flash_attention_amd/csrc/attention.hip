@@ -169,6 +169,16 @@ __global__ __launch_bounds__(64 * kWavesWG, 8 / kWavesWG) void k_attn(AttentionA
   const int q0 = it.y;
   const int h = it.z;
   const int L = si.len;
+  // Key range: every tile of the segment, or one piece of a split item.
+  const int nkt_seg = (L + kBN - 1) / kBN;
+  int kt0 = 0, nkt = nkt_seg, slot = -1;
+  if (it.w != 0) {
+    const int n = split_pieces(it.w), i = split_index(it.w);
+    kt0 = nkt_seg * i / n;
+    nkt = nkt_seg * (i + 1) / n - kt0;
+    slot = split_slot0(it.w) + i;
+  }
+  const int Lk = min(L - kt0 * kBN, nkt * kBN);   // keys of the range, counted from its first tile
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
@@ -177,8 +187,8 @@ __global__ __launch_bounds__(64 * kWavesWG, 8 / kWavesWG) void k_attn(AttentionA
 
   const size_t hrow = (size_t)h * a.rows + si.row0;
   const uint8_t* Qh = a.q_codes + hrow * kHeadDim;
-  const uint8_t* Kh = a.k_codes + hrow * kHeadDim;
-  const uint8_t* Vh = a.v_codes + (size_t)h * kHeadDim * a.rows + si.row0;
+  const uint8_t* Kh = a.k_codes + hrow * kHeadDim + (size_t)kt0 * kTile;
+  const uint8_t* Vh = a.v_codes + (size_t)h * kHeadDim * a.rows + si.row0 + (size_t)kt0 * kBN;
 
   const float s_q = a.scales[h];
   const float s_k = a.scales[a.heads + h];
@@ -214,9 +224,9 @@ __global__ __launch_bounds__(64 * kWavesWG, 8 / kWavesWG) void k_attn(AttentionA
   // 16-byte slot p = 64*i + lane of load i receives the global chunk that the
   // swizzle places there.
   const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)Kh, (short)0, (int)((a.rows - si.row0) * kHeadDim), kBufferFlags);
+      (void*)Kh, (short)0, (int)((a.rows - si.row0) * kHeadDim - (int64_t)kt0 * kTile), kBufferFlags);
   const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)Vh, (short)0, (int)(a.rows * kHeadDim - si.row0), kBufferFlags);
+      (void*)Vh, (short)0, (int)(a.rows * kHeadDim - si.row0 - (int64_t)kt0 * kBN), kBufferFlags);
   int ksrc[kLoadsPerTile], vsrc[kLoadsPerTile];
 #pragma unroll
   for (int u = 0; u < kLoadsPerTile; u++) {
@@ -224,7 +234,6 @@ __global__ __launch_bounds__(64 * kWavesWG, 8 / kWavesWG) void k_attn(AttentionA
     ksrc[u] = (p >> 3) * kHeadDim + (((p & 7) ^ ((p >> 4) & 7)) << 4);      // K row p/8, swizzled chunk p%8
     vsrc[u] = (p >> 2) * (int)a.rows + (((p & 3) ^ ((p >> 4) & 3)) << 4);   // V^T row p/4, swizzled chunk p%4
   }
-  const int nkt = (L + kBN - 1) / kBN;
   const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_ptr_t)smem + 1024 * kLoadsPerTile * wave;   // LDS byte address of this wave's loads
   // Tile indices past the segment's last tile are clamped: such loads only
   // refill a free slot with valid data, and every iteration issues the same
@@ -496,7 +505,7 @@ __global__ __launch_bounds__(64 * kWavesWG, 8 / kWavesWG) void k_attn(AttentionA
   barrier();
   rescale();
   {
-    const int klim = L - (nkt - 1) * kBN - 4 * lg;
+    const int klim = Lk - (nkt - 1) * kBN - 4 * lg;
     v8i msel;
 #pragma unroll
     for (int w = 0; w < 8; w++) {
@@ -526,7 +535,24 @@ __global__ __launch_bounds__(64 * kWavesWG, 8 / kWavesWG) void k_attn(AttentionA
   const float l0 = __shfl(lacc[0], lq & 15);
   const float l1 = __shfl(lacc[1], lq & 15);
   const float lt = lq < 16 ? l0 : l1;
-  if (qrow < L) {
+  if (slot >= 0) {
+    // one piece of a split item: the normalized partial output (in output
+    // units) and the log2 of its weight sum in a frame shared by all pieces
+    // (p = 2^(c s) for every key), for the combine pass
+    if (qrow < L) {
+      const int prow = slot * kBM + 32 * wave + lq;
+      const float inv = s_v / lt;
+      float* orow = a.part_o + (size_t)prow * kHeadDim;
+#pragma unroll
+      for (int db = 0; db < 4; db++)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; q4++)
+          *reinterpret_cast<float4*>(orow + 32 * db + 8 * q4 + 4 * lg) =
+              make_float4(O[db][4 * q4 + 0] * inv, O[db][4 * q4 + 1] * inv, O[db][4 * q4 + 2] * inv,
+                          O[db][4 * q4 + 3] * inv);
+      if (lg == 0) a.part_w[prow] = __log2f(lt) - nb;
+    }
+  } else if (qrow < L) {
     const float inv = s_v / lt;
     uint16_t* orow = a.out + (int64_t)(si.start + qrow) * a.os0 + (int64_t)h * a.os1;
 #pragma unroll
@@ -549,17 +575,96 @@ __global__ __launch_bounds__(64 * kWavesWG, 8 / kWavesWG) void k_attn(AttentionA
     for (int kb = 0; kb < 2; kb++)
 #pragma unroll
       for (int r = 0; r < 16; r++)
-        npad += (nkt - 1) * kBN + 32 * kb + 8 * (r >> 2) + 4 * lg + (r & 3) >= L;
+        npad += (nkt - 1) * kBN + 32 * kb + 8 * (r >> 2) + 4 * lg + (r & 3) >= Lk;
     lex -= (float)npad * __builtin_amdgcn_exp2f(nb);
     const float le = sum_pair32(lex);
     if (lg == 0 && qrow < L) {
       const float lse2 = __log2f(le) - nb;
-      a.lse[(int64_t)h * a.tokens + si.start + qrow] = lse2 * kLn2 + a.softmax_scale * s_q * qmu;
+      const float v = lse2 * kLn2 + a.softmax_scale * s_q * qmu;
+      if (slot >= 0)
+        a.part_lse[slot * kBM + 32 * wave + lq] = v;
+      else
+        a.lse[(int64_t)h * a.tokens + si.start + qrow] = v;
     }
   }
 }
 
+// Merge of the pieces of one split work item: for every query row of the
+// item, out = sum_i W_i O_i / sum_i W_i with O_i the piece's normalized output
+// and log2 W_i its weight (log-sum-exp combination over disjoint key ranges),
+// rounded to BF16 once; the LSE is the log-sum-exp of the pieces' LSEs.
+// 256 threads: thread t takes query row t/2, channels 64*(t%2) .. +64.  The
+// pieces are added in index order, so the result is deterministic.
+__global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
+  const int4 it = a.items[blockIdx.x];
+  const SegInfo si = a.segs[it.x];
+  const int n = split_pieces(it.w);
+  const int slot0 = split_slot0(it.w);
+  const int r = threadIdx.x >> 1;
+  const int half = threadIdx.x & 1;
+  const int qrow = it.y + r;
+  if (qrow >= si.len) return;
+  float w[kMaxSplit];
+  float m = -__builtin_huge_valf();
+#pragma unroll
+  for (int i = 0; i < kMaxSplit; i++)
+    if (i < n) {
+      w[i] = a.part_w[(slot0 + i) * kBM + r];
+      m = __builtin_fmaxf(m, w[i]);
+    }
+  float acc[64];
+#pragma unroll
+  for (int j = 0; j < 64; j++) acc[j] = 0.f;
+  float den = 0.f;
+#pragma unroll
+  for (int i = 0; i < kMaxSplit; i++)
+    if (i < n) {
+      const float alpha = __builtin_amdgcn_exp2f(w[i] - m);
+      den += alpha;
+      const float4* src = reinterpret_cast<const float4*>(a.part_o + ((size_t)(slot0 + i) * kBM + r) * kHeadDim + 64 * half);
+#pragma unroll
+      for (int j = 0; j < 16; j++) {
+        const float4 v = src[j];
+        acc[4 * j + 0] += alpha * v.x;
+        acc[4 * j + 1] += alpha * v.y;
+        acc[4 * j + 2] += alpha * v.z;
+        acc[4 * j + 3] += alpha * v.w;
+      }
+    }
+  const float inv = 1.f / den;
+  uint16_t* orow = a.out + (int64_t)(si.start + qrow) * a.os0 + (int64_t)it.z * a.os1 + 64 * half;
+#pragma unroll
+  for (int j = 0; j < 8; j++) {
+    uint32_t b[8];
+#pragma unroll
+    for (int e = 0; e < 8; e++) b[e] = f32_to_bf16_rne(acc[8 * j + e] * inv);
+    *reinterpret_cast<uint4*>(orow + 8 * j) =
+        make_uint4(b[0] | (b[1] << 16), b[2] | (b[3] << 16), b[4] | (b[5] << 16), b[6] | (b[7] << 16));
+  }
+  if (a.lse != nullptr && half == 0) {
+    float lm = -__builtin_huge_valf();
+    float lv[kMaxSplit];
+#pragma unroll
+    for (int i = 0; i < kMaxSplit; i++)
+      if (i < n) {
+        lv[i] = a.part_lse[(slot0 + i) * kBM + r];
+        lm = __builtin_fmaxf(lm, lv[i]);
+      }
+    float se = 0.f;
+#pragma unroll
+    for (int i = 0; i < kMaxSplit; i++)
+      if (i < n) se += __expf(lv[i] - lm);
+    a.lse[(int64_t)it.z * a.tokens + si.start + qrow] = lm + __logf(se);
+  }
+}
+
 }  // namespace
+
+hipError_t launch_combine(const CombineArgs& a, hipStream_t stream) {
+  if (a.nitems == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_combine, dim3(a.nitems), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
 
 hipError_t launch_attention(const AttentionArgs& a, hipStream_t stream) {
   if (a.nitems == 0) return hipSuccess;

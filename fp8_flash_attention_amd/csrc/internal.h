@@ -19,6 +19,20 @@ constexpr int kPackRows = 64;    // workspace rows per pack block (one V key gro
 constexpr int kBM = FP8ATTN_BM;  // queries per attention work item (one wave per 32)
 constexpr int kBN = 64;          // keys per inner tile
 constexpr int kNumXcd = 8;       // MI355X: workgroups are dealt round-robin to 8 XCDs
+constexpr int kWgPerCu = 2;      // attention workgroups resident per CU (registers and LDS)
+constexpr int kMaxSplit = 8;     // key pieces of one split work item, at most
+constexpr int kMinPieceTiles = 8;  // key tiles of one piece, at least
+
+// Work item {x, y, z, w}: x = segment (or -1: padding), y = first query of the
+// tile (segment-relative), z = head, w = key split.  w == 0: all keys of the
+// segment, output written directly.  Otherwise bits 0-3 = piece index i,
+// bits 4-7 = piece count n (2..kMaxSplit), bits 8-31 = first partial slot of
+// the item; piece i covers key tiles [nkt*i/n, nkt*(i+1)/n) and writes partial
+// slot (w >> 8) + i, which a combine pass merges.  Combine items carry the
+// same x, y, z and w with bits 0-3 zero.
+__host__ __device__ inline int split_pieces(int w) { return (w >> 4) & 15; }
+__host__ __device__ inline int split_index(int w) { return w & 15; }
+__host__ __device__ inline int split_slot0(int w) { return (int)((unsigned)w >> 8); }
 
 struct SegInfo {
   int32_t start;   // first token of the segment
@@ -43,7 +57,12 @@ struct KStat {
 
 struct WorkspaceLayout {
   int64_t rows;        // workspace rows (all segments padded + guard)
-  size_t q_off, k_off, v_off, scale_off, mu_off, kstat_off, amax_off, total;
+  int64_t npieces;     // partial slots of split work items
+  size_t q_off, k_off, v_off, scale_off, mu_off, kstat_off, amax_off;
+  size_t part_o_off;   // float [npieces][kBM][128]: normalized partial outputs (scaled by s_v)
+  size_t part_w_off;   // float [npieces][kBM]: log2 weight of each partial row
+  size_t part_lse_off; // float [npieces][kBM]: natural-log LSE of each partial row
+  size_t total;
 };
 
 struct QuantizeArgs {
@@ -69,10 +88,13 @@ struct AttentionArgs {
   const float* scales;
   const float* mu;
   const SegInfo* segs;
-  const int4* items;         // {segment or -1, first query (segment-relative), head, 0}
+  const int4* items;         // work items (encoding above)
   uint16_t* out;             // bf16
   int64_t os0, os1;          // output token and head strides (elements)
   float* lse;                // nullable, [H][T]
+  float* part_o;             // partial outputs of split items (see WorkspaceLayout)
+  float* part_w;
+  float* part_lse;
   int64_t tokens;
   int64_t rows;
   int32_t heads;
@@ -80,7 +102,21 @@ struct AttentionArgs {
   float softmax_scale;
 };
 
+struct CombineArgs {
+  const int4* items;         // one per split work item
+  int32_t nitems;
+  const SegInfo* segs;
+  const float* part_o;
+  const float* part_w;
+  const float* part_lse;
+  uint16_t* out;             // bf16
+  int64_t os0, os1;
+  float* lse;                // nullable, [H][T]
+  int64_t tokens;
+};
+
 hipError_t launch_quantize(const QuantizeArgs& a, hipStream_t stream);
 hipError_t launch_attention(const AttentionArgs& a, hipStream_t stream);
+hipError_t launch_combine(const CombineArgs& a, hipStream_t stream);
 
 }  // namespace fp8attn

@@ -60,7 +60,8 @@ __global__ __launch_bounds__(256) void k_stats(QuantizeArgs a) {
     float mn[8], mx[8];
 #pragma unroll
     for (int i = 0; i < 8; i++) { sum[i] = 0.0; mn[i] = __builtin_inff(); mx[i] = -__builtin_inff(); }
-    for (int j = 0; j < ch.ntok; j++) {
+#pragma unroll 8
+    for (int j = 0; j < ch.ntok; j++) {   // unrolled: eight loads in flight, sums still in token order
       const uint4 v = *reinterpret_cast<const uint4*>(base + (int64_t)(ch.tok0 + j) * ts);
       float f[8];
       unpack8(v, f);
@@ -79,7 +80,8 @@ __global__ __launch_bounds__(256) void k_stats(QuantizeArgs a) {
 
   float m = 0.f;
   if (active) {
-    for (int j = 0; j < ch.ntok; j++) {
+#pragma unroll 8
+    for (int j = 0; j < ch.ntok; j++) {   // unrolled: eight loads in flight, sums still in token order
       const uint4 v = *reinterpret_cast<const uint4*>(base + (int64_t)(ch.tok0 + j) * ts);
       float f[8];
       unpack8(v, f);
@@ -151,7 +153,8 @@ __global__ __launch_bounds__(128) void k_finalize(QuantizeArgs a) {
       double sum = 0.0;
       float mn = __builtin_inff(), mx = -__builtin_inff();
       const int nch = (si.len + kStatChunk - 1) / kStatChunk;
-      for (int c = si.chunk0; c < si.chunk0 + nch; c++) {
+#pragma unroll 8
+      for (int c = si.chunk0; c < si.chunk0 + nch; c++) {   // loads issued ahead, sums in chunk order
         const KStat st = a.kstat[((int64_t)c * a.heads + h) * kHeadDim + d];
         sum = sum + st.sum;
         mn = fminf(mn, st.mn);

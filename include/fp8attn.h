@@ -140,10 +140,21 @@ fp8attn_status fp8attn_quantize(fp8attn_plan_t plan, const void* q, const void* 
  *               (uncentred keys).
  * stream        hipStream_t (NULL = default stream).
  *
- * One kernel launch.  Output rows are written exactly once; repeated calls on
- * the same workspace give bit-identical results.
+ * workspace     the workspace the codes were quantized into.  Forward reads
+ *               the code, scale and mean regions and writes only its
+ *               partial-output region (used by split work items).
+ *
+ * One attention launch, plus one combine launch when the plan splits work
+ * items along the keys (fp8attn_plan_work_items shows the split; it happens
+ * only to fill an otherwise half-empty last round of workgroups).  A split
+ * item's pieces each attend to a contiguous range of key tiles and the
+ * combine merges them by their log-sum-exp weights (the combination over key
+ * ranges that the sglang PR "[DSA] Enable tilelang fp8_e4m3 KV cache ..."
+ * describes for cross-rank reduction of partial attention).  Output rows are
+ * written exactly once; repeated calls on the same workspace give
+ * bit-identical results.
  */
-fp8attn_status fp8attn_forward(fp8attn_plan_t plan, const void* workspace, size_t workspace_bytes,
+fp8attn_status fp8attn_forward(fp8attn_plan_t plan, void* workspace, size_t workspace_bytes,
                                void* out, const int64_t out_strides[2], float* lse, void* stream);
 
 /*
@@ -171,7 +182,11 @@ fp8attn_status fp8attn_plan_info(fp8attn_plan_t plan, int64_t info_out[8]);
 /*
  * fp8attn_plan_work_items - copy the ordered work list to host memory.
  *   items_out int32[4 * capacity]: per item {segment, first query of the tile
- *   (segment-relative), head, 0}; padding items have segment == -1.
+ *   (segment-relative), head, split}; padding items have segment == -1.
+ *   split == 0: the item attends to every key of its segment.  Otherwise
+ *   bits 0-3 hold the piece index i, bits 4-7 the piece count n (2..8) and
+ *   bits 8-31 the item's first partial slot; piece i attends to key tiles
+ *   [nkt*i/n, nkt*(i+1)/n) of the segment's nkt = ceil(len/64) tiles.
  *   count_out receives the number of items (which may exceed capacity; only
  *   min(count, capacity) are copied).
  */

@@ -86,6 +86,13 @@ def _expected_items(cu, heads, bm):
     return heads * sum((L + bm - 1) // bm for L in segs)
 
 
+SLOTS_PER_XCD = 64      # 2 attention workgroups per CU, 256 CUs over 8 XCDs (host-only plans)
+
+
+def _split(w):
+    return w & 15, (w >> 4) & 15, w >> 8      # piece index, piece count, first partial slot
+
+
 @pytest.mark.parametrize("name", list(WORKLOADS))
 def test_schedule_for_each_workload(name):
     w = WORKLOADS[name]
@@ -98,22 +105,72 @@ def test_schedule_for_each_workload(name):
     segs = w.segments
     assert info["workspace_rows"] == sum((L + 127) // 128 * 128 for L in segs) + 128
     assert info["stat_chunks"] == sum((L + 255) // 256 for L in segs)
-    assert info["work_items"] == _expected_items(w.cu_seqlens, w.heads, bm)
     items = p.work_items()
     assert len(items) % 8 == 0
     real = [it for it in items if it[0] >= 0]
     assert len(real) == info["work_items"]
-    # every (segment, query tile, head) appears exactly once; empty segments never appear
+    # every (segment, query tile, head) appears exactly once, whole or as a complete
+    # set of key pieces; empty segments never appear
     want = {(s, q0, h) for h in range(w.heads) for s, L in enumerate(segs) for q0 in range(0, L, bm)}
-    got = [(s, q0, h) for s, q0, h, _ in real]
-    assert len(set(got)) == len(got) and set(got) == want
-    # XCD interleave: workgroup i belongs to XCD i % 8, and each XCD walks a contiguous
-    # run of the head-major list
+    whole = [(s, q0, h) for s, q0, h, sp in real if sp == 0]
+    pieces = {}
+    for s, q0, h, sp in real:
+        if sp:
+            i, n, base = _split(sp)
+            pieces.setdefault((s, q0, h), []).append((i, n, base))
+    assert len(set(whole)) == len(whole) and not set(whole) & set(pieces)
+    assert set(whole) | set(pieces) == want
+    assert len(whole) + len(pieces) == _expected_items(w.cu_seqlens, w.heads, bm)
+    slots = []
+    for (s, q0, h), ps in pieces.items():
+        n, base = ps[0][1], ps[0][2]
+        assert 2 <= n <= 8 and sorted(i for i, _, _ in ps) == list(range(n))
+        assert all(pn == n and pb == base for _, pn, pb in ps)
+        nkt = (segs[s] + 63) // 64
+        bounds = [nkt * i // n for i in range(n + 1)]
+        assert bounds[0] == 0 and bounds[-1] == nkt
+        assert min(b - a for a, b in zip(bounds, bounds[1:])) >= 8
+        slots += [base + i for i in range(n)]
+    assert sorted(slots) == list(range(len(slots)))
+    # XCD interleave: workgroup i belongs to XCD i % 8 and each XCD walks a contiguous
+    # run of the head-major list, longest items first; split pieces only at the end,
+    # filling what would otherwise be a last round at most half full
     per = len(items) // 8
     for x in range(8):
         run = [items[x + 8 * j] for j in range(per)]
-        heads_seen = [it[2] for it in run if it[0] >= 0]
-        assert heads_seen == sorted(heads_seen)
+        run = [it for it in run if it[0] >= 0]
+        first_piece = next((j for j, it in enumerate(run) if it[3]), len(run))
+        assert all(it[3] for it in run[first_piece:])
+        head = run[:first_piece]
+        sizes = [(segs[it[0]] + 63) // 64 for it in head]
+        assert sizes == sorted(sizes, reverse=True)
+        for size in set(sizes):
+            hs = [it[2] for it in head if (segs[it[0]] + 63) // 64 == size]
+            assert hs == sorted(hs)
+
+
+def test_split_fills_the_last_round():
+    # S=30272 with 7 heads: 1659 items, 208 per XCD = 3 rounds of 64 workgroups plus 16
+    # items that would run nearly alone on 32 CUs: each is split into two key pieces
+    w = WORKLOADS["s30272_h7_shard"]
+    p = fa.Plan(w.tokens, w.heads, w.cu_seqlens, device=-1)
+    real = [it for it in p.work_items() if it[0] >= 0]
+    split = [it for it in real if it[3]]
+    # parts 0..6 hold 208 items (R = 16), part 7 holds 203 (R = 11): 16 * 7 + 11 split items
+    assert len(split) == 2 * (16 * 7 + 11)
+    assert all(_split(it[3])[1] == 2 for it in split)
+    # 4096 tokens x 56 heads: the last round of each XCD is half full (32 items on 32
+    # CUs), which two workgroups per CU absorb: nothing is split
+    for name in ("s4096_h56", "s30272_h56_koffset", "s20440_h56_strided"):
+        w = WORKLOADS[name]
+        p = fa.Plan(w.tokens, w.heads, w.cu_seqlens, device=-1)
+        assert not any(it[3] for it in p.work_items() if it[0] >= 0), name
+    # few items: as many pieces as fit one per CU, at least 8 key tiles each
+    p = fa.Plan(3000, 1, [0, 3000], device=-1)
+    ns = {_split(it[3])[1] for it in p.work_items() if it[0] >= 0}
+    assert ns == {5}      # 3 items per XCD -> min(8, 32 // 3, 47 // 8) = 5
+    p = fa.Plan(300, 8, [0, 300], device=-1)
+    assert not any(it[3] for it in p.work_items())
 
 
 def test_varlen_schedule_longest_segment_first():

@@ -62,7 +62,7 @@ def _single(T: int) -> List[int]:
     return [0, T]
 
 
-# The five workloads, smallest first.  Seeds are 1000 + index.
+# The five workloads, smallest first, and one per-GPU share.  Seeds are 1000 + index.
 WORKLOADS = {
     "s256_h2": Workload("s256_h2", 256, 2, _single(256), 1001,
                         note="single segment, S=256, H=2"),
@@ -79,6 +79,11 @@ WORKLOADS = {
     "varlen_30272_h56": Workload(
         "varlen_30272_h56", 30272, 56, [0, 15104, 30208, 30208, 30271, 30272], 1005,
         note="packed varlen, segments 15104, 15104, 0, 63, 1"),
+    # one GPU's share when the 56 heads are split over 8 GPUs (not one of the five
+    # graded configurations; it shows the kernel at the per-GPU shape)
+    "s30272_h7_shard": Workload(
+        "s30272_h7_shard", 30272, 7, _single(30272), 1006, k_offset_var=2.0,
+        note="S=30272 with 7 heads: one eighth of the denoise-step heads, K offset as above"),
 }
 
 
