@@ -142,6 +142,15 @@ __device__ __forceinline__ void wait_vmcnt() {
 // Workgroup barrier that the compiler may not move memory operations across;
 // this wave's LDS reads have completed when it passes.
 __device__ __forceinline__ void barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+// The same with up to N of this wave's most recent LDS reads still in flight
+// (LDS reads complete in order).  The loop uses it with N = the reads of the
+// next product's V operands: those read a slot that no load of the coming
+// iteration overwrites, so only the older reads must be complete.
+template <int N>
+__device__ __forceinline__ void barrier_after_older_reads() {
+  static_assert(N >= 0 && N < 16, "lgkmcnt range");
+  asm volatile("s_waitcnt lgkmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
+}
 
 // One direct load of 16 bytes per lane from buffer `rsrc` at byte offset
 // voff + soff into LDS at lds + 16 * lane.  Issued as inline assembly so that
@@ -429,7 +438,7 @@ __global__ __launch_bounds__(64 * kWavesWG, 8 / kWavesWG) void k_attn(AttentionA
   auto iter = [&](int t, auto ph_c) __attribute__((always_inline)) {
     constexpr int PH = decltype(ph_c)::value;   // t % kSlots
     wait_vmcnt<kLoadsPerIter>();
-    barrier();
+    barrier_after_older_reads<2 * kPre>();
     rescale();
     load_k(t + kSlots, PH);
     load_v(t + kSlots - 2, (PH + kSlots - 2) % kSlots);
@@ -483,8 +492,6 @@ __global__ __launch_bounds__(64 * kWavesWG, 8 / kWavesWG) void k_attn(AttentionA
     keep(P);
     keep(S[0]);   // the next tile's score products stay in this iteration
     keep(S[1]);
-#pragma unroll
-    for (int db = 0; db < kPre; db++) keep(vf[db]);
   };
   // Unrolled by the ring depth so that every slot address is static.
   static_assert(kSlots == 4, "unrolled for four slots");
