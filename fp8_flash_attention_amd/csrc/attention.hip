@@ -52,13 +52,14 @@
 //     the top of the next iteration, after the P V product of the older tiles
 //     and before that of the tile that moved m.
 //   * K and V^T tiles reach LDS by direct buffer loads (no register staging):
-//     a K ring and a V ring of four 8 KB slots each.  Iteration t loads K of
-//     tile t+4 and V of tile t+2; it reads K of tile t+1 for its score
-//     products, and V of tile t for the P V product of the next iteration, so
-//     that product starts right after the barrier with its operands already
-//     in registers.  One barrier per iteration, after waiting for the loads
-//     issued two iterations earlier, keeps every slot's writes and reads
-//     apart.  16-byte chunks are XOR-swizzled against bank conflicts of the
+//     a K ring and a V ring of four 8 KB slots each.  Iteration t reads K of
+//     tile t+1 for its score products, and V of tile t for the P V product of
+//     the next iteration, so that product starts with its operands already in
+//     registers.  Barriers come every second iteration: at even t, after
+//     waiting for the loads issued at t-2, the wave passes the barrier and
+//     loads K of tiles t+3, t+4 and V of tiles t+2, t+3 for the next two
+//     iterations, into the slots whose last reads the barrier has just
+//     retired.  16-byte chunks are XOR-swizzled against bank conflicts of the
 //     operand reads; the swizzle is applied to the source addresses of the
 //     lane-linear loads.
 #include "internal.h"
@@ -76,10 +77,10 @@ constexpr float kLog2Ref = 6.807354922057604f;   // log2(112): reference maximum
 constexpr float kLog2Max = 8.807354922057604f;   // log2(448), the largest E4M3 value
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kTile = kBN * kHeadDim;            // bytes of one K (or V^T) tile
-constexpr int kSlots = 4;                        // ring slots per operand
+constexpr int kSlots = kBM == 256 ? 8 : 4;       // ring slots per operand
+constexpr int kBarEvery = kSlots / 2;            // iterations per barrier
 constexpr int kWavesWG = kBM / 32;               // waves per workgroup, 32 queries each
 constexpr int kLoadsPerTile = kTile / 1024 / kWavesWG;   // direct 1 KB loads per wave per K (or V) tile
-constexpr int kLoadsPerIter = 2 * kLoadsPerTile; // direct loads per wave per iteration
 constexpr int kVRing = kSlots * kTile;           // V ring follows the K ring in LDS
 constexpr int kBufferFlags = 0x00020000;         // raw buffer descriptor word 3 (gfx9 family)
 static_assert((kBM == 128 || kBM == 256) && kBN == 64, "4 or 8 waves x 32 queries, 64-key tiles");
@@ -142,15 +143,6 @@ __device__ __forceinline__ void wait_vmcnt() {
 // Workgroup barrier that the compiler may not move memory operations across;
 // this wave's LDS reads have completed when it passes.
 __device__ __forceinline__ void barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
-// The same with up to N of this wave's most recent LDS reads still in flight
-// (LDS reads complete in order).  The loop uses it with N = the reads of the
-// next product's V operands: those read a slot that no load of the coming
-// iteration overwrites, so only the older reads must be complete.
-template <int N>
-__device__ __forceinline__ void barrier_after_older_reads() {
-  static_assert(N >= 0 && N < 16, "lgkmcnt range");
-  asm volatile("s_waitcnt lgkmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
-}
 
 // One direct load of 16 bytes per lane from buffer `rsrc` at byte offset
 // voff + soff into LDS at lds + 16 * lane.  Issued as inline assembly so that
@@ -167,6 +159,23 @@ __device__ __forceinline__ void fence() { __builtin_amdgcn_sched_barrier(0); }
 // reads it), so the softmax of a tile is not moved into the next iteration.
 __device__ __forceinline__ void keep(const v8i& v) { asm volatile("" ::"v"(v)); }
 __device__ __forceinline__ void keep(const v16f& v) { asm volatile("" ::"v"(v)); }
+
+// iter(t + I, I + 1 mod N) for I = 0 .. N-1 (one pass over an N-slot ring).
+template <int I, int N, typename F>
+__device__ __forceinline__ void unroll_iters(F& iter, int t) {
+  if constexpr (I < N) {
+    iter(t + I, std::integral_constant<int, (I + 1) % N>{});
+    unroll_iters<I + 1, N>(iter, t);
+  }
+}
+// The remaining iterations (fewer than N - 1 after whole passes), phases P, P + 1, ...
+template <int P, int N, typename F>
+__device__ __forceinline__ void tail_iters(F& iter, int& t, int nkt) {
+  if constexpr (P < N) {
+    if (t < nkt) iter(t++, std::integral_constant<int, P>{});
+    tail_iters<P + 1, N>(iter, t, nkt);
+  }
+}
 
 template <bool LSE>
 __global__ __launch_bounds__(64 * kWavesWG, 8 / kWavesWG) void k_attn(AttentionArgs a) {
@@ -393,41 +402,42 @@ __global__ __launch_bounds__(64 * kWavesWG, 8 / kWavesWG) void k_attn(AttentionA
     qk(1);
   };
 
-  // Prologue: K(0), K(1); then K(i), V(i-2) for i = 2 .. kSlots-1, which are
-  // the loads iterations 2-kSlots .. -1 would issue.  Iteration t issues
-  // K(t+kSlots) and V(t+kSlots-2); at its top it waits for the loads of
-  // iteration t-2, which hold the K(t+2) and V(t) it may read after the
-  // barrier (K(t+1) has been readable since the previous barrier).  A slot is
-  // refilled only after the barrier that follows its last read.
+  // Prologue: K(0), then the loads an iteration -2 would issue (K(1), K(2),
+  // V(0), V(1)).  Even iteration t waits for the loads of iteration t-2, which
+  // hold the K(t+1), K(t+2) and V(t), V(t+1) that iterations t and t+1 read,
+  // passes the barrier, and issues K(t+3), K(t+4), V(t+2), V(t+3).  Slot
+  // (t+3)%4 last held K(t-1) and V(t-1), slot t%4 K(t), slot (t+2)%4 V(t-2):
+  // all read before the barrier, which waits for every LDS read of the wave.
   load_k(0, 0);
-  load_k(1, 1);
 #pragma unroll
-  for (int i = 2; i < kSlots; i++) {
-    load_k(i, i);
-    load_v(i - 2, i - 2);
-  }
-  wait_vmcnt<kLoadsPerIter * (kSlots - 2)>();
+  for (int i = 1; i <= kBarEvery; i++) load_k(i, i);
+#pragma unroll
+  for (int i = 0; i < kBarEvery; i++) load_v(i, i);
+  wait_vmcnt<2 * kBarEvery * kLoadsPerTile>();
   barrier();
   qk(0);
   // Iteration 0: reference from tile 0; nothing to add to O yet.
-  wait_vmcnt<kLoadsPerIter>();
+  wait_vmcnt<0>();
   barrier();
-  load_k(kSlots, 0);
-  load_v(kSlots - 2, kSlots - 2);
+#pragma unroll
+  for (int i = 1; i <= kBarEvery; i++) load_k(kBarEvery + i, (kBarEvery + i) % kSlots);
+#pragma unroll
+  for (int i = 0; i < kBarEvery; i++) load_v(kBarEvery + i, (kBarEvery + i) % kSlots);
   first_tile();
   keep(P);
-  // V operands of the next product, read ahead of its barrier (all four; two
-  // when the LSE sum needs the registers, the other two after the barrier).
+  // V operands of the next product, read at the end of the iteration before
+  // it (all four; two when the LSE sum needs the registers, the other two at
+  // the top of the iteration, still ahead of its barrier).
   constexpr int kPre = LSE ? 2 : 4;
   v8i vf[4];
 #pragma unroll
   for (int db = 0; db < kPre; db++) vf[db] = lds_read32(smem + kVRing + db * 2048, voff[0], voff[1]);
   // Iteration t (S holds tile t's scores, P tile t-1's probabilities, vf the
-  // V(t-1) operands): wait for the loads of iteration t-2, barrier, apply a
-  // pending rescale, load K(t+kSlots) and V(t+kSlots-2), O += P(t-1) V(t-1),
-  // softmax of tile t with the scores of tile t+1 computed into S as its
-  // blocks free up, and V(t) read into vf.  The scores computed by the last
-  // iteration (of a clamped copy of the last tile) are not used.
+  // V(t-1) operands): at even t the barrier and the loads above; a pending
+  // rescale; O += P(t-1) V(t-1), softmax of tile t with the scores of tile
+  // t+1 computed into S as its blocks free up, and V(t) read into vf.  The
+  // scores computed by the last iteration (of a clamped copy of the last
+  // tile) are not used.
   //
   // The body is laid out as nine slots, each one matrix product plus about a
   // ninth of the vector work, with the LDS reads of later products' operands
@@ -437,20 +447,28 @@ __global__ __launch_bounds__(64 * kWavesWG, 8 / kWavesWG) void k_attn(AttentionA
   // other's accumulator.
   auto iter = [&](int t, auto ph_c) __attribute__((always_inline)) {
     constexpr int PH = decltype(ph_c)::value;   // t % kSlots
-    wait_vmcnt<kLoadsPerIter>();
-    barrier_after_older_reads<2 * kPre>();
-    rescale();
-    load_k(t + kSlots, PH);
-    load_v(t + kSlots - 2, (PH + kSlots - 2) % kSlots);
-    const uint8_t* vn = smem + kVRing + PH * kTile;                  // V(t), read for the next iteration
-    const uint8_t* kb = smem + ((PH + 1) % kSlots) * kTile;          // K(t+1)
-    const int kbase = t * kBN;
-    v8i kf[2][2], Pn;
+    // With the LSE sum, two of the four V(t-1) operands are read here, before
+    // the barrier: the loads after it may refill V(t-1)'s slot.
     if (LSE) {
       const uint8_t* vp = smem + kVRing + ((PH + kSlots - 1) % kSlots) * kTile;   // V(t-1)
       vf[2] = lds_read32(vp + 2 * 2048, voff[0], voff[1]);
       vf[3] = lds_read32(vp + 3 * 2048, voff[0], voff[1]);
     }
+    if (PH % kBarEvery == 0) {
+      wait_vmcnt<0>();
+      barrier();
+    }
+    rescale();
+    if (PH % kBarEvery == 0) {
+#pragma unroll
+      for (int i = 1; i <= kBarEvery; i++) load_k(t + kBarEvery + i, (PH + kBarEvery + i) % kSlots);
+#pragma unroll
+      for (int i = 0; i < kBarEvery; i++) load_v(t + kBarEvery + i, (PH + kBarEvery + i) % kSlots);
+    }
+    const uint8_t* vn = smem + kVRing + PH * kTile;                  // V(t), read for the next iteration
+    const uint8_t* kb = smem + ((PH + 1) % kSlots) * kTile;          // K(t+1)
+    const int kbase = t * kBN;
+    v8i kf[2][2], Pn;
     kf[0][0] = lds_read32(kb, koff[0][0], koff[0][1]);
     kf[1][0] = lds_read32(kb + 4096, koff[0][0], koff[0][1]);
     fence();
@@ -494,17 +512,9 @@ __global__ __launch_bounds__(64 * kWavesWG, 8 / kWavesWG) void k_attn(AttentionA
     keep(S[1]);
   };
   // Unrolled by the ring depth so that every slot address is static.
-  static_assert(kSlots == 4, "unrolled for four slots");
   int t = 1;
-  for (; t + 3 < nkt; t += 4) {
-    iter(t, std::integral_constant<int, 1>{});
-    iter(t + 1, std::integral_constant<int, 2>{});
-    iter(t + 2, std::integral_constant<int, 3>{});
-    iter(t + 3, std::integral_constant<int, 0>{});
-  }
-  if (t < nkt) iter(t++, std::integral_constant<int, 1>{});
-  if (t < nkt) iter(t++, std::integral_constant<int, 2>{});
-  if (t < nkt) iter(t++, std::integral_constant<int, 3>{});
+  for (; t + kSlots - 1 < nkt; t += kSlots) unroll_iters<0, kSlots>(iter, t);
+  tail_iters<1, kSlots>(iter, t, nkt);
   // O += P(nkt-1) V(nkt-1) once every load has landed; the row sum counts
   // only keys before the segment end.  Selector byte b of lane 0 or 17 (32 or
   // 49) weights key 32*(b/16) + 8*((b/4)%4) + b%4 (+4) of the tile.
@@ -600,14 +610,15 @@ __global__ __launch_bounds__(64 * kWavesWG, 8 / kWavesWG) void k_attn(AttentionA
 // item, out = sum_i W_i O_i / sum_i W_i with O_i the piece's normalized output
 // and log2 W_i its weight (log-sum-exp combination over disjoint key ranges),
 // rounded to BF16 once; the LSE is the log-sum-exp of the pieces' LSEs.
-// 256 threads: thread t takes query row t/2, channels 64*(t%2) .. +64.  The
-// pieces are added in index order, so the result is deterministic.
+// 256 threads per 128 query rows (blockIdx.y picks the 128-row block of the
+// item): thread t takes row t/2, channels 64*(t%2) .. +64.  The pieces are
+// added in index order, so the result is deterministic.
 __global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
   const int4 it = a.items[blockIdx.x];
   const SegInfo si = a.segs[it.x];
   const int n = split_pieces(it.w);
   const int slot0 = split_slot0(it.w);
-  const int r = threadIdx.x >> 1;
+  const int r = 128 * blockIdx.y + (threadIdx.x >> 1);
   const int half = threadIdx.x & 1;
   const int qrow = it.y + r;
   if (qrow >= si.len) return;
@@ -669,7 +680,7 @@ __global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
 
 hipError_t launch_combine(const CombineArgs& a, hipStream_t stream) {
   if (a.nitems == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_combine, dim3(a.nitems), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(k_combine, dim3(a.nitems, kBM / 128), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

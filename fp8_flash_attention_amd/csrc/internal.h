@@ -19,7 +19,7 @@ constexpr int kPackRows = 64;    // workspace rows per pack block (one V key gro
 constexpr int kBM = FP8ATTN_BM;  // queries per attention work item (one wave per 32)
 constexpr int kBN = 64;          // keys per inner tile
 constexpr int kNumXcd = 8;       // MI355X: workgroups are dealt round-robin to 8 XCDs
-constexpr int kWgPerCu = 2;      // attention workgroups resident per CU (registers and LDS)
+constexpr int kWgPerCu = kBM == 256 ? 1 : 2;   // attention workgroups resident per CU (registers and LDS)
 constexpr int kMaxSplit = 8;     // key pieces of one split work item, at most
 constexpr int kMinPieceTiles = 8;  // key tiles of one piece, at least
 
