@@ -14,7 +14,7 @@ constexpr int kGuardRows = 128;  // zero rows after the last segment
 constexpr int kStatChunk = 256;  // tokens per stats chunk; fixes the K-mean summation order
 constexpr int kPackRows = 64;    // workspace rows per pack block (one V key group)
 #ifndef FP8ATTN_BM
-#define FP8ATTN_BM 128
+#define FP8ATTN_BM 256
 #endif
 constexpr int kBM = FP8ATTN_BM;  // queries per attention work item (one wave per 32)
 constexpr int kBN = 64;          // keys per inner tile

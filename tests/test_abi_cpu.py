@@ -86,7 +86,11 @@ def _expected_items(cu, heads, bm):
     return heads * sum((L + bm - 1) // bm for L in segs)
 
 
-SLOTS_PER_XCD = 64      # 2 attention workgroups per CU, 256 CUs over 8 XCDs (host-only plans)
+CUS_PER_XCD = 32        # host-only plans assume 256 CUs over 8 XCDs
+
+
+def _wg_per_cu(bm):
+    return 1 if bm == 256 else 2     # attention workgroups resident per CU
 
 
 def _split(w):
@@ -149,26 +153,48 @@ def test_schedule_for_each_workload(name):
             assert hs == sorted(hs)
 
 
-def test_split_fills_the_last_round():
-    # S=30272 with 7 heads: 1659 items, 208 per XCD = 3 rounds of 64 workgroups plus 16
-    # items that would run nearly alone on 32 CUs: each is split into two key pieces
-    w = WORKLOADS["s30272_h7_shard"]
+def _expected_pieces(items_in_part, tiles, bm):
+    """The documented split rule for one XCD's part of equal-length items."""
+    slots = _wg_per_cu(bm) * CUS_PER_XCD
+    r = items_in_part % slots
+    if r == 0 or 2 * r > CUS_PER_XCD:
+        return 0, 1
+    return r, min(8, CUS_PER_XCD // r, tiles // 8)
+
+
+@pytest.mark.parametrize("name", ["s30272_h7_shard", "s4096_h56", "s30272_h56_koffset", "s20440_h56_strided"])
+def test_split_fills_the_last_round(name):
+    # single-segment workloads: every XCD part holds equal items; the items of a last
+    # round that would leave at least half the XCD's CUs idle are split into as many
+    # key pieces as fit one per CU (at most 8, at least 8 key tiles each)
+    w = WORKLOADS[name]
     p = fa.Plan(w.tokens, w.heads, w.cu_seqlens, device=-1)
-    real = [it for it in p.work_items() if it[0] >= 0]
-    split = [it for it in real if it[3]]
-    # parts 0..6 hold 208 items (R = 16), part 7 holds 203 (R = 11): 16 * 7 + 11 split items
-    assert len(split) == 2 * (16 * 7 + 11)
-    assert all(_split(it[3])[1] == 2 for it in split)
-    # 4096 tokens x 56 heads: the last round of each XCD is half full (32 items on 32
-    # CUs), which two workgroups per CU absorb: nothing is split
-    for name in ("s4096_h56", "s30272_h56_koffset", "s20440_h56_strided"):
-        w = WORKLOADS[name]
-        p = fa.Plan(w.tokens, w.heads, w.cu_seqlens, device=-1)
-        assert not any(it[3] for it in p.work_items() if it[0] >= 0), name
+    bm = p.info()["query_tile"]
+    tiles = (w.tokens + 63) // 64
+    n_items = w.heads * ((w.tokens + bm - 1) // bm)
+    per = (n_items + 7) // 8
+    want = []
+    for x in range(8):
+        in_part = max(0, min(per, n_items - x * per))
+        r, n = _expected_pieces(in_part, tiles, bm)
+        want.append((r, n if r and n >= 2 else 1))
+    items = p.work_items()
+    for x in range(8):
+        run = [it for it in items[x::8] if it[0] >= 0]
+        pieces = [it for it in run if it[3]]
+        r, n = want[x]
+        if n < 2:
+            assert not pieces
+        else:
+            assert len(pieces) == r * n and {_split(it[3])[1] for it in pieces} == {n}
+
+
+def test_split_small_and_short_cases():
     # few items: as many pieces as fit one per CU, at least 8 key tiles each
     p = fa.Plan(3000, 1, [0, 3000], device=-1)
     ns = {_split(it[3])[1] for it in p.work_items() if it[0] >= 0}
-    assert ns == {5}      # 3 items per XCD -> min(8, 32 // 3, 47 // 8) = 5
+    assert ns == {5}      # <= 2 items per XCD -> min(8, 32 // 2, 47 // 8) = 5
+    # segments shorter than 16 key tiles are never split
     p = fa.Plan(300, 8, [0, 300], device=-1)
     assert not any(it[3] for it in p.work_items())
 
