@@ -138,17 +138,28 @@ def _strides(x: torch.Tensor, name: str):
     return _lib.i64_array([x.stride(0), x.stride(1)])
 
 
+def _on_plan_device(plan: Plan, x: torch.Tensor, name: str) -> None:
+    """Device pointers handed to the library must live on the plan's GPU."""
+    if plan.device_index < 0:
+        raise Fp8AttnError(_lib.EINVAL, name, "host-only plan cannot run")
+    if not x.is_cuda or x.device.index != plan.device_index:
+        raise ValueError(f"{name} must be a tensor on cuda:{plan.device_index} (got {x.device})")
+
+
 def quantize(plan: Plan, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, workspace: torch.Tensor,
              stream=None) -> None:
     """``fp8attn_quantize``: E4M3 codes and per-head scales of q, k, v into ``workspace``."""
     for name, x in (("q", q), ("k", k), ("v", v)):
         if tuple(x.shape[:2]) != (plan.tokens, plan.heads):
             raise ValueError(f"{name} shape {tuple(x.shape)} does not match the plan")
+        _on_plan_device(plan, x, name)
+    _on_plan_device(plan, workspace, "workspace")
     qs, ks, vs = _strides(q, "q"), _strides(k, "k"), _strides(v, "v")
     st = _stream_handle(plan.device, stream)
     _lib.check(_lib.lib().fp8attn_quantize(plan.handle, ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k.data_ptr()),
                                            ctypes.c_void_p(v.data_ptr()), qs, ks, vs,
-                                           ctypes.c_void_p(workspace.data_ptr()), workspace.numel(), st),
+                                           ctypes.c_void_p(workspace.data_ptr()),
+                                           workspace.numel() * workspace.element_size(), st),
                "fp8attn_quantize")
 
 
@@ -159,14 +170,18 @@ def forward(plan: Plan, workspace: torch.Tensor, out: Optional[torch.Tensor] = N
         out = torch.empty((plan.tokens, plan.heads, HEAD_DIM), dtype=torch.bfloat16, device=plan.device)
     if tuple(out.shape) != (plan.tokens, plan.heads, HEAD_DIM):
         raise ValueError("out shape does not match the plan")
+    _on_plan_device(plan, out, "out")
+    _on_plan_device(plan, workspace, "workspace")
     os_ = _strides(out, "out")
     lse_ptr = None
     if lse is not None:
         if lse.dtype != torch.float32 or tuple(lse.shape) != (plan.heads, plan.tokens) or not lse.is_contiguous():
             raise ValueError("lse must be a contiguous float32 [heads, tokens] tensor")
+        _on_plan_device(plan, lse, "lse")
         lse_ptr = ctypes.c_void_p(lse.data_ptr())
     st = _stream_handle(plan.device, stream)
-    _lib.check(_lib.lib().fp8attn_forward(plan.handle, ctypes.c_void_p(workspace.data_ptr()), workspace.numel(),
+    _lib.check(_lib.lib().fp8attn_forward(plan.handle, ctypes.c_void_p(workspace.data_ptr()),
+                                          workspace.numel() * workspace.element_size(),
                                           ctypes.c_void_p(out.data_ptr()), os_, lse_ptr, st), "fp8attn_forward")
     return out
 

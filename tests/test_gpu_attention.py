@@ -289,3 +289,21 @@ def test_split_keys_lse_and_repeat():
     err_d = np.abs(lse.cpu().double().numpy() - diag).max()
     log(f"  split lse max err vs dequantized {err_d:.5f}")
     assert err_d <= 2e-3
+
+
+def test_binding_rejects_tensors_off_the_plan_device():
+    # pointers from another device (or host memory) must never reach the kernels
+    w = WORKLOADS["s256_h2"]
+    q, k, v = generate(w, device="cuda")
+    plan = fa.Plan(w.tokens, w.heads, w.cu_seqlens, w.softmax_scale, device=0)
+    ws = plan.new_workspace()
+    with pytest.raises(ValueError):
+        fa.quantize(plan, q.cpu(), k, v, ws)
+    with pytest.raises(ValueError):
+        fa.quantize(plan, q, k, v, ws.cpu())
+    fa.quantize(plan, q, k, v, ws)
+    with pytest.raises(ValueError):
+        fa.forward(plan, ws, out=torch.empty((w.tokens, w.heads, 128), dtype=torch.bfloat16))
+    with pytest.raises(ValueError):
+        fa.forward(plan, ws, lse=torch.empty((w.heads, w.tokens), dtype=torch.float32))
+    torch.cuda.synchronize()
