@@ -210,9 +210,11 @@ fp8attn_status fp8attn_plan(fp8attn_plan_t* plan_out, int64_t tokens, int32_t he
   }
   for (int g = 0; g < kGuardRows / kPackRows; g++) p->group_seg.push_back(-1);
   row += kGuardRows;
-  if (row > (int64_t)INT32_MAX / 2) {
+  // the attention kernel addresses one head's code rows through 32-bit buffer
+  // offsets: rows * 128 bytes must fit
+  if (row * kHeadDim > (int64_t)INT32_MAX) {
     delete p;
-    return fail(FP8ATTN_EUNSUPPORTED, "too many padded rows");
+    return fail(FP8ATTN_EUNSUPPORTED, "too many padded rows for 32-bit code offsets (about 16.7M tokens at most)");
   }
   int cus = 256;   // MI355X; the device's own count when the plan has one
   if (device >= 0) {

@@ -212,6 +212,18 @@ def test_varlen_schedule_longest_segment_first():
     assert segs[:n] == [0] * n and segs[n:2 * n] == [1] * n and segs[2 * n:] == [3, 4]
 
 
+def test_plan_rejects_rows_beyond_32bit_code_offsets():
+    # one head's code rows are addressed with 32-bit byte offsets: rows * 128 < 2^31
+    ok = 16_777_087 - 127              # padded to a multiple of 128, plus 128 guard rows
+    st, h = _plan(ok, 1, [0, ok])
+    assert st == _lib.OK
+    _lib.lib().fp8attn_plan_destroy(h)
+    big = 16_777_216
+    st, h = _plan(big, 1, [0, big])
+    assert st == _lib.EUNSUPPORTED and h.value is None
+    assert "32-bit" in _lib.lib().fp8attn_last_error().decode()
+
+
 def test_empty_input_plan():
     p = fa.Plan(0, 3, [0, 0], device=-1)
     info = p.info()
