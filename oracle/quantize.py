@@ -39,6 +39,14 @@ derive the expected Q codes from the inputs alone.  ``quantize`` uses it when a
 Parity pins live in ``tests/test_oracle_quantize.py`` (for ``q_scale_pow2``:
 the scale is at least amax/448 and below twice it, and the score factor is a
 power of two up to float32 rounding).
+
+Per-(segment, head) scales (``quantize_segments``) are a variant the product
+offers for packed batches: the sglang PR quantizes per head over the whole
+call, and a packed batch of unrelated sequences then shares one scale per
+head; here each segment gets the per-head rule over its own tokens.  Pins:
+a single segment reproduces ``quantize``; codes of a segment do not change
+when another segment's values do; scaling one segment's tensor by a power of
+two scales only that segment's scale by it and leaves every code unchanged.
 """
 from __future__ import annotations
 
@@ -158,6 +166,40 @@ def quantize(q, k, v, cu_seqlens: List[int], softmax_scale: float = None) -> Dic
         "scales": np.stack([rq["scale"], rk["scale"], rv["scale"]]).astype(np.float32),
         "mu": rk["mu"],
     }
+
+
+def quantize_segments(q, k, v, cu_seqlens: List[int], softmax_scale: float = None) -> Dict[str, np.ndarray]:
+    """Per-(segment, head) scales: every segment is quantized as if it were the
+    whole call, with the per-head rule above applied to that segment's tokens
+    only (so no segment's codes depend on another segment's values).
+
+    Keys as ``quantize`` except ``scales`` [3, nseg, H] (rows Q, K, V).  An
+    empty segment gets the scales of an all-zero head (1.0, and Q's rounded
+    value for it when ``softmax_scale`` is given).
+    """
+    qf, kf, vf = _as_f32(q), _as_f32(k), _as_f32(v)
+    T, H, D = qf.shape
+    nseg = len(cu_seqlens) - 1
+    out = {"q_codes": np.zeros((T, H, D), np.uint8), "k_codes": np.zeros((T, H, D), np.uint8),
+           "v_codes": np.zeros((T, H, D), np.uint8), "scales": np.zeros((3, nseg, H), np.float32),
+           "mu": np.zeros((nseg, H, D), np.float32)}
+    for s in range(nseg):
+        a, b = cu_seqlens[s], cu_seqlens[s + 1]
+        r = quantize(qf[a:b], kf[a:b], vf[a:b], [0, b - a], softmax_scale)
+        for name in ("q_codes", "k_codes", "v_codes"):
+            out[name][a:b] = r[name]
+        out["scales"][:, s] = r["scales"]
+        out["mu"][s] = r["mu"][0]
+    return out
+
+
+def dequantize_segments(codes: np.ndarray, scales: np.ndarray, cu_seqlens: List[int]) -> np.ndarray:
+    """float64 values of per-(segment, head) codes: scales [nseg, H]."""
+    out = np.zeros(codes.shape, np.float64)
+    for s in range(len(cu_seqlens) - 1):
+        a, b = cu_seqlens[s], cu_seqlens[s + 1]
+        out[a:b] = dequantize(codes[a:b], scales[s])
+    return out
 
 
 def dequantize(codes: np.ndarray, scale: np.ndarray) -> np.ndarray:

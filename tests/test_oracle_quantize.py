@@ -167,3 +167,49 @@ def test_quantize_with_softmax_scale_changes_only_q():
     ref = (torch.from_numpy(q.float().numpy() / r1["scales"][0][None, :, None])
            .to(torch.float8_e4m3fn).view(torch.uint8).numpy())
     assert np.array_equal(r1["q_codes"], ref)
+
+
+def test_segment_scales_single_segment_is_per_head():
+    q, k, v = _bf16((300, 3, 128), 11), _bf16((300, 3, 128), 12, 1.0, 0.7), _bf16((300, 3, 128), 13)
+    a = Qz.quantize(q, k, v, [0, 300], 0.088)
+    b = Qz.quantize_segments(q, k, v, [0, 300], 0.088)
+    for name in ("q_codes", "k_codes", "v_codes", "mu"):
+        assert np.array_equal(a[name], b[name]), name
+    assert np.array_equal(a["scales"], b["scales"][:, 0])
+
+
+def test_segment_scales_are_independent_of_other_segments():
+    cu = [0, 130, 130, 400, 401]
+    q, k, v = _bf16((401, 2, 128), 21), _bf16((401, 2, 128), 22), _bf16((401, 2, 128), 23)
+    base = Qz.quantize_segments(q, k, v, cu, 0.088)
+    q2, k2, v2 = q.clone(), k.clone(), v.clone()
+    q2[130:400] *= 7
+    k2[130:400] += 3
+    v2[130:400] *= 0.01
+    pert = Qz.quantize_segments(q2, k2, v2, cu, 0.088)
+    for name in ("q_codes", "k_codes", "v_codes"):
+        assert np.array_equal(base[name][:130], pert[name][:130]), name
+        assert np.array_equal(base[name][400:], pert[name][400:]), name
+    for s in (0, 1, 3):
+        assert np.array_equal(base["scales"][:, s], pert["scales"][:, s])
+    # the empty segment carries the all-zero-head scales
+    assert np.all(base["scales"][1, 1] == 1.0) and np.all(base["scales"][2, 1] == 1.0)
+    # per-head scales over the whole call would have changed segment 0's V codes
+    ph = Qz.quantize(q, k, v2, cu, 0.088)["v_codes"][:130]
+    assert not np.array_equal(ph, Qz.quantize(q, k, v, cu, 0.088)["v_codes"][:130])
+
+
+def test_segment_scales_power_of_two_rescaling():
+    cu = [0, 200, 333]
+    q, k, v = _bf16((333, 2, 128), 31), _bf16((333, 2, 128), 32), _bf16((333, 2, 128), 33)
+    base = Qz.quantize_segments(q, k, v, cu)
+    v2 = v.clone()
+    v2[200:] *= 8                                     # exact in bf16
+    r = Qz.quantize_segments(q, k, v2, cu)
+    assert np.array_equal(r["v_codes"], base["v_codes"])
+    assert np.array_equal(r["scales"][2, 1], base["scales"][2, 1] * np.float32(8))
+    assert np.array_equal(r["scales"][2, 0], base["scales"][2, 0])
+    # dequantized values follow the scaling exactly
+    dv = Qz.dequantize_segments(r["v_codes"], r["scales"][2], cu)
+    db = Qz.dequantize_segments(base["v_codes"], base["scales"][2], cu)
+    assert np.array_equal(dv[200:], 8 * db[200:]) and np.array_equal(dv[:200], db[:200])
