@@ -43,14 +43,15 @@ def _stream_handle(device: torch.device, stream=None) -> ctypes.c_void_p:
 
 
 class Plan:
-    """A validated segment table and work schedule (``fp8attn_plan``).
+    """A validated segment table and work schedule (``fp8attn_plan_ex``).
 
     ``device=None`` uses the current CUDA/HIP device; ``device=-1`` builds a
-    host-only plan that can be inspected but not run.
+    host-only plan that can be inspected but not run.  ``segment_scales=True``
+    quantizes every segment with its own per-head scales.
     """
 
     def __init__(self, tokens: int, heads: int, cu_seqlens: Optional[Sequence[int]] = None,
-                 softmax_scale: Optional[float] = None, device=None):
+                 softmax_scale: Optional[float] = None, device=None, segment_scales: bool = False):
         L = _lib.lib()
         if cu_seqlens is None:
             cu_seqlens = [0, tokens]
@@ -66,11 +67,14 @@ class Plan:
         self.heads = int(heads)
         self.cu_seqlens = tuple(cu)
         self.softmax_scale = float(DEFAULT_SCALE if softmax_scale is None else softmax_scale)
+        self.segment_scales = bool(segment_scales)
         arr = (ctypes.c_int32 * len(cu))(*cu)
         h = ctypes.c_void_p()
         self._h = None
-        _lib.check(L.fp8attn_plan(ctypes.byref(h), self.tokens, self.heads, arr, len(cu) - 1,
-                                  ctypes.c_float(self.softmax_scale), self.device_index), "fp8attn_plan")
+        flags = _lib.PLAN_SEGMENT_SCALES if self.segment_scales else 0
+        _lib.check(L.fp8attn_plan_ex(ctypes.byref(h), self.tokens, self.heads, arr, len(cu) - 1,
+                                     ctypes.c_float(self.softmax_scale), self.device_index, flags),
+                   "fp8attn_plan_ex")
         self._h = h
         self.workspace_bytes = int(L.fp8attn_workspace_bytes(h))
 
@@ -83,10 +87,10 @@ class Plan:
         return torch.device("cuda", self.device_index)
 
     def info(self) -> Dict[str, int]:
-        buf = (ctypes.c_int64 * 8)()
+        buf = (ctypes.c_int64 * 10)()
         _lib.check(_lib.lib().fp8attn_plan_info(self._h, buf), "fp8attn_plan_info")
         keys = ["tokens", "heads", "num_segments", "workspace_rows", "work_items", "stat_chunks",
-                "query_tile", "key_tile"]
+                "query_tile", "key_tile", "segment_scales", "partial_slots"]
         return dict(zip(keys, list(buf)))
 
     def work_items(self):
@@ -112,8 +116,8 @@ class Plan:
             n = shape[0] * shape[1] * shape[2]
             return workspace[off: off + n].view(shape)
         n = shape[0] * shape[1] * shape[2]
-        if which == _lib.REGION_SCALES:
-            shape = shape[:2]
+        if which == _lib.REGION_SCALES and shape[1] == 1:
+            shape = (shape[0], shape[2])          # per-head scales: [3][H]
         return workspace[off: off + 4 * n].view(torch.float32).view(shape)
 
     def close(self):
@@ -189,23 +193,26 @@ def forward(plan: Plan, workspace: torch.Tensor, out: Optional[torch.Tensor] = N
 _PLANS: Dict[Tuple, Plan] = {}
 
 
-def get_plan(tokens: int, heads: int, cu_seqlens: Sequence[int], softmax_scale: float, device: int) -> Plan:
-    """Plans are cached per (cu_seqlens, heads, scale, device), as the FlashInfer page caches its
-    segment plan per (cu_seqlens, heads, device).  A plan holds only small tables."""
-    key = (tuple(int(x) for x in cu_seqlens), int(heads), float(softmax_scale), int(device))
+def get_plan(tokens: int, heads: int, cu_seqlens: Sequence[int], softmax_scale: float, device: int,
+             segment_scales: bool = False) -> Plan:
+    """Plans are cached per (cu_seqlens, heads, scale, device, scale mode), as the FlashInfer page
+    caches its segment plan per (cu_seqlens, heads, device).  A plan holds only small tables."""
+    key = (tuple(int(x) for x in cu_seqlens), int(heads), float(softmax_scale), int(device), bool(segment_scales))
     p = _PLANS.get(key)
     if p is None:
-        p = Plan(tokens, heads, cu_seqlens, softmax_scale, device)
+        p = Plan(tokens, heads, cu_seqlens, softmax_scale, device, segment_scales=segment_scales)
         _PLANS[key] = p
     return p
 
 
 def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: Optional[Sequence[int]] = None,
               softmax_scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
-              return_lse: bool = False, causal: bool = False, workspace: Optional[torch.Tensor] = None):
+              return_lse: bool = False, causal: bool = False, workspace: Optional[torch.Tensor] = None,
+              segment_scales: bool = False):
     """Dense non-causal FP8 attention over packed [tokens, heads, 128] BF16 q/k/v.
 
     ``cu_seqlens`` is a host sequence of segment boundaries (None = one segment).
+    ``segment_scales`` quantizes every segment with its own per-head scales.
     Causal attention is not supported and raises (there is no fallback path).
     """
     if causal:
@@ -220,7 +227,7 @@ def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: Opt
         cu_seqlens = cu_seqlens.tolist()
     scale = DEFAULT_SCALE if softmax_scale is None else float(softmax_scale)
     dev = q.device.index if q.device.index is not None else torch.cuda.current_device()
-    plan = get_plan(T, H, cu_seqlens, scale, dev)
+    plan = get_plan(T, H, cu_seqlens, scale, dev, segment_scales)
     ws = workspace if workspace is not None else plan.new_workspace()
     quantize(plan, q, k, v, ws)
     lse = torch.empty((H, T), dtype=torch.float32, device=q.device) if return_lse else None

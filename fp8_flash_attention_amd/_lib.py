@@ -16,6 +16,7 @@ OK, EINVAL, EUNSUPPORTED, ENOMEM, EWORKSPACE, EHIP = range(6)
 STATUS_NAMES = {0: "FP8ATTN_OK", 1: "FP8ATTN_EINVAL", 2: "FP8ATTN_EUNSUPPORTED",
                 3: "FP8ATTN_ENOMEM", 4: "FP8ATTN_EWORKSPACE", 5: "FP8ATTN_EHIP"}
 REGION_Q, REGION_K, REGION_V, REGION_SCALES, REGION_MU, REGION_ROWMAP = range(6)
+PLAN_SEGMENT_SCALES = 1          # FP8ATTN_PLAN_SEGMENT_SCALES
 
 # Every symbol include/fp8attn.h declares, with (restype, argtypes).
 _i64p = ctypes.POINTER(ctypes.c_int64)
@@ -23,6 +24,8 @@ _i32p = ctypes.POINTER(ctypes.c_int32)
 SIGNATURES = {
     "fp8attn_plan": (ctypes.c_int, [ctypes.POINTER(ctypes.c_void_p), ctypes.c_int64, ctypes.c_int32,
                                     _i32p, ctypes.c_int32, ctypes.c_float, ctypes.c_int32]),
+    "fp8attn_plan_ex": (ctypes.c_int, [ctypes.POINTER(ctypes.c_void_p), ctypes.c_int64, ctypes.c_int32,
+                                       _i32p, ctypes.c_int32, ctypes.c_float, ctypes.c_int32, ctypes.c_uint32]),
     "fp8attn_workspace_bytes": (ctypes.c_size_t, [ctypes.c_void_p]),
     "fp8attn_quantize": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                         _i64p, _i64p, _i64p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),

@@ -27,6 +27,8 @@ struct fp8attn_plan_s {
   int64_t tokens = 0;
   int32_t heads = 0;
   int32_t nseg = 0;
+  int32_t seg_scales = 0;         // FP8ATTN_PLAN_SEGMENT_SCALES
+  int32_t nscale = 1;             // scale sets: nseg with segment scales, else 1
   float scale = 0.f;
   int device = -1;
   std::vector<int32_t> cu;
@@ -59,7 +61,7 @@ fp8attn_status fail(fp8attn_status s, const std::string& msg) {
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-WorkspaceLayout make_layout(int64_t rows, int heads, int nseg, int nchunks, int64_t npieces) {
+WorkspaceLayout make_layout(int64_t rows, int heads, int nseg, int nscale, int nchunks, int64_t npieces) {
   WorkspaceLayout w{};
   w.rows = rows;
   w.npieces = npieces;
@@ -68,7 +70,7 @@ WorkspaceLayout make_layout(int64_t rows, int heads, int nseg, int nchunks, int6
   w.q_off = off; off = align_up(off + codes, 256);
   w.k_off = off; off = align_up(off + codes, 256);
   w.v_off = off; off = align_up(off + codes, 256);
-  w.scale_off = off; off = align_up(off + sizeof(float) * 3 * heads, 256);
+  w.scale_off = off; off = align_up(off + sizeof(float) * 3 * (size_t)nscale * heads, 256);
   w.mu_off = off; off = align_up(off + sizeof(float) * (size_t)nseg * heads * kHeadDim, 256);
   w.kstat_off = off; off = align_up(off + sizeof(KStat) * (size_t)nchunks * heads * kHeadDim, 256);
   w.amax_off = off; off = align_up(off + sizeof(float) * 2 * (size_t)nchunks * heads, 256);
@@ -173,8 +175,15 @@ extern "C" {
 fp8attn_status fp8attn_plan(fp8attn_plan_t* plan_out, int64_t tokens, int32_t heads,
                             const int32_t* cu, int32_t num_segments, float softmax_scale,
                             int32_t device) {
+  return fp8attn_plan_ex(plan_out, tokens, heads, cu, num_segments, softmax_scale, device, 0u);
+}
+
+fp8attn_status fp8attn_plan_ex(fp8attn_plan_t* plan_out, int64_t tokens, int32_t heads,
+                               const int32_t* cu, int32_t num_segments, float softmax_scale,
+                               int32_t device, uint32_t flags) {
   if (plan_out == nullptr) return fail(FP8ATTN_EINVAL, "plan_out is NULL");
   *plan_out = nullptr;
+  if ((flags & ~FP8ATTN_PLAN_SEGMENT_SCALES) != 0) return fail(FP8ATTN_EINVAL, "unknown plan flags");
   if (cu == nullptr) return fail(FP8ATTN_EINVAL, "cu_seqlens_host is NULL");
   if (num_segments < 1) return fail(FP8ATTN_EINVAL, "num_segments must be >= 1");
   if (heads < 1) return fail(FP8ATTN_EINVAL, "heads must be >= 1");
@@ -195,6 +204,8 @@ fp8attn_status fp8attn_plan(fp8attn_plan_t* plan_out, int64_t tokens, int32_t he
   p->nseg = num_segments;
   p->scale = softmax_scale;
   p->device = device;
+  p->seg_scales = (flags & FP8ATTN_PLAN_SEGMENT_SCALES) ? 1 : 0;
+  p->nscale = p->seg_scales ? num_segments : 1;
   p->cu.assign(cu, cu + num_segments + 1);
   int64_t row = 0;
   int32_t chunk = 0;
@@ -226,7 +237,7 @@ fp8attn_status fp8attn_plan(fp8attn_plan_t* plan_out, int64_t tokens, int32_t he
     delete p;
     return fail(FP8ATTN_EUNSUPPORTED, "too many split work items");
   }
-  p->ws = make_layout(row, heads, num_segments, (int)p->chunks.size(), p->npieces);
+  p->ws = make_layout(row, heads, num_segments, p->nscale, (int)p->chunks.size(), p->npieces);
 
   if (device >= 0) {
     DeviceGuard g(device);
@@ -324,6 +335,7 @@ fp8attn_status fp8attn_quantize(fp8attn_plan_t p, const void* q, const void* k, 
   a.nseg = p->nseg;
   a.nchunks = (int32_t)p->chunks.size();
   a.ngroups = (int32_t)p->group_seg.size();
+  a.seg_scales = p->seg_scales;
   a.rows = p->ws.rows;
   a.softmax_scale = p->scale;
   hipError_t e = launch_quantize(a, static_cast<hipStream_t>(stream));
@@ -366,6 +378,7 @@ fp8attn_status fp8attn_forward(fp8attn_plan_t p, void* workspace, size_t workspa
   a.rows = p->ws.rows;
   a.heads = p->heads;
   a.nitems = p->real_items > 0 ? (int32_t)p->items.size() : 0;
+  a.nscale = p->nscale;
   a.softmax_scale = p->scale;
   hipError_t e = launch_attention(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(FP8ATTN_EHIP, std::string("attention launch failed: ") + hipGetErrorString(e));
@@ -404,14 +417,14 @@ fp8attn_status fp8attn_workspace_region(fp8attn_plan_t p, const void* workspace,
     case FP8ATTN_REGION_Q_CODES: *ptr_out = ws + p->ws.q_off; dims_out[0] = H; dims_out[1] = R; dims_out[2] = D; break;
     case FP8ATTN_REGION_K_CODES: *ptr_out = ws + p->ws.k_off; dims_out[0] = H; dims_out[1] = R; dims_out[2] = D; break;
     case FP8ATTN_REGION_V_CODES: *ptr_out = ws + p->ws.v_off; dims_out[0] = H; dims_out[1] = D; dims_out[2] = R; break;
-    case FP8ATTN_REGION_SCALES: *ptr_out = ws + p->ws.scale_off; dims_out[0] = 3; dims_out[1] = H; dims_out[2] = 1; break;
+    case FP8ATTN_REGION_SCALES: *ptr_out = ws + p->ws.scale_off; dims_out[0] = 3; dims_out[1] = p->nscale; dims_out[2] = H; break;
     case FP8ATTN_REGION_MU: *ptr_out = ws + p->ws.mu_off; dims_out[0] = p->nseg; dims_out[1] = H; dims_out[2] = D; break;
     default: return fail(FP8ATTN_EINVAL, "unknown region");
   }
   return FP8ATTN_OK;
 }
 
-fp8attn_status fp8attn_plan_info(fp8attn_plan_t p, int64_t info[8]) {
+fp8attn_status fp8attn_plan_info(fp8attn_plan_t p, int64_t info[10]) {
   if (p == nullptr || info == nullptr) return fail(FP8ATTN_EINVAL, "NULL argument");
   info[0] = p->tokens;
   info[1] = p->heads;
@@ -421,6 +434,8 @@ fp8attn_status fp8attn_plan_info(fp8attn_plan_t p, int64_t info[8]) {
   info[5] = (int64_t)p->chunks.size();
   info[6] = kBM;
   info[7] = kBN;
+  info[8] = p->seg_scales;
+  info[9] = p->npieces;
   return FP8ATTN_OK;
 }
 

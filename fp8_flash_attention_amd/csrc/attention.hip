@@ -211,9 +211,11 @@ __global__ __launch_bounds__(64 * kWavesWG, 8 / kWavesWG) void k_attn(AttentionA
   const uint8_t* Kh = a.k_codes + hrow * kHeadDim + (size_t)kt0 * kTile;
   const uint8_t* Vh = a.v_codes + (size_t)h * kHeadDim * a.rows + si.row0 + (size_t)kt0 * kBN;
 
-  const float s_q = a.scales[h];
-  const float s_k = a.scales[a.heads + h];
-  const float s_v = a.scales[2 * a.heads + h];
+  // scales [3][S][H]: S = 1, or one set per segment
+  const int sset = a.nscale > 1 ? it.x : 0;
+  const float s_q = a.scales[(0 * a.nscale + sset) * a.heads + h];
+  const float s_k = a.scales[(1 * a.nscale + sset) * a.heads + h];
+  const float s_v = a.scales[(2 * a.nscale + sset) * a.heads + h];
   // Score factor c = softmax_scale * s_q * s_k * log2(e).  The quantizer picks
   // s_q so that c is a power of two up to the rounding of this product, so its
   // E8M0 code (the biased exponent rounded to nearest) scales the score

@@ -69,7 +69,7 @@ struct QuantizeArgs {
   const uint16_t* x[3];      // bf16 Q, K, V
   int64_t ts[3], hs[3];      // token and head strides in elements
   uint8_t* codes[3];         // Q, K: [H][rows][128]; V: [H][128][rows] permuted
-  float* scales;             // [3][H]
+  float* scales;             // [3][S][H], S = nseg with per-segment scales, else 1
   float* mu;                 // [nseg][H][128]
   KStat* kstat;              // [nchunks][H][128]
   float* amax;               // [2][nchunks][H]  (Q, V partial amax)
@@ -77,6 +77,7 @@ struct QuantizeArgs {
   const Chunk* chunks;
   const int32_t* group_seg;  // [ngroups]: segment of each 64-row pack group, -1 = guard
   int32_t heads, nseg, nchunks, ngroups;
+  int32_t seg_scales;        // 1: one scale per (tensor, segment, head)
   int64_t rows;
   float softmax_scale;       // fixes Q's scale (see k_finalize)
 };
@@ -85,7 +86,7 @@ struct AttentionArgs {
   const uint8_t* q_codes;
   const uint8_t* k_codes;
   const uint8_t* v_codes;
-  const float* scales;
+  const float* scales;       // [3][S][H]
   const float* mu;
   const SegInfo* segs;
   const int4* items;         // work items (encoding above)
@@ -99,6 +100,7 @@ struct AttentionArgs {
   int64_t rows;
   int32_t heads;
   int32_t nitems;
+  int32_t nscale;            // S: scale sets (segments with per-segment scales, else 1)
   float softmax_scale;
 };
 

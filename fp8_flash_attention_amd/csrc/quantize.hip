@@ -104,7 +104,8 @@ __global__ __launch_bounds__(256) void k_stats(QuantizeArgs a) {
 // +0.0; K amax = max over segments and channels of |fl32(max - mu)| and
 // |fl32(min - mu)|, which equals max |fl32(x - mu)| over the tokens because
 // rounding is monotone; s = fl32(amax / 448), or 1 for amax == 0, for K and
-// V; Q's scale is rounded up from that (q_scale_of).
+// V; Q's scale is rounded up from that (q_scale_of).  With per-segment
+// scales the same is done for every segment over its own chunks only.
 // ---------------------------------------------------------------------------
 __device__ float block_max128(float v, float* red) {
 #pragma unroll
@@ -141,18 +142,20 @@ __global__ __launch_bounds__(128) void k_finalize(QuantizeArgs a) {
   const int h = blockIdx.x;
   const int d = threadIdx.x;
   float qa = 0.f, va = 0.f;
-  for (int c = d; c < a.nchunks; c += 128) {
-    qa = fmaxf(qa, a.amax[(int64_t)c * a.heads + h]);
-    va = fmaxf(va, a.amax[((int64_t)a.nchunks + c) * a.heads + h]);
+  if (!a.seg_scales) {
+    for (int c = d; c < a.nchunks; c += 128) {
+      qa = fmaxf(qa, a.amax[(int64_t)c * a.heads + h]);
+      va = fmaxf(va, a.amax[((int64_t)a.nchunks + c) * a.heads + h]);
+    }
   }
   float ka = 0.f;
   for (int s = 0; s < a.nseg; s++) {
     const SegInfo si = a.segs[s];
-    float mu = 0.f;
+    const int nch = (si.len + kStatChunk - 1) / kStatChunk;
+    float mu = 0.f, kas = 0.f;
     if (si.len > 0) {
       double sum = 0.0;
       float mn = __builtin_inff(), mx = -__builtin_inff();
-      const int nch = (si.len + kStatChunk - 1) / kStatChunk;
 #pragma unroll 8
       for (int c = si.chunk0; c < si.chunk0 + nch; c++) {   // loads issued ahead, sums in chunk order
         const KStat st = a.kstat[((int64_t)c * a.heads + h) * kHeadDim + d];
@@ -161,17 +164,40 @@ __global__ __launch_bounds__(128) void k_finalize(QuantizeArgs a) {
         mx = fmaxf(mx, st.mx);
       }
       mu = (float)(sum / (double)si.len);
-      ka = fmaxf(ka, fmaxf(fabsf(mx - mu), fabsf(mn - mu)));
+      kas = fmaxf(fabsf(mx - mu), fabsf(mn - mu));
     }
     a.mu[((int64_t)s * a.heads + h) * kHeadDim + d] = mu;
+    if (a.seg_scales) {
+      // this segment's own amax of Q, K and V (its chunks' partials), so its
+      // scales do not depend on the other segments
+      float qs = 0.f, vs = 0.f;
+      for (int c = si.chunk0 + d; c < si.chunk0 + nch; c += 128) {
+        qs = fmaxf(qs, a.amax[(int64_t)c * a.heads + h]);
+        vs = fmaxf(vs, a.amax[((int64_t)a.nchunks + c) * a.heads + h]);
+      }
+      qs = block_max128(qs, red);
+      vs = block_max128(vs, red);
+      const float ks = block_max128(kas, red);
+      if (d == 0) {
+        const int64_t o = (int64_t)s * a.heads + h;      // scales [3][nseg][H]
+        const int64_t n = (int64_t)a.nseg * a.heads;
+        a.scales[o] = q_scale_of(qs, scale_of(ks), a.softmax_scale);
+        a.scales[n + o] = scale_of(ks);
+        a.scales[2 * n + o] = scale_of(vs);
+      }
+    } else {
+      ka = fmaxf(ka, kas);
+    }
   }
-  qa = block_max128(qa, red);
-  va = block_max128(va, red);
-  ka = block_max128(ka, red);
-  if (d == 0) {
-    a.scales[h] = q_scale_of(qa, scale_of(ka), a.softmax_scale);
-    a.scales[a.heads + h] = scale_of(ka);
-    a.scales[2 * a.heads + h] = scale_of(va);
+  if (!a.seg_scales) {
+    qa = block_max128(qa, red);
+    va = block_max128(va, red);
+    ka = block_max128(ka, red);
+    if (d == 0) {
+      a.scales[h] = q_scale_of(qa, scale_of(ka), a.softmax_scale);
+      a.scales[a.heads + h] = scale_of(ka);
+      a.scales[2 * a.heads + h] = scale_of(va);
+    }
   }
 }
 
@@ -196,7 +222,9 @@ __global__ __launch_bounds__(256) void k_pack(QuantizeArgs a) {
   const int64_t R = (int64_t)g * kPackRows;  // first workspace row of the group
   SegInfo si{0, 0, 0, 0};
   if (seg >= 0) si = a.segs[seg];
-  const float s = a.scales[tensor * a.heads + h];
+  const int nset = a.seg_scales ? a.nseg : 1;       // scales [3][nset][H]
+  const int sset = a.seg_scales && seg >= 0 ? seg : 0;
+  const float s = a.scales[((int64_t)tensor * nset + sset) * a.heads + h];
   const int c0 = (t % 16) * 8;
   const uint16_t* base = a.x[tensor] + (int64_t)h * a.hs[tensor] + c0;
   const int64_t ts = a.ts[tensor];

@@ -61,7 +61,8 @@ typedef enum {
   FP8ATTN_REGION_Q_CODES = 0, /* uint8 [H][rows][128]                                  */
   FP8ATTN_REGION_K_CODES = 1, /* uint8 [H][rows][128] (centred K)                       */
   FP8ATTN_REGION_V_CODES = 2, /* uint8 [H][128][rows], keys permuted in 64-key groups  */
-  FP8ATTN_REGION_SCALES = 3,  /* float [3][H]: rows Q, K, V                             */
+  FP8ATTN_REGION_SCALES = 3,  /* float [3][S][H]: rows Q, K, V; S = num_segments with
+                                 FP8ATTN_PLAN_SEGMENT_SCALES, else 1                   */
   FP8ATTN_REGION_MU = 4,      /* float [num_segments][H][128]: per-channel K means     */
   FP8ATTN_REGION_ROWMAP = 5   /* plan-owned device int32 [num_segments]: first workspace
                                  row of each segment (rows are padded per segment)    */
@@ -91,6 +92,24 @@ typedef enum {
 fp8attn_status fp8attn_plan(fp8attn_plan_t* plan_out, int64_t tokens, int32_t heads,
                             const int32_t* cu_seqlens_host, int32_t num_segments,
                             float softmax_scale, int32_t device);
+
+/* Flags of fp8attn_plan_ex. */
+#define FP8ATTN_PLAN_SEGMENT_SCALES 1u
+
+/*
+ * fp8attn_plan_ex - fp8attn_plan with flags (fp8attn_plan is flags == 0).
+ *
+ * FP8ATTN_PLAN_SEGMENT_SCALES: one scale per (tensor, segment, head) instead
+ *   of per (tensor, head): every segment is quantized by the per-head rule of
+ *   fp8attn_quantize applied to its own tokens, so no segment's codes depend
+ *   on another segment's values (a packed batch of unrelated sequences).  An
+ *   empty segment gets the scales of an all-zero head.  The attention reads
+ *   each segment's scales.
+ * Unknown flag bits: FP8ATTN_EINVAL.
+ */
+fp8attn_status fp8attn_plan_ex(fp8attn_plan_t* plan_out, int64_t tokens, int32_t heads,
+                               const int32_t* cu_seqlens_host, int32_t num_segments,
+                               float softmax_scale, int32_t device, uint32_t flags);
 
 /* Bytes of workspace fp8attn_quantize/fp8attn_forward need for this plan (0 on NULL). */
 size_t fp8attn_workspace_bytes(fp8attn_plan_t plan);
@@ -174,10 +193,11 @@ fp8attn_status fp8attn_workspace_region(fp8attn_plan_t plan, const void* workspa
 
 /*
  * fp8attn_plan_info - schedule facts (for tests and tools).
- *   info_out int64[8]: {tokens, heads, num_segments, workspace_rows,
- *                       work_items, stat_chunks, query_tile, key_tile}
+ *   info_out int64[10]: {tokens, heads, num_segments, workspace_rows,
+ *                        work_items, stat_chunks, query_tile, key_tile,
+ *                        segment_scales (0 or 1), partial_slots}
  */
-fp8attn_status fp8attn_plan_info(fp8attn_plan_t plan, int64_t info_out[8]);
+fp8attn_status fp8attn_plan_info(fp8attn_plan_t plan, int64_t info_out[10]);
 
 /*
  * fp8attn_plan_work_items - copy the ordered work list to host memory.

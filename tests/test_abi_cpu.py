@@ -224,6 +224,28 @@ def test_plan_rejects_rows_beyond_32bit_code_offsets():
     assert "32-bit" in _lib.lib().fp8attn_last_error().decode()
 
 
+def test_plan_ex_flags_and_segment_scale_layout():
+    L = _lib.lib()
+    cu = (ctypes.c_int32 * 4)(0, 100, 100, 300)
+    h = ctypes.c_void_p()
+    assert L.fp8attn_plan_ex(ctypes.byref(h), 300, 2, cu, 3, ctypes.c_float(0.088), -1, 2) == _lib.EINVAL
+    assert "flags" in L.fp8attn_last_error().decode()
+    base = fa.Plan(300, 2, [0, 100, 100, 300], device=-1)
+    seg = fa.Plan(300, 2, [0, 100, 100, 300], device=-1, segment_scales=True)
+    assert base.info()["segment_scales"] == 0 and seg.info()["segment_scales"] == 1
+    ptr = ctypes.c_void_p()
+    dims = (ctypes.c_int64 * 3)()
+    assert L.fp8attn_workspace_region(base.handle, ctypes.c_void_p(1 << 20), _lib.REGION_SCALES,
+                                      ctypes.byref(ptr), dims) == 0
+    assert tuple(dims) == (3, 1, 2)
+    assert L.fp8attn_workspace_region(seg.handle, ctypes.c_void_p(1 << 20), _lib.REGION_SCALES,
+                                      ctypes.byref(ptr), dims) == 0
+    assert tuple(dims) == (3, 3, 2)                 # one set per segment, the empty one included
+    assert seg.workspace_bytes >= base.workspace_bytes
+    # the work schedule does not depend on the scale mode
+    assert seg.work_items() == base.work_items()
+
+
 def test_empty_input_plan():
     p = fa.Plan(0, 3, [0, 0], device=-1)
     info = p.info()

@@ -354,3 +354,42 @@ def test_split_items_into_strided_output():
     torch.cuda.synchronize()
     assert torch.equal(big[:, 1:-1], ref)
     assert not big[:, 0].any() and not big[:, -1].any()
+
+
+def test_segment_scales_attention_and_independence():
+    from tests.test_gpu_quantize import _segment_scaled_inputs
+    w, q, k, v = _segment_scaled_inputs()
+    plan = fa.Plan(w.tokens, w.heads, w.cu_seqlens, w.softmax_scale, device=0, segment_scales=True)
+    ws = plan.new_workspace()
+    log(f"attention with per-segment scales cu={w.cu_seqlens}")
+    fa.quantize(plan, q.cuda(), k.cuda(), v.cuda(), ws)
+    lse = torch.empty((w.heads, w.tokens), dtype=torch.float32, device="cuda")
+    out = fa.forward(plan, ws, lse=lse)
+    torch.cuda.synchronize()
+    got = out.cpu().double().numpy()
+    ref = A.attention(q, k, v, w.cu_seqlens, w.softmax_scale).numpy()
+    r = Qz.quantize_segments(q, k, v, w.cu_seqlens, w.softmax_scale)
+    cu = w.cu_seqlens
+    dq = Qz.dequantize_segments(r["q_codes"], r["scales"][0], cu)
+    dk = Qz.dequantize_segments(r["k_codes"], r["scales"][1], cu)
+    dv = Qz.dequantize_segments(r["v_codes"], r["scales"][2], cu)
+    diag = A.attention(dq, dk, dv, cu, w.softmax_scale).numpy()
+    rr, rd = compare.rel_rms(got, ref), compare.rel_rms(got, diag)
+    log(f"  rel_rms={rr:.5f} diagnostic={rd:.5f}")
+    assert rr <= compare.REL_RMS_BAR and rd <= DIAG_BAR
+    assert compare.allclose_excess(got, diag) <= 0.0
+    # LSE of the uncentred scores from the per-segment operands
+    for s, (a, b) in enumerate(zip(cu[:-1], cu[1:])):
+        dk[a:b] += r["mu"][s][None].astype(np.float64)
+    ld = A.lse_rows(torch.from_numpy(dq), torch.from_numpy(dk), cu, w.softmax_scale).numpy().T
+    assert np.abs(lse.cpu().double().numpy() - ld).max() <= 2e-3
+    # segments are independent: scaling another segment's inputs changes nothing here
+    q2, k2, v2 = q.clone(), k.clone(), v.clone()
+    q2[513:699] *= 16
+    v2[513:699] *= 16
+    k2[513:699] -= 5
+    fa.quantize(plan, q2.cuda(), k2.cuda(), v2.cuda(), ws)
+    out2 = fa.forward(plan, ws)
+    torch.cuda.synchronize()
+    for a, b in [(0, 200), (200, 513), (699, 700)]:
+        assert torch.equal(out[a:b], out2[a:b])

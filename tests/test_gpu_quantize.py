@@ -119,3 +119,37 @@ def test_empty_input():
     out = fa.forward(plan, ws)
     torch.cuda.synchronize()
     assert out.shape == (0, 2, 128)
+
+
+def _segment_scaled_inputs():
+    # segments of very different magnitudes, an empty segment and a 1-token one
+    cu = [0, 200, 200, 513, 699, 700]
+    w = make_workload("segscale", 700, 3, cu, seed=111)
+    q, k, v = generate(w)
+    q[200:513] *= 8
+    k[0:200] += 2
+    v[513:699] *= 0.25
+    v[699:] *= 40
+    return w, q, k, v
+
+
+def test_segment_scales_codes_bit_exact():
+    w, q, k, v = _segment_scaled_inputs()
+    plan = fa.Plan(w.tokens, w.heads, w.cu_seqlens, w.softmax_scale, device=0, segment_scales=True)
+    ws = plan.new_workspace()
+    ws.fill_(0xFF)
+    log(f"quantize with per-segment scales cu={w.cu_seqlens}")
+    fa.quantize(plan, q.cuda(), k.cuda(), v.cuda(), ws)
+    torch.cuda.synchronize()
+    got = read_codes(plan, ws)
+    exp = Qz.quantize_segments(q, k, v, w.cu_seqlens, w.softmax_scale)
+    for name in ("q_codes", "k_codes", "v_codes"):
+        assert np.array_equal(got[name], exp[name]), name
+    assert got["scales"].shape == (3, len(w.cu_seqlens) - 1, w.heads)
+    assert np.array_equal(got["scales"].view(np.uint32), exp["scales"].view(np.uint32))
+    assert np.array_equal(got["mu"].view(np.uint32), exp["mu"].view(np.uint32))
+    for name, pad in got["pads"].items():
+        assert not pad.size or not pad.any(), f"{name} padding bytes not zero"
+    # per-head scales over the whole call differ on these inputs
+    base = Qz.quantize(q, k, v, w.cu_seqlens, w.softmax_scale)
+    assert not np.array_equal(base["v_codes"], exp["v_codes"])
