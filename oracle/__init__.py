@@ -10,8 +10,11 @@ it; the two share no code.  The oracle is plain and slow on purpose:
   segment's per-channel mean).
 * ``oracle.e4m3``      - bit-level OCP E4M3 encoder/decoder.
 * ``oracle.compare``   - relative-RMS and max-abs comparators.
+* ``oracle.mxfp4``     - the block-scaled FP4 variant: E2M1 codes with one
+  power-of-two scale per 32 elements for Q (centred by its 128-row block
+  mean, the mean term added back), K, V and the probabilities.
 
 Every function is pinned by ``-m "not gpu"`` tests in ``tests/test_oracle_*.py``
 against closed forms, brute force, a library routine or invariants.
 """
-from . import attention, compare, e4m3, quantize  # noqa: F401
+from . import attention, compare, e4m3, mxfp4, quantize  # noqa: F401

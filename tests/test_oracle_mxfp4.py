@@ -1,0 +1,268 @@
+"""Pins for the CPU reference of the block-scaled FP4 variant (oracle/mxfp4.py).
+
+Checked against things other than the module itself:
+* the E2M1 value table of the OCP MX specification
+  (``tests/golden/e2m1_values.txt``) and a brute-force nearest-value search
+  written here from that table, with its own tie-break;
+* a brute-force search for the block exponent over every integer;
+* error bounds of round-to-nearest on the E2M1 grid;
+* closed forms of the attention: a dominating key returns its value row,
+  equal scores return the mean of V, an integer shift of a row's scores
+  leaves the normalized weights unchanged;
+* the whole quantize + attention pipeline against the plain float64 softmax
+  attention (oracle/attention.py) on inputs for which every quantization step
+  is lossless, with and without Q centring, and a planted mistake (the
+  block-mean term dropped) that this pin catches;
+* independence of segments and of Q mean blocks.
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import attention as exact
+from oracle import mxfp4
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "e2m1_values.txt")
+GRID = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+
+
+def _golden():
+    rows = []
+    for line in open(GOLDEN):
+        if line.startswith("#") or not line.strip():
+            continue
+        f = line.split()
+        rows.append((int(f[0], 16), float(f[1])))
+    return rows
+
+
+def test_e2m1_table_against_ocp_values():
+    rows = _golden()
+    assert len(rows) == 16
+    for code, val in rows:
+        got = float(mxfp4.e2m1_decode(np.array([code]))[0])
+        assert got == val and np.signbit(got) == np.signbit(val), (code, got, val)
+        assert int(mxfp4.e2m1_encode(np.array([val]))[0]) == code
+
+
+def _brute(y):
+    """Nearest grid magnitude, ties to the even code, saturating; sign copied."""
+    a = np.minimum(np.abs(np.asarray(y, np.float64)), 100.0)
+    d = np.abs(a[:, None] - GRID[None, :])
+    best = d.min(axis=1, keepdims=True)
+    cand = d == best
+    even = cand & (np.arange(8)[None, :] % 2 == 0)
+    idx = np.where(even.any(axis=1), even.argmax(axis=1), cand.argmax(axis=1))
+    return (idx | (np.signbit(y).astype(np.int64) << 3)).astype(np.uint8)
+
+
+def test_e2m1_encode_brute_force():
+    grid = np.arange(-8 * 64, 8 * 64 + 1) / 64.0            # every midpoint and tie of the grid
+    rng = np.random.default_rng(3)
+    rand = rng.standard_normal(20000) * 3.0
+    big = np.array([6.0001, 7.0, 7.9, 8.0, 1e30, -1e30, -6.5])
+    y = np.concatenate([grid, rand, big]).astype(np.float32)
+    np.testing.assert_array_equal(mxfp4.e2m1_encode(y), _brute(y))
+    assert int(mxfp4.e2m1_encode(np.array([-0.0]))[0]) == 8
+
+
+def test_block_exp_brute_force():
+    rng = np.random.default_rng(4)
+    vals = list(np.abs(rng.standard_normal(300) * 10.0 ** rng.integers(-20, 20, 300)).astype(np.float32))
+    for k in range(-20, 20):                                  # boundaries 6 * 2^k and neighbours
+        b = np.float32(6.0 * 2.0 ** k)
+        vals += [b, np.nextafter(b, np.float32(0)), np.nextafter(b, np.float32(np.inf)), np.float32(3.0 * 2.0 ** k)]
+    vals = np.array(vals, np.float32)
+    got = mxfp4.block_exp(vals)
+    for a, e in zip(vals, got):
+        want = min(e2 for e2 in range(-200, 200) if float(a) <= 6.0 * 2.0 ** e2)
+        assert e == max(-127, min(127, want)), (a, e, want)
+    assert int(mxfp4.block_exp(np.array([0.0]))[0]) == -127
+    assert int(mxfp4.block_exp(np.array([1e-45], np.float32))[0]) == -127   # clamped
+
+
+def test_mx_quantize_error_bound_and_range():
+    rng = np.random.default_rng(5)
+    y = (rng.standard_normal((64, 128)) * np.exp(rng.standard_normal((64, 1)) * 3)).astype(np.float32)
+    r = mxfp4.mx_quantize(y, axis=1)
+    assert r["e"].shape == (64, 4)
+    yhat = mxfp4.mx_dequantize(r["codes"], r["e"], axis=1)
+    s = np.ldexp(1.0, np.repeat(r["e"], 32, axis=1))
+    a = np.abs(y.astype(np.float64)) / s
+    half_step = np.where(a < 2, 0.25, np.where(a < 4, 0.5, 1.0))
+    assert np.all(np.abs(yhat - y) <= half_step * s)
+    bmax = np.abs(y).reshape(64, 4, 32).max(axis=2) / np.ldexp(1.0, r["e"])
+    assert np.all((bmax > 3.0) & (bmax <= 6.0))              # amax/6 rounded up to a power of two
+
+
+def test_quantize_probs_closed_forms():
+    rng = np.random.default_rng(6)
+    x = rng.standard_normal((5, 77)) * 4
+    p = mxfp4.quantize_probs(x)
+    # an integer shift of a row's scores scales its weights by exactly 2^n
+    for n in (-3, 1, 17):
+        np.testing.assert_array_equal(mxfp4.quantize_probs(x + n), p * 2.0 ** n)
+    # error bound per element: half a grid step at the block's scale
+    for b0 in range(0, 77, 32):
+        xb = x[:, b0:b0 + 32]
+        E = np.ceil(xb.max(axis=1, keepdims=True) - np.log2(6.0))
+        a = np.exp2(xb - E)
+        half_step = np.where(a < 2, 0.25, np.where(a < 4, 0.5, 1.0))
+        assert np.all(np.abs(p[:, b0:b0 + 32] - np.exp2(xb)) <= half_step * np.exp2(E) * (1 + 1e-12))
+
+
+def _ops(T, H, rng, scale=1.0):
+    Q = rng.standard_normal((T, H, 128)) * scale
+    K = rng.standard_normal((T, H, 128))
+    V = rng.standard_normal((T, H, 128))
+    return Q, np.zeros_like(Q), K, V
+
+
+def test_one_hot_key_returns_its_value_row():
+    rng = np.random.default_rng(7)
+    T, H = 70, 2
+    Q, QM, K, V = _ops(T, H, rng)
+    Q[:] = 0.0
+    Q[:, :, 0] = 1.0
+    K[:] = 0.0
+    K[:, :, 0] = -300.0
+    K[41, :, 0] = 0.0                                         # key 41: score 0, every other -300
+    out = mxfp4.attention_from_operands(Q, QM, K, V, [0, T])
+    for h in range(H):
+        np.testing.assert_allclose(out[:, h], np.broadcast_to(V[41, h], (T, 128)), rtol=1e-12, atol=1e-12)
+
+
+def test_equal_scores_return_mean_of_v():
+    rng = np.random.default_rng(8)
+    T, H = 90, 3
+    Q, QM, K, V = _ops(T, H, rng)
+    Q[:] = 0.0
+    out = mxfp4.attention_from_operands(Q, QM, K, V, [0, 37, 90])
+    for a, b in ((0, 37), (37, 90)):
+        np.testing.assert_allclose(out[a:b], np.broadcast_to(V[a:b].mean(axis=0), (b - a, H, 128)), rtol=1e-12, atol=1e-12)
+
+
+# softmax_scale whose score factor fl32(fl32(s) * fl32(log2 e)) is exactly 1/8
+SIGMA_C8 = float(np.float32(0.0866434))
+
+
+def _lossless_inputs(cu, H, seed):
+    """Inputs for which every quantization step of the variant is exact and
+    every score (log2 units) lies within 3 of its row's maximum, so the
+    E2M1 probabilities are exact powers of two and the variant equals the
+    plain softmax attention.
+
+    Q rows: channel 0 = 16, channel 1 = 16 s (s = 0 or 1, half of each 128-row
+    block each), so the block mean is (16, 8) and the centred rows (0, +-8).
+    K rows: mu + d with the segment mean mu on the E2M1 grid and d = (0.5,
+    -0.5) or (-0.5, 0.5) in channels 0, 1, half the keys each (d has zero
+    mean).  Scores: x = c q.d = 1 - s or s - 1 (plus a per-row constant).
+    V: E2M1 grid values with a 4 in every 32-key block of every channel.
+    """
+    rng = np.random.default_rng(seed)
+    T = cu[-1]
+    q = np.zeros((T, H, 128), np.float32)
+    k = np.zeros((T, H, 128), np.float32)
+    v = rng.choice(GRID, size=(T, H, 128)) * rng.choice([-1.0, 1.0], size=(T, H, 128))
+    for a, b in zip(cu[:-1], cu[1:]):
+        L = b - a
+        assert L % 128 == 0
+        mu = rng.choice(GRID[:5], size=(H, 128)) * rng.choice([-1.0, 1.0], size=(H, 128))
+        for h in range(H):
+            s = np.concatenate([rng.permutation(np.repeat([0.0, 1.0], 64)) for _ in range(L // 128)])
+            q[a:b, h, 0] = 16.0
+            q[a:b, h, 1] = 16.0 * s
+            sign = rng.permutation(np.repeat([1.0, -1.0], L // 2))
+            k[a:b, h] = mu[h][None]
+            k[a:b, h, 0] += 0.5 * sign
+            k[a:b, h, 1] -= 0.5 * sign
+        for j in range(a, b, 32):
+            v[j, :, :] = 4.0
+    return (torch.from_numpy(q).bfloat16(), torch.from_numpy(k).bfloat16(),
+            torch.from_numpy(v.astype(np.float32)).bfloat16())
+
+
+@pytest.mark.parametrize("q_centre", [True, False])
+def test_lossless_inputs_reduce_to_plain_softmax(q_centre):
+    cu = [0, 256, 384]
+    q, k, v = _lossless_inputs(cu, 2, seed=9)
+    assert mxfp4.score_factor(SIGMA_C8) == np.float32(0.125)
+    got = mxfp4.attention_mxfp4(q, k, v, cu, SIGMA_C8, q_centre=q_centre)
+    want = exact.attention(q, k, v, cu, SIGMA_C8).numpy()
+    # the float64 softmax uses sigma * log2(e), which differs from c = 1/8 by
+    # float32 rounding (about 3e-9 relative); nothing else may differ
+    np.testing.assert_allclose(got, want, rtol=1e-8, atol=1e-8)
+    z = mxfp4.quantize_mxfp4(q, k, v, cu, SIGMA_C8, q_centre=q_centre)
+    if q_centre:
+        np.testing.assert_array_equal(z["qm"][:, :, :2], np.broadcast_to([16.0, 8.0], (3, 2, 2)))
+        assert np.all(np.abs(mxfp4.e2m1_decode(z["q_codes"][:, :, 1])) == 4.0)   # +-8 c = +-1 at scale 1/4
+
+
+def test_dropping_the_block_mean_term_fails_the_lossless_pin():
+    """Planted mistake: the centred scores without the qm . k add-back."""
+    cu = [0, 256, 384]
+    q, k, v = _lossless_inputs(cu, 2, seed=9)
+    z = mxfp4.quantize_mxfp4(q, k, v, cu, SIGMA_C8, q_centre=True)
+    ops = mxfp4.dequantized_operands(z, cu)
+    bad = mxfp4.attention_from_operands(ops["Q"], np.zeros_like(ops["QM"]), ops["K"], ops["V"], cu)
+    want = exact.attention(q, k, v, cu, SIGMA_C8).numpy()
+    assert np.abs(bad - want).max() > 0.1
+
+
+def test_segments_and_q_blocks_are_independent():
+    rng = np.random.default_rng(10)
+    T, H = 400, 2
+    cu = [0, 300, 400]
+    base = [torch.from_numpy(rng.standard_normal((T, H, 128)).astype(np.float32)).bfloat16() for _ in range(3)]
+    z0 = mxfp4.quantize_mxfp4(*base, cu, 0.088)
+    o0 = mxfp4.attention_mxfp4(*base, cu, 0.088)
+    # another segment's values change: this segment's codes and output do not
+    changed = [t.clone() for t in base]
+    for t in changed:
+        t[300:] = t[300:] * 3 + 1
+    z1 = mxfp4.quantize_mxfp4(*changed, cu, 0.088)
+    o1 = mxfp4.attention_mxfp4(*changed, cu, 0.088)
+    for name in ("q_codes", "k_codes", "v_codes", "q_e", "k_e"):
+        np.testing.assert_array_equal(z0[name][:300], z1[name][:300])
+    np.testing.assert_array_equal(o0[:300], o1[:300])
+    # Q rows of the second 128-row block change: the first block's Q codes and mean do not
+    q2 = base[0].clone()
+    q2[128:256] = q2[128:256] + 5
+    z2 = mxfp4.quantize_mxfp4(q2, base[1], base[2], cu, 0.088)
+    np.testing.assert_array_equal(z0["q_codes"][:128], z2["q_codes"][:128])
+    np.testing.assert_array_equal(z0["qm"][0], z2["qm"][0])
+    assert not np.array_equal(z0["qm"][1], z2["qm"][1])
+
+
+def test_block_mean_centring_identical_rows():
+    """A block whose rows are identical centres to zero codes; its scores are
+    the block-mean operand's alone."""
+    rng = np.random.default_rng(11)
+    T, H = 128, 2
+    row = rng.standard_normal((1, H, 128)).astype(np.float32)
+    q = torch.from_numpy(np.repeat(row, T, axis=0)).bfloat16()
+    k = torch.from_numpy(rng.standard_normal((T, H, 128)).astype(np.float32)).bfloat16()
+    z = mxfp4.quantize_mxfp4(q, k, k, [0, T], 0.088)
+    assert np.all((z["q_codes"] & 7) == 0)
+    rowf = q[0].float().numpy()
+    np.testing.assert_array_equal(z["qm"][0], rowf)
+    want = mxfp4.mx_quantize((rowf * mxfp4.score_factor(0.088)).astype(np.float32), axis=1)
+    np.testing.assert_array_equal(z["qm_codes"][0], want["codes"])
+    np.testing.assert_array_equal(z["qm_e"][0], want["e"])
+
+
+def test_fp4_error_is_bounded_on_gaussian_inputs():
+    """Gaussian inputs: the variant stays within the pages' FP4 tolerance
+    (atol 1.0, rtol 0.1 against the float oracle) and its relative RMS error
+    is a few times the E4M3 path's."""
+    rng = np.random.default_rng(12)
+    T, H = 512, 2
+    q, k, v = (torch.from_numpy(rng.standard_normal((T, H, 128)).astype(np.float32)).bfloat16() for _ in range(3))
+    cu = [0, 200, 512]
+    got = mxfp4.attention_mxfp4(q, k, v, cu, 128 ** -0.5)
+    want = exact.attention(q, k, v, cu, 128 ** -0.5).numpy()
+    assert np.all(np.abs(got - want) <= 1.0 + 0.1 * np.abs(want))
+    rel = np.linalg.norm(got - want) / np.linalg.norm(want)
+    assert 0.1 < rel < 0.35
