@@ -17,7 +17,10 @@ or, with an explicit plan and workspace (no allocation per call):
 The computation, for every segment [a, b) of cu_seqlens and every head h, is
 ``out[a:b, h] = softmax(q[a:b, h] @ k[a:b, h]^T * softmax_scale) @ v[a:b, h]``
 (FlashInfer "minimax_h3_sm120_varlen_attention_nvfp4" page), with Q/K/V
-quantized per head to E4M3 and both products on FP8 MFMA.
+quantized per head to E4M3 and both products on FP8 MFMA.  ``fmt="mxfp4"``
+selects the block-scaled FP4 variant (E2M1 operands and probabilities with
+one power-of-two scale per 32 elements; ``q_centre=True`` adds the page's Q
+block-mean centring).
 """
 from __future__ import annotations
 
@@ -47,11 +50,14 @@ class Plan:
 
     ``device=None`` uses the current CUDA/HIP device; ``device=-1`` builds a
     host-only plan that can be inspected but not run.  ``segment_scales=True``
-    quantizes every segment with its own per-head scales.
+    quantizes every segment with its own per-head scales.  ``fmt`` is
+    ``"e4m3"`` (default) or ``"mxfp4"``; ``q_centre`` (mxfp4 only) centres Q
+    by its 128-row block means.
     """
 
     def __init__(self, tokens: int, heads: int, cu_seqlens: Optional[Sequence[int]] = None,
-                 softmax_scale: Optional[float] = None, device=None, segment_scales: bool = False):
+                 softmax_scale: Optional[float] = None, device=None, segment_scales: bool = False,
+                 fmt: str = "e4m3", q_centre: bool = False):
         L = _lib.lib()
         if cu_seqlens is None:
             cu_seqlens = [0, tokens]
@@ -68,10 +74,15 @@ class Plan:
         self.cu_seqlens = tuple(cu)
         self.softmax_scale = float(DEFAULT_SCALE if softmax_scale is None else softmax_scale)
         self.segment_scales = bool(segment_scales)
+        if fmt not in ("e4m3", "mxfp4"):
+            raise ValueError(f"fmt must be 'e4m3' or 'mxfp4' (got {fmt!r})")
+        self.fmt = fmt
+        self.q_centre = bool(q_centre)
         arr = (ctypes.c_int32 * len(cu))(*cu)
         h = ctypes.c_void_p()
         self._h = None
-        flags = _lib.PLAN_SEGMENT_SCALES if self.segment_scales else 0
+        flags = ((_lib.PLAN_SEGMENT_SCALES if self.segment_scales else 0)
+                 | (_lib.PLAN_MXFP4 if fmt == "mxfp4" else 0) | (_lib.PLAN_Q_CENTRE if self.q_centre else 0))
         _lib.check(L.fp8attn_plan_ex(ctypes.byref(h), self.tokens, self.heads, arr, len(cu) - 1,
                                      ctypes.c_float(self.softmax_scale), self.device_index, flags),
                    "fp8attn_plan_ex")
@@ -87,10 +98,10 @@ class Plan:
         return torch.device("cuda", self.device_index)
 
     def info(self) -> Dict[str, int]:
-        buf = (ctypes.c_int64 * 10)()
+        buf = (ctypes.c_int64 * _lib.PLAN_INFO_LEN)()
         _lib.check(_lib.lib().fp8attn_plan_info(self._h, buf), "fp8attn_plan_info")
         keys = ["tokens", "heads", "num_segments", "workspace_rows", "work_items", "stat_chunks",
-                "query_tile", "key_tile", "segment_scales", "partial_slots"]
+                "query_tile", "key_tile", "segment_scales", "partial_slots", "mxfp4", "q_centre"]
         return dict(zip(keys, list(buf)))
 
     def work_items(self):
@@ -112,7 +123,8 @@ class Plan:
                                                        ctypes.byref(ptr), dims), "fp8attn_workspace_region")
         off = ptr.value - workspace.data_ptr()
         shape = tuple(dims)
-        if which in (_lib.REGION_Q, _lib.REGION_K, _lib.REGION_V):
+        if which in (_lib.REGION_Q, _lib.REGION_K, _lib.REGION_V, _lib.REGION_Q_BSCALES, _lib.REGION_K_BSCALES,
+                     _lib.REGION_V_BSCALES, _lib.REGION_QM_CODES, _lib.REGION_QM_SCALES):
             n = shape[0] * shape[1] * shape[2]
             return workspace[off: off + n].view(shape)
         n = shape[0] * shape[1] * shape[2]
@@ -194,13 +206,15 @@ _PLANS: Dict[Tuple, Plan] = {}
 
 
 def get_plan(tokens: int, heads: int, cu_seqlens: Sequence[int], softmax_scale: float, device: int,
-             segment_scales: bool = False) -> Plan:
-    """Plans are cached per (cu_seqlens, heads, scale, device, scale mode), as the FlashInfer page
-    caches its segment plan per (cu_seqlens, heads, device).  A plan holds only small tables."""
-    key = (tuple(int(x) for x in cu_seqlens), int(heads), float(softmax_scale), int(device), bool(segment_scales))
+             segment_scales: bool = False, fmt: str = "e4m3", q_centre: bool = False) -> Plan:
+    """Plans are cached per (cu_seqlens, heads, scale, device, quantization mode), as the FlashInfer
+    page caches its segment plan per (cu_seqlens, heads, device).  A plan holds only small tables."""
+    key = (tuple(int(x) for x in cu_seqlens), int(heads), float(softmax_scale), int(device), bool(segment_scales),
+           fmt, bool(q_centre))
     p = _PLANS.get(key)
     if p is None:
-        p = Plan(tokens, heads, cu_seqlens, softmax_scale, device, segment_scales=segment_scales)
+        p = Plan(tokens, heads, cu_seqlens, softmax_scale, device, segment_scales=segment_scales, fmt=fmt,
+                 q_centre=q_centre)
         _PLANS[key] = p
     return p
 
@@ -208,11 +222,13 @@ def get_plan(tokens: int, heads: int, cu_seqlens: Sequence[int], softmax_scale: 
 def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: Optional[Sequence[int]] = None,
               softmax_scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
               return_lse: bool = False, causal: bool = False, workspace: Optional[torch.Tensor] = None,
-              segment_scales: bool = False):
+              segment_scales: bool = False, fmt: str = "e4m3", q_centre: bool = False):
     """Dense non-causal FP8 attention over packed [tokens, heads, 128] BF16 q/k/v.
 
     ``cu_seqlens`` is a host sequence of segment boundaries (None = one segment).
     ``segment_scales`` quantizes every segment with its own per-head scales.
+    ``fmt="mxfp4"`` runs the block-scaled FP4 variant (``q_centre`` adds Q
+    block-mean centring); it returns no LSE.
     Causal attention is not supported and raises (there is no fallback path).
     """
     if causal:
@@ -227,7 +243,7 @@ def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: Opt
         cu_seqlens = cu_seqlens.tolist()
     scale = DEFAULT_SCALE if softmax_scale is None else float(softmax_scale)
     dev = q.device.index if q.device.index is not None else torch.cuda.current_device()
-    plan = get_plan(T, H, cu_seqlens, scale, dev, segment_scales)
+    plan = get_plan(T, H, cu_seqlens, scale, dev, segment_scales, fmt, q_centre)
     ws = workspace if workspace is not None else plan.new_workspace()
     quantize(plan, q, k, v, ws)
     lse = torch.empty((H, T), dtype=torch.float32, device=q.device) if return_lse else None

@@ -16,7 +16,11 @@ OK, EINVAL, EUNSUPPORTED, ENOMEM, EWORKSPACE, EHIP = range(6)
 STATUS_NAMES = {0: "FP8ATTN_OK", 1: "FP8ATTN_EINVAL", 2: "FP8ATTN_EUNSUPPORTED",
                 3: "FP8ATTN_ENOMEM", 4: "FP8ATTN_EWORKSPACE", 5: "FP8ATTN_EHIP"}
 REGION_Q, REGION_K, REGION_V, REGION_SCALES, REGION_MU, REGION_ROWMAP = range(6)
+REGION_Q_BSCALES, REGION_K_BSCALES, REGION_V_BSCALES, REGION_QM_CODES, REGION_QM_SCALES = range(6, 11)
 PLAN_SEGMENT_SCALES = 1          # FP8ATTN_PLAN_SEGMENT_SCALES
+PLAN_MXFP4 = 2                   # FP8ATTN_PLAN_MXFP4
+PLAN_Q_CENTRE = 4                # FP8ATTN_PLAN_Q_CENTRE
+PLAN_INFO_LEN = 12
 
 # Every symbol include/fp8attn.h declares, with (restype, argtypes).
 _i64p = ctypes.POINTER(ctypes.c_int64)

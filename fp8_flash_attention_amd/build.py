@@ -16,7 +16,7 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libfp8attn.so")
 ARCH = "gfx950"
 
-SOURCES = ["api.cpp", "quantize.hip", "attention.hip", "skeleton.hip"]
+SOURCES = ["api.cpp", "quantize.hip", "attention.hip", "attention_mx.hip", "skeleton.hip"]
 
 # -Xclang -target-feature -Xclang -packed-fp32-ops keeps the device compiler from
 # emitting packed FP32 (v_pk_*_f32) instructions.

@@ -29,6 +29,8 @@ struct fp8attn_plan_s {
   int32_t nseg = 0;
   int32_t seg_scales = 0;         // FP8ATTN_PLAN_SEGMENT_SCALES
   int32_t nscale = 1;             // scale sets: nseg with segment scales, else 1
+  int32_t mx = 0;                 // FP8ATTN_PLAN_MXFP4
+  int32_t q_centre = 0;           // FP8ATTN_PLAN_Q_CENTRE
   float scale = 0.f;
   int device = -1;
   std::vector<int32_t> cu;
@@ -60,6 +62,28 @@ fp8attn_status fail(fp8attn_status s, const std::string& msg) {
 }
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// FP4 plans: codes of half the size, block scales, block-mean operand.
+WorkspaceLayout make_layout_mx(int64_t rows, int heads, int nseg, int nchunks) {
+  WorkspaceLayout w{};
+  w.rows = rows;
+  const size_t codes = (size_t)heads * rows * kMxRow;
+  const size_t scales = (size_t)heads * rows * 4;
+  const size_t qblocks = (size_t)heads * (rows / kMxQBlock);
+  size_t off = 0;
+  w.q_off = off; off = align_up(off + codes, 256);
+  w.k_off = off; off = align_up(off + codes, 256);
+  w.v_off = off; off = align_up(off + codes, 256);
+  w.qs_off = off; off = align_up(off + scales, 256);
+  w.ks_off = off; off = align_up(off + scales, 256);
+  w.vs_off = off; off = align_up(off + scales, 256);   // rows/64 tiles x 256 bytes
+  w.qm_off = off; off = align_up(off + qblocks * kMxRow, 256);
+  w.qms_off = off; off = align_up(off + qblocks * 4, 256);
+  w.mu_off = off; off = align_up(off + sizeof(float) * (size_t)nseg * heads * kHeadDim, 256);
+  w.kstat_off = off; off = align_up(off + sizeof(KStat) * (size_t)nchunks * heads * kHeadDim, 256);
+  w.total = off;
+  return w;
+}
 
 WorkspaceLayout make_layout(int64_t rows, int heads, int nseg, int nscale, int nchunks, int64_t npieces) {
   WorkspaceLayout w{};
@@ -98,7 +122,7 @@ WorkspaceLayout make_layout(int64_t rows, int heads, int nseg, int nscale, int n
 // log-sum-exp combination over key ranges that the pages use to merge partial
 // attention (sglang PR "[DSA] Enable tilelang fp8_e4m3 KV cache ...", note that
 // the FP8 path must return the LSE for cross-rank reduction).
-void build_items(fp8attn_plan_s* p, int cus) {
+void build_items(fp8attn_plan_s* p, int cus, bool allow_split) {
   const int slots = kWgPerCu * cus;
   std::vector<int> order(p->nseg);
   for (int s = 0; s < p->nseg; s++) order[s] = s;
@@ -121,7 +145,7 @@ void build_items(fp8attn_plan_s* p, int cus) {
     part.assign(list.begin() + b, list.begin() + e);
     std::stable_sort(part.begin(), part.end(), [&](const int4& u, const int4& v) { return tiles(u) > tiles(v); });
     const size_t R = part.size() % (size_t)slots;
-    if (R == 0 || 2 * R > (size_t)cus) continue;
+    if (!allow_split || R == 0 || 2 * R > (size_t)cus) continue;
     std::vector<int4> tail(part.end() - R, part.end()), pieces;
     part.resize(part.size() - R);
     for (const int4& it : tail) {
@@ -183,7 +207,12 @@ fp8attn_status fp8attn_plan_ex(fp8attn_plan_t* plan_out, int64_t tokens, int32_t
                                int32_t device, uint32_t flags) {
   if (plan_out == nullptr) return fail(FP8ATTN_EINVAL, "plan_out is NULL");
   *plan_out = nullptr;
-  if ((flags & ~FP8ATTN_PLAN_SEGMENT_SCALES) != 0) return fail(FP8ATTN_EINVAL, "unknown plan flags");
+  if ((flags & ~(FP8ATTN_PLAN_SEGMENT_SCALES | FP8ATTN_PLAN_MXFP4 | FP8ATTN_PLAN_Q_CENTRE)) != 0)
+    return fail(FP8ATTN_EINVAL, "unknown plan flags");
+  if ((flags & FP8ATTN_PLAN_Q_CENTRE) && !(flags & FP8ATTN_PLAN_MXFP4))
+    return fail(FP8ATTN_EINVAL, "FP8ATTN_PLAN_Q_CENTRE needs FP8ATTN_PLAN_MXFP4");
+  if ((flags & FP8ATTN_PLAN_MXFP4) && (flags & FP8ATTN_PLAN_SEGMENT_SCALES))
+    return fail(FP8ATTN_EINVAL, "FP8ATTN_PLAN_MXFP4 does not take FP8ATTN_PLAN_SEGMENT_SCALES");
   if (cu == nullptr) return fail(FP8ATTN_EINVAL, "cu_seqlens_host is NULL");
   if (num_segments < 1) return fail(FP8ATTN_EINVAL, "num_segments must be >= 1");
   if (heads < 1) return fail(FP8ATTN_EINVAL, "heads must be >= 1");
@@ -206,6 +235,8 @@ fp8attn_status fp8attn_plan_ex(fp8attn_plan_t* plan_out, int64_t tokens, int32_t
   p->device = device;
   p->seg_scales = (flags & FP8ATTN_PLAN_SEGMENT_SCALES) ? 1 : 0;
   p->nscale = p->seg_scales ? num_segments : 1;
+  p->mx = (flags & FP8ATTN_PLAN_MXFP4) ? 1 : 0;
+  p->q_centre = (flags & FP8ATTN_PLAN_Q_CENTRE) ? 1 : 0;
   p->cu.assign(cu, cu + num_segments + 1);
   int64_t row = 0;
   int32_t chunk = 0;
@@ -232,12 +263,13 @@ fp8attn_status fp8attn_plan_ex(fp8attn_plan_t* plan_out, int64_t tokens, int32_t
     int n = 0;
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, device) == hipSuccess && n > 0) cus = n;
   }
-  build_items(p, std::max(1, cus / kNumXcd));
+  build_items(p, std::max(1, cus / kNumXcd), !p->mx);
   if (p->npieces >= (int64_t)1 << 23) {
     delete p;
     return fail(FP8ATTN_EUNSUPPORTED, "too many split work items");
   }
-  p->ws = make_layout(row, heads, num_segments, p->nscale, (int)p->chunks.size(), p->npieces);
+  p->ws = p->mx ? make_layout_mx(row, heads, num_segments, (int)p->chunks.size())
+                : make_layout(row, heads, num_segments, p->nscale, (int)p->chunks.size(), p->npieces);
 
   if (device >= 0) {
     DeviceGuard g(device);
@@ -338,6 +370,17 @@ fp8attn_status fp8attn_quantize(fp8attn_plan_t p, const void* q, const void* k, 
   a.seg_scales = p->seg_scales;
   a.rows = p->ws.rows;
   a.softmax_scale = p->scale;
+  a.mx = p->mx;
+  a.q_centre = p->q_centre;
+  if (p->mx) {
+    a.bscale[0] = ws + p->ws.qs_off;
+    a.bscale[1] = ws + p->ws.ks_off;
+    a.bscale[2] = ws + p->ws.vs_off;
+    a.qm_codes = ws + p->ws.qm_off;
+    a.qm_scales = ws + p->ws.qms_off;
+    a.scales = nullptr;
+    a.amax = nullptr;
+  }
   hipError_t e = launch_quantize(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(FP8ATTN_EHIP, std::string("quantize launch failed: ") + hipGetErrorString(e));
   return FP8ATTN_OK;
@@ -356,9 +399,32 @@ fp8attn_status fp8attn_forward(fp8attn_plan_t p, void* workspace, size_t workspa
     if (!strides_ok(out_strides)) return fail(FP8ATTN_EINVAL, "out strides must be positive multiples of 8");
     if (lse != nullptr && ((uintptr_t)lse & 3) != 0) return fail(FP8ATTN_EINVAL, "lse must be 4-byte aligned");
   }
+  if (p->mx && lse != nullptr) return fail(FP8ATTN_EUNSUPPORTED, "lse is not available for FP8ATTN_PLAN_MXFP4 plans");
   DeviceGuard g(p->device);
   if (!g.ok) return fail(FP8ATTN_EHIP, "cannot select device");
   uint8_t* ws = static_cast<uint8_t*>(workspace);
+  if (p->mx) {
+    MxAttentionArgs m{};
+    m.q_codes = ws + p->ws.q_off;
+    m.k_codes = ws + p->ws.k_off;
+    m.v_codes = ws + p->ws.v_off;
+    m.q_scales = ws + p->ws.qs_off;
+    m.k_scales = ws + p->ws.ks_off;
+    m.v_scales = ws + p->ws.vs_off;
+    m.qm_codes = ws + p->ws.qm_off;
+    m.qm_scales = ws + p->ws.qms_off;
+    m.segs = p->d_segs;
+    m.items = p->d_items;
+    m.out = static_cast<uint16_t*>(out);
+    m.os0 = p->tokens > 0 ? out_strides[0] : 0;
+    m.os1 = p->tokens > 0 ? out_strides[1] : 0;
+    m.rows = p->ws.rows;
+    m.nitems = p->real_items > 0 ? (int32_t)p->items.size() : 0;
+    m.q_centre = p->q_centre;
+    hipError_t e = launch_attention_mx(m, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(FP8ATTN_EHIP, std::string("attention launch failed: ") + hipGetErrorString(e));
+    return FP8ATTN_OK;
+  }
   AttentionArgs a{};
   a.q_codes = ws + p->ws.q_off;
   a.k_codes = ws + p->ws.k_off;
@@ -413,6 +479,21 @@ fp8attn_status fp8attn_workspace_region(fp8attn_plan_t p, const void* workspace,
     return FP8ATTN_OK;
   }
   if (ws == nullptr) return fail(FP8ATTN_EWORKSPACE, "workspace is NULL");
+  if (p->mx) {
+    switch (which) {
+      case FP8ATTN_REGION_Q_CODES: *ptr_out = ws + p->ws.q_off; dims_out[0] = H; dims_out[1] = R; dims_out[2] = kMxRow; break;
+      case FP8ATTN_REGION_K_CODES: *ptr_out = ws + p->ws.k_off; dims_out[0] = H; dims_out[1] = R; dims_out[2] = kMxRow; break;
+      case FP8ATTN_REGION_V_CODES: *ptr_out = ws + p->ws.v_off; dims_out[0] = H; dims_out[1] = R / kBN; dims_out[2] = kMxTile; break;
+      case FP8ATTN_REGION_Q_BSCALES: *ptr_out = ws + p->ws.qs_off; dims_out[0] = H; dims_out[1] = R; dims_out[2] = 4; break;
+      case FP8ATTN_REGION_K_BSCALES: *ptr_out = ws + p->ws.ks_off; dims_out[0] = H; dims_out[1] = R; dims_out[2] = 4; break;
+      case FP8ATTN_REGION_V_BSCALES: *ptr_out = ws + p->ws.vs_off; dims_out[0] = H; dims_out[1] = R / kBN; dims_out[2] = kMxTileScales; break;
+      case FP8ATTN_REGION_QM_CODES: *ptr_out = ws + p->ws.qm_off; dims_out[0] = H; dims_out[1] = R / kMxQBlock; dims_out[2] = kMxRow; break;
+      case FP8ATTN_REGION_QM_SCALES: *ptr_out = ws + p->ws.qms_off; dims_out[0] = H; dims_out[1] = R / kMxQBlock; dims_out[2] = 4; break;
+      case FP8ATTN_REGION_MU: *ptr_out = ws + p->ws.mu_off; dims_out[0] = p->nseg; dims_out[1] = H; dims_out[2] = D; break;
+      default: return fail(FP8ATTN_EINVAL, "region not available for FP8ATTN_PLAN_MXFP4 plans");
+    }
+    return FP8ATTN_OK;
+  }
   switch (which) {
     case FP8ATTN_REGION_Q_CODES: *ptr_out = ws + p->ws.q_off; dims_out[0] = H; dims_out[1] = R; dims_out[2] = D; break;
     case FP8ATTN_REGION_K_CODES: *ptr_out = ws + p->ws.k_off; dims_out[0] = H; dims_out[1] = R; dims_out[2] = D; break;
@@ -424,7 +505,7 @@ fp8attn_status fp8attn_workspace_region(fp8attn_plan_t p, const void* workspace,
   return FP8ATTN_OK;
 }
 
-fp8attn_status fp8attn_plan_info(fp8attn_plan_t p, int64_t info[10]) {
+fp8attn_status fp8attn_plan_info(fp8attn_plan_t p, int64_t info[12]) {
   if (p == nullptr || info == nullptr) return fail(FP8ATTN_EINVAL, "NULL argument");
   info[0] = p->tokens;
   info[1] = p->heads;
@@ -436,6 +517,8 @@ fp8attn_status fp8attn_plan_info(fp8attn_plan_t p, int64_t info[10]) {
   info[7] = kBN;
   info[8] = p->seg_scales;
   info[9] = p->npieces;
+  info[10] = p->mx;
+  info[11] = p->q_centre;
   return FP8ATTN_OK;
 }
 

@@ -55,10 +55,22 @@ struct KStat {
   float mx;
 };
 
+// Block-scaled FP4 operands (plans made with FP8ATTN_PLAN_MXFP4): E2M1 codes,
+// two per byte (low nibble first), one E8M0 scale byte per 32 elements.
+constexpr int kMxBlock = 32;               // elements per scale
+constexpr int kMxRow = kHeadDim / 2;       // code bytes of one Q or K row
+constexpr int kMxQBlock = 128;             // Q rows per mean block
+constexpr int kMxTile = kBN * kHeadDim / 2;   // code bytes of one K (or V^T) tile
+constexpr int kMxTileScales = 256;         // scale bytes of one K (or V^T) tile
+
 struct WorkspaceLayout {
   int64_t rows;        // workspace rows (all segments padded + guard)
   int64_t npieces;     // partial slots of split work items
   size_t q_off, k_off, v_off, scale_off, mu_off, kstat_off, amax_off;
+  // FP4 plans: Q, K scales [H][rows][4] (blocks in byte order 0, 2, 1, 3);
+  // V^T scales [H][rows/64][256] (tile-major, byte (32*(key/32) + d%32)*4 + d/32);
+  // block-mean codes [H][rows/128][64] and scales [H][rows/128][4] (order 0, 2, 1, 3)
+  size_t qs_off, ks_off, vs_off, qm_off, qms_off;
   size_t part_o_off;   // float [npieces][kBM][128]: normalized partial outputs (scaled by s_v)
   size_t part_w_off;   // float [npieces][kBM]: log2 weight of each partial row
   size_t part_lse_off; // float [npieces][kBM]: natural-log LSE of each partial row
@@ -80,6 +92,12 @@ struct QuantizeArgs {
   int32_t seg_scales;        // 1: one scale per (tensor, segment, head)
   int64_t rows;
   float softmax_scale;       // fixes Q's scale (see k_finalize)
+  // FP4 plans
+  int32_t mx;                // 1: block-scaled FP4 operands (codes[] and the fields below)
+  int32_t q_centre;          // 1: Q centred by its 128-row block mean
+  uint8_t* bscale[3];        // Q, K, V^T block scales (WorkspaceLayout)
+  uint8_t* qm_codes;
+  uint8_t* qm_scales;
 };
 
 struct AttentionArgs {
@@ -117,8 +135,28 @@ struct CombineArgs {
   int64_t tokens;
 };
 
+// FP4 attention: codes and block scales as in WorkspaceLayout.
+struct MxAttentionArgs {
+  const uint8_t* q_codes;
+  const uint8_t* k_codes;
+  const uint8_t* v_codes;
+  const uint8_t* q_scales;
+  const uint8_t* k_scales;
+  const uint8_t* v_scales;
+  const uint8_t* qm_codes;   // used with q_centre
+  const uint8_t* qm_scales;
+  const SegInfo* segs;
+  const int4* items;         // work items (no key splits)
+  uint16_t* out;             // bf16
+  int64_t os0, os1;
+  int64_t rows;
+  int32_t nitems;
+  int32_t q_centre;
+};
+
 hipError_t launch_quantize(const QuantizeArgs& a, hipStream_t stream);
 hipError_t launch_attention(const AttentionArgs& a, hipStream_t stream);
+hipError_t launch_attention_mx(const MxAttentionArgs& a, hipStream_t stream);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t stream);
 
 }  // namespace fp8attn

@@ -45,7 +45,7 @@ __device__ __forceinline__ uint32_t cvt4(float a, float b, float c, float d) {
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_stats(QuantizeArgs a) {
   const int c = blockIdx.x;
-  const int tensor = blockIdx.z;
+  const int tensor = a.mx ? 1 : blockIdx.z;   // FP4 plans need only K's statistics
   const int t = threadIdx.x;
   const int h = blockIdx.y * 16 + t / 16;
   const int c0 = (t % 16) * 8;
@@ -142,6 +142,22 @@ __global__ __launch_bounds__(128) void k_finalize(QuantizeArgs a) {
   const int h = blockIdx.x;
   const int d = threadIdx.x;
   float qa = 0.f, va = 0.f;
+  if (a.mx) {
+    // FP4 plans: the K means only (the block scales are set by the pack pass)
+    for (int s = 0; s < a.nseg; s++) {
+      const SegInfo si = a.segs[s];
+      const int nch = (si.len + kStatChunk - 1) / kStatChunk;
+      float mu = 0.f;
+      if (si.len > 0) {
+        double sum = 0.0;
+#pragma unroll 8
+        for (int c = si.chunk0; c < si.chunk0 + nch; c++) sum = sum + a.kstat[((int64_t)c * a.heads + h) * kHeadDim + d].sum;
+        mu = (float)(sum / (double)si.len);
+      }
+      a.mu[((int64_t)s * a.heads + h) * kHeadDim + d] = mu;
+    }
+    return;
+  }
   if (!a.seg_scales) {
     for (int c = d; c < a.nchunks; c += 128) {
       qa = fmaxf(qa, a.amax[(int64_t)c * a.heads + h]);
@@ -283,18 +299,212 @@ __global__ __launch_bounds__(256) void k_pack(QuantizeArgs a) {
   *reinterpret_cast<uint4*>(dst + 16) = make_uint4(w[4], w[5], w[6], w[7]);
 }
 
+
+// ---------------------------------------------------------------------------
+// Block-scaled FP4 pack (plans made with FP8ATTN_PLAN_MXFP4).
+//
+// FlashInfer "minimax_h3_sm120_varlen_attention_nvfp4" page, description of
+// the operands: E2M1 codes with one scale per block of elements along the
+// contraction axis, K centred by its segment's per-channel mean, Q centred by
+// the mean of its 128-row block (the mean term is added back in the attention
+// kernel).  On gfx950's scaled matrix products the scale is an E8M0 power of
+// two per 32 elements: 2^e with e the smallest integer for which
+// amax <= 6 * 2^e, and codes E2M1(x * 2^-e) (round to nearest even).  The
+// score factor c = softmax_scale * log2(e) is folded into Q (and into the
+// block mean) before quantization, so scores come out in log2 units.
+// ---------------------------------------------------------------------------
+
+// Smallest e with amax <= 6 * 2^e, clamped to [-127, 126]: amax = f * 2^E with
+// f in [1, 2) needs e = E - 2 when f <= 1.5 and E - 1 above; zero and
+// subnormal amax (below 2^-126) clamp to -127.
+__device__ __forceinline__ int mx_exp(float amax) {
+  const uint32_t u = __float_as_uint(amax);
+  const int ef = (int)((u >> 23) & 255u);
+  if (ef == 0) return -127;
+  const int e = ef - 129 + ((u & 0x7fffffu) > 0x400000u ? 1 : 0);
+  return e < -127 ? -127 : e;
+}
+
+// 2^-e as a float (e in [-127, 126]: 127 - e in [1, 254], a normal float).
+__device__ __forceinline__ float mx_inv_scale(int e) { return __uint_as_float((uint32_t)(127 - e) << 23); }
+
+// E2M1 codes of 8 values (already divided by the block scale; the products
+// by a power of two are exact), two per byte, low nibble first.
+__device__ __forceinline__ uint32_t cvt8_fp4(const float y[8]) {
+  uint32_t r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, y[0], y[1], 1.0f, 0);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, y[2], y[3], 1.0f, 1);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, y[4], y[5], 1.0f, 2);
+  return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, y[6], y[7], 1.0f, 3);
+}
+
+// Byte position of channel block j (0..3) in a row's 4 scale bytes: blocks
+// 0, 2, 1, 3, so that lanes reading channels 32*(lane/32) + 64*k find their
+// scales for k = 0, 1 in one 16-bit word.
+__device__ __forceinline__ int mx_scale_pos(int j) { return ((j & 1) << 1) | (j >> 1); }
+
+// One row of 128 channels, 16 threads x 8 channels (threads 4j..4j+3 of the 16
+// hold block j): codes and the block exponents of y.
+__device__ __forceinline__ void mx_row(const float y[8], uint8_t* code_row, uint8_t* scale_row, int tq, bool live) {
+  float m = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; i++) m = fmaxf(m, fabsf(y[i]));
+  m = fmaxf(m, __shfl_xor(m, 1, 4));
+  m = fmaxf(m, __shfl_xor(m, 2, 4));
+  const int e = mx_exp(m);
+  const float inv = mx_inv_scale(e);
+  float z[8];
+#pragma unroll
+  for (int i = 0; i < 8; i++) z[i] = y[i] * inv;
+  const uint32_t code = live ? cvt8_fp4(z) : 0u;
+  *reinterpret_cast<uint32_t*>(code_row + 4 * tq) = code;
+  if ((tq & 3) == 0) scale_row[mx_scale_pos(tq >> 2)] = live ? (uint8_t)(e + 127) : 0;
+}
+
+// grid = (ngroups, H, 3), block = 256.  tensor 0 (Q): even groups take a
+// 128-row mean block (two groups), odd groups return; tensor 1 (K) and 2 (V):
+// one 64-row group.  Rows past a segment's end and guard rows get zero codes
+// and zero scale bytes.
+__global__ __launch_bounds__(256) void k_pack_mx(QuantizeArgs a) {
+  __shared__ float tile[kPackRows][kHeadDim + 1];
+  __shared__ float qm_s[kHeadDim];
+  const int g = blockIdx.x;
+  const int h = blockIdx.y;
+  const int tensor = blockIdx.z;
+  const int t = threadIdx.x;
+  if (tensor == 0 && (g & 1)) return;
+  const int seg = a.group_seg[g];
+  const int64_t R = (int64_t)g * kPackRows;
+  SegInfo si{0, 0, 0, 0};
+  if (seg >= 0) si = a.segs[seg];
+  const int rel0 = seg >= 0 ? (int)(R - si.row0) : 0;   // segment-relative first row
+  const int nreal = seg >= 0 ? max(0, min(tensor == 0 ? kMxQBlock : kPackRows, si.len - rel0)) : 0;
+  const int tq = t % 16;
+  const int c0 = tq * 8;
+  const uint16_t* base = a.x[tensor] + (int64_t)h * a.hs[tensor] + c0;
+  const int64_t ts = a.ts[tensor];
+  const float cf = a.softmax_scale * 1.4426950408889634f;   // score factor c
+
+  if (tensor == 0) {
+    // block mean: thread d sums the block's rows in order (float64)
+    if (t < kHeadDim) {
+      float qm = 0.f;
+      if (a.q_centre && nreal > 0) {
+        const uint16_t* col = a.x[0] + (int64_t)h * a.hs[0] + t + (int64_t)(si.start + rel0) * ts;
+        double sum = 0.0;
+#pragma unroll 8
+        for (int i = 0; i < nreal; i++) sum = sum + (double)bf16_to_f32(col[(int64_t)i * ts]);
+        qm = (float)(sum / (double)nreal);
+      }
+      qm_s[t] = qm;
+      // the block-mean operand fl32(qm * c), quantized like a Q row: lanes of
+      // one wave hold channels 64*(t/64) .. +64, two blocks of 32
+      const float y = qm * cf;
+      float m = fabsf(y);
+#pragma unroll
+      for (int off = 16; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 32));
+      const int e = mx_exp(m);
+      const uint32_t c = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, y * mx_inv_scale(e), 0.f, 1.0f, 0) & 15u;
+      const uint32_t hi = __shfl_down(c, 1, 64);
+      const int64_t blk = (int64_t)h * (a.rows / kMxQBlock) + R / kMxQBlock;
+      if ((t & 1) == 0) a.qm_codes[blk * kMxRow + t / 2] = (uint8_t)(c | (hi << 4));
+      if ((t & 31) == 0) a.qm_scales[blk * 4 + mx_scale_pos(t >> 5)] = nreal > 0 ? (uint8_t)(e + 127) : 0;
+    }
+    __syncthreads();
+    float qm[8];
+#pragma unroll
+    for (int i = 0; i < 8; i++) qm[i] = qm_s[c0 + i];
+#pragma unroll
+    for (int pass = 0; pass < kMxQBlock / 16; pass++) {
+      const int i = pass * 16 + t / 16;
+      float y[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+      const bool live = i < nreal;
+      if (live) {
+        const uint4 v = *reinterpret_cast<const uint4*>(base + (int64_t)(si.start + rel0 + i) * ts);
+        float f[8];
+        unpack8(v, f);
+#pragma unroll
+        for (int j = 0; j < 8; j++) y[j] = (f[j] - qm[j]) * cf;   // fl32(fl32(q - qm) * c)
+      }
+      const int64_t row = (int64_t)h * a.rows + R + i;
+      mx_row(y, a.codes[0] + row * kMxRow, a.bscale[0] + row * 4, tq, live);
+    }
+    return;
+  }
+
+  if (tensor == 1) {
+    float mu[8];
+#pragma unroll
+    for (int i = 0; i < 8; i++) mu[i] = seg >= 0 ? a.mu[((int64_t)seg * a.heads + h) * kHeadDim + c0 + i] : 0.f;
+#pragma unroll
+    for (int pass = 0; pass < kPackRows / 16; pass++) {
+      const int i = pass * 16 + t / 16;
+      float y[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+      const bool live = i < nreal;
+      if (live) {
+        const uint4 v = *reinterpret_cast<const uint4*>(base + (int64_t)(si.start + rel0 + i) * ts);
+        float f[8];
+        unpack8(v, f);
+#pragma unroll
+        for (int j = 0; j < 8; j++) y[j] = f[j] - mu[j];            // fl32(k - mu)
+      }
+      const int64_t row = (int64_t)h * a.rows + R + i;
+      mx_row(y, a.codes[1] + row * kMxRow, a.bscale[1] + row * 4, tq, live);
+    }
+    return;
+  }
+
+  // V: the group's 64 keys x 128 channels through LDS, then per (channel,
+  // 32-key block) scales and transposed codes: thread t -> channel d = t/2,
+  // keys 32*(t%2) .. +32 (padding keys are zeros, which leave amax unchanged).
+#pragma unroll
+  for (int pass = 0; pass < kPackRows / 16; pass++) {
+    const int i = pass * 16 + t / 16;
+    float f[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if (i < nreal) {
+      const uint4 v = *reinterpret_cast<const uint4*>(base + (int64_t)(si.start + rel0 + i) * ts);
+      unpack8(v, f);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; j++) tile[i][c0 + j] = f[j];
+  }
+  __syncthreads();
+  const int d = t / 2;
+  const int kh = t % 2;
+  float m = 0.f;
+#pragma unroll
+  for (int j = 0; j < 32; j++) m = fmaxf(m, fabsf(tile[32 * kh + j][d]));
+  const bool live = 32 * kh < nreal;
+  const int e = mx_exp(m);
+  const float inv = mx_inv_scale(e);
+  uint32_t w[4];
+#pragma unroll
+  for (int q = 0; q < 4; q++) {
+    float z[8];
+#pragma unroll
+    for (int j = 0; j < 8; j++) z[j] = tile[32 * kh + 8 * q + j][d] * inv;
+    w[q] = live ? cvt8_fp4(z) : 0u;
+  }
+  const int64_t tile_idx = (int64_t)h * (a.rows / kBN) + g;    // a 64-row group is one key tile
+  uint8_t* dst = a.codes[2] + tile_idx * kMxTile + d * (kBN / 2) + 16 * kh;
+  *reinterpret_cast<uint4*>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
+  a.bscale[2][tile_idx * kMxTileScales + (32 * kh + d % 32) * 4 + d / 32] = live ? (uint8_t)(e + 127) : 0;
+}
+
 }  // namespace
 
 hipError_t launch_quantize(const QuantizeArgs& a, hipStream_t stream) {
   if (a.nchunks > 0) {
-    hipLaunchKernelGGL(k_stats, dim3(a.nchunks, (a.heads + 15) / 16, 3), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(k_stats, dim3(a.nchunks, (a.heads + 15) / 16, a.mx ? 1 : 3), dim3(256), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL(k_finalize, dim3(a.heads), dim3(128), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_pack, dim3(a.ngroups, a.heads, 3), dim3(256), 0, stream, a);
+  if (a.mx)
+    hipLaunchKernelGGL(k_pack_mx, dim3(a.ngroups, a.heads, 3), dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL(k_pack, dim3(a.ngroups, a.heads, 3), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

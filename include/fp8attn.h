@@ -64,8 +64,20 @@ typedef enum {
   FP8ATTN_REGION_SCALES = 3,  /* float [3][S][H]: rows Q, K, V; S = num_segments with
                                  FP8ATTN_PLAN_SEGMENT_SCALES, else 1                   */
   FP8ATTN_REGION_MU = 4,      /* float [num_segments][H][128]: per-channel K means     */
-  FP8ATTN_REGION_ROWMAP = 5   /* plan-owned device int32 [num_segments]: first workspace
+  FP8ATTN_REGION_ROWMAP = 5,  /* plan-owned device int32 [num_segments]: first workspace
                                  row of each segment (rows are padded per segment)    */
+  /* FP8ATTN_PLAN_MXFP4 plans (E2M1 codes two per byte, low nibble first; E8M0
+     scale bytes, one per 32 elements).  For these plans Q_CODES and K_CODES are
+     uint8 [H][rows][64], V_CODES is uint8 [H][rows/64][128][32] (one 4 KB
+     block per 64-key tile: channel d, keys 2i and 2i+1 of the tile in byte i of
+     the channel's 32), and SCALES is not used.                                 */
+  FP8ATTN_REGION_Q_BSCALES = 6,  /* uint8 [H][rows][4]: channel blocks 0, 2, 1, 3     */
+  FP8ATTN_REGION_K_BSCALES = 7,  /* uint8 [H][rows][4]: channel blocks 0, 2, 1, 3     */
+  FP8ATTN_REGION_V_BSCALES = 8,  /* uint8 [H][rows/64][256]: per tile, byte
+                                    4*(32*b + d%32) + d/32 for channel d, keys
+                                    32b .. 32b+31 of the tile                        */
+  FP8ATTN_REGION_QM_CODES = 9,   /* uint8 [H][rows/128][64]: block-mean operand codes */
+  FP8ATTN_REGION_QM_SCALES = 10  /* uint8 [H][rows/128][4]: its scales (0, 2, 1, 3)   */
 } fp8attn_region;
 
 /*
@@ -95,6 +107,8 @@ fp8attn_status fp8attn_plan(fp8attn_plan_t* plan_out, int64_t tokens, int32_t he
 
 /* Flags of fp8attn_plan_ex. */
 #define FP8ATTN_PLAN_SEGMENT_SCALES 1u
+#define FP8ATTN_PLAN_MXFP4 2u
+#define FP8ATTN_PLAN_Q_CENTRE 4u
 
 /*
  * fp8attn_plan_ex - fp8attn_plan with flags (fp8attn_plan is flags == 0).
@@ -105,7 +119,32 @@ fp8attn_status fp8attn_plan(fp8attn_plan_t* plan_out, int64_t tokens, int32_t he
  *   on another segment's values (a packed batch of unrelated sequences).  An
  *   empty segment gets the scales of an all-zero head.  The attention reads
  *   each segment's scales.
- * Unknown flag bits: FP8ATTN_EINVAL.
+ * FP8ATTN_PLAN_MXFP4: block-scaled FP4 operands instead of E4M3 (FlashInfer
+ *   "minimax_h3_sm120_varlen_attention_nvfp4" page, description of the
+ *   kernel), in the OCP MX form that gfx950's scaled matrix products take:
+ *   Q, K, V and the probabilities as E2M1 codes with one power-of-two (E8M0)
+ *   scale per 32 elements of the contraction axis (Q, K: channels; V: keys of
+ *   a segment, from its start; probabilities: keys).  A block's scale is 2^e
+ *   with e the smallest integer for which amax <= 6 * 2^e (-127 for an
+ *   all-zero block), its codes E2M1(x * 2^-e) rounded to nearest even.  K is
+ *   centred by its segment's per-channel mean as for E4M3.  The score factor
+ *   c = fl32(softmax_scale * log2(e)) is folded into Q before quantization:
+ *   Q's operand is fl32(fl32(q - qm) * c), qm = 0 unless
+ *   FP8ATTN_PLAN_Q_CENTRE.  A query's probabilities in key block b are
+ *   2^E * E2M1(2^(x - E)) with x its scores in log2 units and
+ *   E = ceil(max_b x - log2 6); out = sum phat V / sum phat, rounded to BF16.
+ *   Expect several times the E4M3 error (the page reports about 4x for its
+ *   NVFP4 recipe).  fp8attn_forward rejects an lse request for these plans
+ *   (FP8ATTN_EUNSUPPORTED) and never splits work items.
+ * FP8ATTN_PLAN_Q_CENTRE (with FP8ATTN_PLAN_MXFP4 only): Q rows are centred by
+ *   the mean of their 128-row block (blocks of a segment from its start; the
+ *   mean is a float64 sum over the block's rows in order, divided by the row
+ *   count, rounded to float32); the block-mean operand fl32(qm * c), quantized
+ *   like a Q row, is multiplied with K inside the kernel and added to the
+ *   scores, so the softmax is that of the uncentred Q (the page's Q centring).
+ * Unknown flag bits, FP8ATTN_PLAN_Q_CENTRE without FP8ATTN_PLAN_MXFP4, or
+ * FP8ATTN_PLAN_MXFP4 with FP8ATTN_PLAN_SEGMENT_SCALES (its scales are already
+ * local to 32 elements): FP8ATTN_EINVAL.
  */
 fp8attn_status fp8attn_plan_ex(fp8attn_plan_t* plan_out, int64_t tokens, int32_t heads,
                                const int32_t* cu_seqlens_host, int32_t num_segments,
@@ -139,7 +178,9 @@ size_t fp8attn_workspace_bytes(fp8attn_plan_t plan);
  * then chunk sums ascending) and rounded to float32.  Centring K leaves the
  * softmax unchanged (FlashInfer page, description of the K mean).
  * The pass is two-phase (sglang PR, "Modifications", fused_prep: amax, then
- * pack): three launches (stats, finalize, pack) on `stream`.
+ * pack): three launches (stats, finalize, pack) on `stream`.  For
+ * FP8ATTN_PLAN_MXFP4 plans the codes and block scales of fp8attn_plan_ex are
+ * written instead (the statistics pass then reads K only).
  */
 fp8attn_status fp8attn_quantize(fp8attn_plan_t plan, const void* q, const void* k,
                                 const void* v, const int64_t q_strides[2],
@@ -193,11 +234,12 @@ fp8attn_status fp8attn_workspace_region(fp8attn_plan_t plan, const void* workspa
 
 /*
  * fp8attn_plan_info - schedule facts (for tests and tools).
- *   info_out int64[10]: {tokens, heads, num_segments, workspace_rows,
+ *   info_out int64[12]: {tokens, heads, num_segments, workspace_rows,
  *                        work_items, stat_chunks, query_tile, key_tile,
- *                        segment_scales (0 or 1), partial_slots}
+ *                        segment_scales (0 or 1), partial_slots,
+ *                        mxfp4 (0 or 1), q_centre (0 or 1)}
  */
-fp8attn_status fp8attn_plan_info(fp8attn_plan_t plan, int64_t info_out[10]);
+fp8attn_status fp8attn_plan_info(fp8attn_plan_t plan, int64_t info_out[12]);
 
 /*
  * fp8attn_plan_work_items - copy the ordered work list to host memory.

@@ -228,7 +228,7 @@ def test_plan_ex_flags_and_segment_scale_layout():
     L = _lib.lib()
     cu = (ctypes.c_int32 * 4)(0, 100, 100, 300)
     h = ctypes.c_void_p()
-    assert L.fp8attn_plan_ex(ctypes.byref(h), 300, 2, cu, 3, ctypes.c_float(0.088), -1, 2) == _lib.EINVAL
+    assert L.fp8attn_plan_ex(ctypes.byref(h), 300, 2, cu, 3, ctypes.c_float(0.088), -1, 8) == _lib.EINVAL
     assert "flags" in L.fp8attn_last_error().decode()
     base = fa.Plan(300, 2, [0, 100, 100, 300], device=-1)
     seg = fa.Plan(300, 2, [0, 100, 100, 300], device=-1, segment_scales=True)
@@ -276,3 +276,57 @@ def test_python_wrapper_rejects_unsupported():
         fa.attention(q, q, q, causal=True)
     with pytest.raises(fa.Fp8AttnError):
         fa.attention(q.unsqueeze(0), q.unsqueeze(0), q.unsqueeze(0))
+
+
+def test_mxfp4_plan_flags_layout_and_schedule():
+    L = _lib.lib()
+    cu = (ctypes.c_int32 * 4)(0, 100, 100, 300)
+    h = ctypes.c_void_p()
+    # Q centring needs the FP4 format; FP4 takes no per-segment scales
+    assert L.fp8attn_plan_ex(ctypes.byref(h), 300, 2, cu, 3, ctypes.c_float(0.088), -1, _lib.PLAN_Q_CENTRE) == _lib.EINVAL
+    assert L.fp8attn_plan_ex(ctypes.byref(h), 300, 2, cu, 3, ctypes.c_float(0.088), -1,
+                             _lib.PLAN_MXFP4 | _lib.PLAN_SEGMENT_SCALES) == _lib.EINVAL
+    assert h.value is None
+    e4 = fa.Plan(300, 2, [0, 100, 100, 300], device=-1)
+    mx = fa.Plan(300, 2, [0, 100, 100, 300], device=-1, fmt="mxfp4", q_centre=True)
+    info = mx.info()
+    assert info["mxfp4"] == 1 and info["q_centre"] == 1 and e4.info()["mxfp4"] == 0
+    assert info["partial_slots"] == 0
+    rows = info["workspace_rows"]
+    assert rows == 128 + 256 + 128
+    ptr = ctypes.c_void_p()
+    dims = (ctypes.c_int64 * 3)()
+    base = 1 << 20
+    want = {_lib.REGION_Q: (2, rows, 64), _lib.REGION_K: (2, rows, 64), _lib.REGION_V: (2, rows // 64, 4096),
+            _lib.REGION_Q_BSCALES: (2, rows, 4), _lib.REGION_K_BSCALES: (2, rows, 4),
+            _lib.REGION_V_BSCALES: (2, rows // 64, 256), _lib.REGION_QM_CODES: (2, rows // 128, 64),
+            _lib.REGION_QM_SCALES: (2, rows // 128, 4), _lib.REGION_MU: (3, 2, 128)}
+    offs = []
+    for which, shape in want.items():
+        assert L.fp8attn_workspace_region(mx.handle, ctypes.c_void_p(base), which, ctypes.byref(ptr), dims) == 0
+        assert tuple(dims) == shape, which
+        offs.append((ptr.value - base, shape[0] * shape[1] * shape[2] * (4 if which == _lib.REGION_MU else 1)))
+    offs.sort()
+    for (o0, n0), (o1, _) in zip(offs, offs[1:]):
+        assert o0 + n0 <= o1                          # regions do not overlap
+    assert offs[-1][0] + offs[-1][1] <= mx.workspace_bytes
+    assert L.fp8attn_workspace_region(mx.handle, ctypes.c_void_p(base), _lib.REGION_SCALES,
+                                      ctypes.byref(ptr), dims) == _lib.EINVAL
+    # E4M3 regions are not reported for FP4 planes and vice versa
+    assert L.fp8attn_workspace_region(e4.handle, ctypes.c_void_p(base), _lib.REGION_Q_BSCALES,
+                                      ctypes.byref(ptr), dims) == _lib.EINVAL
+    assert mx.workspace_bytes < e4.workspace_bytes
+
+
+def test_mxfp4_plan_never_splits():
+    """A schedule whose E4M3 plan splits its last round has no split items as FP4."""
+    cus = 32 * 8
+    for cu in ([0, 4096], [0, 15104, 30208, 30208, 30271, 30272], [0, 2048, 2100]):
+        T = cu[-1]
+        e4 = fa.Plan(T, 56, cu, device=-1)
+        mx = fa.Plan(T, 56, cu, device=-1, fmt="mxfp4")
+        items = mx.work_items()
+        assert all(it[3] == 0 for it in items)
+        real = [it for it in items if it[0] >= 0]
+        assert sorted(real) == sorted({(s, q, h, 0) for (s, q, h, w) in e4.work_items() if s >= 0})
+        assert mx.info()["work_items"] == len(real)

@@ -1,0 +1,216 @@
+"""GPU parity of the block-scaled FP4 variant (plans made with fmt="mxfp4")
+against the CPU reference ``oracle.mxfp4``.
+
+* Codes and block scales of Q, K, V and of the Q block-mean operand, and the K
+  means: bit for bit, every element of the small cases, sampled heads at the
+  full sizes (quantization is per head).
+* Output: against the reference's own FP4 computation from its quantized
+  operands, element by element (bar below), and against the float64 softmax
+  attention within the pages' FP4 tolerance (atol 1.0, rtol 0.1) with the
+  relative RMS error reported by the reference's pin.
+* Inputs for which every quantization step is lossless give the plain softmax
+  attention up to BF16 rounding.
+
+Element-wise bar against the reference's FP4 computation: the scores are
+exact in both (E2M1 products with power-of-two scales, float32 sums that do
+not round for these magnitudes); the probabilities come from the kernel's
+exp2, which is within an ulp or two of 2^x, so an E2M1 probability code can
+flip only where 2^(x-E) lies within that of a rounding midpoint (about one
+element in 10^6); the rest is float32 accumulation and one BF16 rounding.
+Bar: |gpu - ref| <= 2 BF16 ulps of |ref| + 2^-10 * max|ref| of the row, with
+at most 1e-4 of the elements (code flips) allowed up to 0.05 * max|ref| of
+the row.
+"""
+import numpy as np
+import pytest
+import torch
+
+import fp8_flash_attention_amd as fa
+from fp8_flash_attention_amd import _lib
+from oracle import attention as exact
+from oracle import mxfp4 as M
+from workloads import WORKLOADS, generate, make_workload, sample_rows
+from tests.gpu_helpers import log, bf16_ulp
+
+pytestmark = pytest.mark.gpu
+
+POS = np.array([0, 2, 1, 3])          # byte position of channel block j in a row's scale bytes
+
+
+def _unpack_nibbles(b: np.ndarray) -> np.ndarray:
+    """uint8 [..., n] -> codes [..., 2n] (low nibble first)."""
+    out = np.empty(b.shape[:-1] + (2 * b.shape[-1],), np.uint8)
+    out[..., 0::2] = b & 15
+    out[..., 1::2] = b >> 4
+    return out
+
+
+def _rows_of_tokens(cu):
+    row = np.zeros(cu[-1], np.int64)
+    r0 = 0
+    row0 = []
+    for a, b in zip(cu[:-1], cu[1:]):
+        row[a:b] = r0 + np.arange(b - a)
+        row0.append(r0)
+        r0 += (b - a + 127) // 128 * 128
+    return row, row0
+
+
+def read_mx(plan, ws, heads):
+    """GPU workspace in the reference's layout (see ``oracle.mxfp4.quantize_mxfp4``)."""
+    cu = list(plan.cu_seqlens)
+    hs = list(heads)
+    row, row0 = _rows_of_tokens(cu)
+    get = lambda which: plan.region(ws, which)[hs].cpu().numpy()
+    qc, kc, vc = get(_lib.REGION_Q), get(_lib.REGION_K), get(_lib.REGION_V)
+    qs, ks, vs = get(_lib.REGION_Q_BSCALES), get(_lib.REGION_K_BSCALES), get(_lib.REGION_V_BSCALES)
+    mc, ms = get(_lib.REGION_QM_CODES), get(_lib.REGION_QM_SCALES)
+    out = {}
+    out["q_codes"] = _unpack_nibbles(qc[:, row]).transpose(1, 0, 2)
+    out["k_codes"] = _unpack_nibbles(kc[:, row]).transpose(1, 0, 2)
+    out["q_e"] = qs[:, row][:, :, POS].astype(np.int64).transpose(1, 0, 2) - 127
+    out["k_e"] = ks[:, row][:, :, POS].astype(np.int64).transpose(1, 0, 2) - 127
+    # V: tile t, channel d, byte i -> keys 64t + 2i, 64t + 2i + 1
+    vt = _unpack_nibbles(vc.reshape(len(hs), -1, 128, 32))          # [H, tiles, 128, 64]
+    vrow = vt.transpose(0, 1, 3, 2).reshape(len(hs), -1, 128)       # [H, rows, 128]
+    out["v_codes"] = vrow[:, row].transpose(1, 0, 2)
+    ve = []
+    for s, a, b in M.v_blocks(cu):
+        r = row0[s] + (a - cu[s])
+        t, kb = r // 64, (r % 64) // 32
+        d = np.arange(128)
+        ve.append(vs[:, t, (32 * kb + d % 32) * 4 + d // 32].astype(np.int64) - 127)
+    out["v_e"] = np.array(ve).reshape(-1, len(hs), 128)
+    qb = []
+    qbe = []
+    for s, a, b in M.q_blocks(cu):
+        blk = (row0[s] + (a - cu[s])) // 128
+        qb.append(_unpack_nibbles(mc[:, blk]))
+        qbe.append(ms[:, blk][:, POS].astype(np.int64) - 127)
+    out["qm_codes"] = np.array(qb).reshape(-1, len(hs), 128)
+    out["qm_e"] = np.array(qbe).reshape(-1, len(hs), 4)
+    out["mu"] = plan.region(ws, _lib.REGION_MU).cpu().numpy()[:, hs]
+    return out
+
+
+def _run(w, q_centre, heads=None, poison=True):
+    q, k, v = generate(w, device="cuda")
+    plan = fa.Plan(w.tokens, w.heads, w.cu_seqlens, w.softmax_scale, device=0, fmt="mxfp4", q_centre=q_centre)
+    ws = plan.new_workspace()
+    if poison:
+        ws.fill_(0xFF)
+    out = torch.full((w.tokens, w.heads, 128), float("nan"), dtype=torch.bfloat16, device="cuda")
+    log(f"mxfp4 {w.name} T={w.tokens} H={w.heads} cu={w.cu_seqlens[:8]} q_centre={q_centre} layout={w.layout}")
+    fa.quantize(plan, q, k, v, ws)
+    fa.forward(plan, ws, out)
+    torch.cuda.synchronize()
+    hs = list(range(w.heads)) if heads is None else list(heads)
+    return plan, ws, out, (q.cpu()[:, hs], k.cpu()[:, hs], v.cpu()[:, hs]), hs
+
+
+def _check_codes(got, exp):
+    for name in ("q_codes", "k_codes", "v_codes", "q_e", "k_e", "v_e", "qm_codes", "qm_e"):
+        a, b = np.asarray(got[name]), np.asarray(exp[name])
+        assert a.shape == b.shape, (name, a.shape, b.shape)
+        bad = np.argwhere(a != b)
+        assert bad.size == 0, f"{name}: {len(bad)} mismatches, first at {bad[0]}: gpu={a[tuple(bad[0])]} " \
+                              f"cpu={b[tuple(bad[0])]}"
+    assert np.array_equal(got["mu"].view(np.uint32), exp["mu"].view(np.uint32))
+
+
+def _check_output(o, ref, what):
+    """o, ref: [R, H, 128] (BF16 output as float, float64 reference)."""
+    rmax = np.abs(ref).max(axis=2, keepdims=True)
+    err = np.abs(o - ref)
+    tight = 2 * bf16_ulp(ref) + 2.0 ** -10 * rmax
+    loose = 0.05 * rmax
+    over = err > tight
+    assert not np.any(err > loose), f"{what}: max error {err.max():.4g} beyond the code-flip bound"
+    assert over.mean() <= 1e-4, f"{what}: {over.sum()} of {over.size} elements above the tight bar " \
+                                f"(max excess {(err - tight).max():.3g})"
+
+
+CASES = [
+    make_workload("mx_s256", 256, 2, [0, 256], seed=301),
+    make_workload("mx_ragged", 700, 4, [0, 300, 700], seed=302, k_offset_var=2.0),
+    make_workload("mx_varlen", 1200, 3, [0, 0, 1, 64, 65, 193, 700, 700, 1200], seed=303),
+    make_workload("mx_fused", 500, 4, [0, 130, 500], seed=304, layout="fused"),
+]
+
+
+@pytest.mark.parametrize("q_centre", [True, False])
+@pytest.mark.parametrize("w", CASES, ids=lambda w: w.name)
+def test_mxfp4_codes_and_output_small(w, q_centre):
+    plan, ws, out, (q, k, v), hs = _run(w, q_centre)
+    z = M.quantize_mxfp4(q, k, v, w.cu_seqlens, w.softmax_scale, q_centre=q_centre)
+    _check_codes(read_mx(plan, ws, hs), z)
+    ops = M.dequantized_operands(z, w.cu_seqlens)
+    ref = M.attention_from_operands(ops["Q"], ops["QM"], ops["K"], ops["V"], w.cu_seqlens)
+    o = out.float().cpu().numpy()
+    assert np.isfinite(o).all()
+    _check_output(o, ref, w.name)
+    # and the method's own error against the float64 softmax: the pages' FP4 bar
+    ex = exact.attention(q, k, v, w.cu_seqlens, w.softmax_scale).numpy()
+    assert np.all(np.abs(o - ex) <= 1.0 + 0.1 * np.abs(ex))
+    rel = np.linalg.norm(o - ex) / np.linalg.norm(ex)
+    log(f"  rel RMS vs float64 softmax: {rel:.4f}")
+    assert rel < 0.35
+
+
+def test_mxfp4_lossless_inputs_give_the_softmax():
+    """The reference pin's lossless construction run through the library."""
+    from tests.test_oracle_mxfp4 import SIGMA_C8, _lossless_inputs
+    cu = [0, 256, 384]
+    q, k, v = _lossless_inputs(cu, 2, seed=9)
+    for q_centre in (True, False):
+        plan = fa.Plan(384, 2, cu, SIGMA_C8, device=0, fmt="mxfp4", q_centre=q_centre)
+        ws = plan.new_workspace()
+        log(f"mxfp4 lossless q_centre={q_centre}")
+        fa.quantize(plan, q.cuda(), k.cuda(), v.cuda(), ws)
+        out = fa.forward(plan, ws)
+        torch.cuda.synchronize()
+        want = exact.attention(q, k, v, cu, SIGMA_C8).numpy()
+        o = out.float().cpu().numpy()
+        assert np.all(np.abs(o - want) <= bf16_ulp(want) / 2 + 1e-6)
+
+
+def test_mxfp4_repeat_is_bit_identical_and_strided_output():
+    w = CASES[1]
+    plan, ws, out, _, _ = _run(w, True)
+    big = torch.zeros((w.tokens, w.heads, 256), dtype=torch.bfloat16, device="cuda")
+    view = big[:, :, 64:192]
+    fa.forward(plan, ws, view)
+    fa.forward(plan, ws, out)
+    torch.cuda.synchronize()
+    assert torch.equal(view.cpu(), out.cpu())
+    assert not big[:, :, :64].any() and not big[:, :, 192:].any()
+
+
+def test_mxfp4_rejects_lse_and_empty_input():
+    w = CASES[0]
+    plan, ws, out, _, _ = _run(w, False)
+    lse = torch.empty((w.heads, w.tokens), dtype=torch.float32, device="cuda")
+    with pytest.raises(fa.Fp8AttnError) as e:
+        fa.forward(plan, ws, out, lse)
+    assert e.value.status == _lib.EUNSUPPORTED
+    p0 = fa.Plan(0, 2, [0, 0], device=0, fmt="mxfp4")
+    ws0 = p0.new_workspace()
+    z = torch.empty((0, 2, 128), dtype=torch.bfloat16, device="cuda")
+    fa.quantize(p0, z, z, z, ws0)
+    fa.forward(p0, ws0, z)
+    torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("name", ["s4096_h56", "s30272_h56_koffset", "varlen_30272_h56"])
+def test_mxfp4_full_size_sampled(name):
+    """Full sizes in the launch configuration the bench times: codes of two heads
+    bit for bit, and sampled rows of those heads against the reference."""
+    w = WORKLOADS[name]
+    heads = [0, w.heads - 1]
+    plan, ws, out, (q, k, v), hs = _run(w, True, heads, poison=False)
+    z = M.quantize_mxfp4(q, k, v, w.cu_seqlens, w.softmax_scale, q_centre=True)
+    _check_codes(read_mx(plan, ws, hs), z)
+    rows = sample_rows(w.tokens, 48, seed=77, cu_seqlens=w.cu_seqlens)
+    ref = M.attention_mxfp4_rows(z, w.cu_seqlens, rows, list(range(len(hs))))
+    o = out[rows][:, hs].float().cpu().numpy()
+    _check_output(o, ref, name)
