@@ -13,6 +13,10 @@ torch.cuda.synchronize(); HIP events recorded on the launch stream around
 every forward give the attention kernel's own average duration.
 
 Prints one JSON line.  FLOPs are counted as 4 * sum(L^2) * H * D.
+
+``--fmt mxfp4`` times the block-scaled FP4 variant instead (``--q-centre``
+adds its Q block-mean centring) and reports it against the FP4 matrix-core
+peak; the default line is the E4M3 path.
 """
 from __future__ import annotations
 
@@ -29,16 +33,18 @@ sys.path.insert(0, ROOT)
 
 METRIC = "FP8 attn TFLOP/s (4*S^2*H*D) at S=30272 H=56 D=128; % of FP8 MFMA peak"
 FP8_PEAK_TFLOPS = 5000.0        # MI355X dense FP8 MFMA (published)
+FP4_PEAK_TFLOPS = 10100.0       # MI355X dense FP4 MFMA (published)
+METRIC_FP4 = "FP4 attn TFLOP/s (4*S^2*H*D), block-scaled E2M1 operands; % of FP4 MFMA peak"
 HBM_PEAK_GBS = 8000.0
 DEFAULT_WORKLOAD = "s30272_h56_koffset"
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "attention_counters.json")
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(kernel_file: str = "attention.hip") -> str:
     """sha256 (16 hex) of the attention kernel's code with comments and blank lines
     removed, so that counters stay attached to the code they were taken on."""
     h = hashlib.sha256()
-    for f in ("attention.hip", "internal.h"):
+    for f in (kernel_file, "internal.h"):
         with open(os.path.join(ROOT, "fp8_flash_attention_amd", "csrc", f)) as fh:
             t = fh.read()
         t = re.sub(r"/\*.*?\*/", "", t, flags=re.S)
@@ -47,7 +53,7 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload: str):
+def measured_traffic(key: str, kernel_file: str = "attention.hip"):
     """HBM bytes per attention launch from committed rocprofv3 counters, if they were
     taken on the current kernel source; else None."""
     try:
@@ -55,8 +61,8 @@ def measured_traffic(workload: str):
             d = json.load(f)
     except (OSError, ValueError):
         return None
-    e = d.get(workload)
-    if not e or e.get("kernel_hash") != kernel_source_hash():
+    e = d.get(key)
+    if not e or e.get("kernel_hash") != kernel_source_hash(kernel_file):
         return None
     return e.get("hbm_bytes_per_launch")
 
@@ -98,6 +104,9 @@ def main() -> int:
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-skeleton", action="store_true", help="skip the MFMA-only skeleton runs (profiling)")
+    ap.add_argument("--fmt", choices=("e4m3", "mxfp4"), default="e4m3",
+                    help="operand format: the E4M3 path (default) or the block-scaled FP4 variant")
+    ap.add_argument("--q-centre", action="store_true", help="mxfp4: centre Q by its 128-row block means")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="after timing, run one plain device copy of BYTES bytes (a known-size "
                          "reference dispatch for scaling HBM traffic counters)")
@@ -117,7 +126,9 @@ def main() -> int:
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     q, k, v = generate(w, device="cuda")
-    plan = fa.Plan(w.tokens, w.heads, w.cu_seqlens, w.softmax_scale, device=0)
+    mx = args.fmt == "mxfp4"
+    plan = fa.Plan(w.tokens, w.heads, w.cu_seqlens, w.softmax_scale, device=0, fmt=args.fmt,
+                   q_centre=mx and args.q_centre)
     ws = plan.new_workspace()
     out = torch.empty((w.tokens, w.heads, 128), dtype=torch.bfloat16, device=dev)
     stream = torch.cuda.current_stream(dev)
@@ -165,12 +176,15 @@ def main() -> int:
         rc = _lib.lib().fp8attn_mfma_peak(0, iters, random_operands, ctypes.byref(tf), ctypes.byref(mhz))
         return {"tflops": round(tf.value, 1), "sclk_mhz": round(mhz.value, 0)} if rc == 0 else None
 
-    skeleton = None if args.no_skeleton else skeleton_run(2000, 0)
-    skeleton_random = None if args.no_skeleton else skeleton_run(100000, 1)
+    skeleton = None if args.no_skeleton or mx else skeleton_run(2000, 0)
+    skeleton_random = None if args.no_skeleton or mx else skeleton_run(100000, 1)
 
-    traffic = measured_traffic(w.name)
+    peak = FP4_PEAK_TFLOPS if mx else FP8_PEAK_TFLOPS
+    kfile = "attention_mx.hip" if mx else "attention.hip"
+    key = w.name + (":mxfp4" + (":qc" if args.q_centre else "") if mx else "")
+    traffic = measured_traffic(key, kfile)
     res = {
-        "metric": METRIC,
+        "metric": METRIC_FP4 if mx else METRIC,
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -180,11 +194,12 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8e4m3",
+        "dtype": "fp4e2m1" if mx else "fp8e4m3",
         "data": "synthetic",
         "config": {"workload": w.name, "tokens": w.tokens, "heads": w.heads, "head_dim": 128,
                    "cu_seqlens": list(w.cu_seqlens), "seed": w.seed, "softmax_scale": w.softmax_scale,
-                   "k_offset_var": w.k_offset_var, "step": "quantize + forward"},
+                   "k_offset_var": w.k_offset_var, "step": "quantize + forward",
+                   **({"format": "mxfp4", "q_centre": bool(args.q_centre)} if mx else {})},
         "forward_ms": round(ms_fwd, 4),
         "forward_tflops": round(fwd_tflops, 2),
         "forward_pct_fp8_peak": round(100.0 * fwd_tflops / FP8_PEAK_TFLOPS, 2),
@@ -195,15 +210,17 @@ def main() -> int:
         "forward_frac_of_random_skeleton": (round(fwd_tflops / skeleton_random["tflops"], 4)
                                             if skeleton_random else None),
         "roofline": {
-            "kernel": "k_attn (fp8attn_forward)",
+            "kernel": "k_attn_mx (fp8attn_forward, FP4 plan)" if mx else "k_attn (fp8attn_forward)",
             "bound": "mfma",
             "achieved": round(fwd_tflops, 2),
-            "peak": FP8_PEAK_TFLOPS,
+            "peak": peak,
             "unit": "TFLOP/s",
-            "frac": round(fwd_tflops / FP8_PEAK_TFLOPS, 4),
+            "frac": round(fwd_tflops / peak, 4),
             "traffic": traffic,
             "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
-            "algorithmic_bytes": 5 * w.tokens * w.heads * 128,
+            # codes: 1 B per element (E4M3) or 0.5 B + 1/32 B of scales (FP4) for Q, K, V; BF16 output
+            "algorithmic_bytes": (int(3 * w.tokens * w.heads * (64 + 4) + 2 * w.tokens * w.heads * 128) if mx
+                                  else 5 * w.tokens * w.heads * 128),
         },
     }
     if args.copy_calibration > 0:

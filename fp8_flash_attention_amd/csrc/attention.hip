@@ -548,6 +548,10 @@ __global__ __launch_bounds__(64 * kWavesWG, 8 / kWavesWG) void k_attn(AttentionA
 #pragma unroll
     for (int db = 0; db < 4; db++) O[db] = mfma_fp8(vf[db], P, O[db]);
     lacc = mfma16_fp8(msel, P, lacc);
+    // with every lane active: a matrix instruction moved into the stores'
+    // lane-divergent branches would read inactive lanes' operands as zero
+#pragma unroll
+    for (int db = 0; db < 4; db++) keep(O[db]);
   }
 
   // epilogue: lane l holds O^T for query l%32, channels
