@@ -16,10 +16,16 @@ exactly to float64 and the scale is taken as ``float64(float32(scale))``, the
 value a float32 kernel argument carries.  The maximum is subtracted before the
 exponential only to keep exp() in range; softmax is unchanged by it.
 
+Causal variant (``causal=True``; the pages send causal attention to another
+backend and do not define it, so this is the plain reading for
+self-attention): query i of a segment attends to the keys j <= i of the same
+segment, positions counted from the segment start.
+
 Parity pins live in ``tests/test_oracle_attention.py``.
 """
 from __future__ import annotations
 
+import math
 from typing import List, Optional, Sequence
 
 import numpy as np
@@ -38,12 +44,22 @@ def _sigma(softmax_scale: float) -> float:
     return float(np.float32(softmax_scale))
 
 
-def _segment_rows(qs: torch.Tensor, ks: torch.Tensor, vs: torch.Tensor, sigma: float) -> torch.Tensor:
-    """softmax(qs ks^T sigma) vs for one segment; qs [R, H, D], ks/vs [L, H, D]."""
+def _causal_mask(qpos, L: int) -> torch.Tensor:
+    """[R, L] True where key j lies after query position qpos[r] (segment-relative)."""
+    return torch.arange(L)[None, :] > torch.as_tensor(qpos, dtype=torch.long)[:, None]
+
+
+def _segment_rows(qs: torch.Tensor, ks: torch.Tensor, vs: torch.Tensor, sigma: float,
+                  qpos=None) -> torch.Tensor:
+    """softmax(qs ks^T sigma) vs for one segment; qs [R, H, D], ks/vs [L, H, D].
+    With ``qpos`` (segment-relative positions of the R query rows) keys after
+    each query are excluded (causal)."""
     qh = qs.permute(1, 0, 2)                       # [H, R, D]
     kh = ks.permute(1, 2, 0)                       # [H, D, L]
     vh = vs.permute(1, 0, 2)                       # [H, L, D]
     s = torch.matmul(qh, kh) * sigma               # [H, R, L]
+    if qpos is not None:
+        s = s.masked_fill(_causal_mask(qpos, ks.shape[0])[None], -math.inf)
     m = s.max(dim=-1, keepdim=True).values
     p = torch.exp(s - m)
     l = p.sum(dim=-1, keepdim=True)
@@ -51,7 +67,7 @@ def _segment_rows(qs: torch.Tensor, ks: torch.Tensor, vs: torch.Tensor, sigma: f
     return o.permute(1, 0, 2)                      # [R, H, D]
 
 
-def attention(q, k, v, cu_seqlens: Sequence[int], softmax_scale: float) -> torch.Tensor:
+def attention(q, k, v, cu_seqlens: Sequence[int], softmax_scale: float, causal: bool = False) -> torch.Tensor:
     """Full output, float64 [T, H, D]."""
     qd, kd, vd = _f64(q), _f64(k), _f64(v)
     T, H, D = qd.shape
@@ -62,12 +78,13 @@ def attention(q, k, v, cu_seqlens: Sequence[int], softmax_scale: float) -> torch
             continue
         for r0 in range(a, b, ROW_BLOCK):
             r1 = min(r0 + ROW_BLOCK, b)
-            out[r0:r1] = _segment_rows(qd[r0:r1], kd[a:b], vd[a:b], sigma)
+            qpos = list(range(r0 - a, r1 - a)) if causal else None
+            out[r0:r1] = _segment_rows(qd[r0:r1], kd[a:b], vd[a:b], sigma, qpos)
     return out
 
 
 def attention_rows(q, k, v, cu_seqlens: Sequence[int], softmax_scale: float,
-                   rows: List[int]) -> torch.Tensor:
+                   rows: List[int], causal: bool = False) -> torch.Tensor:
     """Output rows ``rows`` only (each against its own segment), float64 [len(rows), H, D].
 
     Every query row of the definition is independent of the others, so this is
@@ -85,12 +102,13 @@ def attention_rows(q, k, v, cu_seqlens: Sequence[int], softmax_scale: float,
         sel = torch.tensor([rows[i] for i in idx], dtype=torch.long)
         for c0 in range(0, len(idx), ROW_BLOCK):
             part = sel[c0:c0 + ROW_BLOCK]
-            out[torch.tensor(idx[c0:c0 + ROW_BLOCK])] = _segment_rows(qd[part], kd[a:b], vd[a:b], sigma)
+            qpos = (part - a).tolist() if causal else None
+            out[torch.tensor(idx[c0:c0 + ROW_BLOCK])] = _segment_rows(qd[part], kd[a:b], vd[a:b], sigma, qpos)
     return out
 
 
 def lse_rows(q, k, cu_seqlens: Sequence[int], softmax_scale: float,
-             rows: Optional[List[int]] = None) -> torch.Tensor:
+             rows: Optional[List[int]] = None, causal: bool = False) -> torch.Tensor:
     """Natural-log log-sum-exp of the scaled scores per (row, head), float64 [R, H]."""
     qd, kd = _f64(q), _f64(k)
     sigma = _sigma(softmax_scale)
@@ -101,6 +119,7 @@ def lse_rows(q, k, cu_seqlens: Sequence[int], softmax_scale: float,
     for i, r in enumerate(rows):
         s = int(np.searchsorted(np.asarray(cu), r, side="right") - 1)
         a, b = cu[s], cu[s + 1]
-        sc = torch.einsum("hd,lhd->hl", qd[r], kd[a:b]) * sigma
+        kend = r + 1 if causal else b               # causal: keys up to the query itself
+        sc = torch.einsum("hd,lhd->hl", qd[r], kd[a:kend]) * sigma
         out[i] = torch.logsumexp(sc, dim=-1)
     return out

@@ -181,3 +181,67 @@ def test_lse_rows_closed_form():
     k = _rand((T, H, D), 27)
     lse = A.lse_rows(q, k, [0, 33], 0.3, rows=[0, 32])
     assert torch.allclose(lse, torch.full_like(lse, math.log(33)), atol=1e-14)
+
+
+# ---------------------------------------------------------------- causal variant
+
+def _mp_causal(q, k, v, cu, sigma):
+    """mpmath brute force of the causal reading: key j of a segment is visible
+    to query i of the same segment when j - a <= i - a."""
+    mpmath.mp.dps = 50
+    T, H, D = q.shape
+    out = np.zeros((T, H, D))
+    for a, b in zip(cu[:-1], cu[1:]):
+        for h in range(H):
+            for i in range(a, b):
+                js = list(range(a, i + 1))
+                sc = [mpmath.fsum(mpmath.mpf(float(q[i, h, d])) * mpmath.mpf(float(k[j, h, d])) for d in range(D))
+                      * mpmath.mpf(sigma) for j in js]
+                e = [mpmath.exp(x) for x in sc]
+                z = mpmath.fsum(e)
+                for d in range(D):
+                    out[i, h, d] = float(mpmath.fsum(e[n] * mpmath.mpf(float(v[j, h, d])) for n, j in enumerate(js)) / z)
+    return out
+
+
+@pytest.mark.parametrize("T,H,D,cu", [(6, 1, 3, [0, 6]), (9, 2, 4, [0, 4, 4, 9])])
+def test_causal_brute_force_mpmath(T, H, D, cu):
+    q, k, v = _rand((T, H, D), 11, 0.8), _rand((T, H, D), 12), _rand((T, H, D), 13)
+    got = A.attention(q, k, v, cu, 0.7, causal=True).numpy()
+    exp = _mp_causal(q.numpy(), k.numpy(), v.numpy(), cu, float(np.float32(0.7)))
+    assert np.abs(got - exp).max() / np.abs(exp).max() <= 1e-13
+
+
+def test_causal_row_equals_prefix_segment():
+    """Row i of a causal segment is the last row of the plain attention over the
+    segment's prefix [a, a + i + 1); the first row is its V row."""
+    T, H, D = 70, 2, 128
+    cu = [0, 33, 70]
+    q, k, v = _rand((T, H, D), 21), _rand((T, H, D), 22), _rand((T, H, D), 23)
+    got = A.attention(q, k, v, cu, 0.088, causal=True)
+    for a, b in zip(cu[:-1], cu[1:]):
+        for i in (a, a + 1, (a + b) // 2, b - 1):
+            pre = A.attention(q[a:i + 1], k[a:i + 1], v[a:i + 1], [0, i + 1 - a], 0.088)
+            torch.testing.assert_close(got[i], pre[-1], rtol=1e-13, atol=1e-13)
+        torch.testing.assert_close(got[a], v[a], rtol=1e-14, atol=1e-14)
+    # the last row of a segment sees every key: it equals the non-causal row
+    full = A.attention(q, k, v, cu, 0.088)
+    for b in cu[1:]:
+        torch.testing.assert_close(got[b - 1], full[b - 1], rtol=1e-13, atol=1e-13)
+    # rows api and LSE agree with the full causal computation
+    rows = [0, 5, 32, 33, 50, 69]
+    torch.testing.assert_close(A.attention_rows(q, k, v, cu, 0.088, rows, causal=True), got[rows], rtol=1e-13, atol=1e-13)
+    lse = A.lse_rows(q, k, cu, 0.088, rows, causal=True)
+    for n, r in enumerate(rows):
+        a = max(x for x in cu[:-1] if x <= r and r < cu[cu.index(x) + 1])
+        sc = (q[r][None] * k[a:r + 1]).sum(-1) * float(np.float32(0.088))      # [keys, H]
+        torch.testing.assert_close(lse[n], torch.logsumexp(sc, dim=0), rtol=1e-13, atol=1e-13)
+
+
+def test_causal_off_by_one_negative_control():
+    """A planted mistake (each query also sees the next key) must fail the prefix pin."""
+    T, H, D = 40, 1, 16
+    q, k, v = _rand((T, H, D), 31), _rand((T, H, D), 32), _rand((T, H, D), 33)
+    good = A.attention(q, k, v, [0, T], 0.25, causal=True)
+    bad = torch.stack([A.attention(q[:i + 2], k[:i + 2], v[:i + 2], [0, min(i + 2, T)], 0.25)[i] for i in range(T)])
+    assert (good - bad).abs().max() > 1e-3
