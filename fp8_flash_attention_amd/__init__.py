@@ -52,12 +52,13 @@ class Plan:
     host-only plan that can be inspected but not run.  ``segment_scales=True``
     quantizes every segment with its own per-head scales.  ``fmt`` is
     ``"e4m3"`` (default) or ``"mxfp4"``; ``q_centre`` (mxfp4 only) centres Q
-    by its 128-row block means.
+    by its 128-row block means.  ``causal`` (e4m3 only): query i of a segment
+    attends to the keys j <= i of that segment.
     """
 
     def __init__(self, tokens: int, heads: int, cu_seqlens: Optional[Sequence[int]] = None,
                  softmax_scale: Optional[float] = None, device=None, segment_scales: bool = False,
-                 fmt: str = "e4m3", q_centre: bool = False):
+                 fmt: str = "e4m3", q_centre: bool = False, causal: bool = False):
         L = _lib.lib()
         if cu_seqlens is None:
             cu_seqlens = [0, tokens]
@@ -78,11 +79,13 @@ class Plan:
             raise ValueError(f"fmt must be 'e4m3' or 'mxfp4' (got {fmt!r})")
         self.fmt = fmt
         self.q_centre = bool(q_centre)
+        self.causal = bool(causal)
         arr = (ctypes.c_int32 * len(cu))(*cu)
         h = ctypes.c_void_p()
         self._h = None
         flags = ((_lib.PLAN_SEGMENT_SCALES if self.segment_scales else 0)
-                 | (_lib.PLAN_MXFP4 if fmt == "mxfp4" else 0) | (_lib.PLAN_Q_CENTRE if self.q_centre else 0))
+                 | (_lib.PLAN_MXFP4 if fmt == "mxfp4" else 0) | (_lib.PLAN_Q_CENTRE if self.q_centre else 0)
+                 | (_lib.PLAN_CAUSAL if self.causal else 0))
         _lib.check(L.fp8attn_plan_ex(ctypes.byref(h), self.tokens, self.heads, arr, len(cu) - 1,
                                      ctypes.c_float(self.softmax_scale), self.device_index, flags),
                    "fp8attn_plan_ex")
@@ -101,7 +104,7 @@ class Plan:
         buf = (ctypes.c_int64 * _lib.PLAN_INFO_LEN)()
         _lib.check(_lib.lib().fp8attn_plan_info(self._h, buf), "fp8attn_plan_info")
         keys = ["tokens", "heads", "num_segments", "workspace_rows", "work_items", "stat_chunks",
-                "query_tile", "key_tile", "segment_scales", "partial_slots", "mxfp4", "q_centre"]
+                "query_tile", "key_tile", "segment_scales", "partial_slots", "mxfp4", "q_centre", "causal"]
         return dict(zip(keys, list(buf)))
 
     def work_items(self):
@@ -206,15 +209,15 @@ _PLANS: Dict[Tuple, Plan] = {}
 
 
 def get_plan(tokens: int, heads: int, cu_seqlens: Sequence[int], softmax_scale: float, device: int,
-             segment_scales: bool = False, fmt: str = "e4m3", q_centre: bool = False) -> Plan:
+             segment_scales: bool = False, fmt: str = "e4m3", q_centre: bool = False, causal: bool = False) -> Plan:
     """Plans are cached per (cu_seqlens, heads, scale, device, quantization mode), as the FlashInfer
     page caches its segment plan per (cu_seqlens, heads, device).  A plan holds only small tables."""
     key = (tuple(int(x) for x in cu_seqlens), int(heads), float(softmax_scale), int(device), bool(segment_scales),
-           fmt, bool(q_centre))
+           fmt, bool(q_centre), bool(causal))
     p = _PLANS.get(key)
     if p is None:
         p = Plan(tokens, heads, cu_seqlens, softmax_scale, device, segment_scales=segment_scales, fmt=fmt,
-                 q_centre=q_centre)
+                 q_centre=q_centre, causal=causal)
         _PLANS[key] = p
     return p
 
@@ -223,19 +226,31 @@ def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: Opt
               softmax_scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
               return_lse: bool = False, causal: bool = False, workspace: Optional[torch.Tensor] = None,
               segment_scales: bool = False, fmt: str = "e4m3", q_centre: bool = False):
-    """Dense non-causal FP8 attention over packed [tokens, heads, 128] BF16 q/k/v.
+    """FP8 attention over packed [tokens, heads, 128] BF16 q/k/v.
 
     ``cu_seqlens`` is a host sequence of segment boundaries (None = one segment).
     ``segment_scales`` quantizes every segment with its own per-head scales.
     ``fmt="mxfp4"`` runs the block-scaled FP4 variant (``q_centre`` adds Q
-    block-mean centring); it returns no LSE.
-    Causal attention is not supported and raises (there is no fallback path).
+    block-mean centring); it returns no LSE.  ``causal=True`` masks keys after
+    each query (E4M3 only).  Batched [B, T, heads, 128] inputs (views of
+    [B*T, heads, 128]) are run as B segments of T tokens and returned as
+    [B, T, heads, 128] (with the LSE as [heads, B*T]).
     """
-    if causal:
-        raise Fp8AttnError(_lib.EUNSUPPORTED, "attention", "causal attention is not supported")
     if q.dim() == 4:
-        raise Fp8AttnError(_lib.EUNSUPPORTED, "attention", "batched [B, T, H, D] input is not supported; pack "
-                           "the batch along tokens and pass cu_seqlens")
+        if cu_seqlens is not None:
+            raise ValueError("batched [B, T, H, D] input takes no cu_seqlens (each batch entry is one segment)")
+        B, T0 = q.shape[0], q.shape[1]
+        try:
+            flat = [x.view(B * T0, x.shape[2], x.shape[3]) for x in (q, k, v)]
+            oflat = None if out is None else out.view(B * T0, out.shape[2], out.shape[3])
+        except RuntimeError as e:
+            raise ValueError("batched q, k, v (and out) must be viewable as [B*T, H, D]") from e
+        res = attention(*flat, cu_seqlens=[T0 * i for i in range(B + 1)], softmax_scale=softmax_scale, out=oflat,
+                        return_lse=return_lse, causal=causal, workspace=workspace, segment_scales=segment_scales,
+                        fmt=fmt, q_centre=q_centre)
+        if return_lse:
+            return res[0].view(B, T0, *res[0].shape[1:]), res[1]
+        return res.view(B, T0, *res.shape[1:])
     T, H = q.shape[0], q.shape[1]
     if cu_seqlens is None:
         cu_seqlens = [0, T]
@@ -243,7 +258,7 @@ def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: Opt
         cu_seqlens = cu_seqlens.tolist()
     scale = DEFAULT_SCALE if softmax_scale is None else float(softmax_scale)
     dev = q.device.index if q.device.index is not None else torch.cuda.current_device()
-    plan = get_plan(T, H, cu_seqlens, scale, dev, segment_scales, fmt, q_centre)
+    plan = get_plan(T, H, cu_seqlens, scale, dev, segment_scales, fmt, q_centre, causal)
     ws = workspace if workspace is not None else plan.new_workspace()
     quantize(plan, q, k, v, ws)
     lse = torch.empty((H, T), dtype=torch.float32, device=q.device) if return_lse else None

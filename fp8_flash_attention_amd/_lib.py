@@ -20,7 +20,8 @@ REGION_Q_BSCALES, REGION_K_BSCALES, REGION_V_BSCALES, REGION_QM_CODES, REGION_QM
 PLAN_SEGMENT_SCALES = 1          # FP8ATTN_PLAN_SEGMENT_SCALES
 PLAN_MXFP4 = 2                   # FP8ATTN_PLAN_MXFP4
 PLAN_Q_CENTRE = 4                # FP8ATTN_PLAN_Q_CENTRE
-PLAN_INFO_LEN = 12
+PLAN_CAUSAL = 8                  # FP8ATTN_PLAN_CAUSAL
+PLAN_INFO_LEN = 13
 
 # Every symbol include/fp8attn.h declares, with (restype, argtypes).
 _i64p = ctypes.POINTER(ctypes.c_int64)

@@ -31,6 +31,7 @@ struct fp8attn_plan_s {
   int32_t nscale = 1;             // scale sets: nseg with segment scales, else 1
   int32_t mx = 0;                 // FP8ATTN_PLAN_MXFP4
   int32_t q_centre = 0;           // FP8ATTN_PLAN_Q_CENTRE
+  int32_t causal = 0;             // FP8ATTN_PLAN_CAUSAL
   float scale = 0.f;
   int device = -1;
   std::vector<int32_t> cu;
@@ -134,7 +135,11 @@ void build_items(fp8attn_plan_s* p, int cus, bool allow_split) {
       const int L = p->segs[s].len;
       for (int q0 = 0; q0 < L; q0 += kBM) list.push_back(int4{s, q0, h, 0});
     }
-  auto tiles = [&](const int4& it) { return (p->segs[it.x].len + kBN - 1) / kBN; };
+  // key tiles an item attends to (causal: up to its last query)
+  auto tiles = [&](const int4& it) {
+    const int L = p->segs[it.x].len;
+    return ((p->causal ? std::min(L, it.y + kBM) : L) + kBN - 1) / kBN;
+  };
   const size_t per = (list.size() + kNumXcd - 1) / kNumXcd;
   std::vector<std::vector<int4>> parts(kNumXcd);
   int64_t slot = 0;
@@ -207,8 +212,10 @@ fp8attn_status fp8attn_plan_ex(fp8attn_plan_t* plan_out, int64_t tokens, int32_t
                                int32_t device, uint32_t flags) {
   if (plan_out == nullptr) return fail(FP8ATTN_EINVAL, "plan_out is NULL");
   *plan_out = nullptr;
-  if ((flags & ~(FP8ATTN_PLAN_SEGMENT_SCALES | FP8ATTN_PLAN_MXFP4 | FP8ATTN_PLAN_Q_CENTRE)) != 0)
+  if ((flags & ~(FP8ATTN_PLAN_SEGMENT_SCALES | FP8ATTN_PLAN_MXFP4 | FP8ATTN_PLAN_Q_CENTRE | FP8ATTN_PLAN_CAUSAL)) != 0)
     return fail(FP8ATTN_EINVAL, "unknown plan flags");
+  if ((flags & FP8ATTN_PLAN_CAUSAL) && (flags & FP8ATTN_PLAN_MXFP4))
+    return fail(FP8ATTN_EINVAL, "FP8ATTN_PLAN_CAUSAL is not available for FP8ATTN_PLAN_MXFP4 plans");
   if ((flags & FP8ATTN_PLAN_Q_CENTRE) && !(flags & FP8ATTN_PLAN_MXFP4))
     return fail(FP8ATTN_EINVAL, "FP8ATTN_PLAN_Q_CENTRE needs FP8ATTN_PLAN_MXFP4");
   if ((flags & FP8ATTN_PLAN_MXFP4) && (flags & FP8ATTN_PLAN_SEGMENT_SCALES))
@@ -237,6 +244,7 @@ fp8attn_status fp8attn_plan_ex(fp8attn_plan_t* plan_out, int64_t tokens, int32_t
   p->nscale = p->seg_scales ? num_segments : 1;
   p->mx = (flags & FP8ATTN_PLAN_MXFP4) ? 1 : 0;
   p->q_centre = (flags & FP8ATTN_PLAN_Q_CENTRE) ? 1 : 0;
+  p->causal = (flags & FP8ATTN_PLAN_CAUSAL) ? 1 : 0;
   p->cu.assign(cu, cu + num_segments + 1);
   int64_t row = 0;
   int32_t chunk = 0;
@@ -263,7 +271,7 @@ fp8attn_status fp8attn_plan_ex(fp8attn_plan_t* plan_out, int64_t tokens, int32_t
     int n = 0;
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, device) == hipSuccess && n > 0) cus = n;
   }
-  build_items(p, std::max(1, cus / kNumXcd), !p->mx);
+  build_items(p, std::max(1, cus / kNumXcd), !p->mx && !p->causal);
   if (p->npieces >= (int64_t)1 << 23) {
     delete p;
     return fail(FP8ATTN_EUNSUPPORTED, "too many split work items");
@@ -445,6 +453,7 @@ fp8attn_status fp8attn_forward(fp8attn_plan_t p, void* workspace, size_t workspa
   a.heads = p->heads;
   a.nitems = p->real_items > 0 ? (int32_t)p->items.size() : 0;
   a.nscale = p->nscale;
+  a.causal = p->causal;
   a.softmax_scale = p->scale;
   hipError_t e = launch_attention(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(FP8ATTN_EHIP, std::string("attention launch failed: ") + hipGetErrorString(e));
@@ -505,7 +514,7 @@ fp8attn_status fp8attn_workspace_region(fp8attn_plan_t p, const void* workspace,
   return FP8ATTN_OK;
 }
 
-fp8attn_status fp8attn_plan_info(fp8attn_plan_t p, int64_t info[12]) {
+fp8attn_status fp8attn_plan_info(fp8attn_plan_t p, int64_t info[13]) {
   if (p == nullptr || info == nullptr) return fail(FP8ATTN_EINVAL, "NULL argument");
   info[0] = p->tokens;
   info[1] = p->heads;
@@ -519,6 +528,7 @@ fp8attn_status fp8attn_plan_info(fp8attn_plan_t p, int64_t info[12]) {
   info[9] = p->npieces;
   info[10] = p->mx;
   info[11] = p->q_centre;
+  info[12] = p->causal;
   return FP8ATTN_OK;
 }
 

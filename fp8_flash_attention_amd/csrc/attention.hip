@@ -180,7 +180,7 @@ __device__ __forceinline__ void tail_iters(F& iter, int& t, int nkt) {
   }
 }
 
-template <bool LSE>
+template <bool LSE, bool CAUSAL>
 __global__ __launch_bounds__(64 * kWavesWG, 8 / kWavesWG) void k_attn(AttentionArgs a) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * kVRing];
 
@@ -190,8 +190,9 @@ __global__ __launch_bounds__(64 * kWavesWG, 8 / kWavesWG) void k_attn(AttentionA
   const int q0 = it.y;
   const int h = it.z;
   const int L = si.len;
-  // Key range: every tile of the segment, or one piece of a split item.
-  const int nkt_seg = (L + kBN - 1) / kBN;
+  // Key range: every tile of the segment (causal: up to the item's last
+  // query), or one piece of a split item.
+  const int nkt_seg = ((CAUSAL ? min(L, q0 + kBM) : L) + kBN - 1) / kBN;
   int kt0 = 0, nkt = nkt_seg, slot = -1;
   if (it.w != 0) {
     const int n = split_pieces(it.w), i = split_index(it.w);
@@ -398,9 +399,22 @@ __global__ __launch_bounds__(64 * kWavesWG, 8 / kWavesWG) void k_attn(AttentionA
     }
     return cvt4(p[0], p[1], p[2], p[3]);
   };
+  // Causal: scores of keys after this lane's query to -inf in tile t (only
+  // tiles from q0 on hold such keys).  Register r of block kb holds key
+  // t*64 + 32*kb + 8*(r/4) + 4*lg + r%4.
+  const int qq = q0 + 32 * wave + lq;
+  auto mask_causal = [&](int t) __attribute__((always_inline)) {
+    const int dlim = qq - t * kBN - 4 * lg;
+#pragma unroll
+    for (int kb = 0; kb < 2; kb++)
+#pragma unroll
+      for (int r = 0; r < 16; r++)
+        if (32 * kb + 8 * (r >> 2) + (r & 3) > dlim) S[kb][r] = -__builtin_huge_valf();
+  };
   // Softmax of tile 0 (reference from its maximum) into P, then the scores of
   // tile 1 (K in slot 1) into S.
   auto first_tile = [&]() __attribute__((always_inline)) {
+    if (CAUSAL && q0 == 0) mask_causal(0);
     rowmax_update(std::true_type{});
 #pragma unroll
     for (int w = 0; w < 8; w++) P[w] = probs4(w >> 2, w & 3, 0);
@@ -450,6 +464,7 @@ __global__ __launch_bounds__(64 * kWavesWG, 8 / kWavesWG) void k_attn(AttentionA
   // merging the slots.  The two score chains are interleaved (first halves of
   // both 32-key blocks, then the second halves) so neither waits on the
   // other's accumulator.
+  const int tdiag = q0 / kBN;   // causal: tiles from here on hold keys after some query
   auto iter = [&](int t, auto ph_c) __attribute__((always_inline)) {
     constexpr int PH = decltype(ph_c)::value;   // t % kSlots
     // With the LSE sum, two of the four V(t-1) operands are read here, before
@@ -479,6 +494,7 @@ __global__ __launch_bounds__(64 * kWavesWG, 8 / kWavesWG) void k_attn(AttentionA
     fence();
     O[0] = mfma_fp8(vf[0], P, O[0]);
     kf[0][1] = lds_read32(kb, koff[1][0], koff[1][1]);
+    if (CAUSAL && t >= tdiag) mask_causal(t);   // wave-uniform branch, diagonal tiles only
     rowmax_update(std::false_type{});
     fence();
     O[1] = mfma_fp8(vf[1], P, O[1]);
@@ -596,12 +612,14 @@ __global__ __launch_bounds__(64 * kWavesWG, 8 / kWavesWG) void k_attn(AttentionA
   if (LSE) {
     // The padded keys of the last tile have zero codes, so their scores are
     // exactly 0 and each added exp2(nb) in the final frame: remove them.
+    // (Causal: keys past the segment end lie after every stored query and are
+    // masked already.)
     int npad = 0;
 #pragma unroll
     for (int kb = 0; kb < 2; kb++)
 #pragma unroll
       for (int r = 0; r < 16; r++)
-        npad += (nkt - 1) * kBN + 32 * kb + 8 * (r >> 2) + 4 * lg + (r & 3) >= Lk;
+        npad += !CAUSAL && (nkt - 1) * kBN + 32 * kb + 8 * (r >> 2) + 4 * lg + (r & 3) >= Lk;
     lex -= (float)npad * __builtin_amdgcn_exp2f(nb);
     const float le = sum_pair32(lex);
     if (lg == 0 && qrow < L) {
@@ -695,10 +713,17 @@ hipError_t launch_combine(const CombineArgs& a, hipStream_t stream) {
 
 hipError_t launch_attention(const AttentionArgs& a, hipStream_t stream) {
   if (a.nitems == 0) return hipSuccess;
-  if (a.lse != nullptr)
-    hipLaunchKernelGGL(k_attn<true>, dim3(a.nitems), dim3(64 * kWavesWG), 0, stream, a);
-  else
-    hipLaunchKernelGGL(k_attn<false>, dim3(a.nitems), dim3(64 * kWavesWG), 0, stream, a);
+  const dim3 g(a.nitems), b(64 * kWavesWG);
+  if (a.causal) {
+    if (a.lse != nullptr)
+      hipLaunchKernelGGL((k_attn<true, true>), g, b, 0, stream, a);
+    else
+      hipLaunchKernelGGL((k_attn<false, true>), g, b, 0, stream, a);
+  } else if (a.lse != nullptr) {
+    hipLaunchKernelGGL((k_attn<true, false>), g, b, 0, stream, a);
+  } else {
+    hipLaunchKernelGGL((k_attn<false, false>), g, b, 0, stream, a);
+  }
   return hipGetLastError();
 }
 

@@ -119,6 +119,7 @@ struct AttentionArgs {
   int32_t heads;
   int32_t nitems;
   int32_t nscale;            // S: scale sets (segments with per-segment scales, else 1)
+  int32_t causal;            // 1: query i of a segment attends keys j <= i only
   float softmax_scale;
 };
 

@@ -109,6 +109,7 @@ fp8attn_status fp8attn_plan(fp8attn_plan_t* plan_out, int64_t tokens, int32_t he
 #define FP8ATTN_PLAN_SEGMENT_SCALES 1u
 #define FP8ATTN_PLAN_MXFP4 2u
 #define FP8ATTN_PLAN_Q_CENTRE 4u
+#define FP8ATTN_PLAN_CAUSAL 8u
 
 /*
  * fp8attn_plan_ex - fp8attn_plan with flags (fp8attn_plan is flags == 0).
@@ -142,9 +143,16 @@ fp8attn_status fp8attn_plan(fp8attn_plan_t* plan_out, int64_t tokens, int32_t he
  *   count, rounded to float32); the block-mean operand fl32(qm * c), quantized
  *   like a Q row, is multiplied with K inside the kernel and added to the
  *   scores, so the softmax is that of the uncentred Q (the page's Q centring).
- * Unknown flag bits, FP8ATTN_PLAN_Q_CENTRE without FP8ATTN_PLAN_MXFP4, or
+ * FP8ATTN_PLAN_CAUSAL (E4M3 plans): query i of a segment attends only to the
+ *   keys j <= i of the same segment, positions counted from the segment start
+ *   (the pages send causal attention to another backend; this is the plain
+ *   reading for self-attention).  A work item attends to the key tiles up to
+ *   its last query; the tiles from its first query on are masked per element.
+ *   The LSE (if requested) is over the visible keys.  Causal plans never split
+ *   work items.
+ * Unknown flag bits, FP8ATTN_PLAN_Q_CENTRE without FP8ATTN_PLAN_MXFP4,
  * FP8ATTN_PLAN_MXFP4 with FP8ATTN_PLAN_SEGMENT_SCALES (its scales are already
- * local to 32 elements): FP8ATTN_EINVAL.
+ * local to 32 elements) or with FP8ATTN_PLAN_CAUSAL: FP8ATTN_EINVAL.
  */
 fp8attn_status fp8attn_plan_ex(fp8attn_plan_t* plan_out, int64_t tokens, int32_t heads,
                                const int32_t* cu_seqlens_host, int32_t num_segments,
@@ -234,12 +242,12 @@ fp8attn_status fp8attn_workspace_region(fp8attn_plan_t plan, const void* workspa
 
 /*
  * fp8attn_plan_info - schedule facts (for tests and tools).
- *   info_out int64[12]: {tokens, heads, num_segments, workspace_rows,
+ *   info_out int64[13]: {tokens, heads, num_segments, workspace_rows,
  *                        work_items, stat_chunks, query_tile, key_tile,
  *                        segment_scales (0 or 1), partial_slots,
- *                        mxfp4 (0 or 1), q_centre (0 or 1)}
+ *                        mxfp4 (0 or 1), q_centre (0 or 1), causal (0 or 1)}
  */
-fp8attn_status fp8attn_plan_info(fp8attn_plan_t plan, int64_t info_out[12]);
+fp8attn_status fp8attn_plan_info(fp8attn_plan_t plan, int64_t info_out[13]);
 
 /*
  * fp8attn_plan_work_items - copy the ordered work list to host memory.

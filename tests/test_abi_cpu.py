@@ -228,7 +228,7 @@ def test_plan_ex_flags_and_segment_scale_layout():
     L = _lib.lib()
     cu = (ctypes.c_int32 * 4)(0, 100, 100, 300)
     h = ctypes.c_void_p()
-    assert L.fp8attn_plan_ex(ctypes.byref(h), 300, 2, cu, 3, ctypes.c_float(0.088), -1, 8) == _lib.EINVAL
+    assert L.fp8attn_plan_ex(ctypes.byref(h), 300, 2, cu, 3, ctypes.c_float(0.088), -1, 16) == _lib.EINVAL
     assert "flags" in L.fp8attn_last_error().decode()
     base = fa.Plan(300, 2, [0, 100, 100, 300], device=-1)
     seg = fa.Plan(300, 2, [0, 100, 100, 300], device=-1, segment_scales=True)
@@ -271,11 +271,12 @@ def test_workspace_region_host_plan():
 
 def test_python_wrapper_rejects_unsupported():
     import torch
-    q = torch.zeros((4, 2, 128), dtype=torch.bfloat16)
-    with pytest.raises(fa.Fp8AttnError):
-        fa.attention(q, q, q, causal=True)
-    with pytest.raises(fa.Fp8AttnError):
-        fa.attention(q.unsqueeze(0), q.unsqueeze(0), q.unsqueeze(0))
+    with pytest.raises(fa.Fp8AttnError):                 # causal FP4 plans
+        fa.Plan(256, 2, [0, 256], device=-1, fmt="mxfp4", causal=True)
+    with pytest.raises(ValueError):                      # head_dim other than 128
+        fa._strides(torch.zeros((4, 2, 64), dtype=torch.bfloat16), "q")
+    with pytest.raises(TypeError):                       # non-BF16 input
+        fa._strides(torch.zeros((4, 2, 128), dtype=torch.float16), "q")
 
 
 def test_mxfp4_plan_flags_layout_and_schedule():
@@ -330,3 +331,30 @@ def test_mxfp4_plan_never_splits():
         real = [it for it in items if it[0] >= 0]
         assert sorted(real) == sorted({(s, q, h, 0) for (s, q, h, w) in e4.work_items() if s >= 0})
         assert mx.info()["work_items"] == len(real)
+
+
+def test_causal_plan_schedule():
+    """Causal items attend to the key tiles up to their last query; no splits;
+    per XCD part, longer items first."""
+    cu = [0, 4096, 4096, 4500]
+    p = fa.Plan(4500, 8, cu, device=-1, causal=True)
+    assert p.info()["causal"] == 1 and p.info()["partial_slots"] == 0
+    items = [it for it in p.work_items() if it[0] >= 0]
+    assert all(it[3] == 0 for it in items)
+    segs = {0: 4096, 2: 404}
+    want = {(s, q0, h) for s, L in segs.items() for h in range(8) for q0 in range(0, L, 256)}
+    assert {(s, q, h) for s, q, h, _ in items} == want
+    L = _lib.lib()
+    h = ctypes.c_void_p()
+    arr = (ctypes.c_int32 * 2)(0, 256)
+    assert L.fp8attn_plan_ex(ctypes.byref(h), 256, 2, arr, 1, ctypes.c_float(0.088), -1,
+                             _lib.PLAN_CAUSAL | _lib.PLAN_MXFP4) == _lib.EINVAL
+    # a non-causal plan of the same table splits nothing away from these items either
+    assert p.info()["work_items"] == len(items)
+
+
+def test_batched_wrapper_rejects_cu_seqlens():
+    import torch
+    q = torch.zeros((2, 4, 2, 128), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        fa.attention(q, q, q, cu_seqlens=[0, 4, 8])
