@@ -35,6 +35,7 @@ METRIC = "FP8 attn TFLOP/s (4*S^2*H*D) at S=30272 H=56 D=128; % of FP8 MFMA peak
 FP8_PEAK_TFLOPS = 5000.0        # MI355X dense FP8 MFMA (published)
 FP4_PEAK_TFLOPS = 10100.0       # MI355X dense FP4 MFMA (published)
 METRIC_FP4 = "FP4 attn TFLOP/s (4*S^2*H*D), block-scaled E2M1 operands; % of FP4 MFMA peak"
+METRIC_CAUSAL = "FP8 causal attn TFLOP/s (2*S*(S+1)*H*D, visible pairs only); % of FP8 MFMA peak"
 HBM_PEAK_GBS = 8000.0
 DEFAULT_WORKLOAD = "s30272_h56_koffset"
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "attention_counters.json")
@@ -107,6 +108,8 @@ def main() -> int:
     ap.add_argument("--fmt", choices=("e4m3", "mxfp4"), default="e4m3",
                     help="operand format: the E4M3 path (default) or the block-scaled FP4 variant")
     ap.add_argument("--q-centre", action="store_true", help="mxfp4: centre Q by its 128-row block means")
+    ap.add_argument("--causal", action="store_true",
+                    help="e4m3: causal plan (FLOPs then count the visible pairs, 2 * sum L(L+1) * H * D)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="after timing, run one plain device copy of BYTES bytes (a known-size "
                          "reference dispatch for scaling HBM traffic counters)")
@@ -128,7 +131,7 @@ def main() -> int:
     q, k, v = generate(w, device="cuda")
     mx = args.fmt == "mxfp4"
     plan = fa.Plan(w.tokens, w.heads, w.cu_seqlens, w.softmax_scale, device=0, fmt=args.fmt,
-                   q_centre=mx and args.q_centre)
+                   q_centre=mx and args.q_centre, causal=args.causal)
     ws = plan.new_workspace()
     out = torch.empty((w.tokens, w.heads, 128), dtype=torch.bfloat16, device=dev)
     stream = torch.cuda.current_stream(dev)
@@ -161,7 +164,7 @@ def main() -> int:
     ms_step = wall * 1e3 / args.steps
     ms_fwd = sum(fwd_ms) / len(fwd_ms)
     ms_quant = sum(s - f for s, f in zip(step_ms, fwd_ms)) / len(fwd_ms)
-    flops = w.flops
+    flops = (2.0 * sum(L * (L + 1) for L in w.segments) * w.heads * 128) if args.causal else w.flops
     value = flops / (ms_step * 1e-3) / 1e12
     fwd_tflops = flops / (ms_fwd * 1e-3) / 1e12
 
@@ -181,10 +184,10 @@ def main() -> int:
 
     peak = FP4_PEAK_TFLOPS if mx else FP8_PEAK_TFLOPS
     kfile = "attention_mx.hip" if mx else "attention.hip"
-    key = w.name + (":mxfp4" + (":qc" if args.q_centre else "") if mx else "")
+    key = w.name + (":mxfp4" + (":qc" if args.q_centre else "") if mx else "") + (":causal" if args.causal else "")
     traffic = measured_traffic(key, kfile)
     res = {
-        "metric": METRIC_FP4 if mx else METRIC,
+        "metric": METRIC_FP4 if mx else (METRIC_CAUSAL if args.causal else METRIC),
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -199,7 +202,8 @@ def main() -> int:
         "config": {"workload": w.name, "tokens": w.tokens, "heads": w.heads, "head_dim": 128,
                    "cu_seqlens": list(w.cu_seqlens), "seed": w.seed, "softmax_scale": w.softmax_scale,
                    "k_offset_var": w.k_offset_var, "step": "quantize + forward",
-                   **({"format": "mxfp4", "q_centre": bool(args.q_centre)} if mx else {})},
+                   **({"format": "mxfp4", "q_centre": bool(args.q_centre)} if mx else {}),
+                   **({"causal": True} if args.causal else {})},
         "forward_ms": round(ms_fwd, 4),
         "forward_tflops": round(fwd_tflops, 2),
         "forward_pct_fp8_peak": round(100.0 * fwd_tflops / FP8_PEAK_TFLOPS, 2),

@@ -55,6 +55,11 @@ struct fp8attn_plan_s {
 
 namespace {
 
+#ifndef FP8ATTN_CAUSAL_ROUNDS
+#define FP8ATTN_CAUSAL_ROUNDS 4
+#endif
+constexpr int kCausalRounds = FP8ATTN_CAUSAL_ROUNDS;   // see build_items
+
 thread_local std::string g_last_error;
 
 fp8attn_status fail(fp8attn_status s, const std::string& msg) {
@@ -129,17 +134,66 @@ void build_items(fp8attn_plan_s* p, int cus, bool allow_split) {
   for (int s = 0; s < p->nseg; s++) order[s] = s;
   std::stable_sort(order.begin(), order.end(),
                    [&](int x, int y) { return p->segs[x].len > p->segs[y].len; });
-  std::vector<int4> list;
-  for (int h = 0; h < p->heads; h++)
-    for (int s : order) {
-      const int L = p->segs[s].len;
-      for (int q0 = 0; q0 < L; q0 += kBM) list.push_back(int4{s, q0, h, 0});
-    }
   // key tiles an item attends to (causal: up to its last query)
   auto tiles = [&](const int4& it) {
     const int L = p->segs[it.x].len;
     return ((p->causal ? std::min(L, it.y + kBM) : L) + kBN - 1) / kBN;
   };
+  std::vector<int4> list;
+  for (int h = 0; h < p->heads; h++)
+    for (int s : order) {
+      const int L = p->segs[s].len;
+      const int n = (L + kBM - 1) / kBM;
+      // causal items get shorter with q0: longest (last query tile) first
+      for (int i = 0; i < n; i++) list.push_back(int4{s, kBM * (p->causal ? n - 1 - i : i), h, 0});
+    }
+  if (p->causal) {
+    // Causal items differ in length.  The head-major list is cut into kNumXcd
+    // contiguous parts of equal work (key tiles); each part runs in windows of
+    // consecutive heads holding at least kCausalRounds rounds of its longest
+    // item, longest item first inside a window.  A window keeps an XCD's
+    // concurrent workgroups on a few heads, which walk the same K/V tiles
+    // together through its L2; the longest-first order inside it bounds the
+    // idle tail when items are long against the work per compute unit.
+    int64_t total = 0;
+    int maxt = 1;
+    for (const int4& it : list) {
+      total += tiles(it);
+      maxt = std::max(maxt, tiles(it));
+    }
+    std::vector<std::vector<int4>> parts(kNumXcd);
+    int64_t acc = 0;
+    for (const int4& it : list) {
+      const int x = (int)std::min<int64_t>(kNumXcd - 1, acc * kNumXcd / std::max<int64_t>(1, total));
+      parts[x].push_back(it);
+      acc += tiles(it);
+    }
+    const int64_t window = (int64_t)kCausalRounds * kWgPerCu * cus * maxt;
+    for (auto& part : parts) {
+      size_t b = 0;
+      while (b < part.size()) {
+        int64_t w = 0;
+        size_t e = b;
+        // whole heads: extend to the end of the head at which the window is full
+        while (e < part.size() && (w < window || part[e].z == part[e - 1].z)) w += tiles(part[e++]);
+        std::stable_sort(part.begin() + b, part.begin() + e,
+                         [&](const int4& u, const int4& v) { return tiles(u) > tiles(v); });
+        b = e;
+      }
+    }
+    p->combine.clear();
+    p->npieces = 0;
+    size_t longest = 0;
+    p->real_items = 0;
+    for (const auto& part : parts) {
+      longest = std::max(longest, part.size());
+      p->real_items += (int64_t)part.size();
+    }
+    p->items.assign(longest * kNumXcd, int4{-1, 0, 0, 0});
+    for (int x = 0; x < kNumXcd; x++)
+      for (size_t j = 0; j < parts[x].size(); j++) p->items[j * kNumXcd + x] = parts[x][j];
+    return;
+  }
   const size_t per = (list.size() + kNumXcd - 1) / kNumXcd;
   std::vector<std::vector<int4>> parts(kNumXcd);
   int64_t slot = 0;

@@ -358,3 +358,21 @@ def test_batched_wrapper_rejects_cu_seqlens():
     q = torch.zeros((2, 4, 2, 128), dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         fa.attention(q, q, q, cu_seqlens=[0, 4, 8])
+
+
+def test_causal_parts_balanced_and_local():
+    """Causal schedule: the XCD parts (item j*8 + x of the launch order goes to
+    XCD x) carry equal work up to one item, and an XCD's first round of
+    workgroups stays on a few heads."""
+    T, H = 30272, 56
+    p = fa.Plan(T, H, [0, T], device=-1, causal=True)
+    items = p.work_items()
+    tiles = lambda it: (min(T, it[1] + 256) + 63) // 64
+    work = []
+    for x in range(8):
+        part = [it for it in items[x::8] if it[0] >= 0]
+        work.append(sum(tiles(it) for it in part))
+        first_round = part[:32]
+        assert len({it[2] for it in first_round}) <= 4          # heads in flight on the XCD
+        assert tiles(first_round[0]) == max(tiles(it) for it in part[:len(first_round)])
+    assert max(work) - min(work) <= (T + 63) // 64
