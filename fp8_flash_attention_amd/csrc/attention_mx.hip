@@ -369,7 +369,10 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_attn_mx(MxAttentionArgs a) {
   for (int db = 0; db < 4; db++) vf[db] = lds_read16(smem + kVRing + voff[db]);
 
   // Iteration t (1 <= t <= nkt - 2): S holds tile t's scores, P tile t-1's
-  // probabilities, vf/vsc V(t-1).  At even t the barrier and the loads of K(t+3),
+  // probabilities, vf/vsc V(t-1).  The score products of tile t+1 are spread
+  // between the P V products and the softmax of tile t (no scheduling fences:
+  // the compiler interleaves them; 4% faster than fenced slots with Q
+  // centring, the same without).  At even t the barrier and the loads of K(t+3),
   // K(t+4) (waves 0-3) or V(t+2), V(t+3) (waves 4-7); a pending rescale;
   // O += P(t-1) V(t-1); the softmax of tile t; the scores of tile t+1; V(t)
   // read for the next iteration.
@@ -394,26 +397,44 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_attn_mx(MxAttentionArgs a) {
     v4i kf[2][2], Pn;
     int ks[2];
     read_k(kbp, kf, ks);
-    fence();
     O[0] = mfma4<0, 0>(vf[0], P, O[0], vsc, pe);
     const int e = rowmax_update(std::false_type{});
     const float sc = scale_of(e);
-    fence();
+    v16f s0, s1;
     O[1] = mfma4<1, 0>(vf[1], P, O[1], vsc, pe);
+    if (QC) {
+      s0 = mfma4<0, 0>(kf[0][0], mf[0], NB, ks[0], msc);
+      s1 = mfma4<0, 0>(kf[1][0], mf[0], NB, ks[1], msc);
+    } else {
+      s0 = mfma4<0, 0>(kf[0][0], qf[0], NB, ks[0], qsc);
+    }
     Pn[0] = probs8(0, sc);
-    fence();
     O[2] = mfma4<2, 0>(vf[2], P, O[2], vsc, pe);
+    if (QC) {
+      s0 = mfma4<1, 1>(kf[0][1], mf[1], s0, ks[0], msc);
+      s1 = mfma4<1, 1>(kf[1][1], mf[1], s1, ks[1], msc);
+    } else {
+      s1 = mfma4<0, 0>(kf[1][0], qf[0], NB, ks[1], qsc);
+    }
     Pn[1] = probs8(1, sc);
-    fence();
     O[3] = mfma4<3, 0>(vf[3], P, O[3], vsc, pe);
     lacc = mfma16_4(sel, P, lacc, pe);
+    if (QC) {
+      s0 = mfma4<0, 0>(kf[0][0], qf[0], s0, ks[0], qsc);
+      s1 = mfma4<0, 0>(kf[1][0], qf[0], s1, ks[1], qsc);
+    } else {
+      s0 = mfma4<1, 1>(kf[0][1], qf[1], s0, ks[0], qsc);
+    }
     vsc = *reinterpret_cast<const int*>(vn + vso);
 #pragma unroll
     for (int db = 0; db < 4; db++) vf[db] = lds_read16(vn + voff[db]);
     Pn[2] = probs8(2, sc);
-    fence();
-    v16f s0, s1;
-    scores(kf, ks, s0, s1);
+    if (QC) {
+      s0 = mfma4<1, 1>(kf[0][1], qf[1], s0, ks[0], qsc);
+      s1 = mfma4<1, 1>(kf[1][1], qf[1], s1, ks[1], qsc);
+    } else {
+      s1 = mfma4<1, 1>(kf[1][1], qf[1], s1, ks[1], qsc);
+    }
     Pn[3] = probs8(3, sc);
     P = Pn;
     pe = e + 127;
