@@ -86,7 +86,7 @@ def cpu_baseline(w, q, k, v, budget_s: float):
         A.attention_rows(qc, kc, vc, cu, w.softmax_scale, rows)
         for r in rows:
             s = max(i for i in range(len(seg)) if cu[i] <= r)
-            flops += 4.0 * seg[s] * w.heads * 128
+            flops += 4.0 * seg[s] * w.heads * w.head_dim
         rows_done += len(rows)
         if time.time() - t0 >= budget_s:
             break
@@ -131,9 +131,9 @@ def main() -> int:
     q, k, v = generate(w, device="cuda")
     mx = args.fmt == "mxfp4"
     plan = fa.Plan(w.tokens, w.heads, w.cu_seqlens, w.softmax_scale, device=0, fmt=args.fmt,
-                   q_centre=mx and args.q_centre, causal=args.causal)
+                   q_centre=mx and args.q_centre, causal=args.causal, head_dim=w.head_dim)
     ws = plan.new_workspace()
-    out = torch.empty((w.tokens, w.heads, 128), dtype=torch.bfloat16, device=dev)
+    out = torch.empty((w.tokens, w.heads, w.head_dim), dtype=torch.bfloat16, device=dev)
     stream = torch.cuda.current_stream(dev)
 
     def step(ev=None):
@@ -164,7 +164,7 @@ def main() -> int:
     ms_step = wall * 1e3 / args.steps
     ms_fwd = sum(fwd_ms) / len(fwd_ms)
     ms_quant = sum(s - f for s, f in zip(step_ms, fwd_ms)) / len(fwd_ms)
-    flops = (2.0 * sum(L * (L + 1) for L in w.segments) * w.heads * 128) if args.causal else w.flops
+    flops = (2.0 * sum(L * (L + 1) for L in w.segments) * w.heads * w.head_dim) if args.causal else w.flops
     value = flops / (ms_step * 1e-3) / 1e12
     fwd_tflops = flops / (ms_fwd * 1e-3) / 1e12
 
@@ -187,7 +187,8 @@ def main() -> int:
     key = w.name + (":mxfp4" + (":qc" if args.q_centre else "") if mx else "") + (":causal" if args.causal else "")
     traffic = measured_traffic(key, kfile)
     res = {
-        "metric": METRIC_FP4 if mx else (METRIC_CAUSAL if args.causal else METRIC),
+        "metric": (METRIC_FP4 if mx else (METRIC_CAUSAL if args.causal else METRIC)) + (
+            f" [head_dim {w.head_dim}]" if w.head_dim != 128 else ""),
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -199,7 +200,7 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": "fp4e2m1" if mx else "fp8e4m3",
         "data": "synthetic",
-        "config": {"workload": w.name, "tokens": w.tokens, "heads": w.heads, "head_dim": 128,
+        "config": {"workload": w.name, "tokens": w.tokens, "heads": w.heads, "head_dim": w.head_dim,
                    "cu_seqlens": list(w.cu_seqlens), "seed": w.seed, "softmax_scale": w.softmax_scale,
                    "k_offset_var": w.k_offset_var, "step": "quantize + forward",
                    **({"format": "mxfp4", "q_centre": bool(args.q_centre)} if mx else {}),
@@ -224,7 +225,7 @@ def main() -> int:
             "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
             # codes: 1 B per element (E4M3) or 0.5 B + 1/32 B of scales (FP4) for Q, K, V; BF16 output
             "algorithmic_bytes": (int(3 * w.tokens * w.heads * (64 + 4) + 2 * w.tokens * w.heads * 128) if mx
-                                  else 5 * w.tokens * w.heads * 128),
+                                  else 5 * w.tokens * w.heads * w.head_dim),
         },
     }
     if args.copy_calibration > 0:

@@ -53,12 +53,13 @@ class Plan:
     quantizes every segment with its own per-head scales.  ``fmt`` is
     ``"e4m3"`` (default) or ``"mxfp4"``; ``q_centre`` (mxfp4 only) centres Q
     by its 128-row block means.  ``causal`` (e4m3 only): query i of a segment
-    attends to the keys j <= i of that segment.
+    attends to the keys j <= i of that segment.  ``head_dim``: 128, or 64
+    (e4m3 only).
     """
 
     def __init__(self, tokens: int, heads: int, cu_seqlens: Optional[Sequence[int]] = None,
                  softmax_scale: Optional[float] = None, device=None, segment_scales: bool = False,
-                 fmt: str = "e4m3", q_centre: bool = False, causal: bool = False):
+                 fmt: str = "e4m3", q_centre: bool = False, causal: bool = False, head_dim: int = HEAD_DIM):
         L = _lib.lib()
         if cu_seqlens is None:
             cu_seqlens = [0, tokens]
@@ -73,19 +74,22 @@ class Plan:
         self.tokens = int(tokens)
         self.heads = int(heads)
         self.cu_seqlens = tuple(cu)
-        self.softmax_scale = float(DEFAULT_SCALE if softmax_scale is None else softmax_scale)
+        self.softmax_scale = float(1.0 / math.sqrt(head_dim) if softmax_scale is None else softmax_scale)
         self.segment_scales = bool(segment_scales)
         if fmt not in ("e4m3", "mxfp4"):
             raise ValueError(f"fmt must be 'e4m3' or 'mxfp4' (got {fmt!r})")
         self.fmt = fmt
         self.q_centre = bool(q_centre)
         self.causal = bool(causal)
+        if head_dim not in (64, HEAD_DIM):
+            raise ValueError(f"head_dim must be 64 or {HEAD_DIM} (got {head_dim})")
+        self.head_dim = int(head_dim)
         arr = (ctypes.c_int32 * len(cu))(*cu)
         h = ctypes.c_void_p()
         self._h = None
         flags = ((_lib.PLAN_SEGMENT_SCALES if self.segment_scales else 0)
                  | (_lib.PLAN_MXFP4 if fmt == "mxfp4" else 0) | (_lib.PLAN_Q_CENTRE if self.q_centre else 0)
-                 | (_lib.PLAN_CAUSAL if self.causal else 0))
+                 | (_lib.PLAN_CAUSAL if self.causal else 0) | (_lib.PLAN_HEAD_DIM_64 if self.head_dim == 64 else 0))
         _lib.check(L.fp8attn_plan_ex(ctypes.byref(h), self.tokens, self.heads, arr, len(cu) - 1,
                                      ctypes.c_float(self.softmax_scale), self.device_index, flags),
                    "fp8attn_plan_ex")
@@ -104,7 +108,8 @@ class Plan:
         buf = (ctypes.c_int64 * _lib.PLAN_INFO_LEN)()
         _lib.check(_lib.lib().fp8attn_plan_info(self._h, buf), "fp8attn_plan_info")
         keys = ["tokens", "heads", "num_segments", "workspace_rows", "work_items", "stat_chunks",
-                "query_tile", "key_tile", "segment_scales", "partial_slots", "mxfp4", "q_centre", "causal"]
+                "query_tile", "key_tile", "segment_scales", "partial_slots", "mxfp4", "q_centre", "causal",
+                "head_dim"]
         return dict(zip(keys, list(buf)))
 
     def work_items(self):
@@ -147,11 +152,11 @@ class Plan:
             pass
 
 
-def _strides(x: torch.Tensor, name: str):
+def _strides(x: torch.Tensor, name: str, head_dim: int = HEAD_DIM):
     if x.dtype != torch.bfloat16:
         raise TypeError(f"{name} must be bfloat16 (got {x.dtype})")
-    if x.dim() != 3 or x.shape[2] != HEAD_DIM:
-        raise ValueError(f"{name} must have shape [tokens, heads, {HEAD_DIM}] (got {tuple(x.shape)})")
+    if x.dim() != 3 or x.shape[2] != head_dim:
+        raise ValueError(f"{name} must have shape [tokens, heads, {head_dim}] (got {tuple(x.shape)})")
     if x.stride(2) != 1:
         raise ValueError(f"{name} must have unit stride in the head dimension")
     return _lib.i64_array([x.stride(0), x.stride(1)])
@@ -173,7 +178,8 @@ def quantize(plan: Plan, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, work
             raise ValueError(f"{name} shape {tuple(x.shape)} does not match the plan")
         _on_plan_device(plan, x, name)
     _on_plan_device(plan, workspace, "workspace")
-    qs, ks, vs = _strides(q, "q"), _strides(k, "k"), _strides(v, "v")
+    D = plan.head_dim
+    qs, ks, vs = _strides(q, "q", D), _strides(k, "k", D), _strides(v, "v", D)
     st = _stream_handle(plan.device, stream)
     _lib.check(_lib.lib().fp8attn_quantize(plan.handle, ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k.data_ptr()),
                                            ctypes.c_void_p(v.data_ptr()), qs, ks, vs,
@@ -186,12 +192,12 @@ def forward(plan: Plan, workspace: torch.Tensor, out: Optional[torch.Tensor] = N
             lse: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """``fp8attn_forward``: BF16 output from the codes in ``workspace``."""
     if out is None:
-        out = torch.empty((plan.tokens, plan.heads, HEAD_DIM), dtype=torch.bfloat16, device=plan.device)
-    if tuple(out.shape) != (plan.tokens, plan.heads, HEAD_DIM):
+        out = torch.empty((plan.tokens, plan.heads, plan.head_dim), dtype=torch.bfloat16, device=plan.device)
+    if tuple(out.shape) != (plan.tokens, plan.heads, plan.head_dim):
         raise ValueError("out shape does not match the plan")
     _on_plan_device(plan, out, "out")
     _on_plan_device(plan, workspace, "workspace")
-    os_ = _strides(out, "out")
+    os_ = _strides(out, "out", plan.head_dim)
     lse_ptr = None
     if lse is not None:
         if lse.dtype != torch.float32 or tuple(lse.shape) != (plan.heads, plan.tokens) or not lse.is_contiguous():
@@ -209,15 +215,16 @@ _PLANS: Dict[Tuple, Plan] = {}
 
 
 def get_plan(tokens: int, heads: int, cu_seqlens: Sequence[int], softmax_scale: float, device: int,
-             segment_scales: bool = False, fmt: str = "e4m3", q_centre: bool = False, causal: bool = False) -> Plan:
+             segment_scales: bool = False, fmt: str = "e4m3", q_centre: bool = False, causal: bool = False,
+             head_dim: int = HEAD_DIM) -> Plan:
     """Plans are cached per (cu_seqlens, heads, scale, device, quantization mode), as the FlashInfer
     page caches its segment plan per (cu_seqlens, heads, device).  A plan holds only small tables."""
     key = (tuple(int(x) for x in cu_seqlens), int(heads), float(softmax_scale), int(device), bool(segment_scales),
-           fmt, bool(q_centre), bool(causal))
+           fmt, bool(q_centre), bool(causal), int(head_dim))
     p = _PLANS.get(key)
     if p is None:
         p = Plan(tokens, heads, cu_seqlens, softmax_scale, device, segment_scales=segment_scales, fmt=fmt,
-                 q_centre=q_centre, causal=causal)
+                 q_centre=q_centre, causal=causal, head_dim=head_dim)
         _PLANS[key] = p
     return p
 
@@ -232,7 +239,8 @@ def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: Opt
     ``segment_scales`` quantizes every segment with its own per-head scales.
     ``fmt="mxfp4"`` runs the block-scaled FP4 variant (``q_centre`` adds Q
     block-mean centring); it returns no LSE.  ``causal=True`` masks keys after
-    each query (E4M3 only).  Batched [B, T, heads, 128] inputs (views of
+    each query (E4M3 only).  The head size (128, or 64 for E4M3) is taken from
+    the inputs' last dimension.  Batched [B, T, heads, 128] inputs (views of
     [B*T, heads, 128]) are run as B segments of T tokens and returned as
     [B, T, heads, 128] (with the LSE as [heads, B*T]).
     """
@@ -251,14 +259,14 @@ def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: Opt
         if return_lse:
             return res[0].view(B, T0, *res[0].shape[1:]), res[1]
         return res.view(B, T0, *res.shape[1:])
-    T, H = q.shape[0], q.shape[1]
+    T, H, D = q.shape[0], q.shape[1], q.shape[-1]
     if cu_seqlens is None:
         cu_seqlens = [0, T]
     elif isinstance(cu_seqlens, torch.Tensor):
         cu_seqlens = cu_seqlens.tolist()
-    scale = DEFAULT_SCALE if softmax_scale is None else float(softmax_scale)
+    scale = 1.0 / math.sqrt(D) if softmax_scale is None else float(softmax_scale)
     dev = q.device.index if q.device.index is not None else torch.cuda.current_device()
-    plan = get_plan(T, H, cu_seqlens, scale, dev, segment_scales, fmt, q_centre, causal)
+    plan = get_plan(T, H, cu_seqlens, scale, dev, segment_scales, fmt, q_centre, causal, D)
     ws = workspace if workspace is not None else plan.new_workspace()
     quantize(plan, q, k, v, ws)
     lse = torch.empty((H, T), dtype=torch.float32, device=q.device) if return_lse else None

@@ -21,7 +21,8 @@ PLAN_SEGMENT_SCALES = 1          # FP8ATTN_PLAN_SEGMENT_SCALES
 PLAN_MXFP4 = 2                   # FP8ATTN_PLAN_MXFP4
 PLAN_Q_CENTRE = 4                # FP8ATTN_PLAN_Q_CENTRE
 PLAN_CAUSAL = 8                  # FP8ATTN_PLAN_CAUSAL
-PLAN_INFO_LEN = 13
+PLAN_HEAD_DIM_64 = 16            # FP8ATTN_PLAN_HEAD_DIM_64
+PLAN_INFO_LEN = 14
 
 # Every symbol include/fp8attn.h declares, with (restype, argtypes).
 _i64p = ctypes.POINTER(ctypes.c_int64)

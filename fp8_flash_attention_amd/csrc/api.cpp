@@ -32,6 +32,7 @@ struct fp8attn_plan_s {
   int32_t mx = 0;                 // FP8ATTN_PLAN_MXFP4
   int32_t q_centre = 0;           // FP8ATTN_PLAN_Q_CENTRE
   int32_t causal = 0;             // FP8ATTN_PLAN_CAUSAL
+  int32_t head_dim = kHeadDim;    // 64 with FP8ATTN_PLAN_HEAD_DIM_64
   float scale = 0.f;
   int device = -1;
   std::vector<int32_t> cu;
@@ -91,20 +92,20 @@ WorkspaceLayout make_layout_mx(int64_t rows, int heads, int nseg, int nchunks) {
   return w;
 }
 
-WorkspaceLayout make_layout(int64_t rows, int heads, int nseg, int nscale, int nchunks, int64_t npieces) {
+WorkspaceLayout make_layout(int64_t rows, int heads, int nseg, int nscale, int nchunks, int64_t npieces, int D) {
   WorkspaceLayout w{};
   w.rows = rows;
   w.npieces = npieces;
-  const size_t codes = (size_t)heads * rows * kHeadDim;
+  const size_t codes = (size_t)heads * rows * D;
   size_t off = 0;
   w.q_off = off; off = align_up(off + codes, 256);
   w.k_off = off; off = align_up(off + codes, 256);
   w.v_off = off; off = align_up(off + codes, 256);
   w.scale_off = off; off = align_up(off + sizeof(float) * 3 * (size_t)nscale * heads, 256);
-  w.mu_off = off; off = align_up(off + sizeof(float) * (size_t)nseg * heads * kHeadDim, 256);
-  w.kstat_off = off; off = align_up(off + sizeof(KStat) * (size_t)nchunks * heads * kHeadDim, 256);
+  w.mu_off = off; off = align_up(off + sizeof(float) * (size_t)nseg * heads * D, 256);
+  w.kstat_off = off; off = align_up(off + sizeof(KStat) * (size_t)nchunks * heads * D, 256);
   w.amax_off = off; off = align_up(off + sizeof(float) * 2 * (size_t)nchunks * heads, 256);
-  w.part_o_off = off; off = align_up(off + sizeof(float) * (size_t)npieces * kBM * kHeadDim, 256);
+  w.part_o_off = off; off = align_up(off + sizeof(float) * (size_t)npieces * kBM * D, 256);
   w.part_w_off = off; off = align_up(off + sizeof(float) * (size_t)npieces * kBM, 256);
   w.part_lse_off = off; off = align_up(off + sizeof(float) * (size_t)npieces * kBM, 256);
   w.total = off;
@@ -266,8 +267,11 @@ fp8attn_status fp8attn_plan_ex(fp8attn_plan_t* plan_out, int64_t tokens, int32_t
                                int32_t device, uint32_t flags) {
   if (plan_out == nullptr) return fail(FP8ATTN_EINVAL, "plan_out is NULL");
   *plan_out = nullptr;
-  if ((flags & ~(FP8ATTN_PLAN_SEGMENT_SCALES | FP8ATTN_PLAN_MXFP4 | FP8ATTN_PLAN_Q_CENTRE | FP8ATTN_PLAN_CAUSAL)) != 0)
+  if ((flags & ~(FP8ATTN_PLAN_SEGMENT_SCALES | FP8ATTN_PLAN_MXFP4 | FP8ATTN_PLAN_Q_CENTRE | FP8ATTN_PLAN_CAUSAL |
+                 FP8ATTN_PLAN_HEAD_DIM_64)) != 0)
     return fail(FP8ATTN_EINVAL, "unknown plan flags");
+  if ((flags & FP8ATTN_PLAN_HEAD_DIM_64) && (flags & FP8ATTN_PLAN_MXFP4))
+    return fail(FP8ATTN_EINVAL, "FP8ATTN_PLAN_HEAD_DIM_64 is not available for FP8ATTN_PLAN_MXFP4 plans");
   if ((flags & FP8ATTN_PLAN_CAUSAL) && (flags & FP8ATTN_PLAN_MXFP4))
     return fail(FP8ATTN_EINVAL, "FP8ATTN_PLAN_CAUSAL is not available for FP8ATTN_PLAN_MXFP4 plans");
   if ((flags & FP8ATTN_PLAN_Q_CENTRE) && !(flags & FP8ATTN_PLAN_MXFP4))
@@ -299,6 +303,7 @@ fp8attn_status fp8attn_plan_ex(fp8attn_plan_t* plan_out, int64_t tokens, int32_t
   p->mx = (flags & FP8ATTN_PLAN_MXFP4) ? 1 : 0;
   p->q_centre = (flags & FP8ATTN_PLAN_Q_CENTRE) ? 1 : 0;
   p->causal = (flags & FP8ATTN_PLAN_CAUSAL) ? 1 : 0;
+  p->head_dim = (flags & FP8ATTN_PLAN_HEAD_DIM_64) ? 64 : kHeadDim;
   p->cu.assign(cu, cu + num_segments + 1);
   int64_t row = 0;
   int32_t chunk = 0;
@@ -316,9 +321,10 @@ fp8attn_status fp8attn_plan_ex(fp8attn_plan_t* plan_out, int64_t tokens, int32_t
   row += kGuardRows;
   // the attention kernel addresses one head's code rows through 32-bit buffer
   // offsets: rows * 128 bytes must fit
-  if (row * kHeadDim > (int64_t)INT32_MAX) {
+  if (row * p->head_dim > (int64_t)INT32_MAX) {
     delete p;
-    return fail(FP8ATTN_EUNSUPPORTED, "too many padded rows for 32-bit code offsets (about 16.7M tokens at most)");
+    return fail(FP8ATTN_EUNSUPPORTED, "too many padded rows for 32-bit code offsets (about 16.7M tokens at most "
+                                      "at head_dim 128)");
   }
   int cus = 256;   // MI355X; the device's own count when the plan has one
   if (device >= 0) {
@@ -331,7 +337,7 @@ fp8attn_status fp8attn_plan_ex(fp8attn_plan_t* plan_out, int64_t tokens, int32_t
     return fail(FP8ATTN_EUNSUPPORTED, "too many split work items");
   }
   p->ws = p->mx ? make_layout_mx(row, heads, num_segments, (int)p->chunks.size())
-                : make_layout(row, heads, num_segments, p->nscale, (int)p->chunks.size(), p->npieces);
+                : make_layout(row, heads, num_segments, p->nscale, (int)p->chunks.size(), p->npieces, p->head_dim);
 
   if (device >= 0) {
     DeviceGuard g(device);
@@ -434,6 +440,7 @@ fp8attn_status fp8attn_quantize(fp8attn_plan_t p, const void* q, const void* k, 
   a.softmax_scale = p->scale;
   a.mx = p->mx;
   a.q_centre = p->q_centre;
+  a.head_dim = p->head_dim;
   if (p->mx) {
     a.bscale[0] = ws + p->ws.qs_off;
     a.bscale[1] = ws + p->ws.ks_off;
@@ -508,6 +515,7 @@ fp8attn_status fp8attn_forward(fp8attn_plan_t p, void* workspace, size_t workspa
   a.nitems = p->real_items > 0 ? (int32_t)p->items.size() : 0;
   a.nscale = p->nscale;
   a.causal = p->causal;
+  a.head_dim = p->head_dim;
   a.softmax_scale = p->scale;
   hipError_t e = launch_attention(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(FP8ATTN_EHIP, std::string("attention launch failed: ") + hipGetErrorString(e));
@@ -524,6 +532,7 @@ fp8attn_status fp8attn_forward(fp8attn_plan_t p, void* workspace, size_t workspa
     c.os1 = a.os1;
     c.lse = lse;
     c.tokens = p->tokens;
+    c.head_dim = p->head_dim;
     e = launch_combine(c, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(FP8ATTN_EHIP, std::string("combine launch failed: ") + hipGetErrorString(e));
   }
@@ -534,7 +543,7 @@ fp8attn_status fp8attn_workspace_region(fp8attn_plan_t p, const void* workspace,
                                         const void** ptr_out, int64_t dims_out[3]) {
   if (p == nullptr || ptr_out == nullptr || dims_out == nullptr) return fail(FP8ATTN_EINVAL, "NULL argument");
   const uint8_t* ws = static_cast<const uint8_t*>(workspace);
-  const int64_t H = p->heads, R = p->ws.rows, D = kHeadDim;
+  const int64_t H = p->heads, R = p->ws.rows, D = p->head_dim;
   if (which == FP8ATTN_REGION_ROWMAP) {
     if (p->device < 0) return fail(FP8ATTN_EINVAL, "host-only plan has no device tables");
     *ptr_out = p->d_rowmap;
@@ -568,7 +577,7 @@ fp8attn_status fp8attn_workspace_region(fp8attn_plan_t p, const void* workspace,
   return FP8ATTN_OK;
 }
 
-fp8attn_status fp8attn_plan_info(fp8attn_plan_t p, int64_t info[13]) {
+fp8attn_status fp8attn_plan_info(fp8attn_plan_t p, int64_t info[14]) {
   if (p == nullptr || info == nullptr) return fail(FP8ATTN_EINVAL, "NULL argument");
   info[0] = p->tokens;
   info[1] = p->heads;
@@ -583,6 +592,7 @@ fp8attn_status fp8attn_plan_info(fp8attn_plan_t p, int64_t info[13]) {
   info[10] = p->mx;
   info[11] = p->q_centre;
   info[12] = p->causal;
+  info[13] = p->head_dim;
   return FP8ATTN_OK;
 }
 

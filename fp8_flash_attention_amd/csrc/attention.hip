@@ -79,12 +79,9 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLog2Ref = 6.807354922057604f;   // log2(112): reference maximum maps to 448 / 4
 constexpr float kLog2Max = 8.807354922057604f;   // log2(448), the largest E4M3 value
 constexpr float kLn2 = 0.6931471805599453f;
-constexpr int kTile = kBN * kHeadDim;            // bytes of one K (or V^T) tile
 constexpr int kSlots = 4;                        // ring slots per operand
 constexpr int kBarEvery = kSlots / 2;            // iterations per barrier
 constexpr int kWavesWG = kBM / 32;               // waves per workgroup, 32 queries each
-constexpr int kLoadsPerTile = kTile / 1024 / kWavesWG;   // direct 1 KB loads per wave per K (or V) tile
-constexpr int kVRing = kSlots * kTile;           // V ring follows the K ring in LDS
 constexpr int kBufferFlags = 0x00020000;         // raw buffer descriptor word 3 (gfx9 family)
 static_assert((kBM == 128 || kBM == 256) && kBN == 64, "4 or 8 waves x 32 queries, 64-key tiles");
 
@@ -129,10 +126,14 @@ __device__ __forceinline__ v8i lds_read32(const uint8_t* base, int off_lo, int o
   return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
 }
 
-// LDS tile geometry.  K slot: [64 keys][128 B], row r chunk c at
-// r*128 + ((c ^ ((r >> 1) & 7)) * 16).  V^T slot: [128 channels][64 B], row d
-// chunk c at d*64 + ((c ^ ((d >> 2) & 3)) * 16).
-__device__ __forceinline__ int k_lds_off(int row, int chunk) { return row * 128 + ((chunk ^ ((row >> 1) & 7)) << 4); }
+// LDS tile geometry.  K slot: [64 keys][D B]; D = 128: row r chunk c at
+// r*128 + ((c ^ ((r >> 1) & 7)) * 16); D = 64: at r*64 + ((c ^ ((r >> 2) & 3)) * 16)
+// (either way the 16 lanes of a read phase hit 16 distinct bank groups).
+// V^T slot: [D channels][64 B], row d chunk c at d*64 + ((c ^ ((d >> 2) & 3)) * 16).
+template <int D>
+__device__ __forceinline__ int k_swz(int row) { return D == 128 ? ((row >> 1) & 7) : ((row >> 2) & 3); }
+template <int D>
+__device__ __forceinline__ int k_lds_off(int row, int chunk) { return row * D + ((chunk ^ k_swz<D>(row)) << 4); }
 __device__ __forceinline__ int v_lds_off(int d, int chunk) { return d * 64 + ((chunk ^ ((d >> 2) & 3)) << 4); }
 
 // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
@@ -180,8 +181,18 @@ __device__ __forceinline__ void tail_iters(F& iter, int& t, int nkt) {
   }
 }
 
-template <bool LSE, bool CAUSAL>
+template <bool LSE, bool CAUSAL, int D>
 __global__ __launch_bounds__(64 * kWavesWG, 8 / kWavesWG) void k_attn(AttentionArgs a) {
+  constexpr int kTile = kBN * D;                 // bytes of one K (or V^T) tile
+  constexpr int kVRing = kSlots * kTile;         // V ring follows the K ring in LDS
+  constexpr int NH = D / 64;                     // 64-channel halves of Q and K
+  constexpr int NDB = D / 32;                    // 32-channel blocks of O
+  // Direct 1 KB loads per tile: every wave loads kLoadsPerTile of each K and V
+  // tile, or (D = 64, 4 loads a tile) waves 0-3 load K and waves 4-7 V^T.
+  constexpr int kLoads = kTile / 1024;
+  constexpr bool kSplitLoads = kLoads < kWavesWG;
+  constexpr int kLoadsPerTile = kSplitLoads ? 1 : kLoads / kWavesWG;
+  static_assert(D == 128 || (D == 64 && kWavesWG == 8), "head_dim 128, or 64 with 256-query items");
   __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * kVRing];
 
   const int4 it = a.items[blockIdx.x];
@@ -208,9 +219,9 @@ __global__ __launch_bounds__(64 * kWavesWG, 8 / kWavesWG) void k_attn(AttentionA
   const int lg = lane >> 5;
 
   const size_t hrow = (size_t)h * a.rows + si.row0;
-  const uint8_t* Qh = a.q_codes + hrow * kHeadDim;
-  const uint8_t* Kh = a.k_codes + hrow * kHeadDim + (size_t)kt0 * kTile;
-  const uint8_t* Vh = a.v_codes + (size_t)h * kHeadDim * a.rows + si.row0 + (size_t)kt0 * kBN;
+  const uint8_t* Qh = a.q_codes + hrow * D;
+  const uint8_t* Kh = a.k_codes + hrow * D + (size_t)kt0 * kTile;
+  const uint8_t* Vh = a.v_codes + (size_t)h * D * a.rows + si.row0 + (size_t)kt0 * kBN;
 
   // scales [3][S][H]: S = 1, or one set per segment
   const int sset = a.nscale > 1 ? it.x : 0;
@@ -228,17 +239,17 @@ __global__ __launch_bounds__(64 * kWavesWG, 8 / kWavesWG) void k_attn(AttentionA
   // Q as B operands: queries q0 + 32*wave + (lane%32), channels
   // 64*half + 32*(lane/32) .. +32.  Rows past the segment end read zero codes,
   // guard rows or the next segment's rows and are never stored.
-  v8i qf[2];
+  v8i qf[NH];
 #pragma unroll
-  for (int half = 0; half < 2; half++)
-    qf[half] = *reinterpret_cast<const v8i*>(Qh + (size_t)(q0 + 32 * wave + lq) * kHeadDim + 64 * half + 32 * lg);
+  for (int half = 0; half < NH; half++)
+    qf[half] = *reinterpret_cast<const v8i*>(Qh + (size_t)(q0 + 32 * wave + lq) * D + 64 * half + 32 * lg);
 
   // Per-lane LDS read offsets inside a slot.
-  int koff[2][2];   // [half][sub]
+  int koff[NH][2];   // [half][sub]
 #pragma unroll
-  for (int half = 0; half < 2; half++)
+  for (int half = 0; half < NH; half++)
 #pragma unroll
-    for (int sub = 0; sub < 2; sub++) koff[half][sub] = k_lds_off(lq, 4 * half + 2 * lg + sub);
+    for (int sub = 0; sub < 2; sub++) koff[half][sub] = k_lds_off<D>(lq, 4 * half + 2 * lg + sub);
   int voff[2];
 #pragma unroll
   for (int sub = 0; sub < 2; sub++) voff[sub] = v_lds_off(lq, 2 * lg + sub);
@@ -248,29 +259,37 @@ __global__ __launch_bounds__(64 * kWavesWG, 8 / kWavesWG) void k_attn(AttentionA
   // 16-byte slot p = 64*i + lane of load i receives the global chunk that the
   // swizzle places there.
   const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)Kh, (short)0, (int)((a.rows - si.row0) * kHeadDim - (int64_t)kt0 * kTile), kBufferFlags);
+      (void*)Kh, (short)0, (int)((a.rows - si.row0) * D - (int64_t)kt0 * kTile), kBufferFlags);
   const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)Vh, (short)0, (int)(a.rows * kHeadDim - si.row0 - (int64_t)kt0 * kBN), kBufferFlags);
+      (void*)Vh, (short)0, (int)(a.rows * D - si.row0 - (int64_t)kt0 * kBN), kBufferFlags);
+  // with split loads, waves 0..kLoads-1 load K and the others V^T
+  const bool k_wave = !kSplitLoads || wave < kLoads;
+  const int lw = kSplitLoads ? wave % kLoads : wave;   // this wave's load index within a tile
   int ksrc[kLoadsPerTile], vsrc[kLoadsPerTile];
 #pragma unroll
   for (int u = 0; u < kLoadsPerTile; u++) {
-    const int p = 64 * (kLoadsPerTile * wave + u) + lane;
-    ksrc[u] = (p >> 3) * kHeadDim + (((p & 7) ^ ((p >> 4) & 7)) << 4);      // K row p/8, swizzled chunk p%8
+    const int p = 64 * (kLoadsPerTile * lw + u) + lane;
+    const int kr = p / (D / 16);                    // K row of 16-byte slot p, D/16 chunks a row
+    ksrc[u] = kr * D + (((p % (D / 16)) ^ k_swz<D>(kr)) << 4);
     vsrc[u] = (p >> 2) * (int)a.rows + (((p & 3) ^ ((p >> 4) & 3)) << 4);   // V^T row p/4, swizzled chunk p%4
   }
-  const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_ptr_t)smem + 1024 * kLoadsPerTile * wave;   // LDS byte address of this wave's loads
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_ptr_t)smem + 1024 * kLoadsPerTile * lw;   // LDS byte address of this wave's loads
   // Tile indices past the segment's last tile are clamped: such loads only
   // refill a free slot with valid data, and every iteration issues the same
   // number of loads, which the vmcnt waits rely on.
   auto load_k = [&](int kt, int slot) __attribute__((always_inline)) {
     kt = kt < nkt ? kt : nkt - 1;
+    if (k_wave) {
 #pragma unroll
-    for (int u = 0; u < kLoadsPerTile; u++) lds_dma(krs, lds0 + slot * kTile + u * 1024, ksrc[u], kt * kTile);
+      for (int u = 0; u < kLoadsPerTile; u++) lds_dma(krs, lds0 + slot * kTile + u * 1024, ksrc[u], kt * kTile);
+    }
   };
   auto load_v = [&](int kt, int slot) __attribute__((always_inline)) {
     kt = kt < nkt ? kt : nkt - 1;
+    if (!kSplitLoads || !k_wave) {
 #pragma unroll
-    for (int u = 0; u < kLoadsPerTile; u++) lds_dma(vrs, lds0 + kVRing + slot * kTile + u * 1024, vsrc[u], kt * kBN);
+      for (int u = 0; u < kLoadsPerTile; u++) lds_dma(vrs, lds0 + kVRing + slot * kTile + u * 1024, vsrc[u], kt * kBN);
+    }
   };
 
   // q_hat . mu per query, for the natural-log LSE of the uncentred scores:
@@ -278,10 +297,10 @@ __global__ __launch_bounds__(64 * kWavesWG, 8 / kWavesWG) void k_attn(AttentionA
   // so the centred LSE is short by softmax_scale * (q_hat . mu).
   float qmu = 0.f;
   if (LSE) {
-    const float* mu = a.mu + ((size_t)it.x * a.heads + h) * kHeadDim;
+    const float* mu = a.mu + ((size_t)it.x * a.heads + h) * D;
     float dot = 0.f;
 #pragma unroll
-    for (int half = 0; half < 2; half++)
+    for (int half = 0; half < NH; half++)
 #pragma unroll
       for (int w = 0; w < 8; w++) {
         const float* md = mu + 64 * half + 32 * lg + 4 * w;
@@ -300,14 +319,14 @@ __global__ __launch_bounds__(64 * kWavesWG, 8 / kWavesWG) void k_attn(AttentionA
   const int one = sel_lane ? 0x38383838 : 0;
   const v8i sel = v8i{one, one, one, one, one, one, one, one};
 
-  v16f O[4];       // O^T: lane l holds query l%32, channels 32*db + 8*(r/4) + 4*(l/32) + r%4
+  v16f O[NDB];     // O^T: lane l holds query l%32, channels 32*db + 8*(r/4) + 4*(l/32) + r%4
   v4f lacc = {};   // row sums of the packed P: lane j < 16 holds query j (row 0) and 16+j (row 1)
   float lex = 0.f; // FP32 row sum of the unrounded probabilities (LSE only; this lane's keys, current frame)
   float nb = 0.f;  // exp2 argument offset: x = c*s + nb
   float pshift = 0.f;   // reference shift still to be applied to O and l (log2 of the factor)
   bool pending = false; // wave-uniform: some lane has a pshift
 #pragma unroll
-  for (int db = 0; db < 4; db++) O[db] = v16f{};
+  for (int db = 0; db < NDB; db++) O[db] = v16f{};
   v16f NB = {};    // nb in every register: the initial accumulator of the score products
   v16f S[2];       // exp2 arguments x of the current tile [32-key block], refilled with the next tile's
   v8i P;           // packed probabilities of the previous tile, then of the current one
@@ -317,9 +336,13 @@ __global__ __launch_bounds__(64 * kWavesWG, 8 / kWavesWG) void k_attn(AttentionA
     const uint8_t* kb_base = smem + ks * kTile;
 #pragma unroll
     for (int kb = 0; kb < 2; kb++) {
-      const v8i k0 = lds_read32(kb_base + kb * 32 * 128, koff[0][0], koff[0][1]);
-      const v8i k1 = lds_read32(kb_base + kb * 32 * 128, koff[1][0], koff[1][1]);
-      S[kb] = mfma_fp8_scaled(k1, qf[1], mfma_fp8_scaled(k0, qf[0], NB, c_e8m0), c_e8m0);
+      const v8i k0 = lds_read32(kb_base + kb * 32 * D, koff[0][0], koff[0][1]);
+      if constexpr (NH == 2) {
+        const v8i k1 = lds_read32(kb_base + kb * 32 * D, koff[1][0], koff[1][1]);
+        S[kb] = mfma_fp8_scaled(k1, qf[1], mfma_fp8_scaled(k0, qf[0], NB, c_e8m0), c_e8m0);
+      } else {
+        S[kb] = mfma_fp8_scaled(k0, qf[0], NB, c_e8m0);
+      }
     }
   };
   // Apply a pending reference shift to O and l (rare; wave-uniform branch):
@@ -331,7 +354,7 @@ __global__ __launch_bounds__(64 * kWavesWG, 8 / kWavesWG) void k_attn(AttentionA
       lacc[0] *= alpha;
       lacc[1] *= __uint_as_float(pa[1]);   // lane j < 16: alpha of query 16+j
 #pragma unroll
-      for (int db = 0; db < 4; db++) O[db] *= alpha;
+      for (int db = 0; db < NDB; db++) O[db] *= alpha;
       pshift = 0.f;
       pending = false;
     }
@@ -432,7 +455,13 @@ __global__ __launch_bounds__(64 * kWavesWG, 8 / kWavesWG) void k_attn(AttentionA
   for (int i = 1; i <= kBarEvery; i++) load_k(i, i);
 #pragma unroll
   for (int i = 0; i < kBarEvery; i++) load_v(i, i);
-  wait_vmcnt<2 * kBarEvery * kLoadsPerTile>();
+  // K(0) has landed once only the later loads are outstanding (with split
+  // loads only the K waves issued K loads, and only they need to wait)
+  if constexpr (kSplitLoads) {
+    if (k_wave) wait_vmcnt<kBarEvery * kLoadsPerTile>();
+  } else {
+    wait_vmcnt<2 * kBarEvery * kLoadsPerTile>();
+  }
   barrier();
   qk(0);
   // Iteration 0: reference from tile 0; nothing to add to O yet.
@@ -447,8 +476,8 @@ __global__ __launch_bounds__(64 * kWavesWG, 8 / kWavesWG) void k_attn(AttentionA
   // V operands of the next product, read at the end of the iteration before
   // it (all four; two when the LSE sum needs the registers, the other two at
   // the top of the iteration, still ahead of its barrier).
-  constexpr int kPre = LSE ? 2 : 4;
-  v8i vf[4];
+  constexpr int kPre = NDB == 4 ? (LSE ? 2 : 4) : NDB;
+  v8i vf[NDB];
 #pragma unroll
   for (int db = 0; db < kPre; db++) vf[db] = lds_read32(smem + kVRing + db * 2048, voff[0], voff[1]);
   // Iteration t (S holds tile t's scores, P tile t-1's probabilities, vf the
@@ -469,7 +498,7 @@ __global__ __launch_bounds__(64 * kWavesWG, 8 / kWavesWG) void k_attn(AttentionA
     constexpr int PH = decltype(ph_c)::value;   // t % kSlots
     // With the LSE sum, two of the four V(t-1) operands are read here, before
     // the barrier: the loads after it may refill V(t-1)'s slot.
-    if (LSE) {
+    if constexpr (LSE && kPre < NDB) {
       const uint8_t* vp = smem + kVRing + ((PH + kSlots - 1) % kSlots) * kTile;   // V(t-1)
       vf[2] = lds_read32(vp + 2 * 2048, voff[0], voff[1]);
       vf[3] = lds_read32(vp + 3 * 2048, voff[0], voff[1]);
@@ -488,45 +517,78 @@ __global__ __launch_bounds__(64 * kWavesWG, 8 / kWavesWG) void k_attn(AttentionA
     const uint8_t* vn = smem + kVRing + PH * kTile;                  // V(t), read for the next iteration
     const uint8_t* kb = smem + ((PH + 1) % kSlots) * kTile;          // K(t+1)
     const int kbase = t * kBN;
-    v8i kf[2][2], Pn;
-    kf[0][0] = lds_read32(kb, koff[0][0], koff[0][1]);
-    kf[1][0] = lds_read32(kb + 4096, koff[0][0], koff[0][1]);
-    fence();
-    O[0] = mfma_fp8(vf[0], P, O[0]);
-    kf[0][1] = lds_read32(kb, koff[1][0], koff[1][1]);
-    if (CAUSAL && t >= tdiag) mask_causal(t);   // wave-uniform branch, diagonal tiles only
-    rowmax_update(std::false_type{});
-    fence();
-    O[1] = mfma_fp8(vf[1], P, O[1]);
-    kf[1][1] = lds_read32(kb + 4096, koff[1][0], koff[1][1]);
-    Pn[0] = probs4(0, 0, kbase);
-    fence();
-    O[2] = mfma_fp8(vf[2], P, O[2]);
-    Pn[1] = probs4(0, 1, kbase);
-    fence();
-    O[3] = mfma_fp8(vf[3], P, O[3]);
-    Pn[2] = probs4(0, 2, kbase);
-    fence();
-    lacc = mfma16_fp8(sel, P, lacc);
-    vf[0] = lds_read32(vn + 0 * 2048, voff[0], voff[1]);
-    vf[1] = lds_read32(vn + 1 * 2048, voff[0], voff[1]);
-    Pn[3] = probs4(0, 3, kbase);
-    fence();
-    const v16f s0 = mfma_fp8_scaled(kf[0][0], qf[0], NB, c_e8m0);
-    Pn[4] = probs4(1, 0, kbase);
-    fence();
-    const v16f s1 = mfma_fp8_scaled(kf[1][0], qf[0], NB, c_e8m0);
-    if (!LSE) {
-      vf[2] = lds_read32(vn + 2 * 2048, voff[0], voff[1]);
-      vf[3] = lds_read32(vn + 3 * 2048, voff[0], voff[1]);
+    v8i Pn;
+    if constexpr (NH == 2) {
+      v8i kf[2][2];
+      kf[0][0] = lds_read32(kb, koff[0][0], koff[0][1]);
+      kf[1][0] = lds_read32(kb + 4096, koff[0][0], koff[0][1]);
+      fence();
+      O[0] = mfma_fp8(vf[0], P, O[0]);
+      kf[0][1] = lds_read32(kb, koff[1][0], koff[1][1]);
+      if (CAUSAL && t >= tdiag) mask_causal(t);   // wave-uniform branch, diagonal tiles only
+      rowmax_update(std::false_type{});
+      fence();
+      O[1] = mfma_fp8(vf[1], P, O[1]);
+      kf[1][1] = lds_read32(kb + 4096, koff[1][0], koff[1][1]);
+      Pn[0] = probs4(0, 0, kbase);
+      fence();
+      O[2] = mfma_fp8(vf[2], P, O[2]);
+      Pn[1] = probs4(0, 1, kbase);
+      fence();
+      O[3] = mfma_fp8(vf[3], P, O[3]);
+      Pn[2] = probs4(0, 2, kbase);
+      fence();
+      lacc = mfma16_fp8(sel, P, lacc);
+      vf[0] = lds_read32(vn + 0 * 2048, voff[0], voff[1]);
+      vf[1] = lds_read32(vn + 1 * 2048, voff[0], voff[1]);
+      Pn[3] = probs4(0, 3, kbase);
+      fence();
+      const v16f s0 = mfma_fp8_scaled(kf[0][0], qf[0], NB, c_e8m0);
+      Pn[4] = probs4(1, 0, kbase);
+      fence();
+      const v16f s1 = mfma_fp8_scaled(kf[1][0], qf[0], NB, c_e8m0);
+      if (!LSE) {
+        vf[2] = lds_read32(vn + 2 * 2048, voff[0], voff[1]);
+        vf[3] = lds_read32(vn + 3 * 2048, voff[0], voff[1]);
+      }
+      Pn[5] = probs4(1, 1, kbase);
+      fence();
+      S[0] = mfma_fp8_scaled(kf[0][1], qf[1], s0, c_e8m0);
+      Pn[6] = probs4(1, 2, kbase);
+      fence();
+      Pn[7] = probs4(1, 3, kbase);
+      S[1] = mfma_fp8_scaled(kf[1][1], qf[1], s1, c_e8m0);
+    } else {
+      // head_dim 64: two score products and two P V products a tile; the
+      // vector work is the same as for 128 channels, so it sets the pace
+      v8i kf[2];
+      kf[0] = lds_read32(kb, koff[0][0], koff[0][1]);
+      kf[1] = lds_read32(kb + 32 * D, koff[0][0], koff[0][1]);
+      fence();
+      O[0] = mfma_fp8(vf[0], P, O[0]);
+      if (CAUSAL && t >= tdiag) mask_causal(t);
+      rowmax_update(std::false_type{});
+      Pn[0] = probs4(0, 0, kbase);
+      fence();
+      O[1] = mfma_fp8(vf[1], P, O[1]);
+      Pn[1] = probs4(0, 1, kbase);
+      Pn[2] = probs4(0, 2, kbase);
+      fence();
+      lacc = mfma16_fp8(sel, P, lacc);
+      vf[0] = lds_read32(vn + 0 * 2048, voff[0], voff[1]);
+      vf[1] = lds_read32(vn + 1 * 2048, voff[0], voff[1]);
+      Pn[3] = probs4(0, 3, kbase);
+      Pn[4] = probs4(1, 0, kbase);
+      fence();
+      const v16f s0 = mfma_fp8_scaled(kf[0], qf[0], NB, c_e8m0);
+      Pn[5] = probs4(1, 1, kbase);
+      fence();
+      const v16f s1 = mfma_fp8_scaled(kf[1], qf[0], NB, c_e8m0);
+      Pn[6] = probs4(1, 2, kbase);
+      Pn[7] = probs4(1, 3, kbase);
+      S[0] = s0;
+      S[1] = s1;
     }
-    Pn[5] = probs4(1, 1, kbase);
-    fence();
-    S[0] = mfma_fp8_scaled(kf[0][1], qf[1], s0, c_e8m0);
-    Pn[6] = probs4(1, 2, kbase);
-    fence();
-    Pn[7] = probs4(1, 3, kbase);
-    S[1] = mfma_fp8_scaled(kf[1][1], qf[1], s1, c_e8m0);
     P = Pn;
     keep(P);
     keep(S[0]);   // the next tile's score products stay in this iteration
@@ -556,18 +618,18 @@ __global__ __launch_bounds__(64 * kWavesWG, 8 / kWavesWG) void k_attn(AttentionA
       }
       msel[w] = sel_lane ? word : 0;
     }
-    if (LSE) {
+    if constexpr (LSE && kPre < NDB) {
       const uint8_t* vp = smem + kVRing + ((nkt - 1) % kSlots) * kTile;
       vf[2] = lds_read32(vp + 2 * 2048, voff[0], voff[1]);
       vf[3] = lds_read32(vp + 3 * 2048, voff[0], voff[1]);
     }
 #pragma unroll
-    for (int db = 0; db < 4; db++) O[db] = mfma_fp8(vf[db], P, O[db]);
+    for (int db = 0; db < NDB; db++) O[db] = mfma_fp8(vf[db], P, O[db]);
     lacc = mfma16_fp8(msel, P, lacc);
     // with every lane active: a matrix instruction moved into the stores'
     // lane-divergent branches would read inactive lanes' operands as zero
 #pragma unroll
-    for (int db = 0; db < 4; db++) keep(O[db]);
+    for (int db = 0; db < NDB; db++) keep(O[db]);
   }
 
   // epilogue: lane l holds O^T for query l%32, channels
@@ -584,9 +646,9 @@ __global__ __launch_bounds__(64 * kWavesWG, 8 / kWavesWG) void k_attn(AttentionA
     if (qrow < L) {
       const int prow = slot * kBM + 32 * wave + lq;
       const float inv = s_v / lt;
-      float* orow = a.part_o + (size_t)prow * kHeadDim;
+      float* orow = a.part_o + (size_t)prow * D;
 #pragma unroll
-      for (int db = 0; db < 4; db++)
+      for (int db = 0; db < NDB; db++)
 #pragma unroll
         for (int q4 = 0; q4 < 4; q4++)
           *reinterpret_cast<float4*>(orow + 32 * db + 8 * q4 + 4 * lg) =
@@ -598,7 +660,7 @@ __global__ __launch_bounds__(64 * kWavesWG, 8 / kWavesWG) void k_attn(AttentionA
     const float inv = s_v / lt;
     uint16_t* orow = a.out + (int64_t)(si.start + qrow) * a.os0 + (int64_t)h * a.os1;
 #pragma unroll
-    for (int db = 0; db < 4; db++)
+    for (int db = 0; db < NDB; db++)
 #pragma unroll
       for (int q4 = 0; q4 < 4; q4++) {
         const int d = 32 * db + 8 * q4 + 4 * lg;
@@ -638,9 +700,11 @@ __global__ __launch_bounds__(64 * kWavesWG, 8 / kWavesWG) void k_attn(AttentionA
 // and log2 W_i its weight (log-sum-exp combination over disjoint key ranges),
 // rounded to BF16 once; the LSE is the log-sum-exp of the pieces' LSEs.
 // 256 threads per 128 query rows (blockIdx.y picks the 128-row block of the
-// item): thread t takes row t/2, channels 64*(t%2) .. +64.  The pieces are
+// item): thread t takes row t/2, channels (D/2)*(t%2) .. +D/2.  The pieces are
 // added in index order, so the result is deterministic.
+template <int D>
 __global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
+  constexpr int HD = D / 2;   // channels per thread
   const int4 it = a.items[blockIdx.x];
   const SegInfo si = a.segs[it.x];
   const int n = split_pieces(it.w);
@@ -657,18 +721,18 @@ __global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
       w[i] = a.part_w[(slot0 + i) * kBM + r];
       m = __builtin_fmaxf(m, w[i]);
     }
-  float acc[64];
+  float acc[HD];
 #pragma unroll
-  for (int j = 0; j < 64; j++) acc[j] = 0.f;
+  for (int j = 0; j < HD; j++) acc[j] = 0.f;
   float den = 0.f;
 #pragma unroll
   for (int i = 0; i < kMaxSplit; i++)
     if (i < n) {
       const float alpha = __builtin_amdgcn_exp2f(w[i] - m);
       den += alpha;
-      const float4* src = reinterpret_cast<const float4*>(a.part_o + ((size_t)(slot0 + i) * kBM + r) * kHeadDim + 64 * half);
+      const float4* src = reinterpret_cast<const float4*>(a.part_o + ((size_t)(slot0 + i) * kBM + r) * D + HD * half);
 #pragma unroll
-      for (int j = 0; j < 16; j++) {
+      for (int j = 0; j < HD / 4; j++) {
         const float4 v = src[j];
         acc[4 * j + 0] += alpha * v.x;
         acc[4 * j + 1] += alpha * v.y;
@@ -677,9 +741,9 @@ __global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
       }
     }
   const float inv = 1.f / den;
-  uint16_t* orow = a.out + (int64_t)(si.start + qrow) * a.os0 + (int64_t)it.z * a.os1 + 64 * half;
+  uint16_t* orow = a.out + (int64_t)(si.start + qrow) * a.os0 + (int64_t)it.z * a.os1 + HD * half;
 #pragma unroll
-  for (int j = 0; j < 8; j++) {
+  for (int j = 0; j < HD / 8; j++) {
     uint32_t b[8];
 #pragma unroll
     for (int e = 0; e < 8; e++) b[e] = f32_to_bf16_rne(acc[8 * j + e] * inv);
@@ -707,23 +771,34 @@ __global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
 
 hipError_t launch_combine(const CombineArgs& a, hipStream_t stream) {
   if (a.nitems == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_combine, dim3(a.nitems, kBM / 128), dim3(256), 0, stream, a);
+  if (a.head_dim == 64)
+    hipLaunchKernelGGL(k_combine<64>, dim3(a.nitems, kBM / 128), dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL(k_combine<kHeadDim>, dim3(a.nitems, kBM / 128), dim3(256), 0, stream, a);
   return hipGetLastError();
+}
+
+template <int D>
+void launch_attention_d(const AttentionArgs& a, hipStream_t stream) {
+  const dim3 g(a.nitems), b(64 * kWavesWG);
+  if (a.causal) {
+    if (a.lse != nullptr)
+      hipLaunchKernelGGL((k_attn<true, true, D>), g, b, 0, stream, a);
+    else
+      hipLaunchKernelGGL((k_attn<false, true, D>), g, b, 0, stream, a);
+  } else if (a.lse != nullptr) {
+    hipLaunchKernelGGL((k_attn<true, false, D>), g, b, 0, stream, a);
+  } else {
+    hipLaunchKernelGGL((k_attn<false, false, D>), g, b, 0, stream, a);
+  }
 }
 
 hipError_t launch_attention(const AttentionArgs& a, hipStream_t stream) {
   if (a.nitems == 0) return hipSuccess;
-  const dim3 g(a.nitems), b(64 * kWavesWG);
-  if (a.causal) {
-    if (a.lse != nullptr)
-      hipLaunchKernelGGL((k_attn<true, true>), g, b, 0, stream, a);
-    else
-      hipLaunchKernelGGL((k_attn<false, true>), g, b, 0, stream, a);
-  } else if (a.lse != nullptr) {
-    hipLaunchKernelGGL((k_attn<true, false>), g, b, 0, stream, a);
-  } else {
-    hipLaunchKernelGGL((k_attn<false, false>), g, b, 0, stream, a);
-  }
+  if (a.head_dim == 64)
+    launch_attention_d<64>(a, stream);
+  else
+    launch_attention_d<kHeadDim>(a, stream);
   return hipGetLastError();
 }
 

@@ -90,6 +90,7 @@ struct QuantizeArgs {
   const int32_t* group_seg;  // [ngroups]: segment of each 64-row pack group, -1 = guard
   int32_t heads, nseg, nchunks, ngroups;
   int32_t seg_scales;        // 1: one scale per (tensor, segment, head)
+  int32_t head_dim;          // D: 128, or 64 (E4M3 plans)
   int64_t rows;
   float softmax_scale;       // fixes Q's scale (see k_finalize)
   // FP4 plans
@@ -120,6 +121,7 @@ struct AttentionArgs {
   int32_t nitems;
   int32_t nscale;            // S: scale sets (segments with per-segment scales, else 1)
   int32_t causal;            // 1: query i of a segment attends keys j <= i only
+  int32_t head_dim;          // D: 128 or 64
   float softmax_scale;
 };
 
@@ -134,6 +136,7 @@ struct CombineArgs {
   int64_t os0, os1;
   float* lse;                // nullable, [H][T]
   int64_t tokens;
+  int32_t head_dim;          // D: 128 or 64
 };
 
 // FP4 attention: codes and block scales as in WorkspaceLayout.

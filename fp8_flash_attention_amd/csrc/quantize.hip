@@ -39,16 +39,20 @@ __device__ __forceinline__ uint32_t cvt4(float a, float b, float c, float d) {
 }
 
 // ---------------------------------------------------------------------------
-// Pass 1: statistics.  grid = (nchunks, ceil(H/16), 3), block = 256.
-// Thread t handles head 16*blockIdx.y + t/16 and channels 8*(t%16) .. +8 over
-// the chunk's tokens in ascending order.
+// Pass 1: statistics.  D channels per head row; grid = (nchunks, ceil(H/HPB), 3),
+// block = 256.  Thread t handles head HPB*blockIdx.y + t/TPH and channels
+// 8*(t%TPH) .. +8 over the chunk's tokens in ascending order (TPH = D/8
+// threads per head row, HPB = 256/TPH heads per block).
 // ---------------------------------------------------------------------------
+template <int D>
 __global__ __launch_bounds__(256) void k_stats(QuantizeArgs a) {
+  constexpr int TPH = D / 8;
+  constexpr int HPB = 256 / TPH;
   const int c = blockIdx.x;
   const int tensor = a.mx ? 1 : blockIdx.z;   // FP4 plans need only K's statistics
   const int t = threadIdx.x;
-  const int h = blockIdx.y * 16 + t / 16;
-  const int c0 = (t % 16) * 8;
+  const int h = blockIdx.y * HPB + t / TPH;
+  const int c0 = (t % TPH) * 8;
   const bool active = h < a.heads;
   const Chunk ch = a.chunks[c];
   const uint16_t* base = a.x[tensor] + (int64_t)h * a.hs[tensor] + c0;
@@ -72,7 +76,7 @@ __global__ __launch_bounds__(256) void k_stats(QuantizeArgs a) {
         mx[i] = fmaxf(mx[i], f[i]);
       }
     }
-    KStat* out = a.kstat + ((int64_t)c * a.heads + h) * kHeadDim + c0;
+    KStat* out = a.kstat + ((int64_t)c * a.heads + h) * D + c0;
 #pragma unroll
     for (int i = 0; i < 8; i++) out[i] = KStat{sum[i], mn[i], mx[i]};
     return;
@@ -89,17 +93,17 @@ __global__ __launch_bounds__(256) void k_stats(QuantizeArgs a) {
       for (int i = 0; i < 8; i++) m = fmaxf(m, fabsf(f[i]));
     }
   }
-  // reduce over the 16 lanes that share a head (they are consecutive lanes of one wave)
+  // reduce over the TPH lanes that share a head (consecutive lanes of one wave)
 #pragma unroll
-  for (int off = 8; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 16));
-  if (active && (t % 16) == 0) {
+  for (int off = TPH / 2; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, TPH));
+  if (active && (t % TPH) == 0) {
     const int slot = tensor == 0 ? 0 : 1;
     a.amax[((int64_t)slot * a.nchunks + c) * a.heads + h] = m;
   }
 }
 
 // ---------------------------------------------------------------------------
-// Pass 1b: finalize.  grid = H, block = 128 (thread = channel d).
+// Pass 1b: finalize.  grid = H, block = D (thread = channel d).
 // mu[s][h][d] = fl32(sum64 / L) with chunk sums added in ascending order from
 // +0.0; K amax = max over segments and channels of |fl32(max - mu)| and
 // |fl32(min - mu)|, which equals max |fl32(x - mu)| over the tokens because
@@ -107,9 +111,11 @@ __global__ __launch_bounds__(256) void k_stats(QuantizeArgs a) {
 // V; Q's scale is rounded up from that (q_scale_of).  With per-segment
 // scales the same is done for every segment over its own chunks only.
 // ---------------------------------------------------------------------------
-__device__ float block_max128(float v, float* red) {
+template <int D>
+__device__ float block_max(float v, float* red) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
+  if constexpr (D == 64) return v;   // one wave
   const int w = threadIdx.x / 64;
   __syncthreads();
   if ((threadIdx.x % 64) == 0) red[w] = v;
@@ -137,7 +143,8 @@ __device__ __forceinline__ float q_scale_of(float qa, float s_k, float softmax_s
   return ldexpf(1.0f, m) / f;
 }
 
-__global__ __launch_bounds__(128) void k_finalize(QuantizeArgs a) {
+template <int D>
+__global__ __launch_bounds__(D) void k_finalize(QuantizeArgs a) {
   __shared__ float red[2];
   const int h = blockIdx.x;
   const int d = threadIdx.x;
@@ -151,15 +158,15 @@ __global__ __launch_bounds__(128) void k_finalize(QuantizeArgs a) {
       if (si.len > 0) {
         double sum = 0.0;
 #pragma unroll 8
-        for (int c = si.chunk0; c < si.chunk0 + nch; c++) sum = sum + a.kstat[((int64_t)c * a.heads + h) * kHeadDim + d].sum;
+        for (int c = si.chunk0; c < si.chunk0 + nch; c++) sum = sum + a.kstat[((int64_t)c * a.heads + h) * D + d].sum;
         mu = (float)(sum / (double)si.len);
       }
-      a.mu[((int64_t)s * a.heads + h) * kHeadDim + d] = mu;
+      a.mu[((int64_t)s * a.heads + h) * D + d] = mu;
     }
     return;
   }
   if (!a.seg_scales) {
-    for (int c = d; c < a.nchunks; c += 128) {
+    for (int c = d; c < a.nchunks; c += D) {
       qa = fmaxf(qa, a.amax[(int64_t)c * a.heads + h]);
       va = fmaxf(va, a.amax[((int64_t)a.nchunks + c) * a.heads + h]);
     }
@@ -174,7 +181,7 @@ __global__ __launch_bounds__(128) void k_finalize(QuantizeArgs a) {
       float mn = __builtin_inff(), mx = -__builtin_inff();
 #pragma unroll 8
       for (int c = si.chunk0; c < si.chunk0 + nch; c++) {   // loads issued ahead, sums in chunk order
-        const KStat st = a.kstat[((int64_t)c * a.heads + h) * kHeadDim + d];
+        const KStat st = a.kstat[((int64_t)c * a.heads + h) * D + d];
         sum = sum + st.sum;
         mn = fminf(mn, st.mn);
         mx = fmaxf(mx, st.mx);
@@ -182,18 +189,18 @@ __global__ __launch_bounds__(128) void k_finalize(QuantizeArgs a) {
       mu = (float)(sum / (double)si.len);
       kas = fmaxf(fabsf(mx - mu), fabsf(mn - mu));
     }
-    a.mu[((int64_t)s * a.heads + h) * kHeadDim + d] = mu;
+    a.mu[((int64_t)s * a.heads + h) * D + d] = mu;
     if (a.seg_scales) {
       // this segment's own amax of Q, K and V (its chunks' partials), so its
       // scales do not depend on the other segments
       float qs = 0.f, vs = 0.f;
-      for (int c = si.chunk0 + d; c < si.chunk0 + nch; c += 128) {
+      for (int c = si.chunk0 + d; c < si.chunk0 + nch; c += D) {
         qs = fmaxf(qs, a.amax[(int64_t)c * a.heads + h]);
         vs = fmaxf(vs, a.amax[((int64_t)a.nchunks + c) * a.heads + h]);
       }
-      qs = block_max128(qs, red);
-      vs = block_max128(vs, red);
-      const float ks = block_max128(kas, red);
+      qs = block_max<D>(qs, red);
+      vs = block_max<D>(vs, red);
+      const float ks = block_max<D>(kas, red);
       if (d == 0) {
         const int64_t o = (int64_t)s * a.heads + h;      // scales [3][nseg][H]
         const int64_t n = (int64_t)a.nseg * a.heads;
@@ -206,9 +213,9 @@ __global__ __launch_bounds__(128) void k_finalize(QuantizeArgs a) {
     }
   }
   if (!a.seg_scales) {
-    qa = block_max128(qa, red);
-    va = block_max128(va, red);
-    ka = block_max128(ka, red);
+    qa = block_max<D>(qa, red);
+    va = block_max<D>(va, red);
+    ka = block_max<D>(ka, red);
     if (d == 0) {
       a.scales[h] = q_scale_of(qa, scale_of(ka), a.softmax_scale);
       a.scales[a.heads + h] = scale_of(ka);
@@ -228,8 +235,11 @@ __global__ __launch_bounds__(128) void k_finalize(QuantizeArgs a) {
 // probability registers line up with the V operand: byte p = 32j + 16b + 4r + i
 // of a group holds key 32b + 8r + 4j + i.
 // ---------------------------------------------------------------------------
+template <int D>
 __global__ __launch_bounds__(256) void k_pack(QuantizeArgs a) {
-  __shared__ uint8_t tile[kPackRows][kHeadDim + 16];
+  constexpr int TPH = D / 8;        // threads per row, 8 channels each
+  constexpr int RPP = 256 / TPH;    // rows per pass
+  __shared__ uint8_t tile[kPackRows][D + 16];
   const int g = blockIdx.x;
   const int h = blockIdx.y;
   const int tensor = blockIdx.z;
@@ -241,12 +251,12 @@ __global__ __launch_bounds__(256) void k_pack(QuantizeArgs a) {
   const int nset = a.seg_scales ? a.nseg : 1;       // scales [3][nset][H]
   const int sset = a.seg_scales && seg >= 0 ? seg : 0;
   const float s = a.scales[((int64_t)tensor * nset + sset) * a.heads + h];
-  const int c0 = (t % 16) * 8;
+  const int c0 = (t % TPH) * 8;
   const uint16_t* base = a.x[tensor] + (int64_t)h * a.hs[tensor] + c0;
   const int64_t ts = a.ts[tensor];
   float mu[8];
   if (tensor == 1 && seg >= 0) {
-    const float* m = a.mu + ((int64_t)seg * a.heads + h) * kHeadDim + c0;
+    const float* m = a.mu + ((int64_t)seg * a.heads + h) * D + c0;
 #pragma unroll
     for (int i = 0; i < 8; i++) mu[i] = m[i];
   } else {
@@ -255,8 +265,8 @@ __global__ __launch_bounds__(256) void k_pack(QuantizeArgs a) {
   }
 
 #pragma unroll
-  for (int pass = 0; pass < kPackRows / 16; pass++) {
-    const int i = pass * 16 + t / 16;                // row within the group
+  for (int pass = 0; pass < kPackRows / RPP; pass++) {
+    const int i = pass * RPP + t / TPH;              // row within the group
     const int rel = (int)(R - (seg >= 0 ? si.row0 : 0)) + i;  // segment-relative row
     uint2 code = make_uint2(0u, 0u);
     if (seg >= 0 && rel < si.len) {
@@ -270,7 +280,7 @@ __global__ __launch_bounds__(256) void k_pack(QuantizeArgs a) {
       code.y = cvt4(y[4], y[5], y[6], y[7]);
     }
     if (tensor < 2) {
-      uint8_t* dst = a.codes[tensor] + ((int64_t)h * a.rows + R + i) * kHeadDim + c0;
+      uint8_t* dst = a.codes[tensor] + ((int64_t)h * a.rows + R + i) * D + c0;
       *reinterpret_cast<uint2*>(dst) = code;
     } else {
       *reinterpret_cast<uint2*>(&tile[i][c0]) = code;
@@ -279,6 +289,7 @@ __global__ __launch_bounds__(256) void k_pack(QuantizeArgs a) {
   if (tensor < 2) return;
   __syncthreads();
   // transposed, permuted write: thread t -> channel d = t/2, bytes p in [32*(t%2), +32)
+  if (t >= 2 * D) return;
   const int d = t / 2;
   const int j = t % 2;
   uint32_t w[8];
@@ -294,7 +305,7 @@ __global__ __launch_bounds__(256) void k_pack(QuantizeArgs a) {
     }
     w[q] = acc;
   }
-  uint8_t* dst = a.codes[2] + ((int64_t)h * kHeadDim + d) * a.rows + R + 32 * j;
+  uint8_t* dst = a.codes[2] + ((int64_t)h * D + d) * a.rows + R + 32 * j;
   *reinterpret_cast<uint4*>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
   *reinterpret_cast<uint4*>(dst + 16) = make_uint4(w[4], w[5], w[6], w[7]);
 }
@@ -492,20 +503,27 @@ __global__ __launch_bounds__(256) void k_pack_mx(QuantizeArgs a) {
 
 }  // namespace
 
-hipError_t launch_quantize(const QuantizeArgs& a, hipStream_t stream) {
+template <int D>
+hipError_t launch_quantize_d(const QuantizeArgs& a, hipStream_t stream) {
+  constexpr int HPB = 256 / (D / 8);   // heads per stats block
   if (a.nchunks > 0) {
-    hipLaunchKernelGGL(k_stats, dim3(a.nchunks, (a.heads + 15) / 16, a.mx ? 1 : 3), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(k_stats<D>, dim3(a.nchunks, (a.heads + HPB - 1) / HPB, a.mx ? 1 : 3), dim3(256), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(k_finalize, dim3(a.heads), dim3(128), 0, stream, a);
+  hipLaunchKernelGGL(k_finalize<D>, dim3(a.heads), dim3(D), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (a.mx)
     hipLaunchKernelGGL(k_pack_mx, dim3(a.ngroups, a.heads, 3), dim3(256), 0, stream, a);
   else
-    hipLaunchKernelGGL(k_pack, dim3(a.ngroups, a.heads, 3), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(k_pack<D>, dim3(a.ngroups, a.heads, 3), dim3(256), 0, stream, a);
   return hipGetLastError();
+}
+
+hipError_t launch_quantize(const QuantizeArgs& a, hipStream_t stream) {
+  if (a.head_dim == 64) return launch_quantize_d<64>(a, stream);
+  return launch_quantize_d<kHeadDim>(a, stream);
 }
 
 }  // namespace fp8attn

@@ -56,7 +56,8 @@ typedef enum {
   FP8ATTN_EHIP = 5           /* a HIP runtime call or kernel launch failed */
 } fp8attn_status;
 
-/* Workspace regions, for fp8attn_workspace_region(). */
+/* Workspace regions, for fp8attn_workspace_region().  D = 128, or 64 for
+   FP8ATTN_PLAN_HEAD_DIM_64 plans (written 128 below). */
 typedef enum {
   FP8ATTN_REGION_Q_CODES = 0, /* uint8 [H][rows][128]                                  */
   FP8ATTN_REGION_K_CODES = 1, /* uint8 [H][rows][128] (centred K)                       */
@@ -110,6 +111,7 @@ fp8attn_status fp8attn_plan(fp8attn_plan_t* plan_out, int64_t tokens, int32_t he
 #define FP8ATTN_PLAN_MXFP4 2u
 #define FP8ATTN_PLAN_Q_CENTRE 4u
 #define FP8ATTN_PLAN_CAUSAL 8u
+#define FP8ATTN_PLAN_HEAD_DIM_64 16u
 
 /*
  * fp8attn_plan_ex - fp8attn_plan with flags (fp8attn_plan is flags == 0).
@@ -150,9 +152,14 @@ fp8attn_status fp8attn_plan(fp8attn_plan_t* plan_out, int64_t tokens, int32_t he
  *   its last query; the tiles from its first query on are masked per element.
  *   The LSE (if requested) is over the visible keys.  Causal plans never split
  *   work items.
+ * FP8ATTN_PLAN_HEAD_DIM_64 (E4M3 plans): q, k, v and out have 64 channels
+ *   per head instead of FP8ATTN_HEAD_DIM (P1 lists other head sizes among the
+ *   cases it sends elsewhere): every region, stride and scale rule below
+ *   holds with 64 in place of 128.  Combines with the other E4M3 flags.
  * Unknown flag bits, FP8ATTN_PLAN_Q_CENTRE without FP8ATTN_PLAN_MXFP4,
  * FP8ATTN_PLAN_MXFP4 with FP8ATTN_PLAN_SEGMENT_SCALES (its scales are already
- * local to 32 elements) or with FP8ATTN_PLAN_CAUSAL: FP8ATTN_EINVAL.
+ * local to 32 elements), with FP8ATTN_PLAN_CAUSAL or with
+ * FP8ATTN_PLAN_HEAD_DIM_64: FP8ATTN_EINVAL.
  */
 fp8attn_status fp8attn_plan_ex(fp8attn_plan_t* plan_out, int64_t tokens, int32_t heads,
                                const int32_t* cu_seqlens_host, int32_t num_segments,
@@ -242,12 +249,13 @@ fp8attn_status fp8attn_workspace_region(fp8attn_plan_t plan, const void* workspa
 
 /*
  * fp8attn_plan_info - schedule facts (for tests and tools).
- *   info_out int64[13]: {tokens, heads, num_segments, workspace_rows,
+ *   info_out int64[14]: {tokens, heads, num_segments, workspace_rows,
  *                        work_items, stat_chunks, query_tile, key_tile,
  *                        segment_scales (0 or 1), partial_slots,
- *                        mxfp4 (0 or 1), q_centre (0 or 1), causal (0 or 1)}
+ *                        mxfp4 (0 or 1), q_centre (0 or 1), causal (0 or 1),
+ *                        head_dim (128 or 64)}
  */
-fp8attn_status fp8attn_plan_info(fp8attn_plan_t plan, int64_t info_out[13]);
+fp8attn_status fp8attn_plan_info(fp8attn_plan_t plan, int64_t info_out[14]);
 
 /*
  * fp8attn_plan_work_items - copy the ordered work list to host memory.

@@ -228,7 +228,7 @@ def test_plan_ex_flags_and_segment_scale_layout():
     L = _lib.lib()
     cu = (ctypes.c_int32 * 4)(0, 100, 100, 300)
     h = ctypes.c_void_p()
-    assert L.fp8attn_plan_ex(ctypes.byref(h), 300, 2, cu, 3, ctypes.c_float(0.088), -1, 16) == _lib.EINVAL
+    assert L.fp8attn_plan_ex(ctypes.byref(h), 300, 2, cu, 3, ctypes.c_float(0.088), -1, 32) == _lib.EINVAL
     assert "flags" in L.fp8attn_last_error().decode()
     base = fa.Plan(300, 2, [0, 100, 100, 300], device=-1)
     seg = fa.Plan(300, 2, [0, 100, 100, 300], device=-1, segment_scales=True)
@@ -376,3 +376,25 @@ def test_causal_parts_balanced_and_local():
         assert len({it[2] for it in first_round}) <= 4          # heads in flight on the XCD
         assert tiles(first_round[0]) == max(tiles(it) for it in part[:len(first_round)])
     assert max(work) - min(work) <= (T + 63) // 64
+
+
+def test_head_dim_64_plan_layout():
+    L = _lib.lib()
+    h = ctypes.c_void_p()
+    arr = (ctypes.c_int32 * 3)(0, 100, 300)
+    assert L.fp8attn_plan_ex(ctypes.byref(h), 300, 2, arr, 2, ctypes.c_float(0.125), -1,
+                             _lib.PLAN_HEAD_DIM_64 | _lib.PLAN_MXFP4) == _lib.EINVAL
+    p = fa.Plan(300, 2, [0, 100, 300], device=-1, head_dim=64)
+    p128 = fa.Plan(300, 2, [0, 100, 300], device=-1)
+    assert p.info()["head_dim"] == 64 and p128.info()["head_dim"] == 128
+    assert p.softmax_scale == pytest.approx(0.125)
+    rows = p.info()["workspace_rows"]
+    ptr = ctypes.c_void_p()
+    dims = (ctypes.c_int64 * 3)()
+    for which, shape in ((_lib.REGION_Q, (2, rows, 64)), (_lib.REGION_V, (2, 64, rows)), (_lib.REGION_MU, (2, 2, 64))):
+        assert L.fp8attn_workspace_region(p.handle, ctypes.c_void_p(1 << 20), which, ctypes.byref(ptr), dims) == 0
+        assert tuple(dims) == shape
+    assert p.workspace_bytes < p128.workspace_bytes
+    assert p.work_items() == p128.work_items()
+    with pytest.raises(ValueError):
+        fa.Plan(300, 2, [0, 300], device=-1, head_dim=96)

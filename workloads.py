@@ -24,7 +24,7 @@ rounding.
 from __future__ import annotations
 
 import math
-from dataclasses import dataclass, field
+from dataclasses import dataclass
 from typing import List, Optional
 
 import torch
@@ -45,7 +45,12 @@ class Workload:
     #          (token stride 3*H*128 elements, head stride 128).
     layout: str = "thd"
     note: str = ""
-    softmax_scale: float = field(default=1.0 / math.sqrt(HEAD_DIM))
+    head_dim: int = HEAD_DIM
+    softmax_scale: float = -1.0          # -1: 1/sqrt(head_dim)
+
+    def __post_init__(self):
+        if self.softmax_scale < 0:
+            self.softmax_scale = 1.0 / math.sqrt(self.head_dim)
 
     @property
     def segments(self) -> List[int]:
@@ -55,7 +60,7 @@ class Workload:
     @property
     def flops(self) -> float:
         """4 * sum(L^2) * H * D: two L x L x D contractions of 2 flops per term."""
-        return 4.0 * sum(L * L for L in self.segments) * self.heads * HEAD_DIM
+        return 4.0 * sum(L * L for L in self.segments) * self.heads * self.head_dim
 
 
 def _single(T: int) -> List[int]:
@@ -84,12 +89,17 @@ WORKLOADS = {
     "s30272_h7_shard": Workload(
         "s30272_h7_shard", 30272, 7, _single(30272), 1006, k_offset_var=2.0,
         note="S=30272 with 7 heads: one eighth of the denoise-step heads, K offset as above"),
+    # head_dim 64 (not one of the graded configurations): the denoise-step
+    # length with 56 heads of 64 channels
+    "s30272_h56_d64": Workload(
+        "s30272_h56_d64", 30272, 56, _single(30272), 1007, k_offset_var=2.0, head_dim=64,
+        note="S=30272, 56 heads of 64 channels, K offset as above"),
 }
 
 
 def make_workload(name: str, tokens: int, heads: int, cu_seqlens: List[int], seed: int,
-                  k_offset_var: Optional[float] = None, layout: str = "thd") -> Workload:
-    return Workload(name, tokens, heads, list(cu_seqlens), seed, k_offset_var, layout)
+                  k_offset_var: Optional[float] = None, layout: str = "thd", head_dim: int = HEAD_DIM) -> Workload:
+    return Workload(name, tokens, heads, list(cu_seqlens), seed, k_offset_var, layout, head_dim=head_dim)
 
 
 def generate(w: Workload, device: str = "cpu"):
@@ -100,12 +110,12 @@ def generate(w: Workload, device: str = "cpu"):
     """
     g = torch.Generator(device="cpu")
     g.manual_seed(w.seed)
-    shape = (w.tokens, w.heads, HEAD_DIM)
+    shape = (w.tokens, w.heads, w.head_dim)
     q = torch.randn(shape, generator=g, dtype=torch.float32)
     k = torch.randn(shape, generator=g, dtype=torch.float32)
     v = torch.randn(shape, generator=g, dtype=torch.float32)
     if w.k_offset_var is not None:
-        off = math.sqrt(w.k_offset_var) * torch.randn((w.heads, HEAD_DIM), generator=g,
+        off = math.sqrt(w.k_offset_var) * torch.randn((w.heads, w.head_dim), generator=g,
                                                       dtype=torch.float32)
         k = k + off.unsqueeze(0)
     q, k, v = (t.to(torch.bfloat16) for t in (q, k, v))
