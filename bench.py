@@ -116,7 +116,7 @@ def main() -> int:
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); the path shards by "
+        print(f"bench.py: runs on one GPU only (asked for --gpus {args.gpus}); the path shards by "
               "heads across GPUs with no exchange inside attention, but no multi-GPU launch is implemented.",
               file=sys.stderr)
         return 2
