@@ -33,6 +33,8 @@ struct fp8attn_plan_s {
   int32_t q_centre = 0;           // FP8ATTN_PLAN_Q_CENTRE
   int32_t causal = 0;             // FP8ATTN_PLAN_CAUSAL
   int32_t head_dim = kHeadDim;    // 64 with FP8ATTN_PLAN_HEAD_DIM_64
+  int32_t bm = kBM;               // queries per work item (kMxBM for FP4 plans)
+  int32_t wg_per_cu = kWgPerCu;   // attention workgroups resident per CU
   float scale = 0.f;
   int device = -1;
   std::vector<int32_t> cu;
@@ -120,8 +122,8 @@ WorkspaceLayout make_layout(int64_t rows, int heads, int nseg, int nscale, int n
 // through that XCD's L2.
 //
 // Each part is ordered longest item first (stable, so head order is kept).
-// An XCD runs kWgPerCu workgroups on each of its cus = CUs / kNumXcd compute
-// units.  When the part's item count leaves R <= cus / 2 items for a last
+// An XCD runs p->wg_per_cu workgroups on each of its cus = CUs / kNumXcd
+// compute units (one 256-query E4M3 workgroup, or two 128-query FP4 ones).  When the part's item count leaves R <= cus / 2 items for a last
 // round, those run nearly alone; they are split along the keys into n pieces
 // (n <= kMaxSplit, n * R <= cus, at least kMinPieceTiles key tiles a piece),
 // which go last.  A piece writes an unnormalized-frame partial (output, log2 weight,
@@ -130,7 +132,8 @@ WorkspaceLayout make_layout(int64_t rows, int heads, int nseg, int nscale, int n
 // attention (sglang PR "[DSA] Enable tilelang fp8_e4m3 KV cache ...", note that
 // the FP8 path must return the LSE for cross-rank reduction).
 void build_items(fp8attn_plan_s* p, int cus, bool allow_split) {
-  const int slots = kWgPerCu * cus;
+  const int bm = p->bm;
+  const int slots = p->wg_per_cu * cus;
   std::vector<int> order(p->nseg);
   for (int s = 0; s < p->nseg; s++) order[s] = s;
   std::stable_sort(order.begin(), order.end(),
@@ -138,15 +141,15 @@ void build_items(fp8attn_plan_s* p, int cus, bool allow_split) {
   // key tiles an item attends to (causal: up to its last query)
   auto tiles = [&](const int4& it) {
     const int L = p->segs[it.x].len;
-    return ((p->causal ? std::min(L, it.y + kBM) : L) + kBN - 1) / kBN;
+    return ((p->causal ? std::min(L, it.y + bm) : L) + kBN - 1) / kBN;
   };
   std::vector<int4> list;
   for (int h = 0; h < p->heads; h++)
     for (int s : order) {
       const int L = p->segs[s].len;
-      const int n = (L + kBM - 1) / kBM;
+      const int n = (L + bm - 1) / bm;
       // causal items get shorter with q0: longest (last query tile) first
-      for (int i = 0; i < n; i++) list.push_back(int4{s, kBM * (p->causal ? n - 1 - i : i), h, 0});
+      for (int i = 0; i < n; i++) list.push_back(int4{s, bm * (p->causal ? n - 1 - i : i), h, 0});
     }
   if (p->causal) {
     // Causal items differ in length.  The head-major list is cut into kNumXcd
@@ -169,7 +172,7 @@ void build_items(fp8attn_plan_s* p, int cus, bool allow_split) {
       parts[x].push_back(it);
       acc += tiles(it);
     }
-    const int64_t window = (int64_t)kCausalRounds * kWgPerCu * cus * maxt;
+    const int64_t window = (int64_t)kCausalRounds * p->wg_per_cu * cus * maxt;
     for (auto& part : parts) {
       size_t b = 0;
       while (b < part.size()) {
@@ -304,6 +307,10 @@ fp8attn_status fp8attn_plan_ex(fp8attn_plan_t* plan_out, int64_t tokens, int32_t
   p->q_centre = (flags & FP8ATTN_PLAN_Q_CENTRE) ? 1 : 0;
   p->causal = (flags & FP8ATTN_PLAN_CAUSAL) ? 1 : 0;
   p->head_dim = (flags & FP8ATTN_PLAN_HEAD_DIM_64) ? 64 : kHeadDim;
+  if (p->mx) {
+    p->bm = kMxBM;
+    p->wg_per_cu = kMxWgPerCu;
+  }
   p->cu.assign(cu, cu + num_segments + 1);
   int64_t row = 0;
   int32_t chunk = 0;
@@ -585,7 +592,7 @@ fp8attn_status fp8attn_plan_info(fp8attn_plan_t p, int64_t info[14]) {
   info[3] = p->ws.rows;
   info[4] = p->real_items;
   info[5] = (int64_t)p->chunks.size();
-  info[6] = kBM;
+  info[6] = p->bm;
   info[7] = kBN;
   info[8] = p->seg_scales;
   info[9] = p->npieces;

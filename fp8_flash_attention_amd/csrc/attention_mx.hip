@@ -10,8 +10,12 @@
 // BF16 once.
 //
 // gfx950 mapping (shared with the E4M3 kernel where it carries over)
-//   * One workgroup = 8 waves of 32 queries (256 queries of one segment and
-//     head), one per CU; key tiles of 64.  Scores are computed transposed,
+//   * One workgroup = 4 waves of 32 queries (128 queries of one segment and
+//     head), two per CU; key tiles of 64.  Each SIMD then runs one wave of
+//     each workgroup, so a wave waiting at its workgroup's barrier leaves the
+//     SIMD to a wave that is not (8.7% faster than one 8-wave workgroup per
+//     CU, whose two waves per SIMD share every barrier; the halved tile bytes
+//     of FP4 keep the doubled L2-to-LDS traffic cheap).  Scores are computed transposed,
 //     S^T = K Q^T, on v_mfma_scale_f32_32x32x64_f8f6f4 with both operands
 //     E2M1 (cbsz = blgp = 4; 32 clocks a product, half the E4M3 time).  Q and
 //     the block-mean operand stay in registers; K comes from LDS.
@@ -36,7 +40,8 @@
 //   * Row sums: v_mfma_scale_f32_16x16x128_f8f6f4 of the packed P with a 0/1
 //     selector, P's per-lane scale as the B scale.
 //   * K and V^T tiles (4 KB of codes + 256 B of scales each) reach LDS by direct
-//     buffer loads into four-slot rings; barriers every second iteration; the
+//     buffer loads into four-slot rings (34 KB a workgroup); barriers every
+//     second iteration; the
 //     last tile's scores past the segment end are masked to -inf before its
 //     maximum, so padding never moves a probability scale.
 #include "internal.h"
@@ -54,10 +59,10 @@ constexpr float kRefMax = 24.f;                  // move the reference once a sc
 constexpr int kSlot = kMxTile + kMxTileScales;  // bytes of one ring slot (codes, then scales)
 constexpr int kSlots = 4;
 constexpr int kBarEvery = kSlots / 2;
-constexpr int kWaves = 8;
+constexpr int kWaves = kMxBM / 32;            // 4 waves of 32 queries
 constexpr int kVRing = kSlots * kSlot;
 constexpr int kBufferFlags = 0x00020000;
-static_assert(kBM == 256 && kBN == 64, "8 waves x 32 queries, 64-key tiles");
+static_assert(kMxBM == 128 && kBN == 64, "4 waves x 32 queries, 64-key tiles");
 
 __device__ __forceinline__ v8i widen(const v4i& a) { return __builtin_shufflevector(a, a, 0, 1, 2, 3, -1, -1, -1, -1); }
 
@@ -129,7 +134,7 @@ __device__ __forceinline__ void tail_iters(F& iter, int& t, int nlast) {
 }
 
 template <bool QC>
-__global__ __launch_bounds__(64 * kWaves, 1) void k_attn_mx(MxAttentionArgs a) {
+__global__ __launch_bounds__(64 * kWaves, 2) void k_attn_mx(MxAttentionArgs a) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * kVRing];
 
   const int4 it = a.items[blockIdx.x];
@@ -158,7 +163,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_attn_mx(MxAttentionArgs a) {
   v4i mf[2];
   int msc = 0;
   if (QC) {
-    const int64_t blk = (int64_t)h * (a.rows / kMxQBlock) + (si.row0 + q0) / kMxQBlock + wave / 4;
+    const int64_t blk = (int64_t)h * (a.rows / kMxQBlock) + (si.row0 + q0) / kMxQBlock;
 #pragma unroll
     for (int kk = 0; kk < 2; kk++) mf[kk] = *reinterpret_cast<const v4i*>(a.qm_codes + blk * kMxRow + 32 * kk + 16 * lg);
     msc = *reinterpret_cast<const uint16_t*>(a.qm_scales + blk * 4 + 2 * lg);
@@ -178,32 +183,38 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_attn_mx(MxAttentionArgs a) {
   for (int db = 0; db < 4; db++) voff[db] = v_lds_off(32 * db + lq, lg);
   const int vso = kMxTile + (32 * lg + lq) * 4;   // V^T scale bytes of channels lq + 32*db
 
-  // Direct loads: waves 0-3 load 1 KB each of a K tile's codes, waves 4-7 of a
-  // V^T tile's; waves 0 and 4 also the tile's 256 scale bytes.  The 16-byte
-  // LDS chunk p = 64*(wave%4) + lane receives the global chunk the swizzle
-  // places there.
-  const bool is_k = wave < 4;
-  const int p = 64 * (wave & 3) + lane;
-  int src;
-  if (is_k) {
+  // Direct loads: every wave loads 1 KB of each K tile's codes and 1 KB of
+  // each V^T tile's (the 16-byte LDS chunk p = 64*wave + lane receives the
+  // global chunk the swizzle places there); wave 0 also loads the K tile's 256
+  // scale bytes, wave 1 the V^T tile's.  Tile indices past the last tile are
+  // clamped (a free slot refilled with valid data).
+  const int p = 64 * wave + lane;
+  int srck, srcv;
+  {
     const int r = p >> 2;
-    src = r * kMxRow + (((p & 3) ^ k_swz(r)) << 4);
-  } else {
+    srck = r * kMxRow + (((p & 3) ^ k_swz(r)) << 4);
     const int d = p >> 1;
-    src = d * (kBN / 2) + (((p & 1) ^ ((d >> 3) & 1)) << 4);
+    srcv = d * (kBN / 2) + (((p & 1) ^ ((d >> 3) & 1)) << 4);
   }
-  const bool loads_scales = (wave & 3) == 0;
-  const uint8_t* cbase = is_k ? a.k_codes + hrow * kMxRow : a.v_codes + htile * kMxTile;
-  const uint8_t* sbase = is_k ? a.k_scales + hrow * 4 : a.v_scales + htile * kMxTileScales;
-  const __amdgpu_buffer_rsrc_t crs = __builtin_amdgcn_make_buffer_rsrc((void*)cbase, (short)0, nkt * kMxTile, kBufferFlags);
-  const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc((void*)sbase, (short)0, nkt * kMxTileScales, kBufferFlags);
-  const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)smem + (is_k ? 0 : kVRing);
-  // Tile indices past the last tile are clamped (a free slot refilled with valid data).
-  auto load = [&](int kt, int slot) __attribute__((always_inline)) {
+  const uint8_t* kcb = a.k_codes + hrow * kMxRow;
+  const uint8_t* vcb = a.v_codes + htile * kMxTile;
+  const uint8_t* ksb = a.k_scales + hrow * 4;
+  const uint8_t* vsb = a.v_scales + htile * kMxTileScales;
+  const __amdgpu_buffer_rsrc_t kcrs = __builtin_amdgcn_make_buffer_rsrc((void*)kcb, (short)0, nkt * kMxTile, kBufferFlags);
+  const __amdgpu_buffer_rsrc_t vcrs = __builtin_amdgcn_make_buffer_rsrc((void*)vcb, (short)0, nkt * kMxTile, kBufferFlags);
+  const __amdgpu_buffer_rsrc_t ksrs = __builtin_amdgcn_make_buffer_rsrc((void*)ksb, (short)0, nkt * kMxTileScales, kBufferFlags);
+  const __amdgpu_buffer_rsrc_t vsrs = __builtin_amdgcn_make_buffer_rsrc((void*)vsb, (short)0, nkt * kMxTileScales, kBufferFlags);
+  const uint32_t lds_k = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)smem;
+  const uint32_t lds_v = lds_k + kVRing;
+  auto load_k = [&](int kt, int slot) __attribute__((always_inline)) {
     kt = kt < nkt ? kt : nkt - 1;
-    const uint32_t dst = lds_base + slot * kSlot;
-    lds_dma16(crs, dst + 1024 * (wave & 3), src, kt * kMxTile);
-    if (loads_scales) lds_dma4(srs, dst + kMxTile, 4 * lane, kt * kMxTileScales);
+    lds_dma16(kcrs, lds_k + slot * kSlot + 1024 * wave, srck, kt * kMxTile);
+    if (wave == 0) lds_dma4(ksrs, lds_k + slot * kSlot + kMxTile, 4 * lane, kt * kMxTileScales);
+  };
+  auto load_v = [&](int kt, int slot) __attribute__((always_inline)) {
+    kt = kt < nkt ? kt : nkt - 1;
+    lds_dma16(vcrs, lds_v + slot * kSlot + 1024 * wave, srcv, kt * kMxTile);
+    if (wave == 1) lds_dma4(vsrs, lds_v + slot * kSlot + kMxTile, 4 * lane, kt * kMxTileScales);
   };
 
   // Row-sum selector: E2M1 1.0 (code 2) in every nibble of lanes 0 and 32 (row
@@ -321,17 +332,15 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_attn_mx(MxAttentionArgs a) {
         if (32 * lg + 16 * kb + r >= klim) S[kb][r] = -__builtin_huge_valf();
   };
 
-  // Prologue: K(0), K(1), K(2), V(0), V(1); wait for K(0) (waves 0-3 issued
-  // the K loads: two per tile for wave 0, one for waves 1-3).
-  if (is_k) {
-    load(0, 0);
-#pragma unroll
-    for (int i = 1; i <= kBarEvery; i++) load(i, i);
-    if (wave == 0) wait_vmcnt<2 * kBarEvery>(); else wait_vmcnt<kBarEvery>();
-  } else {
-#pragma unroll
-    for (int i = 0; i < kBarEvery; i++) load(i, i);
-  }
+  // Prologue: K(0), K(1), K(2), V(0), V(1); wait for K(0): the loads issued
+  // after it are 6 instructions for waves 0 and 1 (their scale loads) and 4
+  // for waves 2 and 3.
+  load_k(0, 0);
+  load_k(1, 1);
+  load_k(2, 2);
+  load_v(0, 0);
+  load_v(1, 1);
+  if (wave == 0) wait_vmcnt<6>(); else if (wave == 1) wait_vmcnt<6>(); else wait_vmcnt<4>();
   barrier();
   {
     v4i kf[2][2];
@@ -341,13 +350,10 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_attn_mx(MxAttentionArgs a) {
   }
   wait_vmcnt<0>();
   barrier();
-  if (is_k) {
 #pragma unroll
-    for (int i = 1; i <= kBarEvery; i++) load(kBarEvery + i, (kBarEvery + i) % kSlots);
-  } else {
+  for (int i = 1; i <= kBarEvery; i++) load_k(kBarEvery + i, (kBarEvery + i) % kSlots);
 #pragma unroll
-    for (int i = 0; i < kBarEvery; i++) load(kBarEvery + i, (kBarEvery + i) % kSlots);
-  }
+  for (int i = 0; i < kBarEvery; i++) load_v(kBarEvery + i, (kBarEvery + i) % kSlots);
   if (nkt == 1) mask_tail(L);
   {
     pe = rowmax_update(std::true_type{});
@@ -373,7 +379,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_attn_mx(MxAttentionArgs a) {
   // between the P V products and the softmax of tile t (no scheduling fences:
   // the compiler interleaves them; 4% faster than fenced slots with Q
   // centring, the same without).  At even t the barrier and the loads of K(t+3),
-  // K(t+4) (waves 0-3) or V(t+2), V(t+3) (waves 4-7); a pending rescale;
+  // K(t+4), V(t+2), V(t+3); a pending rescale;
   // O += P(t-1) V(t-1); the softmax of tile t; the scores of tile t+1; V(t)
   // read for the next iteration.
   auto iter = [&](int t, auto ph_c) __attribute__((always_inline)) {
@@ -384,13 +390,10 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_attn_mx(MxAttentionArgs a) {
     }
     rescale();
     if (PH % kBarEvery == 0) {
-      if (is_k) {
 #pragma unroll
-        for (int i = 1; i <= kBarEvery; i++) load(t + kBarEvery + i, (PH + kBarEvery + i) % kSlots);
-      } else {
+      for (int i = 1; i <= kBarEvery; i++) load_k(t + kBarEvery + i, (PH + kBarEvery + i) % kSlots);
 #pragma unroll
-        for (int i = 0; i < kBarEvery; i++) load(t + kBarEvery + i, (PH + kBarEvery + i) % kSlots);
-      }
+      for (int i = 0; i < kBarEvery; i++) load_v(t + kBarEvery + i, (PH + kBarEvery + i) % kSlots);
     }
     const uint8_t* vn = smem + kVRing + PH * kSlot;                  // V(t)
     const uint8_t* kbp = smem + ((PH + 1) % kSlots) * kSlot;         // K(t+1)

@@ -62,6 +62,8 @@ constexpr int kMxRow = kHeadDim / 2;       // code bytes of one Q or K row
 constexpr int kMxQBlock = 128;             // Q rows per mean block
 constexpr int kMxTile = kBN * kHeadDim / 2;   // code bytes of one K (or V^T) tile
 constexpr int kMxTileScales = 256;         // scale bytes of one K (or V^T) tile
+constexpr int kMxBM = 128;                 // queries per FP4 work item (4 waves)
+constexpr int kMxWgPerCu = 2;              // FP4 attention workgroups resident per CU
 
 struct WorkspaceLayout {
   int64_t rows;        // workspace rows (all segments padded + guard)

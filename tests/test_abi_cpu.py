@@ -326,10 +326,14 @@ def test_mxfp4_plan_never_splits():
         T = cu[-1]
         e4 = fa.Plan(T, 56, cu, device=-1)
         mx = fa.Plan(T, 56, cu, device=-1, fmt="mxfp4")
+        assert mx.info()["query_tile"] == 128 and e4.info()["query_tile"] == 256
         items = mx.work_items()
         assert all(it[3] == 0 for it in items)
         real = [it for it in items if it[0] >= 0]
-        assert sorted(real) == sorted({(s, q, h, 0) for (s, q, h, w) in e4.work_items() if s >= 0})
+        # every (segment, 128-query tile, head) once
+        want = {(s, q0, h, 0) for s in range(len(cu) - 1) for h in range(56)
+                for q0 in range(0, cu[s + 1] - cu[s], 128)}
+        assert len(real) == len(want) and set(real) == want
         assert mx.info()["work_items"] == len(real)
 
 
