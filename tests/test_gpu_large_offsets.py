@@ -1,0 +1,102 @@
+"""GPU parity at a size whose element offsets pass 2^31: 320 037 tokens x 56
+heads x 128 channels (2.29e9 elements per tensor, 4.6 GB in BF16), in two
+segments (200 000 and a ragged 120 037 tokens).  Offsets into q, k, v and out
+past token 299 593 exceed the int32 range, so a 32-bit index anywhere in the
+quantize, attention or store code would touch the wrong rows.
+
+Checked for two heads (0 and 55): the E4M3 codes, scales and K means bit for
+bit and sampled rows, with the last row of each segment, against the float64
+oracle: element-wise |o - r| <= 0.1 + 0.1 |r| against the exact inputs, and
+relative RMS <= 0.035 against the oracle on the dequantized operands.  The
+relative RMS against the exact inputs is held to the two independent errors
+added in quadrature: the operands' own E4M3 error (the oracle on the dequantized
+operands against the exact inputs, 0.061-0.063 on draws of this shape: above
+the 0.06 that holds at 30k-token segments, as segments of 10^5 keys flatten
+the softmax) and the 0.035 kernel bar.  For the FP4 variant with Q
+centring, its codes and block scales bit for bit and sampled rows against its
+reference.  Inputs are drawn on the GPU from a seeded generator (a 6.9e9-value
+draw on the host would take minutes); the oracle gets the same values, copied
+to the host.
+"""
+import numpy as np
+import pytest
+import torch
+
+import fp8_flash_attention_amd as fa
+from oracle import attention as A
+from oracle import compare
+from oracle import mxfp4 as M
+from oracle import quantize as Qz
+from workloads import sample_rows
+from tests.gpu_helpers import log, read_codes
+from tests.test_gpu_mxfp4 import _check_codes, _check_output, read_mx
+
+pytestmark = pytest.mark.gpu
+
+T, H, D = 320_037, 56, 128
+CU = [0, 200_000, T]
+SCALE = 0.125
+HEADS = [0, 55]
+DIAG_BAR = 0.035
+
+
+@pytest.fixture(scope="module")
+def inputs():
+    assert (T - 1) * H * D > 2 ** 31
+    log(f"large offsets: drawing q, k, v [{T}, {H}, {D}] on the GPU")
+    g = torch.Generator(device="cuda")
+    g.manual_seed(8101)
+    q, k, v = (torch.randn((T, H, D), generator=g, device="cuda", dtype=torch.bfloat16) for _ in range(3))
+    # a per-head, per-channel offset of K, as in the other K-offset workloads
+    k += (2.0 ** 0.5 * torch.randn((H, D), generator=g, device="cuda")).to(torch.bfloat16)
+    torch.cuda.synchronize()
+    host = tuple(x[:, HEADS].cpu() for x in (q, k, v))
+    yield q, k, v, host
+    del q, k, v
+    torch.cuda.empty_cache()
+
+
+def test_e4m3_codes_and_rows_past_int32_offsets(inputs):
+    q, k, v, (qh, kh, vh) = inputs
+    log(f"large offsets E4M3: T={T} H={H} cu={CU}")
+    plan = fa.Plan(T, H, CU, SCALE, device=0)
+    ws = plan.new_workspace()
+    fa.quantize(plan, q, k, v, ws)
+    out = fa.forward(plan, ws)
+    torch.cuda.synchronize()
+    got = read_codes(plan, ws, HEADS)
+    r = Qz.quantize(qh, kh, vh, CU, SCALE)
+    for name in ("q_codes", "k_codes", "v_codes"):
+        assert np.array_equal(got[name], r[name]), name
+    assert np.array_equal(np.asarray(got["scales"])[..., HEADS].view(np.uint32), r["scales"].view(np.uint32))
+    assert np.array_equal(got["mu"][:, HEADS].view(np.uint32), r["mu"].view(np.uint32))
+    rows = sample_rows(T, 64, seed=8102, cu_seqlens=CU)
+    assert rows[-1] == T - 1
+    o = out[rows][:, HEADS].double().cpu().numpy()
+    del out
+    ref = A.attention_rows(qh, kh, vh, CU, SCALE, rows).numpy()
+    dq, dk, dv = (Qz.dequantize(r[n], r["scales"][i]) for i, n in enumerate(("q_codes", "k_codes", "v_codes")))
+    diag = A.attention_rows(dq, dk, dv, CU, SCALE, rows).numpy()
+    rr, rd, ex = compare.rel_rms(o, ref), compare.rel_rms(o, diag), compare.allclose_excess(o, ref)
+    op = compare.rel_rms(diag, ref)   # the E4M3 operands' own error, oracle only
+    bar = max(compare.REL_RMS_BAR, float(np.hypot(op, DIAG_BAR)))
+    log(f"  rel_rms={rr:.5f} (bar {bar:.5f}; operands alone {op:.5f}) vs dequantized={rd:.5f} "
+        f"allclose_excess={ex:.5f}")
+    assert rr <= bar and rd <= DIAG_BAR and ex <= 0.0
+
+
+def test_mxfp4_codes_and_rows_past_int32_offsets(inputs):
+    q, k, v, (qh, kh, vh) = inputs
+    log(f"large offsets FP4 with Q centring: T={T} H={H} cu={CU}")
+    plan = fa.Plan(T, H, CU, SCALE, device=0, fmt="mxfp4", q_centre=True)
+    ws = plan.new_workspace()
+    fa.quantize(plan, q, k, v, ws)
+    out = fa.forward(plan, ws)
+    torch.cuda.synchronize()
+    z = M.quantize_mxfp4(qh, kh, vh, CU, SCALE, q_centre=True)
+    _check_codes(read_mx(plan, ws, HEADS), z)
+    rows = sample_rows(T, 48, seed=8103, cu_seqlens=CU)
+    o = out[rows][:, HEADS].float().cpu().numpy()
+    del out
+    ref = M.attention_mxfp4_rows(z, CU, rows, list(range(len(HEADS))))
+    _check_output(o, ref, "large offsets")
