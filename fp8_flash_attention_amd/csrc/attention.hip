@@ -172,12 +172,13 @@ __device__ __forceinline__ void unroll_iters(F& iter, int t) {
     unroll_iters<I + 1, N>(iter, t);
   }
 }
-// The remaining iterations (fewer than N - 1 after whole passes), phases P, P + 1, ...
-template <int P, int N, typename F>
+// The remaining iterations (at most N after whole passes, the last one of the
+// loop among them), phases P, P + 1, ... mod N.
+template <int P, int E, int N, typename F>
 __device__ __forceinline__ void tail_iters(F& iter, int& t, int nkt) {
-  if constexpr (P < N) {
-    if (t < nkt) iter(t++, std::integral_constant<int, P>{});
-    tail_iters<P + 1, N>(iter, t, nkt);
+  if constexpr (P < E) {
+    if (t < nkt) iter(t++, std::integral_constant<int, P % N>{});
+    tail_iters<P + 1, E, N>(iter, t, nkt);
   }
 }
 
@@ -360,14 +361,9 @@ __global__ __launch_bounds__(64 * kWavesWG, 8 / kWavesWG) void k_attn(AttentionA
     }
   };
   // Reference update for the tile whose exp2 arguments are in S.  FIRST sets
-  // the reference from the tile maximum.  Keys past the segment end are not
-  // masked: their K rows are zero codes, so their scores are exactly 0 (x =
-  // nb), which does not exceed
-  // the row maximum (the centred keys of a segment average to zero, so the
-  // largest score is >= 0 up to rounding); their V rows are zero too, and the
-  // row sum of the last tile uses a selector without them.  Only the FP32 sum
-  // kept for the LSE masks them.  Register r of block kb in lane l holds key
-  // kbase + 32*kb + 8*(r/4) + 4*(l/32) + r%4.
+  // the reference from the tile maximum.  Keys past the end of the range have
+  // been set to -inf (mask_tail) before this runs.  Register r of block kb in
+  // lane l holds key kbase + 32*kb + 8*(r/4) + 4*(l/32) + r%4.
   auto rowmax_update = [&](auto first_c) __attribute__((always_inline)) {
     constexpr bool FIRST = decltype(first_c)::value;
     // this lane's maximum of x: 15 v_max3 + 1 v_max (the pair lane holds the
@@ -416,7 +412,6 @@ __global__ __launch_bounds__(64 * kWavesWG, 8 / kWavesWG) void k_attn(AttentionA
 #pragma unroll
     for (int i = 0; i < 4; i++) p[i] = __builtin_amdgcn_exp2f(S[kb][4 * q4 + i]);
     if (LSE) {
-      // every key of the tile, padded ones included (removed after the loop)
 #pragma unroll
       for (int i = 0; i < 4; i++) lex += p[i];
     }
@@ -434,9 +429,28 @@ __global__ __launch_bounds__(64 * kWavesWG, 8 / kWavesWG) void k_attn(AttentionA
       for (int r = 0; r < 16; r++)
         if (32 * kb + 8 * (r >> 2) + (r & 3) > dlim) S[kb][r] = -__builtin_huge_valf();
   };
+  // Keys past the end of the range (the last tile of a segment whose length is
+  // not a multiple of 64) to -inf in tile t, before the reference update.
+  // Their K rows are zero codes, so unmasked they would score exactly 0: a
+  // whole segment's centred keys average to zero, so some real score is >= 0
+  // and such a key could not move the reference, but the keys of one piece of
+  // a split item need not average to zero, and a zero score far above every
+  // real one would take the reference and flush the real probabilities.
+  // (Causal: keys past the segment end lie after every stored query and are
+  // masked by mask_causal.)
+  const bool ragged = !CAUSAL && Lk < nkt * kBN;
+  auto mask_tail = [&](int t) __attribute__((always_inline)) {
+    const int dlim = Lk - 1 - t * kBN - 4 * lg;
+#pragma unroll
+    for (int kb = 0; kb < 2; kb++)
+#pragma unroll
+      for (int r = 0; r < 16; r++)
+        if (32 * kb + 8 * (r >> 2) + (r & 3) > dlim) S[kb][r] = -__builtin_huge_valf();
+  };
   // Softmax of tile 0 (reference from its maximum) into P, then the scores of
   // tile 1 (K in slot 1) into S.
   auto first_tile = [&]() __attribute__((always_inline)) {
+    if (ragged && nkt == 1) mask_tail(0);
     if (CAUSAL && q0 == 0) mask_causal(0);
     rowmax_update(std::true_type{});
 #pragma unroll
@@ -494,8 +508,9 @@ __global__ __launch_bounds__(64 * kWavesWG, 8 / kWavesWG) void k_attn(AttentionA
   // both 32-key blocks, then the second halves) so neither waits on the
   // other's accumulator.
   const int tdiag = q0 / kBN;   // causal: tiles from here on hold keys after some query
-  auto iter = [&](int t, auto ph_c) __attribute__((always_inline)) {
+  auto iter = [&](int t, auto ph_c, auto tail_c) __attribute__((always_inline)) {
     constexpr int PH = decltype(ph_c)::value;   // t % kSlots
+    constexpr bool TAIL = decltype(tail_c)::value;   // may be the last tile: mask keys past the range end
     // With the LSE sum, two of the four V(t-1) operands are read here, before
     // the barrier: the loads after it may refill V(t-1)'s slot.
     if constexpr (LSE && kPre < NDB) {
@@ -526,6 +541,7 @@ __global__ __launch_bounds__(64 * kWavesWG, 8 / kWavesWG) void k_attn(AttentionA
       O[0] = mfma_fp8(vf[0], P, O[0]);
       kf[0][1] = lds_read32(kb, koff[1][0], koff[1][1]);
       if (CAUSAL && t >= tdiag) mask_causal(t);   // wave-uniform branch, diagonal tiles only
+      if (TAIL && ragged && t == nkt - 1) mask_tail(t);   // wave-uniform branch, last tile only
       rowmax_update(std::false_type{});
       fence();
       O[1] = mfma_fp8(vf[1], P, O[1]);
@@ -567,6 +583,7 @@ __global__ __launch_bounds__(64 * kWavesWG, 8 / kWavesWG) void k_attn(AttentionA
       fence();
       O[0] = mfma_fp8(vf[0], P, O[0]);
       if (CAUSAL && t >= tdiag) mask_causal(t);
+      if (TAIL && ragged && t == nkt - 1) mask_tail(t);
       rowmax_update(std::false_type{});
       Pn[0] = probs4(0, 0, kbase);
       fence();
@@ -594,10 +611,14 @@ __global__ __launch_bounds__(64 * kWavesWG, 8 / kWavesWG) void k_attn(AttentionA
     keep(S[0]);   // the next tile's score products stay in this iteration
     keep(S[1]);
   };
-  // Unrolled by the ring depth so that every slot address is static.
+  // Unrolled by the ring depth so that every slot address is static; the
+  // last tile's iteration is always one of the tail's, where the masking of a
+  // ragged end lives.
+  auto iter_body = [&](int t, auto ph_c) __attribute__((always_inline)) { iter(t, ph_c, std::false_type{}); };
+  auto iter_tail = [&](int t, auto ph_c) __attribute__((always_inline)) { iter(t, ph_c, std::true_type{}); };
   int t = 1;
-  for (; t + kSlots - 1 < nkt; t += kSlots) unroll_iters<0, kSlots>(iter, t);
-  tail_iters<1, kSlots>(iter, t, nkt);
+  for (; t + kSlots < nkt; t += kSlots) unroll_iters<0, kSlots>(iter_body, t);
+  tail_iters<1, kSlots + 1, kSlots>(iter_tail, t, nkt);
   // O += P(nkt-1) V(nkt-1) once every load has landed; the row sum counts
   // only keys before the segment end.  Selector byte b of lane 0 or 17 (32 or
   // 49) weights key 32*(b/16) + 8*((b/4)%4) + b%4 (+4) of the tile.
@@ -642,10 +663,12 @@ __global__ __launch_bounds__(64 * kWavesWG, 8 / kWavesWG) void k_attn(AttentionA
   if (slot >= 0) {
     // one piece of a split item: the normalized partial output (in output
     // units) and the log2 of its weight sum in a frame shared by all pieces
-    // (p = 2^(c s) for every key), for the combine pass
+    // (p = 2^(c s) for every key), for the combine pass.  The reference is the
+    // maximum of the piece's first tile, so some probability is >= 112 and
+    // lt > 0; a zero sum would still give weight 0 (w = -inf) and O = 0.
     if (qrow < L) {
       const int prow = slot * kBM + 32 * wave + lq;
-      const float inv = s_v / lt;
+      const float inv = lt > 0.f ? s_v / lt : 0.f;
       float* orow = a.part_o + (size_t)prow * D;
 #pragma unroll
       for (int db = 0; db < NDB; db++)
@@ -654,7 +677,7 @@ __global__ __launch_bounds__(64 * kWavesWG, 8 / kWavesWG) void k_attn(AttentionA
           *reinterpret_cast<float4*>(orow + 32 * db + 8 * q4 + 4 * lg) =
               make_float4(O[db][4 * q4 + 0] * inv, O[db][4 * q4 + 1] * inv, O[db][4 * q4 + 2] * inv,
                           O[db][4 * q4 + 3] * inv);
-      if (lg == 0) a.part_w[prow] = __log2f(lt) - nb;
+      if (lg == 0) a.part_w[prow] = lt > 0.f ? __log2f(lt) - nb : -__builtin_huge_valf();
     }
   } else if (qrow < L) {
     const float inv = s_v / lt;
@@ -672,17 +695,7 @@ __global__ __launch_bounds__(64 * kWavesWG, 8 / kWavesWG) void k_attn(AttentionA
       }
   }
   if (LSE) {
-    // The padded keys of the last tile have zero codes, so their scores are
-    // exactly 0 and each added exp2(nb) in the final frame: remove them.
-    // (Causal: keys past the segment end lie after every stored query and are
-    // masked already.)
-    int npad = 0;
-#pragma unroll
-    for (int kb = 0; kb < 2; kb++)
-#pragma unroll
-      for (int r = 0; r < 16; r++)
-        npad += !CAUSAL && (nkt - 1) * kBN + 32 * kb + 8 * (r >> 2) + 4 * lg + (r & 3) >= Lk;
-    lex -= (float)npad * __builtin_amdgcn_exp2f(nb);
+    // (keys past the end of the range were masked, so they added nothing)
     const float le = sum_pair32(lex);
     if (lg == 0 && qrow < L) {
       const float lse2 = __log2f(le) - nb;
@@ -721,6 +734,9 @@ __global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
       w[i] = a.part_w[(slot0 + i) * kBM + r];
       m = __builtin_fmaxf(m, w[i]);
     }
+  // a piece of zero weight has w = -inf and contributes nothing; if every
+  // piece had zero weight the row would be written as zeros
+  if (m == -__builtin_huge_valf()) m = 0.f;
   float acc[HD];
 #pragma unroll
   for (int j = 0; j < HD; j++) acc[j] = 0.f;
@@ -740,7 +756,7 @@ __global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
         acc[4 * j + 3] += alpha * v.w;
       }
     }
-  const float inv = 1.f / den;
+  const float inv = den > 0.f ? 1.f / den : 0.f;
   uint16_t* orow = a.out + (int64_t)(si.start + qrow) * a.os0 + (int64_t)it.z * a.os1 + HD * half;
 #pragma unroll
   for (int j = 0; j < HD / 8; j++) {
@@ -760,9 +776,11 @@ __global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
         lm = __builtin_fmaxf(lm, lv[i]);
       }
     float se = 0.f;
+    if (lm != -__builtin_huge_valf()) {
 #pragma unroll
-    for (int i = 0; i < kMaxSplit; i++)
-      if (i < n) se += __expf(lv[i] - lm);
+      for (int i = 0; i < kMaxSplit; i++)
+        if (i < n) se += __expf(lv[i] - lm);
+    }
     a.lse[(int64_t)it.z * a.tokens + si.start + qrow] = lm + __logf(se);
   }
 }

@@ -189,6 +189,25 @@ def test_split_fills_the_last_round(name):
             assert len(pieces) == r * n and {_split(it[3])[1] for it in pieces} == {n}
 
 
+@pytest.mark.parametrize("name,split_items,pieces_each", [
+    ("s256_h2", 0, 0),
+    ("s4096_h56", 128, 2),            # last round of exactly half the CUs of each XCD: split
+    ("s20440_h56_strided", 128, 2),   # likewise
+    ("s30272_h56_koffset", 8, 8),     # one item left per XCD: eight pieces
+    ("varlen_30272_h56", 0, 0),
+])
+def test_graded_workloads_split_counts(name, split_items, pieces_each):
+    # the split schedule of each graded workload on a 256-CU device, as stated
+    # in the design notes
+    w = WORKLOADS[name]
+    p = fa.Plan(w.tokens, w.heads, w.cu_seqlens, device=-1)
+    pieces = [it for it in p.work_items() if it[0] >= 0 and it[3]]
+    items = {(it[0], it[1], it[2]) for it in pieces}
+    assert len(items) == split_items
+    assert len(pieces) == split_items * pieces_each == p.info()["partial_slots"]
+    assert all(_split(it[3])[1] == pieces_each for it in pieces)
+
+
 def test_split_small_and_short_cases():
     # few items: as many pieces as fit one per CU, at least 8 key tiles each
     p = fa.Plan(3000, 1, [0, 3000], device=-1)

@@ -291,6 +291,51 @@ def test_split_keys_lse_and_repeat():
     assert err_d <= 2e-3
 
 
+def test_split_pieces_of_opposing_keys_every_element():
+    # Regression: a split item's last pieces hold only keys whose scores lie far
+    # below every query's maximum (channel 0: q = 40 everywhere, k = +40 on the
+    # first half of the keys and -40 on the second, about -200 in log2 units),
+    # and the last piece ends on a ragged tile.  Keys past the segment end score
+    # exactly 0 (zero codes); unmasked, they would take that piece's reference
+    # and flush its real weights (0/0, then NaN through the combine).  Every
+    # element and the LSE are compared with the oracle.
+    T, H, cu = 3000, 1, [0, 3000]
+    w = make_workload("opposing_keys", T, H, cu, seed=103)
+    q, k, v = generate(w)
+    q[:, :, 0] = 40.0
+    k[:1500, :, 0] = 40.0
+    k[1500:, :, 0] = -40.0
+    plan = fa.Plan(w.tokens, w.heads, w.cu_seqlens, w.softmax_scale, device=0)
+    nkt = (T + 63) // 64
+    assert T % 64 != 0
+    firsts = [64 * (nkt * (it[3] & 15) // ((it[3] >> 4) & 15)) for it in _pieces(plan)
+              if (it[3] & 15) == ((it[3] >> 4) & 15) - 1]
+    log(f"  first keys of the last pieces: {sorted(set(firsts))}")
+    assert firsts and min(firsts) >= 1500
+    ws = plan.new_workspace()
+    log(f"attention opposing_keys T={T} H={H} (split, ragged last piece)")
+    fa.quantize(plan, q.cuda(), k.cuda(), v.cuda(), ws)
+    lse = torch.empty((H, T), dtype=torch.float32, device="cuda")
+    out = fa.forward(plan, ws, lse=lse)
+    torch.cuda.synchronize()
+    got = out.cpu().double().numpy()
+    assert np.isfinite(got).all()
+    ref = A.attention(q, k, v, cu, w.softmax_scale).numpy()
+    dq, dk, dv = _dequantized(q, k, v, cu, w.softmax_scale)
+    diag = A.attention(dq, dk, dv, cu, w.softmax_scale).numpy()
+    rr, rd, ex = compare.rel_rms(got, ref), compare.rel_rms(got, diag), compare.allclose_excess(got, ref)
+    log(f"  rel_rms={rr:.5f} diagnostic rel_rms={rd:.5f} allclose_excess={ex:.5f}")
+    assert rr <= compare.REL_RMS_BAR and rd <= DIAG_BAR and ex <= 0.0
+    r = Qz.quantize(q, k, v, cu, w.softmax_scale)
+    dk = dk + r["mu"][0][None].astype(np.float64)
+    ld = A.lse_rows(torch.from_numpy(dq), torch.from_numpy(dk), cu, w.softmax_scale).numpy().T
+    gl = lse.cpu().double().numpy()
+    assert np.isfinite(gl).all()
+    err_d = np.abs(gl - ld).max()
+    log(f"  lse max err vs dequantized {err_d:.5f}")
+    assert err_d <= 2e-3
+
+
 def test_binding_rejects_tensors_off_the_plan_device():
     # pointers from another device (or host memory) must never reach the kernels
     w = WORKLOADS["s256_h2"]
