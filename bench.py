@@ -6,11 +6,17 @@ which are resident in HBM before timing starts: fp8attn_quantize (stats,
 finalize, pack) followed by fp8attn_forward.  The plan (segment schedule) is
 built once beforehand, as it is reused across calls.
 
-Protocol (sglang PR "[diffusion] attention: add fp8_fa_sm120 FP8 backend for
-SM120 GPUs", "Speed Tests and Profiling": kernel-only times with events after
-warmup): W untimed warmup steps, then K timed steps bracketed by
-torch.cuda.synchronize(); HIP events recorded on the launch stream around
-every forward give the attention kernel's own average duration.
+Timing: W untimed warmup steps, then K timed steps bracketed by
+torch.cuda.synchronize(); ``value`` is the step throughput over those K steps,
+and HIP events recorded on the launch stream around every forward give the
+attention kernel's average launch duration for the roofline.  Then the
+protocol of sglang PR "[diffusion] attention: add fp8_fa_sm120 FP8 backend for
+SM120 GPUs" ("Speed Tests and Profiling": kernel only, CUDA events, 20 warmup,
+5 x 10 iterations) is run on its own for the forward, the quantize and the
+whole step: 20 warmup launches, then 5 repetitions of 10 back-to-back
+launches, reporting the median of the five per-launch means with the min and
+max.  The shader clock is sampled (amdsmi GPU metrics) while the protocol's
+forward launches run.
 
 Prints one JSON line.  FLOPs are counted as 4 * sum(L^2) * H * D.
 
@@ -68,6 +74,104 @@ def measured_traffic(key: str, kernel_file: str = "attention.hip"):
     return e.get("hbm_bytes_per_launch")
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+class ClockSampler:
+    """Samples the GPU shader clock (MHz) from amdsmi GPU metrics on a host thread
+    while GPU work runs; reports nothing if amdsmi is not usable."""
+
+    def __init__(self, index: int = 0, period_s: float = 0.005):
+        import threading
+        self.period = period_s
+        self.samples = []
+        self.error = None
+        self._stop = threading.Event()
+        self._thread = None
+        self._h = None
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            self._amdsmi = amdsmi
+            self._h = amdsmi.amdsmi_get_processor_handles()[index]
+            self._read()
+            self.samples.clear()
+        except Exception as e:  # noqa: BLE001 - report, do not fail the bench
+            self.error = f"{type(e).__name__}: {e}"
+            self._h = None
+        self._threading = threading
+
+    def _read(self):
+        m = self._amdsmi.amdsmi_get_gpu_metrics_info(self._h)
+        vals = m.get("current_gfxclks")
+        if isinstance(vals, (list, tuple)):
+            vals = [v for v in vals if isinstance(v, (int, float)) and 0 < v < 10000]
+            if vals:
+                return sum(vals) / len(vals)
+        v = m.get("current_gfxclk")
+        return float(v) if isinstance(v, (int, float)) and 0 < v < 10000 else None
+
+    def _run(self):
+        while not self._stop.is_set():
+            try:
+                v = self._read()
+                if v is not None:
+                    self.samples.append(v)
+            except Exception as e:  # noqa: BLE001
+                self.error = f"{type(e).__name__}: {e}"
+                return
+            self._stop.wait(self.period)
+
+    def __enter__(self):
+        if self._h is not None:
+            self._thread = self._threading.Thread(target=self._run, daemon=True)
+            self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        if self._thread is not None:
+            self._thread.join()
+        return False
+
+    def summary(self):
+        if not self.samples:
+            return {"samples": 0, "error": self.error}
+        v = sorted(self.samples)
+        pct = lambda f: round(v[min(len(v) - 1, int(f * len(v)))], 0)   # noqa: E731
+        return {"median_mhz": pct(0.5), "p05_mhz": pct(0.05), "p95_mhz": pct(0.95), "samples": len(v),
+                "source": "amdsmi gpu_metrics current_gfxclks (mean over XCDs), sampled every 5 ms"}
+
+
+def protocol(fn, stream, warmup: int = 20, reps: int = 5, per: int = 10):
+    """20 warmup launches, then `reps` x `per` back-to-back launches timed with events
+    on `stream`: median, min and max of the per-launch means (milliseconds)."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    means = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(per):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        means.append(e0.elapsed_time(e1) / per)
+    v = sorted(means)
+    return {"median_ms": round(v[len(v) // 2], 4), "min_ms": round(v[0], 4), "max_ms": round(v[-1], 4),
+            "reps_ms": [round(x, 4) for x in means], "warmup": warmup, "reps": reps, "per_rep": per}
+
+
 def cpu_baseline(w, q, k, v, budget_s: float):
     """The float64 oracle on a bounded sample of query rows (all heads), in TFLOP/s."""
     import torch
@@ -91,7 +195,8 @@ def cpu_baseline(w, q, k, v, budget_s: float):
         if time.time() - t0 >= budget_s:
             break
     dt = time.time() - t0
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "cpu_model": cpu_model(),
+            "kind": "oracle",
             "sample": f"float64 oracle on {rows_done} seeded query rows x {w.heads} heads of {w.name} "
                       f"({dt:.1f} s wall; quantization not included)"}
 
@@ -161,6 +266,14 @@ def main() -> int:
 
     fwd_ms = [a.elapsed_time(b) for a, b in evs]
     step_ms = [a.elapsed_time(b) for a, b in qev]
+
+    # the pages' kernel-only protocol, separately for the forward (with the
+    # shader clock sampled meanwhile), the quantize and the whole step
+    sampler = ClockSampler(0)
+    with sampler:
+        fwd_proto = protocol(lambda: fa.forward(plan, ws, out), stream)
+    quant_proto = protocol(lambda: fa.quantize(plan, q, k, v, ws), stream)
+    step_proto = protocol(step, stream)
     ms_step = wall * 1e3 / args.steps
     ms_fwd = sum(fwd_ms) / len(fwd_ms)
     ms_quant = sum(s - f for s, f in zip(step_ms, fwd_ms)) / len(fwd_ms)
@@ -209,6 +322,13 @@ def main() -> int:
         "forward_tflops": round(fwd_tflops, 2),
         "forward_pct_fp8_peak": round(100.0 * fwd_tflops / FP8_PEAK_TFLOPS, 2),
         "quantize_ms": round(ms_quant, 4),
+        "forward_protocol": fwd_proto,
+        "forward_protocol_tflops": round(flops / (fwd_proto["median_ms"] * 1e-3) / 1e12, 2),
+        "forward_protocol_pct_fp8_peak": round(100.0 * flops / (fwd_proto["median_ms"] * 1e-3) / 1e12
+                                               / FP8_PEAK_TFLOPS, 2),
+        "sclk_during_forward": sampler.summary(),
+        "quantize_protocol": quant_proto,
+        "step_protocol": step_proto,
         "mfma_skeleton": skeleton,
         "mfma_skeleton_random_operands": skeleton_random,
         "forward_frac_of_skeleton": round(fwd_tflops / skeleton["tflops"], 4) if skeleton else None,
