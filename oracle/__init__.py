@@ -5,7 +5,10 @@ CPU-baseline leg of ``bench.py`` may import, call or execute anything in this
 package.  The HIP library never links it and the Python binding never imports
 it; the two share no code.  The oracle is plain and slow on purpose:
 
-* ``oracle.attention`` - float64 softmax(Q K^T * scale) V per segment and head.
+* ``oracle.attention`` - float64 softmax(Q K^T * scale) V per segment and head,
+  its LSE, and the FP8 recipe per row (E4M3 probabilities over dequantized
+  E4M3 operands), used to show which rows no FP8 kernel can bring within the
+  exact element-wise bar.
 * ``oracle.quantize``  - per-head E4M3 quantization of Q/K/V (K centred by its
   segment's per-channel mean).
 * ``oracle.e4m3``      - bit-level OCP E4M3 encoder/decoder.

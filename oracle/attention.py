@@ -21,6 +21,20 @@ backend and do not define it, so this is the plain reading for
 self-attention): query i of a segment attends to the keys j <= i of the same
 segment, positions counted from the segment start.
 
+FP8 recipe (``attention_fp8_recipe``): the arithmetic of the FP8 method of
+sglang PR "[diffusion] attention: add fp8_fa_sm120 FP8 backend for SM120
+GPUs" ("Modifications": E4M3 operands for both products, an FP32 softmax, the
+probabilities packed to E4M3 before the second product), written out per row
+without blocking: scores from the dequantized E4M3 operands, the row maximum
+mapped to 448 (the top of E4M3; the page does not say where the maximum lands,
+and this is the plainest reading that uses the format's whole range), each
+probability rounded to float32 and then to E4M3, and the output normalized by
+the sum of those E4M3 weights (the weights that actually multiply V).  It shows
+how far the method itself, with no blocking, reordering or kernel choices, is
+from the exact result; the pins are in the same test file (equal scores,
+one dominant key, inputs whose probabilities are powers of two so every
+rounding is exact, and a planted missing scale).
+
 Parity pins live in ``tests/test_oracle_attention.py``.
 """
 from __future__ import annotations
@@ -122,4 +136,36 @@ def lse_rows(q, k, cu_seqlens: Sequence[int], softmax_scale: float,
         kend = r + 1 if causal else b               # causal: keys up to the query itself
         sc = torch.einsum("hd,lhd->hl", qd[r], kd[a:kend]) * sigma
         out[i] = torch.logsumexp(sc, dim=-1)
+    return out
+
+
+FP8_P_TOP = 448.0   # where the row maximum of the probabilities lands (the largest E4M3 value)
+
+
+def attention_fp8_recipe(q, k, v, cu_seqlens: Sequence[int], softmax_scale: float, causal: bool = False,
+                         rows: Optional[List[int]] = None) -> torch.Tensor:
+    """The FP8 recipe per row (see the module text), float64 [T or len(rows), H, D].
+
+    ``q``, ``k``, ``v`` are the dequantized E4M3 operands (code value times scale);
+    K may be the centred one, since a per-segment constant added to every key
+    moves every score of a query and its maximum by the same amount.
+    """
+    from . import e4m3
+    qd, kd, vd = _f64(q), _f64(k), _f64(v)
+    T, H, D = qd.shape
+    sigma = _sigma(softmax_scale)
+    cu = list(cu_seqlens)
+    if rows is None:
+        rows = list(range(T))
+    out = torch.zeros((len(rows), H, D), dtype=torch.float64)
+    seg_of = np.searchsorted(np.asarray(cu), np.asarray(rows, dtype=np.int64), side="right") - 1
+    for i, r in enumerate(rows):
+        s_ = int(seg_of[i])
+        a, b = cu[s_], cu[s_ + 1]
+        kend = r + 1 if causal else b
+        sc = torch.einsum("hd,lhd->hl", qd[r], kd[a:kend]) * sigma            # [H, keys]
+        m = sc.max(dim=-1, keepdim=True).values
+        p32 = (torch.exp(sc - m) * FP8_P_TOP).numpy().astype(np.float32)      # FP32 probabilities
+        ph = torch.from_numpy(e4m3.decode(e4m3.encode(p32)))                   # their E4M3 values
+        out[i] = torch.einsum("hl,lhd->hd", ph, vd[a:kend]) / ph.sum(dim=-1, keepdim=True)
     return out

@@ -29,16 +29,17 @@ Fixed-order mean (a reading; the pages fix no summation order): for segment
 
 Empty segments have no mean; their ``mu`` rows are 0.
 
-Q's scale in the product (``q_scale_pow2``): the pages ask for per-head amax
-scaling and fix no exact formula; the product rounds Q's amax/448 scale up so
-that the score factor ``softmax_scale * s_q * s_k * log2(e)`` is a power of two
-(the attention kernel then applies it exactly on the matrix core).  This is the
-product's choice, not a reading of the pages; it is mirrored here so that tests
-derive the expected Q codes from the inputs alone.  ``quantize`` uses it when a
-``softmax_scale`` is given and the plain amax/448 scale otherwise.
-Parity pins live in ``tests/test_oracle_quantize.py`` (for ``q_scale_pow2``:
-the scale is at least amax/448 and below twice it, and the score factor is a
-power of two up to float32 rounding).
+Q's scale (``q_scale_pow2``): the pages ask for per-head amax scaling and fix
+no exact formula.  The reading taken for Q is the smallest scale at or above
+fl32(amax/448) that makes the score factor ``softmax_scale * s_q * s_k *
+log2(e)`` a power of two, so the attention applies it exactly as a power-of-two
+factor of the score products; K and V keep fl32(amax/448).  ``quantize`` uses
+it when a ``softmax_scale`` is given and the plain amax/448 scale otherwise.
+Parity pins live in ``tests/test_oracle_quantize.py``; for ``q_scale_pow2``:
+its float32 bits against the same steps evaluated in exact rational
+arithmetic with a search for the power of two (which catches an off-by-one in
+the exponent where fl32(f * base) is itself a power of two), plus range
+properties (at least amax/448, below twice it, factor a power of two).
 
 Per-(segment, head) scales (``quantize_segments``) are a variant the product
 offers for packed batches: the sglang PR quantizes per head over the whole

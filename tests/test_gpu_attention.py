@@ -24,6 +24,7 @@ from oracle import attention as A
 from oracle import compare
 from oracle import quantize as Qz
 from workloads import WORKLOADS, generate, make_workload, sample_rows
+from tests.cases import FEW_KEYS, random_varlen, visible_keys
 from tests.gpu_helpers import bf16_ulp, log
 
 pytestmark = pytest.mark.gpu
@@ -355,19 +356,14 @@ def test_binding_rejects_tensors_off_the_plan_device():
 
 
 def test_random_varlen_every_element():
-    # thirty segments with lengths around the tile edges (0, 1, 63, 64, 65, 127 ...).
-    # Segments of one or two tokens average one or two V rows of magnitude up to ~4,
-    # whose E4M3 steps are 0.16: where two such rows cancel, the exact result is
-    # small while the input quantization alone moves it by ~0.1, so the element-wise
-    # bar is applied against the oracle on the dequantized operands (the kernel's own
-    # error); the graded relative RMS is against the exact inputs.
-    rng = np.random.default_rng(101)
-    edges = [0, 1, 2, 31, 32, 33, 63, 64, 65, 127, 128, 129, 255, 256, 257, 300, 511, 513]
-    lens = list(rng.choice(edges, size=30))
-    cu = [0]
-    for L in lens:
-        cu.append(cu[-1] + int(L))
-    w = make_workload("rand_varlen", cu[-1], 3, cu, seed=101)
+    # Thirty segments with lengths around the tile edges (0, 1, 63, 64, 65, 127 ...).
+    # A segment of a few tokens averages a few V rows with E4M3-rounded weights:
+    # the FP8 recipe itself breaks the element-wise bar against the exact inputs
+    # on such rows (tests/test_oracle_fp8_recipe.py, on this very case), so rows
+    # that see fewer than FEW_KEYS keys are held to it against the oracle on the
+    # dequantized operands (the kernel's own error), every other row against the
+    # exact inputs; the graded relative RMS is against the exact inputs.
+    w = random_varlen()
     q, k, v = generate(w, device="cuda")
     plan, ws, out, _ = _gpu_attention(w, q, k, v)
     qc, kc, vc = q.cpu(), k.cpu(), v.cpu()
@@ -377,11 +373,14 @@ def test_random_varlen_every_element():
     diag = A.attention(dq, dk, dv, w.cu_seqlens, w.softmax_scale).numpy()
     rr, rd = compare.rel_rms(got, ref), compare.rel_rms(got, diag)
     ex = compare.allclose_excess(got, diag)
-    log(f"  rel_rms={rr:.5f} diagnostic rel_rms={rd:.5f} allclose_excess vs dequantized={ex:.5f}")
+    wide = visible_keys(w.cu_seqlens, False) >= FEW_KEYS
+    ex_w = compare.allclose_excess(got[wide], ref[wide])
+    log(f"  rel_rms={rr:.5f} diagnostic rel_rms={rd:.5f} allclose_excess vs dequantized={ex:.5f}, "
+        f"rows with >= {FEW_KEYS} keys vs exact {ex_w:.5f}")
     assert np.isfinite(got).all()
     assert rr <= compare.REL_RMS_BAR
     assert rd <= DIAG_BAR
-    assert ex <= 0.0
+    assert ex <= 0.0 and ex_w <= 0.0
 
 
 def test_split_items_into_strided_output():

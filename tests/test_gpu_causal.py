@@ -21,6 +21,7 @@ from oracle import attention as A
 from oracle import compare
 from oracle import quantize as Qz
 from workloads import WORKLOADS, generate, make_workload, sample_rows
+from tests.cases import CAUSAL_CASES, FEW_KEYS, visible_keys
 from tests.gpu_helpers import bf16_ulp, log
 
 pytestmark = pytest.mark.gpu
@@ -60,14 +61,14 @@ def _check(w, rows, heads=None):
     dq, dk, dv, _ = _dequantized(q, k, v, w.cu_seqlens, w.softmax_scale)
     diag = A.attention_rows(dq, dk, dv, w.cu_seqlens, w.softmax_scale, rows, causal=True).numpy()
     rd = compare.rel_rms(got, diag)
-    # Rows near a segment start average a handful of V rows, where the E4M3 step
-    # of V alone (0.125-0.25 at |v| ~ 2-4) can exceed the element-wise bar once
-    # two rows cancel: there the element-wise bar is held against the oracle on
-    # the dequantized operands (the kernel's own error), as for one- and
-    # two-token segments; rows that see at least 64 keys meet it against the
-    # exact inputs.
-    pos = np.array([r - max(a for a in w.cu_seqlens[:-1] if a <= r) for r in rows])
-    wide = pos >= 64
+    # Rows near a segment start average a handful of V rows with E4M3-rounded
+    # weights: there the FP8 recipe itself (oracle.attention_fp8_recipe, no
+    # kernel involved) breaks the element-wise bar against the exact inputs
+    # (tests/test_oracle_fp8_recipe.py shows it on these very cases), so such
+    # rows are held to the bar against the oracle on the dequantized operands
+    # (the kernel's own error); rows that see at least FEW_KEYS keys meet it
+    # against the exact inputs.
+    wide = visible_keys(w.cu_seqlens, True)[rows] >= FEW_KEYS
     ex_d = compare.allclose_excess(got, diag)
     ex = compare.allclose_excess(got[wide], ref[wide]) if wide.any() else 0.0
     log(f"  rel_rms={rr:.5f} diagnostic rel_rms={rd:.5f} allclose_excess: vs dequantized {ex_d:.5f}, "
@@ -81,12 +82,7 @@ def _check(w, rows, heads=None):
     return plan, ws, out
 
 
-CASES = [
-    make_workload("c256", 256, 2, [0, 256], seed=401),
-    make_workload("c_ragged", 700, 4, [0, 300, 700], seed=402, k_offset_var=2.0),
-    make_workload("c_varlen", 1500, 3, [0, 0, 1, 64, 65, 193, 700, 700, 1500], seed=403),
-    make_workload("c_long", 1200, 2, [0, 1200], seed=404, k_offset_var=2.0),
-]
+CASES = CAUSAL_CASES
 
 
 @pytest.mark.parametrize("w", CASES, ids=lambda w: w.name)

@@ -10,9 +10,10 @@ oracle: element-wise |o - r| <= 0.1 + 0.1 |r| against the exact inputs, and
 relative RMS <= 0.035 against the oracle on the dequantized operands.  The
 relative RMS against the exact inputs is held to the two independent errors
 added in quadrature: the operands' own E4M3 error (the oracle on the dequantized
-operands against the exact inputs, 0.061-0.063 on draws of this shape: above
+operands against the exact inputs, 0.061-0.065 on draws of this shape: above
 the 0.06 that holds at 30k-token segments, as segments of 10^5 keys flatten
-the softmax) and the 0.035 kernel bar.  For the FP4 variant with Q
+the softmax) and the 0.035 kernel bar; the lifted bar applies only when the
+operands alone exceed 0.06 on the drawn data.  For the FP4 variant with Q
 centring, its codes and block scales bit for bit and sampled rows against its
 reference.  Inputs are drawn on the GPU from a seeded generator (a 6.9e9-value
 draw on the host would take minutes); the oracle gets the same values, copied
@@ -79,7 +80,9 @@ def test_e4m3_codes_and_rows_past_int32_offsets(inputs):
     diag = A.attention_rows(dq, dk, dv, CU, SCALE, rows).numpy()
     rr, rd, ex = compare.rel_rms(o, ref), compare.rel_rms(o, diag), compare.allclose_excess(o, ref)
     op = compare.rel_rms(diag, ref)   # the E4M3 operands' own error, oracle only
-    bar = max(compare.REL_RMS_BAR, float(np.hypot(op, DIAG_BAR)))
+    # the bar is lifted only where the operands alone already break 0.06
+    # (tests/test_oracle_fp8_recipe.py shows they do at this segment length)
+    bar = float(np.hypot(op, DIAG_BAR)) if op > compare.REL_RMS_BAR else compare.REL_RMS_BAR
     log(f"  rel_rms={rr:.5f} (bar {bar:.5f}; operands alone {op:.5f}) vs dequantized={rd:.5f} "
         f"allclose_excess={ex:.5f}")
     assert rr <= bar and rd <= DIAG_BAR and ex <= 0.0

@@ -245,3 +245,38 @@ def test_causal_off_by_one_negative_control():
     good = A.attention(q, k, v, [0, T], 0.25, causal=True)
     bad = torch.stack([A.attention(q[:i + 2], k[:i + 2], v[:i + 2], [0, min(i + 2, T)], 0.25)[i] for i in range(T)])
     assert (good - bad).abs().max() > 1e-3
+
+
+def test_lse_rows_two_keys_closed_form():
+    # two keys with exact scores s1, s2 (D = 1): lse = sigma s1 + log(1 + e^(sigma (s2 - s1))),
+    # with sigma the float32 value of the scale; a dropped or misapplied sigma, a
+    # wrong sign or a wrong key range shows here
+    for scale, (x, a, b) in [(0.3, (2.0, 3.0, -5.0)), (0.08838834764831845, (6.0, 7.5, 7.0)),
+                             (1.7, (-1.5, 4.0, 2.0))]:
+        sigma = float(np.float32(scale))
+        q = torch.tensor([[[x]], [[x]]], dtype=torch.float64)
+        k = torch.tensor([[[a]], [[b]]], dtype=torch.float64)
+        s1, s2 = x * a, x * b
+        want = sigma * s1 + math.log1p(math.exp(sigma * (s2 - s1)))
+        got = A.lse_rows(q, k, [0, 2], scale, rows=[0, 1]).numpy()
+        assert np.allclose(got, want, rtol=0, atol=1e-13)
+        # causal: row 0 sees key 0 only, row 1 both
+        gc = A.lse_rows(q, k, [0, 2], scale, rows=[0, 1], causal=True).numpy()
+        assert abs(gc[0, 0] - sigma * s1) <= 1e-13 and abs(gc[1, 0] - want) <= 1e-13
+
+
+def test_lse_rows_brute_force_mpmath():
+    mpmath.mp.dps = 40
+    T, H, D = 6, 2, 3
+    q, k = _rand((T, H, D), 61), _rand((T, H, D), 62)
+    cu = [0, 2, 6]
+    scale = 0.7
+    sigma = float(np.float32(scale))
+    got = A.lse_rows(q, k, cu, scale).numpy()
+    for s, (a, b) in enumerate(zip(cu[:-1], cu[1:])):
+        for i in range(a, b):
+            for h in range(H):
+                terms = [mpmath.exp(mpmath.mpf(sigma) * mpmath.fsum(
+                    mpmath.mpf(float(q[i, h, d])) * mpmath.mpf(float(k[j, h, d])) for d in range(D)))
+                    for j in range(a, b)]
+                assert abs(got[i, h] - float(mpmath.log(mpmath.fsum(terms)))) <= 1e-12

@@ -13,9 +13,11 @@
   tests/test_oracle_e4m3.py is indirect, so here a few elements are checked
   against torch's float8_e4m3fn cast of the same fl32(x/s).
 """
+import math
 from fractions import Fraction
 
 import numpy as np
+import pytest
 import torch
 
 from oracle import quantize as Qz
@@ -213,3 +215,82 @@ def test_segment_scales_power_of_two_rescaling():
     dv = Qz.dequantize_segments(r["v_codes"], r["scales"][2], cu)
     db = Qz.dequantize_segments(base["v_codes"], base["scales"][2], cu)
     assert np.array_equal(dv[200:], 8 * db[200:]) and np.array_equal(dv[:200], db[:200])
+
+
+# ------------------------------------------------------------------------------
+# Q's power-of-two scale, bit for bit, from exact rational arithmetic.  Every
+# float32 operation of the rule (products, the quotient) is evaluated exactly
+# with fractions.Fraction and rounded to float32 by the format's definition
+# (nearest, ties to even, subnormal quantum 2^-149); the power of two is the
+# smallest 2^m >= t found by search over m, not by frexp.
+
+
+def _fl32(x: Fraction) -> Fraction:
+    if x == 0:
+        return Fraction(0)
+    sign = -1 if x < 0 else 1
+    a = abs(x)
+    e = math.floor(math.log2(float(a)))
+    while Fraction(2) ** e > a:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= a:
+        e += 1
+    quantum = Fraction(2) ** (max(e, -126) - 23)
+    n = a / quantum
+    whole = n.numerator // n.denominator
+    rem = n - whole
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and whole % 2 == 1):
+        whole += 1
+    return sign * whole * quantum
+
+
+def _q_scale_exact(amax_q: float, amax_k: float, sigma: float) -> np.float32:
+    base = _fl32(Fraction(amax_q) / 448) if amax_q > 0 else Fraction(1)
+    s_k = _fl32(Fraction(amax_k) / 448) if amax_k > 0 else Fraction(1)
+    sig = _fl32(Fraction(sigma))                              # the float32 kernel argument
+    log2e = _fl32(Fraction(1.4426950408889634))
+    f = _fl32(_fl32(sig * s_k) * log2e)
+    t = _fl32(f * base)
+    if not (Fraction(2) ** -126 <= t < Fraction(2) ** 126):
+        return np.float32(float(base))
+    m = next(m for m in range(-160, 160) if Fraction(2) ** m >= t)
+    return np.float32(float(_fl32(Fraction(2) ** m / f)))
+
+
+def _bf16_values(n, seed, lo, hi):
+    rng = np.random.default_rng(seed)
+    x = (10.0 ** rng.uniform(lo, hi, n)).astype(np.float32)
+    return torch.from_numpy(x).to(torch.bfloat16).float().numpy()   # amax of BF16 data is a BF16 value
+
+
+@pytest.mark.parametrize("sigma", [1 / math.sqrt(128), 1 / math.sqrt(64), 0.05, 0.3, 1.0, 3.7])
+def test_q_scale_pow2_bits_match_exact_arithmetic(sigma):
+    aq, ak = _bf16_values(300, 31, -3, 3), _bf16_values(300, 32, -3, 3)
+    base = Qz.head_scale(aq)
+    s_k = Qz.head_scale(ak)
+    got = Qz.q_scale_pow2(base, s_k, sigma)
+    want = np.array([_q_scale_exact(float(a), float(b), sigma) for a, b in zip(aq, ak)], np.float32)
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+
+
+def test_q_scale_pow2_bits_where_t_is_a_power_of_two():
+    # cases where fl32(f * base) lands exactly on 2^k: m must be k itself (an
+    # off-by-one in the smallest power of two shows here and nowhere else)
+    rng = np.random.default_rng(33)
+    sigma = 0.08838834764831845
+    hits = 0
+    for _ in range(4000):
+        ak = float(_bf16_values(1, int(rng.integers(1 << 30)), -2, 2)[0])
+        s_k = Qz.head_scale(np.float32([ak]))
+        f = (np.float32(sigma) * s_k) * Qz.LOG2E_F32
+        k = int(rng.integers(-8, 4))
+        base = (np.float32(2.0 ** k) / f).astype(np.float32)
+        if (f * base).astype(np.float32)[0] != np.float32(2.0 ** k):
+            continue
+        aq = base.astype(np.float64)[0] * 448.0
+        if np.float32(aq) / np.float32(448) != base[0]:
+            continue
+        hits += 1
+        got = Qz.q_scale_pow2(base, s_k, sigma)[0]
+        assert got == _q_scale_exact(aq, ak, sigma) == base[0]
+    assert hits >= 20
