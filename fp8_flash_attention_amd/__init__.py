@@ -36,7 +36,8 @@ from ._lib import Fp8AttnError  # noqa: F401
 HEAD_DIM = 128
 DEFAULT_SCALE = 1.0 / math.sqrt(HEAD_DIM)
 
-__all__ = ["Plan", "quantize", "forward", "attention", "Fp8AttnError", "HEAD_DIM", "DEFAULT_SCALE"]
+__all__ = ["Plan", "quantize", "quantize_noalloc", "forward", "attention", "Fp8AttnError", "HEAD_DIM",
+           "DEFAULT_SCALE"]
 
 
 def _stream_handle(device: torch.device, stream=None) -> ctypes.c_void_p:
@@ -140,6 +141,16 @@ class Plan:
             shape = (shape[0], shape[2])          # per-head scales: [3][H]
         return workspace[off: off + 4 * n].view(torch.float32).view(shape)
 
+    def stats_offset(self) -> int:
+        """Bytes of workspace before the statistics region (all that ``quantize_noalloc`` and
+        ``forward`` need)."""
+        ptr = ctypes.c_void_p()
+        dims = (ctypes.c_int64 * 3)()
+        base = 256
+        _lib.check(_lib.lib().fp8attn_workspace_region(self._h, ctypes.c_void_p(base), _lib.REGION_STATS,
+                                                       ctypes.byref(ptr), dims), "fp8attn_workspace_region")
+        return int(ptr.value - base)
+
     def close(self):
         if self._h is not None:
             _lib.lib().fp8attn_plan_destroy(self._h)
@@ -186,6 +197,25 @@ def quantize(plan: Plan, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, work
                                            ctypes.c_void_p(workspace.data_ptr()),
                                            workspace.numel() * workspace.element_size(), st),
                "fp8attn_quantize")
+
+
+def quantize_noalloc(plan: Plan, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, workspace: torch.Tensor,
+                     stream=None) -> None:
+    """``fp8attn_quantize_noalloc``: as ``quantize``, with the statistics in the library's static
+    device buffer; ``workspace`` may stop at ``plan.stats_offset()`` bytes."""
+    for name, x in (("q", q), ("k", k), ("v", v)):
+        if tuple(x.shape[:2]) != (plan.tokens, plan.heads):
+            raise ValueError(f"{name} shape {tuple(x.shape)} does not match the plan")
+        _on_plan_device(plan, x, name)
+    _on_plan_device(plan, workspace, "workspace")
+    D = plan.head_dim
+    qs, ks, vs = _strides(q, "q", D), _strides(k, "k", D), _strides(v, "v", D)
+    st = _stream_handle(plan.device, stream)
+    _lib.check(_lib.lib().fp8attn_quantize_noalloc(plan.handle, ctypes.c_void_p(q.data_ptr()),
+                                                   ctypes.c_void_p(k.data_ptr()), ctypes.c_void_p(v.data_ptr()),
+                                                   qs, ks, vs, ctypes.c_void_p(workspace.data_ptr()),
+                                                   workspace.numel() * workspace.element_size(), st),
+               "fp8attn_quantize_noalloc")
 
 
 def forward(plan: Plan, workspace: torch.Tensor, out: Optional[torch.Tensor] = None,

@@ -17,6 +17,7 @@ STATUS_NAMES = {0: "FP8ATTN_OK", 1: "FP8ATTN_EINVAL", 2: "FP8ATTN_EUNSUPPORTED",
                 3: "FP8ATTN_ENOMEM", 4: "FP8ATTN_EWORKSPACE", 5: "FP8ATTN_EHIP"}
 REGION_Q, REGION_K, REGION_V, REGION_SCALES, REGION_MU, REGION_ROWMAP = range(6)
 REGION_Q_BSCALES, REGION_K_BSCALES, REGION_V_BSCALES, REGION_QM_CODES, REGION_QM_SCALES = range(6, 11)
+REGION_STATS = 11
 PLAN_SEGMENT_SCALES = 1          # FP8ATTN_PLAN_SEGMENT_SCALES
 PLAN_MXFP4 = 2                   # FP8ATTN_PLAN_MXFP4
 PLAN_Q_CENTRE = 4                # FP8ATTN_PLAN_Q_CENTRE
@@ -35,6 +36,9 @@ SIGNATURES = {
     "fp8attn_workspace_bytes": (ctypes.c_size_t, [ctypes.c_void_p]),
     "fp8attn_quantize": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                         _i64p, _i64p, _i64p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+    "fp8attn_quantize_noalloc": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                                ctypes.c_void_p, _i64p, _i64p, _i64p, ctypes.c_void_p,
+                                                ctypes.c_size_t, ctypes.c_void_p]),
     "fp8attn_forward": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
                                        _i64p, ctypes.c_void_p, ctypes.c_void_p]),
     "fp8attn_workspace_region": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,

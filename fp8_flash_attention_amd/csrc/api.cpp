@@ -89,6 +89,7 @@ WorkspaceLayout make_layout_mx(int64_t rows, int heads, int nseg, int nchunks) {
   w.qm_off = off; off = align_up(off + qblocks * kMxRow, 256);
   w.qms_off = off; off = align_up(off + qblocks * 4, 256);
   w.mu_off = off; off = align_up(off + sizeof(float) * (size_t)nseg * heads * kHeadDim, 256);
+  w.stats_off = off;
   w.kstat_off = off; off = align_up(off + sizeof(KStat) * (size_t)nchunks * heads * kHeadDim, 256);
   w.total = off;
   return w;
@@ -105,11 +106,14 @@ WorkspaceLayout make_layout(int64_t rows, int heads, int nseg, int nscale, int n
   w.v_off = off; off = align_up(off + codes, 256);
   w.scale_off = off; off = align_up(off + sizeof(float) * 3 * (size_t)nscale * heads, 256);
   w.mu_off = off; off = align_up(off + sizeof(float) * (size_t)nseg * heads * D, 256);
-  w.kstat_off = off; off = align_up(off + sizeof(KStat) * (size_t)nchunks * heads * D, 256);
-  w.amax_off = off; off = align_up(off + sizeof(float) * 2 * (size_t)nchunks * heads, 256);
   w.part_o_off = off; off = align_up(off + sizeof(float) * (size_t)npieces * kBM * D, 256);
   w.part_w_off = off; off = align_up(off + sizeof(float) * (size_t)npieces * kBM, 256);
   w.part_lse_off = off; off = align_up(off + sizeof(float) * (size_t)npieces * kBM, 256);
+  // the statistics of fp8attn_quantize come last: fp8attn_quantize_noalloc and
+  // fp8attn_forward do not need them
+  w.stats_off = off;
+  w.kstat_off = off; off = align_up(off + sizeof(KStat) * (size_t)nchunks * heads * D, 256);
+  w.amax_off = off; off = align_up(off + sizeof(float) * 2 * (size_t)nchunks * heads, 256);
   w.total = off;
   return w;
 }
@@ -400,15 +404,36 @@ fp8attn_status fp8attn_plan_ex(fp8attn_plan_t* plan_out, int64_t tokens, int32_t
 
 size_t fp8attn_workspace_bytes(fp8attn_plan_t p) { return p == nullptr ? 0 : p->ws.total; }
 
-fp8attn_status fp8attn_quantize(fp8attn_plan_t p, const void* q, const void* k, const void* v,
-                                const int64_t q_strides[2], const int64_t k_strides[2],
-                                const int64_t v_strides[2], void* workspace, size_t workspace_bytes,
-                                void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Statistics bytes of a plan as laid out in the static buffer of
+// fp8attn_quantize_noalloc: K statistics, then the Q/V amax partials.
+size_t static_stats_bytes(const fp8attn_plan_s* p) {
+  const size_t nch = p->chunks.size();
+  const size_t kst = align_up(sizeof(KStat) * nch * (size_t)p->heads * (size_t)p->head_dim, 256);
+  const size_t amx = p->mx ? 0 : align_up(sizeof(float) * 2 * nch * (size_t)p->heads, 256);
+  return kst + amx;
+}
+
+// fp8attn_quantize and fp8attn_quantize_noalloc: the statistics go to the
+// workspace's statistics region, or (noalloc) to the library's static buffer.
+fp8attn_status quantize_impl(fp8attn_plan_t p, const void* q, const void* k, const void* v,
+                             const int64_t q_strides[2], const int64_t k_strides[2],
+                             const int64_t v_strides[2], void* workspace, size_t workspace_bytes,
+                             void* stream, bool noalloc) {
   if (p == nullptr) return fail(FP8ATTN_EINVAL, "plan is NULL");
+  if (noalloc && static_stats_bytes(p) > kStaticStatsBytes)
+    return fail(FP8ATTN_EUNSUPPORTED,
+                "plan needs " + std::to_string(static_stats_bytes(p)) + " bytes of statistics, more than the " +
+                    std::to_string(kStaticStatsBytes) +
+                    "-byte static buffer of fp8attn_quantize_noalloc (use fp8attn_quantize)");
   if (p->device < 0) return fail(FP8ATTN_EINVAL, "host-only plan cannot run");
   if (workspace == nullptr || ((uintptr_t)workspace & 255) != 0)
     return fail(FP8ATTN_EWORKSPACE, "workspace must be non-NULL and 256-byte aligned");
-  if (workspace_bytes < p->ws.total) return fail(FP8ATTN_EWORKSPACE, "workspace too small");
+  if (workspace_bytes < (noalloc ? p->ws.stats_off : p->ws.total))
+    return fail(FP8ATTN_EWORKSPACE, "workspace too small");
   if (p->tokens > 0) {
     if (q == nullptr || k == nullptr || v == nullptr) return fail(FP8ATTN_EINVAL, "q, k, v must be non-NULL");
     if (!aligned16(q) || !aligned16(k) || !aligned16(v))
@@ -419,6 +444,14 @@ fp8attn_status fp8attn_quantize(fp8attn_plan_t p, const void* q, const void* k, 
   DeviceGuard g(p->device);
   if (!g.ok) return fail(FP8ATTN_EHIP, "cannot select device");
   uint8_t* ws = static_cast<uint8_t*>(workspace);
+  uint8_t* stats = ws + p->ws.kstat_off;                      // kstat, then amax (E4M3 plans)
+  size_t amax_rel = p->mx ? 0 : p->ws.amax_off - p->ws.kstat_off;
+  if (noalloc) {
+    const hipError_t e = static_stats_buffer(p->device, &stats);
+    if (e != hipSuccess)
+      return fail(FP8ATTN_EHIP, std::string("static statistics buffer: ") + hipGetErrorString(e));
+    if (!p->mx) amax_rel = align_up(sizeof(KStat) * p->chunks.size() * (size_t)p->heads * (size_t)p->head_dim, 256);
+  }
   QuantizeArgs a{};
   a.x[0] = static_cast<const uint16_t*>(q);
   a.x[1] = static_cast<const uint16_t*>(k);
@@ -433,8 +466,8 @@ fp8attn_status fp8attn_quantize(fp8attn_plan_t p, const void* q, const void* k, 
   a.codes[2] = ws + p->ws.v_off;
   a.scales = reinterpret_cast<float*>(ws + p->ws.scale_off);
   a.mu = reinterpret_cast<float*>(ws + p->ws.mu_off);
-  a.kstat = reinterpret_cast<KStat*>(ws + p->ws.kstat_off);
-  a.amax = reinterpret_cast<float*>(ws + p->ws.amax_off);
+  a.kstat = reinterpret_cast<KStat*>(stats);
+  a.amax = reinterpret_cast<float*>(stats + amax_rel);
   a.segs = p->d_segs;
   a.chunks = p->d_chunks;
   a.group_seg = p->d_group_seg;
@@ -462,13 +495,31 @@ fp8attn_status fp8attn_quantize(fp8attn_plan_t p, const void* q, const void* k, 
   return FP8ATTN_OK;
 }
 
+}  // namespace
+
+extern "C" {
+
+fp8attn_status fp8attn_quantize(fp8attn_plan_t p, const void* q, const void* k, const void* v,
+                                const int64_t q_strides[2], const int64_t k_strides[2],
+                                const int64_t v_strides[2], void* workspace, size_t workspace_bytes,
+                                void* stream) {
+  return quantize_impl(p, q, k, v, q_strides, k_strides, v_strides, workspace, workspace_bytes, stream, false);
+}
+
+fp8attn_status fp8attn_quantize_noalloc(fp8attn_plan_t p, const void* q, const void* k, const void* v,
+                                        const int64_t q_strides[2], const int64_t k_strides[2],
+                                        const int64_t v_strides[2], void* workspace, size_t workspace_bytes,
+                                        void* stream) {
+  return quantize_impl(p, q, k, v, q_strides, k_strides, v_strides, workspace, workspace_bytes, stream, true);
+}
+
 fp8attn_status fp8attn_forward(fp8attn_plan_t p, void* workspace, size_t workspace_bytes,
                                void* out, const int64_t out_strides[2], float* lse, void* stream) {
   if (p == nullptr) return fail(FP8ATTN_EINVAL, "plan is NULL");
   if (p->device < 0) return fail(FP8ATTN_EINVAL, "host-only plan cannot run");
   if (workspace == nullptr || ((uintptr_t)workspace & 255) != 0)
     return fail(FP8ATTN_EWORKSPACE, "workspace must be non-NULL and 256-byte aligned");
-  if (workspace_bytes < p->ws.total) return fail(FP8ATTN_EWORKSPACE, "workspace too small");
+  if (workspace_bytes < p->ws.stats_off) return fail(FP8ATTN_EWORKSPACE, "workspace too small");
   if (p->tokens > 0) {
     if (out == nullptr) return fail(FP8ATTN_EINVAL, "out must be non-NULL");
     if (!aligned16(out)) return fail(FP8ATTN_EINVAL, "out must be 16-byte aligned");
@@ -558,6 +609,11 @@ fp8attn_status fp8attn_workspace_region(fp8attn_plan_t p, const void* workspace,
     return FP8ATTN_OK;
   }
   if (ws == nullptr) return fail(FP8ATTN_EWORKSPACE, "workspace is NULL");
+  if (which == FP8ATTN_REGION_STATS) {
+    *ptr_out = ws + p->ws.stats_off;
+    dims_out[0] = (int64_t)(p->ws.total - p->ws.stats_off); dims_out[1] = 1; dims_out[2] = 1;
+    return FP8ATTN_OK;
+  }
   if (p->mx) {
     switch (which) {
       case FP8ATTN_REGION_Q_CODES: *ptr_out = ws + p->ws.q_off; dims_out[0] = H; dims_out[1] = R; dims_out[2] = kMxRow; break;

@@ -76,8 +76,15 @@ struct WorkspaceLayout {
   size_t part_o_off;   // float [npieces][kBM][128]: normalized partial outputs (scaled by s_v)
   size_t part_w_off;   // float [npieces][kBM]: log2 weight of each partial row
   size_t part_lse_off; // float [npieces][kBM]: natural-log LSE of each partial row
+  size_t stats_off;    // start of the statistics (kstat, amax), the last regions
   size_t total;
 };
+
+// Device buffer for the statistics of fp8attn_quantize_noalloc (a static
+// device array of kStaticStatsBytes, one per device); its address on the
+// current device, looked up once per device.
+constexpr size_t kStaticStatsBytes = size_t(16) << 20;
+hipError_t static_stats_buffer(int device, uint8_t** ptr);
 
 struct QuantizeArgs {
   const uint16_t* x[3];      // bf16 Q, K, V

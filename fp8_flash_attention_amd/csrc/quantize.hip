@@ -13,7 +13,39 @@
 // element, the pack pass reads 2 B and writes 1 B per element.
 #include "internal.h"
 
+#include <mutex>
+
 namespace fp8attn {
+
+// Statistics of fp8attn_quantize_noalloc: per (chunk, head, channel) K sums,
+// minima and maxima and the per (chunk, head) amax partials of Q and V, held
+// in this static device array instead of the caller's workspace.  Every device
+// the library runs on holds its own copy until the process ends; each call on
+// a device overwrites every entry it reads, so nothing needs clearing, and
+// calls that overlap on one device race on it.
+static __device__ __align__(256) uint8_t scratch[kStaticStatsBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+uint8_t* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t static_stats_buffer(int device, uint8_t** ptr) {
+  // The array's name is a host-side stand-in; the device address is looked up
+  // once per device, with that device current (the caller makes it current).
+  if (device < 0 || device >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (g_scratch_ptr[device] == nullptr) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[device] = static_cast<uint8_t*>(p);
+  }
+  *ptr = g_scratch_ptr[device];
+  return hipSuccess;
+}
+
 namespace {
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }

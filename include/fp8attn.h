@@ -78,7 +78,12 @@ typedef enum {
                                     4*(32*b + d%32) + d/32 for channel d, keys
                                     32b .. 32b+31 of the tile                        */
   FP8ATTN_REGION_QM_CODES = 9,   /* uint8 [H][rows/128][64]: block-mean operand codes */
-  FP8ATTN_REGION_QM_SCALES = 10  /* uint8 [H][rows/128][4]: its scales (0, 2, 1, 3)   */
+  FP8ATTN_REGION_QM_SCALES = 10, /* uint8 [H][rows/128][4]: its scales (0, 2, 1, 3)   */
+  /* The statistics of fp8attn_quantize, the last bytes of the workspace:
+     dims_out[0] = their size in bytes.  The pointer's offset into the
+     workspace is the size that fp8attn_quantize_noalloc and fp8attn_forward
+     need (they do not touch the statistics).                                 */
+  FP8ATTN_REGION_STATS = 11
 } fp8attn_region;
 
 /*
@@ -203,6 +208,34 @@ fp8attn_status fp8attn_quantize(fp8attn_plan_t plan, const void* q, const void* 
                                 void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * fp8attn_quantize_noalloc - fp8attn_quantize for callers that cannot
+ * allocate (code under HIP graph capture, serving loops, harnesses that forbid
+ * allocation): the same launches and the same codes, scales and means
+ * (bit for bit), but the statistics pass writes its per-chunk partials into a
+ * static device buffer of the library (16 MiB, one per device, held until the
+ * process ends) instead of the workspace's statistics region.
+ *
+ * Arguments as for fp8attn_quantize, except:
+ * workspace_bytes  at least the offset of FP8ATTN_REGION_STATS (the code,
+ *                  scale, mean and partial regions; the statistics region
+ *                  need not exist and is never touched).
+ * Errors as for fp8attn_quantize, plus FP8ATTN_EUNSUPPORTED (checked first,
+ * also for host-only plans) when the plan's statistics exceed the static
+ * buffer: 2 KB per (256-token chunk, head) at head_dim 128 (1 KB at 64) plus
+ * 8 bytes per (chunk, head), e.g. about 8000 chunk-heads at head_dim 128
+ * (30272 tokens x 56 heads need 6664).  It calls no allocator: the buffer's
+ * device address is looked up once per device on the first call there.
+ * Every call on a device shares that device's buffer and overwrites every
+ * entry it reads, so nothing carries over from earlier calls; calls that
+ * overlap on one device (several streams or threads at once) race on it and
+ * must be serialized by the caller.
+ */
+fp8attn_status fp8attn_quantize_noalloc(fp8attn_plan_t plan, const void* q, const void* k,
+                                        const void* v, const int64_t q_strides[2],
+                                        const int64_t k_strides[2], const int64_t v_strides[2],
+                                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * fp8attn_forward - attention over the codes that the last fp8attn_quantize
  * into `workspace` wrote (stream order).
  *
@@ -217,7 +250,9 @@ fp8attn_status fp8attn_quantize(fp8attn_plan_t plan, const void* q, const void* 
  *
  * workspace     the workspace the codes were quantized into.  Forward reads
  *               the code, scale and mean regions and writes only its
- *               partial-output region (used by split work items).
+ *               partial-output region (used by split work items);
+ *               workspace_bytes must reach at least the offset of
+ *               FP8ATTN_REGION_STATS (the statistics are not needed).
  *
  * One attention launch, plus one combine launch when the plan splits work
  * items along the keys (fp8attn_plan_work_items shows the split; it happens

@@ -421,3 +421,23 @@ def test_head_dim_64_plan_layout():
     assert p.work_items() == p128.work_items()
     with pytest.raises(ValueError):
         fa.Plan(300, 2, [0, 300], device=-1, head_dim=96)
+
+
+def test_quantize_noalloc_rejects_plans_beyond_its_static_buffer():
+    # checked before anything else, so a host-only plan shows it without a GPU
+    L = _lib.lib()
+    big = fa.Plan(320_037, 56, [0, 320_037], device=-1)
+    rc = L.fp8attn_quantize_noalloc(big.handle, None, None, None, None, None, None, None, 0, None)
+    assert rc == _lib.EUNSUPPORTED and b"static buffer" in L.fp8attn_last_error()
+    # a plan whose statistics fit gets past that check (and stops at the host-only one)
+    small = fa.Plan(30272, 56, [0, 15104, 30208, 30208, 30271, 30272], device=-1)
+    rc = L.fp8attn_quantize_noalloc(small.handle, None, None, None, None, None, None, None, 0, None)
+    assert rc == _lib.EINVAL and b"host-only" in L.fp8attn_last_error()
+
+
+def test_statistics_region_is_last():
+    # fp8attn_quantize_noalloc and fp8attn_forward need only the bytes before it
+    for flags in ({}, {"fmt": "mxfp4"}, {"segment_scales": True}, {"head_dim": 64}):
+        p = fa.Plan(4096, 8, [0, 1000, 4096], device=-1, **flags)
+        off = p.stats_offset()
+        assert 0 < off < p.workspace_bytes and off % 256 == 0
