@@ -26,6 +26,7 @@ from __future__ import annotations
 
 import ctypes
 import math
+from collections import OrderedDict
 from typing import Dict, Optional, Sequence, Tuple
 
 import torch
@@ -36,8 +37,8 @@ from ._lib import Fp8AttnError  # noqa: F401
 HEAD_DIM = 128
 DEFAULT_SCALE = 1.0 / math.sqrt(HEAD_DIM)
 
-__all__ = ["Plan", "quantize", "quantize_noalloc", "forward", "attention", "Fp8AttnError", "HEAD_DIM",
-           "DEFAULT_SCALE"]
+__all__ = ["Plan", "quantize", "quantize_noalloc", "forward", "attention", "get_plan", "clear_plan_cache",
+           "Fp8AttnError", "HEAD_DIM", "DEFAULT_SCALE"]
 
 
 def _stream_handle(device: torch.device, stream=None) -> ctypes.c_void_p:
@@ -95,6 +96,7 @@ class Plan:
                                      ctypes.c_float(self.softmax_scale), self.device_index, flags),
                    "fp8attn_plan_ex")
         self._h = h
+        self._used = False          # set once work has been enqueued with this plan
         self.workspace_bytes = int(L.fp8attn_workspace_bytes(h))
 
     @property
@@ -152,7 +154,11 @@ class Plan:
         return int(ptr.value - base)
 
     def close(self):
+        """Free the plan.  Work enqueued with it must be complete first (its device
+        tables are freed), so a plan that has run waits for its device."""
         if self._h is not None:
+            if self._used and self.device_index >= 0:
+                torch.cuda.synchronize(self.device_index)
             _lib.lib().fp8attn_plan_destroy(self._h)
             self._h = None
 
@@ -192,6 +198,7 @@ def quantize(plan: Plan, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, work
     D = plan.head_dim
     qs, ks, vs = _strides(q, "q", D), _strides(k, "k", D), _strides(v, "v", D)
     st = _stream_handle(plan.device, stream)
+    plan._used = True
     _lib.check(_lib.lib().fp8attn_quantize(plan.handle, ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k.data_ptr()),
                                            ctypes.c_void_p(v.data_ptr()), qs, ks, vs,
                                            ctypes.c_void_p(workspace.data_ptr()),
@@ -211,6 +218,7 @@ def quantize_noalloc(plan: Plan, q: torch.Tensor, k: torch.Tensor, v: torch.Tens
     D = plan.head_dim
     qs, ks, vs = _strides(q, "q", D), _strides(k, "k", D), _strides(v, "v", D)
     st = _stream_handle(plan.device, stream)
+    plan._used = True
     _lib.check(_lib.lib().fp8attn_quantize_noalloc(plan.handle, ctypes.c_void_p(q.data_ptr()),
                                                    ctypes.c_void_p(k.data_ptr()), ctypes.c_void_p(v.data_ptr()),
                                                    qs, ks, vs, ctypes.c_void_p(workspace.data_ptr()),
@@ -235,28 +243,47 @@ def forward(plan: Plan, workspace: torch.Tensor, out: Optional[torch.Tensor] = N
         _on_plan_device(plan, lse, "lse")
         lse_ptr = ctypes.c_void_p(lse.data_ptr())
     st = _stream_handle(plan.device, stream)
+    plan._used = True
     _lib.check(_lib.lib().fp8attn_forward(plan.handle, ctypes.c_void_p(workspace.data_ptr()),
                                           workspace.numel() * workspace.element_size(),
                                           ctypes.c_void_p(out.data_ptr()), os_, lse_ptr, st), "fp8attn_forward")
     return out
 
 
-_PLANS: Dict[Tuple, Plan] = {}
+# Plans of attention(), least recently used first.  The FlashInfer page caches
+# its segment plan per (cu_seqlens, heads, device); the review of the sglang
+# PR "[diffusion] attention: add fp8_fa_sm120 FP8 backend for SM120 GPUs" asks
+# that retained state stay bounded across shapes, so the cache holds at most
+# PLAN_CACHE_SIZE plans (a few hundred KB of device tables each at most) and
+# evicts the least recently used one.
+PLAN_CACHE_SIZE = 16
+_PLANS: "OrderedDict[Tuple, Plan]" = OrderedDict()
 
 
 def get_plan(tokens: int, heads: int, cu_seqlens: Sequence[int], softmax_scale: float, device: int,
              segment_scales: bool = False, fmt: str = "e4m3", q_centre: bool = False, causal: bool = False,
              head_dim: int = HEAD_DIM) -> Plan:
-    """Plans are cached per (cu_seqlens, heads, scale, device, quantization mode), as the FlashInfer
-    page caches its segment plan per (cu_seqlens, heads, device).  A plan holds only small tables."""
+    """The cached plan for (cu_seqlens, heads, scale, device, quantization mode), built on first use."""
     key = (tuple(int(x) for x in cu_seqlens), int(heads), float(softmax_scale), int(device), bool(segment_scales),
            fmt, bool(q_centre), bool(causal), int(head_dim))
     p = _PLANS.get(key)
-    if p is None:
-        p = Plan(tokens, heads, cu_seqlens, softmax_scale, device, segment_scales=segment_scales, fmt=fmt,
-                 q_centre=q_centre, causal=causal, head_dim=head_dim)
-        _PLANS[key] = p
+    if p is not None:
+        _PLANS.move_to_end(key)
+        return p
+    p = Plan(tokens, heads, cu_seqlens, softmax_scale, device, segment_scales=segment_scales, fmt=fmt,
+             q_centre=q_centre, causal=causal, head_dim=head_dim)
+    _PLANS[key] = p
+    while len(_PLANS) > max(1, PLAN_CACHE_SIZE):
+        _, old = _PLANS.popitem(last=False)
+        old.close()               # waits for the device if the plan has run
     return p
+
+
+def clear_plan_cache() -> None:
+    """Free every cached plan (each waits for its device if it has run)."""
+    while _PLANS:
+        _, p = _PLANS.popitem(last=False)
+        p.close()
 
 
 def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: Optional[Sequence[int]] = None,

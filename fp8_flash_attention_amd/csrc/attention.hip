@@ -81,9 +81,8 @@ constexpr float kLog2Max = 8.807354922057604f;   // log2(448), the largest E4M3 
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kSlots = 4;                        // ring slots per operand
 constexpr int kBarEvery = kSlots / 2;            // iterations per barrier
-constexpr int kWavesWG = kBM / 32;               // waves per workgroup, 32 queries each
 constexpr int kBufferFlags = 0x00020000;         // raw buffer descriptor word 3 (gfx9 family)
-static_assert((kBM == 128 || kBM == 256) && kBN == 64, "4 or 8 waves x 32 queries, 64-key tiles");
+static_assert(kBN == 64, "64-key tiles");
 
 __device__ __forceinline__ v16f mfma_fp8(const v8i& a, const v8i& b, const v16f& c) {
   // cbsz = blgp = 0 selects E4M3 for both operands; zero scales select the
@@ -182,8 +181,12 @@ __device__ __forceinline__ void tail_iters(F& iter, int& t, int nkt) {
   }
 }
 
-template <bool LSE, bool CAUSAL, int D>
-__global__ __launch_bounds__(64 * kWavesWG, 8 / kWavesWG) void k_attn(AttentionArgs a) {
+// BM queries per work item (256: one 8-wave workgroup per CU; 128: two 4-wave
+// workgroups per CU), D channels per head.
+template <bool LSE, bool CAUSAL, int D, int BM>
+__global__ __launch_bounds__(2 * BM, 256 / BM) void k_attn(AttentionArgs a) {
+  constexpr int kWavesWG = BM / 32;              // waves per workgroup, 32 queries each
+  static_assert(BM == 128 || BM == 256, "4 or 8 waves x 32 queries");
   constexpr int kTile = kBN * D;                 // bytes of one K (or V^T) tile
   constexpr int kVRing = kSlots * kTile;         // V ring follows the K ring in LDS
   constexpr int NH = D / 64;                     // 64-channel halves of Q and K
@@ -204,7 +207,7 @@ __global__ __launch_bounds__(64 * kWavesWG, 8 / kWavesWG) void k_attn(AttentionA
   const int L = si.len;
   // Key range: every tile of the segment (causal: up to the item's last
   // query), or one piece of a split item.
-  const int nkt_seg = ((CAUSAL ? min(L, q0 + kBM) : L) + kBN - 1) / kBN;
+  const int nkt_seg = ((CAUSAL ? min(L, q0 + BM) : L) + kBN - 1) / kBN;
   int kt0 = 0, nkt = nkt_seg, slot = -1;
   if (it.w != 0) {
     const int n = split_pieces(it.w), i = split_index(it.w);
@@ -667,7 +670,7 @@ __global__ __launch_bounds__(64 * kWavesWG, 8 / kWavesWG) void k_attn(AttentionA
     // maximum of the piece's first tile, so some probability is >= 112 and
     // lt > 0; a zero sum would still give weight 0 (w = -inf) and O = 0.
     if (qrow < L) {
-      const int prow = slot * kBM + 32 * wave + lq;
+      const int prow = slot * kPartRows + 32 * wave + lq;
       const float inv = lt > 0.f ? s_v / lt : 0.f;
       float* orow = a.part_o + (size_t)prow * D;
 #pragma unroll
@@ -701,7 +704,7 @@ __global__ __launch_bounds__(64 * kWavesWG, 8 / kWavesWG) void k_attn(AttentionA
       const float lse2 = __log2f(le) - nb;
       const float v = lse2 * kLn2 + a.softmax_scale * s_q * qmu;
       if (slot >= 0)
-        a.part_lse[slot * kBM + 32 * wave + lq] = v;
+        a.part_lse[slot * kPartRows + 32 * wave + lq] = v;
       else
         a.lse[(int64_t)h * a.tokens + si.start + qrow] = v;
     }
@@ -731,7 +734,7 @@ __global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
 #pragma unroll
   for (int i = 0; i < kMaxSplit; i++)
     if (i < n) {
-      w[i] = a.part_w[(slot0 + i) * kBM + r];
+      w[i] = a.part_w[(slot0 + i) * kPartRows + r];
       m = __builtin_fmaxf(m, w[i]);
     }
   // a piece of zero weight has w = -inf and contributes nothing; if every
@@ -746,7 +749,7 @@ __global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
     if (i < n) {
       const float alpha = __builtin_amdgcn_exp2f(w[i] - m);
       den += alpha;
-      const float4* src = reinterpret_cast<const float4*>(a.part_o + ((size_t)(slot0 + i) * kBM + r) * D + HD * half);
+      const float4* src = reinterpret_cast<const float4*>(a.part_o + ((size_t)(slot0 + i) * kPartRows + r) * D + HD * half);
 #pragma unroll
       for (int j = 0; j < HD / 4; j++) {
         const float4 v = src[j];
@@ -772,7 +775,7 @@ __global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
 #pragma unroll
     for (int i = 0; i < kMaxSplit; i++)
       if (i < n) {
-        lv[i] = a.part_lse[(slot0 + i) * kBM + r];
+        lv[i] = a.part_lse[(slot0 + i) * kPartRows + r];
         lm = __builtin_fmaxf(lm, lv[i]);
       }
     float se = 0.f;
@@ -790,33 +793,35 @@ __global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
 hipError_t launch_combine(const CombineArgs& a, hipStream_t stream) {
   if (a.nitems == 0) return hipSuccess;
   if (a.head_dim == 64)
-    hipLaunchKernelGGL(k_combine<64>, dim3(a.nitems, kBM / 128), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(k_combine<64>, dim3(a.nitems, a.bm / 128), dim3(256), 0, stream, a);
   else
-    hipLaunchKernelGGL(k_combine<kHeadDim>, dim3(a.nitems, kBM / 128), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(k_combine<kHeadDim>, dim3(a.nitems, a.bm / 128), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
-template <int D>
+template <int D, int BM>
 void launch_attention_d(const AttentionArgs& a, hipStream_t stream) {
-  const dim3 g(a.nitems), b(64 * kWavesWG);
+  const dim3 g(a.nitems), b(2 * BM);
   if (a.causal) {
     if (a.lse != nullptr)
-      hipLaunchKernelGGL((k_attn<true, true, D>), g, b, 0, stream, a);
+      hipLaunchKernelGGL((k_attn<true, true, D, BM>), g, b, 0, stream, a);
     else
-      hipLaunchKernelGGL((k_attn<false, true, D>), g, b, 0, stream, a);
+      hipLaunchKernelGGL((k_attn<false, true, D, BM>), g, b, 0, stream, a);
   } else if (a.lse != nullptr) {
-    hipLaunchKernelGGL((k_attn<true, false, D>), g, b, 0, stream, a);
+    hipLaunchKernelGGL((k_attn<true, false, D, BM>), g, b, 0, stream, a);
   } else {
-    hipLaunchKernelGGL((k_attn<false, false, D>), g, b, 0, stream, a);
+    hipLaunchKernelGGL((k_attn<false, false, D, BM>), g, b, 0, stream, a);
   }
 }
 
 hipError_t launch_attention(const AttentionArgs& a, hipStream_t stream) {
   if (a.nitems == 0) return hipSuccess;
   if (a.head_dim == 64)
-    launch_attention_d<64>(a, stream);
+    launch_attention_d<64, 256>(a, stream);      // 64 channels: 256-query items only
+  else if (a.bm == 128)
+    launch_attention_d<kHeadDim, 128>(a, stream);
   else
-    launch_attention_d<kHeadDim>(a, stream);
+    launch_attention_d<kHeadDim, 256>(a, stream);
   return hipGetLastError();
 }
 

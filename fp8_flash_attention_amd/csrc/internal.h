@@ -13,13 +13,10 @@ constexpr int kRowPad = 128;     // workspace rows of a segment are padded to th
 constexpr int kGuardRows = 128;  // zero rows after the last segment
 constexpr int kStatChunk = 256;  // tokens per stats chunk; fixes the K-mean summation order
 constexpr int kPackRows = 64;    // workspace rows per pack block (one V key group)
-#ifndef FP8ATTN_BM
-#define FP8ATTN_BM 256
-#endif
-constexpr int kBM = FP8ATTN_BM;  // queries per attention work item (one wave per 32)
+constexpr int kBM = 256;         // queries per E4M3 work item (one wave per 32); 128 for plans with few rounds
+constexpr int kPartRows = 256;   // rows of one partial-output slot (the largest query tile)
 constexpr int kBN = 64;          // keys per inner tile
 constexpr int kNumXcd = 8;       // MI355X: workgroups are dealt round-robin to 8 XCDs
-constexpr int kWgPerCu = kBM == 256 ? 1 : 2;   // attention workgroups resident per CU (registers and LDS)
 constexpr int kMaxSplit = 8;     // key pieces of one split work item, at most
 constexpr int kMinPieceTiles = 8;  // key tiles of one piece, at least
 
@@ -73,9 +70,9 @@ struct WorkspaceLayout {
   // V^T scales [H][rows/64][256] (tile-major, byte (32*(key/32) + d%32)*4 + d/32);
   // block-mean codes [H][rows/128][64] and scales [H][rows/128][4] (order 0, 2, 1, 3)
   size_t qs_off, ks_off, vs_off, qm_off, qms_off;
-  size_t part_o_off;   // float [npieces][kBM][128]: normalized partial outputs (scaled by s_v)
-  size_t part_w_off;   // float [npieces][kBM]: log2 weight of each partial row
-  size_t part_lse_off; // float [npieces][kBM]: natural-log LSE of each partial row
+  size_t part_o_off;   // float [npieces][kPartRows][128]: normalized partial outputs (scaled by s_v)
+  size_t part_w_off;   // float [npieces][kPartRows]: log2 weight of each partial row
+  size_t part_lse_off; // float [npieces][kPartRows]: natural-log LSE of each partial row
   size_t stats_off;    // start of the statistics (kstat, amax), the last regions
   size_t total;
 };
@@ -131,6 +128,7 @@ struct AttentionArgs {
   int32_t nscale;            // S: scale sets (segments with per-segment scales, else 1)
   int32_t causal;            // 1: query i of a segment attends keys j <= i only
   int32_t head_dim;          // D: 128 or 64
+  int32_t bm;                // queries per work item: 256, or 128 (D = 128 only)
   float softmax_scale;
 };
 
@@ -146,6 +144,7 @@ struct CombineArgs {
   float* lse;                // nullable, [H][T]
   int64_t tokens;
   int32_t head_dim;          // D: 128 or 64
+  int32_t bm;                // queries per split item (128 or 256)
 };
 
 // FP4 attention: codes and block scales as in WorkspaceLayout.

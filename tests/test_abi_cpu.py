@@ -189,18 +189,19 @@ def test_split_fills_the_last_round(name):
             assert len(pieces) == r * n and {_split(it[3])[1] for it in pieces} == {n}
 
 
-@pytest.mark.parametrize("name,split_items,pieces_each", [
-    ("s256_h2", 0, 0),
-    ("s4096_h56", 128, 2),            # last round of exactly half the CUs of each XCD: split
-    ("s20440_h56_strided", 128, 2),   # likewise
-    ("s30272_h56_koffset", 8, 8),     # one item left per XCD: eight pieces
-    ("varlen_30272_h56", 0, 0),
+@pytest.mark.parametrize("name,query_tile,split_items,pieces_each", [
+    ("s256_h2", 128, 0, 0),               # a few rounds deep: 128-query items
+    ("s4096_h56", 128, 0, 0),             # 3.5 rounds of 256-query items: 128-query items, 7 full rounds
+    ("s20440_h56_strided", 256, 128, 2),  # last round of exactly half the CUs of each XCD: split
+    ("s30272_h56_koffset", 256, 8, 8),    # one item left per XCD: eight pieces
+    ("varlen_30272_h56", 256, 0, 0),
 ])
-def test_graded_workloads_split_counts(name, split_items, pieces_each):
-    # the split schedule of each graded workload on a 256-CU device, as stated
-    # in the design notes
+def test_graded_workloads_split_counts(name, query_tile, split_items, pieces_each):
+    # the query tile and split schedule of each graded workload on a 256-CU
+    # device, as stated in the design notes
     w = WORKLOADS[name]
     p = fa.Plan(w.tokens, w.heads, w.cu_seqlens, device=-1)
+    assert p.info()["query_tile"] == query_tile
     pieces = [it for it in p.work_items() if it[0] >= 0 and it[3]]
     items = {(it[0], it[1], it[2]) for it in pieces}
     assert len(items) == split_items
@@ -345,7 +346,7 @@ def test_mxfp4_plan_never_splits():
         T = cu[-1]
         e4 = fa.Plan(T, 56, cu, device=-1)
         mx = fa.Plan(T, 56, cu, device=-1, fmt="mxfp4")
-        assert mx.info()["query_tile"] == 128 and e4.info()["query_tile"] == 256
+        assert mx.info()["query_tile"] == 128 and e4.info()["query_tile"] in (128, 256)
         items = mx.work_items()
         assert all(it[3] == 0 for it in items)
         real = [it for it in items if it[0] >= 0]
@@ -418,7 +419,12 @@ def test_head_dim_64_plan_layout():
         assert L.fp8attn_workspace_region(p.handle, ctypes.c_void_p(1 << 20), which, ctypes.byref(ptr), dims) == 0
         assert tuple(dims) == shape
     assert p.workspace_bytes < p128.workspace_bytes
-    assert p.work_items() == p128.work_items()
+    # 64-channel plans always run 256-query items (the 128-channel plan of this
+    # shallow grid runs 128-query ones)
+    assert p.info()["query_tile"] == 256 and p128.info()["query_tile"] == 128
+    real = {it for it in p.work_items() if it[0] >= 0}
+    assert real == {(s, q0, h, 0) for h in range(2) for s, (a, b) in enumerate([(0, 100), (100, 300)])
+                    for q0 in range(0, b - a, 256)}
     with pytest.raises(ValueError):
         fa.Plan(300, 2, [0, 300], device=-1, head_dim=96)
 
@@ -441,3 +447,20 @@ def test_statistics_region_is_last():
         p = fa.Plan(4096, 8, [0, 1000, 4096], device=-1, **flags)
         off = p.stats_offset()
         assert 0 < off < p.workspace_bytes and off % 256 == 0
+
+
+def test_plan_cache_is_bounded_and_lru():
+    # host-only plans: the cache keeps at most PLAN_CACHE_SIZE plans, evicts the least
+    # recently used one and frees it
+    fa.clear_plan_cache()
+    n = fa.PLAN_CACHE_SIZE
+    made = [fa.get_plan(100 + i, 2, [0, 100 + i], 0.1, -1) for i in range(n)]
+    assert len(fa._PLANS) == n
+    again = fa.get_plan(100, 2, [0, 100], 0.1, -1)          # a hit moves it to the back
+    assert again is made[0]
+    extra = [fa.get_plan(1000 + i, 2, [0, 1000 + i], 0.1, -1) for i in range(n + 3)]
+    assert len(fa._PLANS) == n
+    assert all(p.handle is None for p in made)              # evicted and destroyed
+    assert all(p.handle is not None for p in extra[-n:])
+    fa.clear_plan_cache()
+    assert not fa._PLANS and all(p.handle is None for p in extra)
