@@ -145,9 +145,13 @@ class ClockSampler:
     def summary(self):
         if not self.samples:
             return {"samples": 0, "error": self.error}
-        v = sorted(self.samples)
+        # samples taken while the GPU idled (before the first launch, between
+        # repetitions) read the idle clock: keep those above half the highest
+        top = max(self.samples)
+        v = sorted(x for x in self.samples if x >= 0.5 * top)
         pct = lambda f: round(v[min(len(v) - 1, int(f * len(v)))], 0)   # noqa: E731
         return {"median_mhz": pct(0.5), "p05_mhz": pct(0.05), "p95_mhz": pct(0.95), "samples": len(v),
+                "idle_samples_dropped": len(self.samples) - len(v),
                 "source": "amdsmi gpu_metrics current_gfxclks (mean over XCDs), sampled every 5 ms"}
 
 
