@@ -50,6 +50,14 @@ power-of-two scale per 32 elements, and this variant is built on that):
    log2 6) and phat_ij = 2^E * e2m1(2^(x_ij - E)).  phat depends on x alone, not
    on any running reference (the kernel's references are whole powers of two).
 7. out_i = sum_j phat_ij Vhat_j / sum_j phat_ij.
+8. Causal (``causal=True``; the E4M3 path's reading): query i of a segment
+   sees the keys j <= i of it; its probability blocks are the key blocks of
+   reading 1 cut at the last visible key (the last block holds the visible
+   keys only).
+9. LSE (``lse_mxfp4_rows``): the natural-log log-sum-exp of the uncentred
+   scores over the row's visible keys from the dequantized operands:
+   ln 2 * (log2 sum_j 2^(x_ij) + (Qhat_i + QMhat_i) . mu), the second term
+   adding back what centring K by its segment mean mu took out.
 
 Parity pins live in ``tests/test_oracle_mxfp4.py``.
 """
@@ -256,8 +264,8 @@ def quantize_probs(x: np.ndarray) -> np.ndarray:
     return p.reshape(xp.shape)[..., :L]
 
 
-def attention_from_operands(Q, QM, K, V, cu_seqlens: Sequence[int]) -> np.ndarray:
-    """Readings 5-7 on dequantized float64 operands [T, H, D] (scores
+def attention_from_operands(Q, QM, K, V, cu_seqlens: Sequence[int], causal: bool = False) -> np.ndarray:
+    """Readings 5-8 on dequantized float64 operands [T, H, D] (scores
     x = Q.K + QM.K in log2 units).  Returns float64 [T, H, D]."""
     Q, QM, K, V = (np.asarray(t, np.float64) for t in (Q, QM, K, V))
     T, H, D = Q.shape
@@ -270,32 +278,59 @@ def attention_from_operands(Q, QM, K, V, cu_seqlens: Sequence[int]) -> np.ndarra
         for h in range(H):
             Kh = K[a:b, h]                                   # [L, D]
             x = Q[a:b, h] @ Kh.T + QM[a:b, h] @ Kh.T         # [L, L]
+            if causal:
+                for i in range(b - a):                       # row i sees keys 0 .. i
+                    p = quantize_probs(x[i, :i + 1])
+                    out[a + i, h] = (p @ V[a:a + i + 1, h]) / p.sum()
+                continue
             p = quantize_probs(x)
             out[a:b, h] = (p @ V[a:b, h]) / p.sum(axis=1, keepdims=True)
     return out
 
 
 def attention_mxfp4(q, k, v, cu_seqlens: Sequence[int], softmax_scale: float,
-                    q_centre: bool = True) -> np.ndarray:
-    """The whole variant: quantize, then readings 5-7.  float64 [T, H, D]."""
+                    q_centre: bool = True, causal: bool = False) -> np.ndarray:
+    """The whole variant: quantize, then readings 5-8.  float64 [T, H, D]."""
     z = quantize_mxfp4(q, k, v, cu_seqlens, softmax_scale, q_centre)
     ops = dequantized_operands(z, cu_seqlens)
-    return attention_from_operands(ops["Q"], ops["QM"], ops["K"], ops["V"], cu_seqlens)
+    return attention_from_operands(ops["Q"], ops["QM"], ops["K"], ops["V"], cu_seqlens, causal)
+
+
+def _row_keys(cu: List[int], r: int, causal: bool):
+    s = int(np.searchsorted(cu, r, side="right")) - 1
+    return s, cu[s], (r + 1 if causal else cu[s + 1])
 
 
 def attention_mxfp4_rows(z: Dict[str, np.ndarray], cu_seqlens: Sequence[int],
-                         rows: Sequence[int], heads: Sequence[int]) -> np.ndarray:
-    """Selected output rows and heads of readings 5-7 from quantized operands
+                         rows: Sequence[int], heads: Sequence[int], causal: bool = False) -> np.ndarray:
+    """Selected output rows and heads of readings 5-8 from quantized operands
     ``z`` (each row against its own segment).  float64 [len(rows), len(heads), D]."""
     cu = list(cu_seqlens)
     ops = dequantized_operands(z, cu)
     out = np.zeros((len(rows), len(heads), ops["Q"].shape[2]), np.float64)
     for n, r in enumerate(rows):
-        s = int(np.searchsorted(cu, r, side="right")) - 1
-        a, b = cu[s], cu[s + 1]
+        _, a, e = _row_keys(cu, r, causal)
         for m, h in enumerate(heads):
-            Kh = ops["K"][a:b, h]
+            Kh = ops["K"][a:e, h]
             x = Kh @ ops["Q"][r, h] + Kh @ ops["QM"][r, h]
             p = quantize_probs(x)
-            out[n, m] = (p @ ops["V"][a:b, h]) / p.sum()
+            out[n, m] = (p @ ops["V"][a:e, h]) / p.sum()
+    return out
+
+
+def lse_mxfp4_rows(z: Dict[str, np.ndarray], cu_seqlens: Sequence[int],
+                   rows: Sequence[int], heads: Sequence[int], causal: bool = False) -> np.ndarray:
+    """Reading 9: natural-log LSE of the uncentred scores per (row, head) from
+    the dequantized operands of ``z``.  float64 [len(rows), len(heads)]."""
+    cu = list(cu_seqlens)
+    ops = dequantized_operands(z, cu)
+    out = np.zeros((len(rows), len(heads)), np.float64)
+    for n, r in enumerate(rows):
+        s, a, e = _row_keys(cu, r, causal)
+        for m, h in enumerate(heads):
+            qop = ops["Q"][r, h] + ops["QM"][r, h]
+            x = ops["K"][a:e, h] @ qop
+            mx = x.max()
+            lse2 = mx + np.log2(np.sum(np.exp2(x - mx))) + qop @ z["mu"][s, h].astype(np.float64)
+            out[n, m] = lse2 * np.log(2.0)
     return out

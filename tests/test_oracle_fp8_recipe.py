@@ -29,6 +29,7 @@ import torch
 
 from oracle import attention as A
 from oracle import compare
+from oracle import e4m3
 from oracle import quantize as Qz
 from tests.cases import CAUSAL_CASES, FEW_KEYS, random_varlen, visible_keys
 from workloads import generate, make_workload, sample_rows
@@ -140,3 +141,43 @@ def test_operands_alone_exceed_the_rel_rms_bar_at_1e5_keys():
     ref = A.attention_rows(q, k, v, CU, 0.125, rows).numpy()
     diag = A.attention_rows(dq, dk, dv, CU, 0.125, rows).numpy()
     assert compare.rel_rms(diag, ref) > compare.REL_RMS_BAR
+
+
+def _qdq_per_head(x: np.ndarray) -> np.ndarray:
+    """E4M3 round trip with one amax/448 scale per head (axis 1), as the quantizer does."""
+    s = (np.abs(x).max(axis=(0, 2)) / np.float32(448)).astype(np.float32)
+    return e4m3.decode(e4m3.encode(x / s[None, :, None])) * s[None, :, None]
+
+
+def test_q_block_mean_centring_gains_little_for_e4m3():
+    # Why E4M3 plans take no Q centring: on Q with a per-channel offset of
+    # variance 2, subtracting the 128-row block mean and quantizing the mean
+    # as a second E4M3 operand (the FP4 variant's add-back) leaves the FP8
+    # recipe's error where it was, since E4M3's error is relative and the
+    # quantized mean carries the offset's error; only a mean term kept exact
+    # (a per-key term in FP32, one more vector addition per score) helps.
+    import math
+    T, H = 2048, 2
+    w = make_workload("q_offset", T, H, [0, T], seed=77, k_offset_var=2.0)
+    q, k, v = generate(w)
+    g = torch.Generator().manual_seed(5)
+    q = (q.float() + math.sqrt(2.0) * torch.randn((H, 128), generator=g)[None]).to(torch.bfloat16)
+    ref = A.attention(q, k, v, w.cu_seqlens, w.softmax_scale).numpy()
+    r = Qz.quantize(q, k, v, w.cu_seqlens, w.softmax_scale)
+    dq, dk, dv = (Qz.dequantize(r[n], r["scales"][i]) for i, n in enumerate(("q_codes", "k_codes", "v_codes")))
+    rows = list(range(0, T, 8))
+
+    def err(qop):
+        o = A.attention_fp8_recipe(qop, dk, dv, w.cu_seqlens, w.softmax_scale, rows=rows).numpy()
+        return compare.rel_rms(o, ref[rows])
+
+    qf = q.float().numpy().astype(np.float64)
+    qm = np.zeros_like(qf)
+    for b0 in range(0, T, 128):
+        qm[b0:b0 + 128] = qf[b0:b0 + 128].mean(axis=0, keepdims=True).astype(np.float32)
+    qc = (qf - qm).astype(np.float32)
+    plain = err(dq)
+    centred_quantized_mean = err(_qdq_per_head(qc) + _qdq_per_head(qm.astype(np.float32)))
+    centred_exact_mean = err(_qdq_per_head(qc) + qm)
+    assert abs(centred_quantized_mean - plain) <= 0.05 * plain
+    assert centred_exact_mean <= 0.92 * plain

@@ -266,3 +266,57 @@ def test_fp4_error_is_bounded_on_gaussian_inputs():
     assert np.all(np.abs(got - want) <= 1.0 + 0.1 * np.abs(want))
     rel = np.linalg.norm(got - want) / np.linalg.norm(want)
     assert 0.1 < rel < 0.35
+
+
+# ----------------------------------------------------------------- causal, LSE
+
+@pytest.mark.parametrize("q_centre", [True, False])
+def test_causal_lossless_inputs_reduce_to_plain_causal_softmax(q_centre):
+    # reading 8: every row's visible scores keep the lossless property, so the
+    # causal variant equals the float64 causal softmax attention
+    cu = [0, 256, 384]
+    q, k, v = _lossless_inputs(cu, 2, seed=19)
+    got = mxfp4.attention_mxfp4(q, k, v, cu, SIGMA_C8, q_centre=q_centre, causal=True)
+    want = exact.attention(q, k, v, cu, SIGMA_C8, causal=True).numpy()
+    np.testing.assert_allclose(got, want, rtol=1e-8, atol=1e-8)
+    z = mxfp4.quantize_mxfp4(q, k, v, cu, SIGMA_C8, q_centre=q_centre)
+    rows = [0, 1, 31, 32, 33, 255, 256, 300, 383]
+    np.testing.assert_allclose(mxfp4.attention_mxfp4_rows(z, cu, rows, [0, 1], causal=True), got[rows],
+                               rtol=1e-12, atol=1e-12)
+
+
+def test_causal_off_by_one_fails_the_lossless_pin(monkeypatch):
+    """Planted mistake: each query also sees the next key."""
+    cu = [0, 256]
+    q, k, v = _lossless_inputs(cu, 1, seed=20)
+    want = exact.attention(q, k, v, cu, SIGMA_C8, causal=True).numpy()
+    real = mxfp4._row_keys
+    monkeypatch.setattr(mxfp4, "_row_keys", lambda c, r, causal: (lambda s, a, e: (s, a, min(e + 1, c[s + 1])))(
+        *real(c, r, causal)))
+    z = mxfp4.quantize_mxfp4(q, k, v, cu, SIGMA_C8)
+    bad = mxfp4.attention_mxfp4_rows(z, cu, list(range(256)), [0], causal=True)
+    assert np.abs(bad - want).max() > 0.1
+
+
+@pytest.mark.parametrize("q_centre,causal", [(True, False), (False, False), (True, True)])
+def test_lse_lossless_inputs_equal_the_float64_lse(q_centre, causal):
+    # reading 9: with every operand exact, the LSE of the dequantized operands
+    # (centred keys plus the q . mu term) is the float64 LSE of the inputs
+    cu = [0, 256, 384]
+    q, k, v = _lossless_inputs(cu, 2, seed=21)
+    z = mxfp4.quantize_mxfp4(q, k, v, cu, SIGMA_C8, q_centre=q_centre)
+    rows = list(range(0, 384, 7)) + [255, 256, 383]
+    got = mxfp4.lse_mxfp4_rows(z, cu, rows, [0, 1], causal=causal)
+    want = exact.lse_rows(q, k, cu, SIGMA_C8, rows=rows, causal=causal).numpy()
+    np.testing.assert_allclose(got, want, rtol=1e-8, atol=1e-7)
+
+
+def test_lse_without_the_mean_term_fails(monkeypatch):
+    """Planted mistake: the LSE of the centred scores only (q . mu dropped)."""
+    cu = [0, 256]
+    q, k, v = _lossless_inputs(cu, 2, seed=22)
+    z = mxfp4.quantize_mxfp4(q, k, v, cu, SIGMA_C8)
+    want = exact.lse_rows(q, k, cu, SIGMA_C8, rows=list(range(0, 256, 5))).numpy()
+    z0 = dict(z, mu=np.zeros_like(z["mu"]))
+    bad = mxfp4.lse_mxfp4_rows(z0, cu, list(range(0, 256, 5)), [0, 1])
+    assert np.abs(bad - want).max() > 0.1
