@@ -217,6 +217,8 @@ def main() -> int:
     ap.add_argument("--fmt", choices=("e4m3", "mxfp4"), default="e4m3",
                     help="operand format: the E4M3 path (default) or the block-scaled FP4 variant")
     ap.add_argument("--q-centre", action="store_true", help="mxfp4: centre Q by its 128-row block means")
+    ap.add_argument("--exact-probs", action="store_true",
+                    help="e4m3: probabilities rounded from the FP32 exp2 instead of the log-linear code")
     ap.add_argument("--causal", action="store_true",
                     help="e4m3: causal plan (FLOPs then count the visible pairs, 2 * sum L(L+1) * H * D)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
@@ -240,7 +242,8 @@ def main() -> int:
     q, k, v = generate(w, device="cuda")
     mx = args.fmt == "mxfp4"
     plan = fa.Plan(w.tokens, w.heads, w.cu_seqlens, w.softmax_scale, device=0, fmt=args.fmt,
-                   q_centre=mx and args.q_centre, causal=args.causal, head_dim=w.head_dim)
+                   q_centre=mx and args.q_centre, causal=args.causal, head_dim=w.head_dim,
+                   exact_probs=args.exact_probs and not mx)
     ws = plan.new_workspace()
     out = torch.empty((w.tokens, w.heads, w.head_dim), dtype=torch.bfloat16, device=dev)
     stream = torch.cuda.current_stream(dev)
@@ -301,7 +304,8 @@ def main() -> int:
 
     peak = FP4_PEAK_TFLOPS if mx else FP8_PEAK_TFLOPS
     kfile = "attention_mx.hip" if mx else "attention.hip"
-    key = w.name + (":mxfp4" + (":qc" if args.q_centre else "") if mx else "") + (":causal" if args.causal else "")
+    key = (w.name + (":mxfp4" + (":qc" if args.q_centre else "") if mx else "") + (":causal" if args.causal else "")
+           + (":exact" if args.exact_probs and not mx else ""))
     traffic = measured_traffic(key, kfile)
     res = {
         "metric": (METRIC_FP4 if mx else (METRIC_CAUSAL if args.causal else METRIC)) + (
@@ -321,7 +325,8 @@ def main() -> int:
                    "cu_seqlens": list(w.cu_seqlens), "seed": w.seed, "softmax_scale": w.softmax_scale,
                    "k_offset_var": w.k_offset_var, "step": "quantize + forward",
                    **({"format": "mxfp4", "q_centre": bool(args.q_centre)} if mx else {}),
-                   **({"causal": True} if args.causal else {})},
+                   **({"causal": True} if args.causal else {}),
+                   **({} if mx else {"probabilities": "exact exp2" if args.exact_probs else "log-linear E4M3 code"})},
         "forward_ms": round(ms_fwd, 4),
         "forward_tflops": round(fwd_tflops, 2),
         "forward_pct_fp8_peak": round(100.0 * fwd_tflops / FP8_PEAK_TFLOPS, 2),

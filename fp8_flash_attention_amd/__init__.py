@@ -56,12 +56,15 @@ class Plan:
     ``"e4m3"`` (default) or ``"mxfp4"``; ``q_centre`` (mxfp4 only) centres Q
     by its 128-row block means.  ``causal`` (e4m3 only): query i of a segment
     attends to the keys j <= i of that segment.  ``head_dim``: 128, or 64
-    (e4m3 only).
+    (e4m3 only).  ``exact_probs`` (e4m3 only): probabilities rounded from the
+    FP32 exp2 instead of the default log-linear E4M3 code (slower, a little
+    more accurate).
     """
 
     def __init__(self, tokens: int, heads: int, cu_seqlens: Optional[Sequence[int]] = None,
                  softmax_scale: Optional[float] = None, device=None, segment_scales: bool = False,
-                 fmt: str = "e4m3", q_centre: bool = False, causal: bool = False, head_dim: int = HEAD_DIM):
+                 fmt: str = "e4m3", q_centre: bool = False, causal: bool = False, head_dim: int = HEAD_DIM,
+                 exact_probs: bool = False):
         L = _lib.lib()
         if cu_seqlens is None:
             cu_seqlens = [0, tokens]
@@ -86,12 +89,14 @@ class Plan:
         if head_dim not in (64, HEAD_DIM):
             raise ValueError(f"head_dim must be 64 or {HEAD_DIM} (got {head_dim})")
         self.head_dim = int(head_dim)
+        self.exact_probs = bool(exact_probs)
         arr = (ctypes.c_int32 * len(cu))(*cu)
         h = ctypes.c_void_p()
         self._h = None
         flags = ((_lib.PLAN_SEGMENT_SCALES if self.segment_scales else 0)
                  | (_lib.PLAN_MXFP4 if fmt == "mxfp4" else 0) | (_lib.PLAN_Q_CENTRE if self.q_centre else 0)
-                 | (_lib.PLAN_CAUSAL if self.causal else 0) | (_lib.PLAN_HEAD_DIM_64 if self.head_dim == 64 else 0))
+                 | (_lib.PLAN_CAUSAL if self.causal else 0) | (_lib.PLAN_HEAD_DIM_64 if self.head_dim == 64 else 0)
+                 | (_lib.PLAN_EXACT_PROBS if self.exact_probs else 0))
         _lib.check(L.fp8attn_plan_ex(ctypes.byref(h), self.tokens, self.heads, arr, len(cu) - 1,
                                      ctypes.c_float(self.softmax_scale), self.device_index, flags),
                    "fp8attn_plan_ex")
@@ -262,16 +267,16 @@ _PLANS: "OrderedDict[Tuple, Plan]" = OrderedDict()
 
 def get_plan(tokens: int, heads: int, cu_seqlens: Sequence[int], softmax_scale: float, device: int,
              segment_scales: bool = False, fmt: str = "e4m3", q_centre: bool = False, causal: bool = False,
-             head_dim: int = HEAD_DIM) -> Plan:
+             head_dim: int = HEAD_DIM, exact_probs: bool = False) -> Plan:
     """The cached plan for (cu_seqlens, heads, scale, device, quantization mode), built on first use."""
     key = (tuple(int(x) for x in cu_seqlens), int(heads), float(softmax_scale), int(device), bool(segment_scales),
-           fmt, bool(q_centre), bool(causal), int(head_dim))
+           fmt, bool(q_centre), bool(causal), int(head_dim), bool(exact_probs))
     p = _PLANS.get(key)
     if p is not None:
         _PLANS.move_to_end(key)
         return p
     p = Plan(tokens, heads, cu_seqlens, softmax_scale, device, segment_scales=segment_scales, fmt=fmt,
-             q_centre=q_centre, causal=causal, head_dim=head_dim)
+             q_centre=q_centre, causal=causal, head_dim=head_dim, exact_probs=exact_probs)
     _PLANS[key] = p
     while len(_PLANS) > max(1, PLAN_CACHE_SIZE):
         _, old = _PLANS.popitem(last=False)
@@ -289,7 +294,7 @@ def clear_plan_cache() -> None:
 def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: Optional[Sequence[int]] = None,
               softmax_scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
               return_lse: bool = False, causal: bool = False, workspace: Optional[torch.Tensor] = None,
-              segment_scales: bool = False, fmt: str = "e4m3", q_centre: bool = False):
+              segment_scales: bool = False, fmt: str = "e4m3", q_centre: bool = False, exact_probs: bool = False):
     """FP8 attention over packed [tokens, heads, 128] BF16 q/k/v.
 
     ``cu_seqlens`` is a host sequence of segment boundaries (None = one segment).
@@ -312,7 +317,7 @@ def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: Opt
             raise ValueError("batched q, k, v (and out) must be viewable as [B*T, H, D]") from e
         res = attention(*flat, cu_seqlens=[T0 * i for i in range(B + 1)], softmax_scale=softmax_scale, out=oflat,
                         return_lse=return_lse, causal=causal, workspace=workspace, segment_scales=segment_scales,
-                        fmt=fmt, q_centre=q_centre)
+                        fmt=fmt, q_centre=q_centre, exact_probs=exact_probs)
         if return_lse:
             return res[0].view(B, T0, *res[0].shape[1:]), res[1]
         return res.view(B, T0, *res.shape[1:])
@@ -323,7 +328,7 @@ def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: Opt
         cu_seqlens = cu_seqlens.tolist()
     scale = 1.0 / math.sqrt(D) if softmax_scale is None else float(softmax_scale)
     dev = q.device.index if q.device.index is not None else torch.cuda.current_device()
-    plan = get_plan(T, H, cu_seqlens, scale, dev, segment_scales, fmt, q_centre, causal, D)
+    plan = get_plan(T, H, cu_seqlens, scale, dev, segment_scales, fmt, q_centre, causal, D, exact_probs)
     ws = workspace if workspace is not None else plan.new_workspace()
     quantize(plan, q, k, v, ws)
     lse = torch.empty((H, T), dtype=torch.float32, device=q.device) if return_lse else None

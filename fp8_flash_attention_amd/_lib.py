@@ -23,6 +23,7 @@ PLAN_MXFP4 = 2                   # FP8ATTN_PLAN_MXFP4
 PLAN_Q_CENTRE = 4                # FP8ATTN_PLAN_Q_CENTRE
 PLAN_CAUSAL = 8                  # FP8ATTN_PLAN_CAUSAL
 PLAN_HEAD_DIM_64 = 16            # FP8ATTN_PLAN_HEAD_DIM_64
+PLAN_EXACT_PROBS = 32            # FP8ATTN_PLAN_EXACT_PROBS
 PLAN_INFO_LEN = 14
 
 # Every symbol include/fp8attn.h declares, with (restype, argtypes).

@@ -33,6 +33,7 @@ struct fp8attn_plan_s {
   int32_t q_centre = 0;           // FP8ATTN_PLAN_Q_CENTRE
   int32_t causal = 0;             // FP8ATTN_PLAN_CAUSAL
   int32_t head_dim = kHeadDim;    // 64 with FP8ATTN_PLAN_HEAD_DIM_64
+  int32_t exact_probs = 0;        // FP8ATTN_PLAN_EXACT_PROBS
   int32_t bm = kBM;               // queries per work item (kMxBM for FP4 plans; see choose_query_tile)
   int32_t wg_per_cu = 1;          // attention workgroups resident per CU
   float scale = 0.f;
@@ -296,8 +297,10 @@ fp8attn_status fp8attn_plan_ex(fp8attn_plan_t* plan_out, int64_t tokens, int32_t
   if (plan_out == nullptr) return fail(FP8ATTN_EINVAL, "plan_out is NULL");
   *plan_out = nullptr;
   if ((flags & ~(FP8ATTN_PLAN_SEGMENT_SCALES | FP8ATTN_PLAN_MXFP4 | FP8ATTN_PLAN_Q_CENTRE | FP8ATTN_PLAN_CAUSAL |
-                 FP8ATTN_PLAN_HEAD_DIM_64)) != 0)
+                 FP8ATTN_PLAN_HEAD_DIM_64 | FP8ATTN_PLAN_EXACT_PROBS)) != 0)
     return fail(FP8ATTN_EINVAL, "unknown plan flags");
+  if ((flags & FP8ATTN_PLAN_EXACT_PROBS) && (flags & FP8ATTN_PLAN_MXFP4))
+    return fail(FP8ATTN_EINVAL, "FP8ATTN_PLAN_EXACT_PROBS applies to E4M3 plans only");
   if ((flags & FP8ATTN_PLAN_HEAD_DIM_64) && (flags & FP8ATTN_PLAN_MXFP4))
     return fail(FP8ATTN_EINVAL, "FP8ATTN_PLAN_HEAD_DIM_64 is not available for FP8ATTN_PLAN_MXFP4 plans");
   if ((flags & FP8ATTN_PLAN_CAUSAL) && (flags & FP8ATTN_PLAN_MXFP4))
@@ -332,6 +335,7 @@ fp8attn_status fp8attn_plan_ex(fp8attn_plan_t* plan_out, int64_t tokens, int32_t
   p->q_centre = (flags & FP8ATTN_PLAN_Q_CENTRE) ? 1 : 0;
   p->causal = (flags & FP8ATTN_PLAN_CAUSAL) ? 1 : 0;
   p->head_dim = (flags & FP8ATTN_PLAN_HEAD_DIM_64) ? 64 : kHeadDim;
+  p->exact_probs = (flags & FP8ATTN_PLAN_EXACT_PROBS) ? 1 : 0;
   if (p->mx) {
     p->bm = kMxBM;
     p->wg_per_cu = kMxWgPerCu;
@@ -597,6 +601,7 @@ fp8attn_status fp8attn_forward(fp8attn_plan_t p, void* workspace, size_t workspa
   a.causal = p->causal;
   a.head_dim = p->head_dim;
   a.bm = p->bm;
+  a.exact_probs = p->exact_probs;
   a.softmax_scale = p->scale;
   hipError_t e = launch_attention(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(FP8ATTN_EHIP, std::string("attention launch failed: ") + hipGetErrorString(e));

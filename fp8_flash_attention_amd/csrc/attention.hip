@@ -42,18 +42,24 @@
 //     row 1.  l is the sum of the E4M3 probabilities that actually weight V.
 //     When the caller asks for the LSE, an FP32 sum of the unrounded
 //     probabilities is kept as well.
-//   * Probabilities: p = exp2(x), x = c*s + nb with c = softmax_scale * s_q *
-//     s_k * log2(e) and nb = log2(112) - c*m for a per-query reference maximum
-//     m.  The quantizer makes c a power of two, so the score products run on
-//     the scaled MFMA (E8M0 factor c) with nb as the initial accumulator and
-//     deliver x itself: the vector work per score is one exp2 and half a
-//     conversion.  The first tile sets m to its row maximum (mapped to 112 =
-//     448/4).  Later tiles move m only when their maximum would give a p above
-//     448, the largest E4M3 value, so most tiles need no rescale: the common
-//     path is a max tree and one wave-wide vote; the rare path shifts x, nb and
-//     the accumulator offset, and the rescale of O and l by 2^shift runs at
-//     the top of the next iteration, after the P V product of the older tiles
-//     and before that of the tile that moved m.
+//   * Probabilities: p = 2^x, x = c*s + nbx with c = softmax_scale * s_q *
+//     s_k * log2(e) and nbx = log2(112) - c*m for a per-query reference
+//     maximum m.  The quantizer makes c a power of two, so the score products
+//     run on the scaled MFMA (E8M0 factor c) with the offset as the initial
+//     accumulator and deliver the exponent itself.  By default they deliver
+//     y = 8 x + kYBias (factor 8 c), and the E4M3 code of p is y rounded to
+//     an integer, one v_cvt_pk_u8_f32 per score: the integer part of 8 x steps
+//     the code's exponent, the fraction its 3-bit mantissa (2^f read as 1 + f,
+//     centred by kYBias), about 0.031 relative RMS of the kernel's own error
+//     against 0.026 for exact rounding, 12% faster.  With exact probabilities
+//     they deliver x, and p = E4M3(exp2(x)): an exp2 and half a conversion.
+//     The first tile sets m to its row maximum (mapped to 112 = 448/4).
+//     Later tiles move m only when their maximum would give a p above 448,
+//     the largest E4M3 value, so most tiles need no rescale: the common path
+//     is a max tree and one wave-wide vote; the rare path shifts the scores,
+//     the offset and the accumulator initial value, and the rescale of O and
+//     l by 2^shift runs at the top of the next iteration, after the P V
+//     product of the older tiles and before that of the tile that moved m.
 //   * K and V^T tiles reach LDS by direct buffer loads (no register staging):
 //     a K ring and a V ring of four 8 KB slots each.  Iteration t reads K of
 //     tile t+1 for its score products, and V of tile t for the P V product of
@@ -76,8 +82,19 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 constexpr float kLog2e = 1.4426950408889634f;
+// Probability frames.  Exact probabilities (FP8ATTN_PLAN_EXACT_PROBS): the
+// score products deliver x = log2(p) and p = E4M3(exp2(x)).  Log-linear (the
+// default): they deliver y = 8 x + kYBias and the E4M3 code of p is y rounded
+// to an integer (v_cvt_pk_u8_f32, round to nearest even, clamped to [0, 255]):
+// an E4M3 code is 8 * (biased exponent) + mantissa, so the integer part of
+// 8 x + 56 steps the exponent and the fraction the 3-bit mantissa linearly
+// (2^f read as 1 + f on each octave); kYBias = 56 - 0.4588 centres that
+// approximation and puts the reference at code 110 (the value 112).
 constexpr float kLog2Ref = 6.807354922057604f;   // log2(112): reference maximum maps to 448 / 4
 constexpr float kLog2Max = 8.807354922057604f;   // log2(448), the largest E4M3 value
+constexpr float kYBias = 55.54116061995f;        // y = 8 x + kYBias
+constexpr float kYRef = 110.0f;                  // y of the reference maximum: code 110 = 112
+constexpr float kYMax = 126.5f;                  // above this y a code would pass 0x7E (448)
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kSlots = 4;                        // ring slots per operand
 constexpr int kBarEvery = kSlots / 2;            // iterations per barrier
@@ -183,9 +200,13 @@ __device__ __forceinline__ void tail_iters(F& iter, int& t, int nkt) {
 
 // BM queries per work item (256: one 8-wave workgroup per CU; 128: two 4-wave
 // workgroups per CU), D channels per head.
-template <bool LSE, bool CAUSAL, int D, int BM>
+template <bool LSE, bool CAUSAL, int D, int BM, bool EXACT>
 __global__ __launch_bounds__(2 * BM, 256 / BM) void k_attn(AttentionArgs a) {
   constexpr int kWavesWG = BM / 32;              // waves per workgroup, 32 queries each
+  // frame constants in the units the score products deliver (x, or y = 8 x + kYBias)
+  constexpr float kRef = EXACT ? kLog2Ref : kYRef;
+  constexpr float kMax = EXACT ? kLog2Max : kYMax;
+  constexpr float kUnit = EXACT ? 1.f : 0.125f;   // log2 units per unit of the frame
   static_assert(BM == 128 || BM == 256, "4 or 8 waves x 32 queries");
   constexpr int kTile = kBN * D;                 // bytes of one K (or V^T) tile
   constexpr int kVRing = kSlots * kTile;         // V ring follows the K ring in LDS
@@ -238,7 +259,7 @@ __global__ __launch_bounds__(2 * BM, 256 / BM) void k_attn(AttentionArgs a) {
   // products exactly: x = c * (q . k) + nb comes out of the matrix core with the
   // per-query exp2 offset nb as the accumulator's initial value.
   const float c = a.softmax_scale * s_q * s_k * kLog2e;
-  const int c_e8m0 = min((int)((__float_as_uint(c) + 0x400000u) >> 23), 254);
+  const int c_e8m0 = min((int)((__float_as_uint(c) + 0x400000u) >> 23) + (EXACT ? 0 : 3), 254);   // c, or 8 c
 
   // Q as B operands: queries q0 + 32*wave + (lane%32), channels
   // 64*half + 32*(lane/32) .. +32.  Rows past the segment end read zero codes,
@@ -353,7 +374,7 @@ __global__ __launch_bounds__(2 * BM, 256 / BM) void k_attn(AttentionArgs a) {
   // they hold the products of tiles up to t-1, computed in the old frame.
   auto rescale = [&]() __attribute__((always_inline)) {
     if (pending) {
-      const float alpha = __builtin_amdgcn_exp2f(pshift);
+      const float alpha = __builtin_amdgcn_exp2f(pshift * kUnit);
       auto pa = __builtin_amdgcn_permlane16_swap(__float_as_uint(alpha), __float_as_uint(alpha), false, false);
       lacc[0] *= alpha;
       lacc[1] *= __uint_as_float(pa[1]);   // lane j < 16: alpha of query 16+j
@@ -388,22 +409,22 @@ __global__ __launch_bounds__(2 * BM, 256 / BM) void k_attn(AttentionArgs a) {
     if (FIRST) {
       auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(tl), __float_as_uint(tl), false, false);
       const float tm = __builtin_fmaxf(__uint_as_float(pr[0]), __uint_as_float(pr[1]));
-      const float shift = kLog2Ref - tm;
+      const float shift = kRef - tm;
       nb = shift;
 #pragma unroll
       for (int i = 0; i < 16; i++) { S[0][i] += shift; S[1][i] += shift; NB[i] = shift; }
     } else {
       // move the reference only if the tile's largest p would exceed 448: one
       // vote over the wave; the row maxima and shifts only on the rare path
-      pending = __builtin_amdgcn_ballot_w64(tl > kLog2Max) != 0;
+      pending = __builtin_amdgcn_ballot_w64(tl > kMax) != 0;
       if (pending) {
         auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(tl), __float_as_uint(tl), false, false);
         const float xm = __builtin_fmaxf(__uint_as_float(pr[0]), __uint_as_float(pr[1]));
-        const bool over = xm > kLog2Max;
-        const float shift = over ? kLog2Ref - xm : 0.f;
+        const bool over = xm > kMax;
+        const float shift = over ? kRef - xm : 0.f;
         nb += shift;
         pshift = shift;
-        if (LSE) lex *= __builtin_amdgcn_exp2f(shift);   // lex takes this tile's p in the new frame
+        if (LSE) lex *= __builtin_amdgcn_exp2f(shift * kUnit);   // lex takes this tile's p in the new frame
 #pragma unroll
         for (int i = 0; i < 16; i++) { S[0][i] += shift; S[1][i] += shift; NB[i] += shift; }
       }
@@ -411,14 +432,27 @@ __global__ __launch_bounds__(2 * BM, 256 / BM) void k_attn(AttentionArgs a) {
   };
   // E4M3 probabilities of keys 8*q4 + 4*(lane/32) + 0..3 of block kb (one P dword).
   auto probs4 = [&](int kb, int q4, int kbase) __attribute__((always_inline)) {
-    float p[4];
+    if constexpr (EXACT) {
+      float p[4];
 #pragma unroll
-    for (int i = 0; i < 4; i++) p[i] = __builtin_amdgcn_exp2f(S[kb][4 * q4 + i]);
-    if (LSE) {
+      for (int i = 0; i < 4; i++) p[i] = __builtin_amdgcn_exp2f(S[kb][4 * q4 + i]);
+      if (LSE) {
 #pragma unroll
-      for (int i = 0; i < 4; i++) lex += p[i];
+        for (int i = 0; i < 4; i++) lex += p[i];
+      }
+      return cvt4(p[0], p[1], p[2], p[3]);
+    } else {
+      if (LSE) {   // the FP32 sum takes exp2 of x = (y - kYBias) / 8
+#pragma unroll
+        for (int i = 0; i < 4; i++)
+          lex += __builtin_amdgcn_exp2f(__builtin_fmaf(S[kb][4 * q4 + i], 0.125f, -kYBias * 0.125f));
+      }
+      uint32_t w = __builtin_amdgcn_cvt_pk_u8_f32(S[kb][4 * q4 + 0], 0, 0u);
+      w = __builtin_amdgcn_cvt_pk_u8_f32(S[kb][4 * q4 + 1], 1, w);
+      w = __builtin_amdgcn_cvt_pk_u8_f32(S[kb][4 * q4 + 2], 2, w);
+      w = __builtin_amdgcn_cvt_pk_u8_f32(S[kb][4 * q4 + 3], 3, w);
+      return (int)w;
     }
-    return cvt4(p[0], p[1], p[2], p[3]);
   };
   // Causal: scores of keys after this lane's query to -inf in tile t (only
   // tiles from q0 on hold such keys).  Register r of block kb holds key
@@ -659,6 +693,8 @@ __global__ __launch_bounds__(2 * BM, 256 / BM) void k_attn(AttentionArgs a) {
   // epilogue: lane l holds O^T for query l%32, channels
   // 32*db + 8*(r/4) + 4*(l/32) + r%4 in register r of block db.
   const int qrow = q0 + 32 * wave + lq;
+  // the frame offset in log2 units: p = 2^(c s + nbx) for every key
+  const float nbx = EXACT ? nb : (nb - kYBias) * 0.125f;
   // row sum of the E4M3 probabilities (the weights actually applied to V)
   const float l0 = __shfl(lacc[0], lq & 15);
   const float l1 = __shfl(lacc[1], lq & 15);
@@ -680,7 +716,7 @@ __global__ __launch_bounds__(2 * BM, 256 / BM) void k_attn(AttentionArgs a) {
           *reinterpret_cast<float4*>(orow + 32 * db + 8 * q4 + 4 * lg) =
               make_float4(O[db][4 * q4 + 0] * inv, O[db][4 * q4 + 1] * inv, O[db][4 * q4 + 2] * inv,
                           O[db][4 * q4 + 3] * inv);
-      if (lg == 0) a.part_w[prow] = lt > 0.f ? __log2f(lt) - nb : -__builtin_huge_valf();
+      if (lg == 0) a.part_w[prow] = lt > 0.f ? __log2f(lt) - nbx : -__builtin_huge_valf();
     }
   } else if (qrow < L) {
     const float inv = s_v / lt;
@@ -701,7 +737,7 @@ __global__ __launch_bounds__(2 * BM, 256 / BM) void k_attn(AttentionArgs a) {
     // (keys past the end of the range were masked, so they added nothing)
     const float le = sum_pair32(lex);
     if (lg == 0 && qrow < L) {
-      const float lse2 = __log2f(le) - nb;
+      const float lse2 = __log2f(le) - nbx;
       const float v = lse2 * kLn2 + a.softmax_scale * s_q * qmu;
       if (slot >= 0)
         a.part_lse[slot * kPartRows + 32 * wave + lq] = v;
@@ -799,29 +835,37 @@ hipError_t launch_combine(const CombineArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <int D, int BM>
+template <int D, int BM, bool EXACT>
 void launch_attention_d(const AttentionArgs& a, hipStream_t stream) {
   const dim3 g(a.nitems), b(2 * BM);
   if (a.causal) {
     if (a.lse != nullptr)
-      hipLaunchKernelGGL((k_attn<true, true, D, BM>), g, b, 0, stream, a);
+      hipLaunchKernelGGL((k_attn<true, true, D, BM, EXACT>), g, b, 0, stream, a);
     else
-      hipLaunchKernelGGL((k_attn<false, true, D, BM>), g, b, 0, stream, a);
+      hipLaunchKernelGGL((k_attn<false, true, D, BM, EXACT>), g, b, 0, stream, a);
   } else if (a.lse != nullptr) {
-    hipLaunchKernelGGL((k_attn<true, false, D, BM>), g, b, 0, stream, a);
+    hipLaunchKernelGGL((k_attn<true, false, D, BM, EXACT>), g, b, 0, stream, a);
   } else {
-    hipLaunchKernelGGL((k_attn<false, false, D, BM>), g, b, 0, stream, a);
+    hipLaunchKernelGGL((k_attn<false, false, D, BM, EXACT>), g, b, 0, stream, a);
   }
+}
+
+template <bool EXACT>
+void launch_attention_e(const AttentionArgs& a, hipStream_t stream) {
+  if (a.head_dim == 64)
+    launch_attention_d<64, 256, EXACT>(a, stream);      // 64 channels: 256-query items only
+  else if (a.bm == 128)
+    launch_attention_d<kHeadDim, 128, EXACT>(a, stream);
+  else
+    launch_attention_d<kHeadDim, 256, EXACT>(a, stream);
 }
 
 hipError_t launch_attention(const AttentionArgs& a, hipStream_t stream) {
   if (a.nitems == 0) return hipSuccess;
-  if (a.head_dim == 64)
-    launch_attention_d<64, 256>(a, stream);      // 64 channels: 256-query items only
-  else if (a.bm == 128)
-    launch_attention_d<kHeadDim, 128>(a, stream);
+  if (a.exact_probs)
+    launch_attention_e<true>(a, stream);
   else
-    launch_attention_d<kHeadDim, 256>(a, stream);
+    launch_attention_e<false>(a, stream);
   return hipGetLastError();
 }
 

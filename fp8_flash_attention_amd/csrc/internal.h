@@ -129,6 +129,7 @@ struct AttentionArgs {
   int32_t causal;            // 1: query i of a segment attends keys j <= i only
   int32_t head_dim;          // D: 128 or 64
   int32_t bm;                // queries per work item: 256, or 128 (D = 128 only)
+  int32_t exact_probs;       // 1: p = E4M3(exp2(x)); 0: the log-linear code of 2^x
   float softmax_scale;
 };
 

@@ -248,8 +248,12 @@ def test_plan_ex_flags_and_segment_scale_layout():
     L = _lib.lib()
     cu = (ctypes.c_int32 * 4)(0, 100, 100, 300)
     h = ctypes.c_void_p()
-    assert L.fp8attn_plan_ex(ctypes.byref(h), 300, 2, cu, 3, ctypes.c_float(0.088), -1, 32) == _lib.EINVAL
+    assert L.fp8attn_plan_ex(ctypes.byref(h), 300, 2, cu, 3, ctypes.c_float(0.088), -1, 64) == _lib.EINVAL
     assert "flags" in L.fp8attn_last_error().decode()
+    assert L.fp8attn_plan_ex(ctypes.byref(h), 300, 2, cu, 3, ctypes.c_float(0.088), -1,
+                             _lib.PLAN_EXACT_PROBS | _lib.PLAN_MXFP4) == _lib.EINVAL
+    assert L.fp8attn_plan_ex(ctypes.byref(h), 300, 2, cu, 3, ctypes.c_float(0.088), -1, _lib.PLAN_EXACT_PROBS) == 0
+    L.fp8attn_plan_destroy(h)
     base = fa.Plan(300, 2, [0, 100, 100, 300], device=-1)
     seg = fa.Plan(300, 2, [0, 100, 100, 300], device=-1, segment_scales=True)
     assert base.info()["segment_scales"] == 0 and seg.info()["segment_scales"] == 1

@@ -32,9 +32,9 @@ pytestmark = pytest.mark.gpu
 DIAG_BAR = 0.035
 
 
-def _gpu_attention(w, q, k, v, lse=False):
-    log(f"attention {w.name} T={w.tokens} H={w.heads} cu={list(w.cu_seqlens)[:8]}")
-    plan = fa.Plan(w.tokens, w.heads, w.cu_seqlens, w.softmax_scale, device=0)
+def _gpu_attention(w, q, k, v, lse=False, exact=False):
+    log(f"attention {w.name} T={w.tokens} H={w.heads} cu={list(w.cu_seqlens)[:8]} exact_probs={exact}")
+    plan = fa.Plan(w.tokens, w.heads, w.cu_seqlens, w.softmax_scale, device=0, exact_probs=exact)
     ws = plan.new_workspace()
     fa.quantize(plan, q, k, v, ws)
     l = torch.empty((w.heads, w.tokens), dtype=torch.float32, device="cuda") if lse else None
@@ -50,9 +50,9 @@ def _dequantized(q, k, v, cu, softmax_scale):
             Qz.dequantize(r["v_codes"], sc[2]))
 
 
-def _check_rows(w, rows, heads=None, pure_atol=False):
+def _check_rows(w, rows, heads=None, pure_atol=False, exact=False):
     q, k, v = generate(w, device="cuda")
-    plan, ws, out, _ = _gpu_attention(w, q, k, v)
+    plan, ws, out, _ = _gpu_attention(w, q, k, v, exact=exact)
     qc, kc, vc = q.cpu(), k.cpu(), v.cpu()
     hs = slice(None) if heads is None else list(heads)
     if heads is not None:
