@@ -220,7 +220,7 @@ def main() -> int:
     ap.add_argument("--exact-probs", action="store_true",
                     help="e4m3: probabilities rounded from the FP32 exp2 instead of the log-linear code")
     ap.add_argument("--causal", action="store_true",
-                    help="e4m3: causal plan (FLOPs then count the visible pairs, 2 * sum L(L+1) * H * D)")
+                    help="causal plan (FLOPs then count the visible pairs, 2 * sum L(L+1) * H * D)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="after timing, run one plain device copy of BYTES bytes (a known-size "
                          "reference dispatch for scaling HBM traffic counters)")
@@ -309,6 +309,7 @@ def main() -> int:
     traffic = measured_traffic(key, kfile)
     res = {
         "metric": (METRIC_FP4 if mx else (METRIC_CAUSAL if args.causal else METRIC)) + (
+            " [causal: visible pairs only]" if mx and args.causal else "") + (
             f" [head_dim {w.head_dim}]" if w.head_dim != 128 else ""),
         "value": round(value, 2),
         "unit": "TFLOP/s",

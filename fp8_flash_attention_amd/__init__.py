@@ -54,8 +54,8 @@ class Plan:
     host-only plan that can be inspected but not run.  ``segment_scales=True``
     quantizes every segment with its own per-head scales.  ``fmt`` is
     ``"e4m3"`` (default) or ``"mxfp4"``; ``q_centre`` (mxfp4 only) centres Q
-    by its 128-row block means.  ``causal`` (e4m3 only): query i of a segment
-    attends to the keys j <= i of that segment.  ``head_dim``: 128, or 64
+    by its 128-row block means.  ``causal``: query i of a segment attends to
+    the keys j <= i of that segment.  ``head_dim``: 128, or 64
     (e4m3 only).  ``exact_probs`` (e4m3 only): probabilities rounded from the
     FP32 exp2 instead of the default log-linear E4M3 code (slower, a little
     more accurate).
@@ -300,8 +300,7 @@ def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: Opt
     ``cu_seqlens`` is a host sequence of segment boundaries (None = one segment).
     ``segment_scales`` quantizes every segment with its own per-head scales.
     ``fmt="mxfp4"`` runs the block-scaled FP4 variant (``q_centre`` adds Q
-    block-mean centring); it returns no LSE.  ``causal=True`` masks keys after
-    each query (E4M3 only).  The head size (128, or 64 for E4M3) is taken from
+    block-mean centring).  ``causal=True`` masks keys after each query.  The head size (128, or 64 for E4M3) is taken from
     the inputs' last dimension.  Batched [B, T, heads, 128] inputs (views of
     [B*T, heads, 128]) are run as B segments of T tokens and returned as
     [B, T, heads, 128] (with the LSE as [heads, B*T]).

@@ -74,9 +74,10 @@ fp8attn_status fail(fp8attn_status s, const std::string& msg) {
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 // FP4 plans: codes of half the size, block scales, block-mean operand.
-WorkspaceLayout make_layout_mx(int64_t rows, int heads, int nseg, int nchunks) {
+WorkspaceLayout make_layout_mx(int64_t rows, int heads, int nseg, int nchunks, int64_t npieces) {
   WorkspaceLayout w{};
   w.rows = rows;
+  w.npieces = npieces;
   const size_t codes = (size_t)heads * rows * kMxRow;
   const size_t scales = (size_t)heads * rows * 4;
   const size_t qblocks = (size_t)heads * (rows / kMxQBlock);
@@ -90,6 +91,9 @@ WorkspaceLayout make_layout_mx(int64_t rows, int heads, int nseg, int nchunks) {
   w.qm_off = off; off = align_up(off + qblocks * kMxRow, 256);
   w.qms_off = off; off = align_up(off + qblocks * 4, 256);
   w.mu_off = off; off = align_up(off + sizeof(float) * (size_t)nseg * heads * kHeadDim, 256);
+  w.part_o_off = off; off = align_up(off + sizeof(float) * (size_t)npieces * kPartRows * kHeadDim, 256);
+  w.part_w_off = off; off = align_up(off + sizeof(float) * (size_t)npieces * kPartRows, 256);
+  w.part_lse_off = off; off = align_up(off + sizeof(float) * (size_t)npieces * kPartRows, 256);
   w.stats_off = off;
   w.kstat_off = off; off = align_up(off + sizeof(KStat) * (size_t)nchunks * heads * kHeadDim, 256);
   w.total = off;
@@ -303,8 +307,6 @@ fp8attn_status fp8attn_plan_ex(fp8attn_plan_t* plan_out, int64_t tokens, int32_t
     return fail(FP8ATTN_EINVAL, "FP8ATTN_PLAN_EXACT_PROBS applies to E4M3 plans only");
   if ((flags & FP8ATTN_PLAN_HEAD_DIM_64) && (flags & FP8ATTN_PLAN_MXFP4))
     return fail(FP8ATTN_EINVAL, "FP8ATTN_PLAN_HEAD_DIM_64 is not available for FP8ATTN_PLAN_MXFP4 plans");
-  if ((flags & FP8ATTN_PLAN_CAUSAL) && (flags & FP8ATTN_PLAN_MXFP4))
-    return fail(FP8ATTN_EINVAL, "FP8ATTN_PLAN_CAUSAL is not available for FP8ATTN_PLAN_MXFP4 plans");
   if ((flags & FP8ATTN_PLAN_Q_CENTRE) && !(flags & FP8ATTN_PLAN_MXFP4))
     return fail(FP8ATTN_EINVAL, "FP8ATTN_PLAN_Q_CENTRE needs FP8ATTN_PLAN_MXFP4");
   if ((flags & FP8ATTN_PLAN_MXFP4) && (flags & FP8ATTN_PLAN_SEGMENT_SCALES))
@@ -368,12 +370,12 @@ fp8attn_status fp8attn_plan_ex(fp8attn_plan_t* plan_out, int64_t tokens, int32_t
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, device) == hipSuccess && n > 0) cus = n;
   }
   choose_query_tile(p, cus);
-  build_items(p, std::max(1, cus / kNumXcd), !p->mx && !p->causal);
+  build_items(p, std::max(1, cus / kNumXcd), !p->causal);
   if (p->npieces >= (int64_t)1 << 23) {
     delete p;
     return fail(FP8ATTN_EUNSUPPORTED, "too many split work items");
   }
-  p->ws = p->mx ? make_layout_mx(row, heads, num_segments, (int)p->chunks.size())
+  p->ws = p->mx ? make_layout_mx(row, heads, num_segments, (int)p->chunks.size(), p->npieces)
                 : make_layout(row, heads, num_segments, p->nscale, (int)p->chunks.size(), p->npieces, p->head_dim);
 
   if (device >= 0) {
@@ -552,10 +554,16 @@ fp8attn_status fp8attn_forward(fp8attn_plan_t p, void* workspace, size_t workspa
     if (!strides_ok(out_strides)) return fail(FP8ATTN_EINVAL, "out strides must be positive multiples of 8");
     if (lse != nullptr && ((uintptr_t)lse & 3) != 0) return fail(FP8ATTN_EINVAL, "lse must be 4-byte aligned");
   }
-  if (p->mx && lse != nullptr) return fail(FP8ATTN_EUNSUPPORTED, "lse is not available for FP8ATTN_PLAN_MXFP4 plans");
   DeviceGuard g(p->device);
   if (!g.ok) return fail(FP8ATTN_EHIP, "cannot select device");
   uint8_t* ws = static_cast<uint8_t*>(workspace);
+  float* part_o = reinterpret_cast<float*>(ws + p->ws.part_o_off);
+  float* part_w = reinterpret_cast<float*>(ws + p->ws.part_w_off);
+  float* part_lse = reinterpret_cast<float*>(ws + p->ws.part_lse_off);
+  const int64_t os0 = p->tokens > 0 ? out_strides[0] : 0;
+  const int64_t os1 = p->tokens > 0 ? out_strides[1] : 0;
+  const int32_t nitems = p->real_items > 0 ? (int32_t)p->items.size() : 0;
+  hipError_t e;
   if (p->mx) {
     MxAttentionArgs m{};
     m.q_codes = ws + p->ws.q_off;
@@ -566,56 +574,63 @@ fp8attn_status fp8attn_forward(fp8attn_plan_t p, void* workspace, size_t workspa
     m.v_scales = ws + p->ws.vs_off;
     m.qm_codes = ws + p->ws.qm_off;
     m.qm_scales = ws + p->ws.qms_off;
+    m.mu = reinterpret_cast<const float*>(ws + p->ws.mu_off);
     m.segs = p->d_segs;
     m.items = p->d_items;
     m.out = static_cast<uint16_t*>(out);
-    m.os0 = p->tokens > 0 ? out_strides[0] : 0;
-    m.os1 = p->tokens > 0 ? out_strides[1] : 0;
+    m.os0 = os0;
+    m.os1 = os1;
+    m.lse = lse;
+    m.part_o = part_o;
+    m.part_w = part_w;
+    m.part_lse = part_lse;
+    m.tokens = p->tokens;
     m.rows = p->ws.rows;
-    m.nitems = p->real_items > 0 ? (int32_t)p->items.size() : 0;
+    m.heads = p->heads;
+    m.nitems = nitems;
     m.q_centre = p->q_centre;
-    hipError_t e = launch_attention_mx(m, static_cast<hipStream_t>(stream));
-    if (e != hipSuccess) return fail(FP8ATTN_EHIP, std::string("attention launch failed: ") + hipGetErrorString(e));
-    return FP8ATTN_OK;
+    m.causal = p->causal;
+    e = launch_attention_mx(m, static_cast<hipStream_t>(stream));
+  } else {
+    AttentionArgs a{};
+    a.q_codes = ws + p->ws.q_off;
+    a.k_codes = ws + p->ws.k_off;
+    a.v_codes = ws + p->ws.v_off;
+    a.scales = reinterpret_cast<const float*>(ws + p->ws.scale_off);
+    a.mu = reinterpret_cast<const float*>(ws + p->ws.mu_off);
+    a.segs = p->d_segs;
+    a.items = p->d_items;
+    a.out = static_cast<uint16_t*>(out);
+    a.os0 = os0;
+    a.os1 = os1;
+    a.lse = lse;
+    a.part_o = part_o;
+    a.part_w = part_w;
+    a.part_lse = part_lse;
+    a.tokens = p->tokens;
+    a.rows = p->ws.rows;
+    a.heads = p->heads;
+    a.nitems = nitems;
+    a.nscale = p->nscale;
+    a.causal = p->causal;
+    a.head_dim = p->head_dim;
+    a.bm = p->bm;
+    a.exact_probs = p->exact_probs;
+    a.softmax_scale = p->scale;
+    e = launch_attention(a, static_cast<hipStream_t>(stream));
   }
-  AttentionArgs a{};
-  a.q_codes = ws + p->ws.q_off;
-  a.k_codes = ws + p->ws.k_off;
-  a.v_codes = ws + p->ws.v_off;
-  a.scales = reinterpret_cast<const float*>(ws + p->ws.scale_off);
-  a.mu = reinterpret_cast<const float*>(ws + p->ws.mu_off);
-  a.segs = p->d_segs;
-  a.items = p->d_items;
-  a.out = static_cast<uint16_t*>(out);
-  a.os0 = p->tokens > 0 ? out_strides[0] : 0;
-  a.os1 = p->tokens > 0 ? out_strides[1] : 0;
-  a.lse = lse;
-  a.part_o = reinterpret_cast<float*>(ws + p->ws.part_o_off);
-  a.part_w = reinterpret_cast<float*>(ws + p->ws.part_w_off);
-  a.part_lse = reinterpret_cast<float*>(ws + p->ws.part_lse_off);
-  a.tokens = p->tokens;
-  a.rows = p->ws.rows;
-  a.heads = p->heads;
-  a.nitems = p->real_items > 0 ? (int32_t)p->items.size() : 0;
-  a.nscale = p->nscale;
-  a.causal = p->causal;
-  a.head_dim = p->head_dim;
-  a.bm = p->bm;
-  a.exact_probs = p->exact_probs;
-  a.softmax_scale = p->scale;
-  hipError_t e = launch_attention(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(FP8ATTN_EHIP, std::string("attention launch failed: ") + hipGetErrorString(e));
   if (!p->combine.empty()) {
     CombineArgs c{};
     c.items = p->d_combine;
     c.nitems = (int32_t)p->combine.size();
     c.segs = p->d_segs;
-    c.part_o = a.part_o;
-    c.part_w = a.part_w;
-    c.part_lse = a.part_lse;
-    c.out = a.out;
-    c.os0 = a.os0;
-    c.os1 = a.os1;
+    c.part_o = part_o;
+    c.part_w = part_w;
+    c.part_lse = part_lse;
+    c.out = static_cast<uint16_t*>(out);
+    c.os0 = os0;
+    c.os1 = os1;
     c.lse = lse;
     c.tokens = p->tokens;
     c.head_dim = p->head_dim;

@@ -454,18 +454,25 @@ __global__ __launch_bounds__(2 * BM, 256 / BM) void k_attn(AttentionArgs a) {
       return (int)w;
     }
   };
+  // Scores of this lane's keys with tile-relative offset 32*kb + 8*(r/4) + r%4
+  // (register r of block kb; the lane's keys add 4*lg) above dlim to -inf:
+  // min(S, +-inf) with the sign of dlim + 1/2 - offset, so no compare or
+  // condition register per score.
+  auto mask_after = [&](int dlim) __attribute__((always_inline)) {
+    const float df = (float)dlim + 0.5f;
+#pragma unroll
+    for (int kb = 0; kb < 2; kb++)
+#pragma unroll
+      for (int r = 0; r < 16; r++) {
+        const float d = df - (float)(32 * kb + 8 * (r >> 2) + (r & 3));
+        S[kb][r] = __builtin_fminf(S[kb][r], __uint_as_float((__float_as_uint(d) & 0x80000000u) | 0x7f800000u));
+      }
+  };
   // Causal: scores of keys after this lane's query to -inf in tile t (only
   // tiles from q0 on hold such keys).  Register r of block kb holds key
   // t*64 + 32*kb + 8*(r/4) + 4*lg + r%4.
   const int qq = q0 + 32 * wave + lq;
-  auto mask_causal = [&](int t) __attribute__((always_inline)) {
-    const int dlim = qq - t * kBN - 4 * lg;
-#pragma unroll
-    for (int kb = 0; kb < 2; kb++)
-#pragma unroll
-      for (int r = 0; r < 16; r++)
-        if (32 * kb + 8 * (r >> 2) + (r & 3) > dlim) S[kb][r] = -__builtin_huge_valf();
-  };
+  auto mask_causal = [&](int t) __attribute__((always_inline)) { mask_after(qq - t * kBN - 4 * lg); };
   // Keys past the end of the range (the last tile of a segment whose length is
   // not a multiple of 64) to -inf in tile t, before the reference update.
   // Their K rows are zero codes, so unmasked they would score exactly 0: a
@@ -476,14 +483,7 @@ __global__ __launch_bounds__(2 * BM, 256 / BM) void k_attn(AttentionArgs a) {
   // (Causal: keys past the segment end lie after every stored query and are
   // masked by mask_causal.)
   const bool ragged = !CAUSAL && Lk < nkt * kBN;
-  auto mask_tail = [&](int t) __attribute__((always_inline)) {
-    const int dlim = Lk - 1 - t * kBN - 4 * lg;
-#pragma unroll
-    for (int kb = 0; kb < 2; kb++)
-#pragma unroll
-      for (int r = 0; r < 16; r++)
-        if (32 * kb + 8 * (r >> 2) + (r & 3) > dlim) S[kb][r] = -__builtin_huge_valf();
-  };
+  auto mask_tail = [&](int t) __attribute__((always_inline)) { mask_after(Lk - 1 - t * kBN - 4 * lg); };
   // Softmax of tile 0 (reference from its maximum) into P, then the scores of
   // tile 1 (K in slot 1) into S.
   auto first_tile = [&]() __attribute__((always_inline)) {

@@ -56,6 +56,7 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2Six = 2.584962500721156f;   // log2(6), the largest E2M1 value
 constexpr float kRefMax = 24.f;                  // move the reference once a score passes this
+constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kSlot = kMxTile + kMxTileScales;  // bytes of one ring slot (codes, then scales)
 constexpr int kSlots = 4;
 constexpr int kBarEvery = kSlots / 2;
@@ -73,6 +74,39 @@ __device__ __forceinline__ v16f mfma4(const v4i& a, const v4i& b, const v16f& c,
 }
 __device__ __forceinline__ v4f mfma16_4(const v4i& a, const v4i& b, const v4f& c, int sb) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(widen(a), widen(b), c, 4, 4, 0, 127, 0, sb);
+}
+
+// sum of x over lanes l and l^32 (v_permlane32_swap of (x, x) hands each
+// lane the other half's value in one of the two results)
+__device__ __forceinline__ float sum_pair32(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// value of an E2M1 code (OCP MX: sign, 2 exponent bits with bias 1, 1
+// mantissa bit; magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6), built as float bits
+__device__ __forceinline__ float e2m1_value(uint32_t n) {
+  const uint32_t e = (n >> 1) & 3u, m = n & 1u;
+  const uint32_t mag = e != 0u ? ((e + 126u) << 23) | (m << 22) : (m != 0u ? 126u << 23 : 0u);
+  return __uint_as_float(mag | ((n & 8u) << 28));
+}
+
+// sum over this lane's 64 channels of an E2M1 B operand (f[kk]: channels
+// 64*kk + 32*(lane/32) .. +32, two per byte, low nibble first; scale byte kk
+// of sc) times mu (mu[c] for those channels, c = 64*kk + j, already offset by
+// 32*(lane/32))
+__device__ __forceinline__ float dot_mu(const v4i f[2], int sc, const float* mu) {
+  float s = 0.f;
+#pragma unroll
+  for (int kk = 0; kk < 2; kk++) {
+    float t = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; w++)
+#pragma unroll
+      for (int j = 0; j < 8; j++) t += e2m1_value(((uint32_t)f[kk][w] >> (4 * j)) & 15u) * mu[64 * kk + 8 * w + j];
+    s += __builtin_ldexpf(t, ((sc >> (8 * kk)) & 255) - 127);
+  }
+  return s;
 }
 
 __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
@@ -133,7 +167,7 @@ __device__ __forceinline__ void tail_iters(F& iter, int& t, int nlast) {
   }
 }
 
-template <bool QC>
+template <bool QC, bool LSE, bool CAUSAL>
 __global__ __launch_bounds__(64 * kWaves, 2) void k_attn_mx(MxAttentionArgs a) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * kVRing];
 
@@ -143,7 +177,19 @@ __global__ __launch_bounds__(64 * kWaves, 2) void k_attn_mx(MxAttentionArgs a) {
   const int q0 = it.y;
   const int h = it.z;
   const int L = si.len;
-  const int nkt = (L + kBN - 1) / kBN;
+  // key tiles of the item (causal: up to its last query), or of one piece of
+  // a split item: tiles [kt0, kt0 + nkt), whose keys past the range end (Lk
+  // keys from the range start) are masked in the last tile
+  const int nkt_seg = ((CAUSAL ? min(L, q0 + kMxBM) : L) + kBN - 1) / kBN;
+  int kt0 = 0, nkt = nkt_seg, slot = -1;
+  if (it.w != 0) {
+    const int n = split_pieces(it.w), i = split_index(it.w);
+    kt0 = nkt_seg * i / n;
+    nkt = nkt_seg * (i + 1) / n - kt0;
+    slot = split_slot0(it.w) + i;
+  }
+  const int Lk = min(L - kt0 * kBN, nkt * kBN);
+  const int tdiag = q0 / kBN;   // causal: tiles from here on hold keys after some query of the item
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
@@ -152,6 +198,7 @@ __global__ __launch_bounds__(64 * kWaves, 2) void k_attn_mx(MxAttentionArgs a) {
 
   const int64_t hrow = (int64_t)h * a.rows + si.row0;          // first workspace row of the segment
   const int64_t htile = (int64_t)h * (a.rows / kBN) + si.row0 / kBN;
+  const int qi = q0 + 32 * wave + lq;                           // this lane's query (segment-relative)
 
   // Q (B operand): query q0 + 32*wave + lq, channels 64*kk + 32*lg .. +32, and
   // the two scale bytes of those blocks (bytes kk = 0, 1).
@@ -196,10 +243,10 @@ __global__ __launch_bounds__(64 * kWaves, 2) void k_attn_mx(MxAttentionArgs a) {
     const int d = p >> 1;
     srcv = d * (kBN / 2) + (((p & 1) ^ ((d >> 3) & 1)) << 4);
   }
-  const uint8_t* kcb = a.k_codes + hrow * kMxRow;
-  const uint8_t* vcb = a.v_codes + htile * kMxTile;
-  const uint8_t* ksb = a.k_scales + hrow * 4;
-  const uint8_t* vsb = a.v_scales + htile * kMxTileScales;
+  const uint8_t* kcb = a.k_codes + (hrow + kt0 * kBN) * kMxRow;
+  const uint8_t* vcb = a.v_codes + (htile + kt0) * kMxTile;
+  const uint8_t* ksb = a.k_scales + (hrow + kt0 * kBN) * 4;
+  const uint8_t* vsb = a.v_scales + (htile + kt0) * kMxTileScales;
   const __amdgpu_buffer_rsrc_t kcrs = __builtin_amdgcn_make_buffer_rsrc((void*)kcb, (short)0, nkt * kMxTile, kBufferFlags);
   const __amdgpu_buffer_rsrc_t vcrs = __builtin_amdgcn_make_buffer_rsrc((void*)vcb, (short)0, nkt * kMxTile, kBufferFlags);
   const __amdgpu_buffer_rsrc_t ksrs = __builtin_amdgcn_make_buffer_rsrc((void*)ksb, (short)0, nkt * kMxTileScales, kBufferFlags);
@@ -234,6 +281,10 @@ __global__ __launch_bounds__(64 * kWaves, 2) void k_attn_mx(MxAttentionArgs a) {
   v16f S[2];       // exp2 arguments of the current tile, lane keys 32*lg + 16*kb + r
   v4i P;           // E2M1 probabilities of the previous tile, then of the current one
   int pe = 127;    // E8M0 scale byte of this lane's probabilities
+  // LSE: sum of the exact 2^x of this lane's keys, in the frame of nb, over
+  // the tiles whose probabilities have gone into O (lex), and over the tile in
+  // P (lp; added once the rescale for its reference has been applied to lex)
+  float lex = 0.f, lp = 0.f;
 
   auto scores = [&](const v4i kf[2][2], const int ks[2], v16f& s0, v16f& s1) __attribute__((always_inline)) {
     if (QC) {
@@ -264,6 +315,7 @@ __global__ __launch_bounds__(64 * kWaves, 2) void k_attn_mx(MxAttentionArgs a) {
       auto pa = __builtin_amdgcn_permlane16_swap(__float_as_uint(alpha), __float_as_uint(alpha), false, false);
       lacc[0] *= alpha;
       lacc[1] *= __uint_as_float(pa[1]);   // lane j < 16: alpha of query 16+j
+      if (LSE) lex *= alpha;
 #pragma unroll
       for (int db = 0; db < 4; db++) O[db] *= alpha;
       pshift = 0.f;
@@ -320,16 +372,26 @@ __global__ __launch_bounds__(64 * kWaves, 2) void k_attn_mx(MxAttentionArgs a) {
     float p[8];
 #pragma unroll
     for (int i = 0; i < 8; i++) p[i] = __builtin_amdgcn_exp2f(S[w >> 1][8 * (w & 1) + i]);
+    if (LSE) lp += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
     return cvt8(p, scale);
   };
   auto scale_of = [](int e) { return __uint_as_float((uint32_t)(e + 127) << 23); };
-  // scores past the segment end (tile-relative key >= klim) to -inf
+  // scores of tile-relative keys >= klim to -inf (klim may differ per lane)
+  // Without compares: min(S, +-inf) with the sign of (klim - key - 1/2).
   auto mask_tail = [&](int klim) __attribute__((always_inline)) {
+    const float kf = (float)(klim - 32 * lg) - 0.5f;
 #pragma unroll
     for (int kb = 0; kb < 2; kb++)
 #pragma unroll
-      for (int r = 0; r < 16; r++)
-        if (32 * lg + 16 * kb + r >= klim) S[kb][r] = -__builtin_huge_valf();
+      for (int r = 0; r < 16; r++) {
+        const float d = kf - (float)(16 * kb + r);
+        S[kb][r] = __builtin_fminf(S[kb][r], __uint_as_float((__float_as_uint(d) & 0x80000000u) | 0x7f800000u));
+      }
+  };
+  // the limit of tile t: keys past the range end and, causal, keys after this
+  // lane's query
+  auto klim_of = [&](int t) __attribute__((always_inline)) {
+    return CAUSAL ? min(Lk, qi + 1) - t * kBN : Lk - t * kBN;
   };
 
   // Prologue: K(0), K(1), K(2), V(0), V(1); wait for K(0): the loads issued
@@ -354,7 +416,7 @@ __global__ __launch_bounds__(64 * kWaves, 2) void k_attn_mx(MxAttentionArgs a) {
   for (int i = 1; i <= kBarEvery; i++) load_k(kBarEvery + i, (kBarEvery + i) % kSlots);
 #pragma unroll
   for (int i = 0; i < kBarEvery; i++) load_v(kBarEvery + i, (kBarEvery + i) % kSlots);
-  if (nkt == 1) mask_tail(L);
+  if (nkt == 1 || (CAUSAL && tdiag == 0)) mask_tail(klim_of(0));
   {
     pe = rowmax_update(std::true_type{});
     const float sc = scale_of(pe);
@@ -389,6 +451,10 @@ __global__ __launch_bounds__(64 * kWaves, 2) void k_attn_mx(MxAttentionArgs a) {
       barrier();
     }
     rescale();
+    if (LSE) {
+      lex += lp;
+      lp = 0.f;
+    }
     if (PH % kBarEvery == 0) {
 #pragma unroll
       for (int i = 1; i <= kBarEvery; i++) load_k(t + kBarEvery + i, (PH + kBarEvery + i) % kSlots);
@@ -401,6 +467,7 @@ __global__ __launch_bounds__(64 * kWaves, 2) void k_attn_mx(MxAttentionArgs a) {
     int ks[2];
     read_k(kbp, kf, ks);
     O[0] = mfma4<0, 0>(vf[0], P, O[0], vsc, pe);
+    if (CAUSAL && t >= tdiag) mask_tail(klim_of(t));   // wave-uniform branch, diagonal tiles only
     const int e = rowmax_update(std::false_type{});
     const float sc = scale_of(e);
     v16f s0, s1;
@@ -457,12 +524,16 @@ __global__ __launch_bounds__(64 * kWaves, 2) void k_attn_mx(MxAttentionArgs a) {
   wait_vmcnt<0>();
   barrier();
   rescale();
+  if (LSE) {
+    lex += lp;
+    lp = 0.f;
+  }
   if (nkt > 1) {
     const int tl = nkt - 1;
 #pragma unroll
     for (int db = 0; db < 4; db++) O[db] = mfma4<0, 0>(vf[db], P, O[db], __builtin_amdgcn_ubfe(vsc, 8 * db, 8), pe);
     lacc = mfma16_4(sel, P, lacc, pe);
-    mask_tail(L - tl * kBN);
+    mask_tail(klim_of(tl));
     const int e = rowmax_update(std::false_type{});
     rescale();
     const float sc = scale_of(e);
@@ -477,18 +548,39 @@ __global__ __launch_bounds__(64 * kWaves, 2) void k_attn_mx(MxAttentionArgs a) {
 #pragma unroll
   for (int db = 0; db < 4; db++) O[db] = mfma4<0, 0>(vf[db], P, O[db], __builtin_amdgcn_ubfe(vsc, 8 * db, 8), pe);
   lacc = mfma16_4(sel, P, lacc, pe);
+  if (LSE) lex += lp;
   // The products must run with every lane active: a matrix instruction inside
   // the store's lane-divergent branch would read the operands of inactive
   // lanes (other queries' keys and channels) as zero.
 #pragma unroll
   for (int db = 0; db < 4; db++) keep(O[db]);
 
-  // epilogue: out = O / l, rounded to BF16 once
-  const int qrow = q0 + 32 * wave + lq;
+  // epilogue: out = O / l, rounded to BF16 once; O^T: lane l holds query
+  // l%32, channels 32*db + 8*(r/4) + 4*(l/32) + r%4 in register r of block db
+  const int qrow = qi;
   const float l0 = __shfl(lacc[0], lq & 15);
   const float l1 = __shfl(lacc[1], lq & 15);
   const float lt = lq < 16 ? l0 : l1;
-  if (qrow < L) {
+  if (slot >= 0) {
+    // one piece of a split item: the normalized partial output and the log2
+    // of its weight sum with the frame offset taken out (the probabilities
+    // scale by exactly 2^nb), for the combine pass.  The piece's first tile
+    // sets nb so that its largest probability is near 1, so lt > 0; a zero
+    // sum would still give weight 0 (w = -inf) and O = 0.
+    if (qrow < L) {
+      const int prow = slot * kPartRows + 32 * wave + lq;
+      const float inv = lt > 0.f ? 1.f / lt : 0.f;
+      float* orow = a.part_o + (size_t)prow * kHeadDim;
+#pragma unroll
+      for (int db = 0; db < 4; db++)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; q4++)
+          *reinterpret_cast<float4*>(orow + 32 * db + 8 * q4 + 4 * lg) =
+              make_float4(O[db][4 * q4 + 0] * inv, O[db][4 * q4 + 1] * inv, O[db][4 * q4 + 2] * inv,
+                          O[db][4 * q4 + 3] * inv);
+      if (lg == 0) a.part_w[prow] = lt > 0.f ? __log2f(lt) - nb : -__builtin_huge_valf();
+    }
+  } else if (qrow < L) {
     const float inv = 1.f / lt;
     uint16_t* orow = a.out + (int64_t)(si.start + qrow) * a.os0 + (int64_t)h * a.os1;
 #pragma unroll
@@ -503,16 +595,50 @@ __global__ __launch_bounds__(64 * kWaves, 2) void k_attn_mx(MxAttentionArgs a) {
         *reinterpret_cast<uint2*>(orow + d) = make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
       }
   }
+  if (LSE) {
+    // natural-log LSE of the uncentred scores: the exact sum of 2^x over the
+    // visible keys (masked keys added 0), the frame offset nb taken out, plus
+    // (Qhat + QMhat) . mu, the part of every score that centring K by its
+    // segment mean mu took out (both operands carry the score factor, so the
+    // term is in log2 units).  Each lane holds half of its query's channels.
+    const float* mu = a.mu + ((size_t)it.x * a.heads + h) * kHeadDim + 32 * lg;
+    float qmu = dot_mu(qf, qsc, mu);
+    if (QC) qmu += dot_mu(mf, msc, mu);
+    const float le = sum_pair32(lex);
+    const float qm_all = sum_pair32(qmu);
+    if (lg == 0 && qrow < L) {
+      const float v = (__log2f(le) - nb + qm_all) * kLn2;
+      if (slot >= 0)
+        a.part_lse[slot * kPartRows + 32 * wave + lq] = v;
+      else
+        a.lse[(int64_t)h * a.tokens + si.start + qrow] = v;
+    }
+  }
 }
 
 }  // namespace
 
+template <bool QC>
+void launch_mx_q(const MxAttentionArgs& a, hipStream_t stream) {
+  const dim3 g(a.nitems), b(64 * kWaves);
+  if (a.causal) {
+    if (a.lse != nullptr)
+      hipLaunchKernelGGL((k_attn_mx<QC, true, true>), g, b, 0, stream, a);
+    else
+      hipLaunchKernelGGL((k_attn_mx<QC, false, true>), g, b, 0, stream, a);
+  } else if (a.lse != nullptr) {
+    hipLaunchKernelGGL((k_attn_mx<QC, true, false>), g, b, 0, stream, a);
+  } else {
+    hipLaunchKernelGGL((k_attn_mx<QC, false, false>), g, b, 0, stream, a);
+  }
+}
+
 hipError_t launch_attention_mx(const MxAttentionArgs& a, hipStream_t stream) {
   if (a.nitems == 0) return hipSuccess;
   if (a.q_centre)
-    hipLaunchKernelGGL(k_attn_mx<true>, dim3(a.nitems), dim3(64 * kWaves), 0, stream, a);
+    launch_mx_q<true>(a, stream);
   else
-    hipLaunchKernelGGL(k_attn_mx<false>, dim3(a.nitems), dim3(64 * kWaves), 0, stream, a);
+    launch_mx_q<false>(a, stream);
   return hipGetLastError();
 }
 

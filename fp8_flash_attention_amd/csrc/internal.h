@@ -158,13 +158,21 @@ struct MxAttentionArgs {
   const uint8_t* v_scales;
   const uint8_t* qm_codes;   // used with q_centre
   const uint8_t* qm_scales;
+  const float* mu;           // [nseg][H][128]: K's segment means (for the LSE)
   const SegInfo* segs;
-  const int4* items;         // work items (no key splits)
+  const int4* items;         // work items (encoding above)
   uint16_t* out;             // bf16
   int64_t os0, os1;
+  float* lse;                // nullable, [H][T]
+  float* part_o;             // partial outputs of split items (as for E4M3 plans)
+  float* part_w;
+  float* part_lse;
+  int64_t tokens;
   int64_t rows;
+  int32_t heads;
   int32_t nitems;
   int32_t q_centre;
+  int32_t causal;            // 1: query i of a segment attends keys j <= i only
 };
 
 hipError_t launch_quantize(const QuantizeArgs& a, hipStream_t stream);

@@ -50,7 +50,7 @@ typedef struct fp8attn_plan_s* fp8attn_plan_t;
 typedef enum {
   FP8ATTN_OK = 0,
   FP8ATTN_EINVAL = 1,        /* bad argument (NULL, size, stride, alignment, cu_seqlens) */
-  FP8ATTN_EUNSUPPORTED = 2,  /* a request outside dense non-causal D=128 BF16 */
+  FP8ATTN_EUNSUPPORTED = 2,  /* a size beyond the library's limits (32-bit offsets, static buffer) */
   FP8ATTN_ENOMEM = 3,        /* host or device allocation of plan tables failed */
   FP8ATTN_EWORKSPACE = 4,    /* workspace pointer NULL/misaligned or smaller than needed */
   FP8ATTN_EHIP = 5           /* a HIP runtime call or kernel launch failed */
@@ -143,21 +143,25 @@ fp8attn_status fp8attn_plan(fp8attn_plan_t* plan_out, int64_t tokens, int32_t he
  *   2^E * E2M1(2^(x - E)) with x its scores in log2 units and
  *   E = ceil(max_b x - log2 6); out = sum phat V / sum phat, rounded to BF16.
  *   Expect several times the E4M3 error (the page reports about 4x for its
- *   NVFP4 recipe).  fp8attn_forward rejects an lse request for these plans
- *   (FP8ATTN_EUNSUPPORTED) and never splits work items.
+ *   NVFP4 recipe).  The LSE (if requested) is the natural-log log-sum-exp of
+ *   the uncentred scores from the dequantized operands:
+ *   ln 2 * (log2 sum_j 2^(x_j) + (Qhat + QMhat) . mu), the FP32 sum of the
+ *   unrounded 2^x (not of the E2M1 probabilities).  Work items split along
+ *   the keys as for E4M3 plans (128-query items, two workgroups per CU).
  * FP8ATTN_PLAN_Q_CENTRE (with FP8ATTN_PLAN_MXFP4 only): Q rows are centred by
  *   the mean of their 128-row block (blocks of a segment from its start; the
  *   mean is a float64 sum over the block's rows in order, divided by the row
  *   count, rounded to float32); the block-mean operand fl32(qm * c), quantized
  *   like a Q row, is multiplied with K inside the kernel and added to the
  *   scores, so the softmax is that of the uncentred Q (the page's Q centring).
- * FP8ATTN_PLAN_CAUSAL (E4M3 plans): query i of a segment attends only to the
+ * FP8ATTN_PLAN_CAUSAL: query i of a segment attends only to the
  *   keys j <= i of the same segment, positions counted from the segment start
  *   (the pages send causal attention to another backend; this is the plain
  *   reading for self-attention).  A work item attends to the key tiles up to
  *   its last query; the tiles from its first query on are masked per element.
  *   The LSE (if requested) is over the visible keys.  Causal plans never split
- *   work items.
+ *   work items.  With FP8ATTN_PLAN_MXFP4 a query's last probability block
+ *   holds its visible keys only (its scale comes from their maximum).
  * FP8ATTN_PLAN_HEAD_DIM_64 (E4M3 plans): q, k, v and out have 64 channels
  *   per head instead of FP8ATTN_HEAD_DIM (P1 lists other head sizes among the
  *   cases it sends elsewhere): every region, stride and scale rule below
@@ -170,8 +174,7 @@ fp8attn_status fp8attn_plan(fp8attn_plan_t* plan_out, int64_t tokens, int32_t he
  * Unknown flag bits, FP8ATTN_PLAN_Q_CENTRE without FP8ATTN_PLAN_MXFP4,
  * FP8ATTN_PLAN_EXACT_PROBS with FP8ATTN_PLAN_MXFP4,
  * FP8ATTN_PLAN_MXFP4 with FP8ATTN_PLAN_SEGMENT_SCALES (its scales are already
- * local to 32 elements), with FP8ATTN_PLAN_CAUSAL or with
- * FP8ATTN_PLAN_HEAD_DIM_64: FP8ATTN_EINVAL.
+ * local to 32 elements) or with FP8ATTN_PLAN_HEAD_DIM_64: FP8ATTN_EINVAL.
  */
 fp8attn_status fp8attn_plan_ex(fp8attn_plan_t* plan_out, int64_t tokens, int32_t heads,
                                const int32_t* cu_seqlens_host, int32_t num_segments,

@@ -295,8 +295,8 @@ def test_workspace_region_host_plan():
 
 def test_python_wrapper_rejects_unsupported():
     import torch
-    with pytest.raises(fa.Fp8AttnError):                 # causal FP4 plans
-        fa.Plan(256, 2, [0, 256], device=-1, fmt="mxfp4", causal=True)
+    with pytest.raises(fa.Fp8AttnError):                 # FP4 plans of 64 channels
+        fa.Plan(256, 2, [0, 256], device=-1, fmt="mxfp4", head_dim=64)
     with pytest.raises(ValueError):                      # head_dim other than 128
         fa._strides(torch.zeros((4, 2, 64), dtype=torch.bfloat16), "q")
     with pytest.raises(TypeError):                       # non-BF16 input
@@ -343,9 +343,11 @@ def test_mxfp4_plan_flags_layout_and_schedule():
     assert mx.workspace_bytes < e4.workspace_bytes
 
 
-def test_mxfp4_plan_never_splits():
-    """A schedule whose E4M3 plan splits its last round has no split items as FP4."""
-    cus = 32 * 8
+def test_mxfp4_plan_schedule_and_splits():
+    """The graded schedules have no split items as FP4 (every (segment,
+    128-query tile, head) once); a schedule that leaves a short last round is
+    split along the keys as for E4M3 plans, and its workspace holds the
+    partial regions."""
     for cu in ([0, 4096], [0, 15104, 30208, 30208, 30271, 30272], [0, 2048, 2100]):
         T = cu[-1]
         e4 = fa.Plan(T, 56, cu, device=-1)
@@ -354,11 +356,26 @@ def test_mxfp4_plan_never_splits():
         items = mx.work_items()
         assert all(it[3] == 0 for it in items)
         real = [it for it in items if it[0] >= 0]
-        # every (segment, 128-query tile, head) once
         want = {(s, q0, h, 0) for s in range(len(cu) - 1) for h in range(56)
                 for q0 in range(0, cu[s + 1] - cu[s], 128)}
         assert len(real) == len(want) and set(real) == want
         assert mx.info()["work_items"] == len(real)
+    # 2048 tokens x 4 heads: 64 items, 8 per XCD, a last round of 8 items
+    # for 32 compute units: each item in four pieces of 8 key tiles
+    cu = [0, 2048]
+    mx = fa.Plan(2048, 4, cu, device=-1, fmt="mxfp4")
+    items = [it for it in mx.work_items() if it[0] >= 0]
+    assert all(it[3] != 0 for it in items)
+    assert {(it[3] >> 4) & 15 for it in items} == {4}
+    assert mx.info()["partial_slots"] == 64 * 4
+    pieces = {}
+    for s, q0, h, w in items:
+        pieces.setdefault((s, q0, h, w >> 8), []).append(w & 15)
+    assert len(pieces) == 64 and all(sorted(v) == [0, 1, 2, 3] for v in pieces.values())
+    nosplit = fa.Plan(4096, 56, [0, 4096], device=-1, fmt="mxfp4")
+    assert nosplit.info()["partial_slots"] == 0
+    # the partial slots (256 rows of 128 floats, plus two floats a row) are in the workspace
+    assert mx.workspace_bytes >= 256 * 256 * (128 + 2) * 4
 
 
 def test_causal_plan_schedule():
@@ -372,13 +389,14 @@ def test_causal_plan_schedule():
     segs = {0: 4096, 2: 404}
     want = {(s, q0, h) for s, L in segs.items() for h in range(8) for q0 in range(0, L, 256)}
     assert {(s, q, h) for s, q, h, _ in items} == want
-    L = _lib.lib()
-    h = ctypes.c_void_p()
-    arr = (ctypes.c_int32 * 2)(0, 256)
-    assert L.fp8attn_plan_ex(ctypes.byref(h), 256, 2, arr, 1, ctypes.c_float(0.088), -1,
-                             _lib.PLAN_CAUSAL | _lib.PLAN_MXFP4) == _lib.EINVAL
-    # a non-causal plan of the same table splits nothing away from these items either
     assert p.info()["work_items"] == len(items)
+    # causal FP4 plans: 128-query items, no splits, every (segment, tile, head) once
+    mx = fa.Plan(4500, 8, cu, device=-1, causal=True, fmt="mxfp4", q_centre=True)
+    assert mx.info()["causal"] == 1 and mx.info()["partial_slots"] == 0 and mx.info()["query_tile"] == 128
+    items = [it for it in mx.work_items() if it[0] >= 0]
+    assert all(it[3] == 0 for it in items)
+    want = {(s, q0, h) for s, L in segs.items() for h in range(8) for q0 in range(0, L, 128)}
+    assert len(items) == len(want) and {(s, q, h) for s, q, h, _ in items} == want
 
 
 def test_batched_wrapper_rejects_cu_seqlens():

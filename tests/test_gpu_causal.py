@@ -16,7 +16,6 @@ import pytest
 import torch
 
 import fp8_flash_attention_amd as fa
-from fp8_flash_attention_amd import _lib
 from oracle import attention as A
 from oracle import compare
 from oracle import quantize as Qz
@@ -131,8 +130,3 @@ def test_batched_input_through_the_binding():
         ref = A.attention(q.cpu(), k.cpu(), v.cpu(), w.cu_seqlens, w.softmax_scale, causal=causal).numpy()
         assert compare.rel_rms(o3.cpu().double().numpy(), ref) <= compare.REL_RMS_BAR
 
-
-def test_causal_rejected_for_fp4_plans():
-    with pytest.raises(fa.Fp8AttnError) as e:
-        fa.Plan(256, 2, [0, 256], device=0, fmt="mxfp4", causal=True)
-    assert e.value.status == _lib.EINVAL
