@@ -110,21 +110,27 @@ class ClockSampler:
         self._threading = threading
 
     def _read(self):
+        """(metrics timestamp, MHz) of the current metrics table, or None."""
         m = self._amdsmi.amdsmi_get_gpu_metrics_info(self._h)
+        ts = m.get("system_clock_counter")
         vals = m.get("current_gfxclks")
         if isinstance(vals, (list, tuple)):
             vals = [v for v in vals if isinstance(v, (int, float)) and 0 < v < 10000]
             if vals:
-                return sum(vals) / len(vals)
+                return ts, sum(vals) / len(vals)
         v = m.get("current_gfxclk")
-        return float(v) if isinstance(v, (int, float)) and 0 < v < 10000 else None
+        return (ts, float(v)) if isinstance(v, (int, float)) and 0 < v < 10000 else None
 
     def _run(self):
+        seen = set()
         while not self._stop.is_set():
             try:
-                v = self._read()
-                if v is not None:
-                    self.samples.append(v)
+                r = self._read()
+                # keep one sample per refresh of the metrics table: the driver
+                # updates it far less often than this thread reads it
+                if r is not None and (r[0] is None or r[0] not in seen):
+                    seen.add(r[0])
+                    self.samples.append(r[1])
             except Exception as e:  # noqa: BLE001
                 self.error = f"{type(e).__name__}: {e}"
                 return
@@ -143,8 +149,9 @@ class ClockSampler:
         return False
 
     def summary(self):
-        if not self.samples:
-            return {"samples": 0, "error": self.error}
+        if len(self.samples) < 2:
+            return {"samples": len(self.samples), "error": self.error or
+                    "the metrics table was not refreshed during the timed region"}
         # samples taken while the GPU idled (before the first launch, between
         # repetitions) read the idle clock: keep those above half the highest
         top = max(self.samples)
@@ -152,7 +159,8 @@ class ClockSampler:
         pct = lambda f: round(v[min(len(v) - 1, int(f * len(v)))], 0)   # noqa: E731
         return {"median_mhz": pct(0.5), "p05_mhz": pct(0.05), "p95_mhz": pct(0.95), "samples": len(v),
                 "idle_samples_dropped": len(self.samples) - len(v),
-                "source": "amdsmi gpu_metrics current_gfxclks (mean over XCDs), sampled every 5 ms"}
+                "source": "amdsmi gpu_metrics current_gfxclks (mean over XCDs), one sample per refresh "
+                          "of the metrics table (polled every 5 ms)"}
 
 
 def protocol(fn, stream, warmup: int = 20, reps: int = 5, per: int = 10):
@@ -221,6 +229,7 @@ def main() -> int:
                     help="e4m3: probabilities rounded from the FP32 exp2 instead of the log-linear code")
     ap.add_argument("--causal", action="store_true",
                     help="causal plan (FLOPs then count the visible pairs, 2 * sum L(L+1) * H * D)")
+    ap.add_argument("--lse", action="store_true", help="the forward also writes the LSE output")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="after timing, run one plain device copy of BYTES bytes (a known-size "
                          "reference dispatch for scaling HBM traffic counters)")
@@ -246,13 +255,14 @@ def main() -> int:
                    exact_probs=args.exact_probs and not mx)
     ws = plan.new_workspace()
     out = torch.empty((w.tokens, w.heads, w.head_dim), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((w.heads, w.tokens), dtype=torch.float32, device=dev) if args.lse else None
     stream = torch.cuda.current_stream(dev)
 
     def step(ev=None):
         fa.quantize(plan, q, k, v, ws)
         if ev is not None:
             ev[0].record(stream)
-        fa.forward(plan, ws, out)
+        fa.forward(plan, ws, out, lse)
         if ev is not None:
             ev[1].record(stream)
 
@@ -278,7 +288,7 @@ def main() -> int:
     # shader clock sampled meanwhile), the quantize and the whole step
     sampler = ClockSampler(0)
     with sampler:
-        fwd_proto = protocol(lambda: fa.forward(plan, ws, out), stream)
+        fwd_proto = protocol(lambda: fa.forward(plan, ws, out, lse), stream)
     quant_proto = protocol(lambda: fa.quantize(plan, q, k, v, ws), stream)
     step_proto = protocol(step, stream)
     ms_step = wall * 1e3 / args.steps
@@ -305,7 +315,7 @@ def main() -> int:
     peak = FP4_PEAK_TFLOPS if mx else FP8_PEAK_TFLOPS
     kfile = "attention_mx.hip" if mx else "attention.hip"
     key = (w.name + (":mxfp4" + (":qc" if args.q_centre else "") if mx else "") + (":causal" if args.causal else "")
-           + (":exact" if args.exact_probs and not mx else ""))
+           + (":exact" if args.exact_probs and not mx else "") + (":lse" if args.lse else ""))
     traffic = measured_traffic(key, kfile)
     res = {
         "metric": (METRIC_FP4 if mx else (METRIC_CAUSAL if args.causal else METRIC)) + (
@@ -327,6 +337,7 @@ def main() -> int:
                    "k_offset_var": w.k_offset_var, "step": "quantize + forward",
                    **({"format": "mxfp4", "q_centre": bool(args.q_centre)} if mx else {}),
                    **({"causal": True} if args.causal else {}),
+                   **({"lse": True} if args.lse else {}),
                    **({} if mx else {"probabilities": "exact exp2" if args.exact_probs else "log-linear E4M3 code"})},
         "forward_ms": round(ms_fwd, 4),
         "forward_tflops": round(fwd_tflops, 2),

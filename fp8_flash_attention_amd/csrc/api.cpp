@@ -314,6 +314,7 @@ fp8attn_status fp8attn_plan_ex(fp8attn_plan_t* plan_out, int64_t tokens, int32_t
   if (cu == nullptr) return fail(FP8ATTN_EINVAL, "cu_seqlens_host is NULL");
   if (num_segments < 1) return fail(FP8ATTN_EINVAL, "num_segments must be >= 1");
   if (heads < 1) return fail(FP8ATTN_EINVAL, "heads must be >= 1");
+  if (heads > 65535) return fail(FP8ATTN_EUNSUPPORTED, "heads must be <= 65535 (grid dimension)");
   if (tokens < 0) return fail(FP8ATTN_EINVAL, "tokens must be >= 0");
   if (tokens > (int64_t)INT32_MAX / 2) return fail(FP8ATTN_EUNSUPPORTED, "tokens too large (int32 indexing)");
   if (!std::isfinite(softmax_scale) || !(softmax_scale > 0.f))
@@ -359,10 +360,10 @@ fp8attn_status fp8attn_plan_ex(fp8attn_plan_t* plan_out, int64_t tokens, int32_t
   row += kGuardRows;
   // the attention kernel addresses one head's code rows through 32-bit buffer
   // offsets: rows * 128 bytes must fit
-  if (row * p->head_dim > (int64_t)INT32_MAX) {
+  if (row * p->head_dim > (int64_t)INT32_MAX || (row / kPackRows) * heads > (int64_t)INT32_MAX) {
     delete p;
     return fail(FP8ATTN_EUNSUPPORTED, "too many padded rows for 32-bit code offsets (about 16.7M tokens at most "
-                                      "at head_dim 128)");
+                                      "at head_dim 128) or too many 64-row groups times heads for one grid");
   }
   int cus = 256;   // MI355X; the device's own count when the plan has one
   if (device >= 0) {

@@ -40,8 +40,9 @@
 //     constant 0/1 selector, which adds the 64 key bytes of query j (lanes j
 //     and j+32) into row 0 and those of query 16+j (lanes j+16 and j+48) into
 //     row 1.  l is the sum of the E4M3 probabilities that actually weight V.
-//     When the caller asks for the LSE, an FP32 sum of the unrounded
-//     probabilities is kept as well.
+//     The LSE, when asked for, is the log of l (the denominator the output
+//     is normalized by, so partial results combine exactly by it); with exact
+//     probabilities an FP32 sum of the unrounded 2^x is kept for it instead.
 //   * Probabilities: p = 2^x, x = c*s + nbx with c = softmax_scale * s_q *
 //     s_k * log2(e) and nbx = log2(112) - c*m for a per-query reference
 //     maximum m.  The quantizer makes c a power of two, so the score products
@@ -207,6 +208,7 @@ __global__ __launch_bounds__(2 * BM, 256 / BM) void k_attn(AttentionArgs a) {
   constexpr float kRef = EXACT ? kLog2Ref : kYRef;
   constexpr float kMax = EXACT ? kLog2Max : kYMax;
   constexpr float kUnit = EXACT ? 1.f : 0.125f;   // log2 units per unit of the frame
+  constexpr bool LSUM = LSE && EXACT;             // the LSE from an FP32 sum of the unrounded 2^x
   static_assert(BM == 128 || BM == 256, "4 or 8 waves x 32 queries");
   constexpr int kTile = kBN * D;                 // bytes of one K (or V^T) tile
   constexpr int kVRing = kSlots * kTile;         // V ring follows the K ring in LDS
@@ -346,7 +348,7 @@ __global__ __launch_bounds__(2 * BM, 256 / BM) void k_attn(AttentionArgs a) {
 
   v16f O[NDB];     // O^T: lane l holds query l%32, channels 32*db + 8*(r/4) + 4*(l/32) + r%4
   v4f lacc = {};   // row sums of the packed P: lane j < 16 holds query j (row 0) and 16+j (row 1)
-  float lex = 0.f; // FP32 row sum of the unrounded probabilities (LSE only; this lane's keys, current frame)
+  float lex = 0.f; // FP32 row sum of the unrounded probabilities (LSUM only; this lane's keys, current frame)
   float nb = 0.f;  // exp2 argument offset: x = c*s + nb
   float pshift = 0.f;   // reference shift still to be applied to O and l (log2 of the factor)
   bool pending = false; // wave-uniform: some lane has a pshift
@@ -424,7 +426,7 @@ __global__ __launch_bounds__(2 * BM, 256 / BM) void k_attn(AttentionArgs a) {
         const float shift = over ? kRef - xm : 0.f;
         nb += shift;
         pshift = shift;
-        if (LSE) lex *= __builtin_amdgcn_exp2f(shift * kUnit);   // lex takes this tile's p in the new frame
+        if (LSUM) lex *= __builtin_amdgcn_exp2f(shift * kUnit);   // lex takes this tile's p in the new frame
 #pragma unroll
         for (int i = 0; i < 16; i++) { S[0][i] += shift; S[1][i] += shift; NB[i] += shift; }
       }
@@ -436,17 +438,12 @@ __global__ __launch_bounds__(2 * BM, 256 / BM) void k_attn(AttentionArgs a) {
       float p[4];
 #pragma unroll
       for (int i = 0; i < 4; i++) p[i] = __builtin_amdgcn_exp2f(S[kb][4 * q4 + i]);
-      if (LSE) {
+      if (LSUM) {
 #pragma unroll
         for (int i = 0; i < 4; i++) lex += p[i];
       }
       return cvt4(p[0], p[1], p[2], p[3]);
     } else {
-      if (LSE) {   // the FP32 sum takes exp2 of x = (y - kYBias) / 8
-#pragma unroll
-        for (int i = 0; i < 4; i++)
-          lex += __builtin_amdgcn_exp2f(__builtin_fmaf(S[kb][4 * q4 + i], 0.125f, -kYBias * 0.125f));
-      }
       uint32_t w = __builtin_amdgcn_cvt_pk_u8_f32(S[kb][4 * q4 + 0], 0, 0u);
       w = __builtin_amdgcn_cvt_pk_u8_f32(S[kb][4 * q4 + 1], 1, w);
       w = __builtin_amdgcn_cvt_pk_u8_f32(S[kb][4 * q4 + 2], 2, w);
@@ -527,7 +524,7 @@ __global__ __launch_bounds__(2 * BM, 256 / BM) void k_attn(AttentionArgs a) {
   // V operands of the next product, read at the end of the iteration before
   // it (all four; two when the LSE sum needs the registers, the other two at
   // the top of the iteration, still ahead of its barrier).
-  constexpr int kPre = NDB == 4 ? (LSE ? 2 : 4) : NDB;
+  constexpr int kPre = NDB == 4 ? (LSUM ? 2 : 4) : NDB;
   v8i vf[NDB];
 #pragma unroll
   for (int db = 0; db < kPre; db++) vf[db] = lds_read32(smem + kVRing + db * 2048, voff[0], voff[1]);
@@ -550,7 +547,7 @@ __global__ __launch_bounds__(2 * BM, 256 / BM) void k_attn(AttentionArgs a) {
     constexpr bool TAIL = decltype(tail_c)::value;   // may be the last tile: mask keys past the range end
     // With the LSE sum, two of the four V(t-1) operands are read here, before
     // the barrier: the loads after it may refill V(t-1)'s slot.
-    if constexpr (LSE && kPre < NDB) {
+    if constexpr (LSUM && kPre < NDB) {
       const uint8_t* vp = smem + kVRing + ((PH + kSlots - 1) % kSlots) * kTile;   // V(t-1)
       vf[2] = lds_read32(vp + 2 * 2048, voff[0], voff[1]);
       vf[3] = lds_read32(vp + 3 * 2048, voff[0], voff[1]);
@@ -600,7 +597,7 @@ __global__ __launch_bounds__(2 * BM, 256 / BM) void k_attn(AttentionArgs a) {
       Pn[4] = probs4(1, 0, kbase);
       fence();
       const v16f s1 = mfma_fp8_scaled(kf[1][0], qf[0], NB, c_e8m0);
-      if (!LSE) {
+      if (!LSUM) {
         vf[2] = lds_read32(vn + 2 * 2048, voff[0], voff[1]);
         vf[3] = lds_read32(vn + 3 * 2048, voff[0], voff[1]);
       }
@@ -676,7 +673,7 @@ __global__ __launch_bounds__(2 * BM, 256 / BM) void k_attn(AttentionArgs a) {
       }
       msel[w] = sel_lane ? word : 0;
     }
-    if constexpr (LSE && kPre < NDB) {
+    if constexpr (LSUM && kPre < NDB) {
       const uint8_t* vp = smem + kVRing + ((nkt - 1) % kSlots) * kTile;
       vf[2] = lds_read32(vp + 2 * 2048, voff[0], voff[1]);
       vf[3] = lds_read32(vp + 3 * 2048, voff[0], voff[1]);
@@ -734,8 +731,10 @@ __global__ __launch_bounds__(2 * BM, 256 / BM) void k_attn(AttentionArgs a) {
       }
   }
   if (LSE) {
-    // (keys past the end of the range were masked, so they added nothing)
-    const float le = sum_pair32(lex);
+    // the log of the denominator (l, or with exact probabilities the FP32 sum
+    // of 2^x; keys past the end of the range were masked, so they added
+    // nothing), back in the frame of the uncentred scores
+    const float le = LSUM ? sum_pair32(lex) : lt;
     if (lg == 0 && qrow < L) {
       const float lse2 = __log2f(le) - nbx;
       const float v = lse2 * kLn2 + a.softmax_scale * s_q * qmu;

@@ -96,8 +96,8 @@ __global__ __launch_bounds__(256) void k_stats(QuantizeArgs a) {
     float mn[8], mx[8];
 #pragma unroll
     for (int i = 0; i < 8; i++) { sum[i] = 0.0; mn[i] = __builtin_inff(); mx[i] = -__builtin_inff(); }
-#pragma unroll 8
-    for (int j = 0; j < ch.ntok; j++) {   // unrolled: eight loads in flight, sums still in token order
+#pragma unroll 16
+    for (int j = 0; j < ch.ntok; j++) {   // unrolled: 16 loads in flight, sums still in token order
       const uint4 v = *reinterpret_cast<const uint4*>(base + (int64_t)(ch.tok0 + j) * ts);
       float f[8];
       unpack8(v, f);
@@ -116,8 +116,8 @@ __global__ __launch_bounds__(256) void k_stats(QuantizeArgs a) {
 
   float m = 0.f;
   if (active) {
-#pragma unroll 8
-    for (int j = 0; j < ch.ntok; j++) {   // unrolled: eight loads in flight, sums still in token order
+#pragma unroll 16
+    for (int j = 0; j < ch.ntok; j++) {   // unrolled: 16 loads in flight, sums still in token order
       const uint4 v = *reinterpret_cast<const uint4*>(base + (int64_t)(ch.tok0 + j) * ts);
       float f[8];
       unpack8(v, f);
@@ -257,10 +257,15 @@ __global__ __launch_bounds__(D) void k_finalize(QuantizeArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Pass 2: pack.  grid = (ngroups, H, 3), block = 256.  One block writes one
+// Pass 2: pack.  grid = (ngroups * H, 1, 3), block = 256.  One block writes one
 // 64-row group of one head of one tensor; rows past the segment's end (and the
 // guard rows) are written as zero codes, so every workspace byte the attention
-// kernel can read is defined and finite.
+// kernel can read is defined and finite.  Blocks run head-fastest (the blocks
+// in flight together read whole token rows of the [T][H][128] input) and in
+// reverse (V, K, Q; last groups first), starting on rows the statistics pass
+// read last, which the last-level cache may still hold: 0.685 -> 0.647 ms for
+// the whole quantize at S=30272, H=56 (with 16 statistics loads in flight,
+// 0.635 ms).
 //
 // Q, K codes: row-major [H][rows][128].  V codes: transposed [H][128][rows]
 // with the keys of each 64-row group permuted so that the attention kernel's
@@ -272,9 +277,10 @@ __global__ __launch_bounds__(256) void k_pack(QuantizeArgs a) {
   constexpr int TPH = D / 8;        // threads per row, 8 channels each
   constexpr int RPP = 256 / TPH;    // rows per pass
   __shared__ uint8_t tile[kPackRows][D + 16];
-  const int g = blockIdx.x;
-  const int h = blockIdx.y;
-  const int tensor = blockIdx.z;
+  const int bx = gridDim.x - 1 - blockIdx.x;
+  const int g = bx / a.heads;
+  const int h = bx % a.heads;
+  const int tensor = 2 - blockIdx.z;
   const int t = threadIdx.x;
   const int seg = a.group_seg[g];
   const int64_t R = (int64_t)g * kPackRows;  // first workspace row of the group
@@ -549,7 +555,7 @@ hipError_t launch_quantize_d(const QuantizeArgs& a, hipStream_t stream) {
   if (a.mx)
     hipLaunchKernelGGL(k_pack_mx, dim3(a.ngroups, a.heads, 3), dim3(256), 0, stream, a);
   else
-    hipLaunchKernelGGL(k_pack<D>, dim3(a.ngroups, a.heads, 3), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(k_pack<D>, dim3(a.ngroups * a.heads, 1, 3), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

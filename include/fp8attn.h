@@ -91,7 +91,7 @@ typedef enum {
  *
  *   plan_out         receives the new plan (set to NULL on error).
  *   tokens           T >= 0, total tokens of the packed batch.
- *   heads            H >= 1.
+ *   heads            1 <= H <= 65535 (FP8ATTN_EUNSUPPORTED above).
  *   cu_seqlens_host  host int32 array of num_segments + 1 entries: cu[0] == 0,
  *                    non-decreasing, cu[num_segments] == tokens (FlashInfer page,
  *                    parameter "cu_seqlens").  Copied; the caller keeps ownership.
@@ -105,7 +105,9 @@ typedef enum {
  *
  * Workspace rows: each segment occupies round_up(L, 128) rows of the code
  * regions, segments in order, followed by 128 guard rows; every row past a
- * segment's end is written as zero codes by fp8attn_quantize.
+ * segment's end is written as zero codes by fp8attn_quantize.  A plan whose
+ * rows times head_dim, or rows / 64 times heads, passes 2^31 - 1 is rejected
+ * with FP8ATTN_EUNSUPPORTED (32-bit code offsets and grid sizes).
  */
 fp8attn_status fp8attn_plan(fp8attn_plan_t* plan_out, int64_t tokens, int32_t heads,
                             const int32_t* cu_seqlens_host, int32_t num_segments,
@@ -254,8 +256,14 @@ fp8attn_status fp8attn_quantize_noalloc(fp8attn_plan_t plan, const void* q, cons
  *               multiples of 8, base 16-byte aligned.  Every row of every
  *               non-empty segment is written.
  * lse           NULL, or device float [heads][tokens]: natural-log
- *               log-sum-exp of softmax_scale * q.k over the row's segment
- *               (uncentred keys).
+ *               log-sum-exp of softmax_scale * q.k over the row's keys
+ *               (uncentred keys), taken as the log of the denominator that
+ *               normalizes the row: for default E4M3 plans the sum of the
+ *               probability weights applied to V (each within a factor
+ *               [0.9203, 1.0645] of the exact exp, see below), so partial
+ *               results combine by it exactly; with
+ *               FP8ATTN_PLAN_EXACT_PROBS and for FP4 plans the FP32 sum of
+ *               the unrounded exponentials.
  * stream        hipStream_t (NULL = default stream).
  *
  * workspace     the workspace the codes were quantized into.  Forward reads
@@ -272,8 +280,12 @@ fp8attn_status fp8attn_quantize_noalloc(fp8attn_plan_t plan, const void* q, cons
  * from the integer part and the 3-bit mantissa from the fraction (2^f taken as
  * 1 + f, centred); one conversion per probability instead of an exp2 and a
  * pack.  The row sum that normalizes the output adds the same E4M3 values.
- * FP8ATTN_PLAN_EXACT_PROBS rounds the FP32 exp2 instead.  The LSE, if asked
- * for, sums FP32 exp2 values either way.
+ * FP8ATTN_PLAN_EXACT_PROBS rounds the FP32 exp2 instead.  On E4M3's normal
+ * codes a log-linear weight is the exact 2^x times a factor in
+ * [0.9203, 1.0645], so the default LSE is within [-0.083, +0.063] of the
+ * exact one (about 1e-3 on rows of many keys; the error is centred); asking
+ * for it costs nothing extra.  With FP8ATTN_PLAN_EXACT_PROBS the LSE costs an
+ * FP32 addition per score.
  *
  * One attention launch, plus one combine launch when the plan splits work
  * items along the keys (fp8attn_plan_work_items shows the split; it happens

@@ -36,3 +36,16 @@ def visible_keys(cu_seqlens, causal):
     for a, b in zip(cu[:-1], cu[1:]):
         out[a:b] = np.arange(1, b - a + 1) if causal else b - a
     return out
+
+
+# The default E4M3 probability of a score is the E4M3 value of the code
+# rne(y), y = 8 x + LOGLIN_BIAS with x in log2 units (the reference frame
+# shifts y by whole multiples of 8, which scales normal E4M3 values by exact
+# powers of two).  On E4M3's normal codes (8 .. 126) the weight is 2^x times
+# a factor in [LOGLIN_RATIO_MIN, LOGLIN_RATIO_MAX] (tests/test_loglinear_bounds.py
+# derives the range), so the log of a row's weight sum (the LSE of default
+# plans) lies within [ln MIN, ln MAX] of the exact log-sum-exp of the same
+# scores.
+LOGLIN_BIAS = 55.54116061995
+LOGLIN_RATIO_MIN = 0.9202
+LOGLIN_RATIO_MAX = 1.0645

@@ -67,3 +67,24 @@ def bf16_ulp(x: np.ndarray) -> np.ndarray:
     """Spacing of bfloat16 numbers at |x| (8 significant bits)."""
     ax = np.maximum(np.abs(x), 2.0 ** -126)
     return np.exp2(np.floor(np.log2(ax)) - 7)
+
+
+def check_lse(got: np.ndarray, ref_deq: np.ndarray, exact_probs: bool, what: str = "") -> None:
+    """LSE of an E4M3 plan against the exact log-sum-exp of the dequantized
+    operands' uncentred scores.  Exact probabilities: the kernel sums the
+    FP32 2^x, so only FP32 accumulation and exp2 remain (2e-3).  Default
+    (log-linear) codes: the LSE is the log of the weights applied to V, each
+    2^x times a factor in [LOGLIN_RATIO_MIN, LOGLIN_RATIO_MAX] (tests/cases.py),
+    so every row lies in that log range (plus 2e-3 of FP32 slack) and, as the
+    code's error is centred, the median row error is small."""
+    from tests.cases import LOGLIN_RATIO_MAX, LOGLIN_RATIO_MIN
+    d = np.asarray(got, np.float64) - np.asarray(ref_deq, np.float64)
+    assert np.isfinite(d).all()
+    if exact_probs:
+        log(f"  {what} lse max err vs dequantized {np.abs(d).max():.5f}")
+        assert np.abs(d).max() <= 2e-3
+        return
+    med = float(np.median(d))
+    log(f"  {what} lse err vs dequantized: min {d.min():.5f} max {d.max():.5f} median {med:.5f}")
+    assert d.min() >= np.log(LOGLIN_RATIO_MIN) - 2e-3 and d.max() <= np.log(LOGLIN_RATIO_MAX) + 2e-3
+    assert abs(med) <= 0.01

@@ -242,6 +242,14 @@ def test_plan_rejects_rows_beyond_32bit_code_offsets():
     st, h = _plan(big, 1, [0, big])
     assert st == _lib.EUNSUPPORTED and h.value is None
     assert "32-bit" in _lib.lib().fp8attn_last_error().decode()
+    # the pack grid holds (rows / 64) x heads blocks in one dimension; heads in another
+    st, h = _plan(4_000_000, 40_000, [0, 4_000_000])
+    assert st == _lib.EUNSUPPORTED and h.value is None
+    st, h = _plan(64, 65536, [0, 64])
+    assert st == _lib.EUNSUPPORTED and h.value is None
+    st, h = _plan(64, 65535, [0, 64])
+    assert st == _lib.OK
+    _lib.lib().fp8attn_plan_destroy(h)
 
 
 def test_plan_ex_flags_and_segment_scale_layout():

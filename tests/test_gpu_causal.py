@@ -21,7 +21,7 @@ from oracle import compare
 from oracle import quantize as Qz
 from workloads import WORKLOADS, generate, make_workload, sample_rows
 from tests.cases import CAUSAL_CASES, FEW_KEYS, visible_keys
-from tests.gpu_helpers import bf16_ulp, log
+from tests.gpu_helpers import check_lse, bf16_ulp, log
 
 pytestmark = pytest.mark.gpu
 
@@ -109,10 +109,7 @@ def test_causal_lse_and_repeat():
         dk[a:b] += r["mu"][s][None].astype(np.float64)
     diag = A.lse_rows(torch.from_numpy(dq), torch.from_numpy(dk), w.cu_seqlens, w.softmax_scale,
                       causal=True).numpy().T
-    got = lse.cpu().double().numpy()
-    err = np.abs(got - diag).max()
-    log(f"  causal lse max err vs dequantized {err:.5f}")
-    assert err <= 2e-3
+    check_lse(lse.cpu().double().numpy(), diag, False, "causal")
 
 
 def test_batched_input_through_the_binding():

@@ -12,7 +12,7 @@ from oracle import attention as A
 from oracle import compare
 from oracle import quantize as Qz
 from workloads import WORKLOADS, generate, make_workload, sample_rows
-from tests.gpu_helpers import log
+from tests.gpu_helpers import check_lse, log
 from tests.test_gpu_attention import DIAG_BAR, _check_rows, _dequantized, _gpu_attention
 
 pytestmark = pytest.mark.gpu
@@ -46,14 +46,15 @@ def test_edge_and_split_every_element(cu):
 
 def test_lse_and_log_linear_default_agree_closely():
     # the two probability encodings differ by the encoding alone: outputs within
-    # the kernel-only error of each other, LSEs (FP32 exp2 sums in both) equal up
-    # to accumulation order
+    # the kernel-only error of each other; the exact plan's LSE is the FP32 sum
+    # of 2^x, the default plan's the log of its applied weights, within the
+    # log-linear code's error range of it
     w = make_workload("exact_lse", 1000, 3, [0, 400, 1000], seed=132, k_offset_var=2.0)
     q, k, v = generate(w, device="cuda")
     _, _, o_e, l_e = _gpu_attention(w, q, k, v, lse=True, exact=True)
     _, _, o_d, l_d = _gpu_attention(w, q, k, v, lse=True, exact=False)
     assert compare.rel_rms(o_d.cpu().double().numpy(), o_e.cpu().double().numpy()) <= 0.06
-    assert (l_e - l_d).abs().max().item() <= 1e-3
+    check_lse(l_d.cpu().double().numpy(), l_e.cpu().double().numpy(), False, "default vs exact")
     r = Qz.quantize(q.cpu(), k.cpu(), v.cpu(), w.cu_seqlens, w.softmax_scale)
     dq = Qz.dequantize(r["q_codes"], r["scales"][0])
     dk = Qz.dequantize(r["k_codes"], r["scales"][1])
