@@ -375,7 +375,7 @@ __global__ __launch_bounds__(2 * BM, 256 / BM) void k_attn(AttentionArgs a) {
   // Apply a pending reference shift to O and l (rare; wave-uniform branch):
   // they hold the products of tiles up to t-1, computed in the old frame.
   auto rescale = [&]() __attribute__((always_inline)) {
-    if (pending) {
+    if (__builtin_expect(pending, 0)) {
       const float alpha = __builtin_amdgcn_exp2f(pshift * kUnit);
       auto pa = __builtin_amdgcn_permlane16_swap(__float_as_uint(alpha), __float_as_uint(alpha), false, false);
       lacc[0] *= alpha;
@@ -390,24 +390,64 @@ __global__ __launch_bounds__(2 * BM, 256 / BM) void k_attn(AttentionArgs a) {
   // the reference from the tile maximum.  Keys past the end of the range have
   // been set to -inf (mask_tail) before this runs.  Register r of block kb in
   // lane l holds key kbase + 32*kb + 8*(r/4) + 4*(l/32) + r%4.
-  auto rowmax_update = [&](auto first_c) __attribute__((always_inline)) {
+  // The rare path: the row maxima of the pair lanes, the shift that puts them
+  // on kRef (only where they pass kMax), applied to S, the offset of later
+  // tiles (NB) and the rescale flagged for O and l.
+  auto apply_shift = [&](float tl) __attribute__((always_inline)) {
+    auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(tl), __float_as_uint(tl), false, false);
+    const float xm = __builtin_fmaxf(__uint_as_float(pr[0]), __uint_as_float(pr[1]));
+    const bool over = xm > kMax;
+    const float shift = over ? kRef - xm : 0.f;
+    nb += shift;
+    pshift = shift;
+    if (LSUM) lex *= __builtin_amdgcn_exp2f(shift * kUnit);   // lex takes this tile's p in the new frame
+#pragma unroll
+    for (int i = 0; i < 16; i++) { S[0][i] += shift; S[1][i] += shift; NB[i] += shift; }
+  };
+  // FIRST: set the reference from this tile.  Otherwise vote, and unless
+  // VOTE_ONLY apply a shift at once; VOTE_ONLY returns the lane maximum for
+  // the caller to apply later (before anything reads S or NB).
+  auto rowmax_update = [&](auto first_c, auto vote_only_c) __attribute__((always_inline)) {
     constexpr bool FIRST = decltype(first_c)::value;
-    // this lane's maximum of x: 15 v_max3 + 1 v_max (the pair lane holds the
-    // other half of the row)
-    float m8[8];
+    constexpr bool VOTE_ONLY = decltype(vote_only_c)::value;
+    // this lane's maximum of x: 16 three-input maxima (the pair lane holds the
+    // other half of the row).  After the first tile only "is any x above kMax"
+    // matters, and for that the maximum of the bit patterns as signed
+    // integers serves: they order like the floats on positive values and
+    // every negative float is a negative integer (kMax > 0), with no NaN
+    // canonicalization in the integer maximum.  The float maximum is then
+    // exact whenever it exceeds kMax, the only case the rare path uses it.
+    auto mx3 = [](auto a, auto b, auto c) {
+      if constexpr (FIRST)
+        return __builtin_fmaxf(__builtin_fmaxf(a, b), c);
+      else
+        return max(max(a, b), c);
+    };
+    auto val = [&](int kb, int r) {
+      if constexpr (FIRST)
+        return S[kb][r];
+      else
+        return __float_as_int(S[kb][r]);
+    };
+    using T = decltype(val(0, 0));
+    T m8[8];
 #pragma unroll
-    for (int i = 0; i < 5; i++) m8[i] = __builtin_fmaxf(__builtin_fmaxf(S[0][3 * i], S[0][3 * i + 1]), S[0][3 * i + 2]);
-    m8[5] = __builtin_fmaxf(__builtin_fmaxf(S[0][15], S[1][0]), S[1][1]);
+    for (int i = 0; i < 5; i++) m8[i] = mx3(val(0, 3 * i), val(0, 3 * i + 1), val(0, 3 * i + 2));
+    m8[5] = mx3(val(0, 15), val(1, 0), val(1, 1));
 #pragma unroll
-    for (int i = 0; i < 2; i++)
-      m8[6 + i] = __builtin_fmaxf(__builtin_fmaxf(S[1][2 + 3 * i], S[1][3 + 3 * i]), S[1][4 + 3 * i]);
-    const float n0 = __builtin_fmaxf(__builtin_fmaxf(S[1][8], S[1][9]), S[1][10]);
-    const float n1 = __builtin_fmaxf(__builtin_fmaxf(S[1][11], S[1][12]), S[1][13]);
-    const float n2 = __builtin_fmaxf(__builtin_fmaxf(S[1][14], S[1][15]), m8[0]);
-    const float n3 = __builtin_fmaxf(__builtin_fmaxf(m8[1], m8[2]), m8[3]);
-    const float n4 = __builtin_fmaxf(__builtin_fmaxf(m8[4], m8[5]), m8[6]);
-    const float n5 = __builtin_fmaxf(__builtin_fmaxf(m8[7], n0), n1);
-    const float tl = __builtin_fmaxf(__builtin_fmaxf(__builtin_fmaxf(n2, n3), n4), n5);
+    for (int i = 0; i < 2; i++) m8[6 + i] = mx3(val(1, 2 + 3 * i), val(1, 3 + 3 * i), val(1, 4 + 3 * i));
+    const T n0 = mx3(val(1, 8), val(1, 9), val(1, 10));
+    const T n1 = mx3(val(1, 11), val(1, 12), val(1, 13));
+    const T n2 = mx3(val(1, 14), val(1, 15), m8[0]);
+    const T n3 = mx3(m8[1], m8[2], m8[3]);
+    const T n4 = mx3(m8[4], m8[5], m8[6]);
+    const T n5 = mx3(m8[7], n0, n1);
+    const T tb = mx3(mx3(n2, n3, n4), n5, n5);
+    float tl;
+    if constexpr (FIRST)
+      tl = tb;
+    else
+      tl = __int_as_float(tb);
     if (FIRST) {
       auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(tl), __float_as_uint(tl), false, false);
       const float tm = __builtin_fmaxf(__uint_as_float(pr[0]), __uint_as_float(pr[1]));
@@ -418,19 +458,11 @@ __global__ __launch_bounds__(2 * BM, 256 / BM) void k_attn(AttentionArgs a) {
     } else {
       // move the reference only if the tile's largest p would exceed 448: one
       // vote over the wave; the row maxima and shifts only on the rare path
-      pending = __builtin_amdgcn_ballot_w64(tl > kMax) != 0;
-      if (pending) {
-        auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(tl), __float_as_uint(tl), false, false);
-        const float xm = __builtin_fmaxf(__uint_as_float(pr[0]), __uint_as_float(pr[1]));
-        const bool over = xm > kMax;
-        const float shift = over ? kRef - xm : 0.f;
-        nb += shift;
-        pshift = shift;
-        if (LSUM) lex *= __builtin_amdgcn_exp2f(shift * kUnit);   // lex takes this tile's p in the new frame
-#pragma unroll
-        for (int i = 0; i < 16; i++) { S[0][i] += shift; S[1][i] += shift; NB[i] += shift; }
-      }
+      pending = __builtin_amdgcn_ballot_w64(tb > __float_as_int(kMax)) != 0;
+      if constexpr (!VOTE_ONLY)
+        if (pending) apply_shift(tl);
     }
+    return tl;
   };
   // E4M3 probabilities of keys 8*q4 + 4*(lane/32) + 0..3 of block kb (one P dword).
   auto probs4 = [&](int kb, int q4, int kbase) __attribute__((always_inline)) {
@@ -486,7 +518,7 @@ __global__ __launch_bounds__(2 * BM, 256 / BM) void k_attn(AttentionArgs a) {
   auto first_tile = [&]() __attribute__((always_inline)) {
     if (ragged && nkt == 1) mask_tail(0);
     if (CAUSAL && q0 == 0) mask_causal(0);
-    rowmax_update(std::true_type{});
+    rowmax_update(std::true_type{}, std::false_type{});
 #pragma unroll
     for (int w = 0; w < 8; w++) P[w] = probs4(w >> 2, w & 3, 0);
     qk(1);
@@ -576,10 +608,14 @@ __global__ __launch_bounds__(2 * BM, 256 / BM) void k_attn(AttentionArgs a) {
       kf[0][1] = lds_read32(kb, koff[1][0], koff[1][1]);
       if (CAUSAL && t >= tdiag) mask_causal(t);   // wave-uniform branch, diagonal tiles only
       if (TAIL && ragged && t == nkt - 1) mask_tail(t);   // wave-uniform branch, last tile only
-      rowmax_update(std::false_type{});
+      // log-linear codes: the vote's outcome is looked at one product later,
+      // so the branch does not wait on the maximum tree
+      const float tlv = rowmax_update(std::false_type{}, std::integral_constant<bool, !EXACT>{});
       fence();
       O[1] = mfma_fp8(vf[1], P, O[1]);
       kf[1][1] = lds_read32(kb + 4096, koff[1][0], koff[1][1]);
+      if constexpr (!EXACT)
+        if (__builtin_expect(pending, 0)) apply_shift(tlv);
       Pn[0] = probs4(0, 0, kbase);
       fence();
       O[2] = mfma_fp8(vf[2], P, O[2]);
@@ -618,7 +654,7 @@ __global__ __launch_bounds__(2 * BM, 256 / BM) void k_attn(AttentionArgs a) {
       O[0] = mfma_fp8(vf[0], P, O[0]);
       if (CAUSAL && t >= tdiag) mask_causal(t);
       if (TAIL && ragged && t == nkt - 1) mask_tail(t);
-      rowmax_update(std::false_type{});
+      rowmax_update(std::false_type{}, std::false_type{});
       Pn[0] = probs4(0, 0, kbase);
       fence();
       O[1] = mfma_fp8(vf[1], P, O[1]);
