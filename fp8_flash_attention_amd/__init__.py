@@ -55,8 +55,9 @@ class Plan:
     quantizes every segment with its own per-head scales.  ``fmt`` is
     ``"e4m3"`` (default) or ``"mxfp4"``; ``q_centre`` (mxfp4 only) centres Q
     by its 128-row block means.  ``causal``: query i of a segment attends to
-    the keys j <= i of that segment.  ``head_dim``: 128, or 64
-    (e4m3 only).  ``exact_probs`` (e4m3 only): probabilities rounded from the
+    the keys j <= i of that segment.  ``head_dim``: 128, or (e4m3 only) any
+    multiple of 8 from 8 to 128 (run at the kernel width 64 or 128 with the
+    missing channels as zeros).  ``exact_probs`` (e4m3 only): probabilities rounded from the
     FP32 exp2 instead of the default log-linear E4M3 code (slower, a little
     more accurate).
     """
@@ -79,6 +80,8 @@ class Plan:
         self.tokens = int(tokens)
         self.heads = int(heads)
         self.cu_seqlens = tuple(cu)
+        if not (8 <= head_dim <= HEAD_DIM and head_dim % 8 == 0):
+            raise ValueError(f"head_dim must be a multiple of 8 from 8 to {HEAD_DIM} (got {head_dim})")
         self.softmax_scale = float(1.0 / math.sqrt(head_dim) if softmax_scale is None else softmax_scale)
         self.segment_scales = bool(segment_scales)
         if fmt not in ("e4m3", "mxfp4"):
@@ -86,8 +89,6 @@ class Plan:
         self.fmt = fmt
         self.q_centre = bool(q_centre)
         self.causal = bool(causal)
-        if head_dim not in (64, HEAD_DIM):
-            raise ValueError(f"head_dim must be 64 or {HEAD_DIM} (got {head_dim})")
         self.head_dim = int(head_dim)
         self.exact_probs = bool(exact_probs)
         arr = (ctypes.c_int32 * len(cu))(*cu)
@@ -95,7 +96,8 @@ class Plan:
         self._h = None
         flags = ((_lib.PLAN_SEGMENT_SCALES if self.segment_scales else 0)
                  | (_lib.PLAN_MXFP4 if fmt == "mxfp4" else 0) | (_lib.PLAN_Q_CENTRE if self.q_centre else 0)
-                 | (_lib.PLAN_CAUSAL if self.causal else 0) | (_lib.PLAN_HEAD_DIM_64 if self.head_dim == 64 else 0)
+                 | (_lib.PLAN_CAUSAL if self.causal else 0)
+                 | (_lib.plan_head_dim(self.head_dim) if self.head_dim != HEAD_DIM else 0)
                  | (_lib.PLAN_EXACT_PROBS if self.exact_probs else 0))
         _lib.check(L.fp8attn_plan_ex(ctypes.byref(h), self.tokens, self.heads, arr, len(cu) - 1,
                                      ctypes.c_float(self.softmax_scale), self.device_index, flags),
@@ -295,15 +297,16 @@ def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: Opt
               softmax_scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
               return_lse: bool = False, causal: bool = False, workspace: Optional[torch.Tensor] = None,
               segment_scales: bool = False, fmt: str = "e4m3", q_centre: bool = False, exact_probs: bool = False):
-    """FP8 attention over packed [tokens, heads, 128] BF16 q/k/v.
+    """FP8 attention over packed [tokens, heads, D] BF16 q/k/v.
 
     ``cu_seqlens`` is a host sequence of segment boundaries (None = one segment).
     ``segment_scales`` quantizes every segment with its own per-head scales.
     ``fmt="mxfp4"`` runs the block-scaled FP4 variant (``q_centre`` adds Q
-    block-mean centring).  ``causal=True`` masks keys after each query.  The head size (128, or 64 for E4M3) is taken from
-    the inputs' last dimension.  Batched [B, T, heads, 128] inputs (views of
-    [B*T, heads, 128]) are run as B segments of T tokens and returned as
-    [B, T, heads, 128] (with the LSE as [heads, B*T]).
+    block-mean centring).  ``causal=True`` masks keys after each query.  The
+    head size D (128, or for E4M3 any multiple of 8 up to 128) is taken from
+    the inputs' last dimension.  Batched [B, T, heads, D] inputs (views of
+    [B*T, heads, D]) are run as B segments of T tokens and returned as
+    [B, T, heads, D] (with the LSE as [heads, B*T]).
     """
     if q.dim() == 4:
         if cu_seqlens is not None:

@@ -24,6 +24,11 @@ PLAN_Q_CENTRE = 4                # FP8ATTN_PLAN_Q_CENTRE
 PLAN_CAUSAL = 8                  # FP8ATTN_PLAN_CAUSAL
 PLAN_HEAD_DIM_64 = 16            # FP8ATTN_PLAN_HEAD_DIM_64
 PLAN_EXACT_PROBS = 32            # FP8ATTN_PLAN_EXACT_PROBS
+
+
+def plan_head_dim(d: int) -> int:
+    """FP8ATTN_PLAN_HEAD_DIM(d): the head size in bits 8..12 of the plan flags."""
+    return (int(d) // 8) << 8
 PLAN_INFO_LEN = 14
 
 # Every symbol include/fp8attn.h declares, with (restype, argtypes).

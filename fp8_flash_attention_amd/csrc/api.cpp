@@ -32,7 +32,8 @@ struct fp8attn_plan_s {
   int32_t mx = 0;                 // FP8ATTN_PLAN_MXFP4
   int32_t q_centre = 0;           // FP8ATTN_PLAN_Q_CENTRE
   int32_t causal = 0;             // FP8ATTN_PLAN_CAUSAL
-  int32_t head_dim = kHeadDim;    // 64 with FP8ATTN_PLAN_HEAD_DIM_64
+  int32_t head_dim = kHeadDim;    // channels of q, k, v and out (FP8ATTN_PLAN_HEAD_DIM_64, FP8ATTN_PLAN_HEAD_DIM)
+  int32_t dk = kHeadDim;          // kernel width: 64 for head_dim <= 64, else 128 (missing channels are zeros)
   int32_t exact_probs = 0;        // FP8ATTN_PLAN_EXACT_PROBS
   int32_t bm = kBM;               // queries per work item (kMxBM for FP4 plans; see choose_query_tile)
   int32_t wg_per_cu = 1;          // attention workgroups resident per CU
@@ -256,7 +257,7 @@ void build_items(fp8attn_plan_s* p, int cus, bool allow_split) {
 constexpr int64_t kSmallWorkPerCu = 768;   // key-tile iterations of 256-query items per CU
 
 void choose_query_tile(fp8attn_plan_s* p, int cus) {
-  if (p->mx || p->causal || p->head_dim != kHeadDim) return;
+  if (p->mx || p->causal || p->dk != kHeadDim) return;
   int64_t work = 0;
   for (const SegInfo& s : p->segs) work += (int64_t)((s.len + kBM - 1) / kBM) * ((s.len + kBN - 1) / kBN);
   work *= p->heads;
@@ -301,12 +302,20 @@ fp8attn_status fp8attn_plan_ex(fp8attn_plan_t* plan_out, int64_t tokens, int32_t
   if (plan_out == nullptr) return fail(FP8ATTN_EINVAL, "plan_out is NULL");
   *plan_out = nullptr;
   if ((flags & ~(FP8ATTN_PLAN_SEGMENT_SCALES | FP8ATTN_PLAN_MXFP4 | FP8ATTN_PLAN_Q_CENTRE | FP8ATTN_PLAN_CAUSAL |
-                 FP8ATTN_PLAN_HEAD_DIM_64 | FP8ATTN_PLAN_EXACT_PROBS)) != 0)
+                 FP8ATTN_PLAN_HEAD_DIM_64 | FP8ATTN_PLAN_EXACT_PROBS | FP8ATTN_PLAN_HEAD_DIM(248))) != 0)
     return fail(FP8ATTN_EINVAL, "unknown plan flags");
+  int32_t head_dim = (int32_t)((flags >> 8) & 31u) * 8;
+  if (flags & FP8ATTN_PLAN_HEAD_DIM_64) {
+    if (head_dim != 0 && head_dim != 64)
+      return fail(FP8ATTN_EINVAL, "FP8ATTN_PLAN_HEAD_DIM_64 with another FP8ATTN_PLAN_HEAD_DIM");
+    head_dim = 64;
+  }
+  if (head_dim == 0) head_dim = kHeadDim;
+  if (head_dim > kHeadDim) return fail(FP8ATTN_EINVAL, "head_dim must be a multiple of 8 from 8 to 128");
+  if (head_dim != kHeadDim && (flags & FP8ATTN_PLAN_MXFP4))
+    return fail(FP8ATTN_EINVAL, "FP8ATTN_PLAN_MXFP4 plans take head_dim 128 only");
   if ((flags & FP8ATTN_PLAN_EXACT_PROBS) && (flags & FP8ATTN_PLAN_MXFP4))
     return fail(FP8ATTN_EINVAL, "FP8ATTN_PLAN_EXACT_PROBS applies to E4M3 plans only");
-  if ((flags & FP8ATTN_PLAN_HEAD_DIM_64) && (flags & FP8ATTN_PLAN_MXFP4))
-    return fail(FP8ATTN_EINVAL, "FP8ATTN_PLAN_HEAD_DIM_64 is not available for FP8ATTN_PLAN_MXFP4 plans");
   if ((flags & FP8ATTN_PLAN_Q_CENTRE) && !(flags & FP8ATTN_PLAN_MXFP4))
     return fail(FP8ATTN_EINVAL, "FP8ATTN_PLAN_Q_CENTRE needs FP8ATTN_PLAN_MXFP4");
   if ((flags & FP8ATTN_PLAN_MXFP4) && (flags & FP8ATTN_PLAN_SEGMENT_SCALES))
@@ -337,7 +346,8 @@ fp8attn_status fp8attn_plan_ex(fp8attn_plan_t* plan_out, int64_t tokens, int32_t
   p->mx = (flags & FP8ATTN_PLAN_MXFP4) ? 1 : 0;
   p->q_centre = (flags & FP8ATTN_PLAN_Q_CENTRE) ? 1 : 0;
   p->causal = (flags & FP8ATTN_PLAN_CAUSAL) ? 1 : 0;
-  p->head_dim = (flags & FP8ATTN_PLAN_HEAD_DIM_64) ? 64 : kHeadDim;
+  p->head_dim = head_dim;
+  p->dk = head_dim <= 64 ? 64 : kHeadDim;
   p->exact_probs = (flags & FP8ATTN_PLAN_EXACT_PROBS) ? 1 : 0;
   if (p->mx) {
     p->bm = kMxBM;
@@ -360,7 +370,7 @@ fp8attn_status fp8attn_plan_ex(fp8attn_plan_t* plan_out, int64_t tokens, int32_t
   row += kGuardRows;
   // the attention kernel addresses one head's code rows through 32-bit buffer
   // offsets: rows * 128 bytes must fit
-  if (row * p->head_dim > (int64_t)INT32_MAX || (row / kPackRows) * heads > (int64_t)INT32_MAX) {
+  if (row * p->dk > (int64_t)INT32_MAX || (row / kPackRows) * heads > (int64_t)INT32_MAX) {
     delete p;
     return fail(FP8ATTN_EUNSUPPORTED, "too many padded rows for 32-bit code offsets (about 16.7M tokens at most "
                                       "at head_dim 128) or too many 64-row groups times heads for one grid");
@@ -377,7 +387,7 @@ fp8attn_status fp8attn_plan_ex(fp8attn_plan_t* plan_out, int64_t tokens, int32_t
     return fail(FP8ATTN_EUNSUPPORTED, "too many split work items");
   }
   p->ws = p->mx ? make_layout_mx(row, heads, num_segments, (int)p->chunks.size(), p->npieces)
-                : make_layout(row, heads, num_segments, p->nscale, (int)p->chunks.size(), p->npieces, p->head_dim);
+                : make_layout(row, heads, num_segments, p->nscale, (int)p->chunks.size(), p->npieces, p->dk);
 
   if (device >= 0) {
     DeviceGuard g(device);
@@ -441,7 +451,7 @@ namespace {
 // fp8attn_quantize_noalloc: K statistics, then the Q/V amax partials.
 size_t static_stats_bytes(const fp8attn_plan_s* p) {
   const size_t nch = p->chunks.size();
-  const size_t kst = align_up(sizeof(KStat) * nch * (size_t)p->heads * (size_t)p->head_dim, 256);
+  const size_t kst = align_up(sizeof(KStat) * nch * (size_t)p->heads * (size_t)p->dk, 256);
   const size_t amx = p->mx ? 0 : align_up(sizeof(float) * 2 * nch * (size_t)p->heads, 256);
   return kst + amx;
 }
@@ -479,7 +489,7 @@ fp8attn_status quantize_impl(fp8attn_plan_t p, const void* q, const void* k, con
     const hipError_t e = static_stats_buffer(p->device, &stats);
     if (e != hipSuccess)
       return fail(FP8ATTN_EHIP, std::string("static statistics buffer: ") + hipGetErrorString(e));
-    if (!p->mx) amax_rel = align_up(sizeof(KStat) * p->chunks.size() * (size_t)p->heads * (size_t)p->head_dim, 256);
+    if (!p->mx) amax_rel = align_up(sizeof(KStat) * p->chunks.size() * (size_t)p->heads * (size_t)p->dk, 256);
   }
   QuantizeArgs a{};
   a.x[0] = static_cast<const uint16_t*>(q);
@@ -509,7 +519,8 @@ fp8attn_status quantize_impl(fp8attn_plan_t p, const void* q, const void* k, con
   a.softmax_scale = p->scale;
   a.mx = p->mx;
   a.q_centre = p->q_centre;
-  a.head_dim = p->head_dim;
+  a.head_dim = p->dk;
+  a.d_real = p->head_dim;
   if (p->mx) {
     a.bscale[0] = ws + p->ws.qs_off;
     a.bscale[1] = ws + p->ws.ks_off;
@@ -614,7 +625,8 @@ fp8attn_status fp8attn_forward(fp8attn_plan_t p, void* workspace, size_t workspa
     a.nitems = nitems;
     a.nscale = p->nscale;
     a.causal = p->causal;
-    a.head_dim = p->head_dim;
+    a.head_dim = p->dk;
+    a.d_real = p->head_dim;
     a.bm = p->bm;
     a.exact_probs = p->exact_probs;
     a.softmax_scale = p->scale;
@@ -634,7 +646,8 @@ fp8attn_status fp8attn_forward(fp8attn_plan_t p, void* workspace, size_t workspa
     c.os1 = os1;
     c.lse = lse;
     c.tokens = p->tokens;
-    c.head_dim = p->head_dim;
+    c.head_dim = p->dk;
+    c.d_real = p->head_dim;
     c.bm = p->bm;
     e = launch_combine(c, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(FP8ATTN_EHIP, std::string("combine launch failed: ") + hipGetErrorString(e));
@@ -646,7 +659,7 @@ fp8attn_status fp8attn_workspace_region(fp8attn_plan_t p, const void* workspace,
                                         const void** ptr_out, int64_t dims_out[3]) {
   if (p == nullptr || ptr_out == nullptr || dims_out == nullptr) return fail(FP8ATTN_EINVAL, "NULL argument");
   const uint8_t* ws = static_cast<const uint8_t*>(workspace);
-  const int64_t H = p->heads, R = p->ws.rows, D = p->head_dim;
+  const int64_t H = p->heads, R = p->ws.rows, D = p->dk;
   if (which == FP8ATTN_REGION_ROWMAP) {
     if (p->device < 0) return fail(FP8ATTN_EINVAL, "host-only plan has no device tables");
     *ptr_out = p->d_rowmap;

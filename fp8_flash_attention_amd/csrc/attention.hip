@@ -759,11 +759,13 @@ __global__ __launch_bounds__(2 * BM, 256 / BM) void k_attn(AttentionArgs a) {
 #pragma unroll
       for (int q4 = 0; q4 < 4; q4++) {
         const int d = 32 * db + 8 * q4 + 4 * lg;
-        const uint32_t b0 = f32_to_bf16_rne(O[db][4 * q4 + 0] * inv);
-        const uint32_t b1 = f32_to_bf16_rne(O[db][4 * q4 + 1] * inv);
-        const uint32_t b2 = f32_to_bf16_rne(O[db][4 * q4 + 2] * inv);
-        const uint32_t b3 = f32_to_bf16_rne(O[db][4 * q4 + 3] * inv);
-        *reinterpret_cast<uint2*>(orow + d) = make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
+        if (d < a.d_real) {   // channels past head_dim are padding
+          const uint32_t b0 = f32_to_bf16_rne(O[db][4 * q4 + 0] * inv);
+          const uint32_t b1 = f32_to_bf16_rne(O[db][4 * q4 + 1] * inv);
+          const uint32_t b2 = f32_to_bf16_rne(O[db][4 * q4 + 2] * inv);
+          const uint32_t b3 = f32_to_bf16_rne(O[db][4 * q4 + 3] * inv);
+          *reinterpret_cast<uint2*>(orow + d) = make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
+        }
       }
   }
   if (LSE) {
@@ -834,6 +836,7 @@ __global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
   uint16_t* orow = a.out + (int64_t)(si.start + qrow) * a.os0 + (int64_t)it.z * a.os1 + HD * half;
 #pragma unroll
   for (int j = 0; j < HD / 8; j++) {
+    if (HD * half + 8 * j >= a.d_real) break;   // channels past head_dim are padding
     uint32_t b[8];
 #pragma unroll
     for (int e = 0; e < 8; e++) b[e] = f32_to_bf16_rne(acc[8 * j + e] * inv);

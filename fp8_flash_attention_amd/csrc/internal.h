@@ -96,7 +96,8 @@ struct QuantizeArgs {
   const int32_t* group_seg;  // [ngroups]: segment of each 64-row pack group, -1 = guard
   int32_t heads, nseg, nchunks, ngroups;
   int32_t seg_scales;        // 1: one scale per (tensor, segment, head)
-  int32_t head_dim;          // D: 128, or 64 (E4M3 plans)
+  int32_t head_dim;          // D: kernel width, 128 or 64 (E4M3 plans)
+  int32_t d_real;            // channels present in q, k, v (<= D; the rest read as zeros)
   int64_t rows;
   float softmax_scale;       // fixes Q's scale (see k_finalize)
   // FP4 plans
@@ -127,7 +128,8 @@ struct AttentionArgs {
   int32_t nitems;
   int32_t nscale;            // S: scale sets (segments with per-segment scales, else 1)
   int32_t causal;            // 1: query i of a segment attends keys j <= i only
-  int32_t head_dim;          // D: 128 or 64
+  int32_t head_dim;          // D: kernel width, 128 or 64
+  int32_t d_real;            // channels written to out (<= D)
   int32_t bm;                // queries per work item: 256, or 128 (D = 128 only)
   int32_t exact_probs;       // 1: p = E4M3(exp2(x)); 0: the log-linear code of 2^x
   float softmax_scale;
@@ -144,7 +146,8 @@ struct CombineArgs {
   int64_t os0, os1;
   float* lse;                // nullable, [H][T]
   int64_t tokens;
-  int32_t head_dim;          // D: 128 or 64
+  int32_t head_dim;          // D: kernel width, 128 or 64
+  int32_t d_real;            // channels written to out (<= D)
   int32_t bm;                // queries per split item (128 or 256)
 };
 

@@ -60,6 +60,14 @@ __device__ __forceinline__ void unpack8(const uint4 v, float f[8]) {
   }
 }
 
+// 8 BF16 channels at p, or zeros when the thread's channels lie past the
+// plan's head_dim (p then points at channel 0 of the same row, so the load
+// stays in bounds and is not a branch).
+__device__ __forceinline__ uint4 load8(const uint16_t* p, bool live) {
+  const uint4 v = *reinterpret_cast<const uint4*>(p);
+  return live ? v : make_uint4(0u, 0u, 0u, 0u);
+}
+
 // E4M3 codes of 4 floats packed little-endian into one dword.  v_cvt_pk_fp8_f32
 // on gfx950 converts to OCP E4M3 with round-to-nearest-even and keeps
 // subnormals; the quantizer's inputs lie within a few ulps of +-448 at most,
@@ -87,7 +95,8 @@ __global__ __launch_bounds__(256) void k_stats(QuantizeArgs a) {
   const int c0 = (t % TPH) * 8;
   const bool active = h < a.heads;
   const Chunk ch = a.chunks[c];
-  const uint16_t* base = a.x[tensor] + (int64_t)h * a.hs[tensor] + c0;
+  const bool live = c0 < a.d_real;   // channels past head_dim read as zeros
+  const uint16_t* base = a.x[tensor] + (int64_t)h * a.hs[tensor] + (live ? c0 : 0);
   const int64_t ts = a.ts[tensor];
 
   if (tensor == 1) {
@@ -98,7 +107,7 @@ __global__ __launch_bounds__(256) void k_stats(QuantizeArgs a) {
     for (int i = 0; i < 8; i++) { sum[i] = 0.0; mn[i] = __builtin_inff(); mx[i] = -__builtin_inff(); }
 #pragma unroll 16
     for (int j = 0; j < ch.ntok; j++) {   // unrolled: 16 loads in flight, sums still in token order
-      const uint4 v = *reinterpret_cast<const uint4*>(base + (int64_t)(ch.tok0 + j) * ts);
+      const uint4 v = load8(base + (int64_t)(ch.tok0 + j) * ts, live);
       float f[8];
       unpack8(v, f);
 #pragma unroll
@@ -118,7 +127,7 @@ __global__ __launch_bounds__(256) void k_stats(QuantizeArgs a) {
   if (active) {
 #pragma unroll 16
     for (int j = 0; j < ch.ntok; j++) {   // unrolled: 16 loads in flight, sums still in token order
-      const uint4 v = *reinterpret_cast<const uint4*>(base + (int64_t)(ch.tok0 + j) * ts);
+      const uint4 v = load8(base + (int64_t)(ch.tok0 + j) * ts, live);
       float f[8];
       unpack8(v, f);
 #pragma unroll
@@ -290,7 +299,8 @@ __global__ __launch_bounds__(256) void k_pack(QuantizeArgs a) {
   const int sset = a.seg_scales && seg >= 0 ? seg : 0;
   const float s = a.scales[((int64_t)tensor * nset + sset) * a.heads + h];
   const int c0 = (t % TPH) * 8;
-  const uint16_t* base = a.x[tensor] + (int64_t)h * a.hs[tensor] + c0;
+  const bool live = c0 < a.d_real;   // channels past head_dim read as zeros (codes 0)
+  const uint16_t* base = a.x[tensor] + (int64_t)h * a.hs[tensor] + (live ? c0 : 0);
   const int64_t ts = a.ts[tensor];
   float mu[8];
   if (tensor == 1 && seg >= 0) {
@@ -308,7 +318,7 @@ __global__ __launch_bounds__(256) void k_pack(QuantizeArgs a) {
     const int rel = (int)(R - (seg >= 0 ? si.row0 : 0)) + i;  // segment-relative row
     uint2 code = make_uint2(0u, 0u);
     if (seg >= 0 && rel < si.len) {
-      const uint4 v = *reinterpret_cast<const uint4*>(base + (int64_t)(si.start + rel) * ts);
+      const uint4 v = load8(base + (int64_t)(si.start + rel) * ts, live);
       float f[8];
       unpack8(v, f);
       float y[8];

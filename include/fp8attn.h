@@ -56,8 +56,9 @@ typedef enum {
   FP8ATTN_EHIP = 5           /* a HIP runtime call or kernel launch failed */
 } fp8attn_status;
 
-/* Workspace regions, for fp8attn_workspace_region().  D = 128, or 64 for
-   FP8ATTN_PLAN_HEAD_DIM_64 plans (written 128 below). */
+/* Workspace regions, for fp8attn_workspace_region().  D = the plan's kernel
+   width: 128, or 64 for plans of at most 64 channels (written 128 below);
+   channels past the plan's head_dim hold zero codes and zero means. */
 typedef enum {
   FP8ATTN_REGION_Q_CODES = 0, /* uint8 [H][rows][128]                                  */
   FP8ATTN_REGION_K_CODES = 1, /* uint8 [H][rows][128] (centred K)                       */
@@ -120,6 +121,9 @@ fp8attn_status fp8attn_plan(fp8attn_plan_t* plan_out, int64_t tokens, int32_t he
 #define FP8ATTN_PLAN_CAUSAL 8u
 #define FP8ATTN_PLAN_HEAD_DIM_64 16u
 #define FP8ATTN_PLAN_EXACT_PROBS 32u
+/* head_dim d (a multiple of 8, 8 <= d <= 128) in bits 8..12 of the flags; 0
+   there means 128 (or 64 with FP8ATTN_PLAN_HEAD_DIM_64). */
+#define FP8ATTN_PLAN_HEAD_DIM(d) ((uint32_t)((d) / 8) << 8)
 
 /*
  * fp8attn_plan_ex - fp8attn_plan with flags (fp8attn_plan is flags == 0).
@@ -168,6 +172,13 @@ fp8attn_status fp8attn_plan(fp8attn_plan_t* plan_out, int64_t tokens, int32_t he
  *   per head instead of FP8ATTN_HEAD_DIM (P1 lists other head sizes among the
  *   cases it sends elsewhere): every region, stride and scale rule below
  *   holds with 64 in place of 128.  Combines with the other E4M3 flags.
+ * FP8ATTN_PLAN_HEAD_DIM(d) (E4M3 plans): q, k, v and out have d channels per
+ *   head, d a multiple of 8 from 8 to 128.  The kernels run at the width 64
+ *   (d <= 64) or 128 with the missing channels taken as zeros: they add
+ *   nothing to any score, their K mean is 0, they are left out of every
+ *   amax (so the codes of the d channels are those of an unpadded
+ *   quantizer), and out receives the d channels only.  The same as
+ *   FP8ATTN_PLAN_HEAD_DIM_64 for d = 64.
  * FP8ATTN_PLAN_EXACT_PROBS (E4M3 plans): the probabilities are the E4M3
  *   rounding (nearest, ties to even) of the FP32 exp2 of the scores, as in the
  *   sglang PR's recipe, instead of the default log-linear code (see
@@ -176,7 +187,9 @@ fp8attn_status fp8attn_plan(fp8attn_plan_t* plan_out, int64_t tokens, int32_t he
  * Unknown flag bits, FP8ATTN_PLAN_Q_CENTRE without FP8ATTN_PLAN_MXFP4,
  * FP8ATTN_PLAN_EXACT_PROBS with FP8ATTN_PLAN_MXFP4,
  * FP8ATTN_PLAN_MXFP4 with FP8ATTN_PLAN_SEGMENT_SCALES (its scales are already
- * local to 32 elements) or with FP8ATTN_PLAN_HEAD_DIM_64: FP8ATTN_EINVAL.
+ * local to 32 elements) or with a head_dim other than 128, a head_dim that is
+ * not a multiple of 8 in [8, 128], or FP8ATTN_PLAN_HEAD_DIM_64 with another
+ * FP8ATTN_PLAN_HEAD_DIM(d): FP8ATTN_EINVAL.
  */
 fp8attn_status fp8attn_plan_ex(fp8attn_plan_t* plan_out, int64_t tokens, int32_t heads,
                                const int32_t* cu_seqlens_host, int32_t num_segments,
@@ -188,8 +201,10 @@ size_t fp8attn_workspace_bytes(fp8attn_plan_t plan);
 /*
  * fp8attn_quantize - BF16 Q/K/V views -> E4M3 codes + per-head scales in the workspace.
  *
- * q, k, v       device pointers to bfloat16 data viewed as [tokens][heads][128]:
- *               element (t, h, d) is at base[t * strides[0] + h * strides[1] + d]
+ * q, k, v       device pointers to bfloat16 data viewed as
+ *               [tokens][heads][head_dim] (head_dim 128 unless the plan says
+ *               otherwise): element (t, h, d) is at
+ *               base[t * strides[0] + h * strides[1] + d]
  *               (strides in elements, dim stride 1).  Strides must be positive
  *               multiples of 8 and bases 16-byte aligned.  Views of one fused
  *               [T][3][H][128] buffer are fine.  Read-only.
@@ -251,7 +266,7 @@ fp8attn_status fp8attn_quantize_noalloc(fp8attn_plan_t plan, const void* q, cons
  * fp8attn_forward - attention over the codes that the last fp8attn_quantize
  * into `workspace` wrote (stream order).
  *
- * out           device bfloat16 [tokens][heads][128] with element (t, h, d) at
+ * out           device bfloat16 [tokens][heads][head_dim] with element (t, h, d) at
  *               out[t * out_strides[0] + h * out_strides[1] + d]; strides positive
  *               multiples of 8, base 16-byte aligned.  Every row of every
  *               non-empty segment is written.

@@ -455,8 +455,42 @@ def test_head_dim_64_plan_layout():
     real = {it for it in p.work_items() if it[0] >= 0}
     assert real == {(s, q0, h, 0) for h in range(2) for s, (a, b) in enumerate([(0, 100), (100, 300)])
                     for q0 in range(0, b - a, 256)}
-    with pytest.raises(ValueError):
-        fa.Plan(300, 2, [0, 300], device=-1, head_dim=96)
+    for bad in (0, 4, 100, 136, 256):
+        with pytest.raises(ValueError):
+            fa.Plan(300, 2, [0, 300], device=-1, head_dim=bad)
+
+
+@pytest.mark.parametrize("d,dk", [(8, 64), (32, 64), (64, 64), (72, 128), (96, 128), (120, 128), (128, 128)])
+def test_head_dim_flag_and_kernel_width(d, dk):
+    """FP8ATTN_PLAN_HEAD_DIM(d): q, k, v and out have d channels; the code
+    regions and K means have the kernel width (64 or 128)."""
+    L = _lib.lib()
+    p = fa.Plan(300, 2, [0, 100, 300], device=-1, head_dim=d)
+    assert p.info()["head_dim"] == d and p.softmax_scale == pytest.approx(d ** -0.5)
+    rows = p.info()["workspace_rows"]
+    ptr = ctypes.c_void_p()
+    dims = (ctypes.c_int64 * 3)()
+    for which, shape in ((_lib.REGION_Q, (2, rows, dk)), (_lib.REGION_V, (2, dk, rows)), (_lib.REGION_MU, (2, 2, dk))):
+        assert L.fp8attn_workspace_region(p.handle, ctypes.c_void_p(1 << 20), which, ctypes.byref(ptr), dims) == 0
+        assert tuple(dims) == shape
+    same = fa.Plan(300, 2, [0, 100, 300], device=-1, head_dim=64 if dk == 64 else 128)
+    assert p.workspace_bytes == same.workspace_bytes
+    assert p.info()["query_tile"] == same.info()["query_tile"]
+
+
+def test_head_dim_flag_errors():
+    L = _lib.lib()
+    h = ctypes.c_void_p()
+    arr = (ctypes.c_int32 * 2)(0, 256)
+    def plan(flags):
+        return L.fp8attn_plan_ex(ctypes.byref(h), 256, 2, arr, 1, ctypes.c_float(0.125), -1, flags)
+    assert plan(_lib.plan_head_dim(96) | _lib.PLAN_MXFP4) == _lib.EINVAL           # FP4: 128 only
+    assert plan(_lib.plan_head_dim(96) | _lib.PLAN_HEAD_DIM_64) == _lib.EINVAL     # two different sizes
+    assert plan(_lib.plan_head_dim(136)) == _lib.EINVAL                            # above 128
+    assert plan(_lib.plan_head_dim(64) | _lib.PLAN_HEAD_DIM_64) == _lib.OK         # the same size twice
+    L.fp8attn_plan_destroy(h)
+    assert plan(_lib.plan_head_dim(40) | _lib.PLAN_CAUSAL | _lib.PLAN_SEGMENT_SCALES) == _lib.OK
+    L.fp8attn_plan_destroy(h)
 
 
 def test_quantize_noalloc_rejects_plans_beyond_its_static_buffer():
