@@ -419,16 +419,19 @@ __device__ __forceinline__ void mx_row(const float y[8], uint8_t* code_row, uint
   if ((tq & 3) == 0) scale_row[mx_scale_pos(tq >> 2)] = live ? (uint8_t)(e + 127) : 0;
 }
 
-// grid = (ngroups, H, 3), block = 256.  tensor 0 (Q): even groups take a
-// 128-row mean block (two groups), odd groups return; tensor 1 (K) and 2 (V):
-// one 64-row group.  Rows past a segment's end and guard rows get zero codes
+// grid = (ngroups * H, 1, 3), block = 256, heads fastest and in reverse
+// order as for the E4M3 pack (0.619 -> 0.531 ms for the whole FP4 quantize
+// at S=30272, H=56; 0.829 -> 0.647 ms with Q centring).  tensor 0 (Q): even
+// groups take a 128-row mean block (two groups), odd groups return; tensor 1
+// (K) and 2 (V): one 64-row group.  Rows past a segment's end and guard rows get zero codes
 // and zero scale bytes.
 __global__ __launch_bounds__(256) void k_pack_mx(QuantizeArgs a) {
   __shared__ float tile[kPackRows][kHeadDim + 1];
   __shared__ float qm_s[kHeadDim];
-  const int g = blockIdx.x;
-  const int h = blockIdx.y;
-  const int tensor = blockIdx.z;
+  const int bx = gridDim.x - 1 - blockIdx.x;
+  const int g = bx / a.heads;
+  const int h = bx % a.heads;
+  const int tensor = 2 - blockIdx.z;
   const int t = threadIdx.x;
   if (tensor == 0 && (g & 1)) return;
   const int seg = a.group_seg[g];
@@ -563,7 +566,7 @@ hipError_t launch_quantize_d(const QuantizeArgs& a, hipStream_t stream) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (a.mx)
-    hipLaunchKernelGGL(k_pack_mx, dim3(a.ngroups, a.heads, 3), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(k_pack_mx, dim3(a.ngroups * a.heads, 1, 3), dim3(256), 0, stream, a);
   else
     hipLaunchKernelGGL(k_pack<D>, dim3(a.ngroups * a.heads, 1, 3), dim3(256), 0, stream, a);
   return hipGetLastError();
