@@ -22,8 +22,9 @@
 //     iteration t runs the softmax of tile t on the vector unit while the
 //     matrix core computes the scores of tile t+1 and the P V product of tile
 //     t-1.  Nothing in an iteration waits for a matrix result of the same
-//     iteration, and the iteration body is one basic block the compiler can
-//     interleave freely.
+//     iteration.  The body is laid out as nine slots of one matrix product
+//     each, separated by scheduling fences; the rare paths (a reference
+//     shift, the rescale it asks for) are branches laid out of line.
 //   * Scores are computed transposed, S^T = K Q^T, with
 //     v_mfma_f32_32x32x64_f8f6f4 (A = 32 keys x 64 channels read from LDS,
 //     B = 32 queries x 64 channels held in registers for the whole loop).  In
@@ -31,8 +32,8 @@
 //     32-key block, so a row maximum is in-lane plus one exchange between
 //     lanes l and l^32 (v_permlane32_swap).
 //   * The accumulators of the two 32-key blocks of a tile, converted to E4M3
-//     with v_cvt_pk_fp8_f32, are exactly the B operand (64 keys x 32 queries)
-//     of O^T += V^T P^T.  The key order this implies inside a 64-key group is
+//     codes in registers (below), are exactly the B operand (64 keys x 32
+//     queries) of O^T += V^T P^T.  The key order this implies inside a 64-key group is
 //     baked into the workspace V layout by the pack pass, so the P registers
 //     never leave the lane.
 //   * Row sums l come from the matrix core too: one
@@ -57,8 +58,10 @@
 //     The first tile sets m to its row maximum (mapped to 112 = 448/4).
 //     Later tiles move m only when their maximum would give a p above 448,
 //     the largest E4M3 value, so most tiles need no rescale: the common path
-//     is a max tree and one wave-wide vote; the rare path shifts the scores,
-//     the offset and the accumulator initial value, and the rescale of O and
+//     is a max tree (integer maxima of the float bits, which order like the
+//     floats above the threshold) and one wave-wide vote; the rare path
+//     shifts the scores, the offset and the accumulator initial value, and
+//     the rescale of O and
 //     l by 2^shift runs at the top of the next iteration, after the P V
 //     product of the older tiles and before that of the tile that moved m.
 //   * K and V^T tiles reach LDS by direct buffer loads (no register staging):
