@@ -61,9 +61,9 @@
 //     is a max tree (integer maxima of the float bits, which order like the
 //     floats above the threshold) and one wave-wide vote; the rare path
 //     shifts the scores, the offset and the accumulator initial value, and
-//     the rescale of O and
-//     l by 2^shift runs at the top of the next iteration, after the P V
-//     product of the older tiles and before that of the tile that moved m.
+//     the rescale of O and l by 2^shift runs at the top of the next
+//     iteration, after the P V product of the older tiles and before that of
+//     the tile that moved m.
 //   * K and V^T tiles reach LDS by direct buffer loads (no register staging):
 //     a K ring and a V ring of four 8 KB slots each.  Iteration t reads K of
 //     tile t+1 for its score products, and V of tile t for the P V product of
