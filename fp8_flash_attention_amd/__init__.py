@@ -38,6 +38,7 @@ HEAD_DIM = 128
 DEFAULT_SCALE = 1.0 / math.sqrt(HEAD_DIM)
 
 __all__ = ["Plan", "quantize", "quantize_noalloc", "forward", "attention", "get_plan", "clear_plan_cache",
+           "varlen_attention_fp8", "varlen_attention_mxfp4", "workspace_bytes",
            "Fp8AttnError", "HEAD_DIM", "DEFAULT_SCALE"]
 
 
@@ -336,3 +337,80 @@ def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: Opt
     lse = torch.empty((H, T), dtype=torch.float32, device=q.device) if return_lse else None
     out = forward(plan, ws, out, lse)
     return (out, lse) if return_lse else out
+
+
+# ---------------------------------------------------------------------------
+# The pages' varlen entry points (FlashInfer page
+# "minimax_h3_sm120_varlen_attention_nvfp4", its signature and parameters):
+# q, k, v [tokens, heads, 128], a device cu_seqlens with an optional host copy
+# that saves the device-to-host read, an optional preallocated out, the
+# softmax scale, and a grow-only per-device workspace shared by the FP8 and
+# FP4 forms.  Calls that overlap on one device (several streams or threads)
+# share that workspace and must be serialized by the caller.
+# ---------------------------------------------------------------------------
+
+_SHARED_WS = {}
+
+
+def _shared_workspace(device_index: int, nbytes: int) -> torch.Tensor:
+    ws = _SHARED_WS.get(device_index)
+    if ws is None or ws.numel() < nbytes:
+        if ws is not None:
+            torch.cuda.synchronize(device_index)   # work queued on the old buffer finishes first
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=torch.device("cuda", device_index))
+        _SHARED_WS[device_index] = ws
+    return ws
+
+
+def workspace_bytes(device=None) -> int:
+    """Bytes of the shared workspace the varlen entry points hold on a device (0 if none)."""
+    if isinstance(device, torch.device):
+        device = device.index
+    idx = torch.cuda.current_device() if device is None else int(device)
+    ws = _SHARED_WS.get(idx)
+    return 0 if ws is None else int(ws.numel())
+
+
+def _varlen(q, k, v, cu_seqlens, out, cu_seqlens_host, softmax_scale, return_lse, fmt, q_centre):
+    if not isinstance(cu_seqlens, torch.Tensor) or cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1:
+        raise ValueError("cu_seqlens must be a 1-D int32 tensor [segments + 1]")
+    if cu_seqlens.device != q.device:
+        raise ValueError("cu_seqlens must be on the device of q")
+    if q.dim() != 3 or q.shape[2] != HEAD_DIM:
+        raise ValueError(f"q, k, v must be [tokens, heads, {HEAD_DIM}] (got {tuple(q.shape)})")
+    if cu_seqlens_host is not None:
+        cu = [int(x) for x in cu_seqlens_host]
+        if len(cu) != cu_seqlens.numel():
+            raise ValueError("cu_seqlens_host must have as many entries as cu_seqlens")
+    else:
+        cu = cu_seqlens.tolist()              # one synchronizing device-to-host copy
+    T, H = q.shape[0], q.shape[1]
+    scale = DEFAULT_SCALE if softmax_scale is None else float(softmax_scale)
+    dev = q.device.index if q.device.index is not None else torch.cuda.current_device()
+    plan = get_plan(T, H, cu, scale, dev, False, fmt, q_centre, False, HEAD_DIM, False)
+    ws = _shared_workspace(dev, plan.workspace_bytes)
+    quantize(plan, q, k, v, ws)
+    lse = torch.empty((H, T), dtype=torch.float32, device=q.device) if return_lse else None
+    out = forward(plan, ws, out, lse)
+    return (out, lse) if return_lse else out
+
+
+def varlen_attention_fp8(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: torch.Tensor,
+                         out: Optional[torch.Tensor] = None, *, cu_seqlens_host: Optional[Sequence[int]] = None,
+                         softmax_scale: Optional[float] = None, return_lse: bool = False):
+    """Non-causal packed-varlen self-attention on E4M3 operands: for every
+    segment [a, b) of cu_seqlens and head h, out[a:b, h] = softmax(q[a:b, h]
+    k[a:b, h]^T softmax_scale) v[a:b, h], BF16 [tokens, heads, 128].  The
+    E4M3 path of this library (the sglang PR's FP8 kernel recipe), with the
+    FlashInfer page's calling convention; ``return_lse`` adds the natural-log
+    LSE [heads, tokens]."""
+    return _varlen(q, k, v, cu_seqlens, out, cu_seqlens_host, softmax_scale, return_lse, "e4m3", False)
+
+
+def varlen_attention_mxfp4(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: torch.Tensor,
+                           out: Optional[torch.Tensor] = None, *, cu_seqlens_host: Optional[Sequence[int]] = None,
+                           softmax_scale: Optional[float] = None, return_lse: bool = False):
+    """The same on block-scaled FP4 operands with Q centred by its 128-row
+    block means (the page's recipe in gfx950's MX form: one power-of-two scale
+    per 32 elements); several times the E4M3 error."""
+    return _varlen(q, k, v, cu_seqlens, out, cu_seqlens_host, softmax_scale, return_lse, "mxfp4", True)

@@ -528,3 +528,17 @@ def test_plan_cache_is_bounded_and_lru():
     assert all(p.handle is not None for p in extra[-n:])
     fa.clear_plan_cache()
     assert not fa._PLANS and all(p.handle is None for p in extra)
+
+
+def test_varlen_entry_points_validate_arguments():
+    import torch
+    q = torch.zeros((64, 2, 128), dtype=torch.bfloat16)
+    for bad in ([0, 64], torch.tensor([0, 64], dtype=torch.int64), torch.tensor([[0, 64]], dtype=torch.int32)):
+        with pytest.raises(ValueError):
+            fa.varlen_attention_fp8(q, q, q, bad)
+    with pytest.raises(ValueError):                        # wrong head size
+        z = torch.zeros((64, 2, 96), dtype=torch.bfloat16)
+        fa.varlen_attention_mxfp4(z, z, z, torch.tensor([0, 64], dtype=torch.int32))
+    with pytest.raises(ValueError):                        # host copy of another length
+        fa.varlen_attention_fp8(q, q, q, torch.tensor([0, 64], dtype=torch.int32), cu_seqlens_host=[0, 32, 64])
+    assert fa.workspace_bytes(0) == 0
