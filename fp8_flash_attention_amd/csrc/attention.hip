@@ -791,17 +791,19 @@ __global__ __launch_bounds__(2 * BM, 256 / BM) void k_attn(AttentionArgs a) {
 // item, out = sum_i W_i O_i / sum_i W_i with O_i the piece's normalized output
 // and log2 W_i its weight (log-sum-exp combination over disjoint key ranges),
 // rounded to BF16 once; the LSE is the log-sum-exp of the pieces' LSEs.
-// 256 threads per 128 query rows (blockIdx.y picks the 128-row block of the
-// item): thread t takes row t/2, channels (D/2)*(t%2) .. +D/2.  The pieces are
-// added in index order, so the result is deterministic.
+// 64 threads per 32 query rows (blockIdx.y picks the 32-row block of the
+// item, so even a few split items spread over many compute units): thread t
+// takes row t/2, channels (D/2)*(t%2) .. +D/2.  The pieces are added in index
+// order, so the result is deterministic.
+constexpr int kCombineRows = 32;
 template <int D>
-__global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
+__global__ __launch_bounds__(2 * kCombineRows) void k_combine(CombineArgs a) {
   constexpr int HD = D / 2;   // channels per thread
   const int4 it = a.items[blockIdx.x];
   const SegInfo si = a.segs[it.x];
   const int n = split_pieces(it.w);
   const int slot0 = split_slot0(it.w);
-  const int r = 128 * blockIdx.y + (threadIdx.x >> 1);
+  const int r = kCombineRows * blockIdx.y + (threadIdx.x >> 1);
   const int half = threadIdx.x & 1;
   const int qrow = it.y + r;
   if (qrow >= si.len) return;
@@ -870,9 +872,9 @@ __global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
 hipError_t launch_combine(const CombineArgs& a, hipStream_t stream) {
   if (a.nitems == 0) return hipSuccess;
   if (a.head_dim == 64)
-    hipLaunchKernelGGL(k_combine<64>, dim3(a.nitems, a.bm / 128), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(k_combine<64>, dim3(a.nitems, a.bm / kCombineRows), dim3(2 * kCombineRows), 0, stream, a);
   else
-    hipLaunchKernelGGL(k_combine<kHeadDim>, dim3(a.nitems, a.bm / 128), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(k_combine<kHeadDim>, dim3(a.nitems, a.bm / kCombineRows), dim3(2 * kCombineRows), 0, stream, a);
   return hipGetLastError();
 }
 
