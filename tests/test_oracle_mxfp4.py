@@ -253,6 +253,30 @@ def test_block_mean_centring_identical_rows():
     np.testing.assert_array_equal(z["qm_e"][0], want["e"])
 
 
+def test_q_block_means_equal_exact_rational_means():
+    """Q block means (128-row blocks from each segment start, a short block at
+    a segment's end) against exact rational means of the BF16 rows: the block
+    bounds and the row count are pinned here, since the lossless pins cannot
+    see them (x = (Q - m) K + m K for any m)."""
+    from fractions import Fraction
+    rng = np.random.default_rng(12)
+    T, H, D = 470, 2, 128
+    cu = [0, 300, 301, 470]
+    q = torch.from_numpy(rng.standard_normal((T, H, D)).astype(np.float32)).bfloat16()
+    k = torch.from_numpy(rng.standard_normal((T, H, D)).astype(np.float32)).bfloat16()
+    z = mxfp4.quantize_mxfp4(q, k, k, cu, 0.088)
+    qf = q.float().numpy()
+    blocks = [(0, 128), (128, 256), (256, 300), (300, 301), (301, 429), (429, 470)]
+    assert z["qm"].shape[0] == len(blocks)
+    for i, (a, b) in enumerate(blocks):
+        for h in range(H):
+            for d in range(0, D, 17):
+                exact = sum(Fraction(float(v)) for v in qf[a:b, h, d]) / (b - a)
+                # BF16 rows: the float64 sums are exact, so the division and the
+                # float32 cast are the only roundings
+                assert z["qm"][i, h, d] == np.float32(float(exact)), (i, h, d)
+
+
 def test_fp4_error_is_bounded_on_gaussian_inputs():
     """Gaussian inputs: the variant stays within the pages' FP4 tolerance
     (atol 1.0, rtol 0.1 against the float oracle) and its relative RMS error
