@@ -42,8 +42,8 @@
 //     and j+32) into row 0 and those of query 16+j (lanes j+16 and j+48) into
 //     row 1.  l is the sum of the E4M3 probabilities that actually weight V.
 //     The LSE, when asked for, is the log of l (the denominator the output
-//     is normalized by, so partial results combine exactly by it); with exact
-//     probabilities an FP32 sum of the unrounded 2^x is kept for it instead.
+//     is normalized by, so partial results combine exactly by it), with
+//     either probability encoding.
 //   * Probabilities: p = 2^x, x = c*s + nbx with c = softmax_scale * s_q *
 //     s_k * log2(e) and nbx = log2(112) - c*m for a per-query reference
 //     maximum m.  The quantizer makes c a power of two, so the score products
@@ -211,7 +211,6 @@ __global__ __launch_bounds__(2 * BM, 256 / BM) void k_attn(AttentionArgs a) {
   constexpr float kRef = EXACT ? kLog2Ref : kYRef;
   constexpr float kMax = EXACT ? kLog2Max : kYMax;
   constexpr float kUnit = EXACT ? 1.f : 0.125f;   // log2 units per unit of the frame
-  constexpr bool LSUM = LSE && EXACT;             // the LSE from an FP32 sum of the unrounded 2^x
   static_assert(BM == 128 || BM == 256, "4 or 8 waves x 32 queries");
   constexpr int kTile = kBN * D;                 // bytes of one K (or V^T) tile
   constexpr int kVRing = kSlots * kTile;         // V ring follows the K ring in LDS
@@ -351,7 +350,6 @@ __global__ __launch_bounds__(2 * BM, 256 / BM) void k_attn(AttentionArgs a) {
 
   v16f O[NDB];     // O^T: lane l holds query l%32, channels 32*db + 8*(r/4) + 4*(l/32) + r%4
   v4f lacc = {};   // row sums of the packed P: lane j < 16 holds query j (row 0) and 16+j (row 1)
-  float lex = 0.f; // FP32 row sum of the unrounded probabilities (LSUM only; this lane's keys, current frame)
   float nb = 0.f;  // exp2 argument offset: x = c*s + nb
   float pshift = 0.f;   // reference shift still to be applied to O and l (log2 of the factor)
   bool pending = false; // wave-uniform: some lane has a pshift
@@ -403,7 +401,6 @@ __global__ __launch_bounds__(2 * BM, 256 / BM) void k_attn(AttentionArgs a) {
     const float shift = over ? kRef - xm : 0.f;
     nb += shift;
     pshift = shift;
-    if (LSUM) lex *= __builtin_amdgcn_exp2f(shift * kUnit);   // lex takes this tile's p in the new frame
 #pragma unroll
     for (int i = 0; i < 16; i++) { S[0][i] += shift; S[1][i] += shift; NB[i] += shift; }
   };
@@ -473,10 +470,6 @@ __global__ __launch_bounds__(2 * BM, 256 / BM) void k_attn(AttentionArgs a) {
       float p[4];
 #pragma unroll
       for (int i = 0; i < 4; i++) p[i] = __builtin_amdgcn_exp2f(S[kb][4 * q4 + i]);
-      if (LSUM) {
-#pragma unroll
-        for (int i = 0; i < 4; i++) lex += p[i];
-      }
       return cvt4(p[0], p[1], p[2], p[3]);
     } else {
       uint32_t w = __builtin_amdgcn_cvt_pk_u8_f32(S[kb][4 * q4 + 0], 0, 0u);
@@ -556,13 +549,10 @@ __global__ __launch_bounds__(2 * BM, 256 / BM) void k_attn(AttentionArgs a) {
   for (int i = 0; i < kBarEvery; i++) load_v(kBarEvery + i, (kBarEvery + i) % kSlots);
   first_tile();
   keep(P);
-  // V operands of the next product, read at the end of the iteration before
-  // it (all four; two when the LSE sum needs the registers, the other two at
-  // the top of the iteration, still ahead of its barrier).
-  constexpr int kPre = NDB == 4 ? (LSUM ? 2 : 4) : NDB;
+  // V operands of the next product, read at the end of the iteration before it.
   v8i vf[NDB];
 #pragma unroll
-  for (int db = 0; db < kPre; db++) vf[db] = lds_read32(smem + kVRing + db * 2048, voff[0], voff[1]);
+  for (int db = 0; db < NDB; db++) vf[db] = lds_read32(smem + kVRing + db * 2048, voff[0], voff[1]);
   // Iteration t (S holds tile t's scores, P tile t-1's probabilities, vf the
   // V(t-1) operands): at even t the barrier and the loads above; a pending
   // rescale; O += P(t-1) V(t-1), softmax of tile t with the scores of tile
@@ -580,13 +570,6 @@ __global__ __launch_bounds__(2 * BM, 256 / BM) void k_attn(AttentionArgs a) {
   auto iter = [&](int t, auto ph_c, auto tail_c) __attribute__((always_inline)) {
     constexpr int PH = decltype(ph_c)::value;   // t % kSlots
     constexpr bool TAIL = decltype(tail_c)::value;   // may be the last tile: mask keys past the range end
-    // With the LSE sum, two of the four V(t-1) operands are read here, before
-    // the barrier: the loads after it may refill V(t-1)'s slot.
-    if constexpr (LSUM && kPre < NDB) {
-      const uint8_t* vp = smem + kVRing + ((PH + kSlots - 1) % kSlots) * kTile;   // V(t-1)
-      vf[2] = lds_read32(vp + 2 * 2048, voff[0], voff[1]);
-      vf[3] = lds_read32(vp + 3 * 2048, voff[0], voff[1]);
-    }
     if (PH % kBarEvery == 0) {
       wait_vmcnt<0>();
       barrier();
@@ -636,10 +619,8 @@ __global__ __launch_bounds__(2 * BM, 256 / BM) void k_attn(AttentionArgs a) {
       Pn[4] = probs4(1, 0, kbase);
       fence();
       const v16f s1 = mfma_fp8_scaled(kf[1][0], qf[0], NB, c_e8m0);
-      if (!LSUM) {
-        vf[2] = lds_read32(vn + 2 * 2048, voff[0], voff[1]);
-        vf[3] = lds_read32(vn + 3 * 2048, voff[0], voff[1]);
-      }
+      vf[2] = lds_read32(vn + 2 * 2048, voff[0], voff[1]);
+      vf[3] = lds_read32(vn + 3 * 2048, voff[0], voff[1]);
       Pn[5] = probs4(1, 1, kbase);
       fence();
       S[0] = mfma_fp8_scaled(kf[0][1], qf[1], s0, c_e8m0);
@@ -712,11 +693,6 @@ __global__ __launch_bounds__(2 * BM, 256 / BM) void k_attn(AttentionArgs a) {
       }
       msel[w] = sel_lane ? word : 0;
     }
-    if constexpr (LSUM && kPre < NDB) {
-      const uint8_t* vp = smem + kVRing + ((nkt - 1) % kSlots) * kTile;
-      vf[2] = lds_read32(vp + 2 * 2048, voff[0], voff[1]);
-      vf[3] = lds_read32(vp + 3 * 2048, voff[0], voff[1]);
-    }
 #pragma unroll
     for (int db = 0; db < NDB; db++) O[db] = mfma_fp8(vf[db], P, O[db]);
     lacc = mfma16_fp8(msel, P, lacc);
@@ -772,12 +748,10 @@ __global__ __launch_bounds__(2 * BM, 256 / BM) void k_attn(AttentionArgs a) {
       }
   }
   if (LSE) {
-    // the log of the denominator (l, or with exact probabilities the FP32 sum
-    // of 2^x; keys past the end of the range were masked, so they added
-    // nothing), back in the frame of the uncentred scores
-    const float le = LSUM ? sum_pair32(lex) : lt;
+    // the log of the denominator l (keys past the end of the range were
+    // masked, so they added nothing), back in the frame of the uncentred scores
     if (lg == 0 && qrow < L) {
-      const float lse2 = __log2f(le) - nbx;
+      const float lse2 = __log2f(lt) - nbx;
       const float v = lse2 * kLn2 + a.softmax_scale * s_q * qmu;
       if (slot >= 0)
         a.part_lse[slot * kPartRows + 32 * wave + lq] = v;
@@ -882,10 +856,14 @@ template <int D, int BM, bool EXACT>
 void launch_attention_d(const AttentionArgs& a, hipStream_t stream) {
   const dim3 g(a.nitems), b(2 * BM);
   if (a.causal) {
-    if (a.lse != nullptr)
-      hipLaunchKernelGGL((k_attn<true, true, D, BM, EXACT>), g, b, 0, stream, a);
-    else
-      hipLaunchKernelGGL((k_attn<false, true, D, BM, EXACT>), g, b, 0, stream, a);
+    // causal plans always use 256-query items (the planner picks 128 only
+    // for small non-causal work), so no 128-query causal kernel is built
+    if constexpr (BM == 256) {
+      if (a.lse != nullptr)
+        hipLaunchKernelGGL((k_attn<true, true, D, BM, EXACT>), g, b, 0, stream, a);
+      else
+        hipLaunchKernelGGL((k_attn<false, true, D, BM, EXACT>), g, b, 0, stream, a);
+    }
   } else if (a.lse != nullptr) {
     hipLaunchKernelGGL((k_attn<true, false, D, BM, EXACT>), g, b, 0, stream, a);
   } else {
@@ -905,6 +883,7 @@ void launch_attention_e(const AttentionArgs& a, hipStream_t stream) {
 
 hipError_t launch_attention(const AttentionArgs& a, hipStream_t stream) {
   if (a.nitems == 0) return hipSuccess;
+  if (a.causal && a.bm != 256) return hipErrorInvalidValue;   // see launch_attention_d
   if (a.exact_probs)
     launch_attention_e<true>(a, stream);
   else

@@ -273,12 +273,13 @@ fp8attn_status fp8attn_quantize_noalloc(fp8attn_plan_t plan, const void* q, cons
  * lse           NULL, or device float [heads][tokens]: natural-log
  *               log-sum-exp of softmax_scale * q.k over the row's keys
  *               (uncentred keys), taken as the log of the denominator that
- *               normalizes the row: for default E4M3 plans the sum of the
+ *               normalizes the row: for E4M3 plans the sum of the
  *               probability weights applied to V (each within a factor
- *               [0.9203, 1.0645] of the exact exp, see below), so partial
- *               results combine by it exactly; with
- *               FP8ATTN_PLAN_EXACT_PROBS and for FP4 plans the FP32 sum of
- *               the unrounded exponentials.
+ *               [0.9203, 1.0645] of the exact exp with the default code, see
+ *               below, and [1 - 2^-4, 1 + 2^-4] with
+ *               FP8ATTN_PLAN_EXACT_PROBS), so partial results combine by it
+ *               exactly; for FP4 plans the FP32 sum of the unrounded
+ *               exponentials.
  * stream        hipStream_t (NULL = default stream).
  *
  * workspace     the workspace the codes were quantized into.  Forward reads
