@@ -281,10 +281,6 @@ __global__ __launch_bounds__(64 * kWaves, 2) void k_attn_mx(MxAttentionArgs a) {
   v16f S[2];       // exp2 arguments of the current tile, lane keys 32*lg + 16*kb + r
   v4i P;           // E2M1 probabilities of the previous tile, then of the current one
   int pe = 127;    // E8M0 scale byte of this lane's probabilities
-  // LSE: sum of the exact 2^x of this lane's keys, in the frame of nb, over
-  // the tiles whose probabilities have gone into O (lex), and over the tile in
-  // P (lp; added once the rescale for its reference has been applied to lex)
-  float lex = 0.f, lp = 0.f;
 
   auto scores = [&](const v4i kf[2][2], const int ks[2], v16f& s0, v16f& s1) __attribute__((always_inline)) {
     if (QC) {
@@ -315,7 +311,6 @@ __global__ __launch_bounds__(64 * kWaves, 2) void k_attn_mx(MxAttentionArgs a) {
       auto pa = __builtin_amdgcn_permlane16_swap(__float_as_uint(alpha), __float_as_uint(alpha), false, false);
       lacc[0] *= alpha;
       lacc[1] *= __uint_as_float(pa[1]);   // lane j < 16: alpha of query 16+j
-      if (LSE) lex *= alpha;
 #pragma unroll
       for (int db = 0; db < 4; db++) O[db] *= alpha;
       pshift = 0.f;
@@ -372,7 +367,6 @@ __global__ __launch_bounds__(64 * kWaves, 2) void k_attn_mx(MxAttentionArgs a) {
     float p[8];
 #pragma unroll
     for (int i = 0; i < 8; i++) p[i] = __builtin_amdgcn_exp2f(S[w >> 1][8 * (w & 1) + i]);
-    if (LSE) lp += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
     return cvt8(p, scale);
   };
   auto scale_of = [](int e) { return __uint_as_float((uint32_t)(e + 127) << 23); };
@@ -451,10 +445,6 @@ __global__ __launch_bounds__(64 * kWaves, 2) void k_attn_mx(MxAttentionArgs a) {
       barrier();
     }
     rescale();
-    if (LSE) {
-      lex += lp;
-      lp = 0.f;
-    }
     if (PH % kBarEvery == 0) {
 #pragma unroll
       for (int i = 1; i <= kBarEvery; i++) load_k(t + kBarEvery + i, (PH + kBarEvery + i) % kSlots);
@@ -524,10 +514,6 @@ __global__ __launch_bounds__(64 * kWaves, 2) void k_attn_mx(MxAttentionArgs a) {
   wait_vmcnt<0>();
   barrier();
   rescale();
-  if (LSE) {
-    lex += lp;
-    lp = 0.f;
-  }
   if (nkt > 1) {
     const int tl = nkt - 1;
 #pragma unroll
@@ -548,7 +534,6 @@ __global__ __launch_bounds__(64 * kWaves, 2) void k_attn_mx(MxAttentionArgs a) {
 #pragma unroll
   for (int db = 0; db < 4; db++) O[db] = mfma4<0, 0>(vf[db], P, O[db], __builtin_amdgcn_ubfe(vsc, 8 * db, 8), pe);
   lacc = mfma16_4(sel, P, lacc, pe);
-  if (LSE) lex += lp;
   // The products must run with every lane active: a matrix instruction inside
   // the store's lane-divergent branch would read the operands of inactive
   // lanes (other queries' keys and channels) as zero.
@@ -596,18 +581,18 @@ __global__ __launch_bounds__(64 * kWaves, 2) void k_attn_mx(MxAttentionArgs a) {
       }
   }
   if (LSE) {
-    // natural-log LSE of the uncentred scores: the exact sum of 2^x over the
-    // visible keys (masked keys added 0), the frame offset nb taken out, plus
+    // natural-log LSE of the uncentred scores: the log of the row's
+    // normalizer l (the sum of the block-scaled E2M1 weights applied to V;
+    // masked keys added 0), the frame offset nb taken out, plus
     // (Qhat + QMhat) . mu, the part of every score that centring K by its
     // segment mean mu took out (both operands carry the score factor, so the
     // term is in log2 units).  Each lane holds half of its query's channels.
     const float* mu = a.mu + ((size_t)it.x * a.heads + h) * kHeadDim + 32 * lg;
     float qmu = dot_mu(qf, qsc, mu);
     if (QC) qmu += dot_mu(mf, msc, mu);
-    const float le = sum_pair32(lex);
     const float qm_all = sum_pair32(qmu);
     if (lg == 0 && qrow < L) {
-      const float v = (__log2f(le) - nb + qm_all) * kLn2;
+      const float v = (__log2f(lt) - nb + qm_all) * kLn2;
       if (slot >= 0)
         a.part_lse[slot * kPartRows + 32 * wave + lq] = v;
       else

@@ -150,9 +150,8 @@ fp8attn_status fp8attn_plan(fp8attn_plan_t* plan_out, int64_t tokens, int32_t he
  *   E = ceil(max_b x - log2 6); out = sum phat V / sum phat, rounded to BF16.
  *   Expect several times the E4M3 error (the page reports about 4x for its
  *   NVFP4 recipe).  The LSE (if requested) is the natural-log log-sum-exp of
- *   the uncentred scores from the dequantized operands:
- *   ln 2 * (log2 sum_j 2^(x_j) + (Qhat + QMhat) . mu), the FP32 sum of the
- *   unrounded 2^x (not of the E2M1 probabilities).  Work items split along
+ *   the uncentred scores from the dequantized operands, taken as the log of
+ *   the row's normalizer: ln 2 * (log2 sum_j phat_j + (Qhat + QMhat) . mu).  Work items split along
  *   the keys as for E4M3 plans (128-query items, two workgroups per CU).
  * FP8ATTN_PLAN_Q_CENTRE (with FP8ATTN_PLAN_MXFP4 only): Q rows are centred by
  *   the mean of their 128-row block (blocks of a segment from its start; the
@@ -278,8 +277,8 @@ fp8attn_status fp8attn_quantize_noalloc(fp8attn_plan_t plan, const void* q, cons
  *               [0.9203, 1.0645] of the exact exp with the default code, see
  *               below, and [1 - 2^-4, 1 + 2^-4] with
  *               FP8ATTN_PLAN_EXACT_PROBS), so partial results combine by it
- *               exactly; for FP4 plans the FP32 sum of the unrounded
- *               exponentials.
+ *               exactly; for FP4 plans likewise the sum of the block-scaled
+ *               E2M1 weights.
  * stream        hipStream_t (NULL = default stream).
  *
  * workspace     the workspace the codes were quantized into.  Forward reads

@@ -55,9 +55,11 @@ power-of-two scale per 32 elements, and this variant is built on that):
    reading 1 cut at the last visible key (the last block holds the visible
    keys only).
 9. LSE (``lse_mxfp4_rows``): the natural-log log-sum-exp of the uncentred
-   scores over the row's visible keys from the dequantized operands:
-   ln 2 * (log2 sum_j 2^(x_ij) + (Qhat_i + QMhat_i) . mu), the second term
-   adding back what centring K by its segment mean mu took out.
+   scores over the row's visible keys, taken (as for the E4M3 path) as the
+   log of the row's normalizer, the sum of the weights phat of reading 6:
+   ln 2 * (log2 sum_j phat_ij + (Qhat_i + QMhat_i) . mu), the second term
+   adding back what centring K by its segment mean mu took out.  Where every
+   weight is exact (phat = 2^x) this is the log-sum-exp itself.
 
 Parity pins live in ``tests/test_oracle_mxfp4.py``.
 """
@@ -321,7 +323,8 @@ def attention_mxfp4_rows(z: Dict[str, np.ndarray], cu_seqlens: Sequence[int],
 def lse_mxfp4_rows(z: Dict[str, np.ndarray], cu_seqlens: Sequence[int],
                    rows: Sequence[int], heads: Sequence[int], causal: bool = False) -> np.ndarray:
     """Reading 9: natural-log LSE of the uncentred scores per (row, head) from
-    the dequantized operands of ``z``.  float64 [len(rows), len(heads)]."""
+    the dequantized operands of ``z``, as the log of the sum of the row's
+    quantized weights.  float64 [len(rows), len(heads)]."""
     cu = list(cu_seqlens)
     ops = dequantized_operands(z, cu)
     out = np.zeros((len(rows), len(heads)), np.float64)
@@ -330,7 +333,6 @@ def lse_mxfp4_rows(z: Dict[str, np.ndarray], cu_seqlens: Sequence[int],
         for m, h in enumerate(heads):
             qop = ops["Q"][r, h] + ops["QM"][r, h]
             x = ops["K"][a:e, h] @ qop
-            mx = x.max()
-            lse2 = mx + np.log2(np.sum(np.exp2(x - mx))) + qop @ z["mu"][s, h].astype(np.float64)
+            lse2 = np.log2(np.sum(quantize_probs(x))) + qop @ z["mu"][s, h].astype(np.float64)
             out[n, m] = lse2 * np.log(2.0)
     return out

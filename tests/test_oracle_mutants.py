@@ -94,7 +94,8 @@ MXFP4_PINS = ["test_e2m1_table_against_ocp_values", "test_e2m1_encode_brute_forc
               "test_one_hot_key_returns_its_value_row", "test_equal_scores_return_mean_of_v",
               "test_lossless_inputs_reduce_to_plain_softmax", "test_segments_and_q_blocks_are_independent",
               "test_block_mean_centring_identical_rows", "test_causal_lossless_inputs_reduce_to_plain_causal_softmax",
-              "test_lse_lossless_inputs_equal_the_float64_lse", "test_q_block_means_equal_exact_rational_means"]
+              "test_lse_lossless_inputs_equal_the_float64_lse", "test_q_block_means_equal_exact_rational_means",
+              "test_lse_is_the_log_of_the_quantized_weights"]
 
 # (oracle module, function, expression, planted replacement, pins module, pin names, what the mistake is)
 MUTANTS = [

@@ -335,6 +335,23 @@ def test_lse_lossless_inputs_equal_the_float64_lse(q_centre, causal):
     np.testing.assert_allclose(got, want, rtol=1e-8, atol=1e-7)
 
 
+def test_lse_is_the_log_of_the_quantized_weights():
+    """Reading 9 on a lossy row worked by hand: scores +-1.5 (Q operand 1.5 =
+    12 * 1/8, keys +-1 after centring), block exponent E = ceil(1.5 - log2 6)
+    = -1, so 2^(x - E) = 2^2.5 = 5.66 rounds to 6 and 2^-0.5 = 0.71 to 0.5:
+    weights 3 and 0.25, LSE ln 3.25 (the exact log-sum-exp would be
+    ln(2^1.5 + 2^-1.5) = 1.1575, which a sum of the unrounded 2^x gives)."""
+    T, H, D = 2, 1, 128
+    q = torch.zeros((T, H, D))
+    q[:, 0, 0] = 12.0
+    k = torch.zeros((T, H, D))
+    k[0, 0, 0], k[1, 0, 0] = 1.0, -1.0
+    v = torch.ones((T, H, D))
+    z = mxfp4.quantize_mxfp4(q.bfloat16(), k.bfloat16(), v.bfloat16(), [0, T], SIGMA_C8, q_centre=False)
+    got = mxfp4.lse_mxfp4_rows(z, [0, T], [0, 1], [0])
+    np.testing.assert_allclose(got, np.log(3.25), rtol=0, atol=1e-12)
+
+
 def test_lse_without_the_mean_term_fails(monkeypatch):
     """Planted mistake: the LSE of the centred scores only (q . mu dropped)."""
     cu = [0, 256]
