@@ -401,9 +401,11 @@ def varlen_attention_fp8(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_s
     """Non-causal packed-varlen self-attention on E4M3 operands: for every
     segment [a, b) of cu_seqlens and head h, out[a:b, h] = softmax(q[a:b, h]
     k[a:b, h]^T softmax_scale) v[a:b, h], BF16 [tokens, heads, 128].  The
-    E4M3 path of this library (the sglang PR's FP8 kernel recipe), with the
-    FlashInfer page's calling convention; ``return_lse`` adds the natural-log
-    LSE [heads, tokens]."""
+    E4M3 path of this library (the recipe of sglang PR "[diffusion] attention:
+    add fp8_fa_sm120 FP8 backend for SM120 GPUs", "Modifications"), with the
+    calling convention of the FlashInfer page
+    "flashinfer.diffusion_ops.minimax_h3_sm120_varlen_attention_nvfp4";
+    ``return_lse`` adds the natural-log LSE [heads, tokens]."""
     return _varlen(q, k, v, cu_seqlens, out, cu_seqlens_host, softmax_scale, return_lse, "e4m3", False)
 
 
