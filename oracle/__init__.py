@@ -10,7 +10,8 @@ it; the two share no code.  The oracle is plain and slow on purpose:
   E4M3 operands), used to show which rows no FP8 kernel can bring within the
   exact element-wise bar.
 * ``oracle.quantize``  - per-head E4M3 quantization of Q/K/V (K centred by its
-  segment's per-channel mean).
+  segment's per-channel mean; optionally Q centred by its 128-row block mean,
+  with the exact mean term in the Q operand).
 * ``oracle.e4m3``      - bit-level OCP E4M3 encoder/decoder.
 * ``oracle.compare``   - relative-RMS and max-abs comparators.
 * ``oracle.mxfp4``     - the block-scaled FP4 variant: E2M1 codes with one

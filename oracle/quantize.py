@@ -15,7 +15,8 @@ What it follows
   FlashInfer "minimax_h3_sm120_varlen_attention_nvfp4" page does this for its
   block-scaled operands and notes that the softmax is unchanged by it: a
   per-segment constant added to every key only adds a per-query constant to
-  every score of that segment.  Q is not centred.
+  every score of that segment.  Q is not centred unless asked for (Q
+  centring below).
 * Codes: ``e4m3(fl32(y / s_h))`` with IEEE float32 division, where ``y = x``
   for Q and V and ``y = fl32(x - mu)`` for K.
 
@@ -40,6 +41,20 @@ its float32 bits against the same steps evaluated in exact rational
 arithmetic with a search for the power of two (which catches an off-by-one in
 the exponent where fl32(f * base) is itself a power of two), plus range
 properties (at least amax/448, below twice it, factor a power of two).
+
+Q centring (``centre_q``, ``quantize(..., q_centre=True)``): the FlashInfer
+page centres Q rows by the mean of their 128-row block and adds the block-mean
+term qm . k back to the scores, so the softmax is that of the uncentred Q.
+The reading taken for E4M3 operands: Q's amax, scale and codes are those of
+fl32(q - qm); the mean term is added back exactly (``qcentre_operand`` gives
+the float64 operand dequant(code) * s_q + qm, which the attention oracle then
+takes as its Q).  The block mean is the same fixed-order mean as the FP4
+variant's (``mxfp4.block_mean`` over ``mxfp4.q_blocks``).  Pins: a Q whose
+blocks hold equal rows gives all-zero codes and an output equal to the
+float64 attention of the block means; adding a per-block constant to Q (all
+values exact) shifts qm by that constant and leaves every code unchanged;
+zero-mean blocks reproduce the uncentred quantization bit for bit; the block
+means against ``math.fsum`` per block and channel.
 
 Per-(segment, head) scales (``quantize_segments``) are a variant the product
 offers for packed batches: the sglang PR quantizes per head over the whole
@@ -152,31 +167,80 @@ def quantize_k(x, cu_seqlens: List[int]) -> Dict[str, np.ndarray]:
     return {"codes": codes, "scale": sc, "mu": mu}
 
 
-def quantize(q, k, v, cu_seqlens: List[int], softmax_scale: float = None) -> Dict[str, np.ndarray]:
+def centre_q(q, cu_seqlens: List[int]):
+    """Q centred by the mean of its 128-row block (Q centring of the FlashInfer
+    page): returns (fl32(q - qm) [T, H, D] float32, qm [nq, H, D] float32) with
+    qm the fixed-order mean of each block of ``mxfp4.q_blocks`` (segments in
+    order, blocks of a segment counted from its start, the last one possibly
+    shorter): a float64 sum over the block's rows in ascending order, divided
+    by the row count, rounded to float32."""
+    from .mxfp4 import block_mean, q_blocks
+    qf = _as_f32(q)
+    blocks = q_blocks(cu_seqlens)
+    qm = np.zeros((len(blocks), qf.shape[1], qf.shape[2]), np.float32)
+    qc = np.zeros_like(qf)
+    for i, (_, a, b) in enumerate(blocks):
+        qm[i] = block_mean(qf, a, b)
+        qc[a:b] = qf[a:b] - qm[i][None]          # float32 subtraction, correctly rounded
+    return qc, qm
+
+
+def quantize(q, k, v, cu_seqlens: List[int], softmax_scale: float = None,
+             q_centre: bool = False) -> Dict[str, np.ndarray]:
     """All three tensors.  Keys: q_codes, k_codes, v_codes ([T, H, D] uint8),
     scales ([3, H] float32, rows Q, K, V) and mu ([nseg, H, D] float32).  With
     ``softmax_scale`` given, Q's scale is ``q_scale_pow2`` of its amax/448 scale
-    (the product's rule)."""
+    (the product's rule).
+
+    ``q_centre``: Q is replaced by fl32(q - qm) (``centre_q``) before its amax
+    and its codes are taken, and the block means come back as ``qm``
+    [nq, H, D]; the attention then uses the operand ``qcentre_operand``, the
+    dequantized centred Q plus the exact block mean (the mean term qm . k added
+    back to the scores without rounding)."""
     rk = quantize_k(k, cu_seqlens)
+    qm = None
+    if q_centre:
+        q, qm = centre_q(q, cu_seqlens)
     rq = quantize_plain(q)
     if softmax_scale is not None:
         rq = quantize_plain(q, q_scale_pow2(rq["scale"], rk["scale"], softmax_scale))
     rv = quantize_plain(v)
-    return {
+    out = {
         "q_codes": rq["codes"], "k_codes": rk["codes"], "v_codes": rv["codes"],
         "scales": np.stack([rq["scale"], rk["scale"], rv["scale"]]).astype(np.float32),
         "mu": rk["mu"],
     }
+    if q_centre:
+        out["qm"] = qm
+    return out
 
 
-def quantize_segments(q, k, v, cu_seqlens: List[int], softmax_scale: float = None) -> Dict[str, np.ndarray]:
+def qcentre_operand(q_codes: np.ndarray, q_scale: np.ndarray, qm: np.ndarray,
+                    cu_seqlens: List[int]) -> np.ndarray:
+    """float64 Q operand of a Q-centred quantization: e4m3_value(code) * s_q
+    plus the block mean of the row's 128-row block (``qm`` in the order of
+    ``mxfp4.q_blocks``).  ``q_scale`` is [H], or [nseg, H] for per-segment
+    scales."""
+    from .mxfp4 import q_blocks
+    qs = np.asarray(q_scale, np.float64)
+    out = np.zeros(q_codes.shape, np.float64)
+    for i, (s, a, b) in enumerate(q_blocks(cu_seqlens)):
+        sc = qs[s] if qs.ndim == 2 else qs
+        out[a:b] = e4m3.decode(q_codes[a:b]) * sc[None, :, None] + np.asarray(qm[i], np.float64)[None]
+    return out
+
+
+def quantize_segments(q, k, v, cu_seqlens: List[int], softmax_scale: float = None,
+                      q_centre: bool = False) -> Dict[str, np.ndarray]:
     """Per-(segment, head) scales: every segment is quantized as if it were the
     whole call, with the per-head rule above applied to that segment's tokens
     only (so no segment's codes depend on another segment's values).
 
     Keys as ``quantize`` except ``scales`` [3, nseg, H] (rows Q, K, V).  An
     empty segment gets the scales of an all-zero head (1.0, and Q's rounded
-    value for it when ``softmax_scale`` is given).
+    value for it when ``softmax_scale`` is given).  With ``q_centre`` the
+    block means of all segments come back as ``qm`` (blocks of
+    ``mxfp4.q_blocks``, which never cross a segment boundary).
     """
     qf, kf, vf = _as_f32(q), _as_f32(k), _as_f32(v)
     T, H, D = qf.shape
@@ -184,13 +248,18 @@ def quantize_segments(q, k, v, cu_seqlens: List[int], softmax_scale: float = Non
     out = {"q_codes": np.zeros((T, H, D), np.uint8), "k_codes": np.zeros((T, H, D), np.uint8),
            "v_codes": np.zeros((T, H, D), np.uint8), "scales": np.zeros((3, nseg, H), np.float32),
            "mu": np.zeros((nseg, H, D), np.float32)}
+    qms = []
     for s in range(nseg):
         a, b = cu_seqlens[s], cu_seqlens[s + 1]
-        r = quantize(qf[a:b], kf[a:b], vf[a:b], [0, b - a], softmax_scale)
+        r = quantize(qf[a:b], kf[a:b], vf[a:b], [0, b - a], softmax_scale, q_centre=q_centre)
         for name in ("q_codes", "k_codes", "v_codes"):
             out[name][a:b] = r[name]
         out["scales"][:, s] = r["scales"]
         out["mu"][s] = r["mu"][0]
+        if q_centre:
+            qms.append(r["qm"])
+    if q_centre:
+        out["qm"] = np.concatenate(qms, axis=0) if qms else np.zeros((0, H, D), np.float32)
     return out
 
 

@@ -26,6 +26,7 @@ from tests import test_oracle_attention as TA
 from tests import test_oracle_e4m3 as TE
 from tests import test_oracle_fp8_recipe as TF
 from tests import test_oracle_mxfp4 as TM
+from tests import test_oracle_qcentre as TQC
 from tests import test_oracle_quantize as TQ
 
 
@@ -96,6 +97,11 @@ MXFP4_PINS = ["test_e2m1_table_against_ocp_values", "test_e2m1_encode_brute_forc
               "test_block_mean_centring_identical_rows", "test_causal_lossless_inputs_reduce_to_plain_causal_softmax",
               "test_lse_lossless_inputs_equal_the_float64_lse", "test_q_block_means_equal_exact_rational_means",
               "test_lse_is_the_log_of_the_quantized_weights"]
+QCENTRE_PINS = ["test_block_means_against_fsum_over_ragged_segments",
+                "test_equal_rows_give_zero_codes_and_the_attention_of_q",
+                "test_per_block_constant_moves_the_mean_and_keeps_the_codes",
+                "test_zero_mean_blocks_reproduce_the_uncentred_quantizer",
+                "test_segment_scales_centre_each_segment_alone", "test_centring_cuts_the_error_on_offset_q"]
 
 # (oracle module, function, expression, planted replacement, pins module, pin names, what the mistake is)
 MUTANTS = [
@@ -192,6 +198,19 @@ MUTANTS = [
      "short last Q block divided by 128"),
     (M, "score_factor", "np.float32(softmax_scale) * LOG2E_F32", "np.float32(softmax_scale)", TM, MXFP4_PINS,
      "FP4 score factor without log2(e)"),
+    # E4M3 Q centring
+    (Qz, "centre_q", "qc[a:b] = qf[a:b] - qm[i][None]", "qc[a:b] = qf[a:b] + qm[i][None]", TQC, QCENTRE_PINS,
+     "E4M3 Q block mean added instead of subtracted"),
+    (Qz, "centre_q", "qc[a:b] = qf[a:b] - qm[i][None]", "qc[a:b] = qf[a:b]", TQC, QCENTRE_PINS,
+     "E4M3 Q not centred"),
+    (Qz, "centre_q", "qm[i] = block_mean(qf, a, b)", "qm[i] = block_mean(qf, a, min(b, a + 64))", TQC,
+     QCENTRE_PINS, "E4M3 Q mean over 64 rows of the block"),
+    (Qz, "qcentre_operand", "+ np.asarray(qm[i], np.float64)[None]", "- np.asarray(qm[i], np.float64)[None]", TQC,
+     QCENTRE_PINS, "mean term subtracted from the Q operand"),
+    (Qz, "qcentre_operand", "+ np.asarray(qm[i], np.float64)[None]", "+ 0.0", TQC, QCENTRE_PINS,
+     "mean term dropped from the Q operand"),
+    (Qz, "qcentre_operand", "+ np.asarray(qm[i], np.float64)[None]", "+ np.asarray(qm[max(i - 1, 0)], np.float64)[None]",
+     TQC, QCENTRE_PINS, "mean term of the previous block"),
 ]
 
 
@@ -206,5 +225,5 @@ def test_planted_mistake_fails_a_pin(monkeypatch, mod, fname, old, new, tmod, pi
 def test_unmutated_oracle_passes_every_pin_run_here():
     """The harness itself: with no mutant in place every pin listed above passes."""
     for tmod, pins in ((TA, ATTENTION_PINS), (TF, RECIPE_PINS), (TE, E4M3_PINS), (TQ, QUANTIZE_PINS),
-                       (TM, MXFP4_PINS)):
+                       (TM, MXFP4_PINS), (TQC, QCENTRE_PINS)):
         assert _failures(tmod, pins) == []

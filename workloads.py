@@ -19,7 +19,8 @@ Recipe (also stated in the design notes): a CPU ``torch.Generator`` seeded with
 rounds each to bfloat16 (round-to-nearest-even).  When ``k_offset_var`` is set,
 one more draw gives a per-(head, channel) offset ``sqrt(k_offset_var) *
 N(0, 1)`` of shape [H, 128] that is added to K in float32 before the bfloat16
-rounding.
+rounding; ``q_offset_var`` then does the same for Q (a later draw, so the
+other tensors of a workload do not change when it is set).
 """
 from __future__ import annotations
 
@@ -40,6 +41,7 @@ class Workload:
     cu_seqlens: List[int]
     seed: int
     k_offset_var: Optional[float] = None
+    q_offset_var: Optional[float] = None
     # "thd": three separate contiguous [T, H, 128] tensors.
     # "fused": views q/k/v = buf[:, 0/1/2] of one [T, 3, H, 128] buffer
     #          (token stride 3*H*128 elements, head stride 128).
@@ -89,6 +91,11 @@ WORKLOADS = {
     "s30272_h7_shard": Workload(
         "s30272_h7_shard", 30272, 7, _single(30272), 1006, k_offset_var=2.0,
         note="S=30272 with 7 heads: one eighth of the denoise-step heads, K offset as above"),
+    # the denoise-step shape with a per-(head, channel) offset on Q as well as
+    # on K (not one of the graded configurations): the case Q centring is for
+    "s30272_h56_qkoffset": Workload(
+        "s30272_h56_qkoffset", 30272, 56, _single(30272), 1008, k_offset_var=2.0, q_offset_var=2.0,
+        note="S=30272, H=56; K and Q each get a per-(head, channel) offset drawn from N(0, 2)"),
     # head_dim 64 (not one of the graded configurations): the denoise-step
     # length with 56 heads of 64 channels
     "s30272_h56_d64": Workload(
@@ -98,8 +105,10 @@ WORKLOADS = {
 
 
 def make_workload(name: str, tokens: int, heads: int, cu_seqlens: List[int], seed: int,
-                  k_offset_var: Optional[float] = None, layout: str = "thd", head_dim: int = HEAD_DIM) -> Workload:
-    return Workload(name, tokens, heads, list(cu_seqlens), seed, k_offset_var, layout, head_dim=head_dim)
+                  k_offset_var: Optional[float] = None, layout: str = "thd", head_dim: int = HEAD_DIM,
+                  q_offset_var: Optional[float] = None) -> Workload:
+    return Workload(name, tokens, heads, list(cu_seqlens), seed, k_offset_var, q_offset_var, layout,
+                    head_dim=head_dim)
 
 
 def generate(w: Workload, device: str = "cpu"):
@@ -118,6 +127,10 @@ def generate(w: Workload, device: str = "cpu"):
         off = math.sqrt(w.k_offset_var) * torch.randn((w.heads, w.head_dim), generator=g,
                                                       dtype=torch.float32)
         k = k + off.unsqueeze(0)
+    if w.q_offset_var is not None:
+        off = math.sqrt(w.q_offset_var) * torch.randn((w.heads, w.head_dim), generator=g,
+                                                      dtype=torch.float32)
+        q = q + off.unsqueeze(0)
     q, k, v = (t.to(torch.bfloat16) for t in (q, k, v))
     if w.layout == "fused":
         buf = torch.stack([q, k, v], dim=1)  # [T, 3, H, 128]
