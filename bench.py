@@ -20,9 +20,9 @@ forward launches run.
 
 Prints one JSON line.  FLOPs are counted as 4 * sum(L^2) * H * D.
 
-``--fmt mxfp4`` times the block-scaled FP4 variant instead (``--q-centre``
-adds its Q block-mean centring) and reports it against the FP4 matrix-core
-peak; the default line is the E4M3 path.
+``--fmt mxfp4`` times the block-scaled FP4 variant instead and reports it
+against the FP4 matrix-core peak; ``--q-centre`` adds Q block-mean centring
+(either format); the default line is the E4M3 path.
 """
 from __future__ import annotations
 
@@ -224,7 +224,8 @@ def main() -> int:
     ap.add_argument("--no-skeleton", action="store_true", help="skip the MFMA-only skeleton runs (profiling)")
     ap.add_argument("--fmt", choices=("e4m3", "mxfp4"), default="e4m3",
                     help="operand format: the E4M3 path (default) or the block-scaled FP4 variant")
-    ap.add_argument("--q-centre", action="store_true", help="mxfp4: centre Q by its 128-row block means")
+    ap.add_argument("--q-centre", action="store_true",
+                    help="centre Q by its 128-row block means (E4M3: mean term from a precomputed table)")
     ap.add_argument("--exact-probs", action="store_true",
                     help="e4m3: probabilities rounded from the FP32 exp2 instead of the log-linear code")
     ap.add_argument("--causal", action="store_true",
@@ -251,7 +252,7 @@ def main() -> int:
     q, k, v = generate(w, device="cuda")
     mx = args.fmt == "mxfp4"
     plan = fa.Plan(w.tokens, w.heads, w.cu_seqlens, w.softmax_scale, device=0, fmt=args.fmt,
-                   q_centre=mx and args.q_centre, causal=args.causal, head_dim=w.head_dim,
+                   q_centre=args.q_centre, causal=args.causal, head_dim=w.head_dim,
                    exact_probs=args.exact_probs and not mx)
     ws = plan.new_workspace()
     out = torch.empty((w.tokens, w.heads, w.head_dim), dtype=torch.bfloat16, device=dev)
@@ -323,7 +324,7 @@ def main() -> int:
 
     peak = FP4_PEAK_TFLOPS if mx else FP8_PEAK_TFLOPS
     kfile = "attention_mx.hip" if mx else "attention.hip"
-    key = (w.name + (":mxfp4" + (":qc" if args.q_centre else "") if mx else "") + (":causal" if args.causal else "")
+    key = (w.name + (":mxfp4" if mx else "") + (":qc" if args.q_centre else "") + (":causal" if args.causal else "")
            + (":exact" if args.exact_probs and not mx else "") + (":lse" if args.lse else ""))
     traffic = measured_traffic(key, kfile)
     res = {
@@ -344,7 +345,9 @@ def main() -> int:
         "config": {"workload": w.name, "tokens": w.tokens, "heads": w.heads, "head_dim": w.head_dim,
                    "cu_seqlens": list(w.cu_seqlens), "seed": w.seed, "softmax_scale": w.softmax_scale,
                    "k_offset_var": w.k_offset_var, "step": "quantize + forward",
-                   **({"format": "mxfp4", "q_centre": bool(args.q_centre)} if mx else {}),
+                   **({"q_offset_var": w.q_offset_var} if w.q_offset_var is not None else {}),
+                   **({"format": "mxfp4"} if mx else {}),
+                   **({"q_centre": True} if args.q_centre else {}),
                    **({"causal": True} if args.causal else {}),
                    **({"lse": True} if args.lse else {}),
                    **({} if mx else {"probabilities": "exact exp2" if args.exact_probs else "log-linear E4M3 code"})},

@@ -19,8 +19,9 @@ The computation, for every segment [a, b) of cu_seqlens and every head h, is
 (FlashInfer "minimax_h3_sm120_varlen_attention_nvfp4" page), with Q/K/V
 quantized per head to E4M3 and both products on FP8 MFMA.  ``fmt="mxfp4"``
 selects the block-scaled FP4 variant (E2M1 operands and probabilities with
-one power-of-two scale per 32 elements; ``q_centre=True`` adds the page's Q
-block-mean centring).
+one power-of-two scale per 32 elements).  ``q_centre=True`` adds the page's Q
+block-mean centring to either format (E4M3: the mean term added back near
+exactly from a precomputed table, for Q with large per-channel offsets).
 """
 from __future__ import annotations
 
@@ -54,8 +55,10 @@ class Plan:
     ``device=None`` uses the current CUDA/HIP device; ``device=-1`` builds a
     host-only plan that can be inspected but not run.  ``segment_scales=True``
     quantizes every segment with its own per-head scales.  ``fmt`` is
-    ``"e4m3"`` (default) or ``"mxfp4"``; ``q_centre`` (mxfp4 only) centres Q
-    by its 128-row block means.  ``causal``: query i of a segment attends to
+    ``"e4m3"`` (default) or ``"mxfp4"``; ``q_centre`` centres Q by its 128-row
+    block means and adds the mean term back (E4M3: head sizes above 64; its
+    workspace holds one 4-byte mean-term entry per (128-query block, key) of
+    every segment and head).  ``causal``: query i of a segment attends to
     the keys j <= i of that segment.  ``head_dim``: 128, or (e4m3 only) any
     multiple of 8 from 8 to 128 (run at the kernel width 64 or 128 with the
     missing channels as zeros).  ``exact_probs`` (e4m3 only): probabilities rounded from the
@@ -149,6 +152,8 @@ class Plan:
         n = shape[0] * shape[1] * shape[2]
         if which == _lib.REGION_SCALES and shape[1] == 1:
             shape = (shape[0], shape[2])          # per-head scales: [3][H]
+        if which == _lib.REGION_QM_TERM:          # uint32 entries (two bf16), as int32
+            return workspace[off: off + 4 * shape[0] * shape[1]].view(torch.int32).view(shape[0], shape[1])
         return workspace[off: off + 4 * n].view(torch.float32).view(shape)
 
     def stats_offset(self) -> int:
@@ -302,8 +307,8 @@ def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: Opt
 
     ``cu_seqlens`` is a host sequence of segment boundaries (None = one segment).
     ``segment_scales`` quantizes every segment with its own per-head scales.
-    ``fmt="mxfp4"`` runs the block-scaled FP4 variant (``q_centre`` adds Q
-    block-mean centring).  ``causal=True`` masks keys after each query.  The
+    ``fmt="mxfp4"`` runs the block-scaled FP4 variant; ``q_centre`` adds Q
+    block-mean centring (either format).  ``causal=True`` masks keys after each query.  The
     head size D (128, or for E4M3 any multiple of 8 up to 128) is taken from
     the inputs' last dimension.  Batched [B, T, heads, D] inputs (views of
     [B*T, heads, D]) are run as B segments of T tokens and returned as
@@ -397,7 +402,7 @@ def _varlen(q, k, v, cu_seqlens, out, cu_seqlens_host, softmax_scale, return_lse
 
 def varlen_attention_fp8(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: torch.Tensor,
                          out: Optional[torch.Tensor] = None, *, cu_seqlens_host: Optional[Sequence[int]] = None,
-                         softmax_scale: Optional[float] = None, return_lse: bool = False):
+                         softmax_scale: Optional[float] = None, return_lse: bool = False, q_centre: bool = False):
     """Non-causal packed-varlen self-attention on E4M3 operands: for every
     segment [a, b) of cu_seqlens and head h, out[a:b, h] = softmax(q[a:b, h]
     k[a:b, h]^T softmax_scale) v[a:b, h], BF16 [tokens, heads, 128].  The
@@ -405,8 +410,10 @@ def varlen_attention_fp8(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_s
     add fp8_fa_sm120 FP8 backend for SM120 GPUs", "Modifications"), with the
     calling convention of the FlashInfer page
     "flashinfer.diffusion_ops.minimax_h3_sm120_varlen_attention_nvfp4";
-    ``return_lse`` adds the natural-log LSE [heads, tokens]."""
-    return _varlen(q, k, v, cu_seqlens, out, cu_seqlens_host, softmax_scale, return_lse, "e4m3", False)
+    ``return_lse`` adds the natural-log LSE [heads, tokens]; ``q_centre``
+    centres Q by its 128-row block means (the page's Q centring) with the mean
+    term added back from a precomputed table."""
+    return _varlen(q, k, v, cu_seqlens, out, cu_seqlens_host, softmax_scale, return_lse, "e4m3", q_centre)
 
 
 def varlen_attention_mxfp4(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: torch.Tensor,

@@ -18,6 +18,7 @@ STATUS_NAMES = {0: "FP8ATTN_OK", 1: "FP8ATTN_EINVAL", 2: "FP8ATTN_EUNSUPPORTED",
 REGION_Q, REGION_K, REGION_V, REGION_SCALES, REGION_MU, REGION_ROWMAP = range(6)
 REGION_Q_BSCALES, REGION_K_BSCALES, REGION_V_BSCALES, REGION_QM_CODES, REGION_QM_SCALES = range(6, 11)
 REGION_STATS = 11
+REGION_QMEAN, REGION_QM_TERM = 12, 13
 PLAN_SEGMENT_SCALES = 1          # FP8ATTN_PLAN_SEGMENT_SCALES
 PLAN_MXFP4 = 2                   # FP8ATTN_PLAN_MXFP4
 PLAN_Q_CENTRE = 4                # FP8ATTN_PLAN_Q_CENTRE

@@ -45,6 +45,9 @@ struct fp8attn_plan_s {
   std::vector<int32_t> group_seg;
   std::vector<int4> items;        // in launch order (XCD-remapped)
   std::vector<int4> combine;      // one per split work item
+  std::vector<int64_t> mt_seg;    // E4M3 Q centring: first mean-term entry of each segment (per head)
+  std::vector<int4> qmt_units;    // E4M3 Q centring: work units of the mean-term kernel
+  int64_t mt_per_head = 0;
   int64_t real_items = 0;
   int64_t npieces = 0;
   WorkspaceLayout ws{};
@@ -56,6 +59,8 @@ struct fp8attn_plan_s {
   int4* d_items = nullptr;
   int4* d_combine = nullptr;
   int32_t* d_rowmap = nullptr;
+  int64_t* d_mt_seg = nullptr;
+  int4* d_qmt_units = nullptr;
 };
 
 namespace {
@@ -101,17 +106,24 @@ WorkspaceLayout make_layout_mx(int64_t rows, int heads, int nseg, int nchunks, i
   return w;
 }
 
-WorkspaceLayout make_layout(int64_t rows, int heads, int nseg, int nscale, int nchunks, int64_t npieces, int D) {
+WorkspaceLayout make_layout(int64_t rows, int heads, int nseg, int nscale, int nchunks, int64_t npieces, int D,
+                            int64_t mt_per_head) {
   WorkspaceLayout w{};
   w.rows = rows;
   w.npieces = npieces;
+  w.mt_per_head = mt_per_head;
   const size_t codes = (size_t)heads * rows * D;
+  const size_t qblocks = (size_t)(rows / kQmBlock);
   size_t off = 0;
   w.q_off = off; off = align_up(off + codes, 256);
   w.k_off = off; off = align_up(off + codes, 256);
   w.v_off = off; off = align_up(off + codes, 256);
   w.scale_off = off; off = align_up(off + sizeof(float) * 3 * (size_t)nscale * heads, 256);
   w.mu_off = off; off = align_up(off + sizeof(float) * (size_t)nseg * heads * D, 256);
+  if (mt_per_head > 0) {   // Q centring: block means and the mean-term table
+    w.qmean_off = off; off = align_up(off + sizeof(float) * (size_t)heads * qblocks * D, 256);
+    w.mt_off = off; off = align_up(off + sizeof(uint32_t) * (size_t)heads * (size_t)mt_per_head, 256);
+  }
   w.part_o_off = off; off = align_up(off + sizeof(float) * (size_t)npieces * kPartRows * D, 256);
   w.part_w_off = off; off = align_up(off + sizeof(float) * (size_t)npieces * kPartRows, 256);
   w.part_lse_off = off; off = align_up(off + sizeof(float) * (size_t)npieces * kPartRows, 256);
@@ -120,6 +132,9 @@ WorkspaceLayout make_layout(int64_t rows, int heads, int nseg, int nscale, int n
   w.stats_off = off;
   w.kstat_off = off; off = align_up(off + sizeof(KStat) * (size_t)nchunks * heads * D, 256);
   w.amax_off = off; off = align_up(off + sizeof(float) * 2 * (size_t)nchunks * heads, 256);
+  if (mt_per_head > 0) {
+    w.qstat_off = off; off = align_up(off + sizeof(KStat) * qblocks * heads * D, 256);
+  }
   w.total = off;
   return w;
 }
@@ -316,8 +331,8 @@ fp8attn_status fp8attn_plan_ex(fp8attn_plan_t* plan_out, int64_t tokens, int32_t
     return fail(FP8ATTN_EINVAL, "FP8ATTN_PLAN_MXFP4 plans take head_dim 128 only");
   if ((flags & FP8ATTN_PLAN_EXACT_PROBS) && (flags & FP8ATTN_PLAN_MXFP4))
     return fail(FP8ATTN_EINVAL, "FP8ATTN_PLAN_EXACT_PROBS applies to E4M3 plans only");
-  if ((flags & FP8ATTN_PLAN_Q_CENTRE) && !(flags & FP8ATTN_PLAN_MXFP4))
-    return fail(FP8ATTN_EINVAL, "FP8ATTN_PLAN_Q_CENTRE needs FP8ATTN_PLAN_MXFP4");
+  if ((flags & FP8ATTN_PLAN_Q_CENTRE) && !(flags & FP8ATTN_PLAN_MXFP4) && head_dim <= 64)
+    return fail(FP8ATTN_EINVAL, "FP8ATTN_PLAN_Q_CENTRE on E4M3 plans takes head_dim above 64");
   if ((flags & FP8ATTN_PLAN_MXFP4) && (flags & FP8ATTN_PLAN_SEGMENT_SCALES))
     return fail(FP8ATTN_EINVAL, "FP8ATTN_PLAN_MXFP4 does not take FP8ATTN_PLAN_SEGMENT_SCALES");
   if (cu == nullptr) return fail(FP8ATTN_EINVAL, "cu_seqlens_host is NULL");
@@ -368,6 +383,24 @@ fp8attn_status fp8attn_plan_ex(fp8attn_plan_t* plan_out, int64_t tokens, int32_t
   }
   for (int g = 0; g < kGuardRows / kPackRows; g++) p->group_seg.push_back(-1);
   row += kGuardRows;
+  if (p->q_centre && !p->mx) {
+    // mean-term table: per head, per segment, (padded rows / 128) blocks x padded rows
+    p->mt_seg.resize(num_segments);
+    int64_t e = 0;
+    for (int s = 0; s < num_segments; s++) {
+      const int64_t lr = (int64_t)(p->segs[s].len + kRowPad - 1) / kRowPad * kRowPad;
+      p->mt_seg[s] = e;
+      const int64_t nblk = lr / kQmBlock;
+      for (int64_t bg = 0; bg < (nblk + kQmUnitBlocks - 1) / kQmUnitBlocks; bg++)
+        for (int64_t k0 = 0; k0 < lr; k0 += kQmUnitKeys) p->qmt_units.push_back(int4{s, (int)bg, (int)k0, 0});
+      e += nblk * lr;
+    }
+    p->mt_per_head = e;
+    if ((double)e * 4.0 * heads > (double)((int64_t)1 << 40) || (int64_t)p->qmt_units.size() > INT32_MAX) {
+      delete p;
+      return fail(FP8ATTN_EUNSUPPORTED, "Q-centring mean-term table above 1 TiB");
+    }
+  }
   // the attention kernel addresses one head's code rows through 32-bit buffer
   // offsets: rows * 128 bytes must fit
   if (row * p->dk > (int64_t)INT32_MAX || (row / kPackRows) * heads > (int64_t)INT32_MAX) {
@@ -387,7 +420,8 @@ fp8attn_status fp8attn_plan_ex(fp8attn_plan_t* plan_out, int64_t tokens, int32_t
     return fail(FP8ATTN_EUNSUPPORTED, "too many split work items");
   }
   p->ws = p->mx ? make_layout_mx(row, heads, num_segments, (int)p->chunks.size(), p->npieces)
-                : make_layout(row, heads, num_segments, p->nscale, (int)p->chunks.size(), p->npieces, p->dk);
+                : make_layout(row, heads, num_segments, p->nscale, (int)p->chunks.size(), p->npieces, p->dk,
+                              p->mt_per_head);
 
   if (device >= 0) {
     DeviceGuard g(device);
@@ -401,7 +435,9 @@ fp8attn_status fp8attn_plan_ex(fp8attn_plan_t* plan_out, int64_t tokens, int32_t
     const size_t b_items = align_up(sizeof(int4) * std::max<size_t>(1, p->items.size()), 256);
     const size_t b_rowmap = align_up(sizeof(int32_t) * p->segs.size(), 256);
     const size_t b_combine = align_up(sizeof(int4) * std::max<size_t>(1, p->combine.size()), 256);
-    const size_t total = b_segs + b_chunks + b_groups + b_items + b_rowmap + b_combine;
+    const size_t b_mtseg = align_up(sizeof(int64_t) * std::max<size_t>(1, p->mt_seg.size()), 256);
+    const size_t b_units = align_up(sizeof(int4) * std::max<size_t>(1, p->qmt_units.size()), 256);
+    const size_t total = b_segs + b_chunks + b_groups + b_items + b_rowmap + b_combine + b_mtseg + b_units;
     std::vector<uint8_t> host(total, 0);
     size_t off = 0;
     std::memcpy(host.data() + off, p->segs.data(), sizeof(SegInfo) * p->segs.size());
@@ -418,6 +454,10 @@ fp8attn_status fp8attn_plan_ex(fp8attn_plan_t* plan_out, int64_t tokens, int32_t
     }
     off += b_rowmap;
     if (!p->combine.empty()) std::memcpy(host.data() + off, p->combine.data(), sizeof(int4) * p->combine.size());
+    off += b_combine;
+    if (!p->mt_seg.empty()) std::memcpy(host.data() + off, p->mt_seg.data(), sizeof(int64_t) * p->mt_seg.size());
+    off += b_mtseg;
+    if (!p->qmt_units.empty()) std::memcpy(host.data() + off, p->qmt_units.data(), sizeof(int4) * p->qmt_units.size());
     hipError_t e = hipMalloc(&p->dev, total);
     if (e != hipSuccess) {
       delete p;
@@ -436,6 +476,9 @@ fp8attn_status fp8attn_plan_ex(fp8attn_plan_t* plan_out, int64_t tokens, int32_t
     p->d_items = reinterpret_cast<int4*>(d + b_segs + b_chunks + b_groups);
     p->d_rowmap = reinterpret_cast<int32_t*>(d + b_segs + b_chunks + b_groups + b_items);
     p->d_combine = reinterpret_cast<int4*>(d + b_segs + b_chunks + b_groups + b_items + b_rowmap);
+    p->d_mt_seg = reinterpret_cast<int64_t*>(d + b_segs + b_chunks + b_groups + b_items + b_rowmap + b_combine);
+    p->d_qmt_units =
+        reinterpret_cast<int4*>(d + b_segs + b_chunks + b_groups + b_items + b_rowmap + b_combine + b_mtseg);
   }
   *plan_out = p;
   return FP8ATTN_OK;
@@ -453,7 +496,10 @@ size_t static_stats_bytes(const fp8attn_plan_s* p) {
   const size_t nch = p->chunks.size();
   const size_t kst = align_up(sizeof(KStat) * nch * (size_t)p->heads * (size_t)p->dk, 256);
   const size_t amx = p->mx ? 0 : align_up(sizeof(float) * 2 * nch * (size_t)p->heads, 256);
-  return kst + amx;
+  const size_t qst = p->mt_per_head > 0
+                         ? align_up(sizeof(KStat) * (size_t)(p->ws.rows / kQmBlock) * (size_t)p->heads * (size_t)p->dk, 256)
+                         : 0;
+  return kst + amx + qst;
 }
 
 // fp8attn_quantize and fp8attn_quantize_noalloc: the statistics go to the
@@ -483,13 +529,16 @@ fp8attn_status quantize_impl(fp8attn_plan_t p, const void* q, const void* k, con
   DeviceGuard g(p->device);
   if (!g.ok) return fail(FP8ATTN_EHIP, "cannot select device");
   uint8_t* ws = static_cast<uint8_t*>(workspace);
-  uint8_t* stats = ws + p->ws.kstat_off;                      // kstat, then amax (E4M3 plans)
+  uint8_t* stats = ws + p->ws.kstat_off;                      // kstat, then amax (E4M3 plans), then qstat
   size_t amax_rel = p->mx ? 0 : p->ws.amax_off - p->ws.kstat_off;
+  size_t qstat_rel = p->mt_per_head > 0 ? p->ws.qstat_off - p->ws.kstat_off : 0;
   if (noalloc) {
     const hipError_t e = static_stats_buffer(p->device, &stats);
     if (e != hipSuccess)
       return fail(FP8ATTN_EHIP, std::string("static statistics buffer: ") + hipGetErrorString(e));
     if (!p->mx) amax_rel = align_up(sizeof(KStat) * p->chunks.size() * (size_t)p->heads * (size_t)p->dk, 256);
+    if (p->mt_per_head > 0)
+      qstat_rel = amax_rel + align_up(sizeof(float) * 2 * p->chunks.size() * (size_t)p->heads, 256);
   }
   QuantizeArgs a{};
   a.x[0] = static_cast<const uint16_t*>(q);
@@ -521,6 +570,16 @@ fp8attn_status quantize_impl(fp8attn_plan_t p, const void* q, const void* k, con
   a.q_centre = p->q_centre;
   a.head_dim = p->dk;
   a.d_real = p->head_dim;
+  a.exact_probs = p->exact_probs;
+  if (p->mt_per_head > 0) {
+    a.qstat = reinterpret_cast<KStat*>(stats + qstat_rel);
+    a.qmean = reinterpret_cast<float*>(ws + p->ws.qmean_off);
+    a.mt = reinterpret_cast<uint32_t*>(ws + p->ws.mt_off);
+    a.mt_seg = p->d_mt_seg;
+    a.qmt_units = p->d_qmt_units;
+    a.nqmt_units = (int32_t)p->qmt_units.size();
+    a.mt_per_head = p->mt_per_head;
+  }
   if (p->mx) {
     a.bscale[0] = ws + p->ws.qs_off;
     a.bscale[1] = ws + p->ws.ks_off;
@@ -630,6 +689,13 @@ fp8attn_status fp8attn_forward(fp8attn_plan_t p, void* workspace, size_t workspa
     a.bm = p->bm;
     a.exact_probs = p->exact_probs;
     a.softmax_scale = p->scale;
+    if (p->mt_per_head > 0) {
+      a.q_centre = 1;
+      a.qmean = reinterpret_cast<const float*>(ws + p->ws.qmean_off);
+      a.mt = reinterpret_cast<const uint32_t*>(ws + p->ws.mt_off);
+      a.mt_seg = p->d_mt_seg;
+      a.mt_per_head = p->mt_per_head;
+    }
     e = launch_attention(a, static_cast<hipStream_t>(stream));
   }
   if (e != hipSuccess) return fail(FP8ATTN_EHIP, std::string("attention launch failed: ") + hipGetErrorString(e));
@@ -693,6 +759,12 @@ fp8attn_status fp8attn_workspace_region(fp8attn_plan_t p, const void* workspace,
     case FP8ATTN_REGION_V_CODES: *ptr_out = ws + p->ws.v_off; dims_out[0] = H; dims_out[1] = D; dims_out[2] = R; break;
     case FP8ATTN_REGION_SCALES: *ptr_out = ws + p->ws.scale_off; dims_out[0] = 3; dims_out[1] = p->nscale; dims_out[2] = H; break;
     case FP8ATTN_REGION_MU: *ptr_out = ws + p->ws.mu_off; dims_out[0] = p->nseg; dims_out[1] = H; dims_out[2] = D; break;
+    case FP8ATTN_REGION_QMEAN:
+      if (p->mt_per_head == 0) return fail(FP8ATTN_EINVAL, "region needs an E4M3 plan with FP8ATTN_PLAN_Q_CENTRE");
+      *ptr_out = ws + p->ws.qmean_off; dims_out[0] = H; dims_out[1] = R / kQmBlock; dims_out[2] = D; break;
+    case FP8ATTN_REGION_QM_TERM:
+      if (p->mt_per_head == 0) return fail(FP8ATTN_EINVAL, "region needs an E4M3 plan with FP8ATTN_PLAN_Q_CENTRE");
+      *ptr_out = ws + p->ws.mt_off; dims_out[0] = H; dims_out[1] = p->mt_per_head; dims_out[2] = 4; break;
     default: return fail(FP8ATTN_EINVAL, "unknown region");
   }
   return FP8ATTN_OK;

@@ -81,6 +81,8 @@ namespace fp8attn {
 namespace {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef __bf16 v8bf16 __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
@@ -116,6 +118,27 @@ __device__ __forceinline__ v16f mfma_fp8_scaled(const v8i& a, const v8i& b, cons
 }
 __device__ __forceinline__ v4f mfma16_fp8(const v8i& a, const v8i& b, const v4f& c) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+// Q centring: the initial accumulator of a 32-key block's score products, one
+// 32x32x16 bf16 product.  A (lanes l and l+32: key l%32) = {mt_hi, mt_lo, 1, 1,
+// 0 ...}, B (lanes 0-31: query l; lanes 32-63 zero) = {1, 1, nb_hi, nb_lo,
+// 0 ...}, so entry (key, query) = mean term of the key + offset of the query.
+constexpr uint32_t kBf16Ones = 0x3F803F80u;   // two bf16 1.0
+__device__ __forceinline__ v16f mt_init(uint32_t mt, const v4i& bq) {
+  const v4i av = v4i{(int)mt, (int)kBf16Ones, 0, 0};
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf16, av), __builtin_bit_cast(v8bf16, bq),
+                                                 v16f{}, 0, 0, 0);
+}
+// x as a bf16 pair (high half bf16(x), low half bf16 of the rest) and the
+// float sum of the two halves, the value the pair stands for.
+__device__ __forceinline__ uint32_t bf16_pair(float x, float& value) {
+  const uint32_t u = __float_as_uint(x);
+  const uint32_t hi = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+  const float rest = x - __uint_as_float(hi << 16);
+  const uint32_t v = __float_as_uint(rest);
+  const uint32_t lo = (v + 0x7fffu + ((v >> 16) & 1u)) >> 16;
+  value = __uint_as_float(hi << 16) + __uint_as_float(lo << 16);
+  return hi | (lo << 16);
 }
 
 // sum of x over lanes l and l^32.  v_permlane32_swap on (x, x) leaves
@@ -175,6 +198,10 @@ __device__ __forceinline__ void barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n
 __device__ __forceinline__ void lds_dma(__amdgpu_buffer_rsrc_t rsrc, uint32_t lds, int voff, int soff) {
   asm volatile("buffer_load_dwordx4 %1, %2, %3 offen lds" : : "{m0}"(lds), "v"(voff), "s"(rsrc), "s"(soff));
 }
+// The same with 4 bytes per lane (LDS at lds + 4 * lane).
+__device__ __forceinline__ void lds_dma4(__amdgpu_buffer_rsrc_t rsrc, uint32_t lds, int voff, int soff) {
+  asm volatile("buffer_load_dword %1, %2, %3 offen lds" : : "{m0}"(lds), "v"(voff), "s"(rsrc), "s"(soff));
+}
 
 // Scheduling fence: the compiler keeps every instruction on its side.
 __device__ __forceinline__ void fence() { __builtin_amdgcn_sched_barrier(0); }
@@ -204,7 +231,7 @@ __device__ __forceinline__ void tail_iters(F& iter, int& t, int nkt) {
 
 // BM queries per work item (256: one 8-wave workgroup per CU; 128: two 4-wave
 // workgroups per CU), D channels per head.
-template <bool LSE, bool CAUSAL, int D, int BM, bool EXACT>
+template <bool LSE, bool CAUSAL, int D, int BM, bool EXACT, bool QC>
 __global__ __launch_bounds__(2 * BM, 256 / BM) void k_attn(AttentionArgs a) {
   constexpr int kWavesWG = BM / 32;              // waves per workgroup, 32 queries each
   // frame constants in the units the score products deliver (x, or y = 8 x + kYBias)
@@ -222,7 +249,12 @@ __global__ __launch_bounds__(2 * BM, 256 / BM) void k_attn(AttentionArgs a) {
   constexpr bool kSplitLoads = kLoads < kWavesWG;
   constexpr int kLoadsPerTile = kSplitLoads ? 1 : kLoads / kWavesWG;
   static_assert(D == 128 || (D == 64 && kWavesWG == 8), "head_dim 128, or 64 with 256-query items");
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * kVRing];
+  static_assert(!QC || D == 128, "Q centring at 128 channels");
+  // Q centring: a ring of mean-term tiles after the V ring, one 512-byte slot
+  // per key tile (the 64 keys of each of the item's 128-query blocks)
+  constexpr int kMtSlot = 512;
+  constexpr int kMtRing = QC ? kSlots * kMtSlot : 0;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * kVRing + kMtRing];
 
   const int4 it = a.items[blockIdx.x];
   if (it.x < 0) return;
@@ -306,7 +338,7 @@ __global__ __launch_bounds__(2 * BM, 256 / BM) void k_attn(AttentionArgs a) {
   // Tile indices past the segment's last tile are clamped: such loads only
   // refill a free slot with valid data, and every iteration issues the same
   // number of loads, which the vmcnt waits rely on.
-  auto load_k = [&](int kt, int slot) __attribute__((always_inline)) {
+  auto load_k_tile = [&](int kt, int slot) __attribute__((always_inline)) {
     kt = kt < nkt ? kt : nkt - 1;
     if (k_wave) {
 #pragma unroll
@@ -319,6 +351,39 @@ __global__ __launch_bounds__(2 * BM, 256 / BM) void k_attn(AttentionArgs a) {
 #pragma unroll
       for (int u = 0; u < kLoadsPerTile; u++) lds_dma(vrs, lds0 + kVRing + slot * kTile + u * 1024, vsrc[u], kt * kBN);
     }
+  };
+  // Q centring: this wave's 128-query block (bw) and its row of the mean-term
+  // table (the segment's padded rows lr long, from the range's first key);
+  // the first wave of each block loads the block's 64 entries of every key
+  // tile with the K tile, into slot bw of the tile's mean-term ring slot.  A
+  // block past the segment's last one (the upper half of a 256-query item
+  // whose queries end in its lower half) takes the last block's row: its
+  // waves' rows are never stored.
+  const int bw = wave >> 2;
+  const bool mt_wave = QC && (wave & 3) == 0;
+  const int lr = (L + kRowPad - 1) / kRowPad * kRowPad;
+  const int nqb_seg = lr / kQmBlock;                         // the segment's blocks
+  const int qblk = min(q0 / kQmBlock + bw, nqb_seg - 1);     // block of this wave within the segment
+  // the table is tile-major: the chunk of key tile kt and block b is entry
+  // (kt * nqb_seg + b) * 64 of the segment's part
+  const uint32_t* mrow = nullptr;
+  int mbytes = 0;
+  if constexpr (QC) {
+    const int64_t e0 = ((int64_t)kt0 * nqb_seg + qblk) * kBN;
+    mrow = a.mt + (size_t)h * a.mt_per_head + a.mt_seg[it.x] + e0;
+    mbytes = (int)(((int64_t)nqb_seg * lr - e0) * 4);
+  }
+  const __amdgpu_buffer_rsrc_t mtrs = __builtin_amdgcn_make_buffer_rsrc((void*)mrow, (short)0, mbytes, kBufferFlags);
+  const uint32_t lds_mt = (uint32_t)(uintptr_t)(lds_ptr_t)smem + 2 * kVRing + 256 * bw;
+  auto load_mt = [&](int kt, int slot) __attribute__((always_inline)) {
+    if constexpr (QC) {
+      kt = kt < nkt ? kt : nkt - 1;
+      if (mt_wave) lds_dma4(mtrs, lds_mt + slot * kMtSlot, 4 * lane, kt * nqb_seg * kBN * 4);
+    }
+  };
+  auto load_k = [&](int kt, int slot) __attribute__((always_inline)) {
+    load_k_tile(kt, slot);
+    load_mt(kt, slot);
   };
 
   // q_hat . mu per query, for the natural-log LSE of the uncentred scores:
@@ -340,6 +405,16 @@ __global__ __launch_bounds__(2 * BM, 256 / BM) void k_attn(AttentionArgs a) {
       }
     qmu = sum_pair32(dot);
   }
+  // Q centring: the block mean's part of the same correction, qm . mu
+  float qmm = 0.f;
+  if (LSE && QC) {
+    const float* mu = a.mu + ((size_t)it.x * a.heads + h) * D;
+    const float* qmr = a.qmean + ((size_t)h * (a.rows / kQmBlock) + si.row0 / kQmBlock + qblk) * D;
+    float dot = 0.f;
+#pragma unroll
+    for (int j = 0; j < 64; j++) dot += qmr[64 * lg + j] * mu[64 * lg + j];
+    qmm = sum_pair32(dot);
+  }
 
   // Row-sum selector for the 16x16x128 product: E4M3 1.0 in every byte of
   // lanes 0 and 32 (row 0: lanes j and j+32 of P, query j) and lanes 17 and
@@ -356,6 +431,21 @@ __global__ __launch_bounds__(2 * BM, 256 / BM) void k_attn(AttentionArgs a) {
 #pragma unroll
   for (int db = 0; db < NDB; db++) O[db] = v16f{};
   v16f NB = {};    // nb in every register: the initial accumulator of the score products
+  // Q centring: nb enters through the mean-term product instead (B operand
+  // {1, 1, nb_hi, nb_lo, 0 ...} in lanes 0-31, zero in lanes 32-63)
+  v4i bq = v4i{lg ? 0 : (int)kBf16Ones, 0, 0, 0};
+  auto set_nb = [&](float target) __attribute__((always_inline)) {
+    // nb becomes the value of the bf16 pair nearest target; returns the change
+    float value;
+    const uint32_t pair = bf16_pair(target, value);
+    bq[1] = lg ? 0 : (int)pair;
+    const float d = value - nb;
+    nb = value;
+    return d;
+  };
+  auto mt_read = [&](int ks, int kb) __attribute__((always_inline)) {
+    return *reinterpret_cast<const uint32_t*>(smem + 2 * kVRing + ks * kMtSlot + 256 * bw + 4 * (32 * kb + lq));
+  };
   v16f S[2];       // exp2 arguments x of the current tile [32-key block], refilled with the next tile's
   v8i P;           // packed probabilities of the previous tile, then of the current one
 
@@ -367,7 +457,12 @@ __global__ __launch_bounds__(2 * BM, 256 / BM) void k_attn(AttentionArgs a) {
       const v8i k0 = lds_read32(kb_base + kb * 32 * D, koff[0][0], koff[0][1]);
       if constexpr (NH == 2) {
         const v8i k1 = lds_read32(kb_base + kb * 32 * D, koff[1][0], koff[1][1]);
-        S[kb] = mfma_fp8_scaled(k1, qf[1], mfma_fp8_scaled(k0, qf[0], NB, c_e8m0), c_e8m0);
+        v16f init;
+        if constexpr (QC)
+          init = mt_init(mt_read(ks, kb), bq);
+        else
+          init = NB;
+        S[kb] = mfma_fp8_scaled(k1, qf[1], mfma_fp8_scaled(k0, qf[0], init, c_e8m0), c_e8m0);
       } else {
         S[kb] = mfma_fp8_scaled(k0, qf[0], NB, c_e8m0);
       }
@@ -398,11 +493,19 @@ __global__ __launch_bounds__(2 * BM, 256 / BM) void k_attn(AttentionArgs a) {
     auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(tl), __float_as_uint(tl), false, false);
     const float xm = __builtin_fmaxf(__uint_as_float(pr[0]), __uint_as_float(pr[1]));
     const bool over = xm > kMax;
-    const float shift = over ? kRef - xm : 0.f;
-    nb += shift;
+    float shift = over ? kRef - xm : 0.f;
+    if constexpr (QC) {
+      if (over) shift = set_nb(nb + shift);   // the change the rounded pair makes
+    } else {
+      nb += shift;
+    }
     pshift = shift;
 #pragma unroll
-    for (int i = 0; i < 16; i++) { S[0][i] += shift; S[1][i] += shift; NB[i] += shift; }
+    for (int i = 0; i < 16; i++) {
+      S[0][i] += shift;
+      S[1][i] += shift;
+      if constexpr (!QC) NB[i] += shift;
+    }
   };
   // FIRST: set the reference from this tile.  Otherwise vote, and unless
   // VOTE_ONLY apply a shift at once; VOTE_ONLY returns the lane maximum for
@@ -451,10 +554,17 @@ __global__ __launch_bounds__(2 * BM, 256 / BM) void k_attn(AttentionArgs a) {
     if (FIRST) {
       auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(tl), __float_as_uint(tl), false, false);
       const float tm = __builtin_fmaxf(__uint_as_float(pr[0]), __uint_as_float(pr[1]));
-      const float shift = kRef - tm;
-      nb = shift;
+      float shift = kRef - tm;
+      if constexpr (QC)
+        shift = set_nb(shift);   // nb was 0: the pair's value
+      else
+        nb = shift;
 #pragma unroll
-      for (int i = 0; i < 16; i++) { S[0][i] += shift; S[1][i] += shift; NB[i] = shift; }
+      for (int i = 0; i < 16; i++) {
+        S[0][i] += shift;
+        S[1][i] += shift;
+        if constexpr (!QC) NB[i] = shift;
+      }
     } else {
       // move the reference only if the tile's largest p would exceed 448: one
       // vote over the wave; the row maxima and shifts only on the rare path
@@ -535,6 +645,8 @@ __global__ __launch_bounds__(2 * BM, 256 / BM) void k_attn(AttentionArgs a) {
   // loads only the K waves issued K loads, and only they need to wait)
   if constexpr (kSplitLoads) {
     if (k_wave) wait_vmcnt<kBarEvery * kLoadsPerTile>();
+  } else if (mt_wave) {
+    wait_vmcnt<kBarEvery * (2 * kLoadsPerTile + 1)>();   // its mean-term loads follow each K load
   } else {
     wait_vmcnt<2 * kBarEvery * kLoadsPerTile>();
   }
@@ -585,7 +697,56 @@ __global__ __launch_bounds__(2 * BM, 256 / BM) void k_attn(AttentionArgs a) {
     const uint8_t* kb = smem + ((PH + 1) % kSlots) * kTile;          // K(t+1)
     const int kbase = t * kBN;
     v8i Pn;
-    if constexpr (NH == 2) {
+    if constexpr (QC) {
+      // Q centring: as below, with the two mean-term products (the initial
+      // accumulators of the score chains, nb included) ahead of the chains
+      v8i kf[2][2];
+      const uint32_t mtv0 = mt_read((PH + 1) % kSlots, 0);
+      const uint32_t mtv1 = mt_read((PH + 1) % kSlots, 1);
+      kf[0][0] = lds_read32(kb, koff[0][0], koff[0][1]);
+      kf[1][0] = lds_read32(kb + 4096, koff[0][0], koff[0][1]);
+      fence();
+      O[0] = mfma_fp8(vf[0], P, O[0]);
+      kf[0][1] = lds_read32(kb, koff[1][0], koff[1][1]);
+      if (CAUSAL && t >= tdiag) mask_causal(t);
+      if (TAIL && ragged && t == nkt - 1) mask_tail(t);
+      const float tlv = rowmax_update(std::false_type{}, std::integral_constant<bool, !EXACT>{});
+      fence();
+      O[1] = mfma_fp8(vf[1], P, O[1]);
+      kf[1][1] = lds_read32(kb + 4096, koff[1][0], koff[1][1]);
+      if constexpr (!EXACT)
+        if (__builtin_expect(pending, 0)) apply_shift(tlv);
+      Pn[0] = probs4(0, 0, kbase);
+      fence();
+      O[2] = mfma_fp8(vf[2], P, O[2]);
+      Pn[1] = probs4(0, 1, kbase);
+      fence();
+      O[3] = mfma_fp8(vf[3], P, O[3]);
+      Pn[2] = probs4(0, 2, kbase);
+      fence();
+      lacc = mfma16_fp8(sel, P, lacc);
+      vf[0] = lds_read32(vn + 0 * 2048, voff[0], voff[1]);
+      vf[1] = lds_read32(vn + 1 * 2048, voff[0], voff[1]);
+      Pn[3] = probs4(0, 3, kbase);
+      fence();
+      const v16f m0 = mt_init(mtv0, bq);
+      Pn[4] = probs4(1, 0, kbase);
+      fence();
+      const v16f m1 = mt_init(mtv1, bq);
+      Pn[5] = probs4(1, 1, kbase);
+      fence();
+      const v16f s0 = mfma_fp8_scaled(kf[0][0], qf[0], m0, c_e8m0);
+      Pn[6] = probs4(1, 2, kbase);
+      fence();
+      const v16f s1 = mfma_fp8_scaled(kf[1][0], qf[0], m1, c_e8m0);
+      vf[2] = lds_read32(vn + 2 * 2048, voff[0], voff[1]);
+      vf[3] = lds_read32(vn + 3 * 2048, voff[0], voff[1]);
+      Pn[7] = probs4(1, 3, kbase);
+      fence();
+      S[0] = mfma_fp8_scaled(kf[0][1], qf[1], s0, c_e8m0);
+      fence();
+      S[1] = mfma_fp8_scaled(kf[1][1], qf[1], s1, c_e8m0);
+    } else if constexpr (NH == 2) {
       v8i kf[2][2];
       kf[0][0] = lds_read32(kb, koff[0][0], koff[0][1]);
       kf[1][0] = lds_read32(kb + 4096, koff[0][0], koff[0][1]);
@@ -752,7 +913,7 @@ __global__ __launch_bounds__(2 * BM, 256 / BM) void k_attn(AttentionArgs a) {
     // masked, so they added nothing), back in the frame of the uncentred scores
     if (lg == 0 && qrow < L) {
       const float lse2 = __log2f(lt) - nbx;
-      const float v = lse2 * kLn2 + a.softmax_scale * s_q * qmu;
+      const float v = QC ? lse2 * kLn2 + a.softmax_scale * (s_q * qmu + qmm) : lse2 * kLn2 + a.softmax_scale * s_q * qmu;
       if (slot >= 0)
         a.part_lse[slot * kPartRows + 32 * wave + lq] = v;
       else
@@ -852,7 +1013,7 @@ hipError_t launch_combine(const CombineArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <int D, int BM, bool EXACT>
+template <int D, int BM, bool EXACT, bool QC>
 void launch_attention_d(const AttentionArgs& a, hipStream_t stream) {
   const dim3 g(a.nitems), b(2 * BM);
   if (a.causal) {
@@ -860,30 +1021,35 @@ void launch_attention_d(const AttentionArgs& a, hipStream_t stream) {
     // for small non-causal work), so no 128-query causal kernel is built
     if constexpr (BM == 256) {
       if (a.lse != nullptr)
-        hipLaunchKernelGGL((k_attn<true, true, D, BM, EXACT>), g, b, 0, stream, a);
+        hipLaunchKernelGGL((k_attn<true, true, D, BM, EXACT, QC>), g, b, 0, stream, a);
       else
-        hipLaunchKernelGGL((k_attn<false, true, D, BM, EXACT>), g, b, 0, stream, a);
+        hipLaunchKernelGGL((k_attn<false, true, D, BM, EXACT, QC>), g, b, 0, stream, a);
     }
   } else if (a.lse != nullptr) {
-    hipLaunchKernelGGL((k_attn<true, false, D, BM, EXACT>), g, b, 0, stream, a);
+    hipLaunchKernelGGL((k_attn<true, false, D, BM, EXACT, QC>), g, b, 0, stream, a);
   } else {
-    hipLaunchKernelGGL((k_attn<false, false, D, BM, EXACT>), g, b, 0, stream, a);
+    hipLaunchKernelGGL((k_attn<false, false, D, BM, EXACT, QC>), g, b, 0, stream, a);
   }
 }
 
 template <bool EXACT>
 void launch_attention_e(const AttentionArgs& a, hipStream_t stream) {
   if (a.head_dim == 64)
-    launch_attention_d<64, 256, EXACT>(a, stream);      // 64 channels: 256-query items only
+    launch_attention_d<64, 256, EXACT, false>(a, stream);      // 64 channels: 256-query items only
+  else if (a.q_centre && a.bm == 128)
+    launch_attention_d<kHeadDim, 128, EXACT, true>(a, stream);
+  else if (a.q_centre)
+    launch_attention_d<kHeadDim, 256, EXACT, true>(a, stream);
   else if (a.bm == 128)
-    launch_attention_d<kHeadDim, 128, EXACT>(a, stream);
+    launch_attention_d<kHeadDim, 128, EXACT, false>(a, stream);
   else
-    launch_attention_d<kHeadDim, 256, EXACT>(a, stream);
+    launch_attention_d<kHeadDim, 256, EXACT, false>(a, stream);
 }
 
 hipError_t launch_attention(const AttentionArgs& a, hipStream_t stream) {
   if (a.nitems == 0) return hipSuccess;
   if (a.causal && a.bm != 256) return hipErrorInvalidValue;   // see launch_attention_d
+  if (a.q_centre && a.head_dim != kHeadDim) return hipErrorInvalidValue;   // Q centring at 128 channels
   if (a.exact_probs)
     launch_attention_e<true>(a, stream);
   else

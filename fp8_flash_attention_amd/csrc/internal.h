@@ -62,6 +62,20 @@ constexpr int kMxTileScales = 256;         // scale bytes of one K (or V^T) tile
 constexpr int kMxBM = 128;                 // queries per FP4 work item (4 waves)
 constexpr int kMxWgPerCu = 2;              // FP4 attention workgroups resident per CU
 
+// E4M3 plans with Q centring (FP8ATTN_PLAN_Q_CENTRE): Q rows are centred by
+// the mean of their 128-row block (blocks of a segment from its start; with
+// segments padded to kRowPad = 128 rows, block g holds workspace rows
+// [128 g, 128 g + 128)).  The mean term qm . k of every (block, key) pair of a
+// segment is precomputed in the frame of the score products and stored as a
+// bf16 pair (high part, then the rounding of the rest) per entry: for head h,
+// segment s (Lr = its padded rows, nb = Lr / 128 blocks), block b of s and key
+// j < Lr, entry h * mt_per_head + mt_seg[s] + ((j / 64) * nb + b) * 64 + j % 64
+// of a uint32 table (tile-major: the 64-key chunks of all blocks of one key
+// tile are adjacent).
+constexpr int kQmBlock = 128;
+constexpr int kQmUnitKeys = 1024;            // keys per workgroup of the mean-term kernel
+constexpr int kQmUnitBlocks = 32;            // Q blocks per workgroup of the mean-term kernel
+
 struct WorkspaceLayout {
   int64_t rows;        // workspace rows (all segments padded + guard)
   int64_t npieces;     // partial slots of split work items
@@ -74,6 +88,10 @@ struct WorkspaceLayout {
   size_t part_w_off;   // float [npieces][kPartRows]: log2 weight of each partial row
   size_t part_lse_off; // float [npieces][kPartRows]: natural-log LSE of each partial row
   size_t stats_off;    // start of the statistics (kstat, amax), the last regions
+  // E4M3 plans with Q centring: block means float [H][rows/128][D], the mean-term
+  // table uint32 [H][mt_per_head], and (statistics) Q block sums KStat [rows/128][H][D]
+  size_t qmean_off, mt_off, qstat_off;
+  int64_t mt_per_head;
   size_t total;
 };
 
@@ -106,6 +124,15 @@ struct QuantizeArgs {
   uint8_t* bscale[3];        // Q, K, V^T block scales (WorkspaceLayout)
   uint8_t* qm_codes;
   uint8_t* qm_scales;
+  // E4M3 plans with q_centre: Q block statistics and means, the mean-term table
+  KStat* qstat;              // [rows/128][H][D]
+  float* qmean;              // [H][rows/128][D]
+  uint32_t* mt;              // [H][mt_per_head]
+  const int64_t* mt_seg;     // [nseg]: first entry of each segment's part of a head's table
+  const int4* qmt_units;     // work of the mean-term kernel: {segment, block group, first key, 0}
+  int32_t nqmt_units;
+  int32_t exact_probs;       // frame of the mean term: x (1) or y = 8 x (0)
+  int64_t mt_per_head;
 };
 
 struct AttentionArgs {
@@ -132,7 +159,12 @@ struct AttentionArgs {
   int32_t d_real;            // channels written to out (<= D)
   int32_t bm;                // queries per work item: 256, or 128 (D = 128 only)
   int32_t exact_probs;       // 1: p = E4M3(exp2(x)); 0: the log-linear code of 2^x
+  int32_t q_centre;          // 1: Q centred by its 128-row block mean, mean term from mt
   float softmax_scale;
+  const float* qmean;        // q_centre: [H][rows/128][D]
+  const uint32_t* mt;        // q_centre: [H][mt_per_head]
+  const int64_t* mt_seg;     // q_centre: [nseg]
+  int64_t mt_per_head;
 };
 
 struct CombineArgs {

@@ -84,6 +84,30 @@ __device__ __forceinline__ uint32_t cvt4(float a, float b, float c, float d) {
 // 8*(t%TPH) .. +8 over the chunk's tokens in ascending order (TPH = D/8
 // threads per head row, HPB = 256/TPH heads per block).
 // ---------------------------------------------------------------------------
+// Fixed-order float64 sum, minimum and maximum of 8 channels over tokens
+// [tok0 + j0, tok0 + j1), in ascending token order, written to out[0..7].
+__device__ __forceinline__ void stat_rows(const uint16_t* base, int64_t ts, int tok0, int j0, int j1, bool live,
+                                          KStat* out) {
+  double sum[8];
+  float mn[8], mx[8];
+#pragma unroll
+  for (int i = 0; i < 8; i++) { sum[i] = 0.0; mn[i] = __builtin_inff(); mx[i] = -__builtin_inff(); }
+#pragma unroll 16
+  for (int j = j0; j < j1; j++) {   // unrolled: 16 loads in flight, sums still in token order
+    const uint4 v = load8(base + (int64_t)(tok0 + j) * ts, live);
+    float f[8];
+    unpack8(v, f);
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+      sum[i] = sum[i] + (double)f[i];
+      mn[i] = fminf(mn[i], f[i]);
+      mx[i] = fmaxf(mx[i], f[i]);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 8; i++) out[i] = KStat{sum[i], mn[i], mx[i]};
+}
+
 template <int D>
 __global__ __launch_bounds__(256) void k_stats(QuantizeArgs a) {
   constexpr int TPH = D / 8;
@@ -101,25 +125,18 @@ __global__ __launch_bounds__(256) void k_stats(QuantizeArgs a) {
 
   if (tensor == 1) {
     if (!active) return;
-    double sum[8];
-    float mn[8], mx[8];
-#pragma unroll
-    for (int i = 0; i < 8; i++) { sum[i] = 0.0; mn[i] = __builtin_inff(); mx[i] = -__builtin_inff(); }
-#pragma unroll 16
-    for (int j = 0; j < ch.ntok; j++) {   // unrolled: 16 loads in flight, sums still in token order
-      const uint4 v = load8(base + (int64_t)(ch.tok0 + j) * ts, live);
-      float f[8];
-      unpack8(v, f);
-#pragma unroll
-      for (int i = 0; i < 8; i++) {
-        sum[i] = sum[i] + (double)f[i];
-        mn[i] = fminf(mn[i], f[i]);
-        mx[i] = fmaxf(mx[i], f[i]);
-      }
-    }
-    KStat* out = a.kstat + ((int64_t)c * a.heads + h) * D + c0;
-#pragma unroll
-    for (int i = 0; i < 8; i++) out[i] = KStat{sum[i], mn[i], mx[i]};
+    stat_rows(base, ts, ch.tok0, 0, ch.ntok, live, a.kstat + ((int64_t)c * a.heads + h) * D + c0);
+    return;
+  }
+  if (tensor == 0 && a.q_centre) {
+    // Q centring: the same statistics per 128-row Q block.  A chunk starts on
+    // a block boundary of its segment and covers one or two blocks.
+    if (!active) return;
+    const SegInfo si = a.segs[ch.seg];
+    const int64_t g0 = (si.row0 + (ch.tok0 - si.start)) / kQmBlock;
+    stat_rows(base, ts, ch.tok0, 0, min(ch.ntok, kQmBlock), live, a.qstat + (g0 * a.heads + h) * D + c0);
+    if (ch.ntok > kQmBlock)
+      stat_rows(base, ts, ch.tok0, kQmBlock, ch.ntok, live, a.qstat + ((g0 + 1) * a.heads + h) * D + c0);
     return;
   }
 
@@ -206,12 +223,14 @@ __global__ __launch_bounds__(D) void k_finalize(QuantizeArgs a) {
     }
     return;
   }
+  const int64_t nqb = a.rows / kQmBlock;   // Q blocks of the workspace (Q centring)
   if (!a.seg_scales) {
     for (int c = d; c < a.nchunks; c += D) {
-      qa = fmaxf(qa, a.amax[(int64_t)c * a.heads + h]);
+      if (!a.q_centre) qa = fmaxf(qa, a.amax[(int64_t)c * a.heads + h]);
       va = fmaxf(va, a.amax[((int64_t)a.nchunks + c) * a.heads + h]);
     }
   }
+  if (a.q_centre) a.qmean[((int64_t)h * nqb + nqb - 1) * D + d] = 0.f;   // the guard rows' block
   float ka = 0.f;
   for (int s = 0; s < a.nseg; s++) {
     const SegInfo si = a.segs[s];
@@ -231,12 +250,30 @@ __global__ __launch_bounds__(D) void k_finalize(QuantizeArgs a) {
       kas = fmaxf(fabsf(mx - mu), fabsf(mn - mu));
     }
     a.mu[((int64_t)s * a.heads + h) * D + d] = mu;
+    // Q centring: qm = fl32(sum64 / n) per block; Q's amax over the segment is
+    // the maximum of |fl32(max - qm)| and |fl32(min - qm)| (exact: rounding is
+    // monotone), this thread's channel first
+    float qcs = 0.f;
+    if (a.q_centre) {
+      const int64_t g0 = si.row0 / kQmBlock;
+      const int nb = (si.len + kQmBlock - 1) / kQmBlock;
+      const KStat* __restrict__ qst = a.qstat + (g0 * a.heads + h) * D + d;
+      float* __restrict__ qmo = a.qmean + ((int64_t)h * nqb + g0) * D + d;
+#pragma unroll 8
+      for (int b = 0; b < nb; b++) {   // loads issued ahead (no aliasing with the stores)
+        const KStat st = qst[(int64_t)b * a.heads * D];
+        const float qm = (float)(st.sum / (double)min(kQmBlock, si.len - b * kQmBlock));
+        qmo[(int64_t)b * D] = qm;
+        qcs = fmaxf(qcs, fmaxf(fabsf(st.mx - qm), fabsf(st.mn - qm)));
+      }
+      if (!a.seg_scales) qa = fmaxf(qa, qcs);
+    }
     if (a.seg_scales) {
       // this segment's own amax of Q, K and V (its chunks' partials), so its
       // scales do not depend on the other segments
-      float qs = 0.f, vs = 0.f;
+      float qs = a.q_centre ? qcs : 0.f, vs = 0.f;
       for (int c = si.chunk0 + d; c < si.chunk0 + nch; c += D) {
-        qs = fmaxf(qs, a.amax[(int64_t)c * a.heads + h]);
+        if (!a.q_centre) qs = fmaxf(qs, a.amax[(int64_t)c * a.heads + h]);
         vs = fmaxf(vs, a.amax[((int64_t)a.nchunks + c) * a.heads + h]);
       }
       qs = block_max<D>(qs, red);
@@ -307,6 +344,11 @@ __global__ __launch_bounds__(256) void k_pack(QuantizeArgs a) {
     const float* m = a.mu + ((int64_t)seg * a.heads + h) * D + c0;
 #pragma unroll
     for (int i = 0; i < 8; i++) mu[i] = m[i];
+  } else if (tensor == 0 && a.q_centre && seg >= 0) {
+    // Q centring: the mean of the group's 128-row block
+    const float* m = a.qmean + ((int64_t)h * (a.rows / kQmBlock) + R / kQmBlock) * D + c0;
+#pragma unroll
+    for (int i = 0; i < 8; i++) mu[i] = m[i];
   } else {
 #pragma unroll
     for (int i = 0; i < 8; i++) mu[i] = 0.f;
@@ -323,7 +365,7 @@ __global__ __launch_bounds__(256) void k_pack(QuantizeArgs a) {
       unpack8(v, f);
       float y[8];
 #pragma unroll
-      for (int j = 0; j < 8; j++) y[j] = (f[j] - mu[j]) / s;   // K: fl32(x - mu); Q, V: mu = 0
+      for (int j = 0; j < 8; j++) y[j] = (f[j] - mu[j]) / s;   // K: fl32(x - mu); Q: fl32(x - qm) or x; V: x
       code.x = cvt4(y[0], y[1], y[2], y[3]);
       code.y = cvt4(y[4], y[5], y[6], y[7]);
     }
@@ -358,6 +400,132 @@ __global__ __launch_bounds__(256) void k_pack(QuantizeArgs a) {
   *reinterpret_cast<uint4*>(dst + 16) = make_uint4(w[4], w[5], w[6], w[7]);
 }
 
+// ---------------------------------------------------------------------------
+// Pass 3 (E4M3 plans with Q centring): the mean-term table.
+//
+// FlashInfer "minimax_h3_sm120_varlen_attention_nvfp4" page, description of
+// the Q operand: Q rows are centred by their 128-row block mean and the term
+// qm . k is added back to the scores.  With E4M3 operands the error of a
+// rounded mean would be as large as the centring saves, so the term is kept
+// near-exact: for every (block, key) pair of a segment, t = f * (qm . khat)
+// with khat the E4M3 codes of the centred K row and f = softmax_scale * s_k *
+// log2(e) (times 8 in the log-linear frame), the frame the attention's score
+// products deliver, stored as a bf16 pair (hi = bf16(t), lo = bf16(t - hi)).
+//
+// The dot products run on the scaled FP8 matrix core: A = qm (32 blocks x 64
+// channels), split into three E4M3 parts with power-of-two scales 2^e,
+// 2^(e-4), 2^(e-8) per block and 64 channels (each part takes the rounding error of the
+// previous one, so the parts carry about 12 significant bits of every mean),
+// B = khat^T (64 channels x 32 keys), all six products of the 128 channels
+// chained into one FP32 accumulator.  grid = (units, H), block = 256: unit
+// {s, bg, k0, 0} covers blocks 32 bg .. +32 of segment s and keys k0 .. +1024;
+// each wave splits the means once and then takes 32 keys a step.
+// ---------------------------------------------------------------------------
+typedef int v8i_q __attribute__((ext_vector_type(8)));
+typedef float v16f_q __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ uint32_t bf16_rne_bits(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+__global__ __launch_bounds__(256) void k_qmterm(QuantizeArgs a) {
+  const int4 u = a.qmt_units[blockIdx.x];
+  const int h = blockIdx.y;
+  const SegInfo si = a.segs[u.x];
+  const int lr = (si.len + kRowPad - 1) / kRowPad * kRowPad;   // the segment's padded rows
+  const int nblk = lr / kQmBlock;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, lq = lane & 31, lg = lane >> 5;
+  const int blk = kQmUnitBlocks * u.y + lq;   // this lane's A row (zero past the segment's blocks)
+  const bool blk_live = blk < nblk;
+  const int64_t nqb = a.rows / kQmBlock;
+  const float* qm = a.qmean + ((int64_t)h * nqb + si.row0 / kQmBlock + (blk_live ? blk : 0)) * kHeadDim;
+
+  // A operands, once per wave: the block means of this lane's row over
+  // channels 64 half + 32 lg .. +32, in three E4M3 parts
+  v8i_q ap[2][3];
+  int sp[2][3];
+#pragma unroll
+  for (int half = 0; half < 2; half++) {
+    const int ch0 = 64 * half + 32 * lg;
+    float r[32];
+    float m = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; j++) {
+      const float4 x = blk_live ? *reinterpret_cast<const float4*>(qm + ch0 + 4 * j) : make_float4(0.f, 0.f, 0.f, 0.f);
+      r[4 * j + 0] = x.x;
+      r[4 * j + 1] = x.y;
+      r[4 * j + 2] = x.z;
+      r[4 * j + 3] = x.w;
+    }
+#pragma unroll
+    for (int j = 0; j < 32; j++) m = fmaxf(m, fabsf(r[j]));
+    // one scale per row and 64-channel half: lanes l and l + 32 hold the same
+    // row, and a per-32-element scale of an FP8 operand is not guaranteed to
+    // cover exactly the 32 bytes one lane holds
+    m = fmaxf(m, __shfl_xor(m, 32));
+    // smallest e with m <= 448 * 2^e, kept where every part's scale is a normal E8M0 value
+    int e = 0;
+    if (m > 0.f) {
+      int ex;
+      const float fr = frexpf(m / 448.0f, &ex);
+      e = fr == 0.5f ? ex - 1 : ex;
+      e = max(-119, min(e, 126));
+    }
+#pragma unroll
+    for (int part = 0; part < 3; part++) {
+      const int ep = e - 4 * part;
+      const float inv = __uint_as_float((uint32_t)(127 - ep) << 23);   // 2^-ep
+      const float sc = __uint_as_float((uint32_t)(127 + ep) << 23);    // 2^ep
+#pragma unroll
+      for (int w = 0; w < 8; w++) {
+        int c = __builtin_amdgcn_cvt_pk_fp8_f32(r[4 * w + 0] * inv, r[4 * w + 1] * inv, 0, false);
+        c = __builtin_amdgcn_cvt_pk_fp8_f32(r[4 * w + 2] * inv, r[4 * w + 3] * inv, c, true);
+        ap[half][part][w] = c;
+        r[4 * w + 0] -= __builtin_amdgcn_cvt_f32_fp8(c, 0) * sc;   // exact: what the next part takes
+        r[4 * w + 1] -= __builtin_amdgcn_cvt_f32_fp8(c, 1) * sc;
+        r[4 * w + 2] -= __builtin_amdgcn_cvt_f32_fp8(c, 2) * sc;
+        r[4 * w + 3] -= __builtin_amdgcn_cvt_f32_fp8(c, 3) * sc;
+      }
+      sp[half][part] = ep + 127;
+    }
+  }
+  const int nset = a.seg_scales ? a.nseg : 1;
+  const int sset = a.seg_scales ? u.x : 0;
+  const float s_k = a.scales[((int64_t)1 * nset + sset) * a.heads + h];
+  const float f = a.softmax_scale * s_k * 1.4426950408889634f * (a.exact_probs ? 1.0f : 8.0f);
+  uint32_t* seg_tab = a.mt + (int64_t)h * a.mt_per_head + a.mt_seg[u.x];
+  const int kend = min(u.z + kQmUnitKeys, lr);
+  // 32 keys per wave and step: B = khat^T, lane l key key0 + l%32
+  for (int key0 = u.z + 32 * wave; key0 < kend; key0 += 128) {
+    const uint8_t* krow = a.codes[1] + ((int64_t)h * a.rows + si.row0 + key0 + lq) * kHeadDim;
+    v16f_q acc = {};
+#pragma unroll
+    for (int half = 0; half < 2; half++) {
+      const int ch0 = 64 * half + 32 * lg;
+      const uint4 b0 = *reinterpret_cast<const uint4*>(krow + ch0);
+      const uint4 b1 = *reinterpret_cast<const uint4*>(krow + ch0 + 16);
+      const v8i_q bk = v8i_q{(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
+#pragma unroll
+      for (int part = 0; part < 3; part++)
+        acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ap[half][part], bk, acc, 0, 0, 0, sp[half][part], 0,
+                                                             127);
+    }
+    // lane l holds key key0 + l%32 and blocks 8*(r/4) + 4*lg + r%4 of the unit;
+    // tile-major table: entry ((key / 64) * nblk + b) * 64 + key % 64 of the segment
+    uint32_t* dst = seg_tab + (int64_t)(key0 / kBN) * nblk * kBN + key0 % kBN + lq;
+#pragma unroll
+    for (int i = 0; i < 16; i++) {
+      const int b = kQmUnitBlocks * u.y + 8 * (i >> 2) + 4 * lg + (i & 3);
+      if (b < nblk) {
+        const float t = f * acc[i];
+        const uint32_t hi = bf16_rne_bits(t);
+        const uint32_t lo = bf16_rne_bits(t - __uint_as_float(hi << 16));
+        dst[b * kBN] = hi | (lo << 16);
+      }
+    }
+  }
+}
 
 // ---------------------------------------------------------------------------
 // Block-scaled FP4 pack (plans made with FP8ATTN_PLAN_MXFP4).
@@ -569,7 +737,16 @@ hipError_t launch_quantize_d(const QuantizeArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL(k_pack_mx, dim3(a.ngroups * a.heads, 1, 3), dim3(256), 0, stream, a);
   else
     hipLaunchKernelGGL(k_pack<D>, dim3(a.ngroups * a.heads, 1, 3), dim3(256), 0, stream, a);
-  return hipGetLastError();
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (!a.mx && a.q_centre && a.nqmt_units > 0) {
+    if constexpr (D == kHeadDim) {
+      hipLaunchKernelGGL(k_qmterm, dim3(a.nqmt_units, a.heads), dim3(256), 0, stream, a);
+      return hipGetLastError();
+    }
+    return hipErrorInvalidValue;   // the planner allows Q centring at 128 channels only
+  }
+  return hipSuccess;
 }
 
 hipError_t launch_quantize(const QuantizeArgs& a, hipStream_t stream) {

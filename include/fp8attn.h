@@ -84,7 +84,20 @@ typedef enum {
      dims_out[0] = their size in bytes.  The pointer's offset into the
      workspace is the size that fp8attn_quantize_noalloc and fp8attn_forward
      need (they do not touch the statistics).                                 */
-  FP8ATTN_REGION_STATS = 11
+  FP8ATTN_REGION_STATS = 11,
+  /* E4M3 plans with FP8ATTN_PLAN_Q_CENTRE.                                    */
+  FP8ATTN_REGION_QMEAN = 12,   /* float [H][rows/128][128]: block means qm of Q; block g
+                                  holds workspace rows [128 g, 128 g + 128) (zero for
+                                  the guard rows)                                     */
+  FP8ATTN_REGION_QM_TERM = 13  /* uint32 [H][dims_out[1]]: the mean-term table, one
+                                  entry per (block, key) of a segment: for segment s
+                                  (Lr = its rows rounded up to 128, E_s = the sum of
+                                  (Lr/128) * Lr over the segments before it), block b
+                                  of s and key j < Lr, entry
+                                  E_s + ((j / 64) * (Lr / 128) + b) * 64 + j % 64
+                                  holds qm . k in the frame of the score products as two
+                                  bf16 (high half: the rounding of the value; low
+                                  half: the rounding of the rest)                     */
 } fp8attn_region;
 
 /*
@@ -153,12 +166,27 @@ fp8attn_status fp8attn_plan(fp8attn_plan_t* plan_out, int64_t tokens, int32_t he
  *   the uncentred scores from the dequantized operands, taken as the log of
  *   the row's normalizer: ln 2 * (log2 sum_j phat_j + (Qhat + QMhat) . mu).  Work items split along
  *   the keys as for E4M3 plans (128-query items, two workgroups per CU).
- * FP8ATTN_PLAN_Q_CENTRE (with FP8ATTN_PLAN_MXFP4 only): Q rows are centred by
- *   the mean of their 128-row block (blocks of a segment from its start; the
- *   mean is a float64 sum over the block's rows in order, divided by the row
- *   count, rounded to float32); the block-mean operand fl32(qm * c), quantized
+ * FP8ATTN_PLAN_Q_CENTRE: Q rows are centred by the mean qm of their 128-row
+ *   block (blocks of a segment from its start; the mean is a float64 sum over
+ *   the block's rows in order, divided by the row count, rounded to float32)
+ *   and the term qm . k is added back to the scores, so the softmax is that
+ *   of the uncentred Q (the FlashInfer page's Q centring).
+ *   With FP8ATTN_PLAN_MXFP4: the block-mean operand fl32(qm * c), quantized
  *   like a Q row, is multiplied with K inside the kernel and added to the
- *   scores, so the softmax is that of the uncentred Q (the page's Q centring).
+ *   scores.
+ *   E4M3 plans (head_dim above 64): Q's amax, scale and codes are those of
+ *   fl32(q - qm); a rounded mean would carry as much error as centring
+ *   removes, so fp8attn_quantize also writes the mean term of every
+ *   (block, key) pair of a segment, f * (qm . khat) with khat the K codes
+ *   and f = softmax_scale * s_k * log2(e) (times 8 unless
+ *   FP8ATTN_PLAN_EXACT_PROBS), as a bf16 pair (FP8ATTN_REGION_QM_TERM; qm is
+ *   carried in three E4M3 parts with power-of-two scales, about 12
+ *   significant bits), and the attention adds it to the scores through one
+ *   small matrix product per 32-key block.  The table takes 4 bytes per
+ *   (block, key) of every segment and head (1.6 GB at 30272 tokens and 56
+ *   heads); plans whose table would pass 1 TiB are rejected with
+ *   FP8ATTN_EUNSUPPORTED.  The LSE (if requested) is that of the uncentred
+ *   scores, ln 2 * (log2 l - offset) + softmax_scale * (s_q qhat + qm) . mu.
  * FP8ATTN_PLAN_CAUSAL: query i of a segment attends only to the
  *   keys j <= i of the same segment, positions counted from the segment start
  *   (the pages send causal attention to another backend; this is the plain
@@ -183,7 +211,7 @@ fp8attn_status fp8attn_plan(fp8attn_plan_t* plan_out, int64_t tokens, int32_t he
  *   sglang PR's recipe, instead of the default log-linear code (see
  *   fp8attn_forward): about 12% slower, relative RMS error about 0.054 instead
  *   of 0.056 on the pages' normally distributed workloads.
- * Unknown flag bits, FP8ATTN_PLAN_Q_CENTRE without FP8ATTN_PLAN_MXFP4,
+ * Unknown flag bits, FP8ATTN_PLAN_Q_CENTRE on an E4M3 plan of head_dim 64 or less,
  * FP8ATTN_PLAN_EXACT_PROBS with FP8ATTN_PLAN_MXFP4,
  * FP8ATTN_PLAN_MXFP4 with FP8ATTN_PLAN_SEGMENT_SCALES (its scales are already
  * local to 32 elements) or with a head_dim other than 128, a head_dim that is

@@ -315,8 +315,11 @@ def test_mxfp4_plan_flags_layout_and_schedule():
     L = _lib.lib()
     cu = (ctypes.c_int32 * 4)(0, 100, 100, 300)
     h = ctypes.c_void_p()
-    # Q centring needs the FP4 format; FP4 takes no per-segment scales
-    assert L.fp8attn_plan_ex(ctypes.byref(h), 300, 2, cu, 3, ctypes.c_float(0.088), -1, _lib.PLAN_Q_CENTRE) == _lib.EINVAL
+    # E4M3 Q centring needs a head size above 64; FP4 takes no per-segment scales
+    assert L.fp8attn_plan_ex(ctypes.byref(h), 300, 2, cu, 3, ctypes.c_float(0.088), -1,
+                             _lib.PLAN_Q_CENTRE | _lib.PLAN_HEAD_DIM_64) == _lib.EINVAL
+    assert L.fp8attn_plan_ex(ctypes.byref(h), 300, 2, cu, 3, ctypes.c_float(0.088), -1,
+                             _lib.PLAN_Q_CENTRE | _lib.plan_head_dim(40)) == _lib.EINVAL
     assert L.fp8attn_plan_ex(ctypes.byref(h), 300, 2, cu, 3, ctypes.c_float(0.088), -1,
                              _lib.PLAN_MXFP4 | _lib.PLAN_SEGMENT_SCALES) == _lib.EINVAL
     assert h.value is None
@@ -542,3 +545,42 @@ def test_varlen_entry_points_validate_arguments():
     with pytest.raises(ValueError):                        # host copy of another length
         fa.varlen_attention_fp8(q, q, q, torch.tensor([0, 64], dtype=torch.int32), cu_seqlens_host=[0, 32, 64])
     assert fa.workspace_bytes(0) == 0
+
+
+def test_e4m3_q_centre_plan_layout_and_regions():
+    """E4M3 plans with Q centring: block means [H][rows/128][128] and the
+    mean-term table of sum over segments of (Lr/128) * Lr entries per head
+    (Lr = the segment's rows rounded up to 128), both before the statistics;
+    the Q block statistics inside them."""
+    cu = [0, 100, 100, 300, 557]
+    H = 3
+    plain = fa.Plan(557, H, cu, device=-1)
+    qc = fa.Plan(557, H, cu, device=-1, q_centre=True)
+    assert qc.info()["q_centre"] == 1 and plain.info()["q_centre"] == 0
+    rows = qc.info()["workspace_rows"]
+    assert rows == 128 + 256 + 384 + 128
+    lrs = [(b - a + 127) // 128 * 128 for a, b in zip(cu[:-1], cu[1:])]
+    entries = sum((lr // 128) * lr for lr in lrs)
+    assert entries == 128 + 2 * 256 + 3 * 384
+    L = _lib.lib()
+    base = 1 << 20
+    ptr = ctypes.c_void_p()
+    dims = (ctypes.c_int64 * 3)()
+    assert L.fp8attn_workspace_region(qc.handle, ctypes.c_void_p(base), _lib.REGION_QMEAN, ctypes.byref(ptr),
+                                      dims) == _lib.OK
+    assert tuple(dims) == (H, rows // 128, 128)
+    qmean_off = ptr.value - base
+    assert L.fp8attn_workspace_region(qc.handle, ctypes.c_void_p(base), _lib.REGION_QM_TERM, ctypes.byref(ptr),
+                                      dims) == _lib.OK
+    assert tuple(dims) == (H, entries, 4)
+    mt_off = ptr.value - base
+    assert mt_off >= qmean_off + 4 * H * (rows // 128) * 128
+    assert qc.stats_offset() >= mt_off + 4 * H * entries
+    # the statistics grow by the Q block sums (16 bytes per block, head and channel)
+    grow = (qc.workspace_bytes - qc.stats_offset()) - (plain.workspace_bytes - plain.stats_offset())
+    assert grow >= 16 * (rows // 128) * H * 128
+    for which in (_lib.REGION_QMEAN, _lib.REGION_QM_TERM):
+        assert L.fp8attn_workspace_region(plain.handle, ctypes.c_void_p(base), which, ctypes.byref(ptr),
+                                          dims) == _lib.EINVAL
+    # the schedule is the one of the plain plan
+    assert qc.work_items() == plain.work_items()

@@ -1,0 +1,252 @@
+"""GPU parity of E4M3 plans with Q block-mean centring (FP8ATTN_PLAN_Q_CENTRE)
+against the CPU oracle (oracle.quantize with q_centre=True).
+
+The FlashInfer "minimax_h3_sm120_varlen_attention_nvfp4" page centres Q rows
+by the mean of their 128-row block and adds the block-mean term qm . k back to
+the scores.  Checked here:
+* bit for bit: the Q codes of fl32(q - qm), the K and V codes, every scale,
+  the K means and the block means qm (REGION_QMEAN, blocks by workspace row);
+* the mean-term table (REGION_QM_TERM, tile-major): every entry of the checked heads
+  against f * (qm . khat) in float64 (f = softmax_scale * s_k * log2(e),
+  times 8 in the log-linear frame), within 2^-11 of f * sum |qm khat|: the
+  kernel carries qm in three E4M3 parts (about 12 significant bits each
+  element), accumulates in FP32 and stores a bf16 pair (16 bits); padding
+  keys hold exactly 0;
+* the output against the oracle on the dequantized operands with the exact
+  mean term (relative RMS <= 0.035 and |o - r| <= 0.1 + 0.1 |r|, the kernel
+  bars of the other E4M3 tests), and against the exact inputs within the
+  operands' own error and that kernel bar in quadrature (with per-channel Q
+  offsets of variance 2 the E4M3 operands alone exceed 0.06 relative RMS at a
+  few thousand keys: tests/test_oracle_qcentre.py), and below the error of an
+  uncentred plan on the same inputs;
+* the LSE, key splits, causal masking, per-segment scales, exact
+  probabilities and both query tiles (128 and 256 queries per work item).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import fp8_flash_attention_amd as fa
+from fp8_flash_attention_amd import _lib
+from oracle import attention as A
+from oracle import compare
+from oracle import e4m3
+from oracle import quantize as Qz
+from tests.gpu_helpers import check_lse, log, read_codes
+from workloads import WORKLOADS, generate, make_workload, sample_rows
+
+pytestmark = pytest.mark.gpu
+
+DIAG_BAR = 0.035
+LOG2E = 1.4426950408889634
+
+
+def _blocks(cu):
+    """(segment, first row, end row, global block index) of every Q block."""
+    out, r0 = [], 0
+    for s, (a, b) in enumerate(zip(cu[:-1], cu[1:])):
+        for r in range(a, b, 128):
+            out.append((s, r, min(r + 128, b), (r0 + r - a) // 128))
+        r0 += (b - a + 127) // 128 * 128
+    return out
+
+
+def _oracle(q, k, v, cu, sc, segment_scales=False):
+    if segment_scales:
+        r = Qz.quantize_segments(q, k, v, cu, sc, q_centre=True)
+        dk = Qz.dequantize_segments(r["k_codes"], r["scales"][1], cu)
+        dv = Qz.dequantize_segments(r["v_codes"], r["scales"][2], cu)
+    else:
+        r = Qz.quantize(q, k, v, cu, sc, q_centre=True)
+        dk = Qz.dequantize(r["k_codes"], r["scales"][1])
+        dv = Qz.dequantize(r["v_codes"], r["scales"][2])
+    qop = Qz.qcentre_operand(r["q_codes"], r["scales"][0], r["qm"], cu)
+    return r, qop, dk, dv
+
+
+def _run(w, causal=False, lse=False, segment_scales=False, exact_probs=False, q_centre=True):
+    q, k, v = generate(w, device="cuda")
+    plan = fa.Plan(w.tokens, w.heads, w.cu_seqlens, w.softmax_scale, device=0, q_centre=q_centre, causal=causal,
+                   segment_scales=segment_scales, exact_probs=exact_probs)
+    info = plan.info()
+    log(f"qcentre={q_centre} {w.name} T={w.tokens} H={w.heads} cu={list(w.cu_seqlens)[:8]} causal={causal} "
+        f"lse={lse} seg_scales={segment_scales} exact={exact_probs} tile={info['query_tile']} "
+        f"pieces={info['partial_slots']} ws={plan.workspace_bytes}")
+    ws = plan.new_workspace()
+    ws.fill_(0xFF)
+    fa.quantize(plan, q, k, v, ws)
+    l = torch.full((w.heads, w.tokens), float("nan"), dtype=torch.float32, device="cuda") if lse else None
+    out = fa.forward(plan, ws, None, l)
+    torch.cuda.synchronize()
+    return plan, ws, out, l, (q.cpu(), k.cpu(), v.cpu())
+
+
+def _check_codes(plan, ws, r, cu, heads):
+    got = read_codes(plan, ws, heads)
+    for name in ("q_codes", "k_codes", "v_codes"):
+        assert np.array_equal(got[name], r[name][:, heads]), name
+    sc = np.asarray(got["scales"])
+    assert np.array_equal(sc.view(np.uint32), r["scales"].view(np.uint32))
+    assert np.array_equal(got["mu"].view(np.uint32), r["mu"].view(np.uint32))
+    qmean = plan.region(ws, _lib.REGION_QMEAN).cpu().numpy()       # [H][rows/128][128]
+    for i, (s, a, b, g) in enumerate(_blocks(cu)):
+        assert np.array_equal(qmean[heads, g].view(np.uint32), r["qm"][i][heads].view(np.uint32)), (i, g)
+    assert not qmean[:, -1].any(), "guard block mean not zero"
+
+
+def _check_table(plan, ws, r, cu, sc, heads, exact_probs=False, segment_scales=False):
+    """Every mean-term entry of the given heads against float64."""
+    tab = plan.region(ws, _lib.REGION_QM_TERM)                      # [H][entries] int32
+    frame = 1.0 if exact_probs else 8.0
+    blocks = _blocks(cu)
+    e0 = 0
+    worst = 0.0
+    for s, (a, b) in enumerate(zip(cu[:-1], cu[1:])):
+        L = b - a
+        lr = (L + 127) // 128 * 128
+        nb = lr // 128
+        if nb == 0:
+            continue
+        seg_blocks = [i for i, blk in enumerate(blocks) if blk[0] == s]
+        for h in heads:
+            s_k = (r["scales"][1, s, h] if segment_scales else r["scales"][1, h])
+            f = float(np.float32(sc)) * float(s_k) * LOG2E * frame
+            kd = np.zeros((lr, r["k_codes"].shape[2]), np.float64)
+            kd[:L] = e4m3.decode(r["k_codes"][a:b, h])
+            qm = np.stack([r["qm"][i][h].astype(np.float64) for i in seg_blocks])   # [nb, D]
+            exp = f * (qm @ kd.T)                                                   # [nb, lr]
+            mag = f * (np.abs(qm) @ np.abs(kd).T)
+            # tile-major: [key tile][block][64 keys]
+            raw = (tab[h, e0:e0 + nb * lr].cpu().numpy().view(np.uint32).reshape(lr // 64, nb, 64)
+                   .transpose(1, 0, 2).reshape(nb, lr))
+            hi = (raw & 0xFFFF).astype(np.uint32) << 16
+            lo = (raw >> 16).astype(np.uint32) << 16
+            got = hi.view(np.float32).astype(np.float64) + lo.view(np.float32).astype(np.float64)
+            assert (got[:, L:] == 0).all(), "padding keys of the mean-term table not zero"
+            err = np.abs(got - exp)
+            assert (err <= 2.0 ** -11 * mag + 1e-30).all(), (s, h, float((err / np.maximum(mag, 1e-30)).max()))
+            worst = max(worst, float((err / np.maximum(mag, 1e-30)).max()))
+        e0 += nb * lr
+    log(f"  mean-term table: worst error {worst:.2e} of f * sum |qm khat|")
+
+
+def _check_out(w, out, q, k, v, rows, qop, dk, dv, causal=False, few_keys_diag=True):
+    o = out.cpu()[rows].double().numpy()
+    assert np.isfinite(o).all()
+    cu, sc = w.cu_seqlens, w.softmax_scale
+    ref = A.attention_rows(q, k, v, cu, sc, rows, causal=causal).numpy()
+    diag = A.attention_rows(qop, dk, dv, cu, sc, rows, causal=causal).numpy()
+    rr, rd, ro = compare.rel_rms(o, ref), compare.rel_rms(o, diag), compare.rel_rms(diag, ref)
+    ex_d = compare.allclose_excess(o, diag)
+    log(f"  rel_rms vs exact {rr:.5f} (operands alone {ro:.5f}), vs dequantized {rd:.5f}, excess vs dequantized "
+        f"{ex_d:.5f}")
+    assert rd <= DIAG_BAR and ex_d <= 0.0
+    assert rr <= math.sqrt(ro ** 2 + DIAG_BAR ** 2)
+    return rr
+
+
+SMALL = [
+    make_workload("qc_ragged", 700, 3, [0, 300, 700], seed=901, k_offset_var=2.0, q_offset_var=2.0),
+    make_workload("qc_varlen", 1500, 3, [0, 0, 1, 64, 65, 193, 700, 700, 1500], seed=902, q_offset_var=2.0),
+    make_workload("qc_fused", 500, 4, [0, 130, 500], seed=903, layout="fused", q_offset_var=2.0),
+]
+
+
+@pytest.mark.parametrize("w", SMALL, ids=[w.name for w in SMALL])
+def test_codes_means_table_and_every_output(w):
+    plan, ws, out, _, (q, k, v) = _run(w)
+    r, qop, dk, dv = _oracle(q, k, v, w.cu_seqlens, w.softmax_scale)
+    heads = list(range(w.heads))
+    _check_codes(plan, ws, r, w.cu_seqlens, heads)
+    _check_table(plan, ws, r, w.cu_seqlens, w.softmax_scale, heads)
+    _check_out(w, out, q, k, v, list(range(w.tokens)), qop, dk, dv)
+
+
+def test_256_query_items_lse_and_the_gain_over_an_uncentred_plan():
+    w = make_workload("qc_8192", 8192, 48, [0, 8192], seed=904, k_offset_var=2.0, q_offset_var=2.0)
+    plan, ws, out, l, (q, k, v) = _run(w, lse=True)
+    assert plan.info()["query_tile"] == 256
+    r, qop, dk, dv = _oracle(q, k, v, w.cu_seqlens, w.softmax_scale)
+    _check_codes(plan, ws, r, w.cu_seqlens, [0, 23, 47])
+    _check_table(plan, ws, r, w.cu_seqlens, w.softmax_scale, [0, 47])
+    rows = sample_rows(w.tokens, 256, seed=905, cu_seqlens=w.cu_seqlens)
+    rr = _check_out(w, out, q, k, v, rows, qop, dk, dv)
+    # LSE: the log-sum-exp of the uncentred scores of the operands (K with its mean back)
+    dkc = dk + r["mu"][0][None].astype(np.float64)
+    ld = A.lse_rows(torch.from_numpy(qop), torch.from_numpy(dkc), w.cu_seqlens, w.softmax_scale, rows).numpy().T
+    check_lse(l.cpu().double().numpy()[:, rows], ld, False, "q-centred")
+    # the same inputs without centring: centring must cut the error against the exact inputs
+    del ws
+    plan2, ws2, out2, _, _ = _run(w, q_centre=False)
+    o2 = out2.cpu()[rows].double().numpy()
+    ref = A.attention_rows(q, k, v, w.cu_seqlens, w.softmax_scale, rows).numpy()
+    rp = compare.rel_rms(o2, ref)
+    log(f"  uncentred plan rel_rms vs exact {rp:.5f}, centred {rr:.5f}")
+    assert rr <= 0.95 * rp
+
+
+def test_key_splits_and_lse():
+    w = make_workload("qc_split", 3000, 1, [0, 3000], seed=906, k_offset_var=2.0, q_offset_var=2.0)
+    plan, ws, out, l, (q, k, v) = _run(w, lse=True)
+    assert plan.info()["partial_slots"] > 0, "expected a split plan"
+    r, qop, dk, dv = _oracle(q, k, v, w.cu_seqlens, w.softmax_scale)
+    _check_out(w, out, q, k, v, list(range(w.tokens)), qop, dk, dv)
+    dkc = dk + r["mu"][0][None].astype(np.float64)
+    ld = A.lse_rows(torch.from_numpy(qop), torch.from_numpy(dkc), w.cu_seqlens, w.softmax_scale).numpy().T
+    check_lse(l.cpu().double().numpy(), ld, False, "q-centred split")
+
+
+def test_causal():
+    w = make_workload("qc_causal", 700, 4, [0, 300, 700], seed=907, k_offset_var=2.0, q_offset_var=2.0)
+    plan, ws, out, l, (q, k, v) = _run(w, causal=True, lse=True)
+    r, qop, dk, dv = _oracle(q, k, v, w.cu_seqlens, w.softmax_scale)
+    _check_codes(plan, ws, r, w.cu_seqlens, list(range(w.heads)))
+    o = out.cpu().double().numpy()
+    cu, sc = w.cu_seqlens, w.softmax_scale
+    diag = A.attention(qop, dk, dv, cu, sc, causal=True).numpy()
+    rd = compare.rel_rms(o, diag)
+    # rows that see fewer than 64 keys average a few E4M3-rounded weights: the
+    # element-wise bar is kept for the rows that see 64 keys or more
+    pos = np.concatenate([np.arange(b - a) for a, b in zip(cu[:-1], cu[1:])])
+    ex_d = compare.allclose_excess(o[pos >= 64], diag[pos >= 64])
+    log(f"  causal rel_rms vs dequantized {rd:.5f}, excess (>= 64 keys) {ex_d:.5f}")
+    assert rd <= DIAG_BAR and ex_d <= 0.0
+    dkc = dk.copy()
+    for s, (a, b) in enumerate(zip(cu[:-1], cu[1:])):
+        dkc[a:b] += r["mu"][s][None].astype(np.float64)
+    ld = A.lse_rows(torch.from_numpy(qop), torch.from_numpy(dkc), cu, sc, causal=True).numpy().T
+    check_lse(l.cpu().double().numpy(), ld, False, "q-centred causal")
+
+
+def test_segment_scales_and_exact_probabilities():
+    w = make_workload("qc_segsc", 1200, 2, [0, 130, 130, 900, 1200], seed=908, q_offset_var=2.0)
+    for seg, exact in ((True, False), (False, True)):
+        plan, ws, out, _, (q, k, v) = _run(w, segment_scales=seg, exact_probs=exact)
+        r, qop, dk, dv = _oracle(q, k, v, w.cu_seqlens, w.softmax_scale, segment_scales=seg)
+        _check_codes(plan, ws, r, w.cu_seqlens, [0, 1])
+        _check_table(plan, ws, r, w.cu_seqlens, w.softmax_scale, [0, 1], exact_probs=exact, segment_scales=seg)
+        _check_out(w, out, q, k, v, list(range(w.tokens)), qop, dk, dv)
+
+
+def test_varlen_entry_point_matches_attention():
+    w = SMALL[0]
+    q, k, v = generate(w, device="cuda")
+    cu = torch.tensor(w.cu_seqlens, dtype=torch.int32, device="cuda")
+    a = fa.attention(q, k, v, w.cu_seqlens, q_centre=True)
+    b = fa.varlen_attention_fp8(q, k, v, cu, cu_seqlens_host=w.cu_seqlens, q_centre=True)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+def test_denoise_step_shape_with_q_offsets():
+    """S = 30272, 56 heads, K and Q offsets: codes of three heads, the table of
+    one, sampled rows of every head."""
+    w = WORKLOADS["s30272_h56_qkoffset"]
+    plan, ws, out, _, (q, k, v) = _run(w)
+    r, qop, dk, dv = _oracle(q, k, v, w.cu_seqlens, w.softmax_scale)
+    _check_codes(plan, ws, r, w.cu_seqlens, [0, 27, 55])
+    _check_table(plan, ws, r, w.cu_seqlens, w.softmax_scale, [55])
+    rows = sample_rows(w.tokens, 96, seed=909, cu_seqlens=w.cu_seqlens)
+    _check_out(w, out, q, k, v, rows, qop, dk, dv)
