@@ -3,10 +3,11 @@ oracle (test infrastructure; the bars are those of the targeted tests).
 
 E4M3 plans draw the segment table (empty, one-token, tile-edge and longer
 segments), the head count, the head size (any multiple of 8 up to 128), and
-whether the plan is causal, has per-segment scales, exact probabilities and
-a K offset.  Each checks: the E4M3 codes, scales and K means of the real
+whether the plan is causal, has per-segment scales, exact probabilities, a
+K offset and (head sizes above 64) Q block-mean centring.  Each checks: the E4M3 codes, scales and K means of the real
 channels bit for bit (padding channels zero); every output element against
-the oracle on the dequantized operands (|o - r| <= 0.1 + 0.1 |r|, relative
+the oracle on the dequantized operands (with Q centring: the centred codes
+plus the exact block mean) (|o - r| <= 0.1 + 0.1 |r|, relative
 RMS <= 0.035 over rows that see >= 64 keys); rows that see >= 64 keys
 against the exact inputs with the same element-wise bar; the LSE with
 tests/gpu_helpers.check_lse.
@@ -47,9 +48,11 @@ def _table(rng):
 def _e4m3_config(i):
     rng = np.random.default_rng(9100 + i)
     cu = _table(rng)
-    return dict(cu=cu, H=int(rng.integers(1, 5)), D=8 * int(rng.integers(1, 17)), causal=bool(rng.random() < 0.4),
-                seg=bool(rng.random() < 0.3), exact=bool(rng.random() < 0.3),
-                koff=2.0 if rng.random() < 0.5 else None, seed=9100 + i)
+    c = dict(cu=cu, H=int(rng.integers(1, 5)), D=8 * int(rng.integers(1, 17)), causal=bool(rng.random() < 0.4),
+             seg=bool(rng.random() < 0.3), exact=bool(rng.random() < 0.3),
+             koff=2.0 if rng.random() < 0.5 else None, seed=9100 + i)
+    c["qc"] = c["D"] > 64 and bool(rng.random() < 0.5)     # drawn last: the other draws are unchanged
+    return c
 
 
 @pytest.mark.parametrize("i", range(16))
@@ -58,10 +61,10 @@ def test_random_e4m3_config(i):
     cu, H, D = c["cu"], c["H"], c["D"]
     w = make_workload(f"rand{i}", cu[-1], H, cu, seed=c["seed"], k_offset_var=c["koff"], head_dim=D)
     log(f"random e4m3 #{i}: cu={cu} H={H} D={D} causal={c['causal']} segment_scales={c['seg']} "
-        f"exact={c['exact']} k_offset={c['koff']}")
+        f"exact={c['exact']} k_offset={c['koff']} q_centre={c['qc']}")
     q, k, v = generate(w, device="cuda")
     plan = fa.Plan(w.tokens, H, cu, w.softmax_scale, device=0, head_dim=D, causal=c["causal"],
-                   segment_scales=c["seg"], exact_probs=c["exact"])
+                   segment_scales=c["seg"], exact_probs=c["exact"], q_centre=c["qc"])
     ws = plan.new_workspace()
     ws.fill_(0xFF)
     fa.quantize(plan, q, k, v, ws)
@@ -70,11 +73,13 @@ def test_random_e4m3_config(i):
     torch.cuda.synchronize()
     q, k, v = q.cpu(), k.cpu(), v.cpu()
     if c["seg"]:
-        r = Qz.quantize_segments(q, k, v, cu, w.softmax_scale)
+        r = Qz.quantize_segments(q, k, v, cu, w.softmax_scale, q_centre=c["qc"])
         deq = [Qz.dequantize_segments(r[n], r["scales"][j], cu) for j, n in enumerate(("q_codes", "k_codes", "v_codes"))]
     else:
-        r = Qz.quantize(q, k, v, cu, w.softmax_scale)
+        r = Qz.quantize(q, k, v, cu, w.softmax_scale, q_centre=c["qc"])
         deq = [Qz.dequantize(r[n], r["scales"][j]) for j, n in enumerate(("q_codes", "k_codes", "v_codes"))]
+    if c["qc"]:
+        deq[0] = Qz.qcentre_operand(r["q_codes"], r["scales"][0], r["qm"], cu)
     got = read_codes(plan, ws)
     for name in ("q_codes", "k_codes", "v_codes"):
         assert np.array_equal(got[name][..., :D], r[name]), name
