@@ -133,7 +133,7 @@ WorkspaceLayout make_layout(int64_t rows, int heads, int nseg, int nscale, int n
   w.kstat_off = off; off = align_up(off + sizeof(KStat) * (size_t)nchunks * heads * D, 256);
   w.amax_off = off; off = align_up(off + sizeof(float) * 2 * (size_t)nchunks * heads, 256);
   if (mt_per_head > 0) {
-    w.qstat_off = off; off = align_up(off + sizeof(KStat) * qblocks * heads * D, 256);
+    w.qamax_off = off; off = align_up(off + sizeof(float) * qblocks * heads * (D / 8), 256);
   }
   w.total = off;
   return w;
@@ -497,7 +497,7 @@ size_t static_stats_bytes(const fp8attn_plan_s* p) {
   const size_t kst = align_up(sizeof(KStat) * nch * (size_t)p->heads * (size_t)p->dk, 256);
   const size_t amx = p->mx ? 0 : align_up(sizeof(float) * 2 * nch * (size_t)p->heads, 256);
   const size_t qst = p->mt_per_head > 0
-                         ? align_up(sizeof(KStat) * (size_t)(p->ws.rows / kQmBlock) * (size_t)p->heads * (size_t)p->dk, 256)
+                         ? align_up(sizeof(float) * (size_t)(p->ws.rows / kQmBlock) * (size_t)p->heads * (size_t)(p->dk / 8), 256)
                          : 0;
   return kst + amx + qst;
 }
@@ -529,16 +529,16 @@ fp8attn_status quantize_impl(fp8attn_plan_t p, const void* q, const void* k, con
   DeviceGuard g(p->device);
   if (!g.ok) return fail(FP8ATTN_EHIP, "cannot select device");
   uint8_t* ws = static_cast<uint8_t*>(workspace);
-  uint8_t* stats = ws + p->ws.kstat_off;                      // kstat, then amax (E4M3 plans), then qstat
+  uint8_t* stats = ws + p->ws.kstat_off;                      // kstat, then amax (E4M3 plans), then qamax
   size_t amax_rel = p->mx ? 0 : p->ws.amax_off - p->ws.kstat_off;
-  size_t qstat_rel = p->mt_per_head > 0 ? p->ws.qstat_off - p->ws.kstat_off : 0;
+  size_t qamax_rel = p->mt_per_head > 0 ? p->ws.qamax_off - p->ws.kstat_off : 0;
   if (noalloc) {
     const hipError_t e = static_stats_buffer(p->device, &stats);
     if (e != hipSuccess)
       return fail(FP8ATTN_EHIP, std::string("static statistics buffer: ") + hipGetErrorString(e));
     if (!p->mx) amax_rel = align_up(sizeof(KStat) * p->chunks.size() * (size_t)p->heads * (size_t)p->dk, 256);
     if (p->mt_per_head > 0)
-      qstat_rel = amax_rel + align_up(sizeof(float) * 2 * p->chunks.size() * (size_t)p->heads, 256);
+      qamax_rel = amax_rel + align_up(sizeof(float) * 2 * p->chunks.size() * (size_t)p->heads, 256);
   }
   QuantizeArgs a{};
   a.x[0] = static_cast<const uint16_t*>(q);
@@ -572,7 +572,7 @@ fp8attn_status quantize_impl(fp8attn_plan_t p, const void* q, const void* k, con
   a.d_real = p->head_dim;
   a.exact_probs = p->exact_probs;
   if (p->mt_per_head > 0) {
-    a.qstat = reinterpret_cast<KStat*>(stats + qstat_rel);
+    a.qamax = reinterpret_cast<float*>(stats + qamax_rel);
     a.qmean = reinterpret_cast<float*>(ws + p->ws.qmean_off);
     a.mt = reinterpret_cast<uint32_t*>(ws + p->ws.mt_off);
     a.mt_seg = p->d_mt_seg;

@@ -89,8 +89,9 @@ struct WorkspaceLayout {
   size_t part_lse_off; // float [npieces][kPartRows]: natural-log LSE of each partial row
   size_t stats_off;    // start of the statistics (kstat, amax), the last regions
   // E4M3 plans with Q centring: block means float [H][rows/128][D], the mean-term
-  // table uint32 [H][mt_per_head], and (statistics) Q block sums KStat [rows/128][H][D]
-  size_t qmean_off, mt_off, qstat_off;
+  // table uint32 [H][mt_per_head], and (statistics) the blocks' centred amax
+  // partials float [rows/128][H][D/8]
+  size_t qmean_off, mt_off, qamax_off;
   int64_t mt_per_head;
   size_t total;
 };
@@ -124,8 +125,8 @@ struct QuantizeArgs {
   uint8_t* bscale[3];        // Q, K, V^T block scales (WorkspaceLayout)
   uint8_t* qm_codes;
   uint8_t* qm_scales;
-  // E4M3 plans with q_centre: Q block statistics and means, the mean-term table
-  KStat* qstat;              // [rows/128][H][D]
+  // E4M3 plans with q_centre: Q block means and centred amax partials, the mean-term table
+  float* qamax;              // [rows/128][H][D/8]
   float* qmean;              // [H][rows/128][D]
   uint32_t* mt;              // [H][mt_per_head]
   const int64_t* mt_seg;     // [nseg]: first entry of each segment's part of a head's table

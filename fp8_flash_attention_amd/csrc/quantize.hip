@@ -108,7 +108,7 @@ __device__ __forceinline__ void stat_rows(const uint16_t* base, int64_t ts, int 
   for (int i = 0; i < 8; i++) out[i] = KStat{sum[i], mn[i], mx[i]};
 }
 
-template <int D>
+template <int D, bool QC>
 __global__ __launch_bounds__(256) void k_stats(QuantizeArgs a) {
   constexpr int TPH = D / 8;
   constexpr int HPB = 256 / TPH;
@@ -128,15 +128,34 @@ __global__ __launch_bounds__(256) void k_stats(QuantizeArgs a) {
     stat_rows(base, ts, ch.tok0, 0, ch.ntok, live, a.kstat + ((int64_t)c * a.heads + h) * D + c0);
     return;
   }
-  if (tensor == 0 && a.q_centre) {
-    // Q centring: the same statistics per 128-row Q block.  A chunk starts on
-    // a block boundary of its segment and covers one or two blocks.
+  if (QC && tensor == 0) {
+    // Q centring (a kernel of its own, so the other's registers are unchanged):
+    // the same statistics per 128-row Q block (a chunk starts on a
+    // block boundary of its segment and covers one or two blocks), turned
+    // into the block mean qm = fl32(sum64 / n) and this thread's part of the
+    // block's centred amax, max |fl32(max - qm)|, |fl32(min - qm)| over its 8
+    // channels (exact: rounding is monotone).
     if (!active) return;
     const SegInfo si = a.segs[ch.seg];
     const int64_t g0 = (si.row0 + (ch.tok0 - si.start)) / kQmBlock;
-    stat_rows(base, ts, ch.tok0, 0, min(ch.ntok, kQmBlock), live, a.qstat + (g0 * a.heads + h) * D + c0);
-    if (ch.ntok > kQmBlock)
-      stat_rows(base, ts, ch.tok0, kQmBlock, ch.ntok, live, a.qstat + ((g0 + 1) * a.heads + h) * D + c0);
+    const int64_t nqb = a.rows / kQmBlock;
+    for (int half = 0; half < 2; half++) {
+      const int j0 = half * kQmBlock, j1 = min(ch.ntok, j0 + kQmBlock);
+      if (j0 >= j1) break;
+      KStat st[8];
+      stat_rows(base, ts, ch.tok0, j0, j1, live, st);
+      float qm[8];
+      float m = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; i++) {
+        qm[i] = (float)(st[i].sum / (double)(j1 - j0));
+        m = fmaxf(m, fmaxf(fabsf(st[i].mx - qm[i]), fabsf(st[i].mn - qm[i])));
+      }
+      float4* dst = reinterpret_cast<float4*>(a.qmean + ((int64_t)h * nqb + g0 + half) * D + c0);
+      dst[0] = make_float4(qm[0], qm[1], qm[2], qm[3]);
+      dst[1] = make_float4(qm[4], qm[5], qm[6], qm[7]);
+      a.qamax[((g0 + half) * a.heads + h) * TPH + (t % TPH)] = m;
+    }
     return;
   }
 
@@ -250,22 +269,14 @@ __global__ __launch_bounds__(D) void k_finalize(QuantizeArgs a) {
       kas = fmaxf(fabsf(mx - mu), fabsf(mn - mu));
     }
     a.mu[((int64_t)s * a.heads + h) * D + d] = mu;
-    // Q centring: qm = fl32(sum64 / n) per block; Q's amax over the segment is
-    // the maximum of |fl32(max - qm)| and |fl32(min - qm)| (exact: rounding is
-    // monotone), this thread's channel first
+    // Q centring: Q's amax over the segment is the maximum of its blocks'
+    // centred amax partials (D/8 per block and head, from the statistics pass)
     float qcs = 0.f;
     if (a.q_centre) {
+      constexpr int TPH = D / 8;
       const int64_t g0 = si.row0 / kQmBlock;
-      const int nb = (si.len + kQmBlock - 1) / kQmBlock;
-      const KStat* __restrict__ qst = a.qstat + (g0 * a.heads + h) * D + d;
-      float* __restrict__ qmo = a.qmean + ((int64_t)h * nqb + g0) * D + d;
-#pragma unroll 8
-      for (int b = 0; b < nb; b++) {   // loads issued ahead (no aliasing with the stores)
-        const KStat st = qst[(int64_t)b * a.heads * D];
-        const float qm = (float)(st.sum / (double)min(kQmBlock, si.len - b * kQmBlock));
-        qmo[(int64_t)b * D] = qm;
-        qcs = fmaxf(qcs, fmaxf(fabsf(st.mx - qm), fabsf(st.mn - qm)));
-      }
+      const int n = (si.len + kQmBlock - 1) / kQmBlock * TPH;
+      for (int e = d; e < n; e += D) qcs = fmaxf(qcs, a.qamax[((g0 + e / TPH) * a.heads + h) * TPH + e % TPH]);
       if (!a.seg_scales) qa = fmaxf(qa, qcs);
     }
     if (a.seg_scales) {
@@ -496,15 +507,26 @@ __global__ __launch_bounds__(256) void k_qmterm(QuantizeArgs a) {
   const float f = a.softmax_scale * s_k * 1.4426950408889634f * (a.exact_probs ? 1.0f : 8.0f);
   uint32_t* seg_tab = a.mt + (int64_t)h * a.mt_per_head + a.mt_seg[u.x];
   const int kend = min(u.z + kQmUnitKeys, lr);
-  // 32 keys per wave and step: B = khat^T, lane l key key0 + l%32
-  for (int key0 = u.z + 32 * wave; key0 < kend; key0 += 128) {
-    const uint8_t* krow = a.codes[1] + ((int64_t)h * a.rows + si.row0 + key0 + lq) * kHeadDim;
+  // 32 keys per wave and step: B = khat^T, lane l key key0 + l%32, channels
+  // 64 half + 32 lg .. +32; the next step's K bytes are loaded ahead
+  int key0 = u.z + 32 * wave;
+  if (key0 >= kend) return;   // wave-uniform
+  auto load_b = [&](int k0, uint4 (&b)[4]) __attribute__((always_inline)) {
+    const uint8_t* krow = a.codes[1] + ((int64_t)h * a.rows + si.row0 + k0 + lq) * kHeadDim + 32 * lg;
+    b[0] = *reinterpret_cast<const uint4*>(krow);
+    b[1] = *reinterpret_cast<const uint4*>(krow + 16);
+    b[2] = *reinterpret_cast<const uint4*>(krow + 64);
+    b[3] = *reinterpret_cast<const uint4*>(krow + 80);
+  };
+  uint4 bn[4];
+  load_b(key0, bn);
+  for (; key0 < kend; key0 += 128) {
+    const uint4 b[4] = {bn[0], bn[1], bn[2], bn[3]};
+    if (key0 + 128 < kend) load_b(key0 + 128, bn);
     v16f_q acc = {};
 #pragma unroll
     for (int half = 0; half < 2; half++) {
-      const int ch0 = 64 * half + 32 * lg;
-      const uint4 b0 = *reinterpret_cast<const uint4*>(krow + ch0);
-      const uint4 b1 = *reinterpret_cast<const uint4*>(krow + ch0 + 16);
+      const uint4 b0 = b[2 * half], b1 = b[2 * half + 1];
       const v8i_q bk = v8i_q{(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
 #pragma unroll
       for (int part = 0; part < 3; part++)
@@ -726,7 +748,11 @@ template <int D>
 hipError_t launch_quantize_d(const QuantizeArgs& a, hipStream_t stream) {
   constexpr int HPB = 256 / (D / 8);   // heads per stats block
   if (a.nchunks > 0) {
-    hipLaunchKernelGGL(k_stats<D>, dim3(a.nchunks, (a.heads + HPB - 1) / HPB, a.mx ? 1 : 3), dim3(256), 0, stream, a);
+    if (a.q_centre && !a.mx)
+      hipLaunchKernelGGL((k_stats<D, true>), dim3(a.nchunks, (a.heads + HPB - 1) / HPB, 3), dim3(256), 0, stream, a);
+    else
+      hipLaunchKernelGGL((k_stats<D, false>), dim3(a.nchunks, (a.heads + HPB - 1) / HPB, a.mx ? 1 : 3), dim3(256), 0,
+                         stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -576,9 +576,9 @@ def test_e4m3_q_centre_plan_layout_and_regions():
     mt_off = ptr.value - base
     assert mt_off >= qmean_off + 4 * H * (rows // 128) * 128
     assert qc.stats_offset() >= mt_off + 4 * H * entries
-    # the statistics grow by the Q block sums (16 bytes per block, head and channel)
+    # the statistics grow by the blocks' centred amax partials (16 floats per block and head)
     grow = (qc.workspace_bytes - qc.stats_offset()) - (plain.workspace_bytes - plain.stats_offset())
-    assert grow >= 16 * (rows // 128) * H * 128
+    assert grow >= 4 * 16 * (rows // 128) * H
     for which in (_lib.REGION_QMEAN, _lib.REGION_QM_TERM):
         assert L.fp8attn_workspace_region(plain.handle, ctypes.c_void_p(base), which, ctypes.byref(ptr),
                                           dims) == _lib.EINVAL

@@ -1,5 +1,6 @@
 """fp8attn_quantize_noalloc (statistics in the library's static device buffer)
-against fp8attn_quantize: the code, scale and mean regions bit for bit and the
+against fp8attn_quantize: the code, scale and mean regions (with E4M3 Q
+centring also the block means and the mean-term table) bit for bit and the
 forward output from each workspace, on two calls in a row, the second with a
 smaller input; the noalloc workspace stops where the statistics region would
 begin and is poisoned first."""
@@ -30,7 +31,8 @@ def _check(w, fmt="e4m3", q_centre=False):
     ws_na = torch.full((n,), 0xFF, dtype=torch.uint8, device="cuda")
     fa.quantize_noalloc(plan, q, k, v, ws_na)
     torch.cuda.synchronize()
-    for r in (MX_REGIONS if fmt == "mxfp4" else E4M3_REGIONS):
+    regions = MX_REGIONS if fmt == "mxfp4" else E4M3_REGIONS + ([_lib.REGION_QMEAN, _lib.REGION_QM_TERM] if q_centre else [])
+    for r in regions:
         a, b = plan.region(ws_ref, r), plan.region(ws_na, r)
         assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), r
     log("  forward from both workspaces")
@@ -52,6 +54,13 @@ def test_noalloc_fp4_plan_and_segment_edges():
     _check(make_workload("noalloc_mx", 1500, 4, [0, 0, 1, 64, 65, 1500], seed=1203, k_offset_var=2.0),
            fmt="mxfp4", q_centre=True)
     _check(make_workload("noalloc_tiny", 257, 2, [0, 1, 257], seed=1204))
+
+
+def test_noalloc_e4m3_q_centre():
+    # the Q block statistics go to the static buffer as well
+    _check(make_workload("noalloc_qc", 1500, 3, [0, 0, 1, 64, 65, 193, 700, 700, 1500], seed=1205,
+                         k_offset_var=2.0, q_offset_var=2.0), q_centre=True)
+    _check(make_workload("noalloc_qc_small", 300, 2, [0, 300], seed=1206, q_offset_var=2.0), q_centre=True)
 
 
 def test_noalloc_rejects_plans_beyond_the_static_buffer():
