@@ -389,6 +389,13 @@ fp8attn_status fp8attn_plan_ex(fp8attn_plan_t* plan_out, int64_t tokens, int32_t
     int64_t e = 0;
     for (int s = 0; s < num_segments; s++) {
       const int64_t lr = (int64_t)(p->segs[s].len + kRowPad - 1) / kRowPad * kRowPad;
+      // the attention addresses one segment's part of a head's table through
+      // 32-bit buffer offsets: (lr / 128) * lr entries of 4 bytes must fit
+      if ((lr / kQmBlock) * lr * 4 > (int64_t)INT32_MAX) {
+        delete p;
+        return fail(FP8ATTN_EUNSUPPORTED, "Q centring on E4M3 plans takes segments of at most 262016 tokens "
+                                          "(32-bit offsets into the mean-term table)");
+      }
       p->mt_seg[s] = e;
       const int64_t nblk = lr / kQmBlock;
       for (int64_t bg = 0; bg < (nblk + kQmUnitBlocks - 1) / kQmUnitBlocks; bg++)

@@ -184,8 +184,9 @@ fp8attn_status fp8attn_plan(fp8attn_plan_t* plan_out, int64_t tokens, int32_t he
  *   significant bits), and the attention adds it to the scores through one
  *   small matrix product per 32-key block.  The table takes 4 bytes per
  *   (block, key) of every segment and head (1.6 GB at 30272 tokens and 56
- *   heads); plans whose table would pass 1 TiB are rejected with
- *   FP8ATTN_EUNSUPPORTED.  The LSE (if requested) is that of the uncentred
+ *   heads); plans with a segment longer than 262016 tokens (its part of a
+ *   head's table would pass 2^31 bytes) or whose table would pass 1 TiB are
+ *   rejected with FP8ATTN_EUNSUPPORTED.  The LSE (if requested) is that of the uncentred
  *   scores, ln 2 * (log2 l - offset) + softmax_scale * (s_q qhat + qm) . mu.
  * FP8ATTN_PLAN_CAUSAL: query i of a segment attends only to the
  *   keys j <= i of the same segment, positions counted from the segment start

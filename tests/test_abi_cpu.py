@@ -584,3 +584,14 @@ def test_e4m3_q_centre_plan_layout_and_regions():
                                           dims) == _lib.EINVAL
     # the schedule is the one of the plain plan
     assert qc.work_items() == plain.work_items()
+
+
+def test_e4m3_q_centre_rejects_segments_beyond_32_bit_table_offsets():
+    L = _lib.lib()
+    h = ctypes.c_void_p()
+    for T, ok in ((262016, True), (262017, False)):
+        cu = (ctypes.c_int32 * 2)(0, T)
+        st = L.fp8attn_plan_ex(ctypes.byref(h), T, 1, cu, 1, ctypes.c_float(0.088), -1, _lib.PLAN_Q_CENTRE)
+        assert st == (_lib.OK if ok else _lib.EUNSUPPORTED), (T, st)
+        if ok:
+            L.fp8attn_plan_destroy(h)
