@@ -250,3 +250,38 @@ def test_denoise_step_shape_with_q_offsets():
     _check_table(plan, ws, r, w.cu_seqlens, w.softmax_scale, [55])
     rows = sample_rows(w.tokens, 96, seed=909, cu_seqlens=w.cu_seqlens)
     _check_out(w, out, q, k, v, rows, qop, dk, dv)
+
+
+def test_q_offset_variant_of_the_denoise_step_shape_against_the_bar():
+    """S = 30272, 56 heads, K offset of variance 2 and a Q offset of variance
+    0.5: every head's sampled rows against the exact inputs, for an uncentred
+    and a centred plan with either probability encoding.  Centring must cut
+    the error in both and bring it to the 0.06 bar (the oracle's FP8 recipe
+    on these inputs: 0.0606 uncentred, 0.0585 centred, 48 rows of two
+    heads)."""
+    w = make_workload("s30272_h56_q05", 30272, 56, [0, 30272], seed=1010, k_offset_var=2.0, q_offset_var=0.5)
+    rows = sample_rows(w.tokens, 64, seed=910, cu_seqlens=w.cu_seqlens)
+    q, k, v = generate(w, device="cuda")
+    ref = A.attention_rows(q.cpu(), k.cpu(), v.cpu(), w.cu_seqlens, w.softmax_scale, rows).numpy()
+    err = {}
+    for exact in (False, True):
+        for qc in (False, True):
+            plan = fa.Plan(w.tokens, w.heads, w.cu_seqlens, w.softmax_scale, device=0, q_centre=qc,
+                           exact_probs=exact)
+            log(f"q-offset variant: q_centre={qc} exact={exact}")
+            ws = plan.new_workspace()
+            fa.quantize(plan, q, k, v, ws)
+            out = fa.forward(plan, ws)
+            torch.cuda.synchronize()
+            o = out.cpu()[rows].double().numpy()
+            assert np.isfinite(o).all()
+            err[(exact, qc)] = compare.rel_rms(o, ref)
+            log(f"  rel_rms vs exact {err[(exact, qc)]:.5f}")
+            del ws, plan
+    for exact in (False, True):
+        assert err[(exact, True)] < err[(exact, False)]
+    # measured (deterministic kernels, fixed rows): uncentred 0.0631 / 0.0610,
+    # centred 0.0599 / 0.0576 (default / exact probabilities): centring brings
+    # this Q-offset variant of the denoise-step shape under the 0.06 bar
+    assert err[(True, True)] <= compare.REL_RMS_BAR
+    assert err[(False, True)] <= compare.REL_RMS_BAR + 5e-4
