@@ -5,7 +5,9 @@ buffers: every replay, with eager work and synchronizations between replays,
 must reproduce the eager result (output and LSE) bit for bit.  Covered: the
 default E4M3 plan, one whose work items are split along the keys (so the
 combine pass is captured too), causal, a 96-channel head, the LSE output,
-the allocation-free quantize entry point, and an FP4 plan with Q centring.
+the allocation-free quantize entry point, an FP4 plan with Q centring, and
+E4M3 plans with Q centring (its mean-term kernel captured with the
+quantize), one of them split and quantized without allocation.
 """
 import pytest
 import torch
@@ -23,6 +25,8 @@ CASES = {
     "split_lse": dict(lse=True, split=True),
     "head_dim96_lse": dict(head_dim=96, lse=True),
     "mxfp4": dict(fmt="mxfp4", q_centre=True, lse=True),
+    "e4m3_q_centre": dict(q_centre=True, lse=True),
+    "e4m3_q_centre_split_noalloc": dict(q_centre=True, split=True, noalloc=True),
 }
 
 
