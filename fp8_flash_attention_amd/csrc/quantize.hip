@@ -80,7 +80,8 @@ __device__ __forceinline__ uint32_t cvt4(float a, float b, float c, float d) {
 
 // ---------------------------------------------------------------------------
 // Pass 1: statistics.  D channels per head row; grid = (nchunks, ceil(H/HPB), 3),
-// block = 256.  Thread t handles head HPB*blockIdx.y + t/TPH and channels
+// block = HPB * TPH threads (at most 256; the heads are spread evenly over the
+// groups, so no group runs half empty).  Thread t handles head HPB*blockIdx.y + t/TPH and channels
 // 8*(t%TPH) .. +8 over the chunk's tokens in ascending order (TPH = D/8
 // threads per head row, HPB = 256/TPH heads per block).
 // ---------------------------------------------------------------------------
@@ -111,7 +112,7 @@ __device__ __forceinline__ void stat_rows(const uint16_t* base, int64_t ts, int 
 template <int D, bool QC>
 __global__ __launch_bounds__(256) void k_stats(QuantizeArgs a) {
   constexpr int TPH = D / 8;
-  constexpr int HPB = 256 / TPH;
+  const int HPB = blockDim.x / TPH;
   const int c = blockIdx.x;
   const int tensor = a.mx ? 1 : blockIdx.z;   // FP4 plans need only K's statistics
   const int t = threadIdx.x;
@@ -746,12 +747,14 @@ __global__ __launch_bounds__(256) void k_pack_mx(QuantizeArgs a) {
 
 template <int D>
 hipError_t launch_quantize_d(const QuantizeArgs& a, hipStream_t stream) {
-  constexpr int HPB = 256 / (D / 8);   // heads per stats block
+  constexpr int TPH = D / 8;
+  const int ngrp = (a.heads + 256 / TPH - 1) / (256 / TPH);   // head groups of at most 256 / TPH heads
+  const int HPB = (a.heads + ngrp - 1) / ngrp;                // heads per stats block, spread evenly
   if (a.nchunks > 0) {
     if (a.q_centre && !a.mx)
-      hipLaunchKernelGGL((k_stats<D, true>), dim3(a.nchunks, (a.heads + HPB - 1) / HPB, 3), dim3(256), 0, stream, a);
+      hipLaunchKernelGGL((k_stats<D, true>), dim3(a.nchunks, (a.heads + HPB - 1) / HPB, 3), dim3(HPB * TPH), 0, stream, a);
     else
-      hipLaunchKernelGGL((k_stats<D, false>), dim3(a.nchunks, (a.heads + HPB - 1) / HPB, a.mx ? 1 : 3), dim3(256), 0,
+      hipLaunchKernelGGL((k_stats<D, false>), dim3(a.nchunks, (a.heads + HPB - 1) / HPB, a.mx ? 1 : 3), dim3(HPB * TPH), 0,
                          stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
