@@ -56,8 +56,7 @@ class Plan:
     host-only plan that can be inspected but not run.  ``segment_scales=True``
     quantizes every segment with its own per-head scales.  ``fmt`` is
     ``"e4m3"`` (default) or ``"mxfp4"``; ``q_centre`` centres Q by its 128-row
-    block means and adds the mean term back (E4M3: head sizes above 64; its
-    workspace holds one 4-byte mean-term entry per (128-query block, key) of
+    block means and adds the mean term back (E4M3: its workspace holds one 4-byte mean-term entry per (128-query block, key) of
     every segment and head).  ``causal``: query i of a segment attends to
     the keys j <= i of that segment.  ``head_dim``: 128, or (e4m3 only) any
     multiple of 8 from 8 to 128 (run at the kernel width 64 or 128 with the

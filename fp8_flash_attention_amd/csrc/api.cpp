@@ -331,8 +331,6 @@ fp8attn_status fp8attn_plan_ex(fp8attn_plan_t* plan_out, int64_t tokens, int32_t
     return fail(FP8ATTN_EINVAL, "FP8ATTN_PLAN_MXFP4 plans take head_dim 128 only");
   if ((flags & FP8ATTN_PLAN_EXACT_PROBS) && (flags & FP8ATTN_PLAN_MXFP4))
     return fail(FP8ATTN_EINVAL, "FP8ATTN_PLAN_EXACT_PROBS applies to E4M3 plans only");
-  if ((flags & FP8ATTN_PLAN_Q_CENTRE) && !(flags & FP8ATTN_PLAN_MXFP4) && head_dim <= 64)
-    return fail(FP8ATTN_EINVAL, "FP8ATTN_PLAN_Q_CENTRE on E4M3 plans takes head_dim above 64");
   if ((flags & FP8ATTN_PLAN_MXFP4) && (flags & FP8ATTN_PLAN_SEGMENT_SCALES))
     return fail(FP8ATTN_EINVAL, "FP8ATTN_PLAN_MXFP4 does not take FP8ATTN_PLAN_SEGMENT_SCALES");
   if (cu == nullptr) return fail(FP8ATTN_EINVAL, "cu_seqlens_host is NULL");

@@ -249,7 +249,6 @@ __global__ __launch_bounds__(2 * BM, 256 / BM) void k_attn(AttentionArgs a) {
   constexpr bool kSplitLoads = kLoads < kWavesWG;
   constexpr int kLoadsPerTile = kSplitLoads ? 1 : kLoads / kWavesWG;
   static_assert(D == 128 || (D == 64 && kWavesWG == 8), "head_dim 128, or 64 with 256-query items");
-  static_assert(!QC || D == 128, "Q centring at 128 channels");
   // Q centring: a ring of mean-term tiles after the V ring, one 512-byte slot
   // per key tile (the 64 keys of each of the item's 128-query blocks)
   constexpr int kMtSlot = 512;
@@ -412,7 +411,7 @@ __global__ __launch_bounds__(2 * BM, 256 / BM) void k_attn(AttentionArgs a) {
     const float* qmr = a.qmean + ((size_t)h * (a.rows / kQmBlock) + si.row0 / kQmBlock + qblk) * D;
     float dot = 0.f;
 #pragma unroll
-    for (int j = 0; j < 64; j++) dot += qmr[64 * lg + j] * mu[64 * lg + j];
+    for (int j = 0; j < D / 2; j++) dot += qmr[(D / 2) * lg + j] * mu[(D / 2) * lg + j];
     qmm = sum_pair32(dot);
   }
 
@@ -463,6 +462,8 @@ __global__ __launch_bounds__(2 * BM, 256 / BM) void k_attn(AttentionArgs a) {
         else
           init = NB;
         S[kb] = mfma_fp8_scaled(k1, qf[1], mfma_fp8_scaled(k0, qf[0], init, c_e8m0), c_e8m0);
+      } else if constexpr (QC) {
+        S[kb] = mfma_fp8_scaled(k0, qf[0], mt_init(mt_read(ks, kb), bq), c_e8m0);
       } else {
         S[kb] = mfma_fp8_scaled(k0, qf[0], NB, c_e8m0);
       }
@@ -644,7 +645,14 @@ __global__ __launch_bounds__(2 * BM, 256 / BM) void k_attn(AttentionArgs a) {
   // K(0) has landed once only the later loads are outstanding (with split
   // loads only the K waves issued K loads, and only they need to wait)
   if constexpr (kSplitLoads) {
-    if (k_wave) wait_vmcnt<kBarEvery * kLoadsPerTile>();
+    // K waves wait for K(0) (those that also load mean-term tiles for their
+    // MT(0), issued after it); a V wave that loads mean-term tiles waits for MT(0)
+    if (k_wave && mt_wave)
+      wait_vmcnt<kBarEvery * (kLoadsPerTile + 1)>();
+    else if (k_wave)
+      wait_vmcnt<kBarEvery * kLoadsPerTile>();
+    else if (mt_wave)
+      wait_vmcnt<kBarEvery * (kLoadsPerTile + 1)>();
   } else if (mt_wave) {
     wait_vmcnt<kBarEvery * (2 * kLoadsPerTile + 1)>();   // its mean-term loads follow each K load
   } else {
@@ -697,7 +705,7 @@ __global__ __launch_bounds__(2 * BM, 256 / BM) void k_attn(AttentionArgs a) {
     const uint8_t* kb = smem + ((PH + 1) % kSlots) * kTile;          // K(t+1)
     const int kbase = t * kBN;
     v8i Pn;
-    if constexpr (QC) {
+    if constexpr (QC && NH == 2) {
       // Q centring: as below, with the two mean-term products (the initial
       // accumulators of the score chains, nb included) ahead of the chains
       v8i kf[2][2];
@@ -789,6 +797,43 @@ __global__ __launch_bounds__(2 * BM, 256 / BM) void k_attn(AttentionArgs a) {
       fence();
       Pn[7] = probs4(1, 3, kbase);
       S[1] = mfma_fp8_scaled(kf[1][1], qf[1], s1, c_e8m0);
+    } else if constexpr (QC) {
+      // head_dim 64 with Q centring: the two mean-term products ahead of the
+      // two score products
+      v8i kf[2];
+      const uint32_t mtv0 = mt_read((PH + 1) % kSlots, 0);
+      const uint32_t mtv1 = mt_read((PH + 1) % kSlots, 1);
+      kf[0] = lds_read32(kb, koff[0][0], koff[0][1]);
+      kf[1] = lds_read32(kb + 32 * D, koff[0][0], koff[0][1]);
+      fence();
+      O[0] = mfma_fp8(vf[0], P, O[0]);
+      if (CAUSAL && t >= tdiag) mask_causal(t);
+      if (TAIL && ragged && t == nkt - 1) mask_tail(t);
+      rowmax_update(std::false_type{}, std::false_type{});
+      Pn[0] = probs4(0, 0, kbase);
+      fence();
+      O[1] = mfma_fp8(vf[1], P, O[1]);
+      Pn[1] = probs4(0, 1, kbase);
+      Pn[2] = probs4(0, 2, kbase);
+      fence();
+      lacc = mfma16_fp8(sel, P, lacc);
+      vf[0] = lds_read32(vn + 0 * 2048, voff[0], voff[1]);
+      vf[1] = lds_read32(vn + 1 * 2048, voff[0], voff[1]);
+      Pn[3] = probs4(0, 3, kbase);
+      fence();
+      const v16f m0 = mt_init(mtv0, bq);
+      Pn[4] = probs4(1, 0, kbase);
+      fence();
+      const v16f m1 = mt_init(mtv1, bq);
+      Pn[5] = probs4(1, 1, kbase);
+      fence();
+      const v16f s0 = mfma_fp8_scaled(kf[0], qf[0], m0, c_e8m0);
+      Pn[6] = probs4(1, 2, kbase);
+      fence();
+      const v16f s1 = mfma_fp8_scaled(kf[1], qf[0], m1, c_e8m0);
+      Pn[7] = probs4(1, 3, kbase);
+      S[0] = s0;
+      S[1] = s1;
     } else {
       // head_dim 64: two score products and two P V products a tile; the
       // vector work is the same as for 128 channels, so it sets the pace
@@ -1034,8 +1079,10 @@ void launch_attention_d(const AttentionArgs& a, hipStream_t stream) {
 
 template <bool EXACT>
 void launch_attention_e(const AttentionArgs& a, hipStream_t stream) {
-  if (a.head_dim == 64)
-    launch_attention_d<64, 256, EXACT, false>(a, stream);      // 64 channels: 256-query items only
+  if (a.head_dim == 64 && a.q_centre)
+    launch_attention_d<64, 256, EXACT, true>(a, stream);       // 64 channels: 256-query items only
+  else if (a.head_dim == 64)
+    launch_attention_d<64, 256, EXACT, false>(a, stream);
   else if (a.q_centre && a.bm == 128)
     launch_attention_d<kHeadDim, 128, EXACT, true>(a, stream);
   else if (a.q_centre)
@@ -1049,7 +1096,6 @@ void launch_attention_e(const AttentionArgs& a, hipStream_t stream) {
 hipError_t launch_attention(const AttentionArgs& a, hipStream_t stream) {
   if (a.nitems == 0) return hipSuccess;
   if (a.causal && a.bm != 256) return hipErrorInvalidValue;   // see launch_attention_d
-  if (a.q_centre && a.head_dim != kHeadDim) return hipErrorInvalidValue;   // Q centring at 128 channels
   if (a.exact_probs)
     launch_attention_e<true>(a, stream);
   else

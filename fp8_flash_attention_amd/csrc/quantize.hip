@@ -441,7 +441,9 @@ __device__ __forceinline__ uint32_t bf16_rne_bits(float f) {
   return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
 }
 
+template <int D>
 __global__ __launch_bounds__(256) void k_qmterm(QuantizeArgs a) {
+  constexpr int NH = D / 64;   // 64-channel halves
   const int4 u = a.qmt_units[blockIdx.x];
   const int h = blockIdx.y;
   const SegInfo si = a.segs[u.x];
@@ -451,14 +453,14 @@ __global__ __launch_bounds__(256) void k_qmterm(QuantizeArgs a) {
   const int blk = kQmUnitBlocks * u.y + lq;   // this lane's A row (zero past the segment's blocks)
   const bool blk_live = blk < nblk;
   const int64_t nqb = a.rows / kQmBlock;
-  const float* qm = a.qmean + ((int64_t)h * nqb + si.row0 / kQmBlock + (blk_live ? blk : 0)) * kHeadDim;
+  const float* qm = a.qmean + ((int64_t)h * nqb + si.row0 / kQmBlock + (blk_live ? blk : 0)) * D;
 
   // A operands, once per wave: the block means of this lane's row over
   // channels 64 half + 32 lg .. +32, in three E4M3 parts
-  v8i_q ap[2][3];
-  int sp[2][3];
+  v8i_q ap[NH][3];
+  int sp[NH][3];
 #pragma unroll
-  for (int half = 0; half < 2; half++) {
+  for (int half = 0; half < NH; half++) {
     const int ch0 = 64 * half + 32 * lg;
     float r[32];
     float m = 0.f;
@@ -512,21 +514,24 @@ __global__ __launch_bounds__(256) void k_qmterm(QuantizeArgs a) {
   // 64 half + 32 lg .. +32; the next step's K bytes are loaded ahead
   int key0 = u.z + 32 * wave;
   if (key0 >= kend) return;   // wave-uniform
-  auto load_b = [&](int k0, uint4 (&b)[4]) __attribute__((always_inline)) {
-    const uint8_t* krow = a.codes[1] + ((int64_t)h * a.rows + si.row0 + k0 + lq) * kHeadDim + 32 * lg;
-    b[0] = *reinterpret_cast<const uint4*>(krow);
-    b[1] = *reinterpret_cast<const uint4*>(krow + 16);
-    b[2] = *reinterpret_cast<const uint4*>(krow + 64);
-    b[3] = *reinterpret_cast<const uint4*>(krow + 80);
+  auto load_b = [&](int k0, uint4 (&b)[2 * NH]) __attribute__((always_inline)) {
+    const uint8_t* krow = a.codes[1] + ((int64_t)h * a.rows + si.row0 + k0 + lq) * D + 32 * lg;
+#pragma unroll
+    for (int half = 0; half < NH; half++) {
+      b[2 * half] = *reinterpret_cast<const uint4*>(krow + 64 * half);
+      b[2 * half + 1] = *reinterpret_cast<const uint4*>(krow + 64 * half + 16);
+    }
   };
-  uint4 bn[4];
+  uint4 bn[2 * NH];
   load_b(key0, bn);
   for (; key0 < kend; key0 += 128) {
-    const uint4 b[4] = {bn[0], bn[1], bn[2], bn[3]};
+    uint4 b[2 * NH];
+#pragma unroll
+    for (int j = 0; j < 2 * NH; j++) b[j] = bn[j];
     if (key0 + 128 < kend) load_b(key0 + 128, bn);
     v16f_q acc = {};
 #pragma unroll
-    for (int half = 0; half < 2; half++) {
+    for (int half = 0; half < NH; half++) {
       const uint4 b0 = b[2 * half], b1 = b[2 * half + 1];
       const v8i_q bk = v8i_q{(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
 #pragma unroll
@@ -769,11 +774,8 @@ hipError_t launch_quantize_d(const QuantizeArgs& a, hipStream_t stream) {
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (!a.mx && a.q_centre && a.nqmt_units > 0) {
-    if constexpr (D == kHeadDim) {
-      hipLaunchKernelGGL(k_qmterm, dim3(a.nqmt_units, a.heads), dim3(256), 0, stream, a);
-      return hipGetLastError();
-    }
-    return hipErrorInvalidValue;   // the planner allows Q centring at 128 channels only
+    hipLaunchKernelGGL(k_qmterm<D>, dim3(a.nqmt_units, a.heads), dim3(256), 0, stream, a);
+    return hipGetLastError();
   }
   return hipSuccess;
 }

@@ -174,7 +174,7 @@ fp8attn_status fp8attn_plan(fp8attn_plan_t* plan_out, int64_t tokens, int32_t he
  *   With FP8ATTN_PLAN_MXFP4: the block-mean operand fl32(qm * c), quantized
  *   like a Q row, is multiplied with K inside the kernel and added to the
  *   scores.
- *   E4M3 plans (head_dim above 64): Q's amax, scale and codes are those of
+ *   E4M3 plans (any head size): Q's amax, scale and codes are those of
  *   fl32(q - qm); a rounded mean would carry as much error as centring
  *   removes, so fp8attn_quantize also writes the mean term of every
  *   (block, key) pair of a segment, f * (qm . khat) with khat the K codes
@@ -212,7 +212,7 @@ fp8attn_status fp8attn_plan(fp8attn_plan_t* plan_out, int64_t tokens, int32_t he
  *   sglang PR's recipe, instead of the default log-linear code (see
  *   fp8attn_forward): about 12% slower, relative RMS error about 0.054 instead
  *   of 0.056 on the pages' normally distributed workloads.
- * Unknown flag bits, FP8ATTN_PLAN_Q_CENTRE on an E4M3 plan of head_dim 64 or less,
+ * Unknown flag bits,
  * FP8ATTN_PLAN_EXACT_PROBS with FP8ATTN_PLAN_MXFP4,
  * FP8ATTN_PLAN_MXFP4 with FP8ATTN_PLAN_SEGMENT_SCALES (its scales are already
  * local to 32 elements) or with a head_dim other than 128, a head_dim that is

@@ -315,11 +315,12 @@ def test_mxfp4_plan_flags_layout_and_schedule():
     L = _lib.lib()
     cu = (ctypes.c_int32 * 4)(0, 100, 100, 300)
     h = ctypes.c_void_p()
-    # E4M3 Q centring needs a head size above 64; FP4 takes no per-segment scales
-    assert L.fp8attn_plan_ex(ctypes.byref(h), 300, 2, cu, 3, ctypes.c_float(0.088), -1,
-                             _lib.PLAN_Q_CENTRE | _lib.PLAN_HEAD_DIM_64) == _lib.EINVAL
-    assert L.fp8attn_plan_ex(ctypes.byref(h), 300, 2, cu, 3, ctypes.c_float(0.088), -1,
-                             _lib.PLAN_Q_CENTRE | _lib.plan_head_dim(40)) == _lib.EINVAL
+    # E4M3 Q centring takes any head size; FP4 takes no per-segment scales
+    for extra in (_lib.PLAN_HEAD_DIM_64, _lib.plan_head_dim(40), 0):
+        assert L.fp8attn_plan_ex(ctypes.byref(h), 300, 2, cu, 3, ctypes.c_float(0.088), -1,
+                                 _lib.PLAN_Q_CENTRE | extra) == _lib.OK
+        L.fp8attn_plan_destroy(h)
+        h = ctypes.c_void_p()
     assert L.fp8attn_plan_ex(ctypes.byref(h), 300, 2, cu, 3, ctypes.c_float(0.088), -1,
                              _lib.PLAN_MXFP4 | _lib.PLAN_SEGMENT_SCALES) == _lib.EINVAL
     assert h.value is None

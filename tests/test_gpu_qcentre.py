@@ -20,7 +20,8 @@ the scores.  Checked here:
   few thousand keys: tests/test_oracle_qcentre.py), and below the error of an
   uncentred plan on the same inputs;
 * the LSE, key splits, causal masking, per-segment scales, exact
-  probabilities and both query tiles (128 and 256 queries per work item).
+  probabilities, both query tiles (128 and 256 queries per work item) and
+  head sizes of 40, 64, 96 and 128 channels.
 """
 import math
 
@@ -69,7 +70,7 @@ def _oracle(q, k, v, cu, sc, segment_scales=False):
 def _run(w, causal=False, lse=False, segment_scales=False, exact_probs=False, q_centre=True):
     q, k, v = generate(w, device="cuda")
     plan = fa.Plan(w.tokens, w.heads, w.cu_seqlens, w.softmax_scale, device=0, q_centre=q_centre, causal=causal,
-                   segment_scales=segment_scales, exact_probs=exact_probs)
+                   segment_scales=segment_scales, exact_probs=exact_probs, head_dim=w.head_dim)
     info = plan.info()
     log(f"qcentre={q_centre} {w.name} T={w.tokens} H={w.heads} cu={list(w.cu_seqlens)[:8]} causal={causal} "
         f"lse={lse} seg_scales={segment_scales} exact={exact_probs} tile={info['query_tile']} "
@@ -84,15 +85,20 @@ def _run(w, causal=False, lse=False, segment_scales=False, exact_probs=False, q_
 
 
 def _check_codes(plan, ws, r, cu, heads):
+    """Codes, scales, K means and block means bit for bit (the d channels of
+    the head size; the kernel width's other channels zero)."""
+    D = r["q_codes"].shape[2]
     got = read_codes(plan, ws, heads)
     for name in ("q_codes", "k_codes", "v_codes"):
-        assert np.array_equal(got[name], r[name][:, heads]), name
+        assert np.array_equal(got[name][..., :D], r[name][:, heads]), name
+        assert not got[name][..., D:].any(), f"{name}: padding channels not zero"
     sc = np.asarray(got["scales"])
     assert np.array_equal(sc.view(np.uint32), r["scales"].view(np.uint32))
-    assert np.array_equal(got["mu"].view(np.uint32), r["mu"].view(np.uint32))
-    qmean = plan.region(ws, _lib.REGION_QMEAN).cpu().numpy()       # [H][rows/128][128]
+    assert np.array_equal(got["mu"][..., :D].view(np.uint32), r["mu"].view(np.uint32))
+    qmean = plan.region(ws, _lib.REGION_QMEAN).cpu().numpy()       # [H][rows/128][kernel width]
     for i, (s, a, b, g) in enumerate(_blocks(cu)):
-        assert np.array_equal(qmean[heads, g].view(np.uint32), r["qm"][i][heads].view(np.uint32)), (i, g)
+        assert np.array_equal(qmean[heads, g, :D].view(np.uint32), r["qm"][i][heads].view(np.uint32)), (i, g)
+    assert not qmean[:, :, D:].any(), "block means of padding channels not zero"
     assert not qmean[:, -1].any(), "guard block mean not zero"
 
 
@@ -151,6 +157,9 @@ SMALL = [
     make_workload("qc_ragged", 700, 3, [0, 300, 700], seed=901, k_offset_var=2.0, q_offset_var=2.0),
     make_workload("qc_varlen", 1500, 3, [0, 0, 1, 64, 65, 193, 700, 700, 1500], seed=902, q_offset_var=2.0),
     make_workload("qc_fused", 500, 4, [0, 130, 500], seed=903, layout="fused", q_offset_var=2.0),
+    make_workload("qc_d64", 700, 3, [0, 300, 700], seed=911, k_offset_var=2.0, q_offset_var=2.0, head_dim=64),
+    make_workload("qc_d40", 900, 2, [0, 0, 65, 900], seed=912, q_offset_var=2.0, head_dim=40),
+    make_workload("qc_d96", 700, 2, [0, 129, 700], seed=913, k_offset_var=2.0, q_offset_var=2.0, head_dim=96),
 ]
 
 
@@ -285,3 +294,29 @@ def test_q_offset_variant_of_the_denoise_step_shape_against_the_bar():
     # this Q-offset variant of the denoise-step shape under the 0.06 bar
     assert err[(True, True)] <= compare.REL_RMS_BAR
     assert err[(False, True)] <= compare.REL_RMS_BAR + 5e-4
+
+
+def test_head_dim_64_causal_lse_and_split():
+    w = make_workload("qc_d64_causal", 700, 3, [0, 300, 700], seed=914, k_offset_var=2.0, q_offset_var=2.0,
+                      head_dim=64)
+    plan, ws, out, l, (q, k, v) = _run(w, causal=True, lse=True)
+    r, qop, dk, dv = _oracle(q, k, v, w.cu_seqlens, w.softmax_scale)
+    _check_codes(plan, ws, r, w.cu_seqlens, list(range(w.heads)))
+    cu, sc = w.cu_seqlens, w.softmax_scale
+    o = out.cpu().double().numpy()
+    diag = A.attention(qop, dk, dv, cu, sc, causal=True).numpy()
+    pos = np.concatenate([np.arange(b - a) for a, b in zip(cu[:-1], cu[1:])])
+    rd, ex_d = compare.rel_rms(o, diag), compare.allclose_excess(o[pos >= 64], diag[pos >= 64])
+    log(f"  d64 causal rel_rms vs dequantized {rd:.5f}, excess (>= 64 keys) {ex_d:.5f}")
+    assert rd <= DIAG_BAR and ex_d <= 0.0
+    dkc = dk.copy()
+    for s_, (a, b) in enumerate(zip(cu[:-1], cu[1:])):
+        dkc[a:b] += r["mu"][s_][None].astype(np.float64)
+    ld = A.lse_rows(torch.from_numpy(qop), torch.from_numpy(dkc), cu, sc, causal=True).numpy().T
+    check_lse(l.cpu().double().numpy(), ld, False, "q-centred d64 causal")
+    # 256-query items of one head split along the keys
+    w2 = make_workload("qc_d64_split", 3000, 1, [0, 3000], seed=915, k_offset_var=2.0, q_offset_var=2.0, head_dim=64)
+    plan2, ws2, out2, l2, (q2, k2, v2) = _run(w2, lse=True)
+    assert plan2.info()["partial_slots"] > 0, "expected a split plan"
+    r2, qop2, dk2, dv2 = _oracle(q2, k2, v2, w2.cu_seqlens, w2.softmax_scale)
+    _check_out(w2, out2, q2, k2, v2, list(range(w2.tokens)), qop2, dk2, dv2)

@@ -4,7 +4,7 @@ oracle (test infrastructure; the bars are those of the targeted tests).
 E4M3 plans draw the segment table (empty, one-token, tile-edge and longer
 segments), the head count, the head size (any multiple of 8 up to 128), and
 whether the plan is causal, has per-segment scales, exact probabilities, a
-K offset and (head sizes above 64) Q block-mean centring.  Each checks: the E4M3 codes, scales and K means of the real
+K offset and Q block-mean centring.  Each checks: the E4M3 codes, scales and K means of the real
 channels bit for bit (padding channels zero); every output element against
 the oracle on the dequantized operands (with Q centring: the centred codes
 plus the exact block mean) (|o - r| <= 0.1 + 0.1 |r|, relative
@@ -51,7 +51,7 @@ def _e4m3_config(i):
     c = dict(cu=cu, H=int(rng.integers(1, 5)), D=8 * int(rng.integers(1, 17)), causal=bool(rng.random() < 0.4),
              seg=bool(rng.random() < 0.3), exact=bool(rng.random() < 0.3),
              koff=2.0 if rng.random() < 0.5 else None, seed=9100 + i)
-    c["qc"] = c["D"] > 64 and bool(rng.random() < 0.5)     # drawn last: the other draws are unchanged
+    c["qc"] = bool(rng.random() < 0.5)     # drawn last: the other draws are unchanged
     return c
 
 
