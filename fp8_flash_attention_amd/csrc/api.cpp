@@ -384,6 +384,14 @@ fp8attn_status fp8attn_plan_ex(fp8attn_plan_t* plan_out, int64_t tokens, int32_t
   if (p->q_centre && !p->mx) {
     // mean-term table: per head, per segment, (padded rows / 128) blocks x padded rows
     p->mt_seg.resize(num_segments);
+    // mean-term work units: one key chunk of one segment and head is walked by
+    // all its block groups; those units go to one XCD (workgroups reach the
+    // XCDs in turn, so list position p runs on XCD p % 8), where the chunk's
+    // K codes are read from HBM once and then hit that XCD's L2.  Chunks are
+    // dealt to the least-loaded of eight streams, the streams interleaved
+    // and padded with empty units (segment -1) to one length.
+    constexpr int kXcds = 8;
+    std::vector<std::vector<int4>> stream(kXcds);
     int64_t e = 0;
     for (int s = 0; s < num_segments; s++) {
       const int64_t lr = (int64_t)(p->segs[s].len + kRowPad - 1) / kRowPad * kRowPad;
@@ -395,16 +403,33 @@ fp8attn_status fp8attn_plan_ex(fp8attn_plan_t* plan_out, int64_t tokens, int32_t
                                           "(32-bit offsets into the mean-term table)");
       }
       p->mt_seg[s] = e;
-      const int64_t nblk = lr / kQmBlock;
-      for (int64_t bg = 0; bg < (nblk + kQmUnitBlocks - 1) / kQmUnitBlocks; bg++)
-        for (int64_t k0 = 0; k0 < lr; k0 += kQmUnitKeys) p->qmt_units.push_back(int4{s, (int)bg, (int)k0, 0});
-      e += nblk * lr;
+      e += (lr / kQmBlock) * lr;
     }
     p->mt_per_head = e;
-    if ((double)e * 4.0 * heads > (double)((int64_t)1 << 40) || (int64_t)p->qmt_units.size() > INT32_MAX) {
+    if ((double)e * 4.0 * heads > (double)((int64_t)1 << 40)) {
       delete p;
       return fail(FP8ATTN_EUNSUPPORTED, "Q-centring mean-term table above 1 TiB");
     }
+    for (int h = 0; h < heads; h++)
+      for (int s = 0; s < num_segments; s++) {
+        const int64_t lr = (int64_t)(p->segs[s].len + kRowPad - 1) / kRowPad * kRowPad;
+        const int64_t nbg = (lr / kQmBlock + kQmUnitBlocks - 1) / kQmUnitBlocks;
+        for (int64_t k0 = 0; k0 < lr; k0 += kQmUnitKeys) {
+          int best = 0;
+          for (int x = 1; x < kXcds; x++)
+            if (stream[x].size() < stream[best].size()) best = x;
+          for (int64_t bg = 0; bg < nbg; bg++) stream[best].push_back(int4{s, (int)bg, (int)k0, h});
+        }
+      }
+    size_t len = 0;
+    for (const auto& v : stream) len = std::max(len, v.size());
+    if ((double)len * kXcds > (double)INT32_MAX) {
+      delete p;
+      return fail(FP8ATTN_EUNSUPPORTED, "Q-centring mean-term work list above 2^31 units");
+    }
+    p->qmt_units.reserve(len * kXcds);
+    for (size_t i = 0; i < len; i++)
+      for (int x = 0; x < kXcds; x++) p->qmt_units.push_back(i < stream[x].size() ? stream[x][i] : int4{-1, 0, 0, 0});
   }
   // the attention kernel addresses one head's code rows through 32-bit buffer
   // offsets: rows * 128 bytes must fit

@@ -130,7 +130,7 @@ struct QuantizeArgs {
   float* qmean;              // [H][rows/128][D]
   uint32_t* mt;              // [H][mt_per_head]
   const int64_t* mt_seg;     // [nseg]: first entry of each segment's part of a head's table
-  const int4* qmt_units;     // work of the mean-term kernel: {segment, block group, first key, 0}
+  const int4* qmt_units;     // work of the mean-term kernel: {segment, block group, first key, head}; segment -1: none
   int32_t nqmt_units;
   int32_t exact_probs;       // frame of the mean term: x (1) or y = 8 x (0)
   int64_t mt_per_head;

@@ -429,8 +429,9 @@ __global__ __launch_bounds__(256) void k_pack(QuantizeArgs a) {
 // 2^(e-4), 2^(e-8) per block and 64 channels (each part takes the rounding error of the
 // previous one, so the parts carry about 12 significant bits of every mean),
 // B = khat^T (64 channels x 32 keys), all six products of the 128 channels
-// chained into one FP32 accumulator.  grid = (units, H), block = 256: unit
-// {s, bg, k0, 0} covers blocks 32 bg .. +32 of segment s and keys k0 .. +1024;
+// chained into one FP32 accumulator.  grid = units, block = 256: unit
+// {s, bg, k0, h} covers blocks 32 bg .. +32 of segment s and keys k0 .. +1024
+// of head h (s = -1: an empty unit);
 // each wave splits the means once and then takes 32 keys a step.
 // ---------------------------------------------------------------------------
 typedef int v8i_q __attribute__((ext_vector_type(8)));
@@ -445,7 +446,8 @@ template <int D>
 __global__ __launch_bounds__(256) void k_qmterm(QuantizeArgs a) {
   constexpr int NH = D / 64;   // 64-channel halves
   const int4 u = a.qmt_units[blockIdx.x];
-  const int h = blockIdx.y;
+  if (u.x < 0) return;   // padding of the work list
+  const int h = u.w;
   const SegInfo si = a.segs[u.x];
   const int lr = (si.len + kRowPad - 1) / kRowPad * kRowPad;   // the segment's padded rows
   const int nblk = lr / kQmBlock;
@@ -774,7 +776,7 @@ hipError_t launch_quantize_d(const QuantizeArgs& a, hipStream_t stream) {
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (!a.mx && a.q_centre && a.nqmt_units > 0) {
-    hipLaunchKernelGGL(k_qmterm<D>, dim3(a.nqmt_units, a.heads), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(k_qmterm<D>, dim3(a.nqmt_units), dim3(256), 0, stream, a);
     return hipGetLastError();
   }
   return hipSuccess;
