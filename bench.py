@@ -47,6 +47,40 @@ DEFAULT_WORKLOAD = "s30272_h56_koffset"
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "attention_counters.json")
 
 
+def l2_stream_bytes(items, segments, bm, wg_per_cu, key_bytes, q_row_bytes, out_bytes,
+                    causal=False, cus_per_xcd=32, xcds=8, kbn=64):
+    """Bytes a forward launch must move between HBM and the eight per-XCD L2
+    caches when the concurrent workgroups of an XCD walk the K/V tiles of a
+    (segment, head) together: each round of an XCD's workgroups reads the K/V
+    tiles of every (segment, head) it touches once, and every item (or key
+    piece) reads its own Q tile once; the output is written once.
+
+    items: the plan's launch-ordered work list, (segment, q0, head, split) with
+    split = piece | count << 4 | slot << 8 (0: whole item); launch position p
+    runs on XCD p % xcds as the (p // xcds)-th workgroup there.
+    key_bytes: K plus V bytes per key and head; q_row_bytes: Q bytes per query
+    row and head; out_bytes: output bytes per launch.
+    """
+    slots = wg_per_cu * cus_per_xcd
+    rounds = {}
+    q_bytes = 0
+    for p, (seg, q0, head, split) in enumerate(items):
+        if seg < 0:
+            continue
+        L = segments[seg]
+        nkt = (L + kbn - 1) // kbn
+        hi = ((min(L, q0 + bm) + kbn - 1) // kbn) if causal else nkt
+        lo = 0
+        if split:
+            i, n = split & 15, (split >> 4) & 15
+            lo, hi = nkt * i // n, nkt * (i + 1) // n
+        tiles = rounds.setdefault((p % xcds, (p // xcds) // slots), {}).setdefault((seg, head), set())
+        tiles.update(range(lo, hi))
+        q_bytes += bm * q_row_bytes
+    kv = sum(len(t) for r in rounds.values() for t in r.values()) * kbn * key_bytes
+    return int(kv + q_bytes + out_bytes)
+
+
 def kernel_source_hash(kernel_file: str = "attention.hip") -> str:
     """sha256 (16 hex) of the attention kernel's code with comments and blank lines
     removed, so that counters stay attached to the code they were taken on."""
@@ -327,6 +361,13 @@ def main() -> int:
     key = (w.name + (":mxfp4" if mx else "") + (":qc" if args.q_centre else "") + (":causal" if args.causal else "")
            + (":exact" if args.exact_probs and not mx else "") + (":lse" if args.lse else ""))
     traffic = measured_traffic(key, kfile)
+    info = plan.info()
+    kw = 64 if w.head_dim <= 64 and not mx else 128      # channels the kernel reads per row
+    l2_floor = None if args.q_centre else l2_stream_bytes(
+        plan.work_items(), list(w.segments), info["query_tile"], 1 if info["query_tile"] == 256 and not mx else 2,
+        key_bytes=2 * (kw // 2 + kw // 32) if mx else 2 * kw, q_row_bytes=(kw // 2 + kw // 32) if mx else kw,
+        out_bytes=2 * w.tokens * w.heads * w.head_dim, causal=args.causal,
+        cus_per_xcd=torch.cuda.get_device_properties(dev).multi_processor_count // 8)
     res = {
         "metric": (METRIC_FP4 if mx else (METRIC_CAUSAL if args.causal else METRIC)) + (
             " [causal: visible pairs only]" if mx and args.causal else "") + (
@@ -379,6 +420,9 @@ def main() -> int:
             # codes: 1 B per element (E4M3) or 0.5 B + 1/32 B of scales (FP4) for Q, K, V; BF16 output
             "algorithmic_bytes": (int(3 * w.tokens * w.heads * (64 + 4) + 2 * w.tokens * w.heads * 128) if mx
                                   else 5 * w.tokens * w.heads * w.head_dim),
+            # K/V streamed once per (XCD, round of its concurrent workgroups,
+            # segment-head), Q once per item, output once: what per-XCD L2s allow
+            "l2_stream_bytes": l2_floor,
         },
     }
     if args.copy_calibration > 0:

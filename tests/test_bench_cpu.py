@@ -48,3 +48,50 @@ def test_every_profile_summary_names_its_command():
                 t = fh.read()
             assert "rocprofv3 " in t and "bench.py" in t, f
             assert os.path.getsize(os.path.join(pdir, f)) < 64 * 1024, f
+
+
+def _l2_model(name, fmt):
+    import fp8_flash_attention_amd as fa
+    from workloads import WORKLOADS
+    w = WORKLOADS[name]
+    p = fa.Plan(w.tokens, w.heads, w.cu_seqlens, w.softmax_scale, device=-1, fmt=fmt)
+    info = p.info()
+    mx = fmt == "mxfp4"
+    return bench.l2_stream_bytes(p.work_items(), list(w.segments), info["query_tile"],
+                                 1 if info["query_tile"] == 256 and not mx else 2,
+                                 key_bytes=2 * (64 + 4) if mx else 2 * 128, q_row_bytes=(64 + 4) if mx else 128,
+                                 out_bytes=2 * w.tokens * w.heads * w.head_dim)
+
+
+def test_l2_stream_model_explains_the_measured_attention_traffic():
+    # With one workgroup per CU (E4M3, 256-query items) the counters' per-launch
+    # bytes (FETCH_SIZE + WRITE_SIZE, taken on the GPU) sit within 2% of the
+    # model in which each XCD's concurrent workgroups read a (segment, head)'s
+    # K/V tiles once per round: the traffic above the algorithmic bytes is the
+    # eight separate L2s, not tiles re-read by workgroups that drift apart.
+    # With two workgroups per CU (FP4, 128-query items) the model is only a
+    # floor: the measured bytes are about 1.44 times it.
+    with open(bench.COUNTERS_FILE) as f:
+        counters = json.load(f)
+    model = _l2_model("s30272_h56_koffset", "e4m3")
+    measured = counters["s30272_h56_koffset"]["hbm_bytes_per_launch"]
+    assert abs(measured - model) <= 0.02 * model, (measured, model)
+    model = _l2_model("s30272_h56_koffset", "mxfp4")
+    measured = counters["s30272_h56_koffset:mxfp4"]["hbm_bytes_per_launch"]
+    assert model <= measured <= 1.5 * model, (measured, model)
+
+
+def test_l2_stream_model_small_cases():
+    # one XCD round holding two items of one head (launch positions 0 and 8
+    # both run on XCD 0): K/V once, Q twice
+    items = [(0, 0, 0, 0)] + [(-1, 0, 0, 0)] * 7 + [(0, 256, 0, 0)]
+    b = bench.l2_stream_bytes(items, [512], 256, 1, key_bytes=256, q_row_bytes=128, out_bytes=0, cus_per_xcd=32)
+    assert b == 512 * 256 + 2 * 256 * 128
+    # the same two items on XCDs 0 and 1: K/V read by both L2s
+    items = [(0, 0, 0, 0), (0, 256, 0, 0)]
+    b = bench.l2_stream_bytes(items, [512], 256, 1, key_bytes=256, q_row_bytes=128, out_bytes=0, cus_per_xcd=32)
+    assert b == 2 * 512 * 256 + 2 * 256 * 128
+    # two key pieces of one item on two XCDs: each reads its half of the tiles
+    items = [(0, 0, 0, 0 | 2 << 4), (0, 0, 0, 1 | 2 << 4)]
+    b = bench.l2_stream_bytes(items, [512], 256, 1, key_bytes=256, q_row_bytes=128, out_bytes=7, cus_per_xcd=32)
+    assert b == 512 * 256 + 2 * 256 * 128 + 7
