@@ -93,8 +93,8 @@ __device__ __forceinline__ void stat_rows(const uint16_t* base, int64_t ts, int 
   float mn[8], mx[8];
 #pragma unroll
   for (int i = 0; i < 8; i++) { sum[i] = 0.0; mn[i] = __builtin_inff(); mx[i] = -__builtin_inff(); }
-#pragma unroll 16
-  for (int j = j0; j < j1; j++) {   // unrolled: 16 loads in flight, sums still in token order
+#pragma unroll 32
+  for (int j = j0; j < j1; j++) {   // unrolled: 32 loads in flight, sums still in token order
     const uint4 v = load8(base + (int64_t)(tok0 + j) * ts, live);
     float f[8];
     unpack8(v, f);
@@ -162,8 +162,8 @@ __global__ __launch_bounds__(256) void k_stats(QuantizeArgs a) {
 
   float m = 0.f;
   if (active) {
-#pragma unroll 16
-    for (int j = 0; j < ch.ntok; j++) {   // unrolled: 16 loads in flight, sums still in token order
+#pragma unroll 32
+    for (int j = 0; j < ch.ntok; j++) {   // unrolled: 32 loads in flight, sums still in token order
       const uint4 v = load8(base + (int64_t)(ch.tok0 + j) * ts, live);
       float f[8];
       unpack8(v, f);
